@@ -1,0 +1,216 @@
+"""Pins of the fp64 oracle (CPU only), and planted mistakes that the pins must catch."""
+import copy
+import types
+
+import numpy as np
+import pytest
+
+from oracle import layer as L
+from oracle import plan as P
+from oracle.compare import compare
+import pins
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("seed", [0, 7])
+def test_brute_force_mlp(act, bias, seed):
+    pins.check_brute_mlp(L, act, seed=seed, bias=bias)
+
+
+@pytest.mark.parametrize("bias", [True, False])
+def test_brute_force_attnproj(bias):
+    pins.check_brute_attnproj(L, bias=bias)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+@pytest.mark.parametrize("bias", [True, False])
+def test_finite_difference_mlp(act, bias):
+    pins.check_fd_mlp(L, act, bias=bias, seed=3)
+
+
+def test_finite_difference_attnproj():
+    pins.check_fd_attnproj(L, seed=5)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_torch_autograd_float64(act):
+    pins.check_torch_mlp(L, act, bias=(act == "gelu"))
+
+
+def test_textbook_values():
+    pins.check_textbook(L)
+
+
+def test_activation_special_values():
+    pins.check_activation_limits(L)
+
+
+def test_library_activations():
+    pins.check_library_activations(L)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_tp_sum_invariance(act):
+    pins.check_tp_sum(L, act, bias=(act == "gelu"))
+
+
+def test_tp_sum_invariance_tiny_workload_shape():
+    """The tiny GPT workload: h=512, F=2048 at TP 1/4 (shard 512), with a row-parallel bias."""
+    pins.check_tp_sum(L, "gelu", tp=4, M=8, h=512, F=2048, bias=True)
+
+
+# ------------------------------------------------------------------------------- closed forms
+def test_closed_forms():
+    rng = np.random.default_rng(1)
+    M, h = 6, 8
+    X = rng.standard_normal((M, h))
+    W1 = rng.standard_normal((h, h))
+    b1 = rng.standard_normal(h)
+    W2 = rng.standard_normal((h, h))
+    # W2 = 0  =>  Z = 0 exactly
+    assert np.all(L.mlp_fwd(X, W1, b1, np.zeros_like(W2), "gelu")["Z"] == 0.0)
+    # W1 = 0  =>  every row of Z equals act(b1) W2^T
+    Z = L.mlp_fwd(X, np.zeros_like(W1), b1, W2, "gelu")["Z"]
+    row = (0.5 * b1 * (1 + np.vectorize(__import__("math").erf)(b1 / np.sqrt(2)))) @ W2.T
+    assert np.allclose(Z, np.broadcast_to(row, Z.shape), rtol=1e-14, atol=1e-14)
+    # identity weights: Z = gelu(X) ; SwiGLU with W_g = W_u = I: Z = silu(X) X
+    I = np.eye(h)
+    from scipy.special import ndtr
+    assert np.allclose(L.mlp_fwd(X, I, None, I, "gelu")["Z"], X * ndtr(X), rtol=1e-14, atol=1e-15)
+    Zs = L.mlp_fwd(X, np.concatenate([I, I]), None, I, "swiglu")["Z"]
+    assert np.allclose(Zs, X * X / (1 + np.exp(-X)), rtol=1e-14, atol=1e-15)
+    # gate and up are distinguished: W_g = I, W_u = 2 I gives 2 silu(X) X, not silu(2X) X
+    Zg = L.mlp_fwd(X, np.concatenate([I, 2 * I]), None, I, "swiglu")["Z"]
+    assert np.allclose(Zg, 2 * X * X / (1 + np.exp(-X)), rtol=1e-14, atol=1e-15)
+
+
+def test_attnproj_closed_forms():
+    rng = np.random.default_rng(2)
+    X = rng.standard_normal((5, 4))
+    C = rng.standard_normal((5, 3))
+    o = L.attnproj_fwd(X, np.eye(4), None, C, np.zeros((4, 3)))
+    assert np.array_equal(o["QKV"], X) and np.all(o["Z"] == 0)
+
+
+# ------------------------------------------------------------------------------- slice geometry
+def test_even_ranges_cover_and_order():
+    for n, p in [(256, 2), (8192, 4), (16384, 8), (2560, 2), (4096, 2), (7, 7), (12, 1)]:
+        rs = P.even_ranges(n, p)
+        assert rs[0][0] == 0 and rs[-1][1] == n and len(rs) == p
+        assert all(rs[i][1] == rs[i + 1][0] for i in range(p - 1))
+        assert len({b - a for a, b in rs}) == 1
+    for n, p in [(10, 3), (0, 1), (5, 0)]:
+        with pytest.raises(ValueError):
+            P.even_ranges(n, p)
+
+
+def test_handoff_pieces_tile_exactly_once():
+    for rows, cols, r, c in [(256, 512, 2, 2), (16384, 8192, 8, 2), (24, 40, 3, 5)]:
+        cover = np.zeros((rows, cols), dtype=np.int32)
+        pieces = P.handoff_pieces(rows, cols, r, c)
+        assert len(pieces) == r * c
+        for (a, b, x, y) in pieces:
+            cover[a:b, x:y] += 1
+        assert np.all(cover == 1)
+        assert pieces == sorted(pieces)  # row slice major, ascending
+
+
+# ----------------------------------------------------------------------------------- comparator
+def test_comparator_accepts_and_rejects():
+    rng = np.random.default_rng(4)
+    o = rng.standard_normal((64, 48))
+    assert compare(o, o).ok
+    # bf16-level rounding noise passes
+    g = o * (1 + rng.uniform(-2 ** -9, 2 ** -9, o.shape))
+    assert compare(g, o).ok
+    # one large elementwise error fails the elementwise test
+    g = o.copy(); g[3, 5] += 0.5
+    v = compare(g, o)
+    assert not v.ok and v.n_elem_violations == 1 and v.worst_index == (3, 5)
+    # 1% relative noise everywhere fails the Frobenius test (elementwise bound alone would pass)
+    g = o * (1 + 0.01 * rng.choice([-1, 1], o.shape))
+    v = compare(g, o)
+    assert not v.ok and v.n_elem_violations == 0 and v.rel_fro > 5e-3
+    g = o.copy(); g[0, 0] = np.nan
+    assert not compare(g, o).ok
+    with pytest.raises(ValueError):
+        compare(o[:, :3], o)
+
+
+# ------------------------------------------------------------------------------ planted mistakes
+def _mutant(**overrides):
+    """A copy of the oracle's layer module with some functions replaced."""
+    m = types.ModuleType("oracle_mutant")
+    m.__dict__.update({k: v for k, v in vars(L).items() if not k.startswith("__")})
+    m.__dict__.update(overrides)
+    # module functions look up globals in their own module: rebind them to the mutant namespace
+    for k, v in list(m.__dict__.items()):
+        if isinstance(v, types.FunctionType) and k not in overrides:
+            m.__dict__[k] = types.FunctionType(v.__code__, m.__dict__, k, v.__defaults__, v.__closure__)
+    return m
+
+
+def _fails(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_gelu_prime_missing_density_term():
+    bad = _mutant(gelu_prime=lambda u: 0.5 * (1.0 + L.erf(u * L._INV_SQRT2)))
+    assert _fails(lambda: pins.check_fd_mlp(bad, "gelu"))
+
+
+def test_planted_silu_prime_wrong_sign():
+    def silu_prime(g):
+        s = L.sigmoid(g)
+        return s * (1.0 - g * (1.0 - s))
+    bad = _mutant(silu_prime=silu_prime)
+    assert _fails(lambda: pins.check_fd_mlp(bad, "swiglu"))
+
+
+def test_planted_gate_up_swapped():
+    def activate(U, act):
+        if act == "swiglu":
+            G, V = L._split_gate_up(U)
+            return L.silu(V) * G
+        return L.gelu(U)
+    bad = _mutant(activate=activate)
+    assert _fails(lambda: pins.check_brute_mlp(bad, "swiglu"))
+
+
+def test_planted_bias_dropped():
+    def mlp_fwd(X, W1, b1, W2, act):
+        U = X @ W1.T
+        H = L.activate(U, act)
+        return {"U": U, "H": H, "Z": H @ W2.T}
+    bad = _mutant(mlp_fwd=mlp_fwd)
+    assert _fails(lambda: pins.check_brute_mlp(bad, "gelu", bias=True))
+
+
+def test_planted_transposed_operand_in_dgrad():
+    def mlp_bwd(X, W1, W2, U, dY, act, with_bias=False):
+        out = L.mlp_bwd(X, W1, W2, U, dY, act, with_bias)
+        out["dW2"] = out["dW2"][::-1]  # rows in the wrong order
+        return out
+    bad = _mutant(mlp_bwd=mlp_bwd)
+    assert _fails(lambda: pins.check_fd_mlp(bad, "gelu"))
+
+
+def test_planted_gelu_tanh_form_instead_of_erf():
+    def gelu(u):
+        return 0.5 * u * (1 + np.tanh(np.sqrt(2 / np.pi) * (u + 0.044715 * u ** 3)))
+    bad = _mutant(gelu=gelu)
+    assert _fails(lambda: pins.check_textbook(bad))
+
+
+def test_planted_row_parallel_bias_added_to_every_partial():
+    def mlp_fwd(X, W1, b1, W2, act):
+        o = L.mlp_fwd(X, W1, b1, W2, act)
+        o["Z"] = o["Z"] + 0.05  # a bias folded into each partial sum
+        return o
+    bad = _mutant(mlp_fwd=mlp_fwd)
+    assert _fails(lambda: pins.check_tp_sum(bad, "gelu"))
