@@ -1,0 +1,60 @@
+// Internal launch interface of the bf16 MFMA GEMM family (gfx950).
+//
+// C[m][n] = sum_k A(m, k) * B(k, n), fp32 accumulation, fused epilogue. Operand storage:
+//   kFwd   : A(m,k) = A[m*lda + k]   B(k,n) = B[n*ldb + k]   (both read along k)
+//   kDgrad : A(m,k) = A[m*lda + k]   B(k,n) = B[k*ldb + n]
+//   kWgrad : A(m,k) = A[k*lda + m]   B(k,n) = B[k*ldb + n]
+// Requirements (checked by the caller): M, N, K >= 0; N, K multiples of 8; for kWgrad M a
+// multiple of 8; every operand below 4 GiB; 16-byte aligned pointers and leading dimensions that
+// are multiples of 8 elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace tps {
+
+enum GemmLayout : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
+
+enum GemmEpi : int {
+  kEpiBf16 = 0,    // C = bf16(acc + bias)                                     bias [N] or null
+  kEpiGelu = 1,    // U = acc + bias; aux_out = bf16(U) (if set); C = bf16(gelu(U))
+  kEpiSwiglu = 2,  // B rows n and half+n give G and V; aux_out[., n | half+n] = bf16(G | V)
+                   // (if set); C = bf16(silu(G) * V)
+  kEpiDgelu = 3,   // U = aux_in; C = bf16(acc * gelu'(U)); aux_out = bf16(gelu(U))
+  kEpiDswiglu = 4, // G, V = aux_in[., n], aux_in[., half+n]; C[., n] = bf16(acc V silu'(G)),
+                   // C[., half+n] = bf16(acc silu(G)); aux_out = bf16(silu(G) V)
+  kEpiF32 = 5      // C (fp32) = acc, or C + acc when accumulate (C loaded into the accumulator
+                   // before the k loop, so a run split along k reproduces the unsplit sums)
+};
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  const void* bias;
+  const void* aux_in;
+  void* aux_out;
+  int64_t lda, ldb, ldc, ld_in, ld_out;
+  int64_t half;        // column offset of the second half (SwiGLU epilogues)
+  int32_t M, N, K;     // N: output columns (SwiGLU: F')
+  int32_t accumulate;  // kEpiF32 only
+  // filled by launch_gemm
+  uint32_t a_bytes, b_bytes;
+  int32_t tiles_m, tiles_n;
+};
+
+// Queue one GEMM on `stream`. Returns hipSuccess or the launch error.
+hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream);
+
+constexpr int kColsumChunkRows = 256;
+
+// Column sums of a bf16 [M][N] matrix into fp32 out[N] (out += sums when accumulate), in a fixed
+// order: partial sums over 256-row chunks into `partials` ([ceil(M/256)][N] fp32), then the chunks
+// in ascending order.
+hipError_t launch_colsum(const void* X, int64_t ldx, int32_t M, int32_t N, float* partials, float* out,
+                         int32_t accumulate, hipStream_t stream);
+size_t colsum_partials_bytes(int32_t M, int32_t N);
+
+}  // namespace tps

@@ -1,0 +1,185 @@
+// Plan construction and validation (host only, no HIP calls): sizes of one rank's share and the
+// geometry of its independent pieces (Domino page, Abstract: one batch broken into independent
+// pieces). Rows: r equal contiguous token ranges. Columns: c equal ranges of the hand-off output.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "plan.hpp"
+
+namespace tps {
+
+static thread_local char g_last_error[512] = "";
+
+tpslice_status_t fail(tpslice_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+bool plan_ok(const tpslice_plan_s* p) { return p != nullptr && p->magic == kPlanMagic; }
+
+MlpFwdWs mlp_fwd_ws(const tpslice_plan_s* p) {
+  MlpFwdWs w{};
+  w.H = 0;
+  w.total = align_up(size_t(p->M) * size_t(p->Fp) * 2, kWsAlign);
+  return w;
+}
+
+static size_t partials_bytes(int64_t M, int64_t N) {
+  return size_t((M + kColsumRows - 1) / kColsumRows) * size_t(N) * sizeof(float);
+}
+
+MlpBwdWs mlp_bwd_ws(const tpslice_plan_s* p) {
+  MlpBwdWs w{};
+  w.dU = 0;
+  w.H = align_up(size_t(p->M) * size_t(p->N1) * 2, kWsAlign);
+  w.partials = w.H + align_up(size_t(p->M) * size_t(p->Fp) * 2, kWsAlign);
+  w.total = w.partials + align_up(partials_bytes(p->M, p->N1), kWsAlign);
+  return w;
+}
+
+AttnBwdWs attn_bwd_ws(const tpslice_plan_s* p) {
+  AttnBwdWs w{};
+  w.partials = 0;
+  w.total = align_up(partials_bytes(p->M, p->qkv), kWsAlign);
+  return w;
+}
+
+}  // namespace tps
+
+using namespace tps;
+
+static bool fits_4g(int64_t rows, int64_t cols, int64_t elem) {
+  // every operand is addressed through 32-bit buffer offsets
+  const double bytes = double(rows) * double(cols) * double(elem);
+  return rows >= 0 && cols >= 0 && bytes < 4294967296.0 - 4096.0;
+}
+
+extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t* out) {
+  clear_error();
+  if (!out) return fail(TPSLICE_ERR_INVALID, "tpslice_plan: out is NULL");
+  *out = nullptr;
+  if (!d) return fail(TPSLICE_ERR_INVALID, "tpslice_plan: desc is NULL");
+  if (d->act != TPSLICE_ACT_GELU && d->act != TPSLICE_ACT_SWIGLU)
+    return fail(TPSLICE_ERR_INVALID, "act %d is not TPSLICE_ACT_GELU or TPSLICE_ACT_SWIGLU", d->act);
+  if (d->flags & ~(TPSLICE_F_SERIALIZE | TPSLICE_F_COPY_BLIT))
+    return fail(TPSLICE_ERR_INVALID, "unknown flag bits 0x%x", d->flags);
+  if (d->tokens < 0) return fail(TPSLICE_ERR_SHAPE, "tokens %lld < 0", (long long)d->tokens);
+  if (d->hidden <= 0 || d->hidden % 8)
+    return fail(TPSLICE_ERR_SHAPE, "hidden %lld must be a positive multiple of 8", (long long)d->hidden);
+  if (d->tp_size < 1) return fail(TPSLICE_ERR_SHAPE, "tp_size %d < 1", d->tp_size);
+  if (d->ffn <= 0 || d->ffn % d->tp_size)
+    return fail(TPSLICE_ERR_SHAPE, "ffn %lld is not a positive multiple of tp_size %d", (long long)d->ffn,
+                d->tp_size);
+  const int64_t Fp = d->ffn / d->tp_size;
+  if (Fp % 8) return fail(TPSLICE_ERR_SHAPE, "ffn shard %lld is not a multiple of 8", (long long)Fp);
+  if (d->n_row_slices < 1 || d->n_col_slices < 1)
+    return fail(TPSLICE_ERR_SHAPE, "slice counts r=%d c=%d must be >= 1", d->n_row_slices, d->n_col_slices);
+  if (d->tokens % d->n_row_slices)
+    return fail(TPSLICE_ERR_SHAPE, "%d row slices do not divide %lld tokens evenly", d->n_row_slices,
+                (long long)d->tokens);
+  if (d->hidden % d->n_col_slices || (d->hidden / d->n_col_slices) % 8)
+    return fail(TPSLICE_ERR_SHAPE, "%d column slices of hidden %lld must be equal multiples of 8",
+                d->n_col_slices, (long long)d->hidden);
+  if (d->n_streams < 0 || d->n_streams > kMaxStreams)
+    return fail(TPSLICE_ERR_SHAPE, "n_streams %d outside [0, %d]", d->n_streams, kMaxStreams);
+  if (d->n_copy_streams < 0 || d->n_copy_streams > kMaxCopyStreams)
+    return fail(TPSLICE_ERR_SHAPE, "n_copy_streams %d outside [0, %d]", d->n_copy_streams, kMaxCopyStreams);
+  int32_t qh = 0, kvh = 0;
+  if (d->n_heads < 0 || d->n_kv_heads < 0 || d->head_dim < 0)
+    return fail(TPSLICE_ERR_SHAPE, "negative head counts");
+  if (d->n_heads > 0) {
+    if (d->head_dim <= 0 || d->head_dim % 8)
+      return fail(TPSLICE_ERR_SHAPE, "head_dim %d must be a positive multiple of 8", d->head_dim);
+    if (d->n_heads % d->tp_size)
+      return fail(TPSLICE_ERR_SHAPE, "%d heads do not split over tp_size %d", d->n_heads, d->tp_size);
+    if (d->n_kv_heads < 1 || d->n_kv_heads > d->n_heads)
+      return fail(TPSLICE_ERR_SHAPE, "n_kv_heads %d outside [1, n_heads]", d->n_kv_heads);
+    if (d->n_kv_heads >= d->tp_size && d->n_kv_heads % d->tp_size)
+      return fail(TPSLICE_ERR_SHAPE, "%d kv heads do not split over tp_size %d", d->n_kv_heads, d->tp_size);
+    qh = d->n_heads / d->tp_size;
+    kvh = d->n_kv_heads >= d->tp_size ? d->n_kv_heads / d->tp_size : 1;
+  }
+  const int64_t M = d->tokens, h = d->hidden;
+  const int64_t N1 = d->act == TPSLICE_ACT_SWIGLU ? 2 * Fp : Fp;
+  const int64_t qkv = int64_t(qh + 2 * kvh) * d->head_dim, ctx = int64_t(qh) * d->head_dim;
+  if (!fits_4g(M, h, 2) || !fits_4g(M, N1, 2) || !fits_4g(N1, h, 2) || !fits_4g(h, Fp, 2) ||
+      !fits_4g(M, qkv, 2) || !fits_4g(qkv, h, 2) || !fits_4g(M, ctx, 2) || !fits_4g(h, ctx, 2))
+    return fail(TPSLICE_ERR_SHAPE, "an operand exceeds 4 GiB");
+
+  tpslice_plan_s* p = new (std::nothrow) tpslice_plan_s();
+  if (!p) return fail(TPSLICE_ERR_INVALID, "out of host memory");
+  p->magic = kPlanMagic;
+  p->desc = *d;
+  p->M = M; p->h = h; p->Fp = Fp; p->N1 = N1; p->qkv = qkv; p->ctx = ctx;
+  p->r = d->n_row_slices; p->c = d->n_col_slices;
+  p->Ms = M / p->r; p->hc = h / p->c;
+  const bool serial = d->flags & TPSLICE_F_SERIALIZE;
+  p->S = serial ? 1 : (d->n_streams ? d->n_streams : (p->r < 2 ? p->r : 2));
+  p->E = serial ? 1 : (d->n_copy_streams ? d->n_copy_streams : 4);
+  p->qh = qh; p->kvh = kvh;
+  p->trace = 0;
+  p->rt = nullptr;
+  *out = p;
+  return TPSLICE_OK;
+}
+
+extern "C" tpslice_status_t tpslice_plan_info(tpslice_plan_t p, tpslice_plan_info_t* info) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (!info) return fail(TPSLICE_ERR_INVALID, "info is NULL");
+  info->tokens = p->M; info->hidden = p->h; info->ffn_shard = p->Fp; info->n1 = p->N1;
+  info->qkv_width = p->qkv; info->ctx_width = p->ctx;
+  info->rows_per_slice = p->Ms; info->handoff_cols = p->hc;
+  info->n_row_slices = p->r; info->n_col_slices = p->c;
+  info->n_streams = p->S; info->n_copy_streams = p->E;
+  info->q_heads = p->qh; info->kv_heads = p->kvh;
+  return TPSLICE_OK;
+}
+
+extern "C" tpslice_status_t tpslice_plan_piece(tpslice_plan_t p, int32_t index, int64_t out[4]) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (!out) return fail(TPSLICE_ERR_INVALID, "out is NULL");
+  if (index < 0 || index >= p->r * p->c)
+    return fail(TPSLICE_ERR_INVALID, "piece %d outside [0, %d)", index, p->r * p->c);
+  const int32_t i = index / p->c, j = index % p->c;
+  out[0] = int64_t(i) * p->Ms;
+  out[1] = int64_t(i + 1) * p->Ms;
+  out[2] = int64_t(j) * p->hc;
+  out[3] = int64_t(j + 1) * p->hc;
+  return TPSLICE_OK;
+}
+
+extern "C" tpslice_status_t tpslice_workspace_size(tpslice_plan_t p, int32_t op, size_t* bytes) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (!bytes) return fail(TPSLICE_ERR_INVALID, "bytes is NULL");
+  switch (op) {
+    case TPSLICE_OP_MLP_FWD: *bytes = mlp_fwd_ws(p).total; return TPSLICE_OK;
+    case TPSLICE_OP_MLP_BWD: *bytes = mlp_bwd_ws(p).total; return TPSLICE_OK;
+    case TPSLICE_OP_ATTNPROJ_FWD: *bytes = 0; return TPSLICE_OK;
+    case TPSLICE_OP_ATTNPROJ_BWD: *bytes = attn_bwd_ws(p).total; return TPSLICE_OK;
+    default: return fail(TPSLICE_ERR_INVALID, "unknown op %d", op);
+  }
+}
+
+extern "C" const char* tpslice_error_string(tpslice_status_t s) {
+  switch (s) {
+    case TPSLICE_OK: return "ok";
+    case TPSLICE_ERR_INVALID: return "invalid argument";
+    case TPSLICE_ERR_SHAPE: return "unsupported shape";
+    case TPSLICE_ERR_UNSUPPORTED: return "unsupported request";
+    case TPSLICE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case TPSLICE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* tpslice_last_error(void) { return tps::g_last_error; }

@@ -1,0 +1,45 @@
+// Host-side plan of the sliced layer shard: validated sizes and slice geometry. No HIP calls here.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "tpslice.h"
+
+struct tpslice_plan_s {
+  uint32_t magic;
+  tpslice_desc_t desc;
+  int64_t M, h, Fp, N1, qkv, ctx;  // tokens, hidden, F', up-projection width, QKV width, context width
+  int64_t Ms, hc;                  // rows per row slice, hand-off columns per column slice
+  int32_t r, c, S, E;              // row slices, column slices, worker streams, copy streams
+  int32_t qh, kvh;                 // this rank's query / key-value heads
+  int32_t trace;                   // tracing enabled
+  void* rt;                        // device resources (streams, events), created on first execution
+};
+
+namespace tps {
+
+constexpr uint32_t kPlanMagic = 0x74707331u;
+constexpr uint32_t kDeadMagic = 0xdeadbeefu;
+constexpr size_t kWsAlign = 256;
+constexpr int kMaxStreams = 8;
+constexpr int kMaxCopyStreams = 8;
+
+// Record `fmt` as the calling thread's last error and return `st`.
+tpslice_status_t fail(tpslice_status_t st, const char* fmt, ...);
+void clear_error();
+bool plan_ok(const tpslice_plan_s* p);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace regions (byte offsets) of each operation. Bias gradients are column sums reduced in
+// a fixed order through per-chunk partial sums (chunks of kColsumRows token rows, fp32).
+constexpr int64_t kColsumRows = 256;
+struct MlpFwdWs { size_t H, total; };
+struct MlpBwdWs { size_t dU, H, partials, total; };
+struct AttnBwdWs { size_t partials, total; };
+MlpFwdWs mlp_fwd_ws(const tpslice_plan_s* p);
+MlpBwdWs mlp_bwd_ws(const tpslice_plan_s* p);
+AttnBwdWs attn_bwd_ws(const tpslice_plan_s* p);
+
+}  // namespace tps

@@ -1,0 +1,506 @@
+// Slice scheduler and C-ABI entry points of the sliced layer shard.
+//
+// Every call forks from the caller's stream onto the plan's worker streams, runs row slice i on
+// worker i mod S (its products in order), records an event after each finished hand-off piece and
+// lets a copy stream wait on that event and move the piece with a DMA-engine copy while the
+// workers go on computing - the single-GPU stand-in for handing the piece to the tensor-parallel
+// reduction (Domino page, Abstract: independent pieces whose communication overlaps later
+// computation; FiCCO page, Abstract: communication offloaded to the GPU's DMA engines; DHelix
+// review, Referee report: separate computation and communication streams joined by barriers).
+// At the end the caller's stream waits on every worker and copy stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "gemm.hpp"
+#include "plan.hpp"
+
+namespace tps {
+static_assert(kColsumChunkRows == kColsumRows, "workspace sizing and the column-sum kernel disagree");
+namespace {
+
+struct TraceSlot {
+  tpslice_trace_rec_t rec;
+  size_t ev0, ev1;  // indices into Runtime::tpool
+};
+
+struct Runtime {
+  int device = -1;
+  std::vector<hipStream_t> workers, copiers;
+  hipEvent_t fork = nullptr;
+  std::vector<hipEvent_t> piece;   // one per hand-off piece (and reused per call)
+  std::vector<hipEvent_t> slice;   // one per row slice: its products are done
+  std::vector<hipEvent_t> join_w, join_c;
+  // tracing: timing events, recorded around each product / copy of the latest call
+  hipEvent_t t0 = nullptr;
+  bool window_open = false;
+  int32_t calls = 0;
+  std::vector<hipEvent_t> tpool;
+  size_t tused = 0;
+  std::vector<TraceSlot> slots;
+};
+
+#define TPS_TRY_(x)                    \
+  do {                                 \
+    tpslice_status_t st_ = (x);        \
+    if (st_ != TPSLICE_OK) return st_; \
+  } while (0)
+
+#define TPS_HIP(call)                                                                          \
+  do {                                                                                         \
+    hipError_t e_ = (call);                                                                    \
+    if (e_ != hipSuccess) return fail(TPSLICE_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+void destroy_runtime(Runtime* rt) {
+  if (!rt) return;
+  for (auto s : rt->workers) (void)hipStreamDestroy(s);
+  for (auto s : rt->copiers) (void)hipStreamDestroy(s);
+  if (rt->fork) (void)hipEventDestroy(rt->fork);
+  for (auto e : rt->piece) (void)hipEventDestroy(e);
+  for (auto e : rt->slice) (void)hipEventDestroy(e);
+  for (auto e : rt->join_w) (void)hipEventDestroy(e);
+  for (auto e : rt->join_c) (void)hipEventDestroy(e);
+  if (rt->t0) (void)hipEventDestroy(rt->t0);
+  for (auto e : rt->tpool) (void)hipEventDestroy(e);
+  delete rt;
+}
+
+tpslice_status_t make_event(hipEvent_t* e) {
+  TPS_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
+  return TPSLICE_OK;
+}
+
+// Streams and events are created on first use, on the device current at that time.
+tpslice_status_t ensure_runtime(tpslice_plan_s* p, Runtime** out) {
+  int dev = -1;
+  TPS_HIP(hipGetDevice(&dev));
+  Runtime* rt = static_cast<Runtime*>(p->rt);
+  if (rt) {
+    if (rt->device != dev)
+      return fail(TPSLICE_ERR_UNSUPPORTED, "plan was first used on device %d, now device %d", rt->device, dev);
+    *out = rt;
+    return TPSLICE_OK;
+  }
+  rt = new (std::nothrow) Runtime();
+  if (!rt) return fail(TPSLICE_ERR_INVALID, "out of host memory");
+  rt->device = dev;
+  p->rt = rt;  // owned by the plan from here on, also on partial failure
+  const bool serial = p->desc.flags & TPSLICE_F_SERIALIZE;
+  if (!serial) {
+    for (int i = 0; i < p->S; ++i) {
+      hipStream_t s;
+      TPS_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));  // default priority
+      rt->workers.push_back(s);
+    }
+    for (int i = 0; i < p->E; ++i) {
+      hipStream_t s;
+      TPS_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+      rt->copiers.push_back(s);
+    }
+    tpslice_status_t st = make_event(&rt->fork);
+    if (st) return st;
+    rt->join_w.resize(p->S);
+    rt->join_c.resize(p->E);
+    for (auto& e : rt->join_w) if ((st = make_event(&e))) return st;
+    for (auto& e : rt->join_c) if ((st = make_event(&e))) return st;
+    rt->piece.resize(size_t(p->r) * p->c);
+    rt->slice.resize(p->r);
+    for (auto& e : rt->piece) if ((st = make_event(&e))) return st;
+    for (auto& e : rt->slice) if ((st = make_event(&e))) return st;
+  }
+  *out = rt;
+  return TPSLICE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// One call's stream bookkeeping.
+struct Schedule {
+  tpslice_plan_s* p;
+  Runtime* rt;
+  hipStream_t caller;
+  bool serial;
+
+  hipStream_t worker(int i) const { return serial ? caller : rt->workers[i % p->S]; }
+  int worker_id(int i) const { return serial ? -1 : i % p->S; }
+
+  tpslice_status_t trace_event(size_t* idx) {
+    if (rt->tused == rt->tpool.size()) {
+      hipEvent_t e;
+      TPS_HIP(hipEventCreate(&e));
+      rt->tpool.push_back(e);
+    }
+    *idx = rt->tused++;
+    return TPSLICE_OK;
+  }
+
+  // Run `fn` (which queues work on `s`) between two timing events when tracing.
+  template <class F>
+  tpslice_status_t traced(hipStream_t s, int stream_id, int kind, int step, int slice, int piece, double flops,
+                          double bytes, F&& fn) {
+    if (!p->trace) return fn();
+    TraceSlot t{};
+    t.rec.kind = kind; t.rec.step = step; t.rec.slice = slice; t.rec.piece = piece;
+    t.rec.stream = stream_id; t.rec.flops = flops; t.rec.bytes = bytes; t.rec.call = rt->calls - 1;
+    TPS_TRY_(trace_event(&t.ev0));
+    TPS_HIP(hipEventRecord(rt->tpool[t.ev0], s));
+    TPS_TRY_(fn());
+    TPS_TRY_(trace_event(&t.ev1));
+    TPS_HIP(hipEventRecord(rt->tpool[t.ev1], s));
+    rt->slots.push_back(t);
+    return TPSLICE_OK;
+  }
+
+  tpslice_status_t fork() {
+    if (p->trace) {
+      if (!rt->window_open) {
+        if (!rt->t0) TPS_HIP(hipEventCreate(&rt->t0));
+        TPS_HIP(hipEventRecord(rt->t0, caller));
+        rt->window_open = true;
+        rt->calls = 0;
+      }
+      ++rt->calls;
+    }
+    if (serial) return TPSLICE_OK;
+    TPS_HIP(hipEventRecord(rt->fork, caller));
+    for (auto s : rt->workers) TPS_HIP(hipStreamWaitEvent(s, rt->fork, 0));
+    for (auto s : rt->copiers) TPS_HIP(hipStreamWaitEvent(s, rt->fork, 0));
+    return TPSLICE_OK;
+  }
+
+  tpslice_status_t join() {
+    if (serial) return TPSLICE_OK;
+    for (int k = 0; k < p->S; ++k) {
+      TPS_HIP(hipEventRecord(rt->join_w[k], rt->workers[k]));
+      TPS_HIP(hipStreamWaitEvent(caller, rt->join_w[k], 0));
+    }
+    for (int k = 0; k < p->E; ++k) {
+      TPS_HIP(hipEventRecord(rt->join_c[k], rt->copiers[k]));
+      TPS_HIP(hipStreamWaitEvent(caller, rt->join_c[k], 0));
+    }
+    return TPSLICE_OK;
+  }
+
+  // Hand-off of piece (i, j) of a [M][h] bf16 tensor produced on worker(i).
+  tpslice_status_t handoff(int i, int j, const void* src, void* dst) {
+    const int64_t row0 = int64_t(i) * p->Ms, col0 = int64_t(j) * p->hc;
+    const size_t pitch = size_t(p->h) * 2;
+    const char* s = static_cast<const char*>(src) + row0 * pitch + col0 * 2;
+    char* d = static_cast<char*>(dst) + row0 * pitch + col0 * 2;
+    const hipMemcpyKind kind =
+        (p->desc.flags & TPSLICE_F_COPY_BLIT) ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
+    const double piece_bytes = double(p->Ms) * double(p->hc) * 2.0;
+    if (serial) {
+      return traced(caller, -1, TPSLICE_TRACE_COPY, TPSLICE_STEP_HANDOFF, i, j, 0.0, piece_bytes, [&] {
+        if (p->c == 1) TPS_HIP(hipMemcpyAsync(d, s, size_t(p->Ms) * pitch, kind, caller));
+        else TPS_HIP(hipMemcpy2DAsync(d, pitch, s, pitch, size_t(p->hc) * 2, size_t(p->Ms), kind, caller));
+        return TPSLICE_OK;
+      });
+    }
+    hipEvent_t ev = rt->piece[size_t(i) * p->c + j];
+    TPS_HIP(hipEventRecord(ev, worker(i)));
+    if (p->c == 1) {
+      // a whole-row piece is contiguous: spread it over the copy streams in equal row chunks
+      const int64_t E = p->E;
+      for (int64_t k = 0; k < E; ++k) {
+        const int64_t r0 = p->Ms * k / E, r1 = p->Ms * (k + 1) / E;
+        if (r1 <= r0) continue;
+        hipStream_t cs = rt->copiers[k];
+        TPS_HIP(hipStreamWaitEvent(cs, ev, 0));
+        const size_t nbytes = size_t(r1 - r0) * pitch;
+        TPS_TRY_(traced(cs, p->S + int(k), TPSLICE_TRACE_COPY, TPSLICE_STEP_HANDOFF, i, j, 0.0, double(nbytes), [&] {
+          TPS_HIP(hipMemcpyAsync(d + r0 * pitch, s + r0 * pitch, nbytes, kind, cs));
+          return TPSLICE_OK;
+        }));
+      }
+    } else {
+      const int k = int((size_t(i) * p->c + j) % p->E);
+      hipStream_t cs = rt->copiers[k];
+      TPS_HIP(hipStreamWaitEvent(cs, ev, 0));
+      TPS_TRY_(traced(cs, p->S + k, TPSLICE_TRACE_COPY, TPSLICE_STEP_HANDOFF, i, j, 0.0, piece_bytes, [&] {
+        TPS_HIP(hipMemcpy2DAsync(d, pitch, s, pitch, size_t(p->hc) * 2, size_t(p->Ms), kind, cs));
+        return TPSLICE_OK;
+      }));
+    }
+    return TPSLICE_OK;
+  }
+
+  // Queue one product on worker(i) (i = -1: worker 0, all tokens), traced as `step`.
+  tpslice_status_t product(int i, int step, int piece, const GemmArgs& g, int layout, int epi) {
+    const int wi = i < 0 ? 0 : i;
+    const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
+    return traced(worker(wi), worker_id(wi), TPSLICE_TRACE_GEMM, step, i, piece, flops, 0.0, [&] {
+      hipError_t e = launch_gemm(g, layout, epi, worker(wi));
+      if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
+      return TPSLICE_OK;
+    });
+  }
+
+  tpslice_status_t colsum(const void* X, int64_t ld, int64_t M, int64_t N, float* partials, float* out,
+                          int accumulate) {
+    return traced(worker(0), worker_id(0), TPSLICE_TRACE_COLSUM, TPSLICE_STEP_BIAS_GRAD, -1, -1, 0.0,
+                  double(M) * double(N) * 2.0, [&] {
+      hipError_t e = launch_colsum(X, ld, int32_t(M), int32_t(N), partials, out, accumulate, worker(0));
+      if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "column-sum launch: %s", hipGetErrorString(e));
+      return TPSLICE_OK;
+    });
+  }
+
+  // Make worker(0) wait until every row slice's products are finished.
+  tpslice_status_t gather_slices() {
+    if (serial) return TPSLICE_OK;
+    hipStream_t w0 = worker(0);
+    for (int i = 0; i < p->r; ++i) {
+      if (worker(i) == w0) continue;
+      TPS_HIP(hipEventRecord(rt->slice[i], worker(i)));
+      TPS_HIP(hipStreamWaitEvent(w0, rt->slice[i], 0));
+    }
+    return TPSLICE_OK;
+  }
+};
+
+GemmArgs args(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int64_t M,
+              int64_t N, int64_t K) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
+  g.M = int32_t(M); g.N = int32_t(N); g.K = int32_t(K);
+  return g;
+}
+
+const char* bf(const void* p, int64_t elems) { return static_cast<const char*>(p) + elems * 2; }
+char* bfw(void* p, int64_t elems) { return static_cast<char*>(p) + elems * 2; }
+
+tpslice_status_t check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return TPSLICE_OK;
+  if (!ws) return fail(TPSLICE_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+  if (reinterpret_cast<uintptr_t>(ws) % kWsAlign)
+    return fail(TPSLICE_ERR_WORKSPACE, "workspace is not %zu-byte aligned", kWsAlign);
+  if (have < need) return fail(TPSLICE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return TPSLICE_OK;
+}
+
+#define TPS_REQ(ptr)                                                                  \
+  do {                                                                                \
+    if (!(ptr)) return fail(TPSLICE_ERR_INVALID, "%s is NULL", #ptr);                 \
+    if (!aligned16(ptr)) return fail(TPSLICE_ERR_INVALID, "%s is not 16-byte aligned", #ptr); \
+  } while (0)
+#define TPS_OPT(ptr)                                                                  \
+  do {                                                                                \
+    if ((ptr) && !aligned16(ptr)) return fail(TPSLICE_ERR_INVALID, "%s is not 16-byte aligned", #ptr); \
+  } while (0)
+#define TPS_TRY(x)                       \
+  do {                                           \
+    tpslice_status_t st_ = (x);                  \
+    if (st_ != TPSLICE_OK) return st_;           \
+  } while (0)
+
+}  // namespace
+}  // namespace tps
+
+using namespace tps;
+
+extern "C" tpslice_status_t tpslice_plan_destroy(tpslice_plan_t p) {
+  clear_error();
+  if (!p) return TPSLICE_OK;
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  destroy_runtime(static_cast<Runtime*>(p->rt));
+  p->rt = nullptr;
+  p->magic = kDeadMagic;
+  delete p;
+  return TPSLICE_OK;
+}
+
+extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, const void* W1, const void* b1,
+                                            const void* W2, void* Z, void* U_save, void* Z_handoff, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  TPS_REQ(X); TPS_REQ(W1); TPS_REQ(W2); TPS_REQ(Z);
+  TPS_OPT(b1); TPS_OPT(U_save); TPS_OPT(Z_handoff);
+  const MlpFwdWs L = mlp_fwd_ws(p);
+  TPS_TRY(check_ws(ws, ws_bytes, L.total));
+  if (p->M == 0) return TPSLICE_OK;
+  Runtime* rt = nullptr;
+  TPS_TRY(ensure_runtime(p, &rt));
+  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  char* H = static_cast<char*>(ws) + L.H;
+  const int epi = p->desc.act == TPSLICE_ACT_GELU ? kEpiGelu : kEpiSwiglu;
+  TPS_TRY(S.fork());
+  for (int i = 0; i < p->r; ++i) {
+    const int64_t r0 = int64_t(i) * p->Ms;
+    GemmArgs g1 = args(bf(X, r0 * p->h), p->h, W1, p->h, bfw(H, r0 * p->Fp), p->Fp, p->Ms, p->Fp, p->h);
+    g1.bias = b1;
+    g1.half = p->Fp;
+    if (U_save) { g1.aux_out = bfw(U_save, r0 * p->N1); g1.ld_out = p->N1; }
+    TPS_TRY(S.product(i, TPSLICE_STEP_MLP_UP, -1, g1, kFwd, epi));
+    for (int j = 0; j < p->c; ++j) {
+      const int64_t c0 = int64_t(j) * p->hc;
+      GemmArgs g2 = args(bf(H, r0 * p->Fp), p->Fp, bf(W2, c0 * p->Fp), p->Fp, bfw(Z, r0 * p->h + c0), p->h,
+                         p->Ms, p->hc, p->Fp);
+      TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DOWN, j, g2, kFwd, kEpiBf16));
+      if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
+    }
+  }
+  return S.join();
+}
+
+extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X, const void* Wqkv,
+                                                 const void* bqkv, void* QKV, const void* C, const void* Wo,
+                                                 void* Z, void* Z_handoff, void* ws, size_t ws_bytes,
+                                                 void* stream) {
+  clear_error();
+  (void)ws; (void)ws_bytes;
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (p->qh == 0) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads (n_heads = 0)");
+  TPS_REQ(X); TPS_REQ(Wqkv); TPS_REQ(QKV); TPS_REQ(C); TPS_REQ(Wo); TPS_REQ(Z);
+  TPS_OPT(bqkv); TPS_OPT(Z_handoff);
+  if (p->M == 0) return TPSLICE_OK;
+  Runtime* rt = nullptr;
+  TPS_TRY(ensure_runtime(p, &rt));
+  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  TPS_TRY(S.fork());
+  for (int i = 0; i < p->r; ++i) {
+    const int64_t r0 = int64_t(i) * p->Ms;
+    // output projection first: its pieces are the hand-off, the QKV product then runs under the copies
+    for (int j = 0; j < p->c; ++j) {
+      const int64_t c0 = int64_t(j) * p->hc;
+      GemmArgs g = args(bf(C, r0 * p->ctx), p->ctx, bf(Wo, c0 * p->ctx), p->ctx, bfw(Z, r0 * p->h + c0), p->h,
+                        p->Ms, p->hc, p->ctx);
+      TPS_TRY(S.product(i, TPSLICE_STEP_OUT, j, g, kFwd, kEpiBf16));
+      if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
+    }
+    GemmArgs q = args(bf(X, r0 * p->h), p->h, Wqkv, p->h, bfw(QKV, r0 * p->qkv), p->qkv, p->Ms, p->qkv, p->h);
+    q.bias = bqkv;
+    TPS_TRY(S.product(i, TPSLICE_STEP_QKV, -1, q, kFwd, kEpiBf16));
+  }
+  return S.join();
+}
+
+extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, const void* W1, const void* W2,
+                                            const void* U, const void* dY, void* dX, void* dX_handoff,
+                                            float* dW1, float* db1, float* dW2, int32_t accumulate, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  TPS_REQ(X); TPS_REQ(W1); TPS_REQ(W2); TPS_REQ(U); TPS_REQ(dY); TPS_REQ(dX); TPS_REQ(dW1); TPS_REQ(dW2);
+  TPS_OPT(db1); TPS_OPT(dX_handoff);
+  if (accumulate != 0 && accumulate != 1) return fail(TPSLICE_ERR_INVALID, "accumulate must be 0 or 1");
+  const MlpBwdWs L = mlp_bwd_ws(p);
+  TPS_TRY(check_ws(ws, ws_bytes, L.total));
+  Runtime* rt = nullptr;
+  TPS_TRY(ensure_runtime(p, &rt));
+  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  char* dU = static_cast<char*>(ws) + L.dU;
+  char* H = static_cast<char*>(ws) + L.H;
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
+  const bool glu = p->desc.act == TPSLICE_ACT_SWIGLU;
+  TPS_TRY(S.fork());
+  for (int i = 0; i < p->r && p->M > 0; ++i) {
+    const int64_t r0 = int64_t(i) * p->Ms;
+    // dH = dY W2 with the activation's derivative fused: writes dU and (recomputed) H
+    GemmArgs g = args(bf(dY, r0 * p->h), p->h, W2, p->Fp, bfw(dU, r0 * p->N1), p->N1, p->Ms, p->Fp, p->h);
+    g.aux_in = bf(U, r0 * p->N1); g.ld_in = p->N1;
+    g.aux_out = bfw(H, r0 * p->Fp); g.ld_out = p->Fp;
+    g.half = p->Fp;
+    TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DH, -1, g, kDgrad, glu ? kEpiDswiglu : kEpiDgelu));
+    for (int j = 0; j < p->c; ++j) {
+      const int64_t c0 = int64_t(j) * p->hc;
+      GemmArgs gx = args(bf(dU, r0 * p->N1), p->N1, bf(W1, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms, p->hc,
+                         p->N1);
+      TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DX, j, gx, kDgrad, kEpiBf16));
+      if (dX_handoff) TPS_TRY(S.handoff(i, j, dX, dX_handoff));
+    }
+  }
+  // weight gradients over all tokens at once (one k run, no split of the token sum), under the
+  // last pieces' copies
+  TPS_TRY(S.gather_slices());
+  GemmArgs g1 = args(dU, p->N1, X, p->h, dW1, p->h, p->N1, p->h, p->M);
+  g1.accumulate = accumulate;
+  TPS_TRY(S.product(-1, TPSLICE_STEP_MLP_DW1, -1, g1, kWgrad, kEpiF32));
+  GemmArgs g2 = args(dY, p->h, H, p->Fp, dW2, p->Fp, p->h, p->Fp, p->M);
+  g2.accumulate = accumulate;
+  TPS_TRY(S.product(-1, TPSLICE_STEP_MLP_DW2, -1, g2, kWgrad, kEpiF32));
+  if (db1) TPS_TRY(S.colsum(dU, p->N1, p->M, p->N1, partials, db1, accumulate));
+  return S.join();
+}
+
+extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X, const void* Wqkv,
+                                                 const void* dQKV, const void* C, const void* Wo, const void* dY,
+                                                 void* dX, void* dX_handoff, void* dC, float* dWqkv,
+                                                 float* dbqkv, float* dWo, int32_t accumulate, void* ws,
+                                                 size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (p->qh == 0) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads (n_heads = 0)");
+  TPS_REQ(X); TPS_REQ(Wqkv); TPS_REQ(dQKV); TPS_REQ(C); TPS_REQ(Wo); TPS_REQ(dY); TPS_REQ(dX); TPS_REQ(dC);
+  TPS_REQ(dWqkv); TPS_REQ(dWo);
+  TPS_OPT(dbqkv); TPS_OPT(dX_handoff);
+  if (accumulate != 0 && accumulate != 1) return fail(TPSLICE_ERR_INVALID, "accumulate must be 0 or 1");
+  const AttnBwdWs L = attn_bwd_ws(p);
+  TPS_TRY(check_ws(ws, ws_bytes, L.total));
+  Runtime* rt = nullptr;
+  TPS_TRY(ensure_runtime(p, &rt));
+  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
+  TPS_TRY(S.fork());
+  for (int i = 0; i < p->r && p->M > 0; ++i) {
+    const int64_t r0 = int64_t(i) * p->Ms;
+    for (int j = 0; j < p->c; ++j) {
+      const int64_t c0 = int64_t(j) * p->hc;
+      GemmArgs gx = args(bf(dQKV, r0 * p->qkv), p->qkv, bf(Wqkv, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms,
+                         p->hc, p->qkv);
+      TPS_TRY(S.product(i, TPSLICE_STEP_ATTN_DX, j, gx, kDgrad, kEpiBf16));
+      if (dX_handoff) TPS_TRY(S.handoff(i, j, dX, dX_handoff));
+    }
+    GemmArgs gc = args(bf(dY, r0 * p->h), p->h, Wo, p->ctx, bfw(dC, r0 * p->ctx), p->ctx, p->Ms, p->ctx, p->h);
+    TPS_TRY(S.product(i, TPSLICE_STEP_ATTN_DC, -1, gc, kDgrad, kEpiBf16));
+  }
+  TPS_TRY(S.gather_slices());
+  GemmArgs go = args(dY, p->h, C, p->ctx, dWo, p->ctx, p->h, p->ctx, p->M);
+  go.accumulate = accumulate;
+  TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DWO, -1, go, kWgrad, kEpiF32));
+  GemmArgs gq = args(dQKV, p->qkv, X, p->h, dWqkv, p->h, p->qkv, p->h, p->M);
+  gq.accumulate = accumulate;
+  TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DWQKV, -1, gq, kWgrad, kEpiF32));
+  if (dbqkv) TPS_TRY(S.colsum(dQKV, p->qkv, p->M, p->qkv, partials, dbqkv, accumulate));
+  return S.join();
+}
+
+extern "C" tpslice_status_t tpslice_trace_enable(tpslice_plan_t p, int32_t enable) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  p->trace = enable ? 1 : 0;
+  return TPSLICE_OK;
+}
+
+extern "C" tpslice_status_t tpslice_trace_read(tpslice_plan_t p, tpslice_trace_rec_t* recs, int32_t cap,
+                                               int32_t* count) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (!count || (cap > 0 && !recs)) return fail(TPSLICE_ERR_INVALID, "recs/count is NULL");
+  if (!p->trace) return fail(TPSLICE_ERR_INVALID, "tracing is not enabled on this plan");
+  Runtime* rt = static_cast<Runtime*>(p->rt);
+  *count = 0;
+  if (!rt || !rt->window_open) return TPSLICE_OK;
+  *count = int32_t(rt->slots.size());
+  if (cap < *count) return TPSLICE_OK;
+  for (size_t k = 0; k < rt->slots.size(); ++k) {
+    TraceSlot& t = rt->slots[k];
+    TPS_HIP(hipEventSynchronize(rt->tpool[t.ev1]));
+    float a = 0.f, b = 0.f;
+    TPS_HIP(hipEventElapsedTime(&a, rt->t0, rt->tpool[t.ev0]));
+    TPS_HIP(hipEventElapsedTime(&b, rt->t0, rt->tpool[t.ev1]));
+    t.rec.start_ms = a;
+    t.rec.end_ms = b;
+    recs[k] = t.rec;
+  }
+  rt->slots.clear();
+  rt->tused = 0;
+  rt->window_open = false;
+  return TPSLICE_OK;
+}

@@ -1,0 +1,285 @@
+"""Python binding of libtpslice.so: argument marshalling only.
+
+Every function here passes raw device pointers (`tensor.data_ptr()`) and the caller's HIP stream
+(`torch.cuda.Stream.cuda_stream`) to the C ABI declared in include/tpslice.h; all arithmetic runs in
+the library's HIP kernels. PyTorch provides device memory and streams. Importing this module fails
+loudly if the library has not been built; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpslice.so")
+
+OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
+ACT_GELU, ACT_SWIGLU = 1, 2
+F_SERIALIZE, F_COPY_BLIT = 0x1, 0x2
+OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD = range(4)
+EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice_plan_piece",
+           "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",
+           "tpslice_attnproj_bwd", "tpslice_trace_enable", "tpslice_trace_read",
+           "tpslice_error_string", "tpslice_last_error")
+TRACE_GEMM, TRACE_COPY, TRACE_COLSUM = range(3)
+STEPS = ("mlp_up", "mlp_down", "qkv", "out", "mlp_dh", "mlp_dx", "mlp_dw1", "mlp_dw2", "attn_dx", "attn_dc",
+         "attn_dwqkv", "attn_dwo", "bias_grad", "handoff")
+
+
+class TpsliceError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"tpslice error {code}: {msg}")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("ffn", ctypes.c_int64),
+                ("tp_size", ctypes.c_int32), ("n_row_slices", ctypes.c_int32),
+                ("n_col_slices", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("n_streams", ctypes.c_int32), ("n_copy_streams", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("ffn_shard", ctypes.c_int64),
+                ("n1", ctypes.c_int64), ("qkv_width", ctypes.c_int64), ("ctx_width", ctypes.c_int64),
+                ("rows_per_slice", ctypes.c_int64), ("handoff_cols", ctypes.c_int64),
+                ("n_row_slices", ctypes.c_int32), ("n_col_slices", ctypes.c_int32),
+                ("n_streams", ctypes.c_int32), ("n_copy_streams", ctypes.c_int32),
+                ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
+
+
+class TraceRec(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("step", ctypes.c_int32), ("slice", ctypes.c_int32),
+                ("piece", ctypes.c_int32), ("stream", ctypes.c_int32), ("call", ctypes.c_int32),
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double), ("start_ms", ctypes.c_float),
+                ("end_ms", ctypes.c_float)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m comm_overlap_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int
+    lib.tpslice_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(vp)]
+    lib.tpslice_plan_destroy.argtypes = [vp]
+    lib.tpslice_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    lib.tpslice_plan_piece.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int64)]
+    lib.tpslice_workspace_size.argtypes = [vp, i32, ctypes.POINTER(sz)]
+    lib.tpslice_mlp_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tpslice_attnproj_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tpslice_mlp_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.tpslice_attnproj_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.tpslice_trace_enable.argtypes = [vp, i32]
+    lib.tpslice_trace_read.argtypes = [vp, ctypes.POINTER(TraceRec), i32, ctypes.POINTER(i32)]
+    for name in EXPORTS[:11]:
+        getattr(lib, name).restype = st
+    lib.tpslice_error_string.argtypes = [st]
+    lib.tpslice_error_string.restype = ctypes.c_char_p
+    lib.tpslice_last_error.argtypes = []
+    lib.tpslice_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _check(code: int):
+    if code != OK:
+        raise TpsliceError(code, lib.tpslice_last_error().decode() or lib.tpslice_error_string(code).decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=torch.bfloat16, name: str = "tensor"):
+    """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> Optional[ctypes.c_void_p]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape(t: Optional[torch.Tensor], shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+@dataclass
+class Config:
+    tokens: int
+    hidden: int
+    ffn: int
+    tp_size: int = 1
+    n_row_slices: int = 1
+    n_col_slices: int = 1
+    n_heads: int = 0
+    n_kv_heads: int = 0
+    head_dim: int = 0
+    act: str = "gelu"
+    n_streams: int = 0
+    n_copy_streams: int = 0
+    serialize: bool = False
+    copy_blit: bool = False
+
+    def desc(self) -> Desc:
+        return Desc(self.tokens, self.hidden, self.ffn, self.tp_size, self.n_row_slices, self.n_col_slices,
+                    self.n_heads, self.n_kv_heads, self.head_dim,
+                    {"gelu": ACT_GELU, "swiglu": ACT_SWIGLU}.get(self.act, 0), self.n_streams,
+                    self.n_copy_streams,
+                    (F_SERIALIZE if self.serialize else 0) | (F_COPY_BLIT if self.copy_blit else 0))
+
+
+class Plan:
+    """A validated plan (host memory; streams and events are made on first use)."""
+
+    def __init__(self, cfg: Config):
+        self.cfg = cfg
+        h = ctypes.c_void_p()
+        d = cfg.desc()
+        _check(lib.tpslice_plan(ctypes.byref(d), ctypes.byref(h)))
+        self._h = h
+        info = PlanInfo()
+        _check(lib.tpslice_plan_info(self._h, ctypes.byref(info)))
+        self.info = info
+        self._ws = {}
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(lib.tpslice_plan_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def trace(self, enable: bool = True):
+        _check(lib.tpslice_trace_enable(self._h, int(bool(enable))))
+
+    def trace_read(self):
+        """Records accumulated since the last read (then a new window starts): dicts with kind,
+        step, slice, piece, stream, call, flops, bytes, start_ms, end_ms (ms from the first traced
+        call's start on the caller stream)."""
+        n = ctypes.c_int32()
+        _check(lib.tpslice_trace_read(self._h, None, 0, ctypes.byref(n)))
+        recs = (TraceRec * max(1, n.value))()
+        _check(lib.tpslice_trace_read(self._h, recs, n.value, ctypes.byref(n)))
+        out = []
+        for r in recs[:n.value]:
+            out.append(dict(kind=("gemm", "copy", "colsum")[r.kind], step=STEPS[r.step], slice=r.slice,
+                            piece=r.piece, stream=r.stream, call=r.call, flops=r.flops, bytes=r.bytes,
+                            start_ms=r.start_ms, end_ms=r.end_ms))
+        return out
+
+    def piece(self, index: int):
+        out = (ctypes.c_int64 * 4)()
+        _check(lib.tpslice_plan_piece(self._h, index, out))
+        return tuple(out)
+
+    def workspace_size(self, op: int) -> int:
+        n = ctypes.c_size_t()
+        _check(lib.tpslice_workspace_size(self._h, op, ctypes.byref(n)))
+        return n.value
+
+    def workspace(self, op: int, device="cuda") -> Optional[torch.Tensor]:
+        """A cached device workspace for `op` (torch allocations are 256-byte aligned)."""
+        n = self.workspace_size(op)
+        if n == 0:
+            return None
+        ws = self._ws.get(op)
+        if ws is None or ws.numel() < n:
+            ws = torch.empty(n, dtype=torch.uint8, device=device)
+            self._ws[op] = ws
+        return ws
+
+    @staticmethod
+    def _ws_args(ws: Optional[torch.Tensor]):
+        if ws is None:
+            return None, 0
+        return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+    # ------------------------------------------------------------------------------- entry points
+    def mlp_fwd(self, X, W1, b1, W2, Z, U_save=None, Z_handoff=None, workspace=None, stream=None):
+        i = self.info
+        _shape(X, (i.tokens, i.hidden), "X"); _shape(W1, (i.n1, i.hidden), "W1")
+        _shape(b1, (i.n1,), "b1"); _shape(W2, (i.hidden, i.ffn_shard), "W2")
+        _shape(Z, (i.tokens, i.hidden), "Z"); _shape(U_save, (i.tokens, i.n1), "U_save")
+        _shape(Z_handoff, (i.tokens, i.hidden), "Z_handoff")
+        ws = workspace if workspace is not None else self.workspace(OP_MLP_FWD)
+        wp, wn = self._ws_args(ws)
+        _check(lib.tpslice_mlp_fwd(self._h, _ptr(X, name="X"), _ptr(W1, name="W1"), _ptr(b1, name="b1"),
+                                   _ptr(W2, name="W2"), _ptr(Z, name="Z"), _ptr(U_save, name="U_save"),
+                                   _ptr(Z_handoff, name="Z_handoff"), wp, wn, _stream(stream)))
+
+    def attnproj_fwd(self, X, Wqkv, bqkv, QKV, C, Wo, Z, Z_handoff=None, workspace=None, stream=None):
+        i = self.info
+        _shape(X, (i.tokens, i.hidden), "X"); _shape(Wqkv, (i.qkv_width, i.hidden), "Wqkv")
+        _shape(bqkv, (i.qkv_width,), "bqkv"); _shape(QKV, (i.tokens, i.qkv_width), "QKV")
+        _shape(C, (i.tokens, i.ctx_width), "C"); _shape(Wo, (i.hidden, i.ctx_width), "Wo")
+        _shape(Z, (i.tokens, i.hidden), "Z"); _shape(Z_handoff, (i.tokens, i.hidden), "Z_handoff")
+        ws = workspace if workspace is not None else self.workspace(OP_ATTNPROJ_FWD)
+        wp, wn = self._ws_args(ws)
+        _check(lib.tpslice_attnproj_fwd(self._h, _ptr(X, name="X"), _ptr(Wqkv, name="Wqkv"),
+                                        _ptr(bqkv, name="bqkv"), _ptr(QKV, name="QKV"), _ptr(C, name="C"),
+                                        _ptr(Wo, name="Wo"), _ptr(Z, name="Z"),
+                                        _ptr(Z_handoff, name="Z_handoff"), wp, wn, _stream(stream)))
+
+    def mlp_bwd(self, X, W1, W2, U_saved, dY, dX, dW1, dW2, db1=None, dX_handoff=None, accumulate=False,
+                workspace=None, stream=None):
+        i = self.info
+        _shape(X, (i.tokens, i.hidden), "X"); _shape(W1, (i.n1, i.hidden), "W1")
+        _shape(W2, (i.hidden, i.ffn_shard), "W2"); _shape(U_saved, (i.tokens, i.n1), "U_saved")
+        _shape(dY, (i.tokens, i.hidden), "dY"); _shape(dX, (i.tokens, i.hidden), "dX")
+        _shape(dW1, (i.n1, i.hidden), "dW1"); _shape(dW2, (i.hidden, i.ffn_shard), "dW2")
+        _shape(db1, (i.n1,), "db1"); _shape(dX_handoff, (i.tokens, i.hidden), "dX_handoff")
+        ws = workspace if workspace is not None else self.workspace(OP_MLP_BWD)
+        wp, wn = self._ws_args(ws)
+        f32 = torch.float32
+        _check(lib.tpslice_mlp_bwd(self._h, _ptr(X, name="X"), _ptr(W1, name="W1"), _ptr(W2, name="W2"),
+                                   _ptr(U_saved, name="U_saved"), _ptr(dY, name="dY"), _ptr(dX, name="dX"),
+                                   _ptr(dX_handoff, name="dX_handoff"), _ptr(dW1, f32, "dW1"),
+                                   _ptr(db1, f32, "db1"), _ptr(dW2, f32, "dW2"), int(bool(accumulate)),
+                                   wp, wn, _stream(stream)))
+
+    def attnproj_bwd(self, X, Wqkv, dQKV, C, Wo, dY, dX, dC, dWqkv, dWo, dbqkv=None, dX_handoff=None,
+                     accumulate=False, workspace=None, stream=None):
+        i = self.info
+        _shape(X, (i.tokens, i.hidden), "X"); _shape(Wqkv, (i.qkv_width, i.hidden), "Wqkv")
+        _shape(dQKV, (i.tokens, i.qkv_width), "dQKV"); _shape(C, (i.tokens, i.ctx_width), "C")
+        _shape(Wo, (i.hidden, i.ctx_width), "Wo"); _shape(dY, (i.tokens, i.hidden), "dY")
+        _shape(dX, (i.tokens, i.hidden), "dX"); _shape(dC, (i.tokens, i.ctx_width), "dC")
+        _shape(dWqkv, (i.qkv_width, i.hidden), "dWqkv"); _shape(dWo, (i.hidden, i.ctx_width), "dWo")
+        _shape(dbqkv, (i.qkv_width,), "dbqkv"); _shape(dX_handoff, (i.tokens, i.hidden), "dX_handoff")
+        ws = workspace if workspace is not None else self.workspace(OP_ATTNPROJ_BWD)
+        wp, wn = self._ws_args(ws)
+        f32 = torch.float32
+        _check(lib.tpslice_attnproj_bwd(self._h, _ptr(X, name="X"), _ptr(Wqkv, name="Wqkv"),
+                                        _ptr(dQKV, name="dQKV"), _ptr(C, name="C"), _ptr(Wo, name="Wo"),
+                                        _ptr(dY, name="dY"), _ptr(dX, name="dX"),
+                                        _ptr(dX_handoff, name="dX_handoff"), _ptr(dC, name="dC"),
+                                        _ptr(dWqkv, f32, "dWqkv"), _ptr(dbqkv, f32, "dbqkv"),
+                                        _ptr(dWo, f32, "dWo"), int(bool(accumulate)), wp, wn, _stream(stream)))
+
+
+def plan_for(workload, **overrides) -> Plan:
+    """A plan for a synthetic workload description (comm_overlap_amd.synth.Workload)."""
+    kw = dict(tokens=workload.tokens, hidden=workload.hidden, ffn=workload.ffn, tp_size=workload.tp,
+              n_row_slices=workload.row_slices, n_col_slices=workload.col_slices, n_heads=workload.heads,
+              n_kv_heads=workload.kv_heads, head_dim=workload.head_dim, act=workload.act)
+    kw.update(overrides)
+    return Plan(Config(**kw))

@@ -1,0 +1,214 @@
+/*
+ * tpslice.h - C ABI of the sliced tensor-parallel layer shard for MI355X (gfx950).
+ *
+ * One GPU's tensor-parallel share of a transformer layer's dense GEMM chain: a column-parallel
+ * projection, a fused GeLU/SwiGLU epilogue and a row-parallel projection whose output is this rank's
+ * partial sum (the Megatron-LM layer that Domino speeds up: Domino page, Abstract; builds-on list:
+ * "Megatron-LM", "GLU Variants Improve Transformer"). The batch is cut into independent pieces -
+ * contiguous token-row slices, and column slices of the partial-sum output - and each finished piece
+ * is handed off (here: copied by a DMA engine on a side stream, in place of the group's reduction)
+ * while later pieces compute (Domino page, Abstract: break one batch's dependency into independent
+ * pieces and overlap their communication with later computation; FiCCO page, Abstract: overlap below
+ * shard granularity, communication offloaded to GPU DMA engines). Slicing and overlap change no value
+ * (DHelix review, "If this is right": reordering/overlap leaves training semantics unchanged).
+ *
+ * Conventions for every entry point
+ *   - Device pointers are plain `void*` into GPU memory owned by the caller; the library never frees
+ *     or keeps them beyond the call's stream work. 16-byte alignment is required.
+ *   - bf16 tensors are row-major and contiguous. Weights use the [out_features][in_features] layout
+ *     of a linear layer:  W1 [N1][h] (N1 = F' for GeLU, 2F' for SwiGLU with rows [gate | up]),
+ *     W2 [h][F'], Wqkv [(q+2kv)d][h] with rows [Q | K | V], Wo [h][q d].
+ *     Activations: X, Z, dY, dX [M][h]; U [M][N1]; C, dC [M][q d]; QKV, dQKV [M][(q+2kv)d].
+ *     Weight and bias gradients are fp32 in the weight's own layout.
+ *   - `stream` is the caller's hipStream_t (NULL = the null stream). Calls are asynchronous and
+ *     stream-ordered: they start after work already queued on `stream`, and every output (the
+ *     hand-off copy included) is complete when `stream` reaches the point after the call. Internally
+ *     the plan forks onto its own worker and copy streams and joins back onto `stream`.
+ *   - Outputs must not alias inputs or each other. Results are deterministic: the same plan and
+ *     inputs give bitwise identical outputs, whatever the slice timing.
+ *   - Errors are reported by status code only; argument, shape and workspace errors are detected
+ *     before any GPU work is queued. tpslice_last_error() gives the text of the calling thread's last
+ *     failure. A plan must not be used from two host threads at once, nor destroyed while its work
+ *     is still in flight.
+ */
+#ifndef TPSLICE_H
+#define TPSLICE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define TPSLICE_API __attribute__((visibility("default")))
+#else
+#define TPSLICE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TPSLICE_OK = 0,
+  TPSLICE_ERR_INVALID = 1,     /* null required pointer, bad enum value, bad or destroyed plan      */
+  TPSLICE_ERR_SHAPE = 2,       /* sizes the slicing or the kernels cannot take                       */
+  TPSLICE_ERR_UNSUPPORTED = 3, /* valid request outside what the plan describes (e.g. no heads)      */
+  TPSLICE_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned                         */
+  TPSLICE_ERR_HIP = 5          /* a HIP runtime call failed; see tpslice_last_error()                */
+} tpslice_status_t;
+
+typedef enum {
+  TPSLICE_ACT_GELU = 1,   /* H = U * Phi(U), exact erf form                                   */
+  TPSLICE_ACT_SWIGLU = 2  /* U = [G | V]; H = silu(G) * V, silu(g) = g / (1 + e^-g)          */
+} tpslice_act_t;
+
+/* tpslice_desc_t.flags */
+#define TPSLICE_F_SERIALIZE 0x1u /* every product and copy in order on the caller stream (ablation)  */
+#define TPSLICE_F_COPY_BLIT 0x2u /* hand-off copies by the runtime's copy kernel instead of the DMA
+                                    engines (uses compute units; for comparison)                       */
+
+typedef struct {
+  int64_t tokens;         /* M: token rows in the batch (micro-batch x sequence, batch-major)         */
+  int64_t hidden;         /* h: model width; multiple of 8                                            */
+  int64_t ffn;            /* F: full FFN width; this rank holds F' = ffn / tp_size (multiple of 8)    */
+  int32_t tp_size;        /* simulated tensor-parallel group size (>= 1); no communication happens   */
+  int32_t n_row_slices;   /* r: equal contiguous token-row slices; must divide tokens                 */
+  int32_t n_col_slices;   /* c: equal column slices of each hand-off output (width h); h/c % 8 == 0  */
+  int32_t n_heads;        /* full-model query heads; 0 = no attention projections in this plan       */
+  int32_t n_kv_heads;     /* full-model key/value heads (GQA); this rank holds max(1, n_kv/tp_size)   */
+  int32_t head_dim;       /* d; multiple of 8                                                          */
+  int32_t act;            /* tpslice_act_t                                                              */
+  int32_t n_streams;      /* worker streams for the slices (0 = default)                              */
+  int32_t n_copy_streams; /* side streams for hand-off copies (0 = default)                           */
+  uint32_t flags;         /* TPSLICE_F_*                                                                */
+} tpslice_desc_t;
+
+typedef struct tpslice_plan_s* tpslice_plan_t;
+
+typedef struct {
+  int64_t tokens, hidden, ffn_shard, n1, qkv_width, ctx_width;
+  int64_t rows_per_slice;       /* M / r                                                             */
+  int64_t handoff_cols;         /* h / c                                                             */
+  int32_t n_row_slices, n_col_slices, n_streams, n_copy_streams;
+  int32_t q_heads, kv_heads;    /* this rank's head counts                                           */
+} tpslice_plan_info_t;
+
+typedef enum {
+  TPSLICE_OP_MLP_FWD = 0,
+  TPSLICE_OP_ATTNPROJ_FWD = 1,
+  TPSLICE_OP_MLP_BWD = 2,
+  TPSLICE_OP_ATTNPROJ_BWD = 3
+} tpslice_op_t;
+
+/* Validate `desc` and build a plan (host memory only; no GPU call is made). The slice geometry is
+ * r equal contiguous token-row ranges, each cut into c equal column ranges of the hand-off output,
+ * finished in order row slice major (Domino page, Abstract: independent pieces of one batch).
+ * Returns TPSLICE_ERR_INVALID for a null argument or bad enum, TPSLICE_ERR_SHAPE for sizes that do
+ * not divide or are not multiples of 8, or whose operands exceed 4 GiB. On error *out is NULL.     */
+TPSLICE_API tpslice_status_t tpslice_plan(const tpslice_desc_t* desc, tpslice_plan_t* out);
+
+/* Release the plan, its streams and events. NULL is a no-op. Work in flight must have finished.   */
+TPSLICE_API tpslice_status_t tpslice_plan_destroy(tpslice_plan_t plan);
+
+/* Sizes the plan derived from its descriptor.                                                     */
+TPSLICE_API tpslice_status_t tpslice_plan_info(tpslice_plan_t plan, tpslice_plan_info_t* info);
+
+/* The index-th hand-off piece in finish order (0 <= index < r*c): out[0..3] = row begin, row end,
+ * column begin, column end (end exclusive) of the [M][h] hand-off tensor.                         */
+TPSLICE_API tpslice_status_t tpslice_plan_piece(tpslice_plan_t plan, int32_t index, int64_t out[4]);
+
+/* Bytes of device workspace that `op` needs (may be 0). Workspace must be 256-byte aligned.       */
+TPSLICE_API tpslice_status_t tpslice_workspace_size(tpslice_plan_t plan, int32_t op, size_t* bytes);
+
+/* MLP forward (one rank's share).
+ *   U = X W1^T + b1;  H = act(U);  Z = H W2^T   (Z: this rank's partial sum, no row-parallel bias)
+ * Inputs : X [M][h], W1 [N1][h], b1 [N1] bf16 or NULL, W2 [h][F'].
+ * Outputs: Z [M][h] bf16; U_save [M][N1] bf16 or NULL (pre-activation kept for the backward pass);
+ *          Z_handoff [M][h] bf16 or NULL: when given, each finished piece of Z is copied into it on
+ *          a side stream while later pieces compute (Z_handoff == Z bitwise when the call is done).
+ * Workspace: tpslice_workspace_size(TPSLICE_OP_MLP_FWD) bytes (holds H).                          */
+TPSLICE_API tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t plan, const void* X, const void* W1, const void* b1,
+                                 const void* W2, void* Z, void* U_save, void* Z_handoff,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention input/output projections, forward (one rank's heads).
+ *   QKV = X Wqkv^T (+ bqkv)   column-parallel;   Z = C Wo^T   row-parallel partial sum
+ * C is the attention context of this rank's heads (an input: the attention core is not part of this
+ * library). Z_handoff as in tpslice_mlp_fwd. Needs n_heads > 0 in the plan.                       */
+TPSLICE_API tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t plan, const void* X, const void* Wqkv,
+                                      const void* bqkv, void* QKV, const void* C, const void* Wo,
+                                      void* Z, void* Z_handoff, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* MLP backward, given the saved pre-activation U [M][N1] and the upstream gradient dY [M][h]:
+ *   dH = dY W2;  dU = dH * act'(U) (SwiGLU: [dH V silu'(G) | dH silu(G)]);  dX = dU W1
+ *   dW1 (+)= dU^T X;  db1 (+)= column sums of dU;  dW2 (+)= dY^T act(U)
+ * dX [M][h] bf16 is this rank's partial sum and the hand-off tensor (dX_handoff as Z_handoff above).
+ * dW1 [N1][h], dW2 [h][F'] and db1 [N1] (or NULL) are fp32; accumulate = 0 overwrites them,
+ * 1 adds to their contents. Workspace: tpslice_workspace_size(TPSLICE_OP_MLP_BWD).               */
+TPSLICE_API tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t plan, const void* X, const void* W1, const void* W2,
+                                 const void* U_saved, const void* dY, void* dX, void* dX_handoff,
+                                 float* dW1, float* db1, float* dW2, int32_t accumulate,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention projections backward, given dQKV [M][(q+2kv)d] (from the attention core) and dY [M][h]
+ * (into the output projection):
+ *   dC = dY Wo;  dWo (+)= dY^T C;  dX = dQKV Wqkv (partial sum, hand-off);  dWqkv (+)= dQKV^T X;
+ *   dbqkv (+)= column sums of dQKV (or NULL).  dC bf16; weight/bias gradients fp32.              */
+TPSLICE_API tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t plan, const void* X, const void* Wqkv,
+                                      const void* dQKV, const void* C, const void* Wo,
+                                      const void* dY, void* dX, void* dX_handoff, void* dC,
+                                      float* dWqkv, float* dbqkv, float* dWo, int32_t accumulate,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tracing. When enabled, every product and every hand-off copy is bracketed by timing events on
+ * the stream it runs on. Records accumulate over calls until they are read; times are milliseconds
+ * from the start (on the caller stream) of the first call traced since the last read, and `call`
+ * numbers the calls from 0 in that window. Tracing adds event records to the streams; it changes
+ * no result.                                                                                      */
+typedef enum { TPSLICE_TRACE_GEMM = 0, TPSLICE_TRACE_COPY = 1, TPSLICE_TRACE_COLSUM = 2 } tpslice_trace_kind_t;
+typedef enum {
+  TPSLICE_STEP_MLP_UP = 0,     /* X W1^T + activation                 */
+  TPSLICE_STEP_MLP_DOWN = 1,   /* H W2^T (partial sum piece)          */
+  TPSLICE_STEP_QKV = 2,        /* X Wqkv^T                            */
+  TPSLICE_STEP_OUT = 3,        /* C Wo^T (partial sum piece)          */
+  TPSLICE_STEP_MLP_DH = 4,     /* dY W2 with the activation derivative */
+  TPSLICE_STEP_MLP_DX = 5,     /* dU W1 (partial sum piece)           */
+  TPSLICE_STEP_MLP_DW1 = 6,    /* dU^T X                              */
+  TPSLICE_STEP_MLP_DW2 = 7,    /* dY^T H                              */
+  TPSLICE_STEP_ATTN_DX = 8,    /* dQKV Wqkv (partial sum piece)       */
+  TPSLICE_STEP_ATTN_DC = 9,    /* dY Wo                               */
+  TPSLICE_STEP_ATTN_DWQKV = 10,/* dQKV^T X                            */
+  TPSLICE_STEP_ATTN_DWO = 11,  /* dY^T C                              */
+  TPSLICE_STEP_BIAS_GRAD = 12, /* column sums                         */
+  TPSLICE_STEP_HANDOFF = 13    /* hand-off copy                       */
+} tpslice_step_t;
+typedef struct {
+  int32_t kind;     /* tpslice_trace_kind_t                                           */
+  int32_t step;     /* tpslice_step_t                                                 */
+  int32_t slice;    /* row slice (-1: all tokens)                                    */
+  int32_t piece;    /* column piece (-1: none)                                        */
+  int32_t stream;   /* 0..S-1 worker, S..S+E-1 copy stream, -1 caller stream         */
+  int32_t call;     /* index of the call in the current trace window                 */
+  double flops;     /* algorithmic flops, 2*M*N*K (0 for copies)                      */
+  double bytes;     /* bytes copied (copies), 0 otherwise                             */
+  float start_ms, end_ms;
+} tpslice_trace_rec_t;
+
+TPSLICE_API tpslice_status_t tpslice_trace_enable(tpslice_plan_t plan, int32_t enable);
+/* Sets *count to the number of records in the window. With cap >= *count it also copies them into
+ * `recs` (blocking until their events have completed) and starts a new window; with a smaller cap
+ * (e.g. 0) it only reports the count. TPSLICE_ERR_INVALID if tracing is off.                      */
+TPSLICE_API tpslice_status_t tpslice_trace_read(tpslice_plan_t plan, tpslice_trace_rec_t* recs, int32_t cap,
+                                                int32_t* count);
+
+/* Static text for a status code.                                                                   */
+TPSLICE_API const char* tpslice_error_string(tpslice_status_t status);
+
+/* Text of the calling thread's most recent failure ("" if none).                                   */
+TPSLICE_API const char* tpslice_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSLICE_H */

@@ -1,0 +1,132 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, validates plans and
+arguments before any GPU work, and its slice geometry equals the oracle's bit for bit."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from comm_overlap_amd import synth
+from oracle import plan as OP
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+T = pytest.importorskip("comm_overlap_amd.tpslice", reason="libtpslice.so not built")
+
+
+def declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"TPSLICE_API\s+[\w\s\*]+?\b(tpslice_\w+)\s*\(", txt))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(T.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(T.EXPORTS) == names
+
+
+@pytest.mark.parametrize("key", list(synth.WORKLOADS))
+def test_geometry_matches_oracle(key):
+    w = synth.WORKLOADS[key]
+    p = T.plan_for(w)
+    i = p.info
+    assert (i.tokens, i.hidden, i.ffn_shard, i.n1) == (w.tokens, w.hidden, w.ffn_shard, w.n1)
+    if w.has_attn:
+        assert (i.qkv_width, i.ctx_width, i.q_heads, i.kv_heads) == (
+            w.qkv_width, w.ctx_width, w.q_heads_shard, w.kv_heads_shard)
+    pieces = [p.piece(k) for k in range(w.row_slices * w.col_slices)]
+    assert pieces == OP.handoff_pieces(w.tokens, w.hidden, w.row_slices, w.col_slices)
+    with pytest.raises(T.TpsliceError):
+        p.piece(w.row_slices * w.col_slices)
+
+
+@pytest.mark.parametrize("M,h,r,c", [(24, 40, 3, 5), (8, 64, 8, 8), (1024, 1024, 16, 4), (0, 8, 3, 1)])
+def test_geometry_small(M, h, r, c):
+    p = T.Plan(T.Config(tokens=M, hidden=h, ffn=64, n_row_slices=r, n_col_slices=c))
+    got = [p.piece(k) for k in range(r * c)]
+    if M == 0:
+        assert all(g[0] == g[1] == 0 for g in got)
+    else:
+        assert got == OP.handoff_pieces(M, h, r, c)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tokens=100, hidden=64, ffn=64, n_row_slices=3), T.ERR_SHAPE),
+    (dict(tokens=64, hidden=60, ffn=64), T.ERR_SHAPE),
+    (dict(tokens=64, hidden=64, ffn=100, tp_size=2), T.ERR_SHAPE),      # shard 50 not a multiple of 8
+    (dict(tokens=64, hidden=64, ffn=64, tp_size=3), T.ERR_SHAPE),
+    (dict(tokens=64, hidden=64, ffn=64, n_col_slices=3), T.ERR_SHAPE),
+    (dict(tokens=64, hidden=64, ffn=64, n_col_slices=16), T.ERR_SHAPE),  # 4 columns per slice
+    (dict(tokens=64, hidden=64, ffn=64, act="relu"), T.ERR_INVALID),
+    (dict(tokens=64, hidden=64, ffn=64, n_heads=6, n_kv_heads=2, head_dim=12), T.ERR_SHAPE),
+    (dict(tokens=64, hidden=64, ffn=64, n_heads=6, n_kv_heads=0, head_dim=16), T.ERR_SHAPE),
+    (dict(tokens=64, hidden=64, ffn=64, n_streams=99), T.ERR_SHAPE),
+    (dict(tokens=1 << 20, hidden=4096, ffn=4096), T.ERR_SHAPE),          # 8 GiB operand
+])
+def test_plan_rejects(kw, code):
+    with pytest.raises(T.TpsliceError) as e:
+        T.Plan(T.Config(**kw))
+    assert e.value.code == code
+
+
+def test_gqa_kv_heads_below_tp():
+    p = T.plan_for(synth.WORKLOADS["llama3_70b_layer"])
+    assert (p.info.q_heads, p.info.kv_heads, p.info.qkv_width) == (8, 1, 1280)
+
+
+def test_workspace_sizes():
+    w = synth.WORKLOADS["llama3_70b_layer"]
+    p = T.plan_for(w)
+    M, Fp, N1 = w.tokens, w.ffn_shard, w.n1
+    assert p.workspace_size(T.OP_MLP_FWD) == M * Fp * 2
+    assert p.workspace_size(T.OP_MLP_BWD) >= M * N1 * 2 + M * Fp * 2
+    assert p.workspace_size(T.OP_ATTNPROJ_FWD) == 0
+    with pytest.raises(T.TpsliceError):
+        p.workspace_size(7)
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_argument_errors_before_any_gpu_work():
+    """Null, misaligned, workspace and plan errors come back before anything touches the GPU (the
+    pointers below are never dereferenced)."""
+    lib = T.lib
+    p = T.Plan(T.Config(tokens=64, hidden=64, ffn=64, n_row_slices=2))
+    A = _fake(0x100000)
+    ws_need = p.workspace_size(T.OP_MLP_FWD)
+    # NULL required pointer
+    assert lib.tpslice_mlp_fwd(p._h, None, A, None, A, A, None, None, A, ws_need, None) == T.ERR_INVALID
+    assert b"X is NULL" in lib.tpslice_last_error()
+    # misaligned pointer
+    assert lib.tpslice_mlp_fwd(p._h, _fake(0x100002), A, None, A, A, None, None, A, ws_need,
+                               None) == T.ERR_INVALID
+    # workspace too small / missing / misaligned
+    assert lib.tpslice_mlp_fwd(p._h, A, A, None, A, A, None, None, A, ws_need - 1, None) == T.ERR_WORKSPACE
+    assert lib.tpslice_mlp_fwd(p._h, A, A, None, A, A, None, None, None, 0, None) == T.ERR_WORKSPACE
+    assert lib.tpslice_mlp_fwd(p._h, A, A, None, A, A, None, None, _fake(0x100010), ws_need,
+                               None) == T.ERR_WORKSPACE
+    # invalid plan handle
+    assert lib.tpslice_mlp_fwd(None, A, A, None, A, A, None, None, A, ws_need, None) == T.ERR_INVALID
+    # attention entry points on a plan without heads
+    assert lib.tpslice_attnproj_fwd(p._h, A, A, None, A, A, A, A, None, None, 0, None) == T.ERR_UNSUPPORTED
+    assert lib.tpslice_attnproj_bwd(p._h, A, A, A, A, A, A, A, None, A, A, None, A, 0, None, 0,
+                                    None) == T.ERR_UNSUPPORTED
+    # bad accumulate flag
+    wsb = p.workspace_size(T.OP_MLP_BWD)
+    assert lib.tpslice_mlp_bwd(p._h, A, A, A, A, A, A, None, A, None, A, 2, A, wsb, None) == T.ERR_INVALID
+    assert lib.tpslice_error_string(T.ERR_WORKSPACE) == b"workspace too small or misaligned"
+    p.close()
+    p.close()  # idempotent in the binding
+
+
+def test_serialize_plan_uses_one_stream():
+    p = T.Plan(T.Config(tokens=64, hidden=64, ffn=64, n_row_slices=4, serialize=True))
+    assert (p.info.n_streams, p.info.n_copy_streams) == (1, 1)

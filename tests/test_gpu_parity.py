@@ -1,0 +1,248 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle, plus the exact identities
+that slicing and overlap must keep (Domino page, Abstract: the pieces are independent; DHelix review,
+"If this is right": overlap leaves semantics unchanged)."""
+import numpy as np
+import pytest
+import torch
+
+from comm_overlap_amd import synth
+from oracle import layer as L
+import gpu_cases as G
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from comm_overlap_amd import tpslice as T
+
+f64 = L.as_f64
+
+# Small shapes that span several 256-wide tiles with ragged tails in every dimension.
+SMALL_GELU = synth.custom("small_gelu", 901, tokens=640, hidden=528, ffn=328, tp=1, act="gelu", bias=True,
+                          row_slices=2, col_slices=2, backward=True)
+SMALL_SWIGLU = synth.custom("small_swiglu", 902, tokens=576, hidden=272, ffn=400, tp=2, act="swiglu",
+                            bias=False, row_slices=3, col_slices=2, backward=True)
+SMALL_ATTN = synth.custom("small_attn", 903, tokens=520, hidden=264, ffn=64, tp=2, act="gelu", bias=False,
+                          row_slices=2, col_slices=1, heads=6, kv_heads=2, head_dim=40, backward=True)
+
+
+def _print_case(name, **kw):
+    print(f"[case] {name} {kw}", flush=True)
+
+
+@pytest.mark.parametrize("w", [SMALL_GELU, SMALL_SWIGLU], ids=lambda w: w.key)
+def test_mlp_fwd_small(w):
+    _print_case("mlp_fwd", key=w.key)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    out = G.run_mlp_fwd(plan, inp)
+    ref = G.oracle_mlp_fwd(inp, w.act)
+    G.assert_parity(out["Z"], ref["Z"], "Z")
+    G.assert_parity(out["U"], ref["U"], "U")
+    assert torch.equal(out["Zh"], out["Z"])
+
+
+def test_mlp_fwd_tiny_workload():
+    w = synth.WORKLOADS["tiny_gpt_mlp"]
+    _print_case("mlp_fwd", key=w.key)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    out = G.run_mlp_fwd(plan, inp)
+    ref = G.oracle_mlp_fwd(inp, w.act)
+    G.assert_parity(out["Z"], ref["Z"], "Z")
+    G.assert_parity(out["U"], ref["U"], "U")
+    assert torch.equal(out["Zh"], out["Z"])
+
+
+@pytest.mark.parametrize("w", [SMALL_GELU, SMALL_SWIGLU, synth.WORKLOADS["tiny_gpt_mlp"]], ids=lambda w: w.key)
+def test_slicing_is_bit_exact(w):
+    """Sliced == unsliced, serialized == concurrent, blit copy == DMA copy, repeat == first run."""
+    _print_case("bitexact", key=w.key)
+    inp = synth.make_inputs(w)
+    base = G.run_mlp_fwd(T.plan_for(w, n_row_slices=1, n_col_slices=1), inp)
+    for kw in [dict(), dict(serialize=True), dict(copy_blit=True), dict(n_streams=3, n_copy_streams=2)]:
+        out = G.run_mlp_fwd(T.plan_for(w, **kw), inp)
+        assert torch.equal(out["Z"], base["Z"]), kw
+        assert torch.equal(out["U"], base["U"]), kw
+        assert torch.equal(out["Zh"], base["Z"]), kw
+    again = G.run_mlp_fwd(T.plan_for(w), inp)
+    assert torch.equal(again["Z"], base["Z"])
+
+
+def test_closed_forms_exact():
+    w = SMALL_GELU
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    # W2 = 0  =>  Z = 0 exactly
+    z = dict(inp, W2=torch.zeros_like(inp["W2"]))
+    out = G.run_mlp_fwd(plan, z)
+    assert torch.count_nonzero(out["Z"].float()) == 0
+    # W1 = 0  =>  every row of Z is the same (act(b1) W2^T), bit for bit
+    z = dict(inp, W1=torch.zeros_like(inp["W1"]))
+    out = G.run_mlp_fwd(plan, z)
+    assert torch.equal(out["Z"], out["Z"][:1].expand_as(out["Z"]))
+    ref = G.oracle_mlp_fwd({k: v[:1] if k == "X_mlp" else v for k, v in z.items()}, w.act)
+    G.assert_parity(out["Z"][:1], ref["Z"], "Z row")
+    # W2 scaled by 2^3  =>  Z scaled by 2^3 bitwise (exact in binary floating point)
+    base = G.run_mlp_fwd(plan, inp)
+    out = G.run_mlp_fwd(plan, dict(inp, W2=inp["W2"] * 8))
+    assert torch.equal(out["Z"], base["Z"] * 8)
+
+
+def test_row_permutation_commutes():
+    """Permuting token rows permutes output rows, bitwise (rows are independent)."""
+    w = SMALL_SWIGLU
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    perm = torch.randperm(w.tokens, generator=torch.Generator().manual_seed(5))
+    base = G.run_mlp_fwd(plan, inp)
+    out = G.run_mlp_fwd(plan, dict(inp, X_mlp=inp["X_mlp"][perm].contiguous()))
+    assert torch.equal(out["Z"], base["Z"][perm.cuda()])
+
+
+@pytest.mark.parametrize("bias", [True, False])
+def test_attnproj_fwd_small(bias):
+    w = SMALL_ATTN
+    _print_case("attn_fwd", key=w.key, bias=bias)
+    inp = synth.make_inputs(w)
+    bqkv = synth.randn_bf16((w.qkv_width,), 0.01, 77) if bias else None
+    plan = T.plan_for(w)
+    out = G.run_attn_fwd(plan, inp, bias=bqkv)
+    ref = L.attnproj_fwd(f64(inp["X"]), f64(inp["Wqkv"]), f64(bqkv) if bias else None, f64(inp["C"]),
+                         f64(inp["Wo"]))
+    G.assert_parity(out["QKV"], ref["QKV"], "QKV")
+    G.assert_parity(out["Z"], ref["Z"], "Z")
+    assert torch.equal(out["Zh"], out["Z"])
+    one = G.run_attn_fwd(T.plan_for(w, n_row_slices=1), inp, bias=bqkv)
+    assert torch.equal(one["Z"], out["Z"]) and torch.equal(one["QKV"], out["QKV"])
+
+
+@pytest.mark.parametrize("w", [SMALL_GELU, SMALL_SWIGLU], ids=lambda w: w.key)
+def test_mlp_bwd_small(w):
+    _print_case("mlp_bwd", key=w.key)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    out = G.run_mlp_bwd(plan, inp, with_bias=w.bias)
+    ref = L.mlp_bwd(f64(inp["X_mlp"]), f64(inp["W1"]), f64(inp["W2"]), f64(inp["U_saved"]), f64(inp["dY"]),
+                    w.act, with_bias=w.bias)
+    G.assert_parity(out["dX"], ref["dX"], "dX")
+    G.assert_parity(out["dW1"], ref["dW1"], "dW1")
+    G.assert_parity(out["dW2"], ref["dW2"], "dW2")
+    if w.bias:
+        G.assert_parity(out["db1"], ref["db1"], "db1")
+    assert torch.equal(out["dXh"], out["dX"])
+    # accumulate = 1 adds to what is there; the token sum is not split, so it matches bitwise a
+    # run whose fp32 accumulators start from the same values
+    init = tuple(torch.randn_like(t) if t is not None else None for t in (out["dW1"], out["dW2"], out["db1"]))
+    acc = G.run_mlp_bwd(plan, inp, with_bias=w.bias, accumulate=True, init=init)
+    G.assert_parity(acc["dW1"], f64(init[0].cpu()) + ref["dW1"], "dW1 accumulated")
+    G.assert_parity(acc["dW2"], f64(init[1].cpu()) + ref["dW2"], "dW2 accumulated")
+    # sliced == unsliced, serialized == concurrent
+    for kw in [dict(n_row_slices=1, n_col_slices=1), dict(serialize=True)]:
+        o2 = G.run_mlp_bwd(T.plan_for(w, **kw), inp, with_bias=w.bias)
+        for k in ("dX", "dW1", "dW2", "db1"):
+            if out[k] is not None:
+                assert torch.equal(o2[k], out[k]), (kw, k)
+
+
+@pytest.mark.parametrize("bias", [True, False])
+def test_attnproj_bwd_small(bias):
+    w = SMALL_ATTN
+    _print_case("attn_bwd", key=w.key, bias=bias)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    out = G.run_attn_bwd(plan, inp, with_bias=bias)
+    ref = L.attnproj_bwd(f64(inp["X"]), f64(inp["Wqkv"]), f64(inp["dQKV"]), f64(inp["C"]), f64(inp["Wo"]),
+                         f64(inp["dY_attn"]), with_bias=bias)
+    for k in ("dX", "dC", "dWqkv", "dWo") + (("dbqkv",) if bias else ()):
+        G.assert_parity(out[k], ref[k], k)
+    assert torch.equal(out["dXh"], out["dX"])
+
+
+def test_empty_batch():
+    w = synth.custom("empty", 904, tokens=0, hidden=64, ffn=64, tp=1, act="gelu", bias=True, row_slices=2,
+                     col_slices=2, backward=True)
+    plan = T.plan_for(w)
+    inp = synth.make_inputs(w)
+    out = G.run_mlp_fwd(plan, inp)
+    assert out["Z"].numel() == 0
+    nan = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device="cuda")
+    res = G.run_mlp_bwd(plan, inp, with_bias=True, init=(nan(64, 64), nan(64, 64), nan(64)))
+    for k in ("dW1", "dW2", "db1"):
+        assert torch.count_nonzero(res[k]) == 0 and not torch.isnan(res[k]).any(), k
+
+
+def test_one_row_slices():
+    w = synth.custom("one_row", 905, tokens=8, hidden=64, ffn=128, tp=2, act="swiglu", bias=False,
+                     row_slices=8, col_slices=4, backward=True)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    out = G.run_mlp_fwd(plan, inp)
+    G.assert_parity(out["Z"], G.oracle_mlp_fwd(inp, w.act)["Z"], "Z")
+    assert torch.equal(out["Zh"], out["Z"])
+
+
+# ------------------------------------------------------------------- full-size workloads, sampled
+@pytest.mark.parametrize("key", ["gpt3_2.7b_mlp", "llama2_7b_mlp"])
+def test_full_forward_workload(key):
+    w = synth.WORKLOADS[key]
+    _print_case("full_fwd", key=key)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    out = G.run_mlp_fwd(plan, inp)
+    assert torch.equal(out["Zh"], out["Z"])
+    rows = G.sample_rows(w.tokens, w.row_slices)
+    ref = G.oracle_mlp_fwd(inp, w.act, rows=rows)
+    G.assert_parity(out["Z"].cpu()[rows], ref["Z"], "Z rows")
+    G.assert_parity(out["U"].cpu()[rows], ref["U"], "U rows")
+    one = G.run_mlp_fwd(T.plan_for(w, n_row_slices=1, n_col_slices=1), inp, save_u=False, handoff=False)
+    assert torch.equal(one["Z"], out["Z"])
+
+
+@pytest.mark.parametrize("key", ["llama2_13b_layer", "llama3_70b_layer"])
+def test_full_layer_workload(key):
+    w = synth.WORKLOADS[key]
+    _print_case("full_layer", key=key)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    rows = G.sample_rows(w.tokens, w.row_slices, per_slice=4)
+    # forward
+    fo = G.run_mlp_fwd(plan, inp)
+    ref = G.oracle_mlp_fwd(inp, w.act, rows=rows)
+    G.assert_parity(fo["Z"].cpu()[rows], ref["Z"], "mlp Z rows")
+    assert torch.equal(fo["Zh"], fo["Z"])
+    del fo
+    ao = G.run_attn_fwd(plan, inp)
+    ra = L.attnproj_fwd(f64(inp["X"][rows]), f64(inp["Wqkv"]), None, f64(inp["C"][rows]), f64(inp["Wo"]))
+    G.assert_parity(ao["QKV"].cpu()[rows], ra["QKV"], "QKV rows")
+    G.assert_parity(ao["Z"].cpu()[rows], ra["Z"], "attn Z rows")
+    assert torch.equal(ao["Zh"], ao["Z"])
+    del ao
+    # MLP backward: dX on sampled rows; weight gradients on sampled FFN columns (a column subset of
+    # the shard is itself a shard, so the oracle runs on it with all tokens)
+    bo = G.run_mlp_bwd(plan, inp, with_bias=False)
+    assert torch.equal(bo["dXh"], bo["dX"])
+    rb = L.mlp_bwd(f64(inp["X_mlp"][rows]), f64(inp["W1"]), f64(inp["W2"]), f64(inp["U_saved"][rows]),
+                   f64(inp["dY"][rows]), w.act)
+    G.assert_parity(bo["dX"].cpu()[rows], rb["dX"], "dX rows")
+    Fp = w.ffn_shard
+    J = G.sample_cols(Fp, 6)
+    rows1 = np.concatenate([J, Fp + J])
+    rj = L.mlp_bwd(f64(inp["X_mlp"]), f64(inp["W1"][rows1]), f64(inp["W2"][:, J]),
+                   f64(inp["U_saved"][:, rows1]), f64(inp["dY"]), w.act)
+    G.assert_parity(bo["dW1"].cpu()[rows1], rj["dW1"], "dW1 rows")
+    G.assert_parity(bo["dW2"].cpu()[:, J], rj["dW2"], "dW2 cols")
+    del bo
+    # attention-projection backward
+    go = G.run_attn_bwd(plan, inp, with_bias=False)
+    assert torch.equal(go["dXh"], go["dX"])
+    rg = L.attnproj_bwd(f64(inp["X"][rows]), f64(inp["Wqkv"]), f64(inp["dQKV"][rows]), f64(inp["C"][rows]),
+                        f64(inp["Wo"]), f64(inp["dY_attn"][rows]))
+    G.assert_parity(go["dX"].cpu()[rows], rg["dX"], "attn dX rows")
+    G.assert_parity(go["dC"].cpu()[rows], rg["dC"], "dC rows")
+    # weight gradients on sampled output rows: the oracle on that subset of the projections
+    Jq = G.sample_cols(w.qkv_width, 6)
+    Jh = G.sample_cols(w.hidden, 6)
+    rs = L.attnproj_bwd(f64(inp["X"]), f64(inp["Wqkv"][Jq]), f64(inp["dQKV"][:, Jq]), f64(inp["C"]),
+                        f64(inp["Wo"][Jh]), f64(inp["dY_attn"][:, Jh]))
+    G.assert_parity(go["dWqkv"].cpu()[Jq], rs["dWqkv"], "dWqkv rows")
+    G.assert_parity(go["dWo"].cpu()[Jh], rs["dWo"], "dWo rows")
