@@ -48,6 +48,10 @@ struct GemmArgs {
 // Queue one GEMM on `stream`. Returns hipSuccess or the launch error.
 hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream);
 
+// A one-wave kernel that does nothing. Queued on a stream after DMA-engine copies it completes only
+// after them (stream order), so an event recorded after it marks the copies' completion.
+hipError_t launch_fence(hipStream_t stream);
+
 constexpr int kColsumChunkRows = 256;
 
 // Column sums of a bf16 [M][N] matrix into fp32 out[N] (out += sums when accumulate), in a fixed

@@ -124,6 +124,13 @@ struct Schedule {
   Runtime* rt;
   hipStream_t caller;
   bool serial;
+  uint32_t copied = 0;  // bit k: copy stream k received a copy in this call (bit 31: caller stream)
+
+  tpslice_status_t fence(hipStream_t s) {
+    hipError_t e = launch_fence(s);
+    if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "fence launch: %s", hipGetErrorString(e));
+    return TPSLICE_OK;
+  }
 
   hipStream_t worker(int i) const { return serial ? caller : rt->workers[i % p->S]; }
   int worker_id(int i) const { return serial ? -1 : i % p->S; }
@@ -138,10 +145,12 @@ struct Schedule {
     return TPSLICE_OK;
   }
 
-  // Run `fn` (which queues work on `s`) between two timing events when tracing.
+  // Run `fn` (which queues work on `s`) between two timing events when tracing. A traced copy is
+  // closed by a fence kernel so that its end event waits for the DMA engine.
   template <class F>
   tpslice_status_t traced(hipStream_t s, int stream_id, int kind, int step, int slice, int piece, double flops,
                           double bytes, F&& fn) {
+    if (kind == TPSLICE_TRACE_COPY) copied |= stream_id < 0 ? (1u << 31) : (1u << (stream_id - p->S));
     if (!p->trace) return fn();
     TraceSlot t{};
     t.rec.kind = kind; t.rec.step = step; t.rec.slice = slice; t.rec.piece = piece;
@@ -149,6 +158,7 @@ struct Schedule {
     TPS_TRY_(trace_event(&t.ev0));
     TPS_HIP(hipEventRecord(rt->tpool[t.ev0], s));
     TPS_TRY_(fn());
+    if (kind == TPSLICE_TRACE_COPY) TPS_TRY_(fence(s));
     TPS_TRY_(trace_event(&t.ev1));
     TPS_HIP(hipEventRecord(rt->tpool[t.ev1], s));
     rt->slots.push_back(t);
@@ -172,13 +182,19 @@ struct Schedule {
     return TPSLICE_OK;
   }
 
+  // The caller's stream waits for every worker and copy stream. DMA-engine copies are closed by a
+  // fence kernel first, so that the join event covers their completion.
   tpslice_status_t join() {
-    if (serial) return TPSLICE_OK;
+    if (serial) {
+      if (copied) TPS_TRY_(fence(caller));
+      return TPSLICE_OK;
+    }
     for (int k = 0; k < p->S; ++k) {
       TPS_HIP(hipEventRecord(rt->join_w[k], rt->workers[k]));
       TPS_HIP(hipStreamWaitEvent(caller, rt->join_w[k], 0));
     }
     for (int k = 0; k < p->E; ++k) {
+      if (copied & (1u << k)) TPS_TRY_(fence(rt->copiers[k]));
       TPS_HIP(hipEventRecord(rt->join_c[k], rt->copiers[k]));
       TPS_HIP(hipStreamWaitEvent(caller, rt->join_c[k], 0));
     }
@@ -320,7 +336,8 @@ extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, con
                                             size_t ws_bytes, void* stream) {
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
-  TPS_REQ(X); TPS_REQ(W1); TPS_REQ(W2); TPS_REQ(Z);
+  TPS_REQ(W1); TPS_REQ(W2);
+  if (p->M > 0) { TPS_REQ(X); TPS_REQ(Z); } else { TPS_OPT(X); TPS_OPT(Z); }
   TPS_OPT(b1); TPS_OPT(U_save); TPS_OPT(Z_handoff);
   const MlpFwdWs L = mlp_fwd_ws(p);
   TPS_TRY(check_ws(ws, ws_bytes, L.total));
@@ -357,7 +374,9 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
   (void)ws; (void)ws_bytes;
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   if (p->qh == 0) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads (n_heads = 0)");
-  TPS_REQ(X); TPS_REQ(Wqkv); TPS_REQ(QKV); TPS_REQ(C); TPS_REQ(Wo); TPS_REQ(Z);
+  TPS_REQ(Wqkv); TPS_REQ(Wo);
+  if (p->M > 0) { TPS_REQ(X); TPS_REQ(QKV); TPS_REQ(C); TPS_REQ(Z); }
+  else { TPS_OPT(X); TPS_OPT(QKV); TPS_OPT(C); TPS_OPT(Z); }
   TPS_OPT(bqkv); TPS_OPT(Z_handoff);
   if (p->M == 0) return TPSLICE_OK;
   Runtime* rt = nullptr;
@@ -387,7 +406,9 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
                                             size_t ws_bytes, void* stream) {
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
-  TPS_REQ(X); TPS_REQ(W1); TPS_REQ(W2); TPS_REQ(U); TPS_REQ(dY); TPS_REQ(dX); TPS_REQ(dW1); TPS_REQ(dW2);
+  TPS_REQ(W1); TPS_REQ(W2); TPS_REQ(dW1); TPS_REQ(dW2);
+  if (p->M > 0) { TPS_REQ(X); TPS_REQ(U); TPS_REQ(dY); TPS_REQ(dX); }
+  else { TPS_OPT(X); TPS_OPT(U); TPS_OPT(dY); TPS_OPT(dX); }
   TPS_OPT(db1); TPS_OPT(dX_handoff);
   if (accumulate != 0 && accumulate != 1) return fail(TPSLICE_ERR_INVALID, "accumulate must be 0 or 1");
   const MlpBwdWs L = mlp_bwd_ws(p);
@@ -437,8 +458,9 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   if (p->qh == 0) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads (n_heads = 0)");
-  TPS_REQ(X); TPS_REQ(Wqkv); TPS_REQ(dQKV); TPS_REQ(C); TPS_REQ(Wo); TPS_REQ(dY); TPS_REQ(dX); TPS_REQ(dC);
-  TPS_REQ(dWqkv); TPS_REQ(dWo);
+  TPS_REQ(Wqkv); TPS_REQ(Wo); TPS_REQ(dWqkv); TPS_REQ(dWo);
+  if (p->M > 0) { TPS_REQ(X); TPS_REQ(dQKV); TPS_REQ(C); TPS_REQ(dY); TPS_REQ(dX); TPS_REQ(dC); }
+  else { TPS_OPT(X); TPS_OPT(dQKV); TPS_OPT(C); TPS_OPT(dY); TPS_OPT(dX); TPS_OPT(dC); }
   TPS_OPT(dbqkv); TPS_OPT(dX_handoff);
   if (accumulate != 0 && accumulate != 1) return fail(TPSLICE_ERR_INVALID, "accumulate must be 0 or 1");
   const AttnBwdWs L = attn_bwd_ws(p);

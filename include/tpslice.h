@@ -14,7 +14,9 @@
  *
  * Conventions for every entry point
  *   - Device pointers are plain `void*` into GPU memory owned by the caller; the library never frees
- *     or keeps them beyond the call's stream work. 16-byte alignment is required.
+ *     or keeps them beyond the call's stream work. 16-byte alignment is required. Tensors with a
+ *     token dimension may be NULL when the plan's token count is 0 (an empty batch); the weight
+ *     gradients are then set to zero (accumulate = 0) or left as they are (accumulate = 1).
  *   - bf16 tensors are row-major and contiguous. Weights use the [out_features][in_features] layout
  *     of a linear layer:  W1 [N1][h] (N1 = F' for GeLU, 2F' for SwiGLU with rows [gate | up]),
  *     W2 [h][F'], Wqkv [(q+2kv)d][h] with rows [Q | K | V], Wo [h][q d].

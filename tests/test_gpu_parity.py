@@ -246,3 +246,23 @@ def test_full_layer_workload(key):
                         f64(inp["Wo"][Jh]), f64(inp["dY_attn"][:, Jh]))
     G.assert_parity(go["dWqkv"].cpu()[Jq], rs["dWqkv"], "dWqkv rows")
     G.assert_parity(go["dWo"].cpu()[Jh], rs["dWo"], "dWo rows")
+
+
+@pytest.mark.parametrize("copy_blit", [False, True])
+def test_handoff_complete_when_caller_stream_passes(copy_blit):
+    """Work queued on the caller's stream after the call sees the finished hand-off copy (no
+    device-wide synchronization in between)."""
+    w = synth.WORKLOADS["gpt3_2.7b_mlp"]
+    _print_case("join", key=w.key, copy_blit=copy_blit)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w, copy_blit=copy_blit)
+    X, W1, b1, W2 = (G.dev(inp[k]) for k in ("X_mlp", "W1", "b1", "W2"))
+    i = plan.info
+    Z = torch.empty((i.tokens, i.hidden), dtype=torch.bfloat16, device="cuda")
+    Zh = torch.empty_like(Z)
+    for rep in range(3):
+        Zh.fill_(float("nan"))
+        plan.mlp_fwd(X, W1, b1, W2, Z, None, Zh)
+        snap = Zh.clone()          # queued on the caller stream right behind the call
+        torch.cuda.synchronize()
+        assert torch.equal(snap, Z), f"rep {rep}: hand-off not complete at the join"
