@@ -1,9 +1,13 @@
 // bf16 MFMA GEMM family for gfx950 (MI355X) with fused layer epilogues.
 //
-// Block tile 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave 128 x 128 made of
-// 8 x 8 v_mfma_f32_16x16x32_bf16 tiles (fp32 accumulators). Operand tiles are staged global ->
-// VGPR -> LDS (two LDS stages, 128 KB) with 16-byte XOR swizzles:
-//   * an operand read along k ("KC") is kept as [rows][64 k], fragments read with ds_read_b128;
+// Block tile 256 x 256 x 64, 512 threads = 8 waves (two per SIMD, so one wave's waits hide under
+// the other's MFMAs) in a 2 x 4 grid; each wave owns 128 x 64 outputs as 8 x 4
+// v_mfma_f32_16x16x32_bf16 tiles with fp32 accumulators. Operand tiles go global -> LDS by direct
+// loads (buffer_load_dwordx4 ... lds) into two LDS stages (128 KB): block k+1 loads while block k
+// is multiplied. 16-byte XOR swizzles keep LDS traffic at full rate (chosen by measuring each
+// candidate pattern's LDS throughput on gfx950):
+//   * an operand read along k ("KC") is kept as [rows][64 k] (128-byte rows), fragments read
+//     with ds_read_b128;
 //   * an operand read across k ("NC", rows of k in memory) is kept as [64 k][256 cols] and its
 //     fragments come from ds_read_b64_tr_b16, which transposes 16-bit elements across each
 //     16-lane group: result element v of lane i is element i%4 of the 8 bytes addressed by
@@ -11,14 +15,16 @@
 // The MFMA is issued with the B fragment first, so each lane ends up holding four consecutive
 // output columns of one row: lane l, register v of tile (im, in) is
 //   C[row0 + 16 im + l%16][col0 + 16 in + 4 (l/16) + v].
-// Global loads use buffer resources whose range check returns zeros outside the operand, so
-// ragged edges (rows, columns, k) need no separate code path.
+// Loads go through buffer resources: for tiles wholly inside the operands the k offset rides in
+// the scalar offset (no per-lane work); edge tiles and the last partial k block use per-chunk
+// offsets and the range check, which returns zeros outside the operand.
 // Tiles are numbered so that each XCD (workgroups are dispatched round-robin over the 8 XCDs)
 // receives a contiguous run of the grouped tile order, which keeps the operand rows and columns a
 // run shares in that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "gemm.hpp"
 
@@ -32,10 +38,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
-constexpr int kTileBytes = 256 * 64 * 2;        // one operand tile, 32 KB
+constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 512;
+constexpr int kTileBytes = 256 * kBK * 2;       // one operand tile, 16 KB
 constexpr int kStageBytes = 2 * kTileBytes;     // A + B
-constexpr int kLdsBytes = 2 * kStageBytes;      // two stages, 128 KB
+constexpr int kStages = 131072 / kStageBytes;   // ring of LDS stages
+constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KB
+constexpr int kLoadsPerBlock = kTileBytes / 1024 / 8 * 2;  // buffer_load ... lds per wave per k block
 constexpr int kGroupM = 4;                      // tile rows per group of the tile order
 constexpr uint32_t kOob = 0xFFFFF000u;          // buffer offset that reads as zero: operands are
                                                 // smaller than 4 GiB - 4 KiB
@@ -47,8 +55,16 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// 16-byte chunk swizzles (see file comment): KC rows of 128 B, NC rows of 512 B.
-__device__ inline int swz_kc(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+// 16-byte chunk swizzles, chosen by measurement on gfx950 (LDS read throughput of each candidate
+// lane pattern): KC rows of 64 B (4 chunks) XOR the chunk with 2*(r1 ^ r3), which lets the
+// fragment reads (16 consecutive rows per 16-lane group) run at full LDS rate, while the plain
+// layout and the other simple XOR forms run at half rate; NC rows of 512 B XOR with
+// (k & 3) << 1 | (k >> 3 & 1) << 3 for the transpose reads.
+constexpr int kRowBytes = kBK * 2, kChunks = kBK / 8, kRowsPerRun = 1024 / kRowBytes;
+__device__ inline int swz_kc(int row) {
+  if constexpr (kBK == 32) return (((row >> 1) ^ (row >> 3)) & 1) << 1;
+  else return ((row >> 1) & 7) ^ ((row & 1) << 2);
+}
 __device__ inline int swz_nc(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
 __device__ inline float bf2f(unsigned short b) { return __uint_as_float(uint32_t(b) << 16); }
@@ -77,21 +93,23 @@ __device__ inline void store_bf16x4(void* base, int64_t elem, float a, float b, 
 }
 
 // ------------------------------------------------------------------------------ operand staging
-// Each operand tile (32 KB) is filled by direct global -> LDS loads (buffer_load_dwordx4 ... lds):
-// one load instruction writes 64 consecutive 16-byte LDS slots, lane l into slot l. A wave owns
-// eight 1 KB runs of the tile; each lane loads the global chunk that belongs in its slot, so the
-// swizzled layout comes from the choice of global address.
-//   KC tile [256 rows][64 k]: run s holds rows 8s..8s+7; lane l -> row 8s + l/8, physical chunk l%8.
-//   NC tile [64 k][256]     : run s holds k rows 2s, 2s+1; lane l -> k 2s + l/32, physical chunk l%32.
+// Each operand tile (16 KB = 16 runs of 1 KB) is filled by direct global -> LDS loads
+// (buffer_load_dwordx4 ... lds): one load instruction writes 64 consecutive 16-byte LDS slots,
+// lane l into slot l. Each of the 8 waves owns two runs of each tile; each lane loads the global
+// chunk that belongs in its slot, so the swizzled layout comes from the choice of global address.
+//   KC tile [256 rows][32 k]: run s holds rows 16s..16s+15; lane l -> row 16s + l/4, slot chunk l%4.
+//   NC tile [32 k][256]     : run s holds k rows 2s, 2s+1; lane l -> k 2s + l/32, slot chunk l%32.
+constexpr int kRuns = kTileBytes / 1024 / 8;  // runs per wave per operand tile
+
 struct KcLoader {
-  uint32_t off[8];   // byte offset of the lane's chunk at k0 = 0
-  uint32_t kel[8];   // k index (element) of the lane's chunk at k0 = 0
-  uint32_t valid;    // bit j: the chunk's row lies inside the operand
+  uint32_t off[kRuns];   // byte offset of the lane's chunk at k0 = 0
+  uint32_t kel[kRuns];   // k index (element) of the lane's chunk at k0 = 0
+  uint32_t valid;        // bit j: the chunk's row lies inside the operand
   __device__ void init(int wave, int lane, int64_t ld, int row0, int row_limit, bool dual, int64_t half) {
     valid = 0;
-    for (int j = 0; j < 8; ++j) {
-      const int r = (wave * 8 + j) * 8 + (lane >> 3);  // tile row
-      const int ch = (lane & 7) ^ swz_kc(r);          // logical chunk (k / 8)
+    for (int j = 0; j < kRuns; ++j) {
+      const int r = (wave * kRuns + j) * kRowsPerRun + lane / kChunks;  // tile row
+      const int ch = (lane % kChunks) ^ swz_kc(r);                      // logical chunk (k / 8)
       int li = r, gro;
       if (dual) {
         li = r & 127;
@@ -106,24 +124,30 @@ struct KcLoader {
     }
   }
   __device__ void issue(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int K) const {
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kRuns; ++j) {
       const bool ok = ((valid >> j) & 1) && int(kel[j]) + k0 < K;
       const uint32_t o = ok ? off[j] + uint32_t(k0) * 2 : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * 8 + j) * 1024), 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * kRuns + j) * 1024), 16, o, 0, 0, 0);
     }
+  }
+  // every chunk in range: k advances through the scalar offset, no per-lane arithmetic
+  __device__ void issue_fast(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0) const {
+    for (int j = 0; j < kRuns; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * kRuns + j) * 1024), 16, off[j],
+                                               uint32_t(k0) * 2, 0, 0);
   }
 };
 
 struct NcLoader {
-  uint32_t col_off[8];  // byte offset of the lane's chunk within a k row
-  uint32_t krow[8];     // tile k row of the lane's chunk
-  uint32_t valid;       // bit j: the chunk's columns lie inside the operand
+  uint32_t col_off[kRuns];  // byte offset of the lane's chunk within a k row
+  uint32_t krow[kRuns];     // tile k row of the lane's chunk
+  uint32_t valid;           // bit j: the chunk's columns lie inside the operand
   uint32_t ld_bytes;
   __device__ void init(int wave, int lane, int64_t ld, int col0, int col_limit) {
     valid = 0;
     ld_bytes = uint32_t(ld * 2);
-    for (int j = 0; j < 8; ++j) {
-      const int k = (wave * 8 + j) * 2 + (lane >> 5);
+    for (int j = 0; j < kRuns; ++j) {
+      const int k = (wave * kRuns + j) * 2 + (lane >> 5);
       const int ch = (lane & 31) ^ swz_nc(k);
       const int c = col0 + ch * 8;
       const bool ok = c < col_limit;
@@ -133,25 +157,40 @@ struct NcLoader {
     }
   }
   __device__ void issue(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int K) const {
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kRuns; ++j) {
       const int k = k0 + int(krow[j]);
       const bool ok = ((valid >> j) & 1) && k < K;
       const uint32_t o = ok ? uint32_t(k) * ld_bytes + col_off[j] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * 8 + j) * 1024), 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * kRuns + j) * 1024), 16, o, 0, 0, 0);
     }
+  }
+  __device__ void issue_fast(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0) const {
+    for (int j = 0; j < kRuns; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * kRuns + j) * 1024), 16,
+                                               krow[j] * ld_bytes + col_off[j], uint32_t(k0) * ld_bytes, 0, 0);
   }
 };
 
-// ------------------------------------------------------------------------------ fragment reads
-// KC fragment: lane l gets operand[rb + l%16][32 kk + 8 (l/16) + 0..7].
-__device__ inline bf16x8 frag_kc(const char* tile, int rb, int kk, int lane) {
-  const int row = rb + (lane & 15);
-  const int ch = kk * 4 + (lane >> 4);
-  return *reinterpret_cast<const bf16x8*>(tile + row * 128 + ((ch ^ swz_kc(row)) << 4));
+// Wait until at most N of this wave's buffer loads are outstanding, then meet the other waves.
+// Pinned in place (scheduling barriers) so that MFMA work is not moved across it.
+template <int N>
+__device__ inline void wait_loads_and_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// NC fragment: same element assignment as frag_kc, from a [64 k][256] tile, cb = first column.
-__device__ inline bf16x8 frag_nc(const char* tile, int cb, int kk, int lane) {
+
+// ------------------------------------------------------------------------------ fragment reads
+// KC fragment: lane l gets operand[rb + l%16][8 (l/16) + 0..7].
+__device__ inline bf16x8 frag_kc(const char* tile, int rb, int lane, int kk = 0) {
+  const int row = rb + (lane & 15);
+  const int ch = kk * 4 + (lane >> 4);
+  return *reinterpret_cast<const bf16x8*>(tile + row * kRowBytes + ((ch ^ swz_kc(row)) << 4));
+}
+
+// NC fragment: same element assignment as frag_kc, from a [32 k][256] tile, cb = first column.
+__device__ inline bf16x8 frag_nc(const char* tile, int cb, int lane, int kk = 0) {
   const int g = lane >> 4, v = (lane & 15) >> 2, q = lane & 3;
   const int chunk = (cb >> 3) + (q >> 1);
   const int k0 = kk * 32 + 8 * g + v;
@@ -171,7 +210,7 @@ __device__ inline bf16x8 frag_nc(const char* tile, int cb, int kk, int lane) {
 // (SwiGLU: x = gate sums, y = up sums).
 template <int EPI>
 __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, const float (&x)[4],
-                                                    const float (&y)[4]) {
+                                          const float (&y)[4]) {
   const int64_t mr = m;
   float o[4];
   if constexpr (EPI == kEpiF32) {
@@ -233,19 +272,25 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, const
 }
 
 // ------------------------------------------------------------------------------------- kernel
+// 8 waves (2 per SIMD, so one wave's waits hide under the other's MFMAs) in a 2 (m) x 4 (n) grid;
+// wave tile 128 x 64 = 8 x 4 MFMA tiles, 128 fp32 accumulators per lane.
+constexpr int kWavesN = 4;
+constexpr int kFM = 8, kFN = 4;  // MFMA tiles per wave along m and n
+
 template <int LAYOUT, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   constexpr bool kADirect = LAYOUT != kWgrad;   // A read along k
   constexpr bool kBDirect = LAYOUT == kFwd;     // B read along k
   constexpr bool kDual = EPI == kEpiSwiglu;     // B tile = 128 gate rows + 128 up rows
   constexpr int kOutBN = kDual ? kBN / 2 : kBN; // output columns per block
+  constexpr int kWaveN = kOutBN / kWavesN;      // output columns per wave (64, SwiGLU 32)
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: LDS addresses stay scalar
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
 
   // ---- tile coordinates: contiguous runs per XCD, grouped order inside
   const int T = g.tiles_m * g.tiles_n;
@@ -273,21 +318,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   if constexpr (kBDirect) bK.init(wave, lane, g.ldb, n0, g.N, kDual, g.half);
   else bN.init(wave, lane, g.ldb, n0, g.N);
 
-  f32x4 acc[8][8];
+  // B-tile column of fragment `in` (SwiGLU: fragments 0, 1 gate, 2, 3 up of the same outputs)
+  auto bcol = [&](int in) {
+    if constexpr (kDual) return (in < kFN / 2 ? 0 : 128) + wn * kWaveN + 16 * (in % (kFN / 2));
+    else return wn * kWaveN + 16 * in;
+  };
+  // output column of accumulator column `in` (SwiGLU: of the gate half)
+  auto ocol = [&](int in) {
+    if constexpr (kDual) return n0 + wn * kWaveN + 16 * (in % (kFN / 2));
+    else return n0 + wn * kWaveN + 16 * in;
+  };
+
+  f32x4 acc[kFM][kFN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kFM; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (EPI == kEpiF32) {
     if (g.accumulate) {
       const float* C = reinterpret_cast<const float*>(g.C);
 #pragma unroll
-      for (int im = 0; im < 8; ++im) {
+      for (int im = 0; im < kFM; ++im) {
         const int m = m0 + wm * 128 + 16 * im + (lane & 15);
 #pragma unroll
-        for (int in = 0; in < 8; ++in) {
-          const int n = n0 + wn * 128 + 16 * in + 4 * (lane >> 4);
+        for (int in = 0; in < kFN; ++in) {
+          const int n = ocol(in) + 4 * (lane >> 4);
           if (m < g.M && n < g.N) acc[im][in] = *reinterpret_cast<const f32x4*>(C + int64_t(m) * g.ldc + n);
         }
       }
@@ -296,92 +352,96 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 
   const int nk = (g.K + kBK - 1) / kBK;
 
+  // block-uniform: every row and column of this tile lies inside the operands
+  const bool interior = (m0 + kBM <= g.M) && (n0 + kOutBN <= g.N);
   auto issue = [&](int kb) {
-    char* a_tile = smem + (kb & 1) * kStageBytes;
+    char* a_tile = smem + (kb % kStages) * kStageBytes;
     char* b_tile = a_tile + kTileBytes;
     const int k0 = kb * kBK;
-    if constexpr (kADirect) aK.issue(rsA, a_tile, wave, k0, g.K); else aN.issue(rsA, a_tile, wave, k0, g.K);
-    if constexpr (kBDirect) bK.issue(rsB, b_tile, wave, k0, g.K); else bN.issue(rsB, b_tile, wave, k0, g.K);
+    if (interior && k0 + kBK <= g.K) {
+      if constexpr (kADirect) aK.issue_fast(rsA, a_tile, wave, k0); else aN.issue_fast(rsA, a_tile, wave, k0);
+      if constexpr (kBDirect) bK.issue_fast(rsB, b_tile, wave, k0); else bN.issue_fast(rsB, b_tile, wave, k0);
+    } else {
+      if constexpr (kADirect) aK.issue(rsA, a_tile, wave, k0, g.K); else aN.issue(rsA, a_tile, wave, k0, g.K);
+      if constexpr (kBDirect) bK.issue(rsB, b_tile, wave, k0, g.K); else bN.issue(rsB, b_tile, wave, k0, g.K);
+    }
   };
-  auto frags = [&](int kb, int kk, bf16x8 (&af)[8], bf16x8 (&bf)[8]) {
-    const char* a_tile = smem + (kb & 1) * kStageBytes;
+  auto frags = [&](int kb, bf16x8 (&af)[kFM], bf16x8 (&bf)[kFN], int kk = 0) {
+    const char* a_tile = smem + (kb % kStages) * kStageBytes;
     const char* b_tile = a_tile + kTileBytes;
 #pragma unroll
-    for (int in = 0; in < 8; ++in) {
-      int cbase;
-      if constexpr (kDual) cbase = (in < 4 ? 0 : 128) + wn * 64 + 16 * (in & 3);
-      else cbase = wn * 128 + 16 * in;
-      if constexpr (kBDirect) bf[in] = frag_kc(b_tile, cbase, kk, lane);
-      else bf[in] = frag_nc(b_tile, cbase, kk, lane);
+    for (int in = 0; in < kFN; ++in) {
+      if constexpr (kBDirect) bf[in] = frag_kc(b_tile, bcol(in), lane, kk);
+      else bf[in] = frag_nc(b_tile, bcol(in), lane, kk);
     }
 #pragma unroll
-    for (int im = 0; im < 8; ++im) {
+    for (int im = 0; im < kFM; ++im) {
       const int rbase = wm * 128 + 16 * im;
-      if constexpr (kADirect) af[im] = frag_kc(a_tile, rbase, kk, lane);
-      else af[im] = frag_nc(a_tile, rbase, kk, lane);
+      if constexpr (kADirect) af[im] = frag_kc(a_tile, rbase, lane, kk);
+      else af[im] = frag_nc(a_tile, rbase, lane, kk);
     }
   };
-  auto mfmas = [&](const bf16x8 (&af)[8], const bf16x8 (&bf)[8]) {
+  auto mfmas = [&](const bf16x8 (&af)[kFM], const bf16x8 (&bf)[kFN]) {
 #pragma unroll
-    for (int im = 0; im < 8; ++im)
+    for (int im = 0; im < kFM; ++im)
 #pragma unroll
-      for (int in = 0; in < 8; ++in)
+      for (int in = 0; in < kFN; ++in)
         acc[im][in] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[in], af[im], acc[im][in], 0, 0, 0);
   };
+  // wait for block `kb` to land in LDS, given how many later blocks have been issued
+  constexpr int kAhead = kStages - 1;
+  auto wait_block = [&](int kb) {
+    const int later = min(nk - 1, kb + kAhead - 1) - kb;  // blocks issued after kb
+    if constexpr (kAhead >= 3) {
+      if (later >= 2) { wait_loads_and_barrier<2 * kLoadsPerBlock>(); return; }
+    }
+    if (later >= 1) wait_loads_and_barrier<kLoadsPerBlock>();
+    else wait_loads_and_barrier<0>();
+  };
 
-  bf16x8 a0[8], b0[8], a1[8], b1[8];
-  if (nk > 0) {
-    issue(0);
-    __syncthreads();
-    frags(0, 0, a0, b0);
-  }
+  if (nk > 0)
+    for (int kb = 0; kb < min(nk, kAhead); ++kb) issue(kb);
   for (int kb = 0; kb < nk; ++kb) {
-    const bool more = kb + 1 < nk;
-    if (more) issue(kb + 1);
-    frags(kb, 1, a1, b1);
-    mfmas(a0, b0);
-    __syncthreads();  // stage kb+1 landed in LDS; every wave is done reading stage kb
-    if (more) frags(kb + 1, 0, a0, b0);
-    mfmas(a1, b1);
+    wait_block(kb);
+    if (kb + kAhead < nk) issue(kb + kAhead);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 32; ++kk) {
+      bf16x8 af[kFM], bf[kFN];
+      frags(kb, af, bf, kk);
+      mfmas(af, bf);
+    }
   }
   __syncthreads();
 
   // ---- epilogue: per 16-row band, the wave parks its sums in LDS and re-reads them as whole row
   // segments, so global loads and stores of the epilogue are contiguous.
-  constexpr int kEpLd = 132;  // floats per parked row (128 + 4 padding against bank conflicts)
+  constexpr int kEpLd = 136;  // floats per parked row (full-rate LDS writes, measured)
   float* park = reinterpret_cast<float*>(smem) + wave * 16 * kEpLd;
   const int prow = lane & 15, pcol = 4 * (lane >> 4);
 #pragma unroll
-  for (int im = 0; im < 8; ++im) {
+  for (int im = 0; im < kFM; ++im) {
 #pragma unroll
-    for (int in = 0; in < 8; ++in)
+    for (int in = 0; in < kFN; ++in)
       *reinterpret_cast<f32x4*>(park + prow * kEpLd + 16 * in + pcol) = acc[im][in];
     __syncthreads();
     const int mbase = m0 + wm * 128 + 16 * im;
-    if constexpr (kDual) {
-      // columns 0..63 of a parked row are gate sums, 64..127 up sums of the same outputs
+    // a parked row holds the wave's 64 accumulator columns (SwiGLU: 32 gate then 32 up)
+    constexpr int kOutCols = kDual ? 32 : 64;
+    constexpr int kLanesPerRow = kOutCols / 4;
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;
 #pragma unroll 1
-      for (int p = 0; p < 4; ++p) {
-        const int r = p * 4 + (lane >> 4);
-        const int c = 4 * (lane & 15);
-        const int m = mbase + r, n = n0 + wn * 64 + c;
-        if (m < g.M && n < g.N) {
-          const f32x4 xg = *reinterpret_cast<const f32x4*>(park + r * kEpLd + c);
-          const f32x4 xu = *reinterpret_cast<const f32x4*>(park + r * kEpLd + 64 + c);
-          const float x[4] = {xg[0], xg[1], xg[2], xg[3]};
-          const float y[4] = {xu[0], xu[1], xu[2], xu[3]};
+    for (int p = 0; p < 16 / kRowsPerPass; ++p) {
+      const int r = p * kRowsPerPass + lane / kLanesPerRow;
+      const int c = 4 * (lane % kLanesPerRow);
+      const int m = mbase + r, n = n0 + wn * kWaveN + c;
+      if (m < g.M && n < g.N) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(park + r * kEpLd + c);
+        const float x[4] = {xv[0], xv[1], xv[2], xv[3]};
+        if constexpr (kDual) {
+          const f32x4 yv = *reinterpret_cast<const f32x4*>(park + r * kEpLd + 32 + c);
+          const float y[4] = {yv[0], yv[1], yv[2], yv[3]};
           epilogue4<EPI>(g, m, n, x, y);
-        }
-      }
-    } else {
-#pragma unroll 1
-      for (int p = 0; p < 8; ++p) {
-        const int r = p * 2 + (lane >> 5);
-        const int c = 4 * (lane & 31);
-        const int m = mbase + r, n = n0 + wn * 128 + c;
-        if (m < g.M && n < g.N) {
-          const f32x4 xv = *reinterpret_cast<const f32x4*>(park + r * kEpLd + c);
-          const float x[4] = {xv[0], xv[1], xv[2], xv[3]};
+        } else {
           epilogue4<EPI>(g, m, n, x, x);
         }
       }
@@ -412,6 +472,8 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* partials
   for (int c = 0; c < nchunks; ++c) s += partials[int64_t(c) * N + n];
   out[n] = s;
 }
+
+__global__ void fence_kernel() {}
 
 template <int L, int E>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
@@ -453,6 +515,11 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream) {
     case kWgrad * 8 + kEpiF32: return launch_one<kWgrad, kEpiF32>(g, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_fence(hipStream_t stream) {
+  hipLaunchKernelGGL(fence_kernel, dim3(1), dim3(64), 0, stream);
+  return hipGetLastError();
 }
 
 size_t colsum_partials_bytes(int32_t M, int32_t N) {
