@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the sliced tensor-parallel layer shard on one MI355X.
 
-A step is one pass of the whole path over one batch: for a forward MLP workload one
-tpslice_mlp_fwd call (column-parallel up-projection + fused activation, row-parallel
-down-projection in pieces, each finished piece handed off by a DMA copy on a side stream); for a
-layer workload the attention projections and the MLP, forward and backward. Inputs are synthetic,
-seeded, resident in HBM before timing starts.
+A step is one pass of the whole path over one batch. For a forward MLP workload: one
+tpslice_mlp_fwd call (column-parallel up-projection with the fused activation, row-parallel
+down-projection in pieces, each finished piece handed off by a DMA-engine copy on a side stream).
+For a layer workload: the attention projections and the MLP, forward and backward. Steps are
+chained the way consecutive layers are (each call reads the previous call's hand-off buffer) and
+the plan pipelines the hand-off: row slice i of a call waits only for row slice i of the previous
+call's hand-off, so a call's last copies overlap the next call's first products. Inputs are
+synthetic, seeded, and resident in HBM before timing starts.
 
-Prints ONE JSON line: TFLOP/s (algorithmic 2*M*N*K flops of every product / time), the fraction of
-the dense bf16 MFMA peak, the fraction of hand-off copy time hidden behind compute, the roofline of
-the dominant kernel (per-launch HIP-event times on the stream each launch ran on, over the timed
-region) and the fp64 CPU oracle timed on the host (a baseline, not a target).
+Prints ONE JSON line: TFLOP/s (algorithmic 2*M*N*K flops of every product / wall time), the
+fraction of the dense bf16 MFMA peak, the fraction of hand-off copy time hidden behind compute
+(steady state, and for an isolated call), the roofline of the dominant kernel (its launches timed
+with HIP events on the streams they ran on, over the timed region), and the fp64 CPU oracle timed
+on the host's cores (a baseline, not a target).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
 """
@@ -37,117 +41,138 @@ def parse():
     ap.add_argument("--copy-streams", type=int, default=0, help="copy streams (0 = plan default)")
     ap.add_argument("--copy-blit", action="store_true", help="hand-off by copy kernel instead of DMA")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle time")
-    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="finish with plain 256 MiB device copies (counter calibration for profiles)")
     return ap.parse_args()
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CALIB_BYTES = 256 << 20
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, if that
+    summary was taken on the current GEMM source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gemm_kernel_{workload}_traffic.txt")
+    src = os.path.join(ROOT, "comm_overlap_amd", "csrc", "gemm.hip")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("gemm.hip sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def log(*a):
-    print(*a, file=sys.stderr, flush=True)
+    print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-class Step:
-    """Device tensors and the call sequence of one step of a workload."""
+class Chain:
+    """Device buffers and calls of chained steps. Step n writes hand-off buffer set n % 2 and reads
+    the other set as its input, as consecutive layers would."""
 
     def __init__(self, w, plan, inp, handoff=True):
         import torch
-        self.w, self.plan = w, plan
-        d = lambda t: None if t is None else t.to("cuda").contiguous()
-        self.t = {k: d(v) for k, v in inp.items()}
+        self.w, self.plan, self.handoff = w, plan, handoff
+        self.t = {k: v.to("cuda").contiguous() for k, v in inp.items()}
         i = plan.info
         bf, f32 = torch.bfloat16, torch.float32
         e = lambda *s, dt=bf: torch.empty(*s, dtype=dt, device="cuda")
-        o = {}
-        o["Z"] = e(i.tokens, i.hidden)
-        o["U"] = e(i.tokens, i.n1)
-        o["Zh"] = e(i.tokens, i.hidden) if handoff else None
-        if w.has_attn:
-            o["QKV"] = e(i.tokens, i.qkv_width)
-            o["Za"] = e(i.tokens, i.hidden)
-            o["Zah"] = e(i.tokens, i.hidden) if handoff else None
-        if w.backward:
-            o["dX"] = e(i.tokens, i.hidden)
-            o["dXh"] = e(i.tokens, i.hidden) if handoff else None
-            o["dW1"] = e(i.n1, i.hidden, dt=f32)
-            o["dW2"] = e(i.hidden, i.ffn_shard, dt=f32)
-            o["db1"] = e(i.n1, dt=f32) if w.bias else None
+        self.sets = []
+        for _ in range(2):
+            o = {"Z": e(i.tokens, i.hidden), "Zh": e(i.tokens, i.hidden), "U": e(i.tokens, i.n1)}
             if w.has_attn:
-                o["dXa"] = e(i.tokens, i.hidden)
-                o["dXah"] = e(i.tokens, i.hidden) if handoff else None
-                o["dC"] = e(i.tokens, i.ctx_width)
-                o["dWqkv"] = e(i.qkv_width, i.hidden, dt=f32)
-                o["dWo"] = e(i.hidden, i.ctx_width, dt=f32)
-        self.o = o
+                o.update(QKV=e(i.tokens, i.qkv_width), Za=e(i.tokens, i.hidden), Zah=e(i.tokens, i.hidden))
+            if w.backward:
+                o.update(dX=e(i.tokens, i.hidden), dXh=e(i.tokens, i.hidden))
+                if w.has_attn:
+                    o.update(dXa=e(i.tokens, i.hidden), dXah=e(i.tokens, i.hidden), dC=e(i.tokens, i.ctx_width))
+            self.sets.append(o)
+        # the chain's first input is the seeded X; later steps read the previous step's output
+        for o in self.sets:
+            o["Zh"].copy_(self.t["X" if w.has_attn else "X_mlp"])
+            o["Z"].copy_(o["Zh"])
+        self.g = {"dW1": e(i.n1, i.hidden, dt=f32), "dW2": e(i.hidden, i.ffn_shard, dt=f32)}
+        if w.bias:
+            self.g["db1"] = e(i.n1, dt=f32)
+        if w.has_attn:
+            self.g.update(dWqkv=e(i.qkv_width, i.hidden, dt=f32), dWo=e(i.hidden, i.ctx_width, dt=f32))
         for op in range(4):
             plan.workspace(op)
+        self.n = 0
+
+    def handoff_tensors(self):
+        """(source, destination) pairs a step hands off."""
+        o = self.sets[0]
+        pairs = [(o["Z"], o["Zh"])]
+        if self.w.has_attn:
+            pairs.append((o["Za"], o["Zah"]))
+        if self.w.backward:
+            pairs.append((o["dX"], o["dXh"]))
+            if self.w.has_attn:
+                pairs.append((o["dXa"], o["dXah"]))
+        return pairs
 
     def __call__(self):
-        t, o, p = self.t, self.o, self.plan
-        if self.w.has_attn:
-            p.attnproj_fwd(t["X"], t["Wqkv"], None, o["QKV"], t["C"], t["Wo"], o["Za"], o["Zah"])
-        p.mlp_fwd(t["X_mlp"], t["W1"], t.get("b1"), t["W2"], o["Z"], o["U"], o["Zh"])
-        if self.w.backward:
-            p.mlp_bwd(t["X_mlp"], t["W1"], t["W2"], t["U_saved"], t["dY"], o["dX"], o["dW1"], o["dW2"],
-                      db1=o["db1"], dX_handoff=o["dXh"])
-            if self.w.has_attn:
-                p.attnproj_bwd(t["X"], t["Wqkv"], t["dQKV"], t["C"], t["Wo"], t["dY_attn"], o["dXa"], o["dC"],
-                               o["dWqkv"], o["dWo"], dX_handoff=o["dXah"])
+        w, t, p, g = self.w, self.t, self.plan, self.g
+        o, prev = self.sets[self.n % 2], self.sets[(self.n + 1) % 2]
+        h = self.handoff
+        out = lambda k: o[k] if h else None
+        x_prev = prev["Zh"] if h else prev["Z"]
+        if w.has_attn:
+            p.attnproj_fwd(x_prev, t["Wqkv"], None, o["QKV"], t["C"], t["Wo"], o["Za"], out("Zah"))
+            x_mlp = o["Zah"] if h else o["Za"]
+        else:
+            x_mlp = x_prev
+        p.mlp_fwd(x_mlp, t["W1"], t.get("b1"), t["W2"], o["Z"], o["U"], out("Zh"))
+        if w.backward:
+            p.mlp_bwd(x_mlp, t["W1"], t["W2"], t["U_saved"], t["dY"], o["dX"], g["dW1"], g["dW2"],
+                      db1=g.get("db1"), dX_handoff=out("dXh"))
+            if w.has_attn:
+                dy_attn = o["dXh"] if h else o["dX"]
+                p.attnproj_bwd(x_prev, t["Wqkv"], t["dQKV"], t["C"], t["Wo"], dy_attn, o["dXa"], o["dC"],
+                               g["dWqkv"], g["dWo"], dX_handoff=out("dXah"))
+        self.n += 1
 
 
-def timed(step, steps, warmup):
+def timed(fn, steps, warmup, plan=None):
+    """Wall time per step of `steps` back-to-back calls, bracketed by full synchronization."""
     import torch
     for _ in range(warmup):
-        step()
+        fn()
+    if plan is not None:
+        plan.handoff_wait()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record()
     for _ in range(steps):
-        step()
-    e1.record()
+        fn()
+    if plan is not None:
+        plan.handoff_wait()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    return (time.perf_counter() - t0) * 1e3 / max(1, steps)
 
 
-def union_len(intervals):
-    total, cur_s, cur_e = 0.0, None, None
-    for s, e in sorted(intervals):
-        if cur_e is None or s > cur_e:
-            if cur_e is not None:
-                total += cur_e - cur_s
-            cur_s, cur_e = s, e
-        else:
-            cur_e = max(cur_e, e)
-    if cur_e is not None:
-        total += cur_e - cur_s
-    return total
-
-
-def overlap_with_union(iv, intervals):
-    s, e = iv
-    clipped = [(max(s, a), min(e, b)) for a, b in intervals if b > s and a < e]
-    return union_len(clipped)
-
-
-def analyse_trace(recs):
-    gemms = [r for r in recs if r["kind"] in ("gemm", "colsum")]
-    copies = [r for r in recs if r["kind"] == "copy"]
-    giv = [(r["start_ms"], r["end_ms"]) for r in gemms]
-    by_step = {}
-    for r in gemms:
-        d = by_step.setdefault(r["step"], {"n": 0, "ms": 0.0, "flops": 0.0})
+def kernel_stats(recs):
+    by = {}
+    for r in recs:
+        if r["kind"] == "copy":
+            continue
+        d = by.setdefault(r["step"], {"n": 0, "ms": 0.0, "flops": 0.0})
         d["n"] += 1
         d["ms"] += r["end_ms"] - r["start_ms"]
         d["flops"] += r["flops"]
-    copy_ms = sum(r["end_ms"] - r["start_ms"] for r in copies)
-    hidden_ms = sum(overlap_with_union((r["start_ms"], r["end_ms"]), giv) for r in copies)
-    return by_step, copy_ms, hidden_ms, copies
+    return by
 
 
 def cpu_baseline(w, inp, target_s):
-    """Time the fp64 oracle on host cores over a bounded sample of the same workload."""
-    import numpy as np
+    """The fp64 oracle, as it stands, on the host's cores over a bounded row sample of the workload."""
     from oracle import layer as L
     try:
         from threadpoolctl import threadpool_info
@@ -156,102 +181,93 @@ def cpu_baseline(w, inp, target_s):
         threads = os.cpu_count() or 1
     f64 = L.as_f64
     M = w.tokens
-    # rows are independent: a row sample of the forward costs rows/M of the full forward
-    rows = M
-    fl_full = sum(v for k, v in w.gemm_flops().items())
-    est_rate = 2e11  # rough host fp64 flop/s, only to size the sample
-    if fl_full / est_rate > target_s:
-        rows = max(w.row_slices * 64, int(M * target_s * est_rate / fl_full) // 64 * 64)
-        rows = min(rows, M)
+    fl_full = sum(w.gemm_flops().values())
+    # rows are independent: a row sample costs rows/M of the full workload; size it from a probe
+    probe_rows = max(64, min(M, 512))
+    X = f64(inp["X_mlp"][:probe_rows])
+    t0 = time.perf_counter()
+    L.mlp_fwd(X, f64(inp["W1"]), f64(inp["b1"]) if "b1" in inp else None, f64(inp["W2"]), w.act)
+    rate = 2.0 * probe_rows * w.hidden * (w.n1 + w.ffn_shard) / max(1e-6, time.perf_counter() - t0)
+    rows = int(min(M, max(64, target_s * rate / (fl_full / M))) // 64 * 64) or 64
     sel = slice(0, rows)
-    X = f64(inp["X_mlp"][sel]); W1 = f64(inp["W1"]); W2 = f64(inp["W2"])
-    b1 = f64(inp["b1"]) if "b1" in inp else None
-    args = {}
-    if w.has_attn:
-        args.update(X=f64(inp["X"][sel]), Wqkv=f64(inp["Wqkv"]), C=f64(inp["C"][sel]), Wo=f64(inp["Wo"]))
-    if w.backward:
-        args.update(U=f64(inp["U_saved"][sel]), dY=f64(inp["dY"][sel]))
-        if w.has_attn:
-            args.update(dQKV=f64(inp["dQKV"][sel]), dYa=f64(inp["dY_attn"][sel]))
+    A = {k: f64(v[sel]) if v.dim() == 2 and v.shape[0] == M else f64(v) for k, v in inp.items()}
 
     def run():
-        L.mlp_fwd(X, W1, b1, W2, w.act)
+        L.mlp_fwd(A["X_mlp"], A["W1"], A.get("b1"), A["W2"], w.act)
         if w.has_attn:
-            L.attnproj_fwd(args["X"], args["Wqkv"], None, args["C"], args["Wo"])
+            L.attnproj_fwd(A["X"], A["Wqkv"], None, A["C"], A["Wo"])
         if w.backward:
-            L.mlp_bwd(X, W1, W2, args["U"], args["dY"], w.act, with_bias=w.bias)
+            L.mlp_bwd(A["X_mlp"], A["W1"], A["W2"], A["U_saved"], A["dY"], w.act, with_bias=w.bias)
             if w.has_attn:
-                L.attnproj_bwd(args["X"], args["Wqkv"], args["dQKV"], args["C"], args["Wo"], args["dYa"])
+                L.attnproj_bwd(A["X"], A["Wqkv"], A["dQKV"], A["C"], A["Wo"], A["dY_attn"])
 
-    reps, t = 0, 0.0
     t0 = time.perf_counter()
+    reps = 0
     while True:
         run()
         reps += 1
         t = time.perf_counter() - t0
-        if t >= target_s or reps >= 5:
+        if t >= 0.8 * target_s or reps >= 20:
             break
     flops = fl_full * rows / M * reps
     return {"value": round(flops / t / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} of {M} token rows of the same workload (all its products), fp64 numpy/BLAS, "
-                      f"{reps} run(s) in {t:.1f} s"}
+            "sample": f"{rows} of {M} token rows of the same workload (all its products), fp64 NumPy "
+                      f"(OpenBLAS), {reps} run(s) in {t:.1f} s"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path runs on a "
-              f"single MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path is one GPU's "
+              f"tensor-parallel share; DESIGN.md describes how it would shard)", file=sys.stderr)
         return 2
     import torch
     from comm_overlap_amd import synth
     from comm_overlap_amd import tpslice as T
 
     w = synth.WORKLOADS[args.workload]
-    log(f"[bench] workload {w.key}: generating inputs")
+    log(f"workload {w.key}: generating inputs")
     inp = synth.make_inputs(w)
     flops = sum(w.gemm_flops().values())
     kw = dict(n_streams=args.streams, n_copy_streams=args.copy_streams, copy_blit=args.copy_blit)
-    plan = T.plan_for(w, **kw)
-    step = Step(w, plan, inp)
+    plan = T.plan_for(w, pipeline=True, **kw)
+    chain = Chain(w, plan, inp)
     torch.cuda.synchronize()
 
-    # 1) headline: K steps back to back with the hand-off, per-launch events on the worker streams
-    log(f"[bench] warmup {args.warmup}")
-    timed(step, 1, args.warmup)
-    log(f"[bench] timed region: {args.steps} steps (traced)")
-    plan.trace(True)
-    ms, wall = timed(step, args.steps, 0)
+    # 1) headline: K chained steps with the pipelined hand-off; products timed per launch
+    log(f"warmup {args.warmup}")
+    timed(chain, 0, args.warmup, plan)
+    log(f"timed region: {args.steps} steps")
+    plan.trace(True, products=True, copies=False)
+    ms = timed(chain, args.steps, 0, plan)
     recs = plan.trace_read()
-    by_step, copy_ms, hidden_ms, copies = analyse_trace(recs)
     plan.trace(False)
-    # 2) the same without tracing (overhead check)
-    log("[bench] timed region (untraced)")
-    ms_untraced, _ = timed(step, args.steps, 2)
-    # 3) without the hand-off, and the copies alone (serialized plan: nothing to overlap with)
-    log("[bench] compute only / copies alone")
-    step_nc = Step(w, plan, inp, handoff=False)
-    ms_comp, _ = timed(step_nc, args.steps, 2)
-    del step_nc
-    splan = T.plan_for(w, serialize=True, copy_blit=args.copy_blit)
-    sstep = Step(w, splan, inp)
-    timed(sstep, 2, 1)
-    splan.trace(True)
-    sstep()
-    torch.cuda.synchronize()
-    srec = splan.trace_read()
-    copy_alone_ms = sum(r["end_ms"] - r["start_ms"] for r in srec if r["kind"] == "copy")
-    del sstep
+    by = kernel_stats(recs)
+    ms_untraced = timed(chain, args.steps, 2, plan)
+
+    # 2) the same chain without hand-off copies, and the hand-off copies alone
+    log("compute only / copies only")
+    nocopy = Chain(w, plan, inp, handoff=False)
+    ms_comp = timed(nocopy, args.steps, 2, plan)
+    del nocopy
+    pairs = chain.handoff_tensors()
+    ms_copy = timed(lambda: [plan.handoff_copy(s, d) for s, d in pairs], args.steps, 2, plan)
+    hidden = max(0.0, min(1.0, 1.0 - (ms_untraced - ms_comp) / ms_copy)) if ms_copy > 0 else None
+
+    # 3) an isolated call (full join, nothing after it to hide the last pieces' copies)
+    log("isolated calls")
+    jplan = T.plan_for(w, **kw)
+    jchain = Chain(w, jplan, inp)
+    jnocopy = Chain(w, jplan, inp, handoff=False)
+    ms_j = timed(jchain, max(5, args.steps // 4), 2)
+    ms_jc = timed(jnocopy, max(5, args.steps // 4), 2)
+    hidden_single = max(0.0, min(1.0, 1.0 - (ms_j - ms_jc) / ms_copy)) if ms_copy > 0 else None
+    del jchain, jnocopy
 
     tflops = flops / (ms * 1e-3) / 1e12
-    hidden_wall = None
-    if copy_alone_ms > 0:
-        hidden_wall = max(0.0, min(1.0, 1.0 - (ms_untraced - ms_comp) / copy_alone_ms))
-    dom = max(by_step.items(), key=lambda kv: kv[1]["ms"])
-    dom_name, dom_stats = dom
-    dom_avg_ms = dom_stats["ms"] / dom_stats["n"]
-    dom_flops = dom_stats["flops"] / dom_stats["n"]
-    achieved = dom_flops / (dom_avg_ms * 1e-3) / 1e12
+    dom_name, dom = max(by.items(), key=lambda kv: kv[1]["ms"])
+    dom_ms = dom["ms"] / dom["n"]
+    achieved = dom["flops"] / dom["n"] / (dom_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -268,26 +284,35 @@ def main():
         "config": {"workload": w.key, "tokens": w.tokens, "hidden": w.hidden, "ffn_shard": w.ffn_shard,
                    "tp_share": f"1/{w.tp}", "act": w.act, "row_slices": w.row_slices,
                    "col_slices": w.col_slices, "backward": w.backward,
-                   "streams": plan.info.n_streams, "copy_streams": plan.info.n_copy_streams,
-                   "handoff": "blit" if args.copy_blit else "dma"},
+                   "heads_shard": [w.q_heads_shard, w.kv_heads_shard] if w.has_attn else None,
+                   "worker_streams": plan.info.n_streams, "copy_streams": plan.info.n_copy_streams,
+                   "handoff": "blit" if args.copy_blit else "dma", "chain": "pipelined"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "hidden_copy_pct": None if hidden_wall is None else round(100.0 * hidden_wall, 1),
-        "hidden_copy_pct_trace": round(100.0 * hidden_ms / copy_ms, 1) if copy_ms > 0 else None,
+        "hidden_copy_pct": None if hidden is None else round(100.0 * hidden, 1),
+        "hidden_copy_pct_single_call": None if hidden_single is None else round(100.0 * hidden_single, 1),
         "ms_per_step_untraced": round(ms_untraced, 4),
-        "ms_per_step_no_handoff": round(ms_comp, 4),
-        "ms_copies_alone_per_step": round(copy_alone_ms, 4),
-        "roofline": {"bound": "mfma", "kernel": f"gemm ({dom_name})", "achieved": round(achieved, 2),
+        "ms_per_step_without_handoff": round(ms_comp, 4),
+        "ms_handoff_copies_alone": round(ms_copy, 4),
+        "ms_per_isolated_call": round(ms_j, 4),
+        "roofline": {"bound": "mfma", "kernel": f"gemm_kernel ({dom_name})", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "launches": dom_stats["n"], "avg_launch_ms": round(dom_avg_ms, 4)},
+                     "traffic": recorded_traffic(w.key), "launches": dom["n"],
+                     "avg_launch_ms": round(dom_ms, 4)},
         "kernels": {k: {"launches": v["n"], "avg_ms": round(v["ms"] / v["n"], 4),
-                        "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 1)} for k, v in by_step.items()},
+                        "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 1)} for k, v in by.items()},
     }
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (fp64 oracle)")
+        log("cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    plan.handoff_wait()
+    torch.cuda.synchronize()
+    if args.calib_copy:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # elementwise kernel: reads and writes CALIB_BYTES
+        torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
-    plan.close()
-    splan.close()
     return 0
 
 

@@ -21,6 +21,7 @@
 // Tiles are numbered so that each XCD (workgroups are dispatched round-robin over the 8 XCDs)
 // receives a contiguous run of the grouped tile order, which keeps the operand rows and columns a
 // run shares in that XCD's L2.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -476,13 +477,16 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* partials
 __global__ void fence_kernel() {}
 
 template <int L, int E>
-hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
+hipError_t launch_one(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<L, E>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (attr != hipSuccess) return attr;
   const int grid = g.tiles_m * g.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<L, E>), dim3(grid), dim3(kThreads), kLdsBytes, s, g);
+  if (start || stop)
+    hipExtLaunchKernelGGL((gemm_kernel<L, E>), dim3(grid), dim3(kThreads), kLdsBytes, s, start, stop, 0, g);
+  else
+    hipLaunchKernelGGL((gemm_kernel<L, E>), dim3(grid), dim3(kThreads), kLdsBytes, s, g);
   return hipGetLastError();
 }
 
@@ -494,7 +498,7 @@ uint32_t extent_bytes(int64_t rows, int64_t ld, int64_t cols) {
 
 }  // namespace
 
-hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream) {
+hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int out_bn = epi == kEpiSwiglu ? kBN / 2 : kBN;
   g.tiles_m = (g.M + kBM - 1) / kBM;
@@ -506,13 +510,13 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream) {
   else g.b_bytes = extent_bytes(g.K, g.ldb, g.N);
   if (g.K <= 0) { g.a_bytes = 0; g.b_bytes = 0; }
   switch (layout * 8 + epi) {
-    case kFwd * 8 + kEpiBf16: return launch_one<kFwd, kEpiBf16>(g, stream);
-    case kFwd * 8 + kEpiGelu: return launch_one<kFwd, kEpiGelu>(g, stream);
-    case kFwd * 8 + kEpiSwiglu: return launch_one<kFwd, kEpiSwiglu>(g, stream);
-    case kDgrad * 8 + kEpiBf16: return launch_one<kDgrad, kEpiBf16>(g, stream);
-    case kDgrad * 8 + kEpiDgelu: return launch_one<kDgrad, kEpiDgelu>(g, stream);
-    case kDgrad * 8 + kEpiDswiglu: return launch_one<kDgrad, kEpiDswiglu>(g, stream);
-    case kWgrad * 8 + kEpiF32: return launch_one<kWgrad, kEpiF32>(g, stream);
+    case kFwd * 8 + kEpiBf16: return launch_one<kFwd, kEpiBf16>(g, stream, start, stop);
+    case kFwd * 8 + kEpiGelu: return launch_one<kFwd, kEpiGelu>(g, stream, start, stop);
+    case kFwd * 8 + kEpiSwiglu: return launch_one<kFwd, kEpiSwiglu>(g, stream, start, stop);
+    case kDgrad * 8 + kEpiBf16: return launch_one<kDgrad, kEpiBf16>(g, stream, start, stop);
+    case kDgrad * 8 + kEpiDgelu: return launch_one<kDgrad, kEpiDgelu>(g, stream, start, stop);
+    case kDgrad * 8 + kEpiDswiglu: return launch_one<kDgrad, kEpiDswiglu>(g, stream, start, stop);
+    case kWgrad * 8 + kEpiF32: return launch_one<kWgrad, kEpiF32>(g, stream, start, stop);
     default: return hipErrorInvalidValue;
   }
 }

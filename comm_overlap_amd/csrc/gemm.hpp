@@ -45,8 +45,11 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
 };
 
-// Queue one GEMM on `stream`. Returns hipSuccess or the launch error.
-hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream);
+// Queue one GEMM on `stream`. With `start`/`stop` events the launch records the kernel's own start
+// and end times in them (timestamps of the dispatch itself, no extra marker packets).
+// Returns hipSuccess or the launch error.
+hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
 
 // A one-wave kernel that does nothing. Queued on a stream after DMA-engine copies it completes only
 // after them (stream order), so an event recorded after it marks the copies' completion.

@@ -34,6 +34,9 @@ struct Runtime {
   std::vector<hipEvent_t> piece;   // one per hand-off piece (and reused per call)
   std::vector<hipEvent_t> slice;   // one per row slice: its products are done
   std::vector<hipEvent_t> join_w, join_c;
+  // pipelined hand-off: per (row slice, copy stream) completion of the latest call's copies
+  std::vector<hipEvent_t> copied;       // [r][E]
+  std::vector<uint8_t> copied_pending;  // [r][E]: recorded and not yet superseded
   // tracing: timing events, recorded around each product / copy of the latest call
   hipEvent_t t0 = nullptr;
   bool window_open = false;
@@ -57,6 +60,9 @@ struct Runtime {
 
 void destroy_runtime(Runtime* rt) {
   if (!rt) return;
+  // let queued work (e.g. pipelined hand-off copies) drain before the streams go away
+  for (auto s : rt->workers) (void)hipStreamSynchronize(s);
+  for (auto s : rt->copiers) (void)hipStreamSynchronize(s);
   for (auto s : rt->workers) (void)hipStreamDestroy(s);
   for (auto s : rt->copiers) (void)hipStreamDestroy(s);
   if (rt->fork) (void)hipEventDestroy(rt->fork);
@@ -64,6 +70,7 @@ void destroy_runtime(Runtime* rt) {
   for (auto e : rt->slice) (void)hipEventDestroy(e);
   for (auto e : rt->join_w) (void)hipEventDestroy(e);
   for (auto e : rt->join_c) (void)hipEventDestroy(e);
+  for (auto e : rt->copied) (void)hipEventDestroy(e);
   if (rt->t0) (void)hipEventDestroy(rt->t0);
   for (auto e : rt->tpool) (void)hipEventDestroy(e);
   delete rt;
@@ -111,6 +118,9 @@ tpslice_status_t ensure_runtime(tpslice_plan_s* p, Runtime** out) {
     rt->slice.resize(p->r);
     for (auto& e : rt->piece) if ((st = make_event(&e))) return st;
     for (auto& e : rt->slice) if ((st = make_event(&e))) return st;
+    rt->copied.resize(size_t(p->r) * p->E);
+    for (auto& e : rt->copied) if ((st = make_event(&e))) return st;
+    rt->copied_pending.assign(size_t(p->r) * p->E, 0);
   }
   *out = rt;
   return TPSLICE_OK;
@@ -125,6 +135,7 @@ struct Schedule {
   hipStream_t caller;
   bool serial;
   uint32_t copied = 0;  // bit k: copy stream k received a copy in this call (bit 31: caller stream)
+  uint32_t slice_streams = 0;  // copy streams used by the current row slice's pieces
 
   tpslice_status_t fence(hipStream_t s) {
     hipError_t e = launch_fence(s);
@@ -134,6 +145,30 @@ struct Schedule {
 
   hipStream_t worker(int i) const { return serial ? caller : rt->workers[i % p->S]; }
   int worker_id(int i) const { return serial ? -1 : i % p->S; }
+  bool pipelined() const { return !serial && (p->desc.flags & TPSLICE_F_PIPELINE); }
+
+  // Pipelined mode: row slice i's products wait for the previous call's hand-off of row slice i.
+  tpslice_status_t slice_begin(int i) {
+    if (!pipelined()) return TPSLICE_OK;
+    for (int k = 0; k < p->E; ++k) {
+      const size_t x = size_t(i) * p->E + k;
+      if (rt->copied_pending[x]) TPS_HIP(hipStreamWaitEvent(worker(i), rt->copied[x], 0));
+    }
+    return TPSLICE_OK;
+  }
+
+  // Pipelined mode: mark the end of row slice i's hand-off copies on each copy stream it used.
+  tpslice_status_t slice_handed_off(int i, uint32_t streams_used) {
+    if (!pipelined()) return TPSLICE_OK;
+    for (int k = 0; k < p->E; ++k) {
+      if (!(streams_used & (1u << k))) continue;
+      TPS_TRY_(fence(rt->copiers[k]));
+      const size_t x = size_t(i) * p->E + k;
+      TPS_HIP(hipEventRecord(rt->copied[x], rt->copiers[k]));
+      rt->copied_pending[x] = 1;
+    }
+    return TPSLICE_OK;
+  }
 
   tpslice_status_t trace_event(size_t* idx) {
     if (rt->tused == rt->tpool.size()) {
@@ -150,8 +185,13 @@ struct Schedule {
   template <class F>
   tpslice_status_t traced(hipStream_t s, int stream_id, int kind, int step, int slice, int piece, double flops,
                           double bytes, F&& fn) {
-    if (kind == TPSLICE_TRACE_COPY) copied |= stream_id < 0 ? (1u << 31) : (1u << (stream_id - p->S));
-    if (!p->trace) return fn();
+    if (kind == TPSLICE_TRACE_COPY) {
+      const uint32_t bit = stream_id < 0 ? (1u << 31) : (1u << (stream_id - p->S));
+      copied |= bit;
+      slice_streams |= bit;
+    }
+    const int32_t want = kind == TPSLICE_TRACE_COPY ? 2 : 1;
+    if (!(p->trace & want)) return fn();
     TraceSlot t{};
     t.rec.kind = kind; t.rec.step = step; t.rec.slice = slice; t.rec.piece = piece;
     t.rec.stream = stream_id; t.rec.flops = flops; t.rec.bytes = bytes; t.rec.call = rt->calls - 1;
@@ -193,6 +233,7 @@ struct Schedule {
       TPS_HIP(hipEventRecord(rt->join_w[k], rt->workers[k]));
       TPS_HIP(hipStreamWaitEvent(caller, rt->join_w[k], 0));
     }
+    if (pipelined()) return TPSLICE_OK;  // hand-off copies are joined per slice by later calls
     for (int k = 0; k < p->E; ++k) {
       if (copied & (1u << k)) TPS_TRY_(fence(rt->copiers[k]));
       TPS_HIP(hipEventRecord(rt->join_c[k], rt->copiers[k]));
@@ -245,15 +286,26 @@ struct Schedule {
     return TPSLICE_OK;
   }
 
-  // Queue one product on worker(i) (i = -1: worker 0, all tokens), traced as `step`.
+  // Queue one product on worker(i) (i = -1: worker 0, all tokens), traced as `step`. A traced
+  // product carries its timing events on the dispatch itself.
   tpslice_status_t product(int i, int step, int piece, const GemmArgs& g, int layout, int epi) {
     const int wi = i < 0 ? 0 : i;
     const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
-    return traced(worker(wi), worker_id(wi), TPSLICE_TRACE_GEMM, step, i, piece, flops, 0.0, [&] {
-      hipError_t e = launch_gemm(g, layout, epi, worker(wi));
-      if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
-      return TPSLICE_OK;
-    });
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    TraceSlot t{};
+    const bool tr = (p->trace & 1) && g.M > 0 && g.N > 0;
+    if (tr) {
+      t.rec.kind = TPSLICE_TRACE_GEMM; t.rec.step = step; t.rec.slice = i; t.rec.piece = piece;
+      t.rec.stream = worker_id(wi); t.rec.flops = flops; t.rec.call = rt->calls - 1;
+      TPS_TRY_(trace_event(&t.ev0));
+      TPS_TRY_(trace_event(&t.ev1));
+      e0 = rt->tpool[t.ev0];
+      e1 = rt->tpool[t.ev1];
+    }
+    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1);
+    if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
+    if (tr) rt->slots.push_back(t);
+    return TPSLICE_OK;
   }
 
   tpslice_status_t colsum(const void* X, int64_t ld, int64_t M, int64_t N, float* partials, float* out,
@@ -350,6 +402,8 @@ extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, con
   TPS_TRY(S.fork());
   for (int i = 0; i < p->r; ++i) {
     const int64_t r0 = int64_t(i) * p->Ms;
+    TPS_TRY(S.slice_begin(i));
+    S.slice_streams = 0;
     GemmArgs g1 = args(bf(X, r0 * p->h), p->h, W1, p->h, bfw(H, r0 * p->Fp), p->Fp, p->Ms, p->Fp, p->h);
     g1.bias = b1;
     g1.half = p->Fp;
@@ -362,6 +416,7 @@ extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, con
       TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DOWN, j, g2, kFwd, kEpiBf16));
       if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
     }
+    TPS_TRY(S.slice_handed_off(i, S.slice_streams));
   }
   return S.join();
 }
@@ -385,6 +440,8 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
   TPS_TRY(S.fork());
   for (int i = 0; i < p->r; ++i) {
     const int64_t r0 = int64_t(i) * p->Ms;
+    TPS_TRY(S.slice_begin(i));
+    S.slice_streams = 0;
     // output projection first: its pieces are the hand-off, the QKV product then runs under the copies
     for (int j = 0; j < p->c; ++j) {
       const int64_t c0 = int64_t(j) * p->hc;
@@ -393,6 +450,7 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
       TPS_TRY(S.product(i, TPSLICE_STEP_OUT, j, g, kFwd, kEpiBf16));
       if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
     }
+    TPS_TRY(S.slice_handed_off(i, S.slice_streams));
     GemmArgs q = args(bf(X, r0 * p->h), p->h, Wqkv, p->h, bfw(QKV, r0 * p->qkv), p->qkv, p->Ms, p->qkv, p->h);
     q.bias = bqkv;
     TPS_TRY(S.product(i, TPSLICE_STEP_QKV, -1, q, kFwd, kEpiBf16));
@@ -423,6 +481,8 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
   TPS_TRY(S.fork());
   for (int i = 0; i < p->r && p->M > 0; ++i) {
     const int64_t r0 = int64_t(i) * p->Ms;
+    TPS_TRY(S.slice_begin(i));
+    S.slice_streams = 0;
     // dH = dY W2 with the activation's derivative fused: writes dU and (recomputed) H
     GemmArgs g = args(bf(dY, r0 * p->h), p->h, W2, p->Fp, bfw(dU, r0 * p->N1), p->N1, p->Ms, p->Fp, p->h);
     g.aux_in = bf(U, r0 * p->N1); g.ld_in = p->N1;
@@ -436,6 +496,7 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
       TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DX, j, gx, kDgrad, kEpiBf16));
       if (dX_handoff) TPS_TRY(S.handoff(i, j, dX, dX_handoff));
     }
+    TPS_TRY(S.slice_handed_off(i, S.slice_streams));
   }
   // weight gradients over all tokens at once (one k run, no split of the token sum), under the
   // last pieces' copies
@@ -472,6 +533,8 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
   TPS_TRY(S.fork());
   for (int i = 0; i < p->r && p->M > 0; ++i) {
     const int64_t r0 = int64_t(i) * p->Ms;
+    TPS_TRY(S.slice_begin(i));
+    S.slice_streams = 0;
     for (int j = 0; j < p->c; ++j) {
       const int64_t c0 = int64_t(j) * p->hc;
       GemmArgs gx = args(bf(dQKV, r0 * p->qkv), p->qkv, bf(Wqkv, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms,
@@ -479,6 +542,7 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
       TPS_TRY(S.product(i, TPSLICE_STEP_ATTN_DX, j, gx, kDgrad, kEpiBf16));
       if (dX_handoff) TPS_TRY(S.handoff(i, j, dX, dX_handoff));
     }
+    TPS_TRY(S.slice_handed_off(i, S.slice_streams));
     GemmArgs gc = args(bf(dY, r0 * p->h), p->h, Wo, p->ctx, bfw(dC, r0 * p->ctx), p->ctx, p->Ms, p->ctx, p->h);
     TPS_TRY(S.product(i, TPSLICE_STEP_ATTN_DC, -1, gc, kDgrad, kEpiBf16));
   }
@@ -496,7 +560,8 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
 extern "C" tpslice_status_t tpslice_trace_enable(tpslice_plan_t p, int32_t enable) {
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
-  p->trace = enable ? 1 : 0;
+  if (enable < 0 || enable > 3) return fail(TPSLICE_ERR_INVALID, "trace mask %d outside [0, 3]", enable);
+  p->trace = enable;
   return TPSLICE_OK;
 }
 
@@ -525,4 +590,37 @@ extern "C" tpslice_status_t tpslice_trace_read(tpslice_plan_t p, tpslice_trace_r
   rt->tused = 0;
   rt->window_open = false;
   return TPSLICE_OK;
+}
+
+extern "C" tpslice_status_t tpslice_handoff_wait(tpslice_plan_t p, void* stream) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  Runtime* rt = static_cast<Runtime*>(p->rt);
+  if (!rt || rt->copiers.empty()) return TPSLICE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int k = 0; k < p->E; ++k) {
+    hipError_t e = launch_fence(rt->copiers[k]);
+    if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "fence launch: %s", hipGetErrorString(e));
+    TPS_HIP(hipEventRecord(rt->join_c[k], rt->copiers[k]));
+    TPS_HIP(hipStreamWaitEvent(s, rt->join_c[k], 0));
+  }
+  return TPSLICE_OK;
+}
+
+extern "C" tpslice_status_t tpslice_handoff_copy(tpslice_plan_t p, const void* src, void* dst, void* stream) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (p->M > 0) { TPS_REQ(src); TPS_REQ(dst); }
+  if (p->M == 0) return TPSLICE_OK;
+  Runtime* rt = nullptr;
+  TPS_TRY(ensure_runtime(p, &rt));
+  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  TPS_TRY(S.fork());
+  for (int i = 0; i < p->r; ++i) {
+    TPS_TRY(S.slice_begin(i));
+    S.slice_streams = 0;
+    for (int j = 0; j < p->c; ++j) TPS_TRY(S.handoff(i, j, src, dst));
+    TPS_TRY(S.slice_handed_off(i, S.slice_streams));
+  }
+  return S.join();
 }

@@ -1,0 +1,141 @@
+"""Summaries of rocprofv3 runs of the sliced layer shard (reads the rocprofv3 SQLite output).
+
+    python -m comm_overlap_amd.profile_summary trace RESULTS.db [--match gemm_kernel]
+        per-kernel dispatch statistics, DMA-engine copies, and the share of copy time that
+        overlaps kernels matching --match (the trace form of the hidden-copy fraction)
+    python -m comm_overlap_amd.profile_summary traffic FETCH.db WRITE.db --kernel NAME
+                                               --calib-kernel NAME --calib-bytes N
+        HBM bytes per dispatch of NAME from a FETCH_SIZE pass and a WRITE_SIZE pass, each scaled
+        by what the same counter reads for a calibration copy kernel that moves N bytes each way
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import sqlite3
+import sys
+
+
+def _kernels(db):
+    c = sqlite3.connect(db)
+    return list(c.execute("select name, start, end from kernels order by start"))
+
+
+def _copies(db):
+    c = sqlite3.connect(db)
+    try:
+        return list(c.execute("select name, start, end, size from memory_copies order by start"))
+    except sqlite3.OperationalError:
+        return []
+
+
+def _union(iv):
+    out = []
+    for s, e in sorted(iv):
+        if out and s <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], e)
+        else:
+            out.append([s, e])
+    return out
+
+
+def trace(db, match):
+    ks = _kernels(db)
+    stats = collections.OrderedDict()
+    for name, s, e in ks:
+        d = stats.setdefault(name, [])
+        d.append((e - s) / 1e3)
+    print("kernel dispatches (durations in us):")
+    print(f"  {'count':>6} {'avg':>10} {'min':>10} {'max':>10} {'total_ms':>10}  name")
+    for name, d in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        print(f"  {len(d):6d} {sum(d)/len(d):10.2f} {min(d):10.2f} {max(d):10.2f} {sum(d)/1e3:10.3f}  {name[:110]}")
+    cps = _copies(db)
+    if not cps:
+        return
+    by = collections.defaultdict(list)
+    for name, s, e, size in cps:
+        by[(name, size)].append((e - s) / 1e3)
+    print("memory copies (durations in us):")
+    for (name, size), d in sorted(by.items()):
+        gbs = size / (sum(d) / len(d) * 1e-6) / 1e9
+        print(f"  {len(d):6d} x {size:>11d} B  avg {sum(d)/len(d):9.2f}  ({gbs:6.1f} GB/s each)  {name}")
+    busy = _union([(s, e) for name, s, e in ks if match in name])
+    tot = hid = 0.0
+    j = 0
+    for name, s, e, size in cps:
+        if "DEVICE_TO_DEVICE" not in name:
+            continue
+        tot += e - s
+        for a, b in busy:
+            if b <= s:
+                continue
+            if a >= e:
+                break
+            hid += min(e, b) - max(s, a)
+    if tot > 0:
+        print(f"device-to-device copy time overlapped by '{match}' kernels: {100.0 * hid / tot:.1f}% "
+              f"of {tot / 1e6:.3f} ms")
+
+
+def _pmc(db, counter):
+    c = sqlite3.connect(db)
+    per = collections.defaultdict(float)
+    names = {}
+    for name, disp, cname, val in c.execute(
+            "select name, dispatch_id, counter_name, counter_value from pmc_events"):
+        if cname.startswith(counter):
+            per[disp] += val
+            names[disp] = name
+    out = collections.defaultdict(list)
+    for disp, v in per.items():
+        out[names[disp]].append(v)
+    return out
+
+
+def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes):
+    f = _pmc(fetch_db, "FETCH_SIZE")
+    w = _pmc(write_db, "WRITE_SIZE")
+
+    def avg(d, match):
+        vals = [v for n, vs in d.items() if match in n for v in vs]
+        return sum(vals) / len(vals) if vals else None, len(vals)
+
+    fk, nf = avg(f, kernel)
+    wk, nw = avg(w, kernel)
+    fc, _ = avg(f, calib_kernel)
+    wc, _ = avg(w, calib_kernel)
+    if None in (fk, wk, fc, wc):
+        print("missing dispatches for the kernel or the calibration copy", file=sys.stderr)
+        return 1
+    sf = calib_bytes / (fc * 1024.0)
+    sw = calib_bytes / (wc * 1024.0)
+    print(f"calibration copy: FETCH_SIZE {fc:.0f} KiB, WRITE_SIZE {wc:.0f} KiB for {calib_bytes} B each way "
+          f"-> scale {sf:.4f} (fetch), {sw:.4f} (write)")
+    fb, wb = fk * 1024.0 * sf, wk * 1024.0 * sw
+    print(f"kernel '{kernel}': {nf} fetch / {nw} write dispatches; per dispatch FETCH {fk:.0f} KiB, "
+          f"WRITE {wk:.0f} KiB -> {fb/1e6:.2f} MB read + {wb/1e6:.2f} MB written = {(fb+wb)/1e6:.2f} MB")
+    print(f"traffic_bytes_per_launch: {fb + wb:.0f}")
+    return 0
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("--match", default="gemm_kernel")
+    r = sub.add_parser("traffic")
+    r.add_argument("fetch_db")
+    r.add_argument("write_db")
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--calib-kernel", required=True)
+    r.add_argument("--calib-bytes", type=float, required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        trace(a.db, a.match)
+        return 0
+    return traffic(a.fetch_db, a.write_db, a.kernel, a.calib_kernel, a.calib_bytes)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

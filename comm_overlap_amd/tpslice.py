@@ -19,12 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libtpslice.so")
 
 OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 ACT_GELU, ACT_SWIGLU = 1, 2
-F_SERIALIZE, F_COPY_BLIT = 0x1, 0x2
+F_SERIALIZE, F_COPY_BLIT, F_PIPELINE = 0x1, 0x2, 0x4
 OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD = range(4)
 EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice_plan_piece",
            "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",
            "tpslice_attnproj_bwd", "tpslice_trace_enable", "tpslice_trace_read",
-           "tpslice_error_string", "tpslice_last_error")
+           "tpslice_handoff_copy", "tpslice_handoff_wait", "tpslice_error_string", "tpslice_last_error")
 TRACE_GEMM, TRACE_COPY, TRACE_COLSUM = range(3)
 STEPS = ("mlp_up", "mlp_down", "qkv", "out", "mlp_dh", "mlp_dx", "mlp_dw1", "mlp_dw2", "attn_dx", "attn_dc",
          "attn_dwqkv", "attn_dwo", "bias_grad", "handoff")
@@ -77,7 +77,9 @@ def _load():
     lib.tpslice_attnproj_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.tpslice_trace_enable.argtypes = [vp, i32]
     lib.tpslice_trace_read.argtypes = [vp, ctypes.POINTER(TraceRec), i32, ctypes.POINTER(i32)]
-    for name in EXPORTS[:11]:
+    lib.tpslice_handoff_copy.argtypes = [vp, vp, vp, vp]
+    lib.tpslice_handoff_wait.argtypes = [vp, vp]
+    for name in EXPORTS[:13]:
         getattr(lib, name).restype = st
     lib.tpslice_error_string.argtypes = [st]
     lib.tpslice_error_string.restype = ctypes.c_char_p
@@ -134,13 +136,15 @@ class Config:
     n_copy_streams: int = 0
     serialize: bool = False
     copy_blit: bool = False
+    pipeline: bool = False
 
     def desc(self) -> Desc:
         return Desc(self.tokens, self.hidden, self.ffn, self.tp_size, self.n_row_slices, self.n_col_slices,
                     self.n_heads, self.n_kv_heads, self.head_dim,
                     {"gelu": ACT_GELU, "swiglu": ACT_SWIGLU}.get(self.act, 0), self.n_streams,
                     self.n_copy_streams,
-                    (F_SERIALIZE if self.serialize else 0) | (F_COPY_BLIT if self.copy_blit else 0))
+                    (F_SERIALIZE if self.serialize else 0) | (F_COPY_BLIT if self.copy_blit else 0)
+                    | (F_PIPELINE if self.pipeline else 0))
 
 
 class Plan:
@@ -168,8 +172,10 @@ class Plan:
         except Exception:
             pass
 
-    def trace(self, enable: bool = True):
-        _check(lib.tpslice_trace_enable(self._h, int(bool(enable))))
+    def trace(self, enable=True, products=True, copies=True):
+        """Enable tracing (products and/or hand-off copies) or disable it (enable=False)."""
+        mask = (int(products) | (int(copies) << 1)) if enable else 0
+        _check(lib.tpslice_trace_enable(self._h, mask))
 
     def trace_read(self):
         """Records accumulated since the last read (then a new window starts): dicts with kind,
@@ -185,6 +191,16 @@ class Plan:
                             piece=r.piece, stream=r.stream, call=r.call, flops=r.flops, bytes=r.bytes,
                             start_ms=r.start_ms, end_ms=r.end_ms))
         return out
+
+    def handoff_copy(self, src, dst, stream=None):
+        """Only the hand-off copies of a [tokens][hidden] bf16 tensor (no products)."""
+        i = self.info
+        _shape(src, (i.tokens, i.hidden), "src"); _shape(dst, (i.tokens, i.hidden), "dst")
+        _check(lib.tpslice_handoff_copy(self._h, _ptr(src, name="src"), _ptr(dst, name="dst"), _stream(stream)))
+
+    def handoff_wait(self, stream=None):
+        """Make `stream` (default: current) wait for every hand-off copy queued so far."""
+        _check(lib.tpslice_handoff_wait(self._h, _stream(stream)))
 
     def piece(self, index: int):
         out = (ctypes.c_int64 * 4)()

@@ -67,6 +67,14 @@ typedef enum {
 #define TPSLICE_F_SERIALIZE 0x1u /* every product and copy in order on the caller stream (ablation)  */
 #define TPSLICE_F_COPY_BLIT 0x2u /* hand-off copies by the runtime's copy kernel instead of the DMA
                                     engines (uses compute units; for comparison)                       */
+#define TPSLICE_F_PIPELINE 0x4u  /* pipelined hand-off: the caller's stream waits for the products
+                                    only; a later call's row slice i waits just for this call's
+                                    hand-off copies of row slice i. Chained calls (a layer reading
+                                    the previous layer's hand-off) then overlap the last pieces'
+                                    copies with the next call's first pieces (Domino page,
+                                    Abstract: independent pieces pipelined across the batch's work).
+                                    Use tpslice_handoff_wait() before reading a hand-off buffer on
+                                    another stream, or before freeing buffers the copies touch.    */
 
 typedef struct {
   int64_t tokens;         /* M: token rows in the batch (micro-batch x sequence, batch-major)         */
@@ -79,8 +87,8 @@ typedef struct {
   int32_t n_kv_heads;     /* full-model key/value heads (GQA); this rank holds max(1, n_kv/tp_size)   */
   int32_t head_dim;       /* d; multiple of 8                                                          */
   int32_t act;            /* tpslice_act_t                                                              */
-  int32_t n_streams;      /* worker streams for the slices (0 = default)                              */
-  int32_t n_copy_streams; /* side streams for hand-off copies (0 = default)                           */
+  int32_t n_streams;      /* worker streams for the slices (0 = default: 1, slices in order)          */
+  int32_t n_copy_streams; /* side streams for hand-off copies (0 = default: 2)                        */
   uint32_t flags;         /* TPSLICE_F_*                                                                */
 } tpslice_desc_t;
 
@@ -196,12 +204,24 @@ typedef struct {
   float start_ms, end_ms;
 } tpslice_trace_rec_t;
 
+/* enable: 0 off; bit 0 traces products (GEMMs, column sums); bit 1 traces hand-off copies (each
+ * traced copy is closed by a one-wave fence kernel so that its end event covers the DMA engine).   */
 TPSLICE_API tpslice_status_t tpslice_trace_enable(tpslice_plan_t plan, int32_t enable);
 /* Sets *count to the number of records in the window. With cap >= *count it also copies them into
  * `recs` (blocking until their events have completed) and starts a new window; with a smaller cap
  * (e.g. 0) it only reports the count. TPSLICE_ERR_INVALID if tracing is off.                      */
 TPSLICE_API tpslice_status_t tpslice_trace_read(tpslice_plan_t plan, tpslice_trace_rec_t* recs, int32_t cap,
                                                 int32_t* count);
+
+/* Only the hand-off: copy every piece of the [M][h] bf16 tensor `src` into `dst` exactly as a call
+ * hands off its partial sums (same pieces, copy streams and engines), with no products. This is the
+ * communication-only run that the overlap measurement compares against.                         */
+TPSLICE_API tpslice_status_t tpslice_handoff_copy(tpslice_plan_t plan, const void* src, void* dst,
+                                                  void* stream);
+
+/* Make `stream` wait until every hand-off copy the plan has queued so far is complete (needed only
+ * with TPSLICE_F_PIPELINE; a no-op before the plan's first call).                                */
+TPSLICE_API tpslice_status_t tpslice_handoff_wait(tpslice_plan_t plan, void* stream);
 
 /* Static text for a status code.                                                                   */
 TPSLICE_API const char* tpslice_error_string(tpslice_status_t status);

@@ -130,3 +130,11 @@ def test_argument_errors_before_any_gpu_work():
 def test_serialize_plan_uses_one_stream():
     p = T.Plan(T.Config(tokens=64, hidden=64, ffn=64, n_row_slices=4, serialize=True))
     assert (p.info.n_streams, p.info.n_copy_streams) == (1, 1)
+
+
+def test_pipeline_flag_and_handoff_wait_without_gpu_work():
+    p = T.Plan(T.Config(tokens=64, hidden=64, ffn=64, n_row_slices=2, pipeline=True))
+    p.handoff_wait.__func__  # bound
+    # before any call there is nothing to wait for: returns OK without touching the GPU
+    assert T.lib.tpslice_handoff_wait(p._h, None) == T.OK
+    assert T.lib.tpslice_handoff_copy(None, None, None, None) == T.ERR_INVALID

@@ -266,3 +266,65 @@ def test_handoff_complete_when_caller_stream_passes(copy_blit):
         snap = Zh.clone()          # queued on the caller stream right behind the call
         torch.cuda.synchronize()
         assert torch.equal(snap, Z), f"rep {rep}: hand-off not complete at the join"
+
+
+@pytest.mark.parametrize("streams", [1, 2])
+def test_pipelined_chain_matches_joined(streams):
+    """Four chained MLP calls, each reading the previous call's hand-off buffer as its input: the
+    pipelined mode (per-slice waits instead of a full join) gives bitwise the same results."""
+    w = synth.custom("chain", 906, tokens=1024, hidden=512, ffn=2048, tp=2, act="gelu", bias=True,
+                     row_slices=4, col_slices=2)
+    _print_case("pipeline", key=w.key, streams=streams)
+    inp = synth.make_inputs(w)
+    X0, W1, b1, W2 = (G.dev(inp[k]) for k in ("X_mlp", "W1", "b1", "W2"))
+
+    def chain(plan, pipelined):
+        i = plan.info
+        Zs = [torch.empty((i.tokens, i.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+        Hs = [torch.full((i.tokens, i.hidden), float("nan"), dtype=torch.bfloat16, device="cuda")
+              for _ in range(4)]
+        x = X0
+        for n in range(4):
+            plan.mlp_fwd(x, W1, b1, W2, Zs[n], None, Hs[n])
+            x = Hs[n]
+        if pipelined:
+            plan.handoff_wait()
+        torch.cuda.synchronize()
+        return Hs
+
+    ref = chain(T.plan_for(w), False)
+    got = chain(T.plan_for(w, pipeline=True, n_streams=streams), True)
+    for n in range(4):
+        assert torch.equal(got[n], ref[n]), f"layer {n}"
+    r1 = G.oracle_mlp_fwd(inp, w.act)
+    G.assert_parity(ref[0], r1["Z"], "first layer")
+
+
+def test_handoff_copy_only():
+    w = synth.WORKLOADS["llama2_7b_mlp"]
+    plan = T.plan_for(w)
+    src = torch.randn(w.tokens, w.hidden, device="cuda").to(torch.bfloat16)
+    dst = torch.zeros_like(src)
+    plan.handoff_copy(src, dst)
+    snap = dst.clone()
+    torch.cuda.synchronize()
+    assert torch.equal(snap, src)
+
+
+def test_tracing_changes_no_result_and_times_every_launch():
+    w = SMALL_SWIGLU
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    base = G.run_mlp_fwd(plan, inp)
+    plan.trace(True)
+    out = G.run_mlp_fwd(plan, inp)
+    recs = plan.trace_read()
+    plan.trace(False)
+    assert torch.equal(out["Z"], base["Z"]) and torch.equal(out["Zh"], base["Zh"])
+    gemms = [r for r in recs if r["kind"] == "gemm"]
+    copies = [r for r in recs if r["kind"] == "copy"]
+    assert len(gemms) == w.row_slices * (1 + w.col_slices)
+    assert len(copies) >= w.row_slices * w.col_slices
+    assert all(r["end_ms"] > r["start_ms"] >= 0 for r in gemms)
+    fl = w.gemm_flops()
+    assert sum(r["flops"] for r in gemms) == pytest.approx(fl["mlp_up"] + fl["mlp_down"])
