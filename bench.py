@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--streams", type=int, default=0, help="worker streams (0 = plan default)")
     ap.add_argument("--copy-streams", type=int, default=0, help="copy streams (0 = plan default)")
+    ap.add_argument("--row-slices", type=int, default=0, help="row slices (0 = the workload's)")
+    ap.add_argument("--col-slices", type=int, default=0, help="column slices (0 = the workload's)")
+    ap.add_argument("--tile", default="auto", choices=["auto", "large", "small"],
+                    help="block tile of every product (auto = per product, the default)")
     ap.add_argument("--copy-blit", action="store_true", help="hand-off by copy kernel instead of DMA")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
@@ -229,7 +233,11 @@ def main():
     log(f"workload {w.key}: generating inputs")
     inp = synth.make_inputs(w)
     flops = sum(w.gemm_flops().values())
-    kw = dict(n_streams=args.streams, n_copy_streams=args.copy_streams, copy_blit=args.copy_blit)
+    kw = dict(n_streams=args.streams, n_copy_streams=args.copy_streams, copy_blit=args.copy_blit, tile=args.tile)
+    if args.row_slices:
+        kw["n_row_slices"] = args.row_slices
+    if args.col_slices:
+        kw["n_col_slices"] = args.col_slices
     plan = T.plan_for(w, pipeline=True, **kw)
     chain = Chain(w, plan, inp)
     torch.cuda.synchronize()
@@ -282,10 +290,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.key, "tokens": w.tokens, "hidden": w.hidden, "ffn_shard": w.ffn_shard,
-                   "tp_share": f"1/{w.tp}", "act": w.act, "row_slices": w.row_slices,
-                   "col_slices": w.col_slices, "backward": w.backward,
+                   "tp_share": f"1/{w.tp}", "act": w.act, "row_slices": plan.info.n_row_slices,
+                   "col_slices": plan.info.n_col_slices, "backward": w.backward,
                    "heads_shard": [w.q_heads_shard, w.kv_heads_shard] if w.has_attn else None,
                    "worker_streams": plan.info.n_streams, "copy_streams": plan.info.n_copy_streams,
+                   "tile": args.tile,
                    "handoff": "blit" if args.copy_blit else "dma", "chain": "pipelined"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "hidden_copy_pct": None if hidden is None else round(100.0 * hidden, 1),

@@ -1,15 +1,25 @@
 // bf16 MFMA GEMM family for gfx950 (MI355X) with fused layer epilogues.
 //
-// Block tile 256 x 256 x 64, 512 threads = 8 waves (two per SIMD, so one wave's waits hide under
-// the other's MFMAs) in a 2 x 4 grid; each wave owns 128 x 64 outputs as 8 x 4
-// v_mfma_f32_16x16x32_bf16 tiles with fp32 accumulators. Operand tiles go global -> LDS by direct
-// loads (buffer_load_dwordx4 ... lds) into two LDS stages (128 KB): block k+1 loads while block k
-// is multiplied. 16-byte XOR swizzles keep LDS traffic at full rate (chosen by measuring each
-// candidate pattern's LDS throughput on gfx950):
+// Two block tiles share one kernel template (k step 64, v_mfma_f32_16x16x32_bf16, fp32
+// accumulators, two waves per SIMD so one wave's waits hide under the other's MFMAs):
+//   * large: 256 x 256, 512 threads = 8 waves in a 2 x 4 grid, each wave 128 x 64 outputs
+//     (8 x 4 MFMA tiles), one block per CU, 128 KB of LDS;
+//   * small: 128 x 128, 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x 64 outputs
+//     (4 x 4 MFMA tiles), two blocks per CU, 64 KB of LDS each.
+// The launcher picks per product the tile that finishes it sooner on 256 CUs: the large tile
+// moves fewer bytes per flop, the small one keeps the CUs busy when the large tiles are too few
+// (thin slices, narrow weights). Both reduce k in the same order (ascending 64-wide blocks, two
+// 32-wide MFMA steps each), so every output element gets bitwise the same sum whichever tile,
+// slicing or tile position produced it.
+// Operand tiles go global -> LDS by direct loads (buffer_load_dwordx4 ... lds) into two LDS stages:
+// block k+1 loads while block k is multiplied, and the load instructions are spread between the
+// first MFMAs of the block instead of being issued together after the barrier. 16-byte XOR
+// swizzles keep LDS traffic at full rate (chosen by measuring each candidate pattern's LDS
+// throughput on gfx950):
 //   * an operand read along k ("KC") is kept as [rows][64 k] (128-byte rows), fragments read
 //     with ds_read_b128;
-//   * an operand read across k ("NC", rows of k in memory) is kept as [64 k][256 cols] and its
-//     fragments come from ds_read_b64_tr_b16, which transposes 16-bit elements across each
+//   * an operand read across k ("NC", rows of k in memory) is kept as [64 k][tile columns] and
+//     its fragments come from ds_read_b64_tr_b16, which transposes 16-bit elements across each
 //     16-lane group: result element v of lane i is element i%4 of the 8 bytes addressed by
 //     group lane 4v + (i%16)/4.
 // The MFMA is issued with the B fragment first, so each lane ends up holding four consecutive
@@ -30,6 +40,28 @@
 #include "gemm.hpp"
 
 namespace tps {
+
+constexpr int kBKTile = 64;
+// Block tile: BM x BN (BN counts B-tile columns; SwiGLU products hold gate and up halves),
+// waves in a WM x WN grid, `blocks` resident blocks per CU.
+template <int BM_, int BN_, int WM, int WN, int BLOCKS>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, kWavesM = WM, kWavesN = WN, kBlocksPerCU = BLOCKS;
+  static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+  static constexpr int kWaveM = BM / WM;             // output rows per wave
+  static constexpr int kFM = kWaveM / 16;            // MFMA tiles per wave along m
+  static constexpr int kFN = BN / WN / 16;           // MFMA tiles per wave along n
+  static constexpr int kATileBytes = BM * kBKTile * 2, kBTileBytes = BN * kBKTile * 2;
+  static constexpr int kStageBytes = kATileBytes + kBTileBytes;
+  static constexpr int kLdsBytes = 2 * kStageBytes;  // two stages
+  static constexpr int kARuns = kATileBytes / 1024 / kWaves;  // 1-KB load runs per wave
+  static constexpr int kBRuns = kBTileBytes / 1024 / kWaves;
+  static_assert(kARuns % 2 == 0 && kBRuns % 2 == 0, "loads are issued in halves");
+  static_assert(kFM % 4 == 0 || kFM == 2 || kFM == 1, "MFMA rows are issued in four groups");
+};
+using TileL = Tile<256, 256, 2, 4, 1>;
+using TileS = Tile<128, 128, 2, 2, 2>;
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -39,15 +71,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 512;
-constexpr int kTileBytes = 256 * kBK * 2;       // one operand tile, 16 KB
-constexpr int kStageBytes = 2 * kTileBytes;     // A + B
-constexpr int kStages = 131072 / kStageBytes;   // ring of LDS stages
-constexpr int kLdsBytes = kStages * kStageBytes;  // 128 KB
-constexpr int kLoadsPerBlock = kTileBytes / 1024 / 8 * 2;  // buffer_load ... lds per wave per k block
-constexpr int kGroupM = 4;                      // tile rows per group of the tile order
-constexpr uint32_t kOob = 0xFFFFF000u;          // buffer offset that reads as zero: operands are
-                                                // smaller than 4 GiB - 4 KiB
+constexpr int kBK = 64;                          // k per block
+constexpr int kRowBytes = kBK * 2;               // KC tile row: 128 bytes
+constexpr int kChunks = kBK / 8;                 // 16-byte chunks per KC row
+constexpr int kRowsPerRun = 1024 / kRowBytes;    // KC rows per 1-KB load run
+constexpr int kGroupM = 4;                       // tile rows per group of the tile order
+constexpr int kCUs = 256;
+constexpr uint32_t kOob = 0xFFFFF000u;           // buffer offset that reads as zero: operands are
+                                                 // smaller than 4 GiB - 4 KiB
+
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -57,15 +89,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes
 }
 
 // 16-byte chunk swizzles, chosen by measurement on gfx950 (LDS read throughput of each candidate
-// lane pattern): KC rows of 64 B (4 chunks) XOR the chunk with 2*(r1 ^ r3), which lets the
-// fragment reads (16 consecutive rows per 16-lane group) run at full LDS rate, while the plain
-// layout and the other simple XOR forms run at half rate; NC rows of 512 B XOR with
-// (k & 3) << 1 | (k >> 3 & 1) << 3 for the transpose reads.
-constexpr int kRowBytes = kBK * 2, kChunks = kBK / 8, kRowsPerRun = 1024 / kRowBytes;
-__device__ inline int swz_kc(int row) {
-  if constexpr (kBK == 32) return (((row >> 1) ^ (row >> 3)) & 1) << 1;
-  else return ((row >> 1) & 7) ^ ((row & 1) << 2);
-}
+// lane pattern): KC rows of 128 B (8 chunks) XOR the chunk with ((r >> 1) & 7) ^ ((r & 1) << 2),
+// which lets the fragment reads (16 consecutive rows per 16-lane group) run at full LDS rate;
+// NC rows XOR with (k & 3) << 1 | (k >> 3 & 1) << 3 for the transpose reads (each 32-lane half of
+// a read touches 8 k rows x 32 bytes, which this spreads over all 64 banks for 256- and 512-byte
+// rows alike).
+__device__ inline int swz_kc(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
 __device__ inline int swz_nc(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
 __device__ inline float bf2f(unsigned short b) { return __uint_as_float(uint32_t(b) << 16); }
@@ -94,27 +123,30 @@ __device__ inline void store_bf16x4(void* base, int64_t elem, float a, float b, 
 }
 
 // ------------------------------------------------------------------------------ operand staging
-// Each operand tile (16 KB = 16 runs of 1 KB) is filled by direct global -> LDS loads
-// (buffer_load_dwordx4 ... lds): one load instruction writes 64 consecutive 16-byte LDS slots,
-// lane l into slot l. Each of the 8 waves owns two runs of each tile; each lane loads the global
-// chunk that belongs in its slot, so the swizzled layout comes from the choice of global address.
-//   KC tile [256 rows][32 k]: run s holds rows 16s..16s+15; lane l -> row 16s + l/4, slot chunk l%4.
-//   NC tile [32 k][256]     : run s holds k rows 2s, 2s+1; lane l -> k 2s + l/32, slot chunk l%32.
-constexpr int kRuns = kTileBytes / 1024 / 8;  // runs per wave per operand tile
+// Each operand tile is filled by direct global -> LDS loads (buffer_load_dwordx4 ... lds): one load
+// instruction writes 64 consecutive 16-byte LDS slots (a 1-KB run), lane l into slot l. Each wave
+// owns RUNS consecutive runs of each tile; each lane loads the global chunk that belongs in its
+// slot, so the swizzled layout comes from the choice of global address.
+//   KC tile [rows][64 k]: run s holds rows 8s..8s+7; lane l -> row 8s + l/8, slot chunk l%8.
+//   NC tile [64 k][COLS]: run s holds 1024 / (2 COLS) k rows; lane l -> k row
+//                         s * (1024 / (2 COLS)) + l / (COLS / 8), slot chunk l % (COLS / 8).
 
+template <int RUNS>
 struct KcLoader {
-  uint32_t off[kRuns];   // byte offset of the lane's chunk at k0 = 0
-  uint32_t kel[kRuns];   // k index (element) of the lane's chunk at k0 = 0
-  uint32_t valid;        // bit j: the chunk's row lies inside the operand
-  __device__ void init(int wave, int lane, int64_t ld, int row0, int row_limit, bool dual, int64_t half) {
+  uint32_t off[RUNS];   // byte offset of the lane's chunk at k0 = 0
+  uint32_t kel[RUNS];   // k index (element) of the lane's chunk at k0 = 0
+  uint32_t valid;       // bit j: the chunk's row lies inside the operand
+  // dual: the tile's first half_rows rows come from row0.., the rest from half + row0..
+  __device__ void init(int wave, int lane, int64_t ld, int row0, int row_limit, bool dual, int64_t half,
+                       int half_rows) {
     valid = 0;
-    for (int j = 0; j < kRuns; ++j) {
-      const int r = (wave * kRuns + j) * kRowsPerRun + lane / kChunks;  // tile row
+    for (int j = 0; j < RUNS; ++j) {
+      const int r = (wave * RUNS + j) * kRowsPerRun + lane / kChunks;  // tile row
       const int ch = (lane % kChunks) ^ swz_kc(r);                      // logical chunk (k / 8)
       int li = r, gro;
       if (dual) {
-        li = r & 127;
-        gro = (r < 128) ? row0 + li : int(half) + row0 + li;
+        li = r % half_rows;
+        gro = (r < half_rows) ? row0 + li : int(half) + row0 + li;
       } else {
         gro = row0 + r;
       }
@@ -124,32 +156,35 @@ struct KcLoader {
       valid |= uint32_t(ok) << j;
     }
   }
-  __device__ void issue(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int K) const {
-    for (int j = 0; j < kRuns; ++j) {
+  __device__ void issue(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int K, int j0, int j1) const {
+    for (int j = j0; j < j1; ++j) {
       const bool ok = ((valid >> j) & 1) && int(kel[j]) + k0 < K;
       const uint32_t o = ok ? off[j] + uint32_t(k0) * 2 : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * kRuns + j) * 1024), 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16, o, 0, 0, 0);
     }
   }
   // every chunk in range: k advances through the scalar offset, no per-lane arithmetic
-  __device__ void issue_fast(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0) const {
-    for (int j = 0; j < kRuns; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * kRuns + j) * 1024), 16, off[j],
+  __device__ void issue_fast(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int j0, int j1) const {
+    for (int j = j0; j < j1; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16, off[j],
                                                uint32_t(k0) * 2, 0, 0);
   }
 };
 
+template <int RUNS, int COLS>
 struct NcLoader {
-  uint32_t col_off[kRuns];  // byte offset of the lane's chunk within a k row
-  uint32_t krow[kRuns];     // tile k row of the lane's chunk
-  uint32_t valid;           // bit j: the chunk's columns lie inside the operand
+  static constexpr int kCpr = COLS / 8;               // chunks per k row
+  static constexpr int kKpr = 1024 / (COLS * 2);      // k rows per run
+  uint32_t col_off[RUNS];  // byte offset of the lane's chunk within a k row
+  uint32_t krow[RUNS];     // tile k row of the lane's chunk
+  uint32_t valid;          // bit j: the chunk's columns lie inside the operand
   uint32_t ld_bytes;
   __device__ void init(int wave, int lane, int64_t ld, int col0, int col_limit) {
     valid = 0;
     ld_bytes = uint32_t(ld * 2);
-    for (int j = 0; j < kRuns; ++j) {
-      const int k = (wave * kRuns + j) * 2 + (lane >> 5);
-      const int ch = (lane & 31) ^ swz_nc(k);
+    for (int j = 0; j < RUNS; ++j) {
+      const int k = (wave * RUNS + j) * kKpr + lane / kCpr;
+      const int ch = (lane % kCpr) ^ swz_nc(k);
       const int c = col0 + ch * 8;
       const bool ok = c < col_limit;
       col_off[j] = ok ? uint32_t(c) * 2 : 0u;
@@ -157,48 +192,48 @@ struct NcLoader {
       valid |= uint32_t(ok) << j;
     }
   }
-  __device__ void issue(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int K) const {
-    for (int j = 0; j < kRuns; ++j) {
+  __device__ void issue(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int K, int j0, int j1) const {
+    for (int j = j0; j < j1; ++j) {
       const int k = k0 + int(krow[j]);
       const bool ok = ((valid >> j) & 1) && k < K;
       const uint32_t o = ok ? uint32_t(k) * ld_bytes + col_off[j] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * kRuns + j) * 1024), 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16, o, 0, 0, 0);
     }
   }
-  __device__ void issue_fast(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0) const {
-    for (int j = 0; j < kRuns; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * kRuns + j) * 1024), 16,
+  __device__ void issue_fast(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int j0, int j1) const {
+    for (int j = j0; j < j1; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16,
                                                krow[j] * ld_bytes + col_off[j], uint32_t(k0) * ld_bytes, 0, 0);
   }
 };
 
-// Wait until at most N of this wave's buffer loads are outstanding, then meet the other waves.
-// Pinned in place (scheduling barriers) so that MFMA work is not moved across it.
-template <int N>
+// Wait until all of this wave's buffer loads have landed, then meet the other waves. Pinned in
+// place (scheduling barriers) so that MFMA work is not moved across it.
 __device__ inline void wait_loads_and_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
-
 // ------------------------------------------------------------------------------ fragment reads
-// KC fragment: lane l gets operand[rb + l%16][8 (l/16) + 0..7].
-__device__ inline bf16x8 frag_kc(const char* tile, int rb, int lane, int kk = 0) {
+// KC fragment: lane l gets operand[rb + l%16][32 kk + 8 (l/16) + 0..7].
+__device__ inline bf16x8 frag_kc(const char* tile, int rb, int lane, int kk) {
   const int row = rb + (lane & 15);
   const int ch = kk * 4 + (lane >> 4);
   return *reinterpret_cast<const bf16x8*>(tile + row * kRowBytes + ((ch ^ swz_kc(row)) << 4));
 }
 
-// NC fragment: same element assignment as frag_kc, from a [32 k][256] tile, cb = first column.
-__device__ inline bf16x8 frag_nc(const char* tile, int cb, int lane, int kk = 0) {
+// NC fragment: same element assignment as frag_kc, from a [64 k][COLS] tile, cb = first column.
+template <int COLS>
+__device__ inline bf16x8 frag_nc(const char* tile, int cb, int lane, int kk) {
+  constexpr int kRow = COLS * 2;
   const int g = lane >> 4, v = (lane & 15) >> 2, q = lane & 3;
   const int chunk = (cb >> 3) + (q >> 1);
   const int k0 = kk * 32 + 8 * g + v;
   const int k1 = k0 + 4;
   const int byte_in = (q & 1) << 3;
-  const char* p0 = tile + k0 * 512 + ((chunk ^ swz_nc(k0)) << 4) + byte_in;
-  const char* p1 = tile + k1 * 512 + ((chunk ^ swz_nc(k1)) << 4) + byte_in;
+  const char* p0 = tile + k0 * kRow + ((chunk ^ swz_nc(k0)) << 4) + byte_in;
+  const char* p1 = tile + k1 * kRow + ((chunk ^ swz_nc(k1)) << 4) + byte_in;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -272,26 +307,25 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, const
   }
 }
 
-// ------------------------------------------------------------------------------------- kernel
-// 8 waves (2 per SIMD, so one wave's waits hide under the other's MFMAs) in a 2 (m) x 4 (n) grid;
-// wave tile 128 x 64 = 8 x 4 MFMA tiles, 128 fp32 accumulators per lane.
-constexpr int kWavesN = 4;
-constexpr int kFM = 8, kFN = 4;  // MFMA tiles per wave along m and n
+}  // namespace
 
-template <int LAYOUT, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
+// ------------------------------------------------------------------------------------- kernel
+template <class TL, int LAYOUT, int EPI>
+__global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(GemmArgs g) {
   constexpr bool kADirect = LAYOUT != kWgrad;   // A read along k
   constexpr bool kBDirect = LAYOUT == kFwd;     // B read along k
-  constexpr bool kDual = EPI == kEpiSwiglu;     // B tile = 128 gate rows + 128 up rows
-  constexpr int kOutBN = kDual ? kBN / 2 : kBN; // output columns per block
-  constexpr int kWaveN = kOutBN / kWavesN;      // output columns per wave (64, SwiGLU 32)
+  constexpr bool kDual = EPI == kEpiSwiglu;     // B tile = BN/2 gate rows + BN/2 up rows
+  constexpr int kFM = TL::kFM, kFN = TL::kFN;
+  constexpr int kOutBN = kDual ? TL::BN / 2 : TL::BN;  // output columns per block
+  constexpr int kWaveN = kOutBN / TL::kWavesN;         // output columns per wave
+  constexpr int kARuns = TL::kARuns, kBRuns = TL::kBRuns;
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: LDS addresses stay scalar
-  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int wm = wave / TL::kWavesN, wn = wave % TL::kWavesN;
 
   // ---- tile coordinates: contiguous runs per XCD, grouped order inside
   const int T = g.tiles_m * g.tiles_n;
@@ -306,22 +340,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int gsz = min(g.tiles_m - first_m, kGroupM);
   const int tm = first_m + (tile % per_group) % gsz;
   const int tn = (tile % per_group) / gsz;
-  const int m0 = tm * kBM;
+  const int m0 = tm * TL::BM;
   const int n0 = tn * kOutBN;
 
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(g.A, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(g.B, g.b_bytes);
 
-  KcLoader aK, bK;
-  NcLoader aN, bN;
-  if constexpr (kADirect) aK.init(wave, lane, g.lda, m0, g.M, false, 0);
+  KcLoader<kARuns> aK;
+  KcLoader<kBRuns> bK;
+  NcLoader<kARuns, TL::BM> aN;
+  NcLoader<kBRuns, TL::BN> bN;
+  if constexpr (kADirect) aK.init(wave, lane, g.lda, m0, g.M, false, 0, TL::BM);
   else aN.init(wave, lane, g.lda, m0, g.M);
-  if constexpr (kBDirect) bK.init(wave, lane, g.ldb, n0, g.N, kDual, g.half);
+  if constexpr (kBDirect) bK.init(wave, lane, g.ldb, n0, g.N, kDual, g.half, TL::BN / 2);
   else bN.init(wave, lane, g.ldb, n0, g.N);
 
-  // B-tile column of fragment `in` (SwiGLU: fragments 0, 1 gate, 2, 3 up of the same outputs)
+  // B-tile column of fragment `in` (SwiGLU: the first half of the fragments gate, the second
+  // half up, for the same output columns)
   auto bcol = [&](int in) {
-    if constexpr (kDual) return (in < kFN / 2 ? 0 : 128) + wn * kWaveN + 16 * (in % (kFN / 2));
+    if constexpr (kDual) return (in < kFN / 2 ? 0 : TL::BN / 2) + wn * kWaveN + 16 * (in % (kFN / 2));
     else return wn * kWaveN + 16 * in;
   };
   // output column of accumulator column `in` (SwiGLU: of the gate half)
@@ -341,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
       const float* C = reinterpret_cast<const float*>(g.C);
 #pragma unroll
       for (int im = 0; im < kFM; ++im) {
-        const int m = m0 + wm * 128 + 16 * im + (lane & 15);
+        const int m = m0 + wm * TL::kWaveM + 16 * im + (lane & 15);
 #pragma unroll
         for (int in = 0; in < kFN; ++in) {
           const int n = ocol(in) + 4 * (lane >> 4);
@@ -354,63 +391,79 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int nk = (g.K + kBK - 1) / kBK;
 
   // block-uniform: every row and column of this tile lies inside the operands
-  const bool interior = (m0 + kBM <= g.M) && (n0 + kOutBN <= g.N);
-  auto issue = [&](int kb) {
-    char* a_tile = smem + (kb % kStages) * kStageBytes;
-    char* b_tile = a_tile + kTileBytes;
+  const bool interior = (m0 + TL::BM <= g.M) && (n0 + kOutBN <= g.N);
+  // Queue part of block kb's loads: part 0 / 1 = first / second half of the A runs, 2 / 3 = of
+  // the B runs, -1 = all.
+  auto issue = [&](int kb, int part) {
+    char* a_tile = smem + (kb & 1) * TL::kStageBytes;
+    char* b_tile = a_tile + TL::kATileBytes;
     const int k0 = kb * kBK;
+    const bool doA = part < 2, doB = part < 0 || part >= 2;
+    const int a0 = part < 0 ? 0 : (part & 1) * (kARuns / 2), a1 = part < 0 ? kARuns : a0 + kARuns / 2;
+    const int b0 = part < 0 ? 0 : (part & 1) * (kBRuns / 2), b1 = part < 0 ? kBRuns : b0 + kBRuns / 2;
     if (interior && k0 + kBK <= g.K) {
-      if constexpr (kADirect) aK.issue_fast(rsA, a_tile, wave, k0); else aN.issue_fast(rsA, a_tile, wave, k0);
-      if constexpr (kBDirect) bK.issue_fast(rsB, b_tile, wave, k0); else bN.issue_fast(rsB, b_tile, wave, k0);
+      if (doA) {
+        if constexpr (kADirect) aK.issue_fast(rsA, a_tile, wave, k0, a0, a1);
+        else aN.issue_fast(rsA, a_tile, wave, k0, a0, a1);
+      }
+      if (doB) {
+        if constexpr (kBDirect) bK.issue_fast(rsB, b_tile, wave, k0, b0, b1);
+        else bN.issue_fast(rsB, b_tile, wave, k0, b0, b1);
+      }
     } else {
-      if constexpr (kADirect) aK.issue(rsA, a_tile, wave, k0, g.K); else aN.issue(rsA, a_tile, wave, k0, g.K);
-      if constexpr (kBDirect) bK.issue(rsB, b_tile, wave, k0, g.K); else bN.issue(rsB, b_tile, wave, k0, g.K);
+      if (doA) {
+        if constexpr (kADirect) aK.issue(rsA, a_tile, wave, k0, g.K, a0, a1);
+        else aN.issue(rsA, a_tile, wave, k0, g.K, a0, a1);
+      }
+      if (doB) {
+        if constexpr (kBDirect) bK.issue(rsB, b_tile, wave, k0, g.K, b0, b1);
+        else bN.issue(rsB, b_tile, wave, k0, g.K, b0, b1);
+      }
     }
   };
-  auto frags = [&](int kb, bf16x8 (&af)[kFM], bf16x8 (&bf)[kFN], int kk = 0) {
-    const char* a_tile = smem + (kb % kStages) * kStageBytes;
-    const char* b_tile = a_tile + kTileBytes;
+  auto frags = [&](int kb, bf16x8 (&af)[kFM], bf16x8 (&bf)[kFN], int kk) {
+    const char* a_tile = smem + (kb & 1) * TL::kStageBytes;
+    const char* b_tile = a_tile + TL::kATileBytes;
 #pragma unroll
     for (int in = 0; in < kFN; ++in) {
       if constexpr (kBDirect) bf[in] = frag_kc(b_tile, bcol(in), lane, kk);
-      else bf[in] = frag_nc(b_tile, bcol(in), lane, kk);
+      else bf[in] = frag_nc<TL::BN>(b_tile, bcol(in), lane, kk);
     }
 #pragma unroll
     for (int im = 0; im < kFM; ++im) {
-      const int rbase = wm * 128 + 16 * im;
+      const int rbase = wm * TL::kWaveM + 16 * im;
       if constexpr (kADirect) af[im] = frag_kc(a_tile, rbase, lane, kk);
-      else af[im] = frag_nc(a_tile, rbase, lane, kk);
+      else af[im] = frag_nc<TL::BM>(a_tile, rbase, lane, kk);
     }
   };
-  auto mfmas = [&](const bf16x8 (&af)[kFM], const bf16x8 (&bf)[kFN]) {
+  auto mfmas = [&](const bf16x8 (&af)[kFM], const bf16x8 (&bf)[kFN], int im0, int im1) {
 #pragma unroll
-    for (int im = 0; im < kFM; ++im)
+    for (int im = im0; im < im1; ++im)
 #pragma unroll
       for (int in = 0; in < kFN; ++in)
         acc[im][in] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[in], af[im], acc[im][in], 0, 0, 0);
   };
-  // wait for block `kb` to land in LDS, given how many later blocks have been issued
-  constexpr int kAhead = kStages - 1;
-  auto wait_block = [&](int kb) {
-    const int later = min(nk - 1, kb + kAhead - 1) - kb;  // blocks issued after kb
-    if constexpr (kAhead >= 3) {
-      if (later >= 2) { wait_loads_and_barrier<2 * kLoadsPerBlock>(); return; }
-    }
-    if (later >= 1) wait_loads_and_barrier<kLoadsPerBlock>();
-    else wait_loads_and_barrier<0>();
-  };
 
-  if (nk > 0)
-    for (int kb = 0; kb < min(nk, kAhead); ++kb) issue(kb);
+  // Main loop. Block kb+1 is loaded while block kb is multiplied; its four load groups are placed
+  // between the four MFMA row groups of the first 32-wide step (pinned by scheduling barriers), so
+  // the load issue overlaps MFMA work instead of stalling every wave right after the barrier.
+  constexpr int kRowsPerGroup = kFM >= 4 ? kFM / 4 : 1;
+  constexpr int kGroups = kFM / kRowsPerGroup;
+  if (nk > 0) issue(0, -1);
   for (int kb = 0; kb < nk; ++kb) {
-    wait_block(kb);
-    if (kb + kAhead < nk) issue(kb + kAhead);
+    wait_loads_and_barrier();
+    const bool more = kb + 1 < nk;
+    bf16x8 af[kFM], bf[kFN];
+    frags(kb, af, bf, 0);
 #pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      bf16x8 af[kFM], bf[kFN];
-      frags(kb, af, bf, kk);
-      mfmas(af, bf);
+    for (int q = 0; q < 4; ++q) {
+      if (q < kGroups) mfmas(af, bf, q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) issue(kb + 1, q);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    frags(kb, af, bf, 1);
+    mfmas(af, bf, 0, kFM);
   }
   __syncthreads();
 
@@ -425,10 +478,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     for (int in = 0; in < kFN; ++in)
       *reinterpret_cast<f32x4*>(park + prow * kEpLd + 16 * in + pcol) = acc[im][in];
     __syncthreads();
-    const int mbase = m0 + wm * 128 + 16 * im;
-    // a parked row holds the wave's 64 accumulator columns (SwiGLU: 32 gate then 32 up)
-    constexpr int kOutCols = kDual ? 32 : 64;
-    constexpr int kLanesPerRow = kOutCols / 4;
+    const int mbase = m0 + wm * TL::kWaveM + 16 * im;
+    // a parked row holds the wave's 16 kFN accumulator columns (SwiGLU: kWaveN gate then
+    // kWaveN up)
+    constexpr int kLanesPerRow = kWaveN / 4;
     constexpr int kRowsPerPass = 64 / kLanesPerRow;
 #pragma unroll 1
     for (int p = 0; p < 16 / kRowsPerPass; ++p) {
@@ -439,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
         const f32x4 xv = *reinterpret_cast<const f32x4*>(park + r * kEpLd + c);
         const float x[4] = {xv[0], xv[1], xv[2], xv[3]};
         if constexpr (kDual) {
-          const f32x4 yv = *reinterpret_cast<const f32x4*>(park + r * kEpLd + 32 + c);
+          const f32x4 yv = *reinterpret_cast<const f32x4*>(park + r * kEpLd + kWaveN + c);
           const float y[4] = {yv[0], yv[1], yv[2], yv[3]};
           epilogue4<EPI>(g, m, n, x, y);
         } else {
@@ -450,6 +503,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     __syncthreads();
   }
 }
+
+// Explicit instantiations: with only implicit ones (from the launch switch) hipcc emits the host
+// launch stub of the first instance alone.
+#define TPS_GEMM_INSTANCES(TL)                                  \
+  template __global__ void gemm_kernel<TL, kFwd, kEpiBf16>(GemmArgs);     \
+  template __global__ void gemm_kernel<TL, kFwd, kEpiGelu>(GemmArgs);     \
+  template __global__ void gemm_kernel<TL, kFwd, kEpiSwiglu>(GemmArgs);   \
+  template __global__ void gemm_kernel<TL, kDgrad, kEpiBf16>(GemmArgs);   \
+  template __global__ void gemm_kernel<TL, kDgrad, kEpiDgelu>(GemmArgs);  \
+  template __global__ void gemm_kernel<TL, kDgrad, kEpiDswiglu>(GemmArgs); \
+  template __global__ void gemm_kernel<TL, kWgrad, kEpiF32>(GemmArgs);
+TPS_GEMM_INSTANCES(TileL)
+TPS_GEMM_INSTANCES(TileS)
+#undef TPS_GEMM_INSTANCES
+
+namespace {
 
 // ------------------------------------------------------------------------------- column sums
 
@@ -476,18 +545,36 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* partials
 
 __global__ void fence_kernel() {}
 
-template <int L, int E>
+template <class TL, int L, int E>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<L, E>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<TL, L, E>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLdsBytes);
   if (attr != hipSuccess) return attr;
   const int grid = g.tiles_m * g.tiles_n;
   if (start || stop)
-    hipExtLaunchKernelGGL((gemm_kernel<L, E>), dim3(grid), dim3(kThreads), kLdsBytes, s, start, stop, 0, g);
+    hipExtLaunchKernelGGL((gemm_kernel<TL, L, E>), dim3(grid), dim3(TL::kThreads), TL::kLdsBytes, s, start, stop,
+                          0, g);
   else
-    hipLaunchKernelGGL((gemm_kernel<L, E>), dim3(grid), dim3(kThreads), kLdsBytes, s, g);
+    hipLaunchKernelGGL((gemm_kernel<TL, L, E>), dim3(grid), dim3(TL::kThreads), TL::kLdsBytes, s, g);
   return hipGetLastError();
+}
+
+template <class TL>
+hipError_t launch_tile(GemmArgs& g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  const int out_bn = epi == kEpiSwiglu ? TL::BN / 2 : TL::BN;
+  g.tiles_m = (g.M + TL::BM - 1) / TL::BM;
+  g.tiles_n = (g.N + out_bn - 1) / out_bn;
+  switch (layout * 8 + epi) {
+    case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
+    case kFwd * 8 + kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
+    case kFwd * 8 + kEpiSwiglu: return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
+    case kDgrad * 8 + kEpiBf16: return launch_one<TL, kDgrad, kEpiBf16>(g, stream, start, stop);
+    case kDgrad * 8 + kEpiDgelu: return launch_one<TL, kDgrad, kEpiDgelu>(g, stream, start, stop);
+    case kDgrad * 8 + kEpiDswiglu: return launch_one<TL, kDgrad, kEpiDswiglu>(g, stream, start, stop);
+    case kWgrad * 8 + kEpiF32: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, stop);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 uint32_t extent_bytes(int64_t rows, int64_t ld, int64_t cols) {
@@ -498,27 +585,32 @@ uint32_t extent_bytes(int64_t rows, int64_t ld, int64_t cols) {
 
 }  // namespace
 
-hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+int choose_tile(int64_t M, int64_t N, int epi) {
+  // Estimated time in units of one large tile's work at the large tile's rate: whole waves of
+  // resident blocks (256 large, 512 small), a small tile holding a quarter of the work at
+  // kSmallTileRate of the large tile's per-CU throughput (measured on gfx950).
+  constexpr double kSmallTileRate = 0.7;
+  const int64_t out_l = epi == kEpiSwiglu ? TileL::BN / 2 : TileL::BN;
+  const int64_t out_s = epi == kEpiSwiglu ? TileS::BN / 2 : TileS::BN;
+  const int64_t tl = ((M + TileL::BM - 1) / TileL::BM) * ((N + out_l - 1) / out_l);
+  const int64_t ts = ((M + TileS::BM - 1) / TileS::BM) * ((N + out_s - 1) / out_s);
+  const double cost_l = double((tl + kCUs - 1) / kCUs);
+  const double cost_s = double((ts + 2 * kCUs - 1) / (2 * kCUs)) * 0.5 / kSmallTileRate;
+  return cost_s < cost_l ? kTileSmall : kTileLarge;
+}
+
+hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                       int tile) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  const int out_bn = epi == kEpiSwiglu ? kBN / 2 : kBN;
-  g.tiles_m = (g.M + kBM - 1) / kBM;
-  g.tiles_n = (g.N + out_bn - 1) / out_bn;
   // operand extents for the buffer range checks
   if (layout == kWgrad) g.a_bytes = extent_bytes(g.K, g.lda, g.M);
   else g.a_bytes = extent_bytes(g.M, g.lda, g.K);
   if (layout == kFwd) g.b_bytes = extent_bytes(epi == kEpiSwiglu ? g.half + g.N : g.N, g.ldb, g.K);
   else g.b_bytes = extent_bytes(g.K, g.ldb, g.N);
   if (g.K <= 0) { g.a_bytes = 0; g.b_bytes = 0; }
-  switch (layout * 8 + epi) {
-    case kFwd * 8 + kEpiBf16: return launch_one<kFwd, kEpiBf16>(g, stream, start, stop);
-    case kFwd * 8 + kEpiGelu: return launch_one<kFwd, kEpiGelu>(g, stream, start, stop);
-    case kFwd * 8 + kEpiSwiglu: return launch_one<kFwd, kEpiSwiglu>(g, stream, start, stop);
-    case kDgrad * 8 + kEpiBf16: return launch_one<kDgrad, kEpiBf16>(g, stream, start, stop);
-    case kDgrad * 8 + kEpiDgelu: return launch_one<kDgrad, kEpiDgelu>(g, stream, start, stop);
-    case kDgrad * 8 + kEpiDswiglu: return launch_one<kDgrad, kEpiDswiglu>(g, stream, start, stop);
-    case kWgrad * 8 + kEpiF32: return launch_one<kWgrad, kEpiF32>(g, stream, start, stop);
-    default: return hipErrorInvalidValue;
-  }
+  if (tile == kTileAuto) tile = choose_tile(g.M, g.N, epi);
+  if (tile == kTileSmall) return launch_tile<TileS>(g, layout, epi, stream, start, stop);
+  return launch_tile<TileL>(g, layout, epi, stream, start, stop);
 }
 
 hipError_t launch_fence(hipStream_t stream) {

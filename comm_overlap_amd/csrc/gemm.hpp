@@ -45,11 +45,18 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
 };
 
+// Block tile of a launch: 256 x 256 (one block per CU) or 128 x 128 (two per CU); both reduce k in
+// the same order, so the choice never changes a result bit.
+enum GemmTile : int { kTileAuto = 0, kTileLarge = 1, kTileSmall = 2 };
+
+// The tile kTileAuto resolves to for an M x N product (N: output columns).
+int choose_tile(int64_t M, int64_t N, int epi);
+
 // Queue one GEMM on `stream`. With `start`/`stop` events the launch records the kernel's own start
 // and end times in them (timestamps of the dispatch itself, no extra marker packets).
 // Returns hipSuccess or the launch error.
 hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start = nullptr,
-                       hipEvent_t stop = nullptr);
+                       hipEvent_t stop = nullptr, int tile = kTileAuto);
 
 // A one-wave kernel that does nothing. Queued on a stream after DMA-engine copies it completes only
 // after them (stream order), so an event recorded after it marks the copies' completion.

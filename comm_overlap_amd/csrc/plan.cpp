@@ -68,8 +68,11 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   if (!d) return fail(TPSLICE_ERR_INVALID, "tpslice_plan: desc is NULL");
   if (d->act != TPSLICE_ACT_GELU && d->act != TPSLICE_ACT_SWIGLU)
     return fail(TPSLICE_ERR_INVALID, "act %d is not TPSLICE_ACT_GELU or TPSLICE_ACT_SWIGLU", d->act);
-  if (d->flags & ~(TPSLICE_F_SERIALIZE | TPSLICE_F_COPY_BLIT | TPSLICE_F_PIPELINE))
+  if (d->flags & ~(TPSLICE_F_SERIALIZE | TPSLICE_F_COPY_BLIT | TPSLICE_F_PIPELINE | TPSLICE_F_TILE_LARGE |
+                   TPSLICE_F_TILE_SMALL))
     return fail(TPSLICE_ERR_INVALID, "unknown flag bits 0x%x", d->flags);
+  if ((d->flags & TPSLICE_F_TILE_LARGE) && (d->flags & TPSLICE_F_TILE_SMALL))
+    return fail(TPSLICE_ERR_INVALID, "TPSLICE_F_TILE_LARGE and TPSLICE_F_TILE_SMALL are exclusive");
   if (d->tokens < 0) return fail(TPSLICE_ERR_SHAPE, "tokens %lld < 0", (long long)d->tokens);
   if (d->hidden <= 0 || d->hidden % 8)
     return fail(TPSLICE_ERR_SHAPE, "hidden %lld must be a positive multiple of 8", (long long)d->hidden);
@@ -121,7 +124,7 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   p->r = d->n_row_slices; p->c = d->n_col_slices;
   p->Ms = M / p->r; p->hc = h / p->c;
   const bool serial = d->flags & TPSLICE_F_SERIALIZE;
-  p->S = serial ? 1 : (d->n_streams ? d->n_streams : 1);
+  p->S = serial ? 1 : (d->n_streams ? d->n_streams : (p->r > 1 ? 2 : 1));
   p->E = serial ? 1 : (d->n_copy_streams ? d->n_copy_streams : 2);
   p->qh = qh; p->kvh = kvh;
   p->trace = 0;

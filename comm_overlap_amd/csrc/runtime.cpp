@@ -33,6 +33,7 @@ struct Runtime {
   hipEvent_t fork = nullptr;
   std::vector<hipEvent_t> piece;   // one per hand-off piece (and reused per call)
   std::vector<hipEvent_t> slice;   // one per row slice: its products are done
+  std::vector<hipEvent_t> lead;    // one per row slice: its first product is done
   std::vector<hipEvent_t> join_w, join_c;
   // pipelined hand-off: per (row slice, copy stream) completion of the latest call's copies
   std::vector<hipEvent_t> copied;       // [r][E]
@@ -68,6 +69,7 @@ void destroy_runtime(Runtime* rt) {
   if (rt->fork) (void)hipEventDestroy(rt->fork);
   for (auto e : rt->piece) (void)hipEventDestroy(e);
   for (auto e : rt->slice) (void)hipEventDestroy(e);
+  for (auto e : rt->lead) (void)hipEventDestroy(e);
   for (auto e : rt->join_w) (void)hipEventDestroy(e);
   for (auto e : rt->join_c) (void)hipEventDestroy(e);
   for (auto e : rt->copied) (void)hipEventDestroy(e);
@@ -116,8 +118,10 @@ tpslice_status_t ensure_runtime(tpslice_plan_s* p, Runtime** out) {
     for (auto& e : rt->join_c) if ((st = make_event(&e))) return st;
     rt->piece.resize(size_t(p->r) * p->c);
     rt->slice.resize(p->r);
+    rt->lead.resize(p->r);
     for (auto& e : rt->piece) if ((st = make_event(&e))) return st;
     for (auto& e : rt->slice) if ((st = make_event(&e))) return st;
+    for (auto& e : rt->lead) if ((st = make_event(&e))) return st;
     rt->copied.resize(size_t(p->r) * p->E);
     for (auto& e : rt->copied) if ((st = make_event(&e))) return st;
     rt->copied_pending.assign(size_t(p->r) * p->E, 0);
@@ -136,6 +140,8 @@ struct Schedule {
   bool serial;
   uint32_t copied = 0;  // bit k: copy stream k received a copy in this call (bit 31: caller stream)
   uint32_t slice_streams = 0;  // copy streams used by the current row slice's pieces
+  int lead_slice = -1;         // row slice whose first product has not been queued yet
+  int lead_done = -1;          // latest row slice whose first-product event this call recorded
 
   tpslice_status_t fence(hipStream_t s) {
     hipError_t e = launch_fence(s);
@@ -147,8 +153,16 @@ struct Schedule {
   int worker_id(int i) const { return serial ? -1 : i % p->S; }
   bool pipelined() const { return !serial && (p->desc.flags & TPSLICE_F_PIPELINE); }
 
-  // Pipelined mode: row slice i's products wait for the previous call's hand-off of row slice i.
+  // Row slices on different worker streams start in order: slice i's first product waits for
+  // slice i-1's first product, so it runs beside slice i-1's later products (filling the compute
+  // units they leave idle) and the slices finish one after another, each hand-off starting while
+  // later slices still compute. Pipelined mode: row slice i's products also wait for the previous
+  // call's hand-off of row slice i.
   tpslice_status_t slice_begin(int i) {
+    if (serial) return TPSLICE_OK;
+    lead_slice = i;
+    if (i > 0 && lead_done == i - 1 && worker(i) != worker(i - 1))
+      TPS_HIP(hipStreamWaitEvent(worker(i), rt->lead[i - 1], 0));
     if (!pipelined()) return TPSLICE_OK;
     for (int k = 0; k < p->E; ++k) {
       const size_t x = size_t(i) * p->E + k;
@@ -302,8 +316,15 @@ struct Schedule {
       e0 = rt->tpool[t.ev0];
       e1 = rt->tpool[t.ev1];
     }
-    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1);
+    const uint32_t f = p->desc.flags;
+    const int tile = (f & TPSLICE_F_TILE_LARGE) ? kTileLarge : (f & TPSLICE_F_TILE_SMALL) ? kTileSmall : kTileAuto;
+    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1, tile);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
+    if (i >= 0 && i == lead_slice) {
+      TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
+      lead_slice = -1;
+      lead_done = i;
+    }
     if (tr) rt->slots.push_back(t);
     return TPSLICE_OK;
   }

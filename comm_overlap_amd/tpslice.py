@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libtpslice.so")
 
 OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 ACT_GELU, ACT_SWIGLU = 1, 2
-F_SERIALIZE, F_COPY_BLIT, F_PIPELINE = 0x1, 0x2, 0x4
+F_SERIALIZE, F_COPY_BLIT, F_PIPELINE, F_TILE_LARGE, F_TILE_SMALL = 0x1, 0x2, 0x4, 0x8, 0x10
 OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD = range(4)
 EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice_plan_piece",
            "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",
@@ -137,6 +137,7 @@ class Config:
     serialize: bool = False
     copy_blit: bool = False
     pipeline: bool = False
+    tile: str = "auto"  # "auto", "large" (256 x 256 block tiles) or "small" (128 x 128)
 
     def desc(self) -> Desc:
         return Desc(self.tokens, self.hidden, self.ffn, self.tp_size, self.n_row_slices, self.n_col_slices,
@@ -144,7 +145,8 @@ class Config:
                     {"gelu": ACT_GELU, "swiglu": ACT_SWIGLU}.get(self.act, 0), self.n_streams,
                     self.n_copy_streams,
                     (F_SERIALIZE if self.serialize else 0) | (F_COPY_BLIT if self.copy_blit else 0)
-                    | (F_PIPELINE if self.pipeline else 0))
+                    | (F_PIPELINE if self.pipeline else 0)
+                    | {"auto": 0, "large": F_TILE_LARGE, "small": F_TILE_SMALL}[self.tile])
 
 
 class Plan:

@@ -75,6 +75,10 @@ typedef enum {
                                     Abstract: independent pieces pipelined across the batch's work).
                                     Use tpslice_handoff_wait() before reading a hand-off buffer on
                                     another stream, or before freeing buffers the copies touch.    */
+#define TPSLICE_F_TILE_LARGE 0x8u  /* every product with 256 x 256 block tiles (ablation, testing)  */
+#define TPSLICE_F_TILE_SMALL 0x10u /* every product with 128 x 128 block tiles (ablation, testing);
+                                      by default each product takes the tile that fills the 256
+                                      CUs best. The tile never changes a result bit.               */
 
 typedef struct {
   int64_t tokens;         /* M: token rows in the batch (micro-batch x sequence, batch-major)         */
@@ -87,7 +91,9 @@ typedef struct {
   int32_t n_kv_heads;     /* full-model key/value heads (GQA); this rank holds max(1, n_kv/tp_size)   */
   int32_t head_dim;       /* d; multiple of 8                                                          */
   int32_t act;            /* tpslice_act_t                                                              */
-  int32_t n_streams;      /* worker streams for the slices (0 = default: 1, slices in order)          */
+  int32_t n_streams;      /* worker streams for the slices (0 = default: 2 when there are several row
+                             slices, else 1); slice i runs on stream i mod n_streams and starts once
+                             slice i-1's first product is done                                     */
   int32_t n_copy_streams; /* side streams for hand-off copies (0 = default: 2)                        */
   uint32_t flags;         /* TPSLICE_F_*                                                                */
 } tpslice_desc_t;

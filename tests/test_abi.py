@@ -138,3 +138,14 @@ def test_pipeline_flag_and_handoff_wait_without_gpu_work():
     # before any call there is nothing to wait for: returns OK without touching the GPU
     assert T.lib.tpslice_handoff_wait(p._h, None) == T.OK
     assert T.lib.tpslice_handoff_copy(None, None, None, None) == T.ERR_INVALID
+
+
+def test_plan_rejects_both_tile_flags():
+    import ctypes
+    d = T.Config(tokens=64, hidden=64, ffn=64).desc()
+    d.flags = T.F_TILE_LARGE | T.F_TILE_SMALL
+    h = ctypes.c_void_p()
+    assert T.lib.tpslice_plan(ctypes.byref(d), ctypes.byref(h)) == T.ERR_INVALID
+    assert b"exclusive" in T.lib.tpslice_last_error()
+    for tile in ("large", "small", "auto"):
+        T.Plan(T.Config(tokens=64, hidden=64, ffn=64, tile=tile)).close()

@@ -29,11 +29,12 @@ def _print_case(name, **kw):
     print(f"[case] {name} {kw}", flush=True)
 
 
+@pytest.mark.parametrize("tile", ["large", "small"])
 @pytest.mark.parametrize("w", [SMALL_GELU, SMALL_SWIGLU], ids=lambda w: w.key)
-def test_mlp_fwd_small(w):
-    _print_case("mlp_fwd", key=w.key)
+def test_mlp_fwd_small(w, tile):
+    _print_case("mlp_fwd", key=w.key, tile=tile)
     inp = synth.make_inputs(w)
-    plan = T.plan_for(w)
+    plan = T.plan_for(w, tile=tile)
     out = G.run_mlp_fwd(plan, inp)
     ref = G.oracle_mlp_fwd(inp, w.act)
     G.assert_parity(out["Z"], ref["Z"], "Z")
@@ -59,7 +60,8 @@ def test_slicing_is_bit_exact(w):
     _print_case("bitexact", key=w.key)
     inp = synth.make_inputs(w)
     base = G.run_mlp_fwd(T.plan_for(w, n_row_slices=1, n_col_slices=1), inp)
-    for kw in [dict(), dict(serialize=True), dict(copy_blit=True), dict(n_streams=3, n_copy_streams=2)]:
+    for kw in [dict(), dict(serialize=True), dict(copy_blit=True), dict(n_streams=3, n_copy_streams=2),
+               dict(tile="large"), dict(tile="small")]:
         out = G.run_mlp_fwd(T.plan_for(w, **kw), inp)
         assert torch.equal(out["Z"], base["Z"]), kw
         assert torch.equal(out["U"], base["U"]), kw
@@ -112,8 +114,9 @@ def test_attnproj_fwd_small(bias):
     G.assert_parity(out["QKV"], ref["QKV"], "QKV")
     G.assert_parity(out["Z"], ref["Z"], "Z")
     assert torch.equal(out["Zh"], out["Z"])
-    one = G.run_attn_fwd(T.plan_for(w, n_row_slices=1), inp, bias=bqkv)
-    assert torch.equal(one["Z"], out["Z"]) and torch.equal(one["QKV"], out["QKV"])
+    for kw in (dict(n_row_slices=1), dict(tile="large"), dict(tile="small")):
+        one = G.run_attn_fwd(T.plan_for(w, **kw), inp, bias=bqkv)
+        assert torch.equal(one["Z"], out["Z"]) and torch.equal(one["QKV"], out["QKV"]), kw
 
 
 @pytest.mark.parametrize("w", [SMALL_GELU, SMALL_SWIGLU], ids=lambda w: w.key)
@@ -130,6 +133,12 @@ def test_mlp_bwd_small(w):
     if w.bias:
         G.assert_parity(out["db1"], ref["db1"], "db1")
     assert torch.equal(out["dXh"], out["dX"])
+    # either block tile gives the same bits (same k order)
+    for tile in ("large", "small"):
+        o2 = G.run_mlp_bwd(T.plan_for(w, tile=tile), inp, with_bias=w.bias)
+        for k in ("dX", "dW1", "dW2", "db1"):
+            if out[k] is not None:
+                assert torch.equal(o2[k], out[k]), (tile, k)
     # accumulate = 1 adds to what is there; the token sum is not split, so it matches bitwise a
     # run whose fp32 accumulators start from the same values
     init = tuple(torch.randn_like(t) if t is not None else None for t in (out["dW1"], out["dW2"], out["db1"]))
@@ -156,6 +165,10 @@ def test_attnproj_bwd_small(bias):
     for k in ("dX", "dC", "dWqkv", "dWo") + (("dbqkv",) if bias else ()):
         G.assert_parity(out[k], ref[k], k)
     assert torch.equal(out["dXh"], out["dX"])
+    for kw in (dict(tile="large"), dict(tile="small"), dict(n_row_slices=1)):
+        o2 = G.run_attn_bwd(T.plan_for(w, **kw), inp, with_bias=bias)
+        for k in ("dX", "dC", "dWqkv", "dWo") + (("dbqkv",) if bias else ()):
+            assert torch.equal(o2[k], out[k]), (kw, k)
 
 
 def test_empty_batch():
