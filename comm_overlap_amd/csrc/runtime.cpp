@@ -34,6 +34,7 @@ struct Runtime {
   std::vector<hipEvent_t> piece;   // one per hand-off piece (and reused per call)
   std::vector<hipEvent_t> slice;   // one per row slice: its products are done
   std::vector<hipEvent_t> lead;    // one per row slice: its first product is done
+  std::vector<hipEvent_t> gather;  // one per worker stream: its queued products are done
   std::vector<hipEvent_t> join_w, join_c;
   // pipelined hand-off: per (row slice, copy stream) completion of the latest call's copies
   std::vector<hipEvent_t> copied;       // [r][E]
@@ -70,6 +71,7 @@ void destroy_runtime(Runtime* rt) {
   for (auto e : rt->piece) (void)hipEventDestroy(e);
   for (auto e : rt->slice) (void)hipEventDestroy(e);
   for (auto e : rt->lead) (void)hipEventDestroy(e);
+  for (auto e : rt->gather) (void)hipEventDestroy(e);
   for (auto e : rt->join_w) (void)hipEventDestroy(e);
   for (auto e : rt->join_c) (void)hipEventDestroy(e);
   for (auto e : rt->copied) (void)hipEventDestroy(e);
@@ -119,9 +121,11 @@ tpslice_status_t ensure_runtime(tpslice_plan_s* p, Runtime** out) {
     rt->piece.resize(size_t(p->r) * p->c);
     rt->slice.resize(p->r);
     rt->lead.resize(p->r);
+    rt->gather.resize(p->S);
     for (auto& e : rt->piece) if ((st = make_event(&e))) return st;
     for (auto& e : rt->slice) if ((st = make_event(&e))) return st;
     for (auto& e : rt->lead) if ((st = make_event(&e))) return st;
+    for (auto& e : rt->gather) if ((st = make_event(&e))) return st;
     rt->copied.resize(size_t(p->r) * p->E);
     for (auto& e : rt->copied) if ((st = make_event(&e))) return st;
     rt->copied_pending.assign(size_t(p->r) * p->E, 0);
@@ -302,8 +306,8 @@ struct Schedule {
 
   // Queue one product on worker(i) (i = -1: worker 0, all tokens), traced as `step`. A traced
   // product carries its timing events on the dispatch itself.
-  tpslice_status_t product(int i, int step, int piece, const GemmArgs& g, int layout, int epi) {
-    const int wi = i < 0 ? 0 : i;
+  tpslice_status_t product(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int on = 0) {
+    const int wi = i < 0 ? on : i;
     const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
     hipEvent_t e0 = nullptr, e1 = nullptr;
     TraceSlot t{};
@@ -330,24 +334,23 @@ struct Schedule {
   }
 
   tpslice_status_t colsum(const void* X, int64_t ld, int64_t M, int64_t N, float* partials, float* out,
-                          int accumulate) {
-    return traced(worker(0), worker_id(0), TPSLICE_TRACE_COLSUM, TPSLICE_STEP_BIAS_GRAD, -1, -1, 0.0,
+                          int accumulate, int on = 0) {
+    return traced(worker(on), worker_id(on), TPSLICE_TRACE_COLSUM, TPSLICE_STEP_BIAS_GRAD, -1, -1, 0.0,
                   double(M) * double(N) * 2.0, [&] {
-      hipError_t e = launch_colsum(X, ld, int32_t(M), int32_t(N), partials, out, accumulate, worker(0));
+      hipError_t e = launch_colsum(X, ld, int32_t(M), int32_t(N), partials, out, accumulate, worker(on));
       if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "column-sum launch: %s", hipGetErrorString(e));
       return TPSLICE_OK;
     });
   }
 
-  // Make worker(0) wait until every row slice's products are finished.
+  // Make every worker stream wait until every row slice's products are finished, so that the
+  // products over all tokens that follow can be spread over the workers.
   tpslice_status_t gather_slices() {
-    if (serial) return TPSLICE_OK;
-    hipStream_t w0 = worker(0);
-    for (int i = 0; i < p->r; ++i) {
-      if (worker(i) == w0) continue;
-      TPS_HIP(hipEventRecord(rt->slice[i], worker(i)));
-      TPS_HIP(hipStreamWaitEvent(w0, rt->slice[i], 0));
-    }
+    if (serial || p->S == 1) return TPSLICE_OK;
+    for (int k = 0; k < p->S; ++k) TPS_HIP(hipEventRecord(rt->gather[k], rt->workers[k]));
+    for (int k = 0; k < p->S; ++k)
+      for (int q = 0; q < p->S; ++q)
+        if (q != k) TPS_HIP(hipStreamWaitEvent(rt->workers[k], rt->gather[q], 0));
     return TPSLICE_OK;
   }
 };
@@ -520,15 +523,15 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
   }
   // weight gradients over all tokens at once (one k run, no split of the token sum), under the
-  // last pieces' copies
+  // last pieces' copies; dW1 and dW2 run side by side on two workers
   TPS_TRY(S.gather_slices());
   GemmArgs g1 = args(dU, p->N1, X, p->h, dW1, p->h, p->N1, p->h, p->M);
   g1.accumulate = accumulate;
   TPS_TRY(S.product(-1, TPSLICE_STEP_MLP_DW1, -1, g1, kWgrad, kEpiF32));
   GemmArgs g2 = args(dY, p->h, H, p->Fp, dW2, p->Fp, p->h, p->Fp, p->M);
   g2.accumulate = accumulate;
-  TPS_TRY(S.product(-1, TPSLICE_STEP_MLP_DW2, -1, g2, kWgrad, kEpiF32));
-  if (db1) TPS_TRY(S.colsum(dU, p->N1, p->M, p->N1, partials, db1, accumulate));
+  TPS_TRY(S.product(-1, TPSLICE_STEP_MLP_DW2, -1, g2, kWgrad, kEpiF32, 1));
+  if (db1) TPS_TRY(S.colsum(dU, p->N1, p->M, p->N1, partials, db1, accumulate, 1));
   return S.join();
 }
 
@@ -564,17 +567,21 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
       if (dX_handoff) TPS_TRY(S.handoff(i, j, dX, dX_handoff));
     }
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
-    GemmArgs gc = args(bf(dY, r0 * p->h), p->h, Wo, p->ctx, bfw(dC, r0 * p->ctx), p->ctx, p->Ms, p->ctx, p->h);
-    TPS_TRY(S.product(i, TPSLICE_STEP_ATTN_DC, -1, gc, kDgrad, kEpiBf16));
   }
+  // dC is handed to the attention core, not off the GPU: it runs over all tokens (narrow output,
+  // so the whole batch fills the CUs better than a slice), beside the weight gradients
   TPS_TRY(S.gather_slices());
+  if (p->M > 0) {
+    GemmArgs gc = args(dY, p->h, Wo, p->ctx, dC, p->ctx, p->M, p->ctx, p->h);
+    TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DC, -1, gc, kDgrad, kEpiBf16, 1));
+  }
   GemmArgs go = args(dY, p->h, C, p->ctx, dWo, p->ctx, p->h, p->ctx, p->M);
   go.accumulate = accumulate;
-  TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DWO, -1, go, kWgrad, kEpiF32));
+  TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DWO, -1, go, kWgrad, kEpiF32, 1));
   GemmArgs gq = args(dQKV, p->qkv, X, p->h, dWqkv, p->h, p->qkv, p->h, p->M);
   gq.accumulate = accumulate;
-  TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DWQKV, -1, gq, kWgrad, kEpiF32));
-  if (dbqkv) TPS_TRY(S.colsum(dQKV, p->qkv, p->M, p->qkv, partials, dbqkv, accumulate));
+  TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DWQKV, -1, gq, kWgrad, kEpiF32, 0));
+  if (dbqkv) TPS_TRY(S.colsum(dQKV, p->qkv, p->M, p->qkv, partials, dbqkv, accumulate, 0));
   return S.join();
 }
 
