@@ -1,16 +1,19 @@
 // bf16 MFMA GEMM family for gfx950 (MI355X) with fused layer epilogues.
 //
-// Two block tiles share one kernel template (k step 64, v_mfma_f32_16x16x32_bf16, fp32
+// One kernel template serves a family of block tiles (k step 64, v_mfma_f32_16x16x32_bf16, fp32
 // accumulators, two waves per SIMD so one wave's waits hide under the other's MFMAs):
-//   * large: 256 x 256, 512 threads = 8 waves in a 2 x 4 grid, each wave 128 x 64 outputs
-//     (8 x 4 MFMA tiles), one block per CU, 128 KB of LDS;
-//   * small: 128 x 128, 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x 64 outputs
-//     (4 x 4 MFMA tiles), two blocks per CU, 64 KB of LDS each.
-// The launcher picks per product the tile that finishes it sooner on 256 CUs: the large tile
-// moves fewer bytes per flop, the small one keeps the CUs busy when the large tiles are too few
-// (thin slices, narrow weights). Both reduce k in the same order (ascending 64-wide blocks, two
-// 32-wide MFMA steps each), so every output element gets bitwise the same sum whichever tile,
-// slicing or tile position produced it.
+//   * 256 x 256, 8 waves (2 x 4), each wave 128 x 64 outputs, one block per CU (128 KB LDS);
+//   * 256 x 320 and 128 x 320, 8 waves, waves of 128 x 80 / 64 x 80 (products whose operands are
+//     both read along k, without the SwiGLU pairing), one block per CU;
+//   * 128 x 256, 8 waves, waves of 64 x 64, one block per CU (96 KB LDS);
+//   * 128 x 128, 4 waves (2 x 2), waves of 64 x 64, two blocks per CU (64 KB LDS each).
+// The launcher picks per product the tile with the smallest estimated time on 256 CUs: whole
+// rounds of resident blocks times the tile's work over its measured per-CU rate. Larger tiles move
+// fewer bytes per flop; the others cut the last, partly filled round (e.g. a 4096 x 5120 product is
+// 320 tiles of 256 x 256 - two rounds, the second a quarter full - but exactly 256 tiles of
+// 256 x 320). Every tile reduces k in the same order (ascending 64-wide blocks, two 32-wide MFMA
+// steps each), so every output element gets bitwise the same sum whichever tile, slicing or tile
+// position produced it.
 // Operand tiles go global -> LDS by direct loads (buffer_load_dwordx4 ... lds) into two LDS stages:
 // block k+1 loads while block k is multiplied, and the load instructions are spread between the
 // first MFMAs of the block instead of being issued together after the barrier. 16-byte XOR
@@ -56,11 +59,19 @@ struct Tile {
   static constexpr int kLdsBytes = 2 * kStageBytes;  // two stages
   static constexpr int kARuns = kATileBytes / 1024 / kWaves;  // 1-KB load runs per wave
   static constexpr int kBRuns = kBTileBytes / 1024 / kWaves;
-  static_assert(kARuns % 2 == 0 && kBRuns % 2 == 0, "loads are issued in halves");
-  static_assert(kFM % 4 == 0 || kFM == 2 || kFM == 1, "MFMA rows are issued in four groups");
+  // an operand read across k is staged as [64 k][tile columns]: a 1-KB load run must hold whole
+  // k rows, and the SwiGLU pairing needs an even number of MFMA columns per wave
+  static constexpr bool kNcA = 1024 % (BM * 2) == 0, kNcB = 1024 % (BN * 2) == 0;
+  static constexpr bool kDualOk = kFN % 2 == 0;
+  static_assert(kARuns >= 1 && kBRuns >= 1 && kATileBytes % (1024 * kWaves) == 0 &&
+                kBTileBytes % (1024 * kWaves) == 0, "tiles load in whole 1-KB runs per wave");
+  static_assert(kLdsBytes * BLOCKS <= 160 * 1024, "LDS per CU");
 };
 using TileL = Tile<256, 256, 2, 4, 1>;
 using TileS = Tile<128, 128, 2, 2, 2>;
+using TileW = Tile<256, 320, 2, 4, 1>;
+using TileN = Tile<128, 320, 2, 4, 1>;
+using TileM = Tile<128, 256, 2, 4, 1>;
 
 namespace {
 
@@ -319,6 +330,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   constexpr int kOutBN = kDual ? TL::BN / 2 : TL::BN;  // output columns per block
   constexpr int kWaveN = kOutBN / TL::kWavesN;         // output columns per wave
   constexpr int kARuns = TL::kARuns, kBRuns = TL::kBRuns;
+  static_assert((kADirect || TL::kNcA) && (kBDirect || TL::kNcB) && (!kDual || TL::kDualOk),
+                "tile does not support this operand layout");
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -399,8 +412,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
     char* b_tile = a_tile + TL::kATileBytes;
     const int k0 = kb * kBK;
     const bool doA = part < 2, doB = part < 0 || part >= 2;
-    const int a0 = part < 0 ? 0 : (part & 1) * (kARuns / 2), a1 = part < 0 ? kARuns : a0 + kARuns / 2;
-    const int b0 = part < 0 ? 0 : (part & 1) * (kBRuns / 2), b1 = part < 0 ? kBRuns : b0 + kBRuns / 2;
+    const int a0 = part < 0 || part == 0 ? 0 : kARuns / 2, a1 = part < 0 || part == 1 ? kARuns : kARuns / 2;
+    const int b0 = part < 0 || part == 2 ? 0 : kBRuns / 2, b1 = part < 0 || part == 3 ? kBRuns : kBRuns / 2;
     if (interior && k0 + kBK <= g.K) {
       if (doA) {
         if constexpr (kADirect) aK.issue_fast(rsA, a_tile, wave, k0, a0, a1);
@@ -483,12 +496,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
     // kWaveN up)
     constexpr int kLanesPerRow = kWaveN / 4;
     constexpr int kRowsPerPass = 64 / kLanesPerRow;
+    constexpr int kPasses = (16 + kRowsPerPass - 1) / kRowsPerPass;
 #pragma unroll 1
-    for (int p = 0; p < 16 / kRowsPerPass; ++p) {
+    for (int p = 0; p < kPasses; ++p) {
       const int r = p * kRowsPerPass + lane / kLanesPerRow;
       const int c = 4 * (lane % kLanesPerRow);
       const int m = mbase + r, n = n0 + wn * kWaveN + c;
-      if (m < g.M && n < g.N) {
+      if (lane < kRowsPerPass * kLanesPerRow && r < 16 && m < g.M && n < g.N) {
         const f32x4 xv = *reinterpret_cast<const f32x4*>(park + r * kEpLd + c);
         const float x[4] = {xv[0], xv[1], xv[2], xv[3]};
         if constexpr (kDual) {
@@ -516,7 +530,12 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   template __global__ void gemm_kernel<TL, kWgrad, kEpiF32>(GemmArgs);
 TPS_GEMM_INSTANCES(TileL)
 TPS_GEMM_INSTANCES(TileS)
+TPS_GEMM_INSTANCES(TileM)
 #undef TPS_GEMM_INSTANCES
+template __global__ void gemm_kernel<TileW, kFwd, kEpiBf16>(GemmArgs);
+template __global__ void gemm_kernel<TileW, kFwd, kEpiGelu>(GemmArgs);
+template __global__ void gemm_kernel<TileN, kFwd, kEpiBf16>(GemmArgs);
+template __global__ void gemm_kernel<TileN, kFwd, kEpiGelu>(GemmArgs);
 
 namespace {
 
@@ -565,16 +584,44 @@ hipError_t launch_tile(GemmArgs& g, int layout, int epi, hipStream_t stream, hip
   const int out_bn = epi == kEpiSwiglu ? TL::BN / 2 : TL::BN;
   g.tiles_m = (g.M + TL::BM - 1) / TL::BM;
   g.tiles_n = (g.N + out_bn - 1) / out_bn;
-  switch (layout * 8 + epi) {
-    case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
-    case kFwd * 8 + kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
-    case kFwd * 8 + kEpiSwiglu: return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
-    case kDgrad * 8 + kEpiBf16: return launch_one<TL, kDgrad, kEpiBf16>(g, stream, start, stop);
-    case kDgrad * 8 + kEpiDgelu: return launch_one<TL, kDgrad, kEpiDgelu>(g, stream, start, stop);
-    case kDgrad * 8 + kEpiDswiglu: return launch_one<TL, kDgrad, kEpiDswiglu>(g, stream, start, stop);
-    case kWgrad * 8 + kEpiF32: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, stop);
-    default: return hipErrorInvalidValue;
+  if constexpr (TL::kNcA && TL::kNcB && TL::kDualOk) {
+    switch (layout * 8 + epi) {
+      case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
+      case kFwd * 8 + kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
+      case kFwd * 8 + kEpiSwiglu: return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiBf16: return launch_one<TL, kDgrad, kEpiBf16>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiDgelu: return launch_one<TL, kDgrad, kEpiDgelu>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiDswiglu: return launch_one<TL, kDgrad, kEpiDswiglu>(g, stream, start, stop);
+      case kWgrad * 8 + kEpiF32: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, stop);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (layout * 8 + epi) {
+      case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
+      case kFwd * 8 + kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
+      default: return hipErrorInvalidValue;
+    }
   }
+}
+
+// Block tiles the launcher chooses from, with their per-CU throughput relative to 256 x 256 when
+// every CU is busy (measured on gfx950 on an 8192^3 product).
+struct TileChoice {
+  int id, bm, bn, blocks;
+  bool fit_only;  // considered only when the product runs alone (see choose_tile)
+  bool fwd_only;  // operands read along k only, no SwiGLU pairing
+  double rate;
+};
+constexpr TileChoice kTiles[] = {
+    {kTile256x256, 256, 256, 1, false, false, 1.00},
+    {kTile128x128, 128, 128, 2, false, false, 0.70},
+    {kTile256x320, 256, 320, 1, true, true, 0.92},
+    {kTile128x320, 128, 320, 1, true, true, 0.73},
+    {kTile128x256, 128, 256, 1, true, false, 0.77},
+};
+
+bool tile_supports(const TileChoice& t, int layout, int epi) {
+  return !t.fwd_only || (layout == kFwd && epi != kEpiSwiglu);
 }
 
 uint32_t extent_bytes(int64_t rows, int64_t ld, int64_t cols) {
@@ -585,22 +632,43 @@ uint32_t extent_bytes(int64_t rows, int64_t ld, int64_t cols) {
 
 }  // namespace
 
-int choose_tile(int64_t M, int64_t N, int epi) {
-  // Estimated time in units of one large tile's work at the large tile's rate: whole waves of
-  // resident blocks (256 large, 512 small), a small tile holding a quarter of the work at
-  // kSmallTileRate of the large tile's per-CU throughput (measured on gfx950).
-  constexpr double kSmallTileRate = 0.7;
-  const int64_t out_l = epi == kEpiSwiglu ? TileL::BN / 2 : TileL::BN;
-  const int64_t out_s = epi == kEpiSwiglu ? TileS::BN / 2 : TileS::BN;
-  const int64_t tl = ((M + TileL::BM - 1) / TileL::BM) * ((N + out_l - 1) / out_l);
-  const int64_t ts = ((M + TileS::BM - 1) / TileS::BM) * ((N + out_s - 1) / out_s);
-  const double cost_l = double((tl + kCUs - 1) / kCUs);
-  const double cost_s = double((ts + 2 * kCUs - 1) / (2 * kCUs)) * 0.5 / kSmallTileRate;
-  return cost_s < cost_l ? kTileSmall : kTileLarge;
+namespace {
+
+// Estimated time of an M x N product with tile t, in units of one 256 x 256 tile's work at that
+// tile's rate: whole rounds of resident blocks (256 CUs x blocks per CU), each round `blocks`
+// tiles' work per CU at the tile's rate. `fill` receives the share of the block slots the product
+// occupies over those rounds.
+double tile_cost(const TileChoice& t, int64_t M, int64_t N, int epi, double* fill) {
+  const int64_t bn = epi == kEpiSwiglu ? t.bn / 2 : t.bn;
+  const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + bn - 1) / bn);
+  const int64_t slots = int64_t(kCUs) * t.blocks;
+  const int64_t rounds = (tiles + slots - 1) / slots;
+  if (fill) *fill = rounds ? double(tiles) / double(rounds * slots) : 1.0;
+  const double work = double(t.bm) * double(t.bn) / (256.0 * 256.0);
+  return double(rounds) * t.blocks * work / t.rate;
+}
+
+}  // namespace
+
+int choose_tile(int64_t M, int64_t N, int layout, int epi, bool alone, double* fill) {
+  // A product that runs alone gets the tile with the smallest estimated time, including the
+  // tiles that exist to fill the last round. When products of adjacent slices share the GPU, the
+  // CUs one leaves idle run the other's blocks, so only per-CU throughput counts: the 256 x 256
+  // tile, or 128 x 128 when 256 x 256 tiles would leave most CUs idle.
+  int best = kTile256x256;
+  double best_cost = 1e300, best_fill = 1.0;
+  for (const TileChoice& t : kTiles) {
+    if (!tile_supports(t, layout, epi) || (t.fit_only && !alone)) continue;
+    double f = 1.0;
+    const double cost = tile_cost(t, M, N, epi, &f);
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = t.id; best_fill = f; }
+  }
+  if (fill) *fill = best_fill;
+  return best;
 }
 
 hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                       int tile) {
+                       int tile, bool alone) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   // operand extents for the buffer range checks
   if (layout == kWgrad) g.a_bytes = extent_bytes(g.K, g.lda, g.M);
@@ -608,9 +676,20 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipE
   if (layout == kFwd) g.b_bytes = extent_bytes(epi == kEpiSwiglu ? g.half + g.N : g.N, g.ldb, g.K);
   else g.b_bytes = extent_bytes(g.K, g.ldb, g.N);
   if (g.K <= 0) { g.a_bytes = 0; g.b_bytes = 0; }
-  if (tile == kTileAuto) tile = choose_tile(g.M, g.N, epi);
-  if (tile == kTileSmall) return launch_tile<TileS>(g, layout, epi, stream, start, stop);
-  return launch_tile<TileL>(g, layout, epi, stream, start, stop);
+  if (tile != kTileAuto) {
+    // a requested tile that cannot take this product falls back to the automatic choice
+    bool ok = false;
+    for (const TileChoice& t : kTiles) ok = ok || (t.id == tile && tile_supports(t, layout, epi));
+    if (!ok) tile = kTileAuto;
+  }
+  if (tile == kTileAuto) tile = choose_tile(g.M, g.N, layout, epi, alone);
+  switch (tile) {
+    case kTile128x128: return launch_tile<TileS>(g, layout, epi, stream, start, stop);
+    case kTile256x320: return launch_tile<TileW>(g, layout, epi, stream, start, stop);
+    case kTile128x320: return launch_tile<TileN>(g, layout, epi, stream, start, stop);
+    case kTile128x256: return launch_tile<TileM>(g, layout, epi, stream, start, stop);
+    default: return launch_tile<TileL>(g, layout, epi, stream, start, stop);
+  }
 }
 
 hipError_t launch_fence(hipStream_t stream) {

@@ -45,18 +45,30 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
 };
 
-// Block tile of a launch: 256 x 256 (one block per CU) or 128 x 128 (two per CU); both reduce k in
-// the same order, so the choice never changes a result bit.
-enum GemmTile : int { kTileAuto = 0, kTileLarge = 1, kTileSmall = 2 };
+// Block tile of a launch. Every tile reduces k in the same order, so the choice never changes a
+// result bit. The 320-wide tiles take only products whose operands are both read along k, without
+// the SwiGLU pairing; a request they cannot serve falls back to kTileAuto.
+enum GemmTile : int {
+  kTileAuto = 0,
+  kTile256x256 = 1,
+  kTile128x128 = 2,
+  kTile256x320 = 3,
+  kTile128x320 = 4,
+  kTile128x256 = 5,
+  kTileCount = 6
+};
 
-// The tile kTileAuto resolves to for an M x N product (N: output columns).
-int choose_tile(int64_t M, int64_t N, int epi);
+// The tile kTileAuto resolves to for an M x N product (N: output columns). `alone`: the product
+// has the GPU to itself (no products of other slices run beside it), so tiles that fill the last
+// round of blocks are worth their lower per-CU rate. `fill` (optional) receives the share of the
+// block slots the chosen tile occupies over its rounds.
+int choose_tile(int64_t M, int64_t N, int layout, int epi, bool alone, double* fill = nullptr);
 
 // Queue one GEMM on `stream`. With `start`/`stop` events the launch records the kernel's own start
 // and end times in them (timestamps of the dispatch itself, no extra marker packets).
 // Returns hipSuccess or the launch error.
 hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start = nullptr,
-                       hipEvent_t stop = nullptr, int tile = kTileAuto);
+                       hipEvent_t stop = nullptr, int tile = kTileAuto, bool alone = false);
 
 // A one-wave kernel that does nothing. Queued on a stream after DMA-engine copies it completes only
 // after them (stream order), so an event recorded after it marks the copies' completion.

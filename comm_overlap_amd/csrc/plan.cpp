@@ -7,6 +7,7 @@
 #include <new>
 
 #include "plan.hpp"
+#include "gemm.hpp"
 
 namespace tps {
 
@@ -61,6 +62,31 @@ static bool fits_4g(int64_t rows, int64_t cols, int64_t elem) {
   return rows >= 0 && cols >= 0 && bytes < 4294967296.0 - 4096.0;
 }
 
+// Worker streams when the descriptor leaves them open. One stream (slices in order) if every
+// per-slice product fills its rounds of blocks on the 256 CUs with some tile (>= 90% of the slots);
+// otherwise two, so that each slice's products share the CUs with the next slice's first product
+// (the schedule choice between finer pieces and more overlap: FiCCO page, Abstract).
+static int32_t default_streams(const tpslice_plan_s* p) {
+  if (p->r <= 1) return 1;
+  const bool glu = p->desc.act == TPSLICE_ACT_SWIGLU;
+  struct P { int64_t n; int layout, epi; };
+  const P prods[] = {
+      {p->Fp, kFwd, glu ? kEpiSwiglu : kEpiGelu},  // up-projection (+ activation)
+      {p->hc, kFwd, kEpiBf16},                     // down-projection piece
+  };
+  for (const P& q : prods) {
+    double fill = 0.0;
+    choose_tile(p->Ms, q.n, q.layout, q.epi, true, &fill);
+    if (fill < 0.9) return 2;
+  }
+  if (p->qh) {
+    double fill = 0.0;
+    choose_tile(p->Ms, p->qkv, kFwd, kEpiBf16, true, &fill);
+    if (fill < 0.9) return 2;
+  }
+  return 1;
+}
+
 extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t* out) {
   clear_error();
   if (!out) return fail(TPSLICE_ERR_INVALID, "tpslice_plan: out is NULL");
@@ -68,11 +94,11 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   if (!d) return fail(TPSLICE_ERR_INVALID, "tpslice_plan: desc is NULL");
   if (d->act != TPSLICE_ACT_GELU && d->act != TPSLICE_ACT_SWIGLU)
     return fail(TPSLICE_ERR_INVALID, "act %d is not TPSLICE_ACT_GELU or TPSLICE_ACT_SWIGLU", d->act);
-  if (d->flags & ~(TPSLICE_F_SERIALIZE | TPSLICE_F_COPY_BLIT | TPSLICE_F_PIPELINE | TPSLICE_F_TILE_LARGE |
-                   TPSLICE_F_TILE_SMALL))
+  if (d->flags & ~(TPSLICE_F_SERIALIZE | TPSLICE_F_COPY_BLIT | TPSLICE_F_PIPELINE | TPSLICE_F_TILE_MASK))
     return fail(TPSLICE_ERR_INVALID, "unknown flag bits 0x%x", d->flags);
-  if ((d->flags & TPSLICE_F_TILE_LARGE) && (d->flags & TPSLICE_F_TILE_SMALL))
-    return fail(TPSLICE_ERR_INVALID, "TPSLICE_F_TILE_LARGE and TPSLICE_F_TILE_SMALL are exclusive");
+  if (((d->flags & TPSLICE_F_TILE_MASK) >> TPSLICE_F_TILE_SHIFT) >= TPSLICE_TILE_COUNT)
+    return fail(TPSLICE_ERR_INVALID, "tile id %u in the flags is not one of 0..%d",
+                (d->flags & TPSLICE_F_TILE_MASK) >> TPSLICE_F_TILE_SHIFT, TPSLICE_TILE_COUNT - 1);
   if (d->tokens < 0) return fail(TPSLICE_ERR_SHAPE, "tokens %lld < 0", (long long)d->tokens);
   if (d->hidden <= 0 || d->hidden % 8)
     return fail(TPSLICE_ERR_SHAPE, "hidden %lld must be a positive multiple of 8", (long long)d->hidden);
@@ -124,7 +150,8 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   p->r = d->n_row_slices; p->c = d->n_col_slices;
   p->Ms = M / p->r; p->hc = h / p->c;
   const bool serial = d->flags & TPSLICE_F_SERIALIZE;
-  p->S = serial ? 1 : (d->n_streams ? d->n_streams : (p->r > 1 ? 2 : 1));
+  p->qh = qh; p->kvh = kvh;
+  p->S = serial ? 1 : (d->n_streams ? d->n_streams : default_streams(p));
   p->E = serial ? 1 : (d->n_copy_streams ? d->n_copy_streams : 2);
   p->qh = qh; p->kvh = kvh;
   p->trace = 0;

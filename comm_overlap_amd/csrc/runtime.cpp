@@ -320,9 +320,8 @@ struct Schedule {
       e0 = rt->tpool[t.ev0];
       e1 = rt->tpool[t.ev1];
     }
-    const uint32_t f = p->desc.flags;
-    const int tile = (f & TPSLICE_F_TILE_LARGE) ? kTileLarge : (f & TPSLICE_F_TILE_SMALL) ? kTileSmall : kTileAuto;
-    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1, tile);
+    const int tile = int((p->desc.flags & TPSLICE_F_TILE_MASK) >> TPSLICE_F_TILE_SHIFT);
+    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1, tile, serial || p->S == 1);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
     if (i >= 0 && i == lead_slice) {
       TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));

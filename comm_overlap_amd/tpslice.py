@@ -19,7 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libtpslice.so")
 
 OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 ACT_GELU, ACT_SWIGLU = 1, 2
-F_SERIALIZE, F_COPY_BLIT, F_PIPELINE, F_TILE_LARGE, F_TILE_SMALL = 0x1, 0x2, 0x4, 0x8, 0x10
+F_SERIALIZE, F_COPY_BLIT, F_PIPELINE = 0x1, 0x2, 0x4
+F_TILE_SHIFT = 3
+# block tile ids (flags bits 3..5); "large" / "small" name the 256 x 256 / 128 x 128 tiles
+TILES = {"auto": 0, "256x256": 1, "128x128": 2, "256x320": 3, "128x320": 4, "128x256": 5,
+         "large": 1, "small": 2}
 OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD = range(4)
 EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice_plan_piece",
            "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",
@@ -137,7 +141,7 @@ class Config:
     serialize: bool = False
     copy_blit: bool = False
     pipeline: bool = False
-    tile: str = "auto"  # "auto", "large" (256 x 256 block tiles) or "small" (128 x 128)
+    tile: str = "auto"  # a key of TILES
 
     def desc(self) -> Desc:
         return Desc(self.tokens, self.hidden, self.ffn, self.tp_size, self.n_row_slices, self.n_col_slices,
@@ -146,7 +150,7 @@ class Config:
                     self.n_copy_streams,
                     (F_SERIALIZE if self.serialize else 0) | (F_COPY_BLIT if self.copy_blit else 0)
                     | (F_PIPELINE if self.pipeline else 0)
-                    | {"auto": 0, "large": F_TILE_LARGE, "small": F_TILE_SMALL}[self.tile])
+                    | (TILES[self.tile] << F_TILE_SHIFT))
 
 
 class Plan:

@@ -75,10 +75,15 @@ typedef enum {
                                     Abstract: independent pieces pipelined across the batch's work).
                                     Use tpslice_handoff_wait() before reading a hand-off buffer on
                                     another stream, or before freeing buffers the copies touch.    */
-#define TPSLICE_F_TILE_LARGE 0x8u  /* every product with 256 x 256 block tiles (ablation, testing)  */
-#define TPSLICE_F_TILE_SMALL 0x10u /* every product with 128 x 128 block tiles (ablation, testing);
-                                      by default each product takes the tile that fills the 256
-                                      CUs best. The tile never changes a result bit.               */
+/* Block tile of every product (ablation, testing): flags |= TPSLICE_F_TILE(id). By default (id 0)
+   each product takes the tile with the smallest estimated time on the 256 CUs. The tile never
+   changes a result bit. Ids: 1 = 256 x 256, 2 = 128 x 128, 3 = 256 x 320, 4 = 128 x 320,
+   5 = 128 x 256; the 320-wide tiles serve only forward products without the SwiGLU pairing (other
+   products then take the automatic choice).                                                   */
+#define TPSLICE_F_TILE_SHIFT 3
+#define TPSLICE_F_TILE_MASK (0x7u << TPSLICE_F_TILE_SHIFT)
+#define TPSLICE_F_TILE(id) (((uint32_t)(id) << TPSLICE_F_TILE_SHIFT) & TPSLICE_F_TILE_MASK)
+#define TPSLICE_TILE_COUNT 6
 
 typedef struct {
   int64_t tokens;         /* M: token rows in the batch (micro-batch x sequence, batch-major)         */

@@ -140,12 +140,12 @@ def test_pipeline_flag_and_handoff_wait_without_gpu_work():
     assert T.lib.tpslice_handoff_copy(None, None, None, None) == T.ERR_INVALID
 
 
-def test_plan_rejects_both_tile_flags():
+def test_plan_tile_flags():
     import ctypes
     d = T.Config(tokens=64, hidden=64, ffn=64).desc()
-    d.flags = T.F_TILE_LARGE | T.F_TILE_SMALL
+    d.flags = 7 << T.F_TILE_SHIFT
     h = ctypes.c_void_p()
     assert T.lib.tpslice_plan(ctypes.byref(d), ctypes.byref(h)) == T.ERR_INVALID
-    assert b"exclusive" in T.lib.tpslice_last_error()
-    for tile in ("large", "small", "auto"):
+    assert b"tile id" in T.lib.tpslice_last_error()
+    for tile in T.TILES:
         T.Plan(T.Config(tokens=64, hidden=64, ffn=64, tile=tile)).close()

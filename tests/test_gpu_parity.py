@@ -29,7 +29,7 @@ def _print_case(name, **kw):
     print(f"[case] {name} {kw}", flush=True)
 
 
-@pytest.mark.parametrize("tile", ["large", "small"])
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "256x320", "128x320", "128x256"])
 @pytest.mark.parametrize("w", [SMALL_GELU, SMALL_SWIGLU], ids=lambda w: w.key)
 def test_mlp_fwd_small(w, tile):
     _print_case("mlp_fwd", key=w.key, tile=tile)
@@ -61,7 +61,8 @@ def test_slicing_is_bit_exact(w):
     inp = synth.make_inputs(w)
     base = G.run_mlp_fwd(T.plan_for(w, n_row_slices=1, n_col_slices=1), inp)
     for kw in [dict(), dict(serialize=True), dict(copy_blit=True), dict(n_streams=3, n_copy_streams=2),
-               dict(tile="large"), dict(tile="small")]:
+               dict(tile="256x256"), dict(tile="128x128"), dict(tile="256x320"), dict(tile="128x320"),
+               dict(tile="128x256")]:
         out = G.run_mlp_fwd(T.plan_for(w, **kw), inp)
         assert torch.equal(out["Z"], base["Z"]), kw
         assert torch.equal(out["U"], base["U"]), kw
@@ -114,7 +115,8 @@ def test_attnproj_fwd_small(bias):
     G.assert_parity(out["QKV"], ref["QKV"], "QKV")
     G.assert_parity(out["Z"], ref["Z"], "Z")
     assert torch.equal(out["Zh"], out["Z"])
-    for kw in (dict(n_row_slices=1), dict(tile="large"), dict(tile="small")):
+    for kw in (dict(n_row_slices=1), dict(tile="256x256"), dict(tile="128x128"), dict(tile="256x320"),
+               dict(tile="128x320"), dict(tile="128x256")):
         one = G.run_attn_fwd(T.plan_for(w, **kw), inp, bias=bqkv)
         assert torch.equal(one["Z"], out["Z"]) and torch.equal(one["QKV"], out["QKV"]), kw
 
@@ -134,7 +136,7 @@ def test_mlp_bwd_small(w):
         G.assert_parity(out["db1"], ref["db1"], "db1")
     assert torch.equal(out["dXh"], out["dX"])
     # either block tile gives the same bits (same k order)
-    for tile in ("large", "small"):
+    for tile in ("256x256", "128x128", "128x256"):
         o2 = G.run_mlp_bwd(T.plan_for(w, tile=tile), inp, with_bias=w.bias)
         for k in ("dX", "dW1", "dW2", "db1"):
             if out[k] is not None:
@@ -165,7 +167,7 @@ def test_attnproj_bwd_small(bias):
     for k in ("dX", "dC", "dWqkv", "dWo") + (("dbqkv",) if bias else ()):
         G.assert_parity(out[k], ref[k], k)
     assert torch.equal(out["dXh"], out["dX"])
-    for kw in (dict(tile="large"), dict(tile="small"), dict(n_row_slices=1)):
+    for kw in (dict(tile="256x256"), dict(tile="128x128"), dict(tile="128x256"), dict(n_row_slices=1)):
         o2 = G.run_attn_bwd(T.plan_for(w, **kw), inp, with_bias=bias)
         for k in ("dX", "dC", "dWqkv", "dWo") + (("dbqkv",) if bias else ()):
             assert torch.equal(o2[k], out[k]), (kw, k)
