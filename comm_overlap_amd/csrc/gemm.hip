@@ -88,6 +88,10 @@ constexpr int kChunks = kBK / 8;                 // 16-byte chunks per KC row
 constexpr int kRowsPerRun = 1024 / kRowBytes;    // KC rows per 1-KB load run
 constexpr int kGroupM = 4;                       // tile rows per group of the tile order
 constexpr int kCUs = 256;
+// Cache policy of the operand loads: the sc1 scope bit. The tiles stream through each CU once
+// (the vector L1 cannot hold them between uses), and with this bit the direct-to-LDS loads run
+// 3-7% faster on gfx950 than with the default policy (measured on 8192^3 and Llama-shaped products).
+constexpr int kLoadPolicy = 16;
 constexpr uint32_t kOob = 0xFFFFF000u;           // buffer offset that reads as zero: operands are
                                                  // smaller than 4 GiB - 4 KiB
 
@@ -171,14 +175,14 @@ struct KcLoader {
     for (int j = j0; j < j1; ++j) {
       const bool ok = ((valid >> j) & 1) && int(kel[j]) + k0 < K;
       const uint32_t o = ok ? off[j] + uint32_t(k0) * 2 : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16, o, 0, 0, kLoadPolicy);
     }
   }
   // every chunk in range: k advances through the scalar offset, no per-lane arithmetic
   __device__ void issue_fast(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int j0, int j1) const {
     for (int j = j0; j < j1; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16, off[j],
-                                               uint32_t(k0) * 2, 0, 0);
+                                               uint32_t(k0) * 2, 0, kLoadPolicy);
   }
 };
 
@@ -208,13 +212,13 @@ struct NcLoader {
       const int k = k0 + int(krow[j]);
       const bool ok = ((valid >> j) & 1) && k < K;
       const uint32_t o = ok ? uint32_t(k) * ld_bytes + col_off[j] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16, o, 0, 0, kLoadPolicy);
     }
   }
   __device__ void issue_fast(__amdgpu_buffer_rsrc_t rs, char* tile, int wave, int k0, int j0, int j1) const {
     for (int j = j0; j < j1; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + (wave * RUNS + j) * 1024), 16,
-                                               krow[j] * ld_bytes + col_off[j], uint32_t(k0) * ld_bytes, 0, 0);
+                                               krow[j] * ld_bytes + col_off[j], uint32_t(k0) * ld_bytes, 0, kLoadPolicy);
   }
 };
 
