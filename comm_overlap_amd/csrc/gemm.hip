@@ -37,6 +37,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <type_traits>
 
@@ -346,10 +347,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
 
   // ---- tile coordinates: contiguous runs per XCD, grouped order inside
   const int T = g.tiles_m * g.tiles_n;
-  int tile;
+  int tile, split;
   {
-    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3, q = T >> 3, rem = T & 7;
-    tile = xcd < rem ? xcd * (q + 1) + slot : rem * (q + 1) + (xcd - rem) * q + slot;
+    const int G = T * g.splits;
+    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3, q = G >> 3, rem = G & 7;
+    const int L = xcd < rem ? xcd * (q + 1) + slot : rem * (q + 1) + (xcd - rem) * q + slot;
+    split = L / T;
+    tile = L - split * T;
   }
   const int per_group = kGroupM * g.tiles_n;
   const int group = tile / per_group;
@@ -405,7 +409,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
     }
   }
 
-  const int nk = (g.K + kBK - 1) / kBK;
+  const int nk_all = (g.K + kBK - 1) / kBK;
+  // this block's run of k blocks [kb0, nk): all of them unless the product is split along k
+  const int kb0 = split * g.kb_split;
+  const int nk = g.splits > 1 ? min(nk_all, kb0 + g.kb_split) : nk_all;
+  if constexpr (EPI == kEpiF32) {
+    if (g.splits > 1) g.C = reinterpret_cast<float*>(g.C) + int64_t(split) * g.part_stride;
+  }
 
   // block-uniform: every row and column of this tile lies inside the operands
   const bool interior = (m0 + TL::BM <= g.M) && (n0 + kOutBN <= g.N);
@@ -466,8 +476,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   // the load issue overlaps MFMA work instead of stalling every wave right after the barrier.
   constexpr int kRowsPerGroup = kFM >= 4 ? kFM / 4 : 1;
   constexpr int kGroups = kFM / kRowsPerGroup;
-  if (nk > 0) issue(0, -1);
-  for (int kb = 0; kb < nk; ++kb) {
+  if (nk > kb0) issue(kb0, -1);
+  for (int kb = kb0; kb < nk; ++kb) {
     wait_loads_and_barrier();
     const bool more = kb + 1 < nk;
     bf16x8 af[kFM], bf[kFN];
@@ -531,7 +541,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   template __global__ void gemm_kernel<TL, kDgrad, kEpiBf16>(GemmArgs);   \
   template __global__ void gemm_kernel<TL, kDgrad, kEpiDgelu>(GemmArgs);  \
   template __global__ void gemm_kernel<TL, kDgrad, kEpiDswiglu>(GemmArgs); \
-  template __global__ void gemm_kernel<TL, kWgrad, kEpiF32>(GemmArgs);
+  template __global__ void gemm_kernel<TL, kWgrad, kEpiF32>(GemmArgs);    \
+  template __global__ void gemm_kernel<TL, kDgrad, kEpiF32>(GemmArgs);
 TPS_GEMM_INSTANCES(TileL)
 TPS_GEMM_INSTANCES(TileS)
 TPS_GEMM_INSTANCES(TileM)
@@ -574,7 +585,7 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEve
       hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<TL, L, E>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  const int grid = g.tiles_m * g.tiles_n;
+  const int grid = g.tiles_m * g.tiles_n * g.splits;
   if (start || stop)
     hipExtLaunchKernelGGL((gemm_kernel<TL, L, E>), dim3(grid), dim3(TL::kThreads), TL::kLdsBytes, s, start, stop,
                           0, g);
@@ -597,6 +608,7 @@ hipError_t launch_tile(GemmArgs& g, int layout, int epi, hipStream_t stream, hip
       case kDgrad * 8 + kEpiDgelu: return launch_one<TL, kDgrad, kEpiDgelu>(g, stream, start, stop);
       case kDgrad * 8 + kEpiDswiglu: return launch_one<TL, kDgrad, kEpiDswiglu>(g, stream, start, stop);
       case kWgrad * 8 + kEpiF32: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiF32: return launch_one<TL, kDgrad, kEpiF32>(g, stream, start, stop);
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -674,6 +686,10 @@ int choose_tile(int64_t M, int64_t N, int layout, int epi, bool alone, double* f
 hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
                        int tile, bool alone) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.splits < 1) { g.splits = 1; g.kb_split = 0; g.part_stride = 0; }
+  if (g.splits > 1 && (epi != kEpiF32 || g.accumulate || g.splits > 64 || g.kb_split <= 0 ||
+                       g.part_stride < int64_t(g.M) * g.N || g.ldc != g.N))
+    return hipErrorInvalidValue;
   // operand extents for the buffer range checks
   if (layout == kWgrad) g.a_bytes = extent_bytes(g.K, g.lda, g.M);
   else g.a_bytes = extent_bytes(g.M, g.lda, g.K);
@@ -694,6 +710,84 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipE
     case kTile128x256: return launch_tile<TileM>(g, layout, epi, stream, start, stop);
     default: return launch_tile<TileL>(g, layout, epi, stream, start, stop);
   }
+}
+
+namespace {
+
+// out[m][n] = (accumulate ? out[m][n] : 0) + P_0[m][n] + P_1[m][n] + ... in split order, four
+// columns per thread (N is a multiple of 8).
+template <bool BF16>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* P, int splits, int64_t stride, int M, int N,
+                                                           void* out, int64_t ldo, int accumulate) {
+  const int64_t n4 = N / 4, total = int64_t(M) * n4;
+  for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < total; v += int64_t(gridDim.x) * 256) {
+    const int64_t m = v / n4, c = (v - m * n4) * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!BF16) {
+      if (accumulate) acc = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(out) + m * ldo + c);
+    }
+    for (int sp = 0; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4*>(P + sp * stride + m * N + c);
+    if constexpr (BF16) store_bf16x4(out, m * ldo + c, acc[0], acc[1], acc[2], acc[3]);
+    else *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + m * ldo + c) = acc;
+  }
+}
+
+}  // namespace
+
+int choose_split(int64_t M, int64_t N, int64_t K) {
+  // Estimated time in units of one 64-wide k block of a 256 x 256 tile (about 1.9 us at the
+  // tile's per-CU rate): rounds of 256 tiles times the k blocks per split, plus the partials'
+  // write and the reduction's reads and writes (2s + 2 fp32 passes over M x N at ~5 TB/s).
+  const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t nk = (K + kBK - 1) / kBK;
+  if (T <= 0 || nk <= 0) return 1;
+  const double kBlockUs = 1.9;
+  int best = 1;
+  double best_cost = double((T + kCUs - 1) / kCUs) * double(nk);
+  for (int sp = 2; sp <= 8; ++sp) {
+    const int64_t kbs = (nk + sp - 1) / sp;
+    if (kbs < 8) break;  // at least 512 of k per split
+    const double red_us = double(2 * sp + 2) * double(M) * double(N) * 4.0 / 5e12 * 1e6;
+    const double cost = double((T * sp + kCUs - 1) / kCUs) * double(kbs) + red_us / kBlockUs;
+    if (cost < best_cost * 0.95) { best_cost = cost; best = sp; }
+  }
+  return best;
+}
+
+size_t split_partials_bytes(int64_t M, int64_t N, int splits) {
+  return splits > 1 ? size_t(splits) * size_t(M) * size_t(N) * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_split(GemmArgs g, int layout, int out_bf16, int splits, float* partials, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop, int tile) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  void* out = g.C;
+  const int64_t ldo = g.ldc;
+  const int accumulate = g.accumulate;
+  const int nk = (g.K + kBK - 1) / kBK;
+  g.splits = splits;
+  g.kb_split = (nk + splits - 1) / splits;
+  g.part_stride = int64_t(g.M) * g.N;
+  g.C = partials;
+  g.ldc = g.N;
+  g.accumulate = 0;
+  // the reduction closes the timed interval when the product is traced
+  hipError_t e = launch_gemm(g, layout, kEpiF32, stream, start, nullptr, tile);
+  if (e != hipSuccess) return e;
+  const int64_t vecs = int64_t(g.M) * (g.N / 4);
+  const int blocks = int(std::min<int64_t>((vecs + 255) / 256, int64_t(4) * kCUs));
+  if (out_bf16) {
+    if (stop) hipExtLaunchKernelGGL(split_reduce_kernel<true>, dim3(blocks), dim3(256), 0, stream, nullptr, stop, 0,
+                                    partials, splits, g.part_stride, g.M, g.N, out, ldo, 0);
+    else hipLaunchKernelGGL(split_reduce_kernel<true>, dim3(blocks), dim3(256), 0, stream, partials, splits,
+                            g.part_stride, g.M, g.N, out, ldo, 0);
+  } else {
+    if (stop) hipExtLaunchKernelGGL(split_reduce_kernel<false>, dim3(blocks), dim3(256), 0, stream, nullptr, stop, 0,
+                                    partials, splits, g.part_stride, g.M, g.N, out, ldo, accumulate);
+    else hipLaunchKernelGGL(split_reduce_kernel<false>, dim3(blocks), dim3(256), 0, stream, partials, splits,
+                            g.part_stride, g.M, g.N, out, ldo, accumulate);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fence(hipStream_t stream) {

@@ -43,6 +43,9 @@ struct GemmArgs {
   // filled by launch_gemm
   uint32_t a_bytes, b_bytes;
   int32_t tiles_m, tiles_n;
+  int32_t splits;         // k splits (1: none); split s covers k blocks [s kb_split, (s+1) kb_split)
+  int32_t kb_split;       // 64-wide k blocks per split
+  int64_t part_stride;    // floats between the fp32 partial products of consecutive splits
 };
 
 // Block tile of a launch. Every tile reduces k in the same order, so the choice never changes a
@@ -69,6 +72,21 @@ int choose_tile(int64_t M, int64_t N, int layout, int epi, bool alone, double* f
 // Returns hipSuccess or the launch error.
 hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start = nullptr,
                        hipEvent_t stop = nullptr, int tile = kTileAuto, bool alone = false);
+
+// Products whose k is long and whose output is small leave most CUs idle (e.g. a weight gradient
+// over all tokens with a narrow output). Split-k: the k blocks are cut into `splits` equal runs,
+// each run's fp32 product goes to its own partial buffer, and a reduction kernel adds the partials
+// in split order (after the existing output when accumulating) into the fp32 or bf16 output. The
+// split count depends only on the product's shape, so every run of the same product gets the same
+// bits; the sums differ in rounding from an unsplit product.
+// choose_split: split count for an M x N x K product (1 = no split).
+int choose_split(int64_t M, int64_t N, int64_t K);
+// Bytes of partial buffers a split product needs (0 when splits == 1).
+size_t split_partials_bytes(int64_t M, int64_t N, int splits);
+// Queue a split product (epi kEpiF32 into fp32 `out`, or kEpiBf16 into bf16 `out`, no bias):
+// the GEMM into `partials` and the reduction into `out` (ld `ldo`), on `stream`.
+hipError_t launch_gemm_split(GemmArgs g, int layout, int out_bf16, int splits, float* partials, hipStream_t stream,
+                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr, int tile = kTileAuto);
 
 // A one-wave kernel that does nothing. Queued on a stream after DMA-engine copies it completes only
 // after them (stream order), so an event recorded after it marks the copies' completion.

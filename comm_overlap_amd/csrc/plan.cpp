@@ -41,14 +41,19 @@ MlpBwdWs mlp_bwd_ws(const tpslice_plan_s* p) {
   w.dU = 0;
   w.H = align_up(size_t(p->M) * size_t(p->N1) * 2, kWsAlign);
   w.partials = w.H + align_up(size_t(p->M) * size_t(p->Fp) * 2, kWsAlign);
-  w.total = w.partials + align_up(partials_bytes(p->M, p->N1), kWsAlign);
+  w.dw1_split = w.partials + align_up(partials_bytes(p->M, p->N1), kWsAlign);
+  w.dw2_split = w.dw1_split + align_up(split_partials_bytes(p->N1, p->h, p->sp_dw1), kWsAlign);
+  w.total = w.dw2_split + align_up(split_partials_bytes(p->h, p->Fp, p->sp_dw2), kWsAlign);
   return w;
 }
 
 AttnBwdWs attn_bwd_ws(const tpslice_plan_s* p) {
   AttnBwdWs w{};
   w.partials = 0;
-  w.total = align_up(partials_bytes(p->M, p->qkv), kWsAlign);
+  w.dc_split = align_up(partials_bytes(p->M, p->qkv), kWsAlign);
+  w.dwo_split = w.dc_split + align_up(split_partials_bytes(p->M, p->ctx, p->sp_dc), kWsAlign);
+  w.dwqkv_split = w.dwo_split + align_up(split_partials_bytes(p->h, p->ctx, p->sp_dwo), kWsAlign);
+  w.total = w.dwqkv_split + align_up(split_partials_bytes(p->qkv, p->h, p->sp_dwqkv), kWsAlign);
   return w;
 }
 
@@ -156,6 +161,12 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   p->qh = qh; p->kvh = kvh;
   p->trace = 0;
   p->rt = nullptr;
+  // k splits of the products over all tokens (each a function of that product's shape only)
+  p->sp_dw1 = choose_split(N1, h, M);
+  p->sp_dw2 = choose_split(h, Fp, M);
+  p->sp_dc = qh ? choose_split(M, ctx, h) : 1;
+  p->sp_dwo = qh ? choose_split(h, ctx, M) : 1;
+  p->sp_dwqkv = qh ? choose_split(qkv, h, M) : 1;
   *out = p;
   return TPSLICE_OK;
 }

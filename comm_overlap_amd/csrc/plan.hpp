@@ -14,6 +14,8 @@ struct tpslice_plan_s {
   int32_t r, c, S, E;              // row slices, column slices, worker streams, copy streams
   int32_t qh, kvh;                 // this rank's query / key-value heads
   int32_t trace;                   // tracing enabled
+  // k splits of the products over all tokens (1: none): dW1, dW2, dC, dWo, dWqkv
+  int32_t sp_dw1, sp_dw2, sp_dc, sp_dwo, sp_dwqkv;
   void* rt;                        // device resources (streams, events), created on first execution
 };
 
@@ -36,8 +38,10 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // a fixed order through per-chunk partial sums (chunks of kColsumRows token rows, fp32).
 constexpr int64_t kColsumRows = 256;
 struct MlpFwdWs { size_t H, total; };
-struct MlpBwdWs { size_t dU, H, partials, total; };
-struct AttnBwdWs { size_t partials, total; };
+// Split products keep their fp32 partial products in regions of their own (products that may run
+// at the same time never share one).
+struct MlpBwdWs { size_t dU, H, partials, dw1_split, dw2_split, total; };
+struct AttnBwdWs { size_t partials, dc_split, dwo_split, dwqkv_split, total; };
 MlpFwdWs mlp_fwd_ws(const tpslice_plan_s* p);
 MlpBwdWs mlp_bwd_ws(const tpslice_plan_s* p);
 AttnBwdWs attn_bwd_ws(const tpslice_plan_s* p);

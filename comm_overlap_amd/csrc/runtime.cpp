@@ -332,6 +332,29 @@ struct Schedule {
     return TPSLICE_OK;
   }
 
+  // A product over all tokens split along k when `splits` > 1 (fp32 partials in `part`, then the
+  // ordered reduction into the output: fp32 for kEpiF32, bf16 for kEpiBf16).
+  tpslice_status_t product_split(int step, const GemmArgs& g, int layout, int epi, int splits, float* part, int on) {
+    if (splits <= 1) return product(-1, step, -1, g, layout, epi, on);
+    const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    TraceSlot t{};
+    const bool tr = (p->trace & 1) && g.M > 0 && g.N > 0;
+    if (tr) {
+      t.rec.kind = TPSLICE_TRACE_GEMM; t.rec.step = step; t.rec.slice = -1; t.rec.piece = -1;
+      t.rec.stream = worker_id(on); t.rec.flops = flops; t.rec.call = rt->calls - 1;
+      TPS_TRY_(trace_event(&t.ev0));
+      TPS_TRY_(trace_event(&t.ev1));
+      e0 = rt->tpool[t.ev0];
+      e1 = rt->tpool[t.ev1];
+    }
+    const int tile = int((p->desc.flags & TPSLICE_F_TILE_MASK) >> TPSLICE_F_TILE_SHIFT);
+    hipError_t e = launch_gemm_split(g, layout, epi == kEpiBf16, splits, part, worker(on), e0, e1, tile);
+    if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "split GEMM launch: %s", hipGetErrorString(e));
+    if (tr) rt->slots.push_back(t);
+    return TPSLICE_OK;
+  }
+
   tpslice_status_t colsum(const void* X, int64_t ld, int64_t M, int64_t N, float* partials, float* out,
                           int accumulate, int on = 0) {
     return traced(worker(on), worker_id(on), TPSLICE_TRACE_COLSUM, TPSLICE_STEP_BIAS_GRAD, -1, -1, 0.0,
@@ -526,10 +549,12 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
   TPS_TRY(S.gather_slices());
   GemmArgs g1 = args(dU, p->N1, X, p->h, dW1, p->h, p->N1, p->h, p->M);
   g1.accumulate = accumulate;
-  TPS_TRY(S.product(-1, TPSLICE_STEP_MLP_DW1, -1, g1, kWgrad, kEpiF32));
+  TPS_TRY(S.product_split(TPSLICE_STEP_MLP_DW1, g1, kWgrad, kEpiF32, p->sp_dw1,
+                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw1_split), 0));
   GemmArgs g2 = args(dY, p->h, H, p->Fp, dW2, p->Fp, p->h, p->Fp, p->M);
   g2.accumulate = accumulate;
-  TPS_TRY(S.product(-1, TPSLICE_STEP_MLP_DW2, -1, g2, kWgrad, kEpiF32, 1));
+  TPS_TRY(S.product_split(TPSLICE_STEP_MLP_DW2, g2, kWgrad, kEpiF32, p->sp_dw2,
+                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw2_split), 1));
   if (db1) TPS_TRY(S.colsum(dU, p->N1, p->M, p->N1, partials, db1, accumulate, 1));
   return S.join();
 }
@@ -572,14 +597,17 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
   TPS_TRY(S.gather_slices());
   if (p->M > 0) {
     GemmArgs gc = args(dY, p->h, Wo, p->ctx, dC, p->ctx, p->M, p->ctx, p->h);
-    TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DC, -1, gc, kDgrad, kEpiBf16, 1));
+    TPS_TRY(S.product_split(TPSLICE_STEP_ATTN_DC, gc, kDgrad, kEpiBf16, p->sp_dc,
+                            reinterpret_cast<float*>(static_cast<char*>(ws) + L.dc_split), 1));
   }
   GemmArgs go = args(dY, p->h, C, p->ctx, dWo, p->ctx, p->h, p->ctx, p->M);
   go.accumulate = accumulate;
-  TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DWO, -1, go, kWgrad, kEpiF32, 1));
+  TPS_TRY(S.product_split(TPSLICE_STEP_ATTN_DWO, go, kWgrad, kEpiF32, p->sp_dwo,
+                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwo_split), 1));
   GemmArgs gq = args(dQKV, p->qkv, X, p->h, dWqkv, p->h, p->qkv, p->h, p->M);
   gq.accumulate = accumulate;
-  TPS_TRY(S.product(-1, TPSLICE_STEP_ATTN_DWQKV, -1, gq, kWgrad, kEpiF32, 0));
+  TPS_TRY(S.product_split(TPSLICE_STEP_ATTN_DWQKV, gq, kWgrad, kEpiF32, p->sp_dwqkv,
+                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwqkv_split), 0));
   if (dbqkv) TPS_TRY(S.colsum(dQKV, p->qkv, p->M, p->qkv, partials, dbqkv, accumulate, 0));
   return S.join();
 }

@@ -173,6 +173,41 @@ def test_attnproj_bwd_small(bias):
             assert torch.equal(o2[k], out[k]), (kw, k)
 
 
+# Long token sums with narrow outputs: the weight gradients (and dC) are split along k, their fp32
+# partial products reduced in split order.
+SPLIT_K = synth.custom("split_k", 906, tokens=2048, hidden=264, ffn=200, tp=1, act="gelu", bias=True,
+                       row_slices=2, col_slices=1, heads=6, kv_heads=2, head_dim=40, backward=True)
+
+
+def test_split_k_backward():
+    w = SPLIT_K
+    _print_case("split_k", key=w.key)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    out = G.run_mlp_bwd(plan, inp, with_bias=True)
+    ref = L.mlp_bwd(f64(inp["X_mlp"]), f64(inp["W1"]), f64(inp["W2"]), f64(inp["U_saved"]), f64(inp["dY"]),
+                    w.act, with_bias=True)
+    for k in ("dX", "dW1", "dW2", "db1"):
+        G.assert_parity(out[k], ref[k], k)
+    init = (torch.randn_like(out["dW1"]), torch.randn_like(out["dW2"]), torch.randn_like(out["db1"]))
+    acc = G.run_mlp_bwd(plan, inp, with_bias=True, accumulate=True, init=init)
+    G.assert_parity(acc["dW1"], f64(init[0].cpu()) + ref["dW1"], "dW1 accumulated")
+    G.assert_parity(acc["dW2"], f64(init[1].cpu()) + ref["dW2"], "dW2 accumulated")
+    aout = G.run_attn_bwd(plan, inp, with_bias=True)
+    aref = L.attnproj_bwd(f64(inp["X"]), f64(inp["Wqkv"]), f64(inp["dQKV"]), f64(inp["C"]), f64(inp["Wo"]),
+                          f64(inp["dY_attn"]), with_bias=True)
+    for k in ("dX", "dC", "dWqkv", "dWo", "dbqkv"):
+        G.assert_parity(aout[k], aref[k], k)
+    # the split depends on the product's shape only: slicing, tiles and streams keep the bits
+    for kw in (dict(n_row_slices=1), dict(tile="128x128"), dict(tile="256x256"), dict(serialize=True)):
+        o2 = G.run_mlp_bwd(T.plan_for(w, **kw), inp, with_bias=True)
+        for k in ("dX", "dW1", "dW2", "db1"):
+            assert torch.equal(o2[k], out[k]), (kw, k)
+        a2 = G.run_attn_bwd(T.plan_for(w, **kw), inp, with_bias=True)
+        for k in ("dX", "dC", "dWqkv", "dWo", "dbqkv"):
+            assert torch.equal(a2[k], aout[k]), (kw, k)
+
+
 def test_empty_batch():
     w = synth.custom("empty", 904, tokens=0, hidden=64, ffn=64, tp=1, act="gelu", bias=True, row_slices=2,
                      col_slices=2, backward=True)
