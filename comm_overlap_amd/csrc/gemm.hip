@@ -476,21 +476,49 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   // the load issue overlaps MFMA work instead of stalling every wave right after the barrier.
   constexpr int kRowsPerGroup = kFM >= 4 ? kFM / 4 : 1;
   constexpr int kGroups = kFM / kRowsPerGroup;
+  // The second 32-wide step's fragments are read while the first step multiplies. Where registers
+  // allow (at most 32 MFMA tiles per wave): B after the first row group, and each row group's A
+  // registers refilled as soon as that group's MFMAs are issued; otherwise B before the last row
+  // group and A after it. Measured on gfx950: 2-9% over reading them after the first step.
+  constexpr bool kEarlyA = kFM * kFN <= 32;
+  // weight gradients (both operands through transposing reads) keep the plain order: their
+  // fragment reads are twice as many, and reading them early measured 20-30% slower
+  constexpr bool kEarly = LAYOUT != kWgrad;
   if (nk > kb0) issue(kb0, -1);
   for (int kb = kb0; kb < nk; ++kb) {
     wait_loads_and_barrier();
     const bool more = kb + 1 < nk;
-    bf16x8 af[kFM], bf[kFN];
+    bf16x8 af[kFM], bf[kFN], bf1[kFN];
     frags(kb, af, bf, 0);
+    const char* a_tile = smem + (kb & 1) * TL::kStageBytes;
+    const char* b_tile = a_tile + TL::kATileBytes;
+    auto read_b1 = [&]() {
+#pragma unroll
+      for (int in = 0; in < kFN; ++in) {
+        if constexpr (kBDirect) bf1[in] = frag_kc(b_tile, bcol(in), lane, 1);
+        else bf1[in] = frag_nc<TL::BN>(b_tile, bcol(in), lane, 1);
+      }
+    };
+    auto read_a1 = [&](int im0, int im1) {
+#pragma unroll
+      for (int im = im0; im < im1; ++im) {
+        const int rbase = wm * TL::kWaveM + 16 * im;
+        if constexpr (kADirect) af[im] = frag_kc(a_tile, rbase, lane, 1);
+        else af[im] = frag_nc<TL::BM>(a_tile, rbase, lane, 1);
+      }
+    };
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (q < kGroups) mfmas(af, bf, q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
       __builtin_amdgcn_sched_barrier(0);
       if (more) issue(kb + 1, q);
+      if (kEarly && q == (kEarlyA ? 0 : 3)) read_b1();
+      if (kEarly && kEarlyA && q < kGroups) read_a1(q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
       __builtin_amdgcn_sched_barrier(0);
     }
-    frags(kb, af, bf, 1);
-    mfmas(af, bf, 0, kFM);
+    if constexpr (!kEarly) read_b1();
+    if constexpr (!kEarly || !kEarlyA) read_a1(0, kFM);
+    mfmas(af, bf1, 0, kFM);
   }
   __syncthreads();
 
