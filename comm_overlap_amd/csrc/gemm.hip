@@ -57,7 +57,11 @@ struct Tile {
   static constexpr int kFN = BN / WN / 16;           // MFMA tiles per wave along n
   static constexpr int kATileBytes = BM * kBKTile * 2, kBTileBytes = BN * kBKTile * 2;
   static constexpr int kStageBytes = kATileBytes + kBTileBytes;
-  static constexpr int kLdsBytes = 2 * kStageBytes;  // two stages
+  // two operand stages; after the k loop the same memory parks each wave's sums (16 rows of
+  // kEpLd floats per wave), which can be the larger of the two
+  static constexpr int kEpLd = 136;
+  static constexpr int kParkBytes = kWaves * 16 * kEpLd * 4;
+  static constexpr int kLdsBytes = 2 * kStageBytes > kParkBytes ? 2 * kStageBytes : kParkBytes;
   static constexpr int kARuns = kATileBytes / 1024 / kWaves;  // 1-KB load runs per wave
   static constexpr int kBRuns = kBTileBytes / 1024 / kWaves;
   // an operand read across k is staged as [64 k][tile columns]: a 1-KB load run must hold whole
@@ -73,6 +77,7 @@ using TileS = Tile<128, 128, 2, 2, 2>;
 using TileW = Tile<256, 320, 2, 4, 1>;
 using TileN = Tile<128, 320, 2, 4, 1>;
 using TileM = Tile<128, 256, 2, 4, 1>;
+using TileT = Tile<128, 128, 2, 4, 1>;
 
 namespace {
 
@@ -267,6 +272,10 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, const
   float o[4];
   if constexpr (EPI == kEpiF32) {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + mr * g.ldc + n) = f32x4{x[0], x[1], x[2], x[3]};
+  } else if constexpr (EPI == kEpiPartialDual) {
+    float* P = reinterpret_cast<float*>(g.C) + mr * g.ldc;
+    *reinterpret_cast<f32x4*>(P + n) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(P + g.half + n) = f32x4{y[0], y[1], y[2], y[3]};
   } else if constexpr (EPI == kEpiBf16) {
     for (int v = 0; v < 4; ++v) o[v] = x[v];
     if (g.bias) {
@@ -330,7 +339,7 @@ template <class TL, int LAYOUT, int EPI>
 __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(GemmArgs g) {
   constexpr bool kADirect = LAYOUT != kWgrad;   // A read along k
   constexpr bool kBDirect = LAYOUT == kFwd;     // B read along k
-  constexpr bool kDual = EPI == kEpiSwiglu;     // B tile = BN/2 gate rows + BN/2 up rows
+  constexpr bool kDual = EPI == kEpiSwiglu || EPI == kEpiPartialDual;  // B tile = BN/2 gate + BN/2 up rows
   constexpr int kFM = TL::kFM, kFN = TL::kFN;
   constexpr int kOutBN = kDual ? TL::BN / 2 : TL::BN;  // output columns per block
   constexpr int kWaveN = kOutBN / TL::kWavesN;         // output columns per wave
@@ -413,7 +422,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   // this block's run of k blocks [kb0, nk): all of them unless the product is split along k
   const int kb0 = split * g.kb_split;
   const int nk = g.splits > 1 ? min(nk_all, kb0 + g.kb_split) : nk_all;
-  if constexpr (EPI == kEpiF32) {
+  if constexpr (EPI == kEpiF32 || EPI == kEpiPartialDual) {
     if (g.splits > 1) g.C = reinterpret_cast<float*>(g.C) + int64_t(split) * g.part_stride;
   }
 
@@ -524,7 +533,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
 
   // ---- epilogue: per 16-row band, the wave parks its sums in LDS and re-reads them as whole row
   // segments, so global loads and stores of the epilogue are contiguous.
-  constexpr int kEpLd = 136;  // floats per parked row (full-rate LDS writes, measured)
+  constexpr int kEpLd = TL::kEpLd;  // floats per parked row (full-rate LDS writes, measured)
+  static_assert(TL::kWaves * 16 * kEpLd * 4 <= TL::kLdsBytes, "park region inside the block's LDS");
   float* park = reinterpret_cast<float*>(smem) + wave * 16 * kEpLd;
   const int prow = lane & 15, pcol = 4 * (lane >> 4);
 #pragma unroll
@@ -574,7 +584,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
 TPS_GEMM_INSTANCES(TileL)
 TPS_GEMM_INSTANCES(TileS)
 TPS_GEMM_INSTANCES(TileM)
+TPS_GEMM_INSTANCES(TileT)
 #undef TPS_GEMM_INSTANCES
+template __global__ void gemm_kernel<TileL, kFwd, kEpiF32>(GemmArgs);
+template __global__ void gemm_kernel<TileL, kFwd, kEpiPartialDual>(GemmArgs);
 template __global__ void gemm_kernel<TileW, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileW, kFwd, kEpiGelu>(GemmArgs);
 template __global__ void gemm_kernel<TileN, kFwd, kEpiBf16>(GemmArgs);
@@ -622,6 +635,20 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEve
   return hipGetLastError();
 }
 
+// The fp32 partial product of a split product (256 x 256 tiles).
+hipError_t launch_partial(GemmArgs& g, int layout, bool dual, hipStream_t stream, hipEvent_t start) {
+  const int out_bn = dual ? TileL::BN / 2 : TileL::BN;
+  g.tiles_m = (g.M + TileL::BM - 1) / TileL::BM;
+  g.tiles_n = (g.N + out_bn - 1) / out_bn;
+  if (dual) return launch_one<TileL, kFwd, kEpiPartialDual>(g, stream, start, nullptr);
+  switch (layout) {
+    case kFwd: return launch_one<TileL, kFwd, kEpiF32>(g, stream, start, nullptr);
+    case kDgrad: return launch_one<TileL, kDgrad, kEpiF32>(g, stream, start, nullptr);
+    case kWgrad: return launch_one<TileL, kWgrad, kEpiF32>(g, stream, start, nullptr);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <class TL>
 hipError_t launch_tile(GemmArgs& g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const int out_bn = epi == kEpiSwiglu ? TL::BN / 2 : TL::BN;
@@ -662,6 +689,7 @@ constexpr TileChoice kTiles[] = {
     {kTile256x320, 256, 320, 1, true, true, 0.92},
     {kTile128x320, 128, 320, 1, true, true, 0.73},
     {kTile128x256, 128, 256, 1, true, false, 0.77},
+    {kTile128x128w8, 128, 128, 1, true, false, 0.50},
 };
 
 bool tile_supports(const TileChoice& t, int layout, int epi) {
@@ -714,10 +742,7 @@ int choose_tile(int64_t M, int64_t N, int layout, int epi, bool alone, double* f
 hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
                        int tile, bool alone) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  if (g.splits < 1) { g.splits = 1; g.kb_split = 0; g.part_stride = 0; }
-  if (g.splits > 1 && (epi != kEpiF32 || g.accumulate || g.splits > 64 || g.kb_split <= 0 ||
-                       g.part_stride < int64_t(g.M) * g.N || g.ldc != g.N))
-    return hipErrorInvalidValue;
+  g.splits = 1; g.kb_split = 0; g.part_stride = 0;  // split products go through launch_gemm_split
   // operand extents for the buffer range checks
   if (layout == kWgrad) g.a_bytes = extent_bytes(g.K, g.lda, g.M);
   else g.a_bytes = extent_bytes(g.M, g.lda, g.K);
@@ -736,28 +761,49 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipE
     case kTile256x320: return launch_tile<TileW>(g, layout, epi, stream, start, stop);
     case kTile128x320: return launch_tile<TileN>(g, layout, epi, stream, start, stop);
     case kTile128x256: return launch_tile<TileM>(g, layout, epi, stream, start, stop);
+    case kTile128x128w8: return launch_tile<TileT>(g, layout, epi, stream, start, stop);
     default: return launch_tile<TileL>(g, layout, epi, stream, start, stop);
   }
 }
 
 namespace {
 
-// out[m][n] = (accumulate ? out[m][n] : 0) + P_0[m][n] + P_1[m][n] + ... in split order, four
-// columns per thread (N is a multiple of 8).
-template <bool BF16>
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* P, int splits, int64_t stride, int M, int N,
-                                                           void* out, int64_t ldo, int accumulate) {
-  const int64_t n4 = N / 4, total = int64_t(M) * n4;
+// Sum of the split partials of four consecutive outputs (in split order), then the product's
+// epilogue, as the unsplit kernel would apply it. Partials are [splits][M][ldp] fp32; a SwiGLU
+// product keeps gate sums in columns [0, N) and up sums in [N, 2N). N is a multiple of 8.
+template <int EPI>
+__global__ __launch_bounds__(256) void split_epilogue_kernel(GemmArgs g, const float* P, int splits, int64_t stride,
+                                                             int64_t ldp) {
+  const int64_t n4 = g.N / 4, total = int64_t(g.M) * n4;
   for (int64_t v = int64_t(blockIdx.x) * 256 + threadIdx.x; v < total; v += int64_t(gridDim.x) * 256) {
-    const int64_t m = v / n4, c = (v - m * n4) * 4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (!BF16) {
-      if (accumulate) acc = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(out) + m * ldo + c);
+    const int64_t m = v / n4;
+    const int n = int(v - m * n4) * 4;
+    f32x4 xs = {0.f, 0.f, 0.f, 0.f}, ys = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (EPI == kEpiF32) {
+      if (g.accumulate) xs = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(g.C) + m * g.ldc + n);
     }
-    for (int sp = 0; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4*>(P + sp * stride + m * N + c);
-    if constexpr (BF16) store_bf16x4(out, m * ldo + c, acc[0], acc[1], acc[2], acc[3]);
-    else *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + m * ldo + c) = acc;
+    for (int sp = 0; sp < splits; ++sp) {
+      const float* row = P + sp * stride + m * ldp;
+      xs += *reinterpret_cast<const f32x4*>(row + n);
+      if constexpr (EPI == kEpiSwiglu) ys += *reinterpret_cast<const f32x4*>(row + g.N + n);
+    }
+    const float x[4] = {xs[0], xs[1], xs[2], xs[3]};
+    const float y[4] = {ys[0], ys[1], ys[2], ys[3]};
+    epilogue4<EPI>(g, int(m), n, x, y);
   }
+}
+
+template <int EPI>
+hipError_t launch_split_epilogue(const GemmArgs& g, const float* P, int splits, int64_t stride, int64_t ldp,
+                                 hipStream_t s, hipEvent_t stop) {
+  const int64_t vecs = int64_t(g.M) * (g.N / 4);
+  const int blocks = int(std::min<int64_t>((vecs + 255) / 256, int64_t(4) * kCUs));
+  if (stop)
+    hipExtLaunchKernelGGL(split_epilogue_kernel<EPI>, dim3(blocks), dim3(256), 0, s, nullptr, stop, 0, g, P, splits,
+                          stride, ldp);
+  else
+    hipLaunchKernelGGL(split_epilogue_kernel<EPI>, dim3(blocks), dim3(256), 0, s, g, P, splits, stride, ldp);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -786,36 +832,41 @@ size_t split_partials_bytes(int64_t M, int64_t N, int splits) {
   return splits > 1 ? size_t(splits) * size_t(M) * size_t(N) * sizeof(float) : 0;
 }
 
-hipError_t launch_gemm_split(GemmArgs g, int layout, int out_bf16, int splits, float* partials, hipStream_t stream,
-                             hipEvent_t start, hipEvent_t stop, int tile) {
+hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float* partials, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  void* out = g.C;
-  const int64_t ldo = g.ldc;
-  const int accumulate = g.accumulate;
-  const int nk = (g.K + kBK - 1) / kBK;
-  g.splits = splits;
-  g.kb_split = (nk + splits - 1) / splits;
-  g.part_stride = int64_t(g.M) * g.N;
-  g.C = partials;
-  g.ldc = g.N;
-  g.accumulate = 0;
-  // the reduction closes the timed interval when the product is traced
-  hipError_t e = launch_gemm(g, layout, kEpiF32, stream, start, nullptr, tile);
+  const bool dual = epi == kEpiSwiglu;
+  if (splits < 2 || splits > 64 || !partials || (dual && layout != kFwd)) return hipErrorInvalidValue;
+  // operand extents for the buffer range checks (as launch_gemm)
+  GemmArgs p = g;
+  if (layout == kWgrad) p.a_bytes = extent_bytes(p.K, p.lda, p.M);
+  else p.a_bytes = extent_bytes(p.M, p.lda, p.K);
+  if (layout == kFwd) p.b_bytes = extent_bytes(dual ? p.half + p.N : p.N, p.ldb, p.K);
+  else p.b_bytes = extent_bytes(p.K, p.ldb, p.N);
+  if (p.K <= 0) { p.a_bytes = 0; p.b_bytes = 0; }
+  const int64_t ldp = dual ? 2 * int64_t(p.N) : p.N;
+  const int nk = (p.K + kBK - 1) / kBK;
+  p.splits = splits;
+  p.kb_split = (nk + splits - 1) / splits;
+  p.part_stride = int64_t(p.M) * ldp;
+  p.C = partials;
+  p.ldc = ldp;
+  p.half = dual ? p.N : 0;     // up sums' column in the partials; W1's up rows start at the same
+  if (dual && g.half != g.N) return hipErrorInvalidValue;  // offset (SwiGLU: half = F' = N)
+  p.accumulate = 0;
+  p.bias = nullptr; p.aux_in = nullptr; p.aux_out = nullptr;
+  hipError_t e = launch_partial(p, layout, dual, stream, start);
   if (e != hipSuccess) return e;
-  const int64_t vecs = int64_t(g.M) * (g.N / 4);
-  const int blocks = int(std::min<int64_t>((vecs + 255) / 256, int64_t(4) * kCUs));
-  if (out_bf16) {
-    if (stop) hipExtLaunchKernelGGL(split_reduce_kernel<true>, dim3(blocks), dim3(256), 0, stream, nullptr, stop, 0,
-                                    partials, splits, g.part_stride, g.M, g.N, out, ldo, 0);
-    else hipLaunchKernelGGL(split_reduce_kernel<true>, dim3(blocks), dim3(256), 0, stream, partials, splits,
-                            g.part_stride, g.M, g.N, out, ldo, 0);
-  } else {
-    if (stop) hipExtLaunchKernelGGL(split_reduce_kernel<false>, dim3(blocks), dim3(256), 0, stream, nullptr, stop, 0,
-                                    partials, splits, g.part_stride, g.M, g.N, out, ldo, accumulate);
-    else hipLaunchKernelGGL(split_reduce_kernel<false>, dim3(blocks), dim3(256), 0, stream, partials, splits,
-                            g.part_stride, g.M, g.N, out, ldo, accumulate);
+  switch (epi) {
+    case kEpiBf16: return launch_split_epilogue<kEpiBf16>(g, partials, splits, p.part_stride, ldp, stream, stop);
+    case kEpiGelu: return launch_split_epilogue<kEpiGelu>(g, partials, splits, p.part_stride, ldp, stream, stop);
+    case kEpiSwiglu: return launch_split_epilogue<kEpiSwiglu>(g, partials, splits, p.part_stride, ldp, stream, stop);
+    case kEpiDgelu: return launch_split_epilogue<kEpiDgelu>(g, partials, splits, p.part_stride, ldp, stream, stop);
+    case kEpiDswiglu:
+      return launch_split_epilogue<kEpiDswiglu>(g, partials, splits, p.part_stride, ldp, stream, stop);
+    case kEpiF32: return launch_split_epilogue<kEpiF32>(g, partials, splits, p.part_stride, ldp, stream, stop);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_fence(hipStream_t stream) {

@@ -25,8 +25,10 @@ enum GemmEpi : int {
   kEpiDgelu = 3,   // U = aux_in; C = bf16(acc * gelu'(U)); aux_out = bf16(gelu(U))
   kEpiDswiglu = 4, // G, V = aux_in[., n], aux_in[., half+n]; C[., n] = bf16(acc V silu'(G)),
                    // C[., half+n] = bf16(acc silu(G)); aux_out = bf16(silu(G) V)
-  kEpiF32 = 5      // C (fp32) = acc, or C + acc when accumulate (C loaded into the accumulator
+  kEpiF32 = 5,     // C (fp32) = acc, or C + acc when accumulate (C loaded into the accumulator
                    // before the k loop, so a run split along k reproduces the unsplit sums)
+  kEpiPartialDual = 6  // split-k partial of a SwiGLU product: C (fp32) [., n] = gate sums,
+                       // C[., half+n] = up sums (internal to the split path)
 };
 
 struct GemmArgs {
@@ -58,7 +60,8 @@ enum GemmTile : int {
   kTile256x320 = 3,
   kTile128x320 = 4,
   kTile128x256 = 5,
-  kTileCount = 6
+  kTile128x128w8 = 6,  // 128 x 128 with 8 waves, one block per CU
+  kTileCount = 7
 };
 
 // The tile kTileAuto resolves to for an M x N product (N: output columns). `alone`: the product
@@ -73,20 +76,26 @@ int choose_tile(int64_t M, int64_t N, int layout, int epi, bool alone, double* f
 hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipEvent_t start = nullptr,
                        hipEvent_t stop = nullptr, int tile = kTileAuto, bool alone = false);
 
-// Products whose k is long and whose output is small leave most CUs idle (e.g. a weight gradient
-// over all tokens with a narrow output). Split-k: the k blocks are cut into `splits` equal runs,
-// each run's fp32 product goes to its own partial buffer, and a reduction kernel adds the partials
-// in split order (after the existing output when accumulating) into the fp32 or bf16 output. The
-// split count depends only on the product's shape, so every run of the same product gets the same
-// bits; the sums differ in rounding from an unsplit product.
-// choose_split: split count for an M x N x K product (1 = no split).
+// Products whose k is long and whose output is small leave most CUs idle (a weight gradient over
+// all tokens with a narrow output, a thin slice of a narrow projection). Split-k: the k blocks are
+// cut into `splits` equal runs, each run's fp32 product goes to its own partial buffer, and a
+// reduction kernel adds the partials in split order and applies the product's epilogue (bias,
+// activation, saved pre-activation, activation gradient; for kEpiF32 after the existing output
+// when accumulating). Every run of the same product with the same split count gets the same bits;
+// the sums differ in rounding from an unsplit product.
+// choose_split: split count for an M x N x K product (N: output columns; SwiGLU: both halves).
 int choose_split(int64_t M, int64_t N, int64_t K);
-// Bytes of partial buffers a split product needs (0 when splits == 1).
+// Split count of a per-slice product. It must not depend on the slice height, or slicing would
+// change a product's rounding; it is chosen for 2048-row slices (the workloads' slice height).
+constexpr int64_t kSplitRefRows = 2048;
+inline int choose_slice_split(int64_t N, int64_t K) { return choose_split(kSplitRefRows, N, K); }
+// Bytes of partial buffers of an M x N product (N: both halves for SwiGLU) split `splits` ways
+// (0 when splits == 1).
 size_t split_partials_bytes(int64_t M, int64_t N, int splits);
-// Queue a split product (epi kEpiF32 into fp32 `out`, or kEpiBf16 into bf16 `out`, no bias):
-// the GEMM into `partials` and the reduction into `out` (ld `ldo`), on `stream`.
-hipError_t launch_gemm_split(GemmArgs g, int layout, int out_bf16, int splits, float* partials, hipStream_t stream,
-                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr, int tile = kTileAuto);
+// Queue a split product: the GEMM into `partials` (fp32, 256 x 256 tiles), then the reduction
+// with epilogue `epi` into g's outputs, on `stream`. `start`/`stop` bracket both when tracing.
+hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float* partials, hipStream_t stream,
+                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // A one-wave kernel that does nothing. Queued on a stream after DMA-engine copies it completes only
 // after them (stream order), so an event recorded after it marks the copies' completion.

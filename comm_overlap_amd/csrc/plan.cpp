@@ -25,10 +25,22 @@ void clear_error() { g_last_error[0] = '\0'; }
 
 bool plan_ok(const tpslice_plan_s* p) { return p != nullptr && p->magic == kPlanMagic; }
 
+static int32_t worker_regions(const tpslice_plan_s* p) { return p->S > 0 ? p->S : 1; }
+
 MlpFwdWs mlp_fwd_ws(const tpslice_plan_s* p) {
   MlpFwdWs w{};
   w.H = 0;
-  w.total = align_up(size_t(p->M) * size_t(p->Fp) * 2, kWsAlign);
+  w.up_split = align_up(size_t(p->M) * size_t(p->Fp) * 2, kWsAlign);
+  w.up_split_bytes = align_up(split_partials_bytes(p->Ms, p->N1, p->sp_up), kWsAlign);
+  w.total = w.up_split + w.up_split_bytes * size_t(worker_regions(p));
+  return w;
+}
+
+AttnFwdWs attn_fwd_ws(const tpslice_plan_s* p) {
+  AttnFwdWs w{};
+  w.qkv_split = 0;
+  w.qkv_split_bytes = align_up(split_partials_bytes(p->Ms, p->qkv, p->sp_qkv), kWsAlign);
+  w.total = w.qkv_split_bytes * size_t(worker_regions(p));
   return w;
 }
 
@@ -43,7 +55,9 @@ MlpBwdWs mlp_bwd_ws(const tpslice_plan_s* p) {
   w.partials = w.H + align_up(size_t(p->M) * size_t(p->Fp) * 2, kWsAlign);
   w.dw1_split = w.partials + align_up(partials_bytes(p->M, p->N1), kWsAlign);
   w.dw2_split = w.dw1_split + align_up(split_partials_bytes(p->N1, p->h, p->sp_dw1), kWsAlign);
-  w.total = w.dw2_split + align_up(split_partials_bytes(p->h, p->Fp, p->sp_dw2), kWsAlign);
+  w.dh_split = w.dw2_split + align_up(split_partials_bytes(p->h, p->Fp, p->sp_dw2), kWsAlign);
+  w.dh_split_bytes = align_up(split_partials_bytes(p->Ms, p->Fp, p->sp_dh), kWsAlign);
+  w.total = w.dh_split + w.dh_split_bytes * size_t(worker_regions(p));
   return w;
 }
 
@@ -167,6 +181,9 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   p->sp_dc = qh ? choose_split(M, ctx, h) : 1;
   p->sp_dwo = qh ? choose_split(h, ctx, M) : 1;
   p->sp_dwqkv = qh ? choose_split(qkv, h, M) : 1;
+  p->sp_up = choose_slice_split(N1, h);
+  p->sp_qkv = qh ? choose_slice_split(qkv, h) : 1;
+  p->sp_dh = choose_slice_split(Fp, h);
   *out = p;
   return TPSLICE_OK;
 }
@@ -181,6 +198,8 @@ extern "C" tpslice_status_t tpslice_plan_info(tpslice_plan_t p, tpslice_plan_inf
   info->n_row_slices = p->r; info->n_col_slices = p->c;
   info->n_streams = p->S; info->n_copy_streams = p->E;
   info->q_heads = p->qh; info->kv_heads = p->kvh;
+  const int32_t sp[8] = {p->sp_up, p->sp_qkv, p->sp_dh, p->sp_dw1, p->sp_dw2, p->sp_dc, p->sp_dwo, p->sp_dwqkv};
+  for (int k = 0; k < 8; ++k) info->k_splits[k] = sp[k];
   return TPSLICE_OK;
 }
 
@@ -205,7 +224,7 @@ extern "C" tpslice_status_t tpslice_workspace_size(tpslice_plan_t p, int32_t op,
   switch (op) {
     case TPSLICE_OP_MLP_FWD: *bytes = mlp_fwd_ws(p).total; return TPSLICE_OK;
     case TPSLICE_OP_MLP_BWD: *bytes = mlp_bwd_ws(p).total; return TPSLICE_OK;
-    case TPSLICE_OP_ATTNPROJ_FWD: *bytes = 0; return TPSLICE_OK;
+    case TPSLICE_OP_ATTNPROJ_FWD: *bytes = attn_fwd_ws(p).total; return TPSLICE_OK;
     case TPSLICE_OP_ATTNPROJ_BWD: *bytes = attn_bwd_ws(p).total; return TPSLICE_OK;
     default: return fail(TPSLICE_ERR_INVALID, "unknown op %d", op);
   }

@@ -14,8 +14,9 @@ struct tpslice_plan_s {
   int32_t r, c, S, E;              // row slices, column slices, worker streams, copy streams
   int32_t qh, kvh;                 // this rank's query / key-value heads
   int32_t trace;                   // tracing enabled
-  // k splits of the products over all tokens (1: none): dW1, dW2, dC, dWo, dWqkv
-  int32_t sp_dw1, sp_dw2, sp_dc, sp_dwo, sp_dwqkv;
+  // k splits (1: none) of the products over all tokens (dW1, dW2, dC, dWo, dWqkv) and of the row
+  // slices' first products (up-projection, QKV projection, dH)
+  int32_t sp_dw1, sp_dw2, sp_dc, sp_dwo, sp_dwqkv, sp_up, sp_qkv, sp_dh;
   void* rt;                        // device resources (streams, events), created on first execution
 };
 
@@ -37,12 +38,15 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Workspace regions (byte offsets) of each operation. Bias gradients are column sums reduced in
 // a fixed order through per-chunk partial sums (chunks of kColsumRows token rows, fp32).
 constexpr int64_t kColsumRows = 256;
-struct MlpFwdWs { size_t H, total; };
 // Split products keep their fp32 partial products in regions of their own (products that may run
 // at the same time never share one).
-struct MlpBwdWs { size_t dU, H, partials, dw1_split, dw2_split, total; };
+// A split per-slice product has one partial region per worker stream (x_split_bytes each).
+struct MlpFwdWs { size_t H, up_split, up_split_bytes, total; };
+struct AttnFwdWs { size_t qkv_split, qkv_split_bytes, total; };
+struct MlpBwdWs { size_t dU, H, partials, dw1_split, dw2_split, dh_split, dh_split_bytes, total; };
 struct AttnBwdWs { size_t partials, dc_split, dwo_split, dwqkv_split, total; };
 MlpFwdWs mlp_fwd_ws(const tpslice_plan_s* p);
+AttnFwdWs attn_fwd_ws(const tpslice_plan_s* p);
 MlpBwdWs mlp_bwd_ws(const tpslice_plan_s* p);
 AttnBwdWs attn_bwd_ws(const tpslice_plan_s* p);
 

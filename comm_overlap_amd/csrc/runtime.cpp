@@ -334,25 +334,40 @@ struct Schedule {
 
   // A product over all tokens split along k when `splits` > 1 (fp32 partials in `part`, then the
   // ordered reduction into the output: fp32 for kEpiF32, bf16 for kEpiBf16).
-  tpslice_status_t product_split(int step, const GemmArgs& g, int layout, int epi, int splits, float* part, int on) {
-    if (splits <= 1) return product(-1, step, -1, g, layout, epi, on);
-    const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K);
+  // A product split along k when `splits` > 1: fp32 partials in `part`, then the ordered
+  // reduction with the product's epilogue. i >= 0: row slice i's product (on worker(i));
+  // i < 0: a product over all tokens on worker(on).
+  tpslice_status_t product_split(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int splits,
+                                 float* part, int on = 0) {
+    if (splits <= 1) return product(i, step, piece, g, layout, epi, on);
+    const int wi = i < 0 ? on : i;
+    const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
     hipEvent_t e0 = nullptr, e1 = nullptr;
     TraceSlot t{};
     const bool tr = (p->trace & 1) && g.M > 0 && g.N > 0;
     if (tr) {
-      t.rec.kind = TPSLICE_TRACE_GEMM; t.rec.step = step; t.rec.slice = -1; t.rec.piece = -1;
-      t.rec.stream = worker_id(on); t.rec.flops = flops; t.rec.call = rt->calls - 1;
+      t.rec.kind = TPSLICE_TRACE_GEMM; t.rec.step = step; t.rec.slice = i; t.rec.piece = piece;
+      t.rec.stream = worker_id(wi); t.rec.flops = flops; t.rec.call = rt->calls - 1;
       TPS_TRY_(trace_event(&t.ev0));
       TPS_TRY_(trace_event(&t.ev1));
       e0 = rt->tpool[t.ev0];
       e1 = rt->tpool[t.ev1];
     }
-    const int tile = int((p->desc.flags & TPSLICE_F_TILE_MASK) >> TPSLICE_F_TILE_SHIFT);
-    hipError_t e = launch_gemm_split(g, layout, epi == kEpiBf16, splits, part, worker(on), e0, e1, tile);
+    hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "split GEMM launch: %s", hipGetErrorString(e));
+    if (i >= 0 && i == lead_slice) {
+      TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
+      lead_slice = -1;
+      lead_done = i;
+    }
     if (tr) rt->slots.push_back(t);
     return TPSLICE_OK;
+  }
+
+  // This call's partial buffer of worker(i) for a split per-slice product (regions of `bytes`
+  // each from `base`, one per worker stream).
+  float* slice_part(char* base, size_t bytes, int i) const {
+    return reinterpret_cast<float*>(base + size_t(serial ? 0 : i % p->S) * bytes);
   }
 
   tpslice_status_t colsum(const void* X, int64_t ld, int64_t M, int64_t N, float* partials, float* out,
@@ -454,7 +469,8 @@ extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, con
     g1.bias = b1;
     g1.half = p->Fp;
     if (U_save) { g1.aux_out = bfw(U_save, r0 * p->N1); g1.ld_out = p->N1; }
-    TPS_TRY(S.product(i, TPSLICE_STEP_MLP_UP, -1, g1, kFwd, epi));
+    TPS_TRY(S.product_split(i, TPSLICE_STEP_MLP_UP, -1, g1, kFwd, epi, p->sp_up,
+                            S.slice_part(static_cast<char*>(ws) + L.up_split, L.up_split_bytes, i)));
     for (int j = 0; j < p->c; ++j) {
       const int64_t c0 = int64_t(j) * p->hc;
       GemmArgs g2 = args(bf(H, r0 * p->Fp), p->Fp, bf(W2, c0 * p->Fp), p->Fp, bfw(Z, r0 * p->h + c0), p->h,
@@ -472,13 +488,14 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
                                                  void* Z, void* Z_handoff, void* ws, size_t ws_bytes,
                                                  void* stream) {
   clear_error();
-  (void)ws; (void)ws_bytes;
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   if (p->qh == 0) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads (n_heads = 0)");
   TPS_REQ(Wqkv); TPS_REQ(Wo);
   if (p->M > 0) { TPS_REQ(X); TPS_REQ(QKV); TPS_REQ(C); TPS_REQ(Z); }
   else { TPS_OPT(X); TPS_OPT(QKV); TPS_OPT(C); TPS_OPT(Z); }
   TPS_OPT(bqkv); TPS_OPT(Z_handoff);
+  const AttnFwdWs L = attn_fwd_ws(p);
+  TPS_TRY(check_ws(ws, ws_bytes, L.total));
   if (p->M == 0) return TPSLICE_OK;
   Runtime* rt = nullptr;
   TPS_TRY(ensure_runtime(p, &rt));
@@ -499,7 +516,8 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
     GemmArgs q = args(bf(X, r0 * p->h), p->h, Wqkv, p->h, bfw(QKV, r0 * p->qkv), p->qkv, p->Ms, p->qkv, p->h);
     q.bias = bqkv;
-    TPS_TRY(S.product(i, TPSLICE_STEP_QKV, -1, q, kFwd, kEpiBf16));
+    TPS_TRY(S.product_split(i, TPSLICE_STEP_QKV, -1, q, kFwd, kEpiBf16, p->sp_qkv,
+                            S.slice_part(static_cast<char*>(ws) + L.qkv_split, L.qkv_split_bytes, i)));
   }
   return S.join();
 }
@@ -534,7 +552,8 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
     g.aux_in = bf(U, r0 * p->N1); g.ld_in = p->N1;
     g.aux_out = bfw(H, r0 * p->Fp); g.ld_out = p->Fp;
     g.half = p->Fp;
-    TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DH, -1, g, kDgrad, glu ? kEpiDswiglu : kEpiDgelu));
+    TPS_TRY(S.product_split(i, TPSLICE_STEP_MLP_DH, -1, g, kDgrad, glu ? kEpiDswiglu : kEpiDgelu, p->sp_dh,
+                            S.slice_part(static_cast<char*>(ws) + L.dh_split, L.dh_split_bytes, i)));
     for (int j = 0; j < p->c; ++j) {
       const int64_t c0 = int64_t(j) * p->hc;
       GemmArgs gx = args(bf(dU, r0 * p->N1), p->N1, bf(W1, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms, p->hc,
@@ -549,11 +568,11 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
   TPS_TRY(S.gather_slices());
   GemmArgs g1 = args(dU, p->N1, X, p->h, dW1, p->h, p->N1, p->h, p->M);
   g1.accumulate = accumulate;
-  TPS_TRY(S.product_split(TPSLICE_STEP_MLP_DW1, g1, kWgrad, kEpiF32, p->sp_dw1,
+  TPS_TRY(S.product_split(-1, TPSLICE_STEP_MLP_DW1, -1, g1, kWgrad, kEpiF32, p->sp_dw1,
                           reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw1_split), 0));
   GemmArgs g2 = args(dY, p->h, H, p->Fp, dW2, p->Fp, p->h, p->Fp, p->M);
   g2.accumulate = accumulate;
-  TPS_TRY(S.product_split(TPSLICE_STEP_MLP_DW2, g2, kWgrad, kEpiF32, p->sp_dw2,
+  TPS_TRY(S.product_split(-1, TPSLICE_STEP_MLP_DW2, -1, g2, kWgrad, kEpiF32, p->sp_dw2,
                           reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw2_split), 1));
   if (db1) TPS_TRY(S.colsum(dU, p->N1, p->M, p->N1, partials, db1, accumulate, 1));
   return S.join();
@@ -597,16 +616,16 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
   TPS_TRY(S.gather_slices());
   if (p->M > 0) {
     GemmArgs gc = args(dY, p->h, Wo, p->ctx, dC, p->ctx, p->M, p->ctx, p->h);
-    TPS_TRY(S.product_split(TPSLICE_STEP_ATTN_DC, gc, kDgrad, kEpiBf16, p->sp_dc,
+    TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DC, -1, gc, kDgrad, kEpiBf16, p->sp_dc,
                             reinterpret_cast<float*>(static_cast<char*>(ws) + L.dc_split), 1));
   }
   GemmArgs go = args(dY, p->h, C, p->ctx, dWo, p->ctx, p->h, p->ctx, p->M);
   go.accumulate = accumulate;
-  TPS_TRY(S.product_split(TPSLICE_STEP_ATTN_DWO, go, kWgrad, kEpiF32, p->sp_dwo,
+  TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DWO, -1, go, kWgrad, kEpiF32, p->sp_dwo,
                           reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwo_split), 1));
   GemmArgs gq = args(dQKV, p->qkv, X, p->h, dWqkv, p->h, p->qkv, p->h, p->M);
   gq.accumulate = accumulate;
-  TPS_TRY(S.product_split(TPSLICE_STEP_ATTN_DWQKV, gq, kWgrad, kEpiF32, p->sp_dwqkv,
+  TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DWQKV, -1, gq, kWgrad, kEpiF32, p->sp_dwqkv,
                           reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwqkv_split), 0));
   if (dbqkv) TPS_TRY(S.colsum(dQKV, p->qkv, p->M, p->qkv, partials, dbqkv, accumulate, 0));
   return S.join();

@@ -23,7 +23,7 @@ F_SERIALIZE, F_COPY_BLIT, F_PIPELINE = 0x1, 0x2, 0x4
 F_TILE_SHIFT = 3
 # block tile ids (flags bits 3..5); "large" / "small" name the 256 x 256 / 128 x 128 tiles
 TILES = {"auto": 0, "256x256": 1, "128x128": 2, "256x320": 3, "128x320": 4, "128x256": 5,
-         "large": 1, "small": 2}
+         "128x128w8": 6, "large": 1, "small": 2}
 OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD = range(4)
 EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice_plan_piece",
            "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",
@@ -55,7 +55,12 @@ class PlanInfo(ctypes.Structure):
                 ("rows_per_slice", ctypes.c_int64), ("handoff_cols", ctypes.c_int64),
                 ("n_row_slices", ctypes.c_int32), ("n_col_slices", ctypes.c_int32),
                 ("n_streams", ctypes.c_int32), ("n_copy_streams", ctypes.c_int32),
-                ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
+                ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("k_splits", ctypes.c_int32 * 8)]
+
+    SPLIT_NAMES = ("up", "qkv", "dh", "dw1", "dw2", "dc", "dwo", "dwqkv")
+
+    def splits(self):
+        return dict(zip(self.SPLIT_NAMES, list(self.k_splits)))
 
 
 class TraceRec(ctypes.Structure):

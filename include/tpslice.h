@@ -77,13 +77,14 @@ typedef enum {
                                     another stream, or before freeing buffers the copies touch.    */
 /* Block tile of every product (ablation, testing): flags |= TPSLICE_F_TILE(id). By default (id 0)
    each product takes the tile with the smallest estimated time on the 256 CUs. The tile never
-   changes a result bit. Ids: 1 = 256 x 256, 2 = 128 x 128, 3 = 256 x 320, 4 = 128 x 320,
-   5 = 128 x 256; the 320-wide tiles serve only forward products without the SwiGLU pairing (other
-   products then take the automatic choice).                                                   */
+   changes a result bit. Ids: 1 = 256 x 256, 2 = 128 x 128 (4 waves, two blocks per CU),
+   3 = 256 x 320, 4 = 128 x 320, 5 = 128 x 256, 6 = 128 x 128 (8 waves, one block per CU); the
+   320-wide tiles serve only forward products without the SwiGLU pairing (other products then
+   take the automatic choice).                                                                 */
 #define TPSLICE_F_TILE_SHIFT 3
 #define TPSLICE_F_TILE_MASK (0x7u << TPSLICE_F_TILE_SHIFT)
 #define TPSLICE_F_TILE(id) (((uint32_t)(id) << TPSLICE_F_TILE_SHIFT) & TPSLICE_F_TILE_MASK)
-#define TPSLICE_TILE_COUNT 6
+#define TPSLICE_TILE_COUNT 7
 
 typedef struct {
   int64_t tokens;         /* M: token rows in the batch (micro-batch x sequence, batch-major)         */
@@ -111,6 +112,11 @@ typedef struct {
   int64_t handoff_cols;         /* h / c                                                             */
   int32_t n_row_slices, n_col_slices, n_streams, n_copy_streams;
   int32_t q_heads, kv_heads;    /* this rank's head counts                                           */
+  /* k splits (1 = none) the plan takes for, in order: the up-projection, the QKV projection and dH
+     of each row slice, then dW1, dW2, dC, dWo, dWqkv over all tokens. A split product sums its k
+     runs' fp32 partials in order before the epilogue: the same bits for every slicing of the same
+     batch, other rounding than an unsplit product.                                            */
+  int32_t k_splits[8];
 } tpslice_plan_info_t;
 
 typedef enum {

@@ -29,7 +29,7 @@ def _print_case(name, **kw):
     print(f"[case] {name} {kw}", flush=True)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x128", "256x320", "128x320", "128x256"])
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "256x320", "128x320", "128x256", "128x128w8"])
 @pytest.mark.parametrize("w", [SMALL_GELU, SMALL_SWIGLU], ids=lambda w: w.key)
 def test_mlp_fwd_small(w, tile):
     _print_case("mlp_fwd", key=w.key, tile=tile)
@@ -62,7 +62,7 @@ def test_slicing_is_bit_exact(w):
     base = G.run_mlp_fwd(T.plan_for(w, n_row_slices=1, n_col_slices=1), inp)
     for kw in [dict(), dict(serialize=True), dict(copy_blit=True), dict(n_streams=3, n_copy_streams=2),
                dict(tile="256x256"), dict(tile="128x128"), dict(tile="256x320"), dict(tile="128x320"),
-               dict(tile="128x256")]:
+               dict(tile="128x256"), dict(tile="128x128w8")]:
         out = G.run_mlp_fwd(T.plan_for(w, **kw), inp)
         assert torch.equal(out["Z"], base["Z"]), kw
         assert torch.equal(out["U"], base["U"]), kw
@@ -136,7 +136,7 @@ def test_mlp_bwd_small(w):
         G.assert_parity(out["db1"], ref["db1"], "db1")
     assert torch.equal(out["dXh"], out["dX"])
     # either block tile gives the same bits (same k order)
-    for tile in ("256x256", "128x128", "128x256"):
+    for tile in ("256x256", "128x128", "128x256", "128x128w8"):
         o2 = G.run_mlp_bwd(T.plan_for(w, tile=tile), inp, with_bias=w.bias)
         for k in ("dX", "dW1", "dW2", "db1"):
             if out[k] is not None:
@@ -167,7 +167,8 @@ def test_attnproj_bwd_small(bias):
     for k in ("dX", "dC", "dWqkv", "dWo") + (("dbqkv",) if bias else ()):
         G.assert_parity(out[k], ref[k], k)
     assert torch.equal(out["dXh"], out["dX"])
-    for kw in (dict(tile="256x256"), dict(tile="128x128"), dict(tile="128x256"), dict(n_row_slices=1)):
+    for kw in (dict(tile="256x256"), dict(tile="128x128"), dict(tile="128x256"), dict(tile="128x128w8"),
+               dict(n_row_slices=1)):
         o2 = G.run_attn_bwd(T.plan_for(w, **kw), inp, with_bias=bias)
         for k in ("dX", "dC", "dWqkv", "dWo") + (("dbqkv",) if bias else ()):
             assert torch.equal(o2[k], out[k]), (kw, k)
@@ -206,6 +207,50 @@ def test_split_k_backward():
         a2 = G.run_attn_bwd(T.plan_for(w, **kw), inp, with_bias=True)
         for k in ("dX", "dC", "dWqkv", "dWo", "dbqkv"):
             assert torch.equal(a2[k], aout[k]), (kw, k)
+
+
+# A long reduction (h = 2048) with narrow projections: the row slices' first products (up, QKV,
+# dH) are split along k; the split count does not depend on the slice height.
+SLICE_SPLIT = [synth.custom("slice_split_gelu", 907, tokens=1024, hidden=2048, ffn=264, tp=1, act="gelu",
+                            bias=True, row_slices=2, col_slices=1, heads=6, kv_heads=2, head_dim=40,
+                            backward=True),
+               synth.custom("slice_split_swiglu", 908, tokens=1024, hidden=2048, ffn=528, tp=2, act="swiglu",
+                            bias=False, row_slices=4, col_slices=2, backward=True)]
+
+
+@pytest.mark.parametrize("w", SLICE_SPLIT, ids=lambda w: w.key)
+def test_split_k_slice_products(w):
+    _print_case("slice_split", key=w.key)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    sp = plan.info.splits()
+    assert sp["up"] > 1 and sp["dh"] > 1, sp
+    out = G.run_mlp_fwd(plan, inp)
+    ref = G.oracle_mlp_fwd(inp, w.act)
+    G.assert_parity(out["Z"], ref["Z"], "Z")
+    G.assert_parity(out["U"], ref["U"], "U")
+    bo = G.run_mlp_bwd(plan, inp, with_bias=w.bias)
+    rb = L.mlp_bwd(f64(inp["X_mlp"]), f64(inp["W1"]), f64(inp["W2"]), f64(inp["U_saved"]), f64(inp["dY"]),
+                   w.act, with_bias=w.bias)
+    for k in ("dX", "dW1", "dW2") + (("db1",) if w.bias else ()):
+        G.assert_parity(bo[k], rb[k], k)
+    if w.has_attn:
+        assert sp["qkv"] > 1, sp
+        ao = G.run_attn_fwd(plan, inp)
+        ra = L.attnproj_fwd(f64(inp["X"]), f64(inp["Wqkv"]), None, f64(inp["C"]), f64(inp["Wo"]))
+        G.assert_parity(ao["QKV"], ra["QKV"], "QKV")
+        G.assert_parity(ao["Z"], ra["Z"], "attn Z")
+    for kw in (dict(n_row_slices=1, n_col_slices=1), dict(serialize=True), dict(tile="128x128")):
+        p2 = T.plan_for(w, **kw)
+        assert p2.info.splits() == sp, kw
+        o2 = G.run_mlp_fwd(p2, inp)
+        assert torch.equal(o2["Z"], out["Z"]) and torch.equal(o2["U"], out["U"]), kw
+        b2 = G.run_mlp_bwd(p2, inp, with_bias=w.bias)
+        for k in ("dX", "dW1", "dW2") + (("db1",) if w.bias else ()):
+            assert torch.equal(b2[k], bo[k]), (kw, k)
+        if w.has_attn:
+            a2 = G.run_attn_fwd(p2, inp)
+            assert torch.equal(a2["QKV"], ao["QKV"]) and torch.equal(a2["Z"], ao["Z"]), kw
 
 
 def test_empty_batch():
