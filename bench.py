@@ -35,8 +35,8 @@ DEFAULT_WORKLOAD = "gpt3_2.7b_mlp"
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--streams", type=int, default=0, help="worker streams (0 = plan default)")
     ap.add_argument("--copy-streams", type=int, default=0, help="copy streams (0 = plan default)")

@@ -171,7 +171,7 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   const bool serial = d->flags & TPSLICE_F_SERIALIZE;
   p->qh = qh; p->kvh = kvh;
   p->S = serial ? 1 : (d->n_streams ? d->n_streams : default_streams(p));
-  p->E = serial ? 1 : (d->n_copy_streams ? d->n_copy_streams : 2);
+  p->E = serial ? 1 : (d->n_copy_streams ? d->n_copy_streams : 1);
   p->qh = qh; p->kvh = kvh;
   p->trace = 0;
   p->rt = nullptr;

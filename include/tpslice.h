@@ -100,7 +100,7 @@ typedef struct {
   int32_t n_streams;      /* worker streams for the slices (0 = default: 2 when there are several row
                              slices, else 1); slice i runs on stream i mod n_streams and starts once
                              slice i-1's first product is done                                     */
-  int32_t n_copy_streams; /* side streams for hand-off copies (0 = default: 2)                        */
+  int32_t n_copy_streams; /* side streams for hand-off copies (0 = default: 1)                        */
   uint32_t flags;         /* TPSLICE_F_*                                                                */
 } tpslice_desc_t;
 
