@@ -224,8 +224,9 @@ def cpu_baseline(w, inp, target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path is one GPU's "
-              f"tensor-parallel share; DESIGN.md describes how it would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported. The path is one GPU's "
+              f"tensor-parallel share; across GPUs each rank would run it on its own weight shards and "
+              f"sum the hand-off pieces with a collective on the copy stream.", file=sys.stderr)
         return 2
     import torch
     from comm_overlap_amd import synth
