@@ -57,11 +57,7 @@ struct Tile {
   static constexpr int kFN = BN / WN / 16;           // MFMA tiles per wave along n
   static constexpr int kATileBytes = BM * kBKTile * 2, kBTileBytes = BN * kBKTile * 2;
   static constexpr int kStageBytes = kATileBytes + kBTileBytes;
-  // two operand stages; after the k loop the same memory parks each wave's sums (16 rows of
-  // kEpLd floats per wave), which can be the larger of the two
-  static constexpr int kEpLd = 136;
-  static constexpr int kParkBytes = kWaves * 16 * kEpLd * 4;
-  static constexpr int kLdsBytes = 2 * kStageBytes > kParkBytes ? 2 * kStageBytes : kParkBytes;
+  static constexpr int kLdsBytes = 2 * kStageBytes;  // two operand stages
   static constexpr int kARuns = kATileBytes / 1024 / kWaves;  // 1-KB load runs per wave
   static constexpr int kBRuns = kBTileBytes / 1024 / kWaves;
   // an operand read across k is staged as [64 k][tile columns]: a 1-KB load run must hold whole
@@ -120,11 +116,42 @@ __device__ inline int swz_nc(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) <<
 
 __device__ inline float bf2f(unsigned short b) { return __uint_as_float(uint32_t(b) << 16); }
 
-__device__ inline float gelu_f(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
-__device__ inline float gelu_grad_f(float u) {
-  return 0.5f * (1.0f + erff(u * 0.70710678118654752f)) + u * expf(-0.5f * u * u) * 0.39894228040143268f;
+// Activation math, in few VALU instructions: the epilogue's fp32 vector work runs after the MFMA
+// loop and is paid per output element, so the library erff (two polynomial branches) and the
+// correctly rounded division cost a fifth of a GeLU product's time.
+//
+// Normal upper tail Q(a) = P(Z > a) = erfc(a / sqrt 2) / 2 for a = |u|, by the rational
+// approximation of Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erfc(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2), t = 1 / (1 + p x), absolute error
+// below 1.5e-7. Here x = a / sqrt 2, so p becomes p / sqrt 2 and exp(-x^2) = 2^(-a^2 log2(e) / 2);
+// the coefficients carry the factor 1/2. Returns Q(a) and e = exp(-u^2 / 2).
+struct NormalTail { float q, e; };
+__device__ inline NormalTail normal_tail(float u) {
+  const float a = fabsf(u);
+  const float t = __builtin_amdgcn_rcpf(fmaf(a, 0.2316418883f, 1.0f));
+  float p = fmaf(t, 0.5307027145f, -0.7265760135f);
+  p = fmaf(t, p, 0.7107068705f);
+  p = fmaf(t, p, -0.1422483680f);
+  p = fmaf(t, p, 0.1274147960f);
+  const float e = __builtin_amdgcn_exp2f(u * u * -0.72134752044448170f);
+  return {t * p * e, e};
 }
-__device__ inline float sigmoid_f(float g) { return 1.0f / (1.0f + expf(-g)); }
+// GeLU(u) = u Phi(u), with Phi(u) = 1 - Q(u) for u >= 0 and Q(-u) for u < 0:
+// GeLU(u) = (u + |u| (1 - 2 Q(|u|))) / 2. Absolute error below 3e-7 for finite u.
+__device__ inline float gelu_f(float u) {
+  const NormalTail n = normal_tail(u);
+  return 0.5f * fmaf(fabsf(u), fmaf(-2.0f, n.q, 1.0f), u);
+}
+// GeLU'(u) = Phi(u) + u phi(u), phi(u) = exp(-u^2 / 2) / sqrt(2 pi); gelu_and_grad gives both.
+__device__ inline void gelu_and_grad(float u, float& h, float& d) {
+  const NormalTail n = normal_tail(u);
+  h = 0.5f * fmaf(fabsf(u), fmaf(-2.0f, n.q, 1.0f), u);
+  d = (u >= 0.0f ? 1.0f - n.q : n.q) + u * n.e * 0.39894228040143270f;
+}
+// logistic sigmoid 1 / (1 + e^-g), with the hardware exp2 and reciprocal (about 1 ulp each)
+__device__ inline float sigmoid_f(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896339f));
+}
 
 __device__ inline i32x2 pack_bf16x4(float a, float b, float c, float d) {
   bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
@@ -263,72 +290,173 @@ __device__ inline bf16x8 frag_nc(const char* tile, int cb, int lane, int kk) {
 }
 
 // ----------------------------------------------------------------------------------- epilogue
-// Applied to four consecutive output columns (n .. n+3) of row m, values x[4] = fp32 sums
-// (SwiGLU: x = gate sums, y = up sums).
+// Where the epilogue reads and writes. GlobalIO addresses row m of each operand through plain
+// pointers (the split-k reduction kernel). BandIO serves one 16-row band of a GEMM block: each
+// operand is a buffer resource over the band's rows that lie inside it, so rows past M read as
+// zero and drop their stores in the memory unit, and each lane's byte offset at its first column
+// col0 is computed once; a column col then costs an immediate offset (col - col0 is a constant
+// for all but the SwiGLU second half).
+// epilogues that add a bias [N] (SwiGLU: [2 half], gate then up) before their activation
 template <int EPI>
-__device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int n, const float (&x)[4],
-                                          const float (&y)[4]) {
-  const int64_t mr = m;
-  float o[4];
-  if constexpr (EPI == kEpiF32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + mr * g.ldc + n) = f32x4{x[0], x[1], x[2], x[3]};
+constexpr bool epi_has_bias() { return EPI == kEpiBf16 || EPI == kEpiGelu || EPI == kEpiSwiglu; }
+
+struct GlobalIO {
+  const GemmArgs& g;
+  int64_t m;
+  __device__ void load_in(int col, float (&o)[4]) const { load_bf16x4(g.aux_in, m * g.ld_in + col, o); }
+  __device__ void store_c(int col, float a, float b, float c, float d) const {
+    store_bf16x4(g.C, m * g.ldc + col, a, b, c, d);
+  }
+  __device__ void store_out(int col, float a, float b, float c, float d) const {
+    store_bf16x4(g.aux_out, m * g.ld_out + col, a, b, c, d);
+  }
+  __device__ void store_c32(int col, f32x4 v) const {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + m * g.ldc + col) = v;
+  }
+};
+
+__device__ inline __amdgpu_buffer_rsrc_t band_rsrc(const void* p, int64_t ld, int esize, int row, int rows) {
+  return make_rsrc(static_cast<const char*>(p) + int64_t(row) * ld * esize, uint32_t(rows * ld * esize));
+}
+
+struct BandIO {
+  __amdgpu_buffer_rsrc_t c, out, in;
+  uint32_t oc, oo, oi;  // lane byte offsets at (band row lane % 16, column col0)
+  int col0;
+  __device__ void load_in(int col, float (&o)[4]) const {
+    const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(in, oi + uint32_t(col - col0) * 2, 0, 0);
+    o[0] = __uint_as_float(uint32_t(v[0]) << 16);
+    o[1] = __uint_as_float(uint32_t(v[0]) & 0xffff0000u);
+    o[2] = __uint_as_float(uint32_t(v[1]) << 16);
+    o[3] = __uint_as_float(uint32_t(v[1]) & 0xffff0000u);
+  }
+  __device__ void store_c(int col, float a, float b, float c_, float d) const {
+    __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(a, b, c_, d), c, oc + uint32_t(col - col0) * 2, 0, 0);
+  }
+  __device__ void store_out(int col, float a, float b, float c_, float d) const {
+    __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(a, b, c_, d), out, oo + uint32_t(col - col0) * 2, 0, 0);
+  }
+  __device__ void store_c32(int col, f32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), c, oc + uint32_t(col - col0) * 4, 0, 0);
+  }
+  // eight bf16 columns from col (16 bytes)
+  __device__ void store_c16(int col, i32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, c, oc + uint32_t(col - col0) * 2, 0, 0);
+  }
+  __device__ void store_out16(int col, i32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(v, out, oo + uint32_t(col - col0) * 2, 0, 0);
+  }
+};
+
+// The epilogue of one accumulator: four consecutive output columns n .. n+3 of one row, from
+// x[4] = fp32 sums (SwiGLU: x = gate sums, y = up sums), the bias (if any) already added. Results:
+// c -> C[., n], c2 -> C[., half + n], o -> aux_out[., n], o2 -> aux_out[., half + n], each where the
+// epilogue writes it (ep_writes).
+struct EpOut {
+  float c[4], c2[4], o[4], o2[4];
+};
+enum : int { kWc = 1, kWc2 = 2, kWo = 4, kWo2 = 8 };
+template <int EPI>
+__device__ constexpr int ep_writes() {
+  return EPI == kEpiF32 || EPI == kEpiBf16 ? kWc
+       : EPI == kEpiPartialDual ? kWc | kWc2
+       : EPI == kEpiGelu ? kWc | kWo
+       : EPI == kEpiSwiglu ? kWc | kWo | kWo2
+       : EPI == kEpiDgelu ? kWc | kWo
+       : kWc | kWc2 | kWo;  // kEpiDswiglu
+}
+
+template <int EPI, class IO>
+__device__ __forceinline__ void ep_compute(const GemmArgs& g, const IO& io, int n, const float (&x)[4],
+                                           const float (&y)[4], EpOut& r) {
+  if constexpr (EPI == kEpiF32 || EPI == kEpiBf16) {
+    for (int v = 0; v < 4; ++v) r.c[v] = x[v];
   } else if constexpr (EPI == kEpiPartialDual) {
-    float* P = reinterpret_cast<float*>(g.C) + mr * g.ldc;
-    *reinterpret_cast<f32x4*>(P + n) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(P + g.half + n) = f32x4{y[0], y[1], y[2], y[3]};
-  } else if constexpr (EPI == kEpiBf16) {
-    for (int v = 0; v < 4; ++v) o[v] = x[v];
-    if (g.bias) {
-      float b[4];
-      load_bf16x4(g.bias, n, b);
-      for (int v = 0; v < 4; ++v) o[v] += b[v];
-    }
-    store_bf16x4(g.C, mr * g.ldc + n, o[0], o[1], o[2], o[3]);
+    for (int v = 0; v < 4; ++v) { r.c[v] = x[v]; r.c2[v] = y[v]; }
   } else if constexpr (EPI == kEpiGelu) {
-    for (int v = 0; v < 4; ++v) o[v] = x[v];
-    if (g.bias) {
-      float b[4];
-      load_bf16x4(g.bias, n, b);
-      for (int v = 0; v < 4; ++v) o[v] += b[v];
-    }
-    if (g.aux_out) store_bf16x4(g.aux_out, mr * g.ld_out + n, o[0], o[1], o[2], o[3]);
-    for (int v = 0; v < 4; ++v) o[v] = gelu_f(o[v]);
-    store_bf16x4(g.C, mr * g.ldc + n, o[0], o[1], o[2], o[3]);
+    for (int v = 0; v < 4; ++v) { r.o[v] = x[v]; r.c[v] = gelu_f(x[v]); }
   } else if constexpr (EPI == kEpiSwiglu) {
-    float G[4], V[4];
-    for (int v = 0; v < 4; ++v) { G[v] = x[v]; V[v] = y[v]; }
-    if (g.bias) {
-      float bg[4], bu[4];
-      load_bf16x4(g.bias, n, bg);
-      load_bf16x4(g.bias, g.half + n, bu);
-      for (int v = 0; v < 4; ++v) { G[v] += bg[v]; V[v] += bu[v]; }
-    }
-    if (g.aux_out) {
-      store_bf16x4(g.aux_out, mr * g.ld_out + n, G[0], G[1], G[2], G[3]);
-      store_bf16x4(g.aux_out, mr * g.ld_out + g.half + n, V[0], V[1], V[2], V[3]);
-    }
-    for (int v = 0; v < 4; ++v) o[v] = G[v] * sigmoid_f(G[v]) * V[v];
-    store_bf16x4(g.C, mr * g.ldc + n, o[0], o[1], o[2], o[3]);
-  } else if constexpr (EPI == kEpiDgelu) {
-    float u[4], h[4];
-    load_bf16x4(g.aux_in, mr * g.ld_in + n, u);
-    for (int v = 0; v < 4; ++v) { o[v] = x[v] * gelu_grad_f(u[v]); h[v] = gelu_f(u[v]); }
-    store_bf16x4(g.C, mr * g.ldc + n, o[0], o[1], o[2], o[3]);
-    store_bf16x4(g.aux_out, mr * g.ld_out + n, h[0], h[1], h[2], h[3]);
-  } else if constexpr (EPI == kEpiDswiglu) {
-    float G[4], V[4], dV[4], H[4];
-    load_bf16x4(g.aux_in, mr * g.ld_in + n, G);
-    load_bf16x4(g.aux_in, mr * g.ld_in + g.half + n, V);
     for (int v = 0; v < 4; ++v) {
-      const float s = sigmoid_f(G[v]);
-      const float sl = G[v] * s;
-      o[v] = x[v] * V[v] * (s * (1.0f + G[v] * (1.0f - s)));
-      dV[v] = x[v] * sl;
-      H[v] = sl * V[v];
+      r.o[v] = x[v];
+      r.o2[v] = y[v];
+      r.c[v] = x[v] * sigmoid_f(x[v]) * y[v];
     }
-    store_bf16x4(g.C, mr * g.ldc + n, o[0], o[1], o[2], o[3]);
-    store_bf16x4(g.C, mr * g.ldc + g.half + n, dV[0], dV[1], dV[2], dV[3]);
-    store_bf16x4(g.aux_out, mr * g.ld_out + n, H[0], H[1], H[2], H[3]);
+  } else if constexpr (EPI == kEpiDgelu) {
+    float u[4];
+    io.load_in(n, u);
+    for (int v = 0; v < 4; ++v) {
+      float d;
+      gelu_and_grad(u[v], r.o[v], d);
+      r.c[v] = x[v] * d;
+    }
+  } else if constexpr (EPI == kEpiDswiglu) {
+    float G[4], V[4];
+    io.load_in(n, G);
+    io.load_in(int(g.half) + n, V);
+    for (int v = 0; v < 4; ++v) {
+      const float sg = sigmoid_f(G[v]);
+      const float sl = G[v] * sg;
+      r.c[v] = x[v] * V[v] * (sg * (1.0f + G[v] * (1.0f - sg)));
+      r.c2[v] = x[v] * sl;
+      r.o[v] = sl * V[v];
+    }
+  }
+}
+
+// Stores of one accumulator's results, four columns (8 bytes of bf16, 16 of fp32) per lane.
+template <int EPI, class IO>
+__device__ __forceinline__ void ep_store4(const GemmArgs& g, const IO& io, int n, const EpOut& r) {
+  constexpr int w = ep_writes<EPI>();
+  if constexpr (EPI == kEpiF32 || EPI == kEpiPartialDual) {
+    io.store_c32(n, f32x4{r.c[0], r.c[1], r.c[2], r.c[3]});
+    if constexpr ((w & kWc2) != 0) io.store_c32(int(g.half) + n, f32x4{r.c2[0], r.c2[1], r.c2[2], r.c2[3]});
+  } else {
+    io.store_c(n, r.c[0], r.c[1], r.c[2], r.c[3]);
+    if constexpr ((w & kWc2) != 0) io.store_c(int(g.half) + n, r.c2[0], r.c2[1], r.c2[2], r.c2[3]);
+    if (g.aux_out) {
+      if constexpr ((w & kWo) != 0) io.store_out(n, r.o[0], r.o[1], r.o[2], r.o[3]);
+      if constexpr ((w & kWo2) != 0) io.store_out(int(g.half) + n, r.o2[0], r.o2[1], r.o2[2], r.o2[3]);
+    }
+  }
+}
+
+// bf16 results of two accumulators 16 columns apart (a: columns 4q..4q+3 of the first, b: of the
+// second, q = lane / 16) regrouped so that each lane holds eight consecutive columns: lanes
+// exchange with their neighbour 16 lanes over (v_permlane16_swap swaps the odd 16-lane rows of its
+// first operand with the even rows of its second). Afterwards lane quarter q holds the first
+// accumulator's columns 0..7 (q = 0), the second's 0..7 (q = 1), the first's 8..15 (q = 2) or the
+// second's 8..15 (q = 3): column 16 (q & 1) + 8 (q >> 1) of the pair.
+__device__ inline i32x4 pair_cols8(const float (&a)[4], const float (&b)[4]) {
+  const i32x2 x = pack_bf16x4(a[0], a[1], a[2], a[3]);
+  const i32x2 y = pack_bf16x4(b[0], b[1], b[2], b[3]);
+  const auto s0 = __builtin_amdgcn_permlane16_swap(uint32_t(x[0]), uint32_t(y[0]), false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(uint32_t(x[1]), uint32_t(y[1]), false, false);
+  return i32x4{int(s0[0]), int(s1[0]), int(s0[1]), int(s1[1])};
+}
+
+// bf16 stores of two accumulators' results (16 columns apart) as 16-byte stores, eight columns
+// from n_pair per lane (pair_cols8), which gives each row 64 contiguous bytes per instruction.
+// Every lane of the wave must call it (the regrouping reads other lanes); `ok` gates the stores.
+template <int EPI>
+__device__ __forceinline__ void ep_store_pair(const GemmArgs& g, const BandIO& io, int n_pair, bool ok,
+                                              const EpOut& ra, const EpOut& rb) {
+  constexpr int w = ep_writes<EPI>();
+  static_assert(EPI != kEpiF32 && EPI != kEpiPartialDual, "bf16 outputs only");
+  const i32x4 c = pair_cols8(ra.c, rb.c);
+  if (ok) io.store_c16(n_pair, c);
+  if constexpr ((w & kWc2) != 0) {
+    const i32x4 c2 = pair_cols8(ra.c2, rb.c2);
+    if (ok) io.store_c16(int(g.half) + n_pair, c2);
+  }
+  if (g.aux_out) {
+    if constexpr ((w & kWo) != 0) {
+      const i32x4 o = pair_cols8(ra.o, rb.o);
+      if (ok) io.store_out16(n_pair, o);
+    }
+    if constexpr ((w & kWo2) != 0) {
+      const i32x4 o2 = pair_cols8(ra.o2, rb.o2);
+      if (ok) io.store_out16(int(g.half) + n_pair, o2);
+    }
   }
 }
 
@@ -529,44 +657,80 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
     if constexpr (!kEarly || !kEarlyA) read_a1(0, kFM);
     mfmas(af, bf1, 0, kFM);
   }
-  __syncthreads();
 
-  // ---- epilogue: per 16-row band, the wave parks its sums in LDS and re-reads them as whole row
-  // segments, so global loads and stores of the epilogue are contiguous.
-  constexpr int kEpLd = TL::kEpLd;  // floats per parked row (full-rate LDS writes, measured)
-  static_assert(TL::kWaves * 16 * kEpLd * 4 <= TL::kLdsBytes, "park region inside the block's LDS");
-  float* park = reinterpret_cast<float*>(smem) + wave * 16 * kEpLd;
-  const int prow = lane & 15, pcol = 4 * (lane >> 4);
+  // ---- epilogue, straight from the accumulators: per accumulator (im, in), lane l holds columns
+  // ocol(in) + 4 (l / 16) .. + 3 of the wave's band row 16 im + l % 16. Accumulators go in pairs
+  // (in, in + 1): the lanes regroup their bf16 results so that each stores eight consecutive
+  // columns, which gives every row 64 contiguous bytes per store instruction.
+  constexpr int kEs = (EPI == kEpiF32 || EPI == kEpiPartialDual) ? 4 : 2;  // bytes per C element
+  constexpr int kOutFN = kDual ? kFN / 2 : kFN;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int col0 = ocol(0) + 4 * lq;
+  const bool col_edge = n0 + kOutBN > g.N;  // block-uniform: some columns lie past N
+  const uint32_t oc = uint32_t((int64_t(lr) * g.ldc + col0) * kEs);
+  const uint32_t oo = uint32_t((int64_t(lr) * g.ld_out + col0) * 2);
+  const uint32_t oi = uint32_t((int64_t(lr) * g.ld_in + col0) * 2);
+  // the bias of the lane's columns, read once for all bands (SwiGLU: gate in bx, up in by)
+  const bool has_bias = epi_has_bias<EPI>() && g.bias != nullptr;
+  float bx[kOutFN][4], by[kOutFN][4];
+#pragma unroll
+  for (int in = 0; in < kOutFN; ++in) {
+    const int n = ocol(in) + 4 * lq;
+    for (int v = 0; v < 4; ++v) bx[in][v] = by[in][v] = 0.0f;
+    if (has_bias && (!col_edge || n < g.N)) {
+      load_bf16x4(g.bias, n, bx[in]);
+      if constexpr (kDual) load_bf16x4(g.bias, g.half + n, by[in]);
+    }
+  }
 #pragma unroll
   for (int im = 0; im < kFM; ++im) {
+    const int row = m0 + wm * TL::kWaveM + 16 * im;
+    if (row >= g.M) break;
+    const int rows = min(16, g.M - row);
+    BandIO io;
+    io.c = band_rsrc(g.C, g.ldc, kEs, row, rows);
+    io.out = band_rsrc(g.aux_out, g.ld_out, 2, row, rows);
+    io.in = band_rsrc(g.aux_in, g.ld_in, 2, row, rows);
+    io.oc = oc;
+    io.oo = oo;
+    io.oi = oi;
+    io.col0 = col0;
+    // accumulator `in`'s results (a zero bias when there is none: one add instead of a select)
+    auto compute = [&](int in, EpOut& r) {
+      const f32x4 xv = acc[im][in];
+      float x[4] = {xv[0], xv[1], xv[2], xv[3]};
+      if constexpr (epi_has_bias<EPI>())
+        for (int v = 0; v < 4; ++v) x[v] += bx[in][v];
+      if constexpr (kDual) {
+        const f32x4 yv = acc[im][in + kFN / 2];
+        float y[4] = {yv[0], yv[1], yv[2], yv[3]};
+        if constexpr (epi_has_bias<EPI>())
+          for (int v = 0; v < 4; ++v) y[v] += by[in][v];
+        ep_compute<EPI>(g, io, ocol(in) + 4 * lq, x, y, r);
+      } else {
+        ep_compute<EPI>(g, io, ocol(in) + 4 * lq, x, x, r);
+      }
+    };
+    // fp32 outputs already store 16 bytes per lane: no pairs
+    constexpr int kPaired = kEs == 2 ? kOutFN / 2 * 2 : 0;
 #pragma unroll
-    for (int in = 0; in < kFN; ++in)
-      *reinterpret_cast<f32x4*>(park + prow * kEpLd + 16 * in + pcol) = acc[im][in];
-    __syncthreads();
-    const int mbase = m0 + wm * TL::kWaveM + 16 * im;
-    // a parked row holds the wave's 16 kFN accumulator columns (SwiGLU: kWaveN gate then
-    // kWaveN up)
-    constexpr int kLanesPerRow = kWaveN / 4;
-    constexpr int kRowsPerPass = 64 / kLanesPerRow;
-    constexpr int kPasses = (16 + kRowsPerPass - 1) / kRowsPerPass;
-#pragma unroll 1
-    for (int p = 0; p < kPasses; ++p) {
-      const int r = p * kRowsPerPass + lane / kLanesPerRow;
-      const int c = 4 * (lane % kLanesPerRow);
-      const int m = mbase + r, n = n0 + wn * kWaveN + c;
-      if (lane < kRowsPerPass * kLanesPerRow && r < 16 && m < g.M && n < g.N) {
-        const f32x4 xv = *reinterpret_cast<const f32x4*>(park + r * kEpLd + c);
-        const float x[4] = {xv[0], xv[1], xv[2], xv[3]};
-        if constexpr (kDual) {
-          const f32x4 yv = *reinterpret_cast<const f32x4*>(park + r * kEpLd + kWaveN + c);
-          const float y[4] = {yv[0], yv[1], yv[2], yv[3]};
-          epilogue4<EPI>(g, m, n, x, y);
-        } else {
-          epilogue4<EPI>(g, m, n, x, x);
-        }
+    for (int in = 0; in < kPaired; in += 2) {
+      // every lane takes part in the regrouping; only the stores test the columns
+      EpOut ra, rb;
+      compute(in, ra);
+      compute(in + 1, rb);
+      const int np = ocol(in) + 16 * (lq & 1) + 8 * (lq >> 1);
+      if constexpr (kEs == 2) ep_store_pair<EPI>(g, io, np, !col_edge || np < g.N, ra, rb);
+    }
+#pragma unroll
+    for (int in = kPaired; in < kOutFN; ++in) {
+      const int n = ocol(in) + 4 * lq;
+      if (!col_edge || n < g.N) {
+        EpOut r;
+        compute(in, r);
+        ep_store4<EPI>(g, io, n, r);
       }
     }
-    __syncthreads();
   }
 }
 
@@ -787,9 +951,23 @@ __global__ __launch_bounds__(256) void split_epilogue_kernel(GemmArgs g, const f
       xs += *reinterpret_cast<const f32x4*>(row + n);
       if constexpr (EPI == kEpiSwiglu) ys += *reinterpret_cast<const f32x4*>(row + g.N + n);
     }
-    const float x[4] = {xs[0], xs[1], xs[2], xs[3]};
-    const float y[4] = {ys[0], ys[1], ys[2], ys[3]};
-    epilogue4<EPI>(g, int(m), n, x, y);
+    float x[4] = {xs[0], xs[1], xs[2], xs[3]};
+    float y[4] = {ys[0], ys[1], ys[2], ys[3]};
+    if constexpr (epi_has_bias<EPI>()) {
+      if (g.bias) {
+        float b[4];
+        load_bf16x4(g.bias, n, b);
+        for (int v = 0; v < 4; ++v) x[v] += b[v];
+        if constexpr (EPI == kEpiSwiglu) {
+          load_bf16x4(g.bias, g.half + n, b);
+          for (int v = 0; v < 4; ++v) y[v] += b[v];
+        }
+      }
+    }
+    const GlobalIO io{g, m};
+    EpOut r;
+    ep_compute<EPI>(g, io, n, x, y, r);
+    ep_store4<EPI>(g, io, n, r);
   }
 }
 
