@@ -556,30 +556,29 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
 
   // block-uniform: every row and column of this tile lies inside the operands
   const bool interior = (m0 + TL::BM <= g.M) && (n0 + kOutBN <= g.N);
-  // Queue part of block kb's loads: part 0 / 1 = first / second half of the A runs, 2 / 3 = of
-  // the B runs, -1 = all.
-  auto issue = [&](int kb, int part) {
+  // Queue load runs [lo, hi) of block kb: the wave's A runs are numbered first, then its B runs.
+  constexpr int kRuns = kARuns + kBRuns;
+  auto issue = [&](int kb, int lo, int hi) {
     char* a_tile = smem + (kb & 1) * TL::kStageBytes;
     char* b_tile = a_tile + TL::kATileBytes;
     const int k0 = kb * kBK;
-    const bool doA = part < 2, doB = part < 0 || part >= 2;
-    const int a0 = part < 0 || part == 0 ? 0 : kARuns / 2, a1 = part < 0 || part == 1 ? kARuns : kARuns / 2;
-    const int b0 = part < 0 || part == 2 ? 0 : kBRuns / 2, b1 = part < 0 || part == 3 ? kBRuns : kBRuns / 2;
+    const int a0 = lo < kARuns ? lo : kARuns, a1 = hi < kARuns ? hi : kARuns;
+    const int b0 = lo > kARuns ? lo - kARuns : 0, b1 = hi > kARuns ? hi - kARuns : 0;
     if (interior && k0 + kBK <= g.K) {
-      if (doA) {
+      if (a0 < a1) {
         if constexpr (kADirect) aK.issue_fast(rsA, a_tile, wave, k0, a0, a1);
         else aN.issue_fast(rsA, a_tile, wave, k0, a0, a1);
       }
-      if (doB) {
+      if (b0 < b1) {
         if constexpr (kBDirect) bK.issue_fast(rsB, b_tile, wave, k0, b0, b1);
         else bN.issue_fast(rsB, b_tile, wave, k0, b0, b1);
       }
     } else {
-      if (doA) {
+      if (a0 < a1) {
         if constexpr (kADirect) aK.issue(rsA, a_tile, wave, k0, g.K, a0, a1);
         else aN.issue(rsA, a_tile, wave, k0, g.K, a0, a1);
       }
-      if (doB) {
+      if (b0 < b1) {
         if constexpr (kBDirect) bK.issue(rsB, b_tile, wave, k0, g.K, b0, b1);
         else bN.issue(rsB, b_tile, wave, k0, g.K, b0, b1);
       }
@@ -608,20 +607,28 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
         acc[im][in] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[in], af[im], acc[im][in], 0, 0, 0);
   };
 
-  // Main loop. Block kb+1 is loaded while block kb is multiplied; its four load groups are placed
-  // between the four MFMA row groups of the first 32-wide step (pinned by scheduling barriers), so
-  // the load issue overlaps MFMA work instead of stalling every wave right after the barrier.
-  constexpr int kRowsPerGroup = kFM >= 4 ? kFM / 4 : 1;
-  constexpr int kGroups = kFM / kRowsPerGroup;
+  // Main loop. Block kb+1 is loaded while block kb is multiplied, its load runs placed between the
+  // MFMA row groups of the first 32-wide step (pinned by scheduling barriers) so that load issue
+  // overlaps MFMA work instead of stalling every wave right after the barrier.
   // The second 32-wide step's fragments are read while the first step multiplies. Where registers
-  // allow (at most 32 MFMA tiles per wave): B after the first row group, and each row group's A
-  // registers refilled as soon as that group's MFMAs are issued; otherwise B before the last row
-  // group and A after it. Measured on gfx950: 2-9% over reading them after the first step.
+  // allow (at most 32 MFMA tiles per wave): B after the first MFMA row, and each row's A registers
+  // refilled as soon as that row's MFMAs are issued; otherwise B after the last row and A after the
+  // step. Measured on gfx950: 2-9% over reading them after the first step.
   constexpr bool kEarlyA = kFM * kFN <= 32;
   // weight gradients (both operands through transposing reads) keep the plain order: their
   // fragment reads are twice as many, and reading them early measured 20-30% slower
   constexpr bool kEarly = LAYOUT != kWgrad;
-  if (nk > kb0) issue(kb0, -1);
+  // Tiles that refill A early go in four row groups, loading half the A runs, half the A runs, half
+  // the B runs, half the B runs after them. The wide tiles (more than 32 MFMA tiles per wave) load
+  // after every row, an even share each: 1-3% faster for them, 2-5% slower for the others (gfx950).
+  static_assert(kFM % 4 == 0, "four row groups per step");
+  constexpr int kRowsPerGroup = kEarlyA ? kFM / 4 : 1;
+  constexpr int kGroups = kFM / kRowsPerGroup;
+  auto load_bound = [](int q) {
+    if constexpr (kEarlyA) return q == 0 ? 0 : q == 1 ? kARuns / 2 : q == 2 ? kARuns : q == 3 ? kARuns + kBRuns / 2 : kRuns;
+    else return q * kRuns / kFM;
+  };
+  if (nk > kb0) issue(kb0, 0, kRuns);
   for (int kb = kb0; kb < nk; ++kb) {
     wait_loads_and_barrier();
     const bool more = kb + 1 < nk;
@@ -645,12 +652,12 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
       }
     };
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q < kGroups) mfmas(af, bf, q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
+    for (int q = 0; q < kGroups; ++q) {
+      mfmas(af, bf, q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
       __builtin_amdgcn_sched_barrier(0);
-      if (more) issue(kb + 1, q);
-      if (kEarly && q == (kEarlyA ? 0 : 3)) read_b1();
-      if (kEarly && kEarlyA && q < kGroups) read_a1(q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
+      if (more) issue(kb + 1, load_bound(q), load_bound(q + 1));
+      if (kEarly && q == (kEarlyA ? 0 : kGroups - 1)) read_b1();
+      if (kEarly && kEarlyA) read_a1(q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (!kEarly) read_b1();
