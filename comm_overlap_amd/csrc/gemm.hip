@@ -993,6 +993,25 @@ hipError_t launch_split_epilogue(const GemmArgs& g, const float* P, int splits, 
 
 }  // namespace
 
+double estimate_product_us(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, int splits) {
+  constexpr double kBlockUs = 1.9, kLaunchUs = 6.0;
+  if (M <= 0 || N <= 0 || K <= 0) return 0.0;
+  const int64_t nk = (K + kBK - 1) / kBK;
+  if (splits > 1) {
+    // split products run 256 x 256 tiles, `splits` runs each, then the reduction (SwiGLU: over
+    // both halves of the B tile)
+    const int64_t Nt = epi == kEpiSwiglu ? 2 * N : N;
+    const int64_t T = ((M + 255) / 256) * ((Nt + 255) / 256);
+    const int64_t kbs = (nk + splits - 1) / splits;
+    const double red_us = double(2 * splits + 2) * double(M) * double(Nt) * 4.0 / 5e12 * 1e6;
+    return double((T * splits + kCUs - 1) / kCUs) * double(kbs) * kBlockUs + red_us + 2 * kLaunchUs;
+  }
+  const int id = choose_tile(M, N, layout, epi, alone);
+  for (const TileChoice& t : kTiles)
+    if (t.id == id) return tile_cost(t, M, N, epi, nullptr) * double(nk) * kBlockUs + kLaunchUs;
+  return 0.0;
+}
+
 int choose_split(int64_t M, int64_t N, int64_t K) {
   // Estimated time in units of one 64-wide k block of a 256 x 256 tile (about 1.9 us at the
   // tile's per-CU rate): rounds of 256 tiles times the k blocks per split, plus the partials'

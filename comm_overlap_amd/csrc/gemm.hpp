@@ -89,6 +89,12 @@ int choose_split(int64_t M, int64_t N, int64_t K);
 // change a product's rounding; it is chosen for 2048-row slices (the workloads' slice height).
 constexpr int64_t kSplitRefRows = 2048;
 inline int choose_slice_split(int64_t N, int64_t K) { return choose_split(kSplitRefRows, N, K); }
+// Estimated time (us) of one M x N x K product on this GPU (N: output columns; SwiGLU: of each
+// half), with the tile choose_tile picks and
+// `splits` k splits (1: none), from the same per-tile cost model: rounds of 256 CUs times the k
+// blocks per run at about 1.9 us per 64-wide k block of a 256 x 256 tile, plus the split
+// reduction's HBM passes and a fixed launch cost. Used to compare slicings, not as a timing.
+double estimate_product_us(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, int splits = 1);
 // Bytes of partial buffers of an M x N product (N: both halves for SwiGLU) split `splits` ways
 // (0 when splits == 1).
 size_t split_partials_bytes(int64_t M, int64_t N, int splits);

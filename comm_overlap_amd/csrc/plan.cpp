@@ -1,6 +1,7 @@
 // Plan construction and validation (host only, no HIP calls): sizes of one rank's share and the
 // geometry of its independent pieces (Domino page, Abstract: one batch broken into independent
 // pieces). Rows: r equal contiguous token ranges. Columns: c equal ranges of the hand-off output.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -106,6 +107,84 @@ static int32_t default_streams(const tpslice_plan_s* p) {
   return 1;
 }
 
+// Rate of this GPU's local hand-off copy for large pieces (DMA engine, measured 550-760 GB/s for
+// 40-70 MB copies) and the fixed cost of one copy.
+constexpr double kLocalHandoffGbps = 600.0;
+constexpr double kCopyFixedUs = 20.0;
+// Pipelined plans close each row slice's copies with a fence and an event that the next call
+// waits for: measured about 20 us per row slice with one worker stream and 80 us with two (the
+// copy stream then also waits for events of alternating workers).
+constexpr double kSliceSyncUs1 = 20.0, kSliceSyncUs2 = 80.0;
+
+// Predicted time (us) of one call of the forward products with r row and c column slices: the
+// per-slice products from the GEMM cost model, the hand-off pieces at `gbps` plus a fixed cost per
+// copy. With two worker streams, adjacent row slices run side by side, which the model takes as
+// one product over twice the rows for each pair. Row slice i's copies run while later slices
+// compute.
+static double predict_forward_us(const tpslice_desc_t* d, int64_t Fp, int64_t N1, int64_t qkv, int64_t ctx, int r,
+                                 int c, int S, double gbps) {
+  const int64_t Ms = d->tokens / r, h = d->hidden, hc = h / c;
+  const int pair = (S > 1 && r > 1) ? 2 : 1;
+  const int64_t Mp = Ms * pair;  // rows of the products that share the GPU at once
+  const bool alone = pair == 1;
+  const int epi_up = d->act == TPSLICE_ACT_SWIGLU ? kEpiSwiglu : kEpiGelu;
+  double group_us = estimate_product_us(Mp, Fp, h, kFwd, epi_up, alone, choose_slice_split(N1, h)) +
+                    c * estimate_product_us(Mp, hc, Fp, kFwd, kEpiBf16, alone);
+  int tensors = 1;
+  if (qkv > 0) {
+    group_us += estimate_product_us(Mp, qkv, h, kFwd, kEpiBf16, alone, choose_slice_split(qkv, h)) +
+                c * estimate_product_us(Mp, hc, ctx, kFwd, kEpiBf16, alone);
+    tensors = 2;
+  }
+  const double comp_us = group_us * double((r + pair - 1) / pair);
+  const double slice_us = comp_us / r;
+  const double piece_us = double(Ms) * double(hc) * 2.0 * tensors / (gbps * 1e3) + kCopyFixedUs * tensors;
+  const double copy_us = c * piece_us;  // one row slice's pieces
+  if (d->flags & TPSLICE_F_PIPELINE) return std::max(comp_us, r * (copy_us + (S > 1 ? kSliceSyncUs2 : kSliceSyncUs1)));
+  return std::max(comp_us + copy_us, slice_us + r * copy_us);
+}
+
+// Slice counts for a descriptor with r or c = 0 (the header describes the rule).
+static void choose_slices(const tpslice_desc_t* d, int64_t Fp, int64_t N1, int64_t qkv, int64_t ctx, int32_t* r_out,
+                          int32_t* c_out) {
+  const double gbps = d->handoff_gbps > 0.0f ? double(d->handoff_gbps) : kLocalHandoffGbps;
+  int32_t best_r = d->n_row_slices > 0 ? d->n_row_slices : 1;
+  int32_t best_c = d->n_col_slices > 0 ? d->n_col_slices : 1;
+  if (d->tokens <= 0) {
+    *r_out = best_r;
+    *c_out = best_c;
+    return;
+  }
+  double best = 1e300;
+  int best_pieces = 0;
+  for (int32_t r : {1, 2, 4, 8, 16}) {
+    if (d->n_row_slices > 0 && r != d->n_row_slices) continue;
+    if (d->tokens % r) continue;
+    for (int32_t c : {1, 2, 4}) {
+      if (d->n_col_slices > 0 && c != d->n_col_slices) continue;
+      if (d->hidden % c || (d->hidden / c) % 8) continue;
+      // the worker streams the plan would take for this slicing
+      tpslice_plan_s q{};
+      q.desc = *d;
+      q.Fp = Fp; q.N1 = N1; q.qkv = qkv; q.ctx = ctx; q.qh = qkv > 0 ? 1 : 0;
+      q.r = r; q.c = c; q.Ms = d->tokens / r; q.hc = d->hidden / c;
+      const int S = (d->flags & TPSLICE_F_SERIALIZE) ? 1 : d->n_streams > 0 ? d->n_streams : default_streams(&q);
+      const double t = predict_forward_us(d, Fp, N1, qkv, ctx, r, c, S, gbps);
+      const int pieces = r * c;
+      // candidates with more pieces must be 2% faster to be taken
+      const bool better = pieces <= best_pieces ? t < best : t < best * 0.98;
+      if (best_pieces == 0 || better) {
+        best = t;
+        best_pieces = pieces;
+        best_r = r;
+        best_c = c;
+      }
+    }
+  }
+  *r_out = best_r;
+  *c_out = best_c;
+}
+
 extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t* out) {
   clear_error();
   if (!out) return fail(TPSLICE_ERR_INVALID, "tpslice_plan: out is NULL");
@@ -127,12 +206,15 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
                 d->tp_size);
   const int64_t Fp = d->ffn / d->tp_size;
   if (Fp % 8) return fail(TPSLICE_ERR_SHAPE, "ffn shard %lld is not a multiple of 8", (long long)Fp);
-  if (d->n_row_slices < 1 || d->n_col_slices < 1)
-    return fail(TPSLICE_ERR_SHAPE, "slice counts r=%d c=%d must be >= 1", d->n_row_slices, d->n_col_slices);
-  if (d->tokens % d->n_row_slices)
+  if (d->n_row_slices < 0 || d->n_col_slices < 0)
+    return fail(TPSLICE_ERR_SHAPE, "slice counts r=%d c=%d must be >= 0 (0: automatic)", d->n_row_slices,
+                d->n_col_slices);
+  if (!(d->handoff_gbps >= 0.0f) || d->handoff_gbps > 1e6f)
+    return fail(TPSLICE_ERR_SHAPE, "handoff_gbps %g outside [0, 1e6]", double(d->handoff_gbps));
+  if (d->n_row_slices > 0 && d->tokens % d->n_row_slices)
     return fail(TPSLICE_ERR_SHAPE, "%d row slices do not divide %lld tokens evenly", d->n_row_slices,
                 (long long)d->tokens);
-  if (d->hidden % d->n_col_slices || (d->hidden / d->n_col_slices) % 8)
+  if (d->n_col_slices > 0 && (d->hidden % d->n_col_slices || (d->hidden / d->n_col_slices) % 8))
     return fail(TPSLICE_ERR_SHAPE, "%d column slices of hidden %lld must be equal multiples of 8",
                 d->n_col_slices, (long long)d->hidden);
   if (d->n_streams < 0 || d->n_streams > kMaxStreams)
@@ -167,6 +249,9 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   p->desc = *d;
   p->M = M; p->h = h; p->Fp = Fp; p->N1 = N1; p->qkv = qkv; p->ctx = ctx;
   p->r = d->n_row_slices; p->c = d->n_col_slices;
+  if (p->r == 0 || p->c == 0) choose_slices(d, Fp, N1, qkv, ctx, &p->r, &p->c);
+  p->desc.n_row_slices = p->r;
+  p->desc.n_col_slices = p->c;
   p->Ms = M / p->r; p->hc = h / p->c;
   const bool serial = d->flags & TPSLICE_F_SERIALIZE;
   p->qh = qh; p->kvh = kvh;
@@ -200,6 +285,9 @@ extern "C" tpslice_status_t tpslice_plan_info(tpslice_plan_t p, tpslice_plan_inf
   info->q_heads = p->qh; info->kv_heads = p->kvh;
   const int32_t sp[8] = {p->sp_up, p->sp_qkv, p->sp_dh, p->sp_dw1, p->sp_dw2, p->sp_dc, p->sp_dwo, p->sp_dwqkv};
   for (int k = 0; k < 8; ++k) info->k_splits[k] = sp[k];
+  const double gbps = p->desc.handoff_gbps > 0.0f ? double(p->desc.handoff_gbps) : kLocalHandoffGbps;
+  info->predicted_forward_us =
+      predict_forward_us(&p->desc, p->Fp, p->N1, p->qh ? p->qkv : 0, p->ctx, p->r, p->c, p->S, gbps);
   return TPSLICE_OK;
 }
 

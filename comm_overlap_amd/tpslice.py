@@ -46,7 +46,7 @@ class Desc(ctypes.Structure):
                 ("n_col_slices", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("n_streams", ctypes.c_int32), ("n_copy_streams", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("handoff_gbps", ctypes.c_float)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -55,7 +55,8 @@ class PlanInfo(ctypes.Structure):
                 ("rows_per_slice", ctypes.c_int64), ("handoff_cols", ctypes.c_int64),
                 ("n_row_slices", ctypes.c_int32), ("n_col_slices", ctypes.c_int32),
                 ("n_streams", ctypes.c_int32), ("n_copy_streams", ctypes.c_int32),
-                ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("k_splits", ctypes.c_int32 * 8)]
+                ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("k_splits", ctypes.c_int32 * 8),
+                ("predicted_forward_us", ctypes.c_double)]
 
     SPLIT_NAMES = ("up", "qkv", "dh", "dw1", "dw2", "dc", "dwo", "dwqkv")
 
@@ -135,8 +136,8 @@ class Config:
     hidden: int
     ffn: int
     tp_size: int = 1
-    n_row_slices: int = 1
-    n_col_slices: int = 1
+    n_row_slices: int = 1       # 0: chosen by the plan (slice-count model)
+    n_col_slices: int = 1       # 0: chosen by the plan
     n_heads: int = 0
     n_kv_heads: int = 0
     head_dim: int = 0
@@ -147,6 +148,7 @@ class Config:
     copy_blit: bool = False
     pipeline: bool = False
     tile: str = "auto"  # a key of TILES
+    handoff_gbps: float = 0.0  # hand-off rate the automatic slice counts assume (0: local DMA copy)
 
     def desc(self) -> Desc:
         return Desc(self.tokens, self.hidden, self.ffn, self.tp_size, self.n_row_slices, self.n_col_slices,
@@ -155,7 +157,7 @@ class Config:
                     self.n_copy_streams,
                     (F_SERIALIZE if self.serialize else 0) | (F_COPY_BLIT if self.copy_blit else 0)
                     | (F_PIPELINE if self.pipeline else 0)
-                    | (TILES[self.tile] << F_TILE_SHIFT))
+                    | (TILES[self.tile] << F_TILE_SHIFT), float(self.handoff_gbps))
 
 
 class Plan:

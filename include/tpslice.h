@@ -91,8 +91,9 @@ typedef struct {
   int64_t hidden;         /* h: model width; multiple of 8                                            */
   int64_t ffn;            /* F: full FFN width; this rank holds F' = ffn / tp_size (multiple of 8)    */
   int32_t tp_size;        /* simulated tensor-parallel group size (>= 1); no communication happens   */
-  int32_t n_row_slices;   /* r: equal contiguous token-row slices; must divide tokens                 */
-  int32_t n_col_slices;   /* c: equal column slices of each hand-off output (width h); h/c % 8 == 0  */
+  int32_t n_row_slices;   /* r: equal contiguous token-row slices; must divide tokens (0: automatic) */
+  int32_t n_col_slices;   /* c: equal column slices of each hand-off output (width h); h/c % 8 == 0
+                             (0: automatic)                                                         */
   int32_t n_heads;        /* full-model query heads; 0 = no attention projections in this plan       */
   int32_t n_kv_heads;     /* full-model key/value heads (GQA); this rank holds max(1, n_kv/tp_size)   */
   int32_t head_dim;       /* d; multiple of 8                                                          */
@@ -102,7 +103,19 @@ typedef struct {
                              slice i-1's first product is done                                     */
   int32_t n_copy_streams; /* side streams for hand-off copies (0 = default: 1)                        */
   uint32_t flags;         /* TPSLICE_F_*                                                                */
+  float handoff_gbps;     /* hand-off rate in GB/s that the automatic slice counts assume (0: the
+                             local DMA copy of this GPU, about 400 GB/s); ignored for given counts */
 } tpslice_desc_t;
+
+/* Automatic slice counts (Design Space Exploration of DMA based Finer-Grain Compute Communication
+ * Overlap page, Abstract: decomposition and contention slow finer pieces down, and schedules are
+ * picked by heuristics on the operators' static sizes). An r or c of 0 is chosen from r in
+ * {1, 2, 4, 8, 16} dividing tokens and c in {1, 2, 4} keeping h/c a multiple of 8, for the smallest
+ * predicted time of one call of the forward products: the per-slice products' estimated times
+ * (tile, split and launch costs of this GPU) plus the hand-off's exposed time at `handoff_gbps`
+ * (with TPSLICE_F_PIPELINE: the larger of compute and copies per call; without: the copies of the
+ * last row slice, or of all slices when copying is the slower side). Within 2%, fewer pieces win.
+ * tpslice_plan_info reports the counts taken.                                                    */
 
 typedef struct tpslice_plan_s* tpslice_plan_t;
 
@@ -117,6 +130,9 @@ typedef struct {
      runs' fp32 partials in order before the epilogue: the same bits for every slicing of the same
      batch, other rounding than an unsplit product.                                            */
   int32_t k_splits[8];
+  /* the slice-count model's predicted time (us) of one call of the forward products with this
+     plan's r and c (see the automatic slice counts above); a comparison figure, not a timing */
+  double predicted_forward_us;
 } tpslice_plan_info_t;
 
 typedef enum {

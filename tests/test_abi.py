@@ -68,6 +68,9 @@ def test_geometry_small(M, h, r, c):
     (dict(tokens=64, hidden=64, ffn=64, n_heads=6, n_kv_heads=0, head_dim=16), T.ERR_SHAPE),
     (dict(tokens=64, hidden=64, ffn=64, n_streams=99), T.ERR_SHAPE),
     (dict(tokens=1 << 20, hidden=4096, ffn=4096), T.ERR_SHAPE),          # 8 GiB operand
+    (dict(tokens=64, hidden=64, ffn=64, n_row_slices=-1), T.ERR_SHAPE),
+    (dict(tokens=64, hidden=64, ffn=64, n_row_slices=0, handoff_gbps=-1.0), T.ERR_SHAPE),
+    (dict(tokens=64, hidden=64, ffn=64, n_row_slices=0, handoff_gbps=float("nan")), T.ERR_SHAPE),
 ])
 def test_plan_rejects(kw, code):
     with pytest.raises(T.TpsliceError) as e:
@@ -149,3 +152,53 @@ def test_plan_tile_flags():
     assert b"tile id" in T.lib.tpslice_last_error()
     for tile in T.TILES:
         T.Plan(T.Config(tokens=64, hidden=64, ffn=64, tile=tile)).close()
+
+
+LARGE = ["gpt3_2.7b_mlp", "llama2_7b_mlp", "llama2_13b_layer", "llama3_70b_layer"]
+
+
+@pytest.mark.parametrize("key", ["tiny_gpt_mlp"] + LARGE)
+@pytest.mark.parametrize("pipeline", [False, True])
+@pytest.mark.parametrize("gbps", [0.0, 100.0, 25.0])
+def test_automatic_slice_counts_are_valid(key, pipeline, gbps):
+    w = synth.WORKLOADS[key]
+    p = T.plan_for(w, n_row_slices=0, n_col_slices=0, pipeline=pipeline, handoff_gbps=gbps)
+    r, c = p.info.n_row_slices, p.info.n_col_slices
+    assert r in (1, 2, 4, 8, 16) and w.tokens % r == 0
+    assert c in (1, 2, 4) and w.hidden % c == 0 and (w.hidden // c) % 8 == 0
+    assert p.info.rows_per_slice * r == w.tokens and p.info.handoff_cols * c == w.hidden
+    assert p.info.predicted_forward_us > 0
+    # the choice is the model's best over the candidates (fewer pieces within 2%)
+    best = min(T.plan_for(w, n_row_slices=rr, n_col_slices=cc, pipeline=pipeline, handoff_gbps=gbps)
+               .info.predicted_forward_us
+               for rr in (1, 2, 4, 8, 16) if w.tokens % rr == 0
+               for cc in (1, 2, 4) if w.hidden % cc == 0 and (w.hidden // cc) % 8 == 0)
+    assert p.info.predicted_forward_us <= best * 1.02 + 1e-9
+
+
+def test_given_slice_counts_are_kept():
+    w = synth.WORKLOADS["llama3_70b_layer"]
+    for gbps in (0.0, 25.0):
+        p = T.plan_for(w, handoff_gbps=gbps)
+        assert (p.info.n_row_slices, p.info.n_col_slices) == (w.row_slices, w.col_slices)
+    # one count given, the other automatic
+    p = T.plan_for(w, n_row_slices=4, n_col_slices=0)
+    assert p.info.n_row_slices == 4 and p.info.n_col_slices in (1, 2, 4)
+
+
+@pytest.mark.parametrize("key", LARGE)
+def test_slower_handoff_never_takes_fewer_row_slices_for_isolated_calls(key):
+    """Isolated calls expose the last row slice's hand-off, so a slower hand-off is worth at least
+    as many row slices."""
+    w = synth.WORKLOADS[key]
+    rs = [T.plan_for(w, n_row_slices=0, n_col_slices=1, handoff_gbps=g).info.n_row_slices
+          for g in (0.0, 200.0, 100.0, 50.0)]
+    assert rs == sorted(rs), rs
+
+
+@pytest.mark.parametrize("key", LARGE)
+def test_pipelined_chain_on_one_gpu_is_fastest_unsliced(key):
+    """With the local DMA hand-off, a pipelined chain hides the copies of one call behind the next:
+    the model, like the measured sweep, prefers the unsliced products."""
+    p = T.plan_for(synth.WORKLOADS[key], n_row_slices=0, n_col_slices=0, pipeline=True)
+    assert p.info.n_row_slices == 1

@@ -42,6 +42,26 @@ def test_mlp_fwd_small(w, tile):
     assert torch.equal(out["Zh"], out["Z"])
 
 
+AUTO = synth.custom("auto_slices", 909, tokens=2048, hidden=1024, ffn=4096, tp=1, act="gelu", bias=True,
+                    row_slices=1, col_slices=1)
+
+
+@pytest.mark.parametrize("gbps", [0.0, 25.0])
+def test_automatic_slice_counts(gbps):
+    """A plan that chooses its own slice counts computes the same layer (the slower assumed
+    hand-off makes it slice this workload)."""
+    w = AUTO
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w, n_row_slices=0, n_col_slices=0, handoff_gbps=gbps)
+    _print_case("auto_slices", key=w.key, gbps=gbps, r=plan.info.n_row_slices, c=plan.info.n_col_slices)
+    if gbps == 25.0:
+        assert plan.info.n_row_slices * plan.info.n_col_slices > 1
+    out = G.run_mlp_fwd(plan, inp)
+    ref = G.oracle_mlp_fwd(inp, w.act)
+    G.assert_parity(out["Z"], ref["Z"], "Z")
+    assert torch.equal(out["Zh"], out["Z"])
+
+
 def test_mlp_fwd_tiny_workload():
     w = synth.WORKLOADS["tiny_gpt_mlp"]
     _print_case("mlp_fwd", key=w.key)
