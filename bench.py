@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--copy-blit", action="store_true", help="hand-off by copy kernel instead of DMA")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
+    ap.add_argument("--strands", type=int, default=1, choices=[1, 2],
+                    help="2: also time two micro-batches in flight, forward beside backward (layer workloads)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="finish with plain 256 MiB device copies (counter calibration for profiles)")
     return ap.parse_args()
@@ -145,6 +147,61 @@ class Chain:
                 dy_attn = o["dXh"] if h else o["dX"]
                 p.attnproj_bwd(x_prev, t["Wqkv"], t["dQKV"], t["C"], t["Wo"], dy_attn, o["dXa"], o["dC"],
                                g["dWqkv"], g["dWo"], dX_handoff=out("dXah"))
+        self.n += 1
+
+
+class TwoStrands:
+    """Two micro-batches in flight (strand interleaving, Hiding Communication Cost in Distributed
+    LLM Training via Micro-batch Co-execution page, "What carries the argument"), on one GPU: the
+    forward of micro-batch n on one stream beside the backward of micro-batch n-1 on another, so that each
+    strand's products fill the CUs the other's thin products and hand-off copies leave idle. Each
+    strand is a serialized plan (its products and copies in order on its own stream). Micro-batch
+    n-1's backward waits for its forward; micro-batch n+1's forward waits until that backward has
+    read the activation buffers it reuses."""
+
+    def __init__(self, w, inp, kw, blit=False):
+        import torch
+        from comm_overlap_amd import tpslice as T
+        self.w = w
+        kw = dict(kw, copy_blit=blit)
+        self.fwd_plan = T.plan_for(w, serialize=True, **kw)
+        self.bwd_plan = T.plan_for(w, serialize=True, **kw)
+        self.chain = Chain(w, self.fwd_plan, inp)  # activation and output buffers of both sets
+        self.bwd_ws = Chain(w, self.bwd_plan, inp)  # the backward plan's workspaces and gradients
+        self.sa, self.sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+        self.fwd_done = [torch.cuda.Event(), torch.cuda.Event()]
+        self.bwd_done = [torch.cuda.Event(), torch.cuda.Event()]
+        self.n = 0
+
+    def __call__(self):
+        import torch
+        c, w, t = self.chain, self.w, self.chain.t
+        n = self.n
+        o, prev = c.sets[n % 2], c.sets[(n + 1) % 2]
+        with torch.cuda.stream(self.sa):  # forward of micro-batch n
+            if n >= 2:
+                self.sa.wait_event(self.bwd_done[n % 2])
+            p = self.fwd_plan
+            x_prev = prev["Zh"]
+            if w.has_attn:
+                p.attnproj_fwd(x_prev, t["Wqkv"], None, o["QKV"], t["C"], t["Wo"], o["Za"], o["Zah"])
+            x_mlp = o["Zah"] if w.has_attn else x_prev
+            p.mlp_fwd(x_mlp, t["W1"], t.get("b1"), t["W2"], o["Z"], o["U"], o["Zh"])
+            self.fwd_done[n % 2].record(self.sa)
+        if n >= 1:
+            with torch.cuda.stream(self.sb):  # backward of micro-batch n-1, from its set `prev`
+                self.sb.wait_event(self.fwd_done[(n + 1) % 2])
+                p, g, q = self.bwd_plan, self.bwd_ws.g, prev
+                # micro-batch n-1's own layer input is being overwritten by micro-batch n's forward
+                # (it was the hand-off of n-2), so the attention backward reads the seeded input
+                x_in = t["X"] if w.has_attn else q["Zh"]
+                x_mlp = q["Zah"] if w.has_attn else t["X_mlp"]
+                p.mlp_bwd(x_mlp, t["W1"], t["W2"], t["U_saved"], t["dY"], q["dX"], g["dW1"], g["dW2"],
+                          db1=g.get("db1"), dX_handoff=q["dXh"])
+                if w.has_attn:
+                    p.attnproj_bwd(x_in, t["Wqkv"], t["dQKV"], t["C"], t["Wo"], q["dXh"], q["dXa"], q["dC"],
+                                   g["dWqkv"], g["dWo"], dX_handoff=q["dXah"])
+                self.bwd_done[(n + 1) % 2].record(self.sb)
         self.n += 1
 
 
@@ -286,6 +343,22 @@ def main():
     hidden_single = max(0.0, min(1.0, 1.0 - (ms_j - ms_jc) / ms_copy)) if ms_copy > 0 else None
     del jchain, jnocopy
 
+    # 4) optional: two micro-batches in flight (forward of one beside backward of the other)
+    two = None
+    if args.strands == 2 and w.backward:
+        log("two strands")
+        jplan.handoff_wait()
+        torch.cuda.synchronize()
+        jplan.close()  # its streams, so that the two strands' streams have queues of their own
+        two = {}
+        for blit in (False, True):
+            ts = TwoStrands(w, inp, kw, blit=blit)
+            ms_two = timed(ts, args.steps, max(2, args.warmup))
+            two["copy_kernel" if blit else "dma"] = {
+                "ms_per_step": round(ms_two, 4), "tflops": round(flops / (ms_two * 1e-3) / 1e12, 2),
+                "speedup_vs_one_strand": round(ms / ms_two, 3)}
+            del ts
+
     tflops = flops / (ms * 1e-3) / 1e12
     dom_name, dom = max(by.items(), key=lambda kv: kv[1]["ms"])
     dom_ms = dom["ms"] / dom["n"]
@@ -325,10 +398,13 @@ def main():
         "kernels": {k: {"launches": v["n"], "avg_ms": round(v["ms"] / v["n"], 4),
                         "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 1)} for k, v in by.items()},
     }
+    if two is not None:
+        out["two_strands"] = two
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
-    jplan.handoff_wait()
+    if two is None:
+        jplan.handoff_wait()
     torch.cuda.synchronize()
     if args.calib_copy:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")

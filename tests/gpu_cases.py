@@ -26,7 +26,7 @@ def assert_parity(g, o, name):
     return v
 
 
-def run_mlp_fwd(plan, inp, save_u=True, handoff=True):
+def run_mlp_fwd(plan, inp, save_u=True, handoff=True, sync=True):
     X, W1, W2 = dev(inp["X_mlp"]), dev(inp["W1"]), dev(inp["W2"])
     b1 = dev(inp.get("b1"))
     i = plan.info
@@ -34,7 +34,8 @@ def run_mlp_fwd(plan, inp, save_u=True, handoff=True):
     U = torch.empty((i.tokens, i.n1), dtype=torch.bfloat16, device="cuda") if save_u else None
     Zh = torch.full_like(Z, float("nan")) if handoff else None
     plan.mlp_fwd(X, W1, b1, W2, Z, U, Zh)
-    torch.cuda.synchronize()
+    if sync:
+        torch.cuda.synchronize()
     return {"Z": Z, "U": U, "Zh": Zh}
 
 
@@ -43,17 +44,18 @@ def oracle_mlp_fwd(inp, act, rows=None):
     return L.mlp_fwd(f64(X), f64(inp["W1"]), f64(inp["b1"]) if "b1" in inp else None, f64(inp["W2"]), act)
 
 
-def run_attn_fwd(plan, inp, handoff=True, bias=None):
+def run_attn_fwd(plan, inp, handoff=True, bias=None, sync=True):
     i = plan.info
     QKV = torch.empty((i.tokens, i.qkv_width), dtype=torch.bfloat16, device="cuda")
     Z = torch.empty((i.tokens, i.hidden), dtype=torch.bfloat16, device="cuda")
     Zh = torch.empty_like(Z) if handoff else None
     plan.attnproj_fwd(dev(inp["X"]), dev(inp["Wqkv"]), dev(bias), QKV, dev(inp["C"]), dev(inp["Wo"]), Z, Zh)
-    torch.cuda.synchronize()
+    if sync:
+        torch.cuda.synchronize()
     return {"QKV": QKV, "Z": Z, "Zh": Zh}
 
 
-def run_mlp_bwd(plan, inp, with_bias, handoff=True, accumulate=False, init=None):
+def run_mlp_bwd(plan, inp, with_bias, handoff=True, accumulate=False, init=None, sync=True):
     i = plan.info
     dX = torch.empty((i.tokens, i.hidden), dtype=torch.bfloat16, device="cuda")
     dXh = torch.empty_like(dX) if handoff else None
@@ -65,11 +67,12 @@ def run_mlp_bwd(plan, inp, with_bias, handoff=True, accumulate=False, init=None)
         dW1, dW2, db1 = (None if t is None else t.clone() for t in init)
     plan.mlp_bwd(dev(inp["X_mlp"]), dev(inp["W1"]), dev(inp["W2"]), dev(inp["U_saved"]), dev(inp["dY"]),
                  dX, dW1, dW2, db1=db1, dX_handoff=dXh, accumulate=accumulate)
-    torch.cuda.synchronize()
+    if sync:
+        torch.cuda.synchronize()
     return {"dX": dX, "dXh": dXh, "dW1": dW1, "dW2": dW2, "db1": db1}
 
 
-def run_attn_bwd(plan, inp, with_bias, handoff=True, accumulate=False, init=None):
+def run_attn_bwd(plan, inp, with_bias, handoff=True, accumulate=False, init=None, sync=True):
     i = plan.info
     dX = torch.empty((i.tokens, i.hidden), dtype=torch.bfloat16, device="cuda")
     dXh = torch.empty_like(dX) if handoff else None
@@ -83,7 +86,8 @@ def run_attn_bwd(plan, inp, with_bias, handoff=True, accumulate=False, init=None
     plan.attnproj_bwd(dev(inp["X"]), dev(inp["Wqkv"]), dev(inp["dQKV"]), dev(inp["C"]), dev(inp["Wo"]),
                       dev(inp["dY_attn"]), dX, dC, dWqkv, dWo, dbqkv=dbqkv, dX_handoff=dXh,
                       accumulate=accumulate)
-    torch.cuda.synchronize()
+    if sync:
+        torch.cuda.synchronize()
     return {"dX": dX, "dXh": dXh, "dC": dC, "dWqkv": dWqkv, "dWo": dWo, "dbqkv": dbqkv}
 
 

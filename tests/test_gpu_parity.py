@@ -62,6 +62,39 @@ def test_automatic_slice_counts(gbps):
     assert torch.equal(out["Zh"], out["Z"])
 
 
+@pytest.mark.parametrize("copy_blit", [False, True])
+def test_two_strands_match_separate_calls(copy_blit):
+    """The forward of one micro-batch beside the backward of another, each a serialized plan on a
+    stream of its own (the two strands of the micro-batch co-execution page, "What carries the
+    argument"; as bench.py --strands 2 runs them), gives the bits of the same calls run one after
+    the other."""
+    w = SMALL_ATTN
+    _print_case("two_strands", key=w.key, copy_blit=copy_blit)
+    inp = synth.make_inputs(w)
+    fwd_plan = T.plan_for(w, serialize=True, copy_blit=copy_blit)
+    bwd_plan = T.plan_for(w, serialize=True, copy_blit=copy_blit)
+
+    def forward(sync):
+        return G.run_attn_fwd(fwd_plan, inp, sync=sync), G.run_mlp_fwd(fwd_plan, inp, sync=sync)
+
+    def backward(sync):
+        return (G.run_mlp_bwd(bwd_plan, inp, with_bias=w.bias, sync=sync),
+                G.run_attn_bwd(bwd_plan, inp, with_bias=False, sync=sync))
+
+    ref = forward(True) + backward(True)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sa):
+        got_f = forward(False)
+    with torch.cuda.stream(sb):
+        got_b = backward(False)
+    torch.cuda.synchronize()
+    for r, g in zip(ref, got_f + got_b):
+        for k, v in r.items():
+            if v is not None:
+                assert torch.equal(v, g[k]), k
+
+
 def test_mlp_fwd_tiny_workload():
     w = synth.WORKLOADS["tiny_gpt_mlp"]
     _print_case("mlp_fwd", key=w.key)
