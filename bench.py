@@ -153,19 +153,26 @@ class Chain:
 class TwoStrands:
     """Two micro-batches in flight (strand interleaving, Hiding Communication Cost in Distributed
     LLM Training via Micro-batch Co-execution page, "What carries the argument"), on one GPU: the
-    forward of micro-batch n on one stream beside the backward of micro-batch n-1 on another, so that each
-    strand's products fill the CUs the other's thin products and hand-off copies leave idle. Each
-    strand is a serialized plan (its products and copies in order on its own stream). Micro-batch
-    n-1's backward waits for its forward; micro-batch n+1's forward waits until that backward has
-    read the activation buffers it reuses."""
+    forward of micro-batch n on one stream beside the backward of micro-batch n-1 on another, so
+    that each strand's products fill the CUs the other's thin products and hand-off copies leave
+    idle. Micro-batch n-1's backward waits for its forward and that forward's hand-off copies;
+    micro-batch n+1's forward waits until that backward has read the activation buffers it reuses.
 
-    def __init__(self, w, inp, kw, blit=False):
+    mode "dma" / "kernel": each strand a serialized plan (products and copies in order on its
+    stream; the copy by the DMA engines or by a copy kernel). mode "pipelined": each strand a
+    pipelined plan whose worker is the strand's stream and whose DMA copies run on a copy stream
+    of its own (four streams in all, one per hardware queue)."""
+
+    def __init__(self, w, inp, kw, mode):
         import torch
         from comm_overlap_amd import tpslice as T
-        self.w = w
-        kw = dict(kw, copy_blit=blit)
-        self.fwd_plan = T.plan_for(w, serialize=True, **kw)
-        self.bwd_plan = T.plan_for(w, serialize=True, **kw)
+        self.w, self.mode = w, mode
+        if mode == "pipelined":
+            kw = dict(kw, pipeline=True, caller_worker=True, n_streams=1, n_copy_streams=1)
+        else:
+            kw = dict(kw, serialize=True, copy_blit=mode == "kernel")
+        self.fwd_plan = T.plan_for(w, **kw)
+        self.bwd_plan = T.plan_for(w, **kw)
         self.chain = Chain(w, self.fwd_plan, inp)  # activation and output buffers of both sets
         self.bwd_ws = Chain(w, self.bwd_plan, inp)  # the backward plan's workspaces and gradients
         self.sa, self.sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
@@ -178,19 +185,12 @@ class TwoStrands:
         c, w, t = self.chain, self.w, self.chain.t
         n = self.n
         o, prev = c.sets[n % 2], c.sets[(n + 1) % 2]
-        with torch.cuda.stream(self.sa):  # forward of micro-batch n
-            if n >= 2:
-                self.sa.wait_event(self.bwd_done[n % 2])
-            p = self.fwd_plan
-            x_prev = prev["Zh"]
-            if w.has_attn:
-                p.attnproj_fwd(x_prev, t["Wqkv"], None, o["QKV"], t["C"], t["Wo"], o["Za"], o["Zah"])
-            x_mlp = o["Zah"] if w.has_attn else x_prev
-            p.mlp_fwd(x_mlp, t["W1"], t.get("b1"), t["W2"], o["Z"], o["U"], o["Zh"])
-            self.fwd_done[n % 2].record(self.sa)
         if n >= 1:
             with torch.cuda.stream(self.sb):  # backward of micro-batch n-1, from its set `prev`
                 self.sb.wait_event(self.fwd_done[(n + 1) % 2])
+                if self.mode == "pipelined":
+                    # the forward's hand-off copies queued so far are exactly micro-batch n-1's
+                    self.fwd_plan.handoff_wait(self.sb)
                 p, g, q = self.bwd_plan, self.bwd_ws.g, prev
                 # micro-batch n-1's own layer input is being overwritten by micro-batch n's forward
                 # (it was the hand-off of n-2), so the attention backward reads the seeded input
@@ -202,7 +202,22 @@ class TwoStrands:
                     p.attnproj_bwd(x_in, t["Wqkv"], t["dQKV"], t["C"], t["Wo"], q["dXh"], q["dXa"], q["dC"],
                                    g["dWqkv"], g["dWo"], dX_handoff=q["dXah"])
                 self.bwd_done[(n + 1) % 2].record(self.sb)
+        with torch.cuda.stream(self.sa):  # forward of micro-batch n
+            if n >= 2:
+                self.sa.wait_event(self.bwd_done[n % 2])
+            p = self.fwd_plan
+            x_prev = prev["Zh"]
+            if w.has_attn:
+                p.attnproj_fwd(x_prev, t["Wqkv"], None, o["QKV"], t["C"], t["Wo"], o["Za"], o["Zah"])
+            x_mlp = o["Zah"] if w.has_attn else x_prev
+            p.mlp_fwd(x_mlp, t["W1"], t.get("b1"), t["W2"], o["Z"], o["U"], o["Zh"])
+            self.fwd_done[n % 2].record(self.sa)
         self.n += 1
+
+    def handoff_wait(self):
+        """Make the current stream wait for both strands' hand-off copies (timing boundaries)."""
+        self.fwd_plan.handoff_wait()
+        self.bwd_plan.handoff_wait()
 
 
 def timed(fn, steps, warmup, plan=None):
@@ -351,12 +366,11 @@ def main():
         torch.cuda.synchronize()
         jplan.close()  # its streams, so that the two strands' streams have queues of their own
         two = {}
-        for blit in (False, True):
-            ts = TwoStrands(w, inp, kw, blit=blit)
-            ms_two = timed(ts, args.steps, max(2, args.warmup))
-            two["copy_kernel" if blit else "dma"] = {
-                "ms_per_step": round(ms_two, 4), "tflops": round(flops / (ms_two * 1e-3) / 1e12, 2),
-                "speedup_vs_one_strand": round(ms / ms_two, 3)}
+        for mode in ("pipelined", "dma", "kernel"):
+            ts = TwoStrands(w, inp, kw, mode)
+            ms_two = timed(ts, args.steps, max(2, args.warmup), ts)
+            two[mode] = {"ms_per_step": round(ms_two, 4), "tflops": round(flops / (ms_two * 1e-3) / 1e12, 2),
+                         "speedup_vs_one_strand": round(ms / ms_two, 3)}
             del ts
 
     tflops = flops / (ms * 1e-3) / 1e12

@@ -192,7 +192,8 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   if (!d) return fail(TPSLICE_ERR_INVALID, "tpslice_plan: desc is NULL");
   if (d->act != TPSLICE_ACT_GELU && d->act != TPSLICE_ACT_SWIGLU)
     return fail(TPSLICE_ERR_INVALID, "act %d is not TPSLICE_ACT_GELU or TPSLICE_ACT_SWIGLU", d->act);
-  if (d->flags & ~(TPSLICE_F_SERIALIZE | TPSLICE_F_COPY_BLIT | TPSLICE_F_PIPELINE | TPSLICE_F_TILE_MASK))
+  if (d->flags &
+      ~(TPSLICE_F_SERIALIZE | TPSLICE_F_COPY_BLIT | TPSLICE_F_PIPELINE | TPSLICE_F_CALLER_WORKER | TPSLICE_F_TILE_MASK))
     return fail(TPSLICE_ERR_INVALID, "unknown flag bits 0x%x", d->flags);
   if (((d->flags & TPSLICE_F_TILE_MASK) >> TPSLICE_F_TILE_SHIFT) >= TPSLICE_TILE_COUNT)
     return fail(TPSLICE_ERR_INVALID, "tile id %u in the flags is not one of 0..%d",

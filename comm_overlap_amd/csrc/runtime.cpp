@@ -29,8 +29,16 @@ struct TraceSlot {
 
 struct Runtime {
   int device = -1;
+  // worker streams of their own: all S of them, or workers 1..S-1 when worker 0 is the caller's
+  // stream (TPSLICE_F_CALLER_WORKER)
   std::vector<hipStream_t> workers, copiers;
+  int32_t first_own_worker = 0;
   hipEvent_t fork = nullptr;
+  // end of the latest call on its caller's stream (TPSLICE_F_CALLER_WORKER: a call from another
+  // stream waits for it, since the plan's workspace and worker 0 went with the previous caller)
+  hipEvent_t call_done = nullptr;
+  hipStream_t last_caller = nullptr;
+  bool have_last = false;
   std::vector<hipEvent_t> piece;   // one per hand-off piece (and reused per call)
   std::vector<hipEvent_t> slice;   // one per row slice: its products are done
   std::vector<hipEvent_t> lead;    // one per row slice: its first product is done
@@ -68,6 +76,7 @@ void destroy_runtime(Runtime* rt) {
   for (auto s : rt->workers) (void)hipStreamDestroy(s);
   for (auto s : rt->copiers) (void)hipStreamDestroy(s);
   if (rt->fork) (void)hipEventDestroy(rt->fork);
+  if (rt->call_done) (void)hipEventDestroy(rt->call_done);
   for (auto e : rt->piece) (void)hipEventDestroy(e);
   for (auto e : rt->slice) (void)hipEventDestroy(e);
   for (auto e : rt->lead) (void)hipEventDestroy(e);
@@ -102,7 +111,8 @@ tpslice_status_t ensure_runtime(tpslice_plan_s* p, Runtime** out) {
   p->rt = rt;  // owned by the plan from here on, also on partial failure
   const bool serial = p->desc.flags & TPSLICE_F_SERIALIZE;
   if (!serial) {
-    for (int i = 0; i < p->S; ++i) {
+    rt->first_own_worker = (p->desc.flags & TPSLICE_F_CALLER_WORKER) ? 1 : 0;
+    for (int i = rt->first_own_worker; i < p->S; ++i) {
       hipStream_t s;
       TPS_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));  // default priority
       rt->workers.push_back(s);
@@ -114,6 +124,7 @@ tpslice_status_t ensure_runtime(tpslice_plan_s* p, Runtime** out) {
     }
     tpslice_status_t st = make_event(&rt->fork);
     if (st) return st;
+    if ((st = make_event(&rt->call_done))) return st;
     rt->join_w.resize(p->S);
     rt->join_c.resize(p->E);
     for (auto& e : rt->join_w) if ((st = make_event(&e))) return st;
@@ -153,7 +164,11 @@ struct Schedule {
     return TPSLICE_OK;
   }
 
-  hipStream_t worker(int i) const { return serial ? caller : rt->workers[i % p->S]; }
+  // worker stream k: the caller's stream when serialized, or for k = 0 with TPSLICE_F_CALLER_WORKER
+  hipStream_t wk(int k) const {
+    return serial || k < rt->first_own_worker ? caller : rt->workers[k - rt->first_own_worker];
+  }
+  hipStream_t worker(int i) const { return wk(i % p->S); }
   int worker_id(int i) const { return serial ? -1 : i % p->S; }
   bool pipelined() const { return !serial && (p->desc.flags & TPSLICE_F_PIPELINE); }
 
@@ -234,6 +249,8 @@ struct Schedule {
       ++rt->calls;
     }
     if (serial) return TPSLICE_OK;
+    if (rt->first_own_worker && rt->have_last && rt->last_caller != caller)
+      TPS_HIP(hipStreamWaitEvent(caller, rt->call_done, 0));
     TPS_HIP(hipEventRecord(rt->fork, caller));
     for (auto s : rt->workers) TPS_HIP(hipStreamWaitEvent(s, rt->fork, 0));
     for (auto s : rt->copiers) TPS_HIP(hipStreamWaitEvent(s, rt->fork, 0));
@@ -247,15 +264,21 @@ struct Schedule {
       if (copied) TPS_TRY_(fence(caller));
       return TPSLICE_OK;
     }
-    for (int k = 0; k < p->S; ++k) {
-      TPS_HIP(hipEventRecord(rt->join_w[k], rt->workers[k]));
+    for (int k = rt->first_own_worker; k < p->S; ++k) {
+      TPS_HIP(hipEventRecord(rt->join_w[k], wk(k)));
       TPS_HIP(hipStreamWaitEvent(caller, rt->join_w[k], 0));
     }
-    if (pipelined()) return TPSLICE_OK;  // hand-off copies are joined per slice by later calls
-    for (int k = 0; k < p->E; ++k) {
-      if (copied & (1u << k)) TPS_TRY_(fence(rt->copiers[k]));
-      TPS_HIP(hipEventRecord(rt->join_c[k], rt->copiers[k]));
-      TPS_HIP(hipStreamWaitEvent(caller, rt->join_c[k], 0));
+    if (!pipelined()) {  // (pipelined: hand-off copies are joined per slice by later calls)
+      for (int k = 0; k < p->E; ++k) {
+        if (copied & (1u << k)) TPS_TRY_(fence(rt->copiers[k]));
+        TPS_HIP(hipEventRecord(rt->join_c[k], rt->copiers[k]));
+        TPS_HIP(hipStreamWaitEvent(caller, rt->join_c[k], 0));
+      }
+    }
+    if (rt->first_own_worker) {
+      TPS_HIP(hipEventRecord(rt->call_done, caller));
+      rt->last_caller = caller;
+      rt->have_last = true;
     }
     return TPSLICE_OK;
   }
@@ -384,10 +407,10 @@ struct Schedule {
   // products over all tokens that follow can be spread over the workers.
   tpslice_status_t gather_slices() {
     if (serial || p->S == 1) return TPSLICE_OK;
-    for (int k = 0; k < p->S; ++k) TPS_HIP(hipEventRecord(rt->gather[k], rt->workers[k]));
+    for (int k = 0; k < p->S; ++k) TPS_HIP(hipEventRecord(rt->gather[k], wk(k)));
     for (int k = 0; k < p->S; ++k)
       for (int q = 0; q < p->S; ++q)
-        if (q != k) TPS_HIP(hipStreamWaitEvent(rt->workers[k], rt->gather[q], 0));
+        if (q != k) TPS_HIP(hipStreamWaitEvent(wk(k), rt->gather[q], 0));
     return TPSLICE_OK;
   }
 };

@@ -75,6 +75,12 @@ typedef enum {
                                     Abstract: independent pieces pipelined across the batch's work).
                                     Use tpslice_handoff_wait() before reading a hand-off buffer on
                                     another stream, or before freeing buffers the copies touch.    */
+#define TPSLICE_F_CALLER_WORKER 0x40u /* worker stream 0 is the caller's stream (no stream of its own):
+                                    one fork and join fewer per call, and one hardware queue fewer
+                                    (a process has four by default), so that two plans with their
+                                    own copy streams can run side by side, e.g. the forward of one
+                                    micro-batch beside the backward of another. A call from a
+                                    different stream than the previous call waits for it first.    */
 /* Block tile of every product (ablation, testing): flags |= TPSLICE_F_TILE(id). By default (id 0)
    each product takes the tile with the smallest estimated time on the 256 CUs. The tile never
    changes a result bit. Ids: 1 = 256 x 256, 2 = 128 x 128 (4 waves, two blocks per CU),

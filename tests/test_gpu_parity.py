@@ -62,17 +62,20 @@ def test_automatic_slice_counts(gbps):
     assert torch.equal(out["Zh"], out["Z"])
 
 
-@pytest.mark.parametrize("copy_blit", [False, True])
-def test_two_strands_match_separate_calls(copy_blit):
+@pytest.mark.parametrize("mode", ["dma", "kernel", "pipelined"])
+def test_two_strands_match_separate_calls(mode):
     """The forward of one micro-batch beside the backward of another, each a serialized plan on a
     stream of its own (the two strands of the micro-batch co-execution page, "What carries the
     argument"; as bench.py --strands 2 runs them), gives the bits of the same calls run one after
     the other."""
     w = SMALL_ATTN
-    _print_case("two_strands", key=w.key, copy_blit=copy_blit)
+    _print_case("two_strands", key=w.key, mode=mode)
     inp = synth.make_inputs(w)
-    fwd_plan = T.plan_for(w, serialize=True, copy_blit=copy_blit)
-    bwd_plan = T.plan_for(w, serialize=True, copy_blit=copy_blit)
+    if mode == "pipelined":  # worker 0 is the strand's stream; DMA copies on a copy stream each
+        kw = dict(pipeline=True, caller_worker=True, n_streams=1, n_copy_streams=1)
+    else:
+        kw = dict(serialize=True, copy_blit=mode == "kernel")
+    fwd_plan, bwd_plan = T.plan_for(w, **kw), T.plan_for(w, **kw)
 
     def forward(sync):
         return G.run_attn_fwd(fwd_plan, inp, sync=sync), G.run_mlp_fwd(fwd_plan, inp, sync=sync)
@@ -82,12 +85,16 @@ def test_two_strands_match_separate_calls(copy_blit):
                 G.run_attn_bwd(bwd_plan, inp, with_bias=False, sync=sync))
 
     ref = forward(True) + backward(True)
+    fwd_plan.handoff_wait()
+    bwd_plan.handoff_wait()
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.stream(sa):
         got_f = forward(False)
+        fwd_plan.handoff_wait(sa)
     with torch.cuda.stream(sb):
         got_b = backward(False)
+        bwd_plan.handoff_wait(sb)
     torch.cuda.synchronize()
     for r, g in zip(ref, got_f + got_b):
         for k, v in r.items():
