@@ -202,3 +202,19 @@ def test_pipelined_chain_on_one_gpu_is_fastest_unsliced(key):
     the model, like the measured sweep, prefers the unsliced products."""
     p = T.plan_for(synth.WORKLOADS[key], n_row_slices=0, n_col_slices=0, pipeline=True)
     assert p.info.n_row_slices == 1
+
+
+def test_caller_worker_flag():
+    """Worker 0 on the caller's stream: accepted with and without pipelining; nothing to wait for
+    before the first call."""
+    for pipeline in (False, True):
+        p = T.Plan(T.Config(tokens=64, hidden=64, ffn=64, n_row_slices=2, n_streams=2, pipeline=pipeline,
+                            caller_worker=True))
+        assert p.info.n_streams == 2
+        assert T.lib.tpslice_handoff_wait(p._h, None) == T.OK
+        p.close()
+    d = T.Config(tokens=64, hidden=64, ffn=64).desc()
+    d.flags = 0x80  # an unknown bit next to it
+    import ctypes
+    h = ctypes.c_void_p()
+    assert T.lib.tpslice_plan(ctypes.byref(d), ctypes.byref(h)) == T.ERR_INVALID
