@@ -6,7 +6,11 @@
 //   * 256 x 320 and 128 x 320, 8 waves, waves of 128 x 80 / 64 x 80 (products whose operands are
 //     both read along k, without the SwiGLU pairing), one block per CU;
 //   * 128 x 256, 8 waves, waves of 64 x 64, one block per CU (96 KB LDS);
-//   * 128 x 128, 4 waves (2 x 2), waves of 64 x 64, two blocks per CU (64 KB LDS each).
+//   * 128 x 128, 4 waves (2 x 2), waves of 64 x 64, two blocks per CU (64 KB LDS each);
+//   * 256 x 256 and 256 x 160 with 4 waves (2 x 2, one wave per SIMD), waves of 128 x 128 / 128 x
+//     80, one block per CU, for forward products with k a multiple of 64: a software-pipelined
+//     loop (barrier between the two k steps, loads two blocks ahead, LDS reads and load issue
+//     interleaved one by one with the MFMAs) that leaves no wait to another wave.
 // The launcher picks per product the tile with the smallest estimated time on 256 CUs: whole
 // rounds of resident blocks times the tile's work over its measured per-CU rate. Larger tiles move
 // fewer bytes per flop; the others cut the last, partly filled round (e.g. a 4096 x 5120 product is
@@ -74,6 +78,10 @@ using TileW = Tile<256, 320, 2, 4, 1>;
 using TileN = Tile<128, 320, 2, 4, 1>;
 using TileM = Tile<128, 256, 2, 4, 1>;
 using TileT = Tile<128, 128, 2, 4, 1>;
+// Four waves, one per SIMD, each 128 rows x (BN / 2) columns, with the software-pipelined main
+// loop (gemm_kernel); for forward products whose K is a multiple of 64.
+using TileL4 = Tile<256, 256, 2, 2, 1>;
+using TileH4 = Tile<256, 160, 2, 2, 1>;
 
 namespace {
 
@@ -260,6 +268,14 @@ struct NcLoader {
 __device__ inline void wait_loads_and_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The same, also waiting for this wave's LDS reads: the pipelined loop overwrites a stage right
+// after the barrier, while reads of it may still be in flight otherwise.
+__device__ inline void wait_all_and_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -607,62 +623,168 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
         acc[im][in] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[in], af[im], acc[im][in], 0, 0, 0);
   };
 
-  // Main loop. Block kb+1 is loaded while block kb is multiplied, its load runs placed between the
-  // MFMA row groups of the first 32-wide step (pinned by scheduling barriers) so that load issue
-  // overlaps MFMA work instead of stalling every wave right after the barrier.
-  // The second 32-wide step's fragments are read while the first step multiplies. Where registers
-  // allow (at most 32 MFMA tiles per wave): B after the first MFMA row, and each row's A registers
-  // refilled as soon as that row's MFMAs are issued; otherwise B after the last row and A after the
-  // step. Measured on gfx950: 2-9% over reading them after the first step.
-  constexpr bool kEarlyA = kFM * kFN <= 32;
-  // weight gradients (both operands through transposing reads) keep the plain order: their
-  // fragment reads are twice as many, and reading them early measured 20-30% slower
-  constexpr bool kEarly = LAYOUT != kWgrad;
-  // Tiles that refill A early go in four row groups, loading half the A runs, half the A runs, half
-  // the B runs, half the B runs after them. The wide tiles (more than 32 MFMA tiles per wave) load
-  // after every row, an even share each: 1-3% faster for them, 2-5% slower for the others (gfx950).
-  static_assert(kFM % 4 == 0, "four row groups per step");
-  constexpr int kRowsPerGroup = kEarlyA ? kFM / 4 : 1;
-  constexpr int kGroups = kFM / kRowsPerGroup;
-  auto load_bound = [](int q) {
-    if constexpr (kEarlyA) return q == 0 ? 0 : q == 1 ? kARuns / 2 : q == 2 ? kARuns : q == 3 ? kARuns + kBRuns / 2 : kRuns;
-    else return q * kRuns / kFM;
-  };
-  if (nk > kb0) issue(kb0, 0, kRuns);
-  for (int kb = kb0; kb < nk; ++kb) {
-    wait_loads_and_barrier();
-    const bool more = kb + 1 < nk;
-    bf16x8 af[kFM], bf[kFN], bf1[kFN];
-    frags(kb, af, bf, 0);
-    const char* a_tile = smem + (kb & 1) * TL::kStageBytes;
-    const char* b_tile = a_tile + TL::kATileBytes;
-    auto read_b1 = [&]() {
-#pragma unroll
-      for (int in = 0; in < kFN; ++in) {
-        if constexpr (kBDirect) bf1[in] = frag_kc(b_tile, bcol(in), lane, 1);
-        else bf1[in] = frag_nc<TL::BN>(b_tile, bcol(in), lane, 1);
+  // Four-wave tiles: a software-pipelined loop for forward products whose K is a multiple of 64,
+  // unsplit (the launcher checks this). Loads skip the bounds tests: rows past M or N read row 0
+  // (or zero past the operand's end) into rows and columns that the epilogue never stores, and
+  // no k chunk crosses a row. With one wave per SIMD nothing else hides a wait, so the loop keeps
+  // every wait off the MFMA path:
+  //  - the barrier sits between the two 32-wide k steps of a block. After it, the next block's
+  //    step-0 fragments are read and the loads of the block after that are issued, each between two
+  //    MFMAs of step 1; step 1's own fragments are read between the MFMAs of step 0.
+  //  - loads run two blocks ahead: the stage a block's loads fill was released at the barrier
+  //    before (every wave had finished its reads of it), and they have a whole block to land.
+  //  - the loop runs an even number of blocks; with an odd count the last one is all zeros (loads
+  //    past the end read zero), and adding +0 to an fp32 sum that started at +0 changes no bit.
+  //  - the LDS fragment addresses depend only on the lane, the wave and compile-time offsets (the
+  //    KC swizzle of a row depends on its position within 16 rows), and the loop is unrolled over
+  //    the two stages.
+  //  - the MFMAs are inline asm: the 256 accumulators of a wave then stay in AGPRs with no copies,
+  //    which the compiler's own MFMA form did not manage (it shuffled them through VGPRs). The
+  //    compiler does not know their latency, so nothing it places may touch an accumulator early:
+  //    the loop is entered with them zeroed long before (at least 64 instructions on gfx950) and
+  //    leaves only at its bottom, and after it a fixed wait covers the MFMA write-to-read distance
+  //    before every accumulator passes through an empty asm, which orders its reads after the wait.
+  // Measured on gfx950 against the eight-wave tiles, with identical bits: 8192^3 1.38 -> 1.52
+  // PFLOP/s (256 x 256), a 4096 x 2560 x 5120 product 0.97 -> 1.18 PFLOP/s (256 x 160 against 128
+  // x 320).
+  constexpr bool kPipe = TL::kWaves == 4 && TL::BM == 256 && LAYOUT == kFwd;
+  if constexpr (kPipe) {
+    constexpr int kItems = kFM + kFN;  // fragment reads per k step
+    constexpr int kStepM = kFM * kFN;  // MFMAs per k step
+    static_assert(kARuns + kBRuns == kItems, "one load run per fragment read");
+    static_assert(2 * kItems <= kStepM, "a fragment read after every other MFMA of step 0");
+    static_assert((kItems - 1) * kStepM / kItems + 1 < kStepM, "every load run has a slot in step 1");
+    const int lr16 = lane & 15;
+    const int lsw = ((lr16 >> 1) & 7) ^ ((lr16 & 1) << 2);  // swz_kc of any row r with r % 16 == lr16
+    const uint32_t lo0 = lr16 * kRowBytes + (((lane >> 4) ^ lsw) << 4);      // k step 0
+    const uint32_t lo1 = lr16 * kRowBytes + ((((lane >> 4) + 4) ^ lsw) << 4);  // k step 1
+    const uint32_t a_wave = wm * TL::kWaveM * kRowBytes;
+    const uint32_t b_wave = TL::kATileBytes + wn * kWaveN * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rsA0 = make_rsrc(g.A, 0), rsB0 = make_rsrc(g.B, 0);
+    bf16x8 a0[kFM], b0[kFN], a1[kFM], b1[kFN];
+    // fragment read `i` of a k step, in the order the MFMAs first need them: A row 0, the B
+    // columns, the other A rows
+    auto item = [&](int stage, int kk, int i) {
+      const char* st = smem + stage * TL::kStageBytes;
+      const uint32_t lo = kk ? lo1 : lo0;
+      bf16x8(&af)[kFM] = kk ? a1 : a0;
+      bf16x8(&bf)[kFN] = kk ? b1 : b0;
+      if (i == 0 || i > kFN) {
+        const int im = i == 0 ? 0 : i - kFN;
+        af[im] = *reinterpret_cast<const bf16x8*>(st + a_wave + lo + im * 16 * kRowBytes);
+      } else {
+        const int in = i - 1;
+        bf[in] = *reinterpret_cast<const bf16x8*>(st + b_wave + lo + (bcol(in) - wn * kWaveN) * kRowBytes);
       }
     };
-    auto read_a1 = [&](int im0, int im1) {
+    // load run j of block kb into `stage` (the wave's A runs, then its B runs); blocks past the end
+    // go through zero-size resources: every load reads zero and touches no memory
+    auto load_run = [&](int kb, int stage, int j) {
+      char* a_tile = smem + stage * TL::kStageBytes;
+      const bool on = kb < nk;
+      if (j < kARuns) aK.issue_fast(on ? rsA : rsA0, a_tile, wave, kb * kBK, j, j + 1);
+      else bK.issue_fast(on ? rsB : rsB0, a_tile + TL::kATileBytes, wave, kb * kBK, j - kARuns, j - kARuns + 1);
+    };
+    auto mf = [&](int kk, int idx) {
+      const int im = idx / kFN, in = idx % kFN;
+      if (kk) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[im][in]) : "v"(b1[in]), "v"(a1[im]));
+      else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[im][in]) : "v"(b0[in]), "v"(a0[im]));
+    };
+    auto block = [&](int kb, int stage) {
 #pragma unroll
-      for (int im = im0; im < im1; ++im) {
-        const int rbase = wm * TL::kWaveM + 16 * im;
-        if constexpr (kADirect) af[im] = frag_kc(a_tile, rbase, lane, 1);
-        else af[im] = frag_nc<TL::BM>(a_tile, rbase, lane, 1);
+      for (int idx = 0; idx < kStepM; ++idx) {
+        mf(0, idx);
+        if ((idx & 1) && (idx >> 1) < kItems) item(stage, 1, idx >> 1);
+      }
+      wait_all_and_barrier();  // block kb+1 has landed; every wave is done with stage `stage`
+#pragma unroll
+      for (int p = 0; p < kStepM; ++p) {
+        mf(1, p);
+#pragma unroll
+        for (int i = 0; i < kItems; ++i) {
+          const int at = i * kStepM / kItems;  // read i after MFMA `at`, load run i one MFMA later
+          if (at == p) item(stage ^ 1, 0, i);
+          if (at + 1 == p) load_run(kb + 2, stage, i);
+        }
       }
     };
 #pragma unroll
-    for (int q = 0; q < kGroups; ++q) {
-      mfmas(af, bf, q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) issue(kb + 1, load_bound(q), load_bound(q + 1));
-      if (kEarly && q == (kEarlyA ? 0 : kGroups - 1)) read_b1();
-      if (kEarly && kEarlyA) read_a1(q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < kItems; ++j) load_run(0, 0, j);
+    wait_all_and_barrier();
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) item(0, 0, i);
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) load_run(1, 1, j);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kb = 0;; kb += 2) {  // leaves at the bottom only
+      block(kb, 0);
+      block(kb + 1, 1);
+      if (kb + 2 >= nk) break;
     }
-    if constexpr (!kEarly) read_b1();
-    if constexpr (!kEarly || !kEarlyA) read_a1(0, kFM);
-    mfmas(af, bf1, 0, kFM);
+    // 3 x 8 wait states cover the longest MFMA write -> VALU read distance (8-pass MFMA on gfx950)
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int im = 0; im < kFM; ++im)
+#pragma unroll
+      for (int in = 0; in < kFN; ++in) asm volatile("" : "+a"(acc[im][in]));
+  } else {
+    // Main loop. Block kb+1 is loaded while block kb is multiplied, its load runs placed between the
+    // MFMA row groups of the first 32-wide step (pinned by scheduling barriers) so that load issue
+    // overlaps MFMA work instead of stalling every wave right after the barrier.
+    // The second 32-wide step's fragments are read while the first step multiplies. Where registers
+    // allow (at most 32 MFMA tiles per wave): B after the first MFMA row, and each row's A registers
+    // refilled as soon as that row's MFMAs are issued; otherwise B after the last row and A after the
+    // step. Measured on gfx950: 2-9% over reading them after the first step.
+    constexpr bool kEarlyA = kFM * kFN <= 32;
+    // weight gradients (both operands through transposing reads) keep the plain order: their
+    // fragment reads are twice as many, and reading them early measured 20-30% slower
+    constexpr bool kEarly = LAYOUT != kWgrad;
+    // Tiles that refill A early go in four row groups, loading half the A runs, half the A runs, half
+    // the B runs, half the B runs after them. The wide tiles (more than 32 MFMA tiles per wave) load
+    // after every row, an even share each: 1-3% faster for them, 2-5% slower for the others (gfx950).
+    static_assert(kFM % 4 == 0, "four row groups per step");
+    constexpr int kRowsPerGroup = kEarlyA ? kFM / 4 : 1;
+    constexpr int kGroups = kFM / kRowsPerGroup;
+    auto load_bound = [](int q) {
+      if constexpr (kEarlyA) return q == 0 ? 0 : q == 1 ? kARuns / 2 : q == 2 ? kARuns : q == 3 ? kARuns + kBRuns / 2 : kRuns;
+      else return q * kRuns / kFM;
+    };
+    if (nk > kb0) issue(kb0, 0, kRuns);
+    for (int kb = kb0; kb < nk; ++kb) {
+      wait_loads_and_barrier();
+      const bool more = kb + 1 < nk;
+      bf16x8 af[kFM], bf[kFN], bf1[kFN];
+      frags(kb, af, bf, 0);
+      const char* a_tile = smem + (kb & 1) * TL::kStageBytes;
+      const char* b_tile = a_tile + TL::kATileBytes;
+      auto read_b1 = [&]() {
+  #pragma unroll
+        for (int in = 0; in < kFN; ++in) {
+          if constexpr (kBDirect) bf1[in] = frag_kc(b_tile, bcol(in), lane, 1);
+          else bf1[in] = frag_nc<TL::BN>(b_tile, bcol(in), lane, 1);
+        }
+      };
+      auto read_a1 = [&](int im0, int im1) {
+  #pragma unroll
+        for (int im = im0; im < im1; ++im) {
+          const int rbase = wm * TL::kWaveM + 16 * im;
+          if constexpr (kADirect) af[im] = frag_kc(a_tile, rbase, lane, 1);
+          else af[im] = frag_nc<TL::BM>(a_tile, rbase, lane, 1);
+        }
+      };
+  #pragma unroll
+      for (int q = 0; q < kGroups; ++q) {
+        mfmas(af, bf, q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) issue(kb + 1, load_bound(q), load_bound(q + 1));
+        if (kEarly && q == (kEarlyA ? 0 : kGroups - 1)) read_b1();
+        if (kEarly && kEarlyA) read_a1(q * kRowsPerGroup, (q + 1) * kRowsPerGroup);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (!kEarly) read_b1();
+      if constexpr (!kEarly || !kEarlyA) read_a1(0, kFM);
+      mfmas(af, bf1, 0, kFM);
+    }
   }
 
   // ---- epilogue, straight from the accumulators: per accumulator (im, in), lane l holds columns
@@ -763,6 +885,11 @@ template __global__ void gemm_kernel<TileW, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileW, kFwd, kEpiGelu>(GemmArgs);
 template __global__ void gemm_kernel<TileN, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileN, kFwd, kEpiGelu>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kFwd, kEpiBf16>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kFwd, kEpiGelu>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kFwd, kEpiSwiglu>(GemmArgs);
+template __global__ void gemm_kernel<TileH4, kFwd, kEpiBf16>(GemmArgs);
+template __global__ void gemm_kernel<TileH4, kFwd, kEpiGelu>(GemmArgs);
 
 namespace {
 
@@ -846,25 +973,50 @@ hipError_t launch_tile(GemmArgs& g, int layout, int epi, hipStream_t stream, hip
   }
 }
 
+// The four-wave pipelined tiles take forward products only, unsplit, with K a multiple of 64
+// (checked by the launcher).
+template <class TL>
+hipError_t launch_pipe(GemmArgs& g, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  const int out_bn = epi == kEpiSwiglu ? TL::BN / 2 : TL::BN;
+  g.tiles_m = (g.M + TL::BM - 1) / TL::BM;
+  g.tiles_n = (g.N + out_bn - 1) / out_bn;
+  switch (epi) {
+    case kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
+    case kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
+    case kEpiSwiglu:
+      if constexpr (TL::kDualOk) return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
+      else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // Block tiles the launcher chooses from, with their per-CU throughput relative to 256 x 256 when
 // every CU is busy (measured on gfx950 on an 8192^3 product).
 struct TileChoice {
   int id, bm, bn, blocks;
   bool fit_only;  // considered only when the product runs alone (see choose_tile)
-  bool fwd_only;  // operands read along k only, no SwiGLU pairing
+  bool fwd_only;  // operands read along k only, with a bf16 or activation epilogue
+  bool glu_ok;    // takes the SwiGLU pairing
+  bool k64;       // K a multiple of 64 only
   double rate;
 };
+// The four-wave rates: 8192^3 (256 x 256) and a 4096 x 2560 x 5120 product (256 x 160, one round
+// of tiles against 256 x 256's 160 tiles).
 constexpr TileChoice kTiles[] = {
-    {kTile256x256, 256, 256, 1, false, false, 1.00},
-    {kTile128x128, 128, 128, 2, false, false, 0.70},
-    {kTile256x320, 256, 320, 1, true, true, 0.92},
-    {kTile128x320, 128, 320, 1, true, true, 0.73},
-    {kTile128x256, 128, 256, 1, true, false, 0.77},
-    {kTile128x128w8, 128, 128, 1, true, false, 0.50},
+    {kTile256x256, 256, 256, 1, false, false, true, false, 1.00},
+    {kTile128x128, 128, 128, 2, false, false, true, false, 0.70},
+    {kTile256x320, 256, 320, 1, true, true, false, false, 0.92},
+    {kTile128x320, 128, 320, 1, true, true, false, false, 0.73},
+    {kTile128x256, 128, 256, 1, true, false, true, false, 0.77},
+    {kTile128x128w8, 128, 128, 1, true, false, true, false, 0.50},
+    {kTile256x256w4, 256, 256, 1, false, true, true, true, 1.10},
+    {kTile256x160w4, 256, 160, 1, true, true, false, true, 0.83},
 };
 
-bool tile_supports(const TileChoice& t, int layout, int epi) {
-  return !t.fwd_only || (layout == kFwd && epi != kEpiSwiglu);
+bool tile_supports(const TileChoice& t, int64_t K, int layout, int epi) {
+  if (t.fwd_only && (layout != kFwd || (epi != kEpiBf16 && epi != kEpiGelu && epi != kEpiSwiglu))) return false;
+  if (!t.glu_ok && epi == kEpiSwiglu) return false;
+  return !t.k64 || (K > 0 && K % 64 == 0);
 }
 
 uint32_t extent_bytes(int64_t rows, int64_t ld, int64_t cols) {
@@ -893,7 +1045,7 @@ double tile_cost(const TileChoice& t, int64_t M, int64_t N, int epi, double* fil
 
 }  // namespace
 
-int choose_tile(int64_t M, int64_t N, int layout, int epi, bool alone, double* fill) {
+int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, double* fill) {
   // A product that runs alone gets the tile with the smallest estimated time, including the
   // tiles that exist to fill the last round. When products of adjacent slices share the GPU, the
   // CUs one leaves idle run the other's blocks, so only per-CU throughput counts: the 256 x 256
@@ -901,7 +1053,7 @@ int choose_tile(int64_t M, int64_t N, int layout, int epi, bool alone, double* f
   int best = kTile256x256;
   double best_cost = 1e300, best_fill = 1.0;
   for (const TileChoice& t : kTiles) {
-    if (!tile_supports(t, layout, epi) || (t.fit_only && !alone)) continue;
+    if (!tile_supports(t, K, layout, epi) || (t.fit_only && !alone)) continue;
     double f = 1.0;
     const double cost = tile_cost(t, M, N, epi, &f);
     if (cost < best_cost - 1e-9) { best_cost = cost; best = t.id; best_fill = f; }
@@ -923,16 +1075,18 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipE
   if (tile != kTileAuto) {
     // a requested tile that cannot take this product falls back to the automatic choice
     bool ok = false;
-    for (const TileChoice& t : kTiles) ok = ok || (t.id == tile && tile_supports(t, layout, epi));
+    for (const TileChoice& t : kTiles) ok = ok || (t.id == tile && tile_supports(t, g.K, layout, epi));
     if (!ok) tile = kTileAuto;
   }
-  if (tile == kTileAuto) tile = choose_tile(g.M, g.N, layout, epi, alone);
+  if (tile == kTileAuto) tile = choose_tile(g.M, g.N, g.K, layout, epi, alone);
   switch (tile) {
     case kTile128x128: return launch_tile<TileS>(g, layout, epi, stream, start, stop);
     case kTile256x320: return launch_tile<TileW>(g, layout, epi, stream, start, stop);
     case kTile128x320: return launch_tile<TileN>(g, layout, epi, stream, start, stop);
     case kTile128x256: return launch_tile<TileM>(g, layout, epi, stream, start, stop);
     case kTile128x128w8: return launch_tile<TileT>(g, layout, epi, stream, start, stop);
+    case kTile256x256w4: return launch_pipe<TileL4>(g, epi, stream, start, stop);
+    case kTile256x160w4: return launch_pipe<TileH4>(g, epi, stream, start, stop);
     default: return launch_tile<TileL>(g, layout, epi, stream, start, stop);
   }
 }
@@ -1006,7 +1160,7 @@ double estimate_product_us(int64_t M, int64_t N, int64_t K, int layout, int epi,
     const double red_us = double(2 * splits + 2) * double(M) * double(Nt) * 4.0 / 5e12 * 1e6;
     return double((T * splits + kCUs - 1) / kCUs) * double(kbs) * kBlockUs + red_us + 2 * kLaunchUs;
   }
-  const int id = choose_tile(M, N, layout, epi, alone);
+  const int id = choose_tile(M, N, K, layout, epi, alone);
   for (const TileChoice& t : kTiles)
     if (t.id == id) return tile_cost(t, M, N, epi, nullptr) * double(nk) * kBlockUs + kLaunchUs;
   return 0.0;

@@ -52,7 +52,8 @@ struct GemmArgs {
 
 // Block tile of a launch. Every tile reduces k in the same order, so the choice never changes a
 // result bit. The 320-wide tiles take only products whose operands are both read along k, without
-// the SwiGLU pairing; a request they cannot serve falls back to kTileAuto.
+// the SwiGLU pairing, and the four-wave tiles only forward products with K a multiple of 64; a
+// request a tile cannot serve falls back to kTileAuto.
 enum GemmTile : int {
   kTileAuto = 0,
   kTile256x256 = 1,
@@ -61,14 +62,17 @@ enum GemmTile : int {
   kTile128x320 = 4,
   kTile128x256 = 5,
   kTile128x128w8 = 6,  // 128 x 128 with 8 waves, one block per CU
-  kTileCount = 7
+  kTile256x256w4 = 7,  // 256 x 256 with 4 waves and a software-pipelined loop: forward products
+                       // with K a multiple of 64 only
+  kTile256x160w4 = 8,  // 256 x 160, likewise, without the SwiGLU pairing
+  kTileCount = 9
 };
 
-// The tile kTileAuto resolves to for an M x N product (N: output columns). `alone`: the product
+// The tile kTileAuto resolves to for an M x N x K product (N: output columns). `alone`: the product
 // has the GPU to itself (no products of other slices run beside it), so tiles that fill the last
 // round of blocks are worth their lower per-CU rate. `fill` (optional) receives the share of the
 // block slots the chosen tile occupies over its rounds.
-int choose_tile(int64_t M, int64_t N, int layout, int epi, bool alone, double* fill = nullptr);
+int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, double* fill = nullptr);
 
 // Queue one GEMM on `stream`. With `start`/`stop` events the launch records the kernel's own start
 // and end times in them (timestamps of the dispatch itself, no extra marker packets).

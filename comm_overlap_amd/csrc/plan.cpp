@@ -89,19 +89,19 @@ static bool fits_4g(int64_t rows, int64_t cols, int64_t elem) {
 static int32_t default_streams(const tpslice_plan_s* p) {
   if (p->r <= 1) return 1;
   const bool glu = p->desc.act == TPSLICE_ACT_SWIGLU;
-  struct P { int64_t n; int layout, epi; };
+  struct P { int64_t n, k; int layout, epi; };
   const P prods[] = {
-      {p->Fp, kFwd, glu ? kEpiSwiglu : kEpiGelu},  // up-projection (+ activation)
-      {p->hc, kFwd, kEpiBf16},                     // down-projection piece
+      {p->Fp, p->desc.hidden, kFwd, glu ? kEpiSwiglu : kEpiGelu},  // up-projection (+ activation)
+      {p->hc, p->Fp, kFwd, kEpiBf16},                              // down-projection piece
   };
   for (const P& q : prods) {
     double fill = 0.0;
-    choose_tile(p->Ms, q.n, q.layout, q.epi, true, &fill);
+    choose_tile(p->Ms, q.n, q.k, q.layout, q.epi, true, &fill);
     if (fill < 0.9) return 2;
   }
   if (p->qh) {
     double fill = 0.0;
-    choose_tile(p->Ms, p->qkv, kFwd, kEpiBf16, true, &fill);
+    choose_tile(p->Ms, p->qkv, p->desc.hidden, kFwd, kEpiBf16, true, &fill);
     if (fill < 0.9) return 2;
   }
   return 1;

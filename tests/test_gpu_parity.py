@@ -42,6 +42,35 @@ def test_mlp_fwd_small(w, tile):
     assert torch.equal(out["Zh"], out["Z"])
 
 
+# Forward products for the four-wave tiles (k a multiple of 64): whole tiles with an even number of
+# k blocks, and ragged rows and columns with an odd number (the loop then runs one all-zero block).
+WHOLE_GELU = synth.custom("whole_gelu", 904, tokens=1024, hidden=1280, ffn=2560, tp=1, act="gelu", bias=True,
+                          row_slices=2, col_slices=1)
+WHOLE_SWIGLU = synth.custom("whole_swiglu", 905, tokens=1024, hidden=1280, ffn=5120, tp=2, act="swiglu",
+                            bias=False, row_slices=2, col_slices=1)
+RAGGED64_GELU = synth.custom("ragged64_gelu", 906, tokens=1000, hidden=1216, ffn=1344, tp=1, act="gelu",
+                             bias=True, row_slices=2, col_slices=2)
+RAGGED64_SWIGLU = synth.custom("ragged64_swiglu", 907, tokens=744, hidden=704, ffn=2752, tp=2, act="swiglu",
+                               bias=True, row_slices=3, col_slices=1)
+
+
+@pytest.mark.parametrize("w", [WHOLE_GELU, WHOLE_SWIGLU, RAGGED64_GELU, RAGGED64_SWIGLU], ids=lambda w: w.key)
+def test_four_wave_tiles(w):
+    """The software-pipelined four-wave tiles against the oracle, and bit for bit against the
+    eight-wave 256 x 256 tile (same k order), twice in a row."""
+    inp = synth.make_inputs(w)
+    ref = G.oracle_mlp_fwd(inp, w.act)
+    base = G.run_mlp_fwd(T.plan_for(w, tile="256x256"), inp)
+    for tile in ("256x256w4", "256x160w4", "auto", "256x256w4"):
+        _print_case("four_wave", key=w.key, tile=tile)
+        out = G.run_mlp_fwd(T.plan_for(w, tile=tile), inp)
+        G.assert_parity(out["Z"], ref["Z"], "Z")
+        G.assert_parity(out["U"], ref["U"], "U")
+        assert torch.equal(out["Z"], base["Z"]), tile
+        assert torch.equal(out["U"], base["U"]), tile
+        assert torch.equal(out["Zh"], out["Z"]), tile
+
+
 AUTO = synth.custom("auto_slices", 909, tokens=2048, hidden=1024, ffn=4096, tp=1, act="gelu", bias=True,
                     row_slices=1, col_slices=1)
 
