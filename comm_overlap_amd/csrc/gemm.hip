@@ -113,6 +113,44 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// The same descriptor as raw words, for the pipelined loop's own load instruction (dword1: the
+// high address bits, stride 0; dword3: the flags make_rsrc passes).
+__device__ inline i32x4 raw_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xffffu), int(bytes), 0x00020000};
+}
+
+// One direct global -> LDS load (buffer_load_dwordx4 ... lds, sc1): lane l's 16 bytes at
+// voff + soff go to LDS byte address lds + 16 l. It is written out here rather than through the
+// builtin because the compiler, which cannot tell which LDS bytes such a load writes, makes every
+// later ds_read_b64_tr_b16 wait for all loads in flight (s_waitcnt vmcnt(0)); in the pipelined loop
+// that serializes the next block's loads behind each transposing read. The loop's own waits
+// (s_waitcnt vmcnt(0) before the barrier that publishes a stage) order these loads against the
+// reads. M0 carries the LDS address and is restored afterwards; the load writes no register.
+// f(integral_constant<int, i>) for i = I .. N-1, in order
+template <int I, int N, class F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// `lds` (wave-uniform) + OFF is the LDS address.
+template <int OFF>
+__device__ inline void dma16(const i32x4& rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %5\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen sc1 lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rs), "s"(soff), "i"(OFF)
+      : "memory", "scc");
+}
+
 // 16-byte chunk swizzles, chosen by measurement on gfx950 (LDS read throughput of each candidate
 // lane pattern): KC rows of 128 B (8 chunks) XOR the chunk with ((r >> 1) & 7) ^ ((r & 1) << 2),
 // which lets the fragment reads (16 consecutive rows per 16-lane group) run at full LDS rate;
@@ -547,7 +585,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
 #pragma unroll
     for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (EPI == kEpiF32) {
+  // (the four-wave pipelined tiles never take accumulate = 1: the launcher checks this, since their
+  // accumulators are inline-asm operands that nothing the compiler places may write late)
+  constexpr bool kPipe = TL::kWaves == 4 && TL::BM == 256;
+  if constexpr (EPI == kEpiF32 && !kPipe) {
     if (g.accumulate) {
       const float* C = reinterpret_cast<const float*>(g.C);
 #pragma unroll
@@ -623,10 +664,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
         acc[im][in] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[in], af[im], acc[im][in], 0, 0, 0);
   };
 
-  // Four-wave tiles: a software-pipelined loop for forward products whose K is a multiple of 64,
-  // unsplit (the launcher checks this). Loads skip the bounds tests: rows past M or N read row 0
-  // (or zero past the operand's end) into rows and columns that the epilogue never stores, and
-  // no k chunk crosses a row. With one wave per SIMD nothing else hides a wait, so the loop keeps
+  // Four-wave tiles: a software-pipelined loop for products whose K is a multiple of 64 (the
+  // launcher checks this), in every operand layout and for the runs of a split product. Loads
+  // skip the bounds tests: rows past M or N (columns, for an operand stored across k) read row or
+  // column 0 (or zero past the operand's end) into rows and columns that the epilogue never
+  // stores, and no k chunk crosses a row. With one wave per SIMD nothing else hides a wait, so the loop keeps
   // every wait off the MFMA path:
   //  - the barrier sits between the two 32-wide k steps of a block. After it, the next block's
   //    step-0 fragments are read and the loads of the block after that are issued, each between two
@@ -647,7 +689,6 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   // Measured on gfx950 against the eight-wave tiles, with identical bits: 8192^3 1.38 -> 1.52
   // PFLOP/s (256 x 256), a 4096 x 2560 x 5120 product 0.97 -> 1.18 PFLOP/s (256 x 160 against 128
   // x 320).
-  constexpr bool kPipe = TL::kWaves == 4 && TL::BM == 256 && LAYOUT == kFwd;
   if constexpr (kPipe) {
     constexpr int kItems = kFM + kFN;  // fragment reads per k step
     constexpr int kStepM = kFM * kFN;  // MFMAs per k step
@@ -660,7 +701,53 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
     const uint32_t lo1 = lr16 * kRowBytes + ((((lane >> 4) + 4) ^ lsw) << 4);  // k step 1
     const uint32_t a_wave = wm * TL::kWaveM * kRowBytes;
     const uint32_t b_wave = TL::kATileBytes + wn * kWaveN * kRowBytes;
-    const __amdgpu_buffer_rsrc_t rsA0 = make_rsrc(g.A, 0), rsB0 = make_rsrc(g.B, 0);
+    // An operand read across k ([64 k][tile columns]): the lane's first transposing read of the
+    // fragment whose first column is cb in k step 0 (frag_nc's addressing). The swizzle of k rows
+    // 8 (l / 16) + (l % 16) / 4 (+4, +32) is the same for all four, so a fragment's two reads and
+    // the second k step sit at fixed distances; the XOR with the column chunk is per fragment.
+    auto nc_off = [&](int cb, int cols) -> uint32_t {
+      const int gq = lane >> 4, v = (lane & 15) >> 2, q = lane & 3;
+      const int k0 = 8 * gq + v;
+      const int chunk = (cb >> 3) + (q >> 1);
+      return uint32_t(k0 * cols * 2 + ((chunk ^ swz_nc(k0)) << 4) + ((q & 1) << 3));
+    };
+    uint32_t a_nc[kADirect ? 1 : kFM], b_nc[kBDirect ? 1 : kFN];
+    if constexpr (!kADirect) {
+#pragma unroll
+      for (int im = 0; im < kFM; ++im) a_nc[im] = nc_off(wm * TL::kWaveM + 16 * im, TL::BM);
+    }
+    if constexpr (!kBDirect) {
+#pragma unroll
+      for (int in = 0; in < kFN; ++in) b_nc[in] = TL::kATileBytes + nc_off(bcol(in), TL::BN);
+    }
+    auto read_nc = [](const char* p, int row_bytes) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * row_bytes));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, w);
+    };
+    const i32x4 rwA = raw_rsrc(g.A, g.a_bytes), rwB = raw_rsrc(g.B, g.b_bytes);
+    const i32x4 rwA0 = raw_rsrc(g.A, 0), rwB0 = raw_rsrc(g.B, 0);
+    // the wave's first load run in stage 0 (LDS byte address, wave-uniform)
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem)) + uint32_t(wave) * 1024u * kARuns);
+    const uint32_t lds_wave_b = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem)) + uint32_t(wave) * 1024u * kBRuns);
+    // each load run's lane offset (the k offset rides in the scalar offset)
+    uint32_t a_voff[kARuns], b_voff[kBRuns];
+#pragma unroll
+    for (int j = 0; j < kARuns; ++j) {
+      if constexpr (kADirect) a_voff[j] = aK.off[j];
+      else a_voff[j] = aN.krow[j] * aN.ld_bytes + aN.col_off[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kBRuns; ++j) {
+      if constexpr (kBDirect) b_voff[j] = bK.off[j];
+      else b_voff[j] = bN.krow[j] * bN.ld_bytes + bN.col_off[j];
+    }
+    const uint32_t a_kstep = kADirect ? 2u : aN.ld_bytes;  // scalar offset per k element
+    const uint32_t b_kstep = kBDirect ? 2u : bN.ld_bytes;
     bf16x8 a0[kFM], b0[kFN], a1[kFM], b1[kFN];
     // fragment read `i` of a k step, in the order the MFMAs first need them: A row 0, the B
     // columns, the other A rows
@@ -671,19 +758,31 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
       bf16x8(&bf)[kFN] = kk ? b1 : b0;
       if (i == 0 || i > kFN) {
         const int im = i == 0 ? 0 : i - kFN;
-        af[im] = *reinterpret_cast<const bf16x8*>(st + a_wave + lo + im * 16 * kRowBytes);
+        if constexpr (kADirect) af[im] = *reinterpret_cast<const bf16x8*>(st + a_wave + lo + im * 16 * kRowBytes);
+        else af[im] = read_nc(st + a_nc[im] + kk * 32 * TL::BM * 2, TL::BM * 2);
       } else {
         const int in = i - 1;
-        bf[in] = *reinterpret_cast<const bf16x8*>(st + b_wave + lo + (bcol(in) - wn * kWaveN) * kRowBytes);
+        if constexpr (kBDirect)
+          bf[in] = *reinterpret_cast<const bf16x8*>(st + b_wave + lo + (bcol(in) - wn * kWaveN) * kRowBytes);
+        else bf[in] = read_nc(st + b_nc[in] + kk * 32 * TL::BN * 2, TL::BN * 2);
       }
     };
     // load run j of block kb into `stage` (the wave's A runs, then its B runs); blocks past the end
     // go through zero-size resources: every load reads zero and touches no memory
-    auto load_run = [&](int kb, int stage, int j) {
-      char* a_tile = smem + stage * TL::kStageBytes;
+    // The loads of one block: the descriptors (zero-size past the end) and scalar k offsets are
+    // chosen once per block; a run's LDS slot is the wave's base plus a constant.
+    struct BlockLoads { i32x4 ra, rb; uint32_t sa, sb; };
+    auto block_loads = [&](int kb) {
       const bool on = kb < nk;
-      if (j < kARuns) aK.issue_fast(on ? rsA : rsA0, a_tile, wave, kb * kBK, j, j + 1);
-      else bK.issue_fast(on ? rsB : rsB0, a_tile + TL::kATileBytes, wave, kb * kBK, j - kARuns, j - kARuns + 1);
+      return BlockLoads{on ? rwA : rwA0, on ? rwB : rwB0, uint32_t(kb * kBK) * a_kstep, uint32_t(kb * kBK) * b_kstep};
+    };
+    auto load_run = [&](const BlockLoads& bl, int stage, auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < kARuns)
+        dma16<j * 1024>(bl.ra, lds_wave + stage * TL::kStageBytes, a_voff[j], bl.sa);
+      else
+        dma16<(j - kARuns) * 1024>(bl.rb, lds_wave_b + stage * TL::kStageBytes + TL::kATileBytes,
+                                   b_voff[j - kARuns], bl.sb);
     };
     auto mf = [&](int kk, int idx) {
       const int im = idx / kFN, in = idx % kFN;
@@ -697,26 +796,32 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
         if ((idx & 1) && (idx >> 1) < kItems) item(stage, 1, idx >> 1);
       }
       wait_all_and_barrier();  // block kb+1 has landed; every wave is done with stage `stage`
-#pragma unroll
-      for (int p = 0; p < kStepM; ++p) {
+      const BlockLoads bl = block_loads(kb + 2);
+      static_for<0, kStepM>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
         mf(1, p);
-#pragma unroll
-        for (int i = 0; i < kItems; ++i) {
-          const int at = i * kStepM / kItems;  // read i after MFMA `at`, load run i one MFMA later
-          if (at == p) item(stage ^ 1, 0, i);
-          if (at + 1 == p) load_run(kb + 2, stage, i);
-        }
-      }
+        static_for<0, kItems>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          constexpr int at = i * kStepM / kItems;  // read i after MFMA `at`, load run i one MFMA later
+          if constexpr (at == p) item(stage ^ 1, 0, i);
+          if constexpr (at + 1 == p) load_run(bl, stage, ic);
+        });
+      });
     };
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) load_run(0, 0, j);
+    // this block's k blocks start at kb0 (a split product's run; 0 otherwise)
+    {
+      const BlockLoads bl = block_loads(kb0);
+      static_for<0, kItems>([&](auto jc) { load_run(bl, 0, jc); });
+    }
     wait_all_and_barrier();
 #pragma unroll
     for (int i = 0; i < kItems; ++i) item(0, 0, i);
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) load_run(1, 1, j);
+    {
+      const BlockLoads bl = block_loads(kb0 + 1);
+      static_for<0, kItems>([&](auto jc) { load_run(bl, 1, jc); });
+    }
     __builtin_amdgcn_sched_barrier(0);
-    for (int kb = 0;; kb += 2) {  // leaves at the bottom only
+    for (int kb = kb0;; kb += 2) {  // leaves at the bottom only
       block(kb, 0);
       block(kb + 1, 1);
       if (kb + 2 >= nk) break;
@@ -888,6 +993,13 @@ template __global__ void gemm_kernel<TileN, kFwd, kEpiGelu>(GemmArgs);
 template __global__ void gemm_kernel<TileL4, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileL4, kFwd, kEpiGelu>(GemmArgs);
 template __global__ void gemm_kernel<TileL4, kFwd, kEpiSwiglu>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kDgrad, kEpiBf16>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kDgrad, kEpiDgelu>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kDgrad, kEpiDswiglu>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kDgrad, kEpiF32>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kWgrad, kEpiF32>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kFwd, kEpiF32>(GemmArgs);
+template __global__ void gemm_kernel<TileL4, kFwd, kEpiPartialDual>(GemmArgs);
 template __global__ void gemm_kernel<TileH4, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileH4, kFwd, kEpiGelu>(GemmArgs);
 
@@ -933,18 +1045,24 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEve
   return hipGetLastError();
 }
 
-// The fp32 partial product of a split product (256 x 256 tiles).
-hipError_t launch_partial(GemmArgs& g, int layout, bool dual, hipStream_t stream, hipEvent_t start) {
-  const int out_bn = dual ? TileL::BN / 2 : TileL::BN;
-  g.tiles_m = (g.M + TileL::BM - 1) / TileL::BM;
+// The fp32 partial product of a split product (256 x 256 tiles; the four-wave pipelined ones when
+// K is a multiple of 64 and `pipe` allows it; either gives the same bits).
+template <class TL>
+hipError_t launch_partial_tile(GemmArgs& g, int layout, bool dual, hipStream_t stream, hipEvent_t start) {
+  const int out_bn = dual ? TL::BN / 2 : TL::BN;
+  g.tiles_m = (g.M + TL::BM - 1) / TL::BM;
   g.tiles_n = (g.N + out_bn - 1) / out_bn;
-  if (dual) return launch_one<TileL, kFwd, kEpiPartialDual>(g, stream, start, nullptr);
+  if (dual) return launch_one<TL, kFwd, kEpiPartialDual>(g, stream, start, nullptr);
   switch (layout) {
-    case kFwd: return launch_one<TileL, kFwd, kEpiF32>(g, stream, start, nullptr);
-    case kDgrad: return launch_one<TileL, kDgrad, kEpiF32>(g, stream, start, nullptr);
-    case kWgrad: return launch_one<TileL, kWgrad, kEpiF32>(g, stream, start, nullptr);
+    case kFwd: return launch_one<TL, kFwd, kEpiF32>(g, stream, start, nullptr);
+    case kDgrad: return launch_one<TL, kDgrad, kEpiF32>(g, stream, start, nullptr);
+    case kWgrad: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, nullptr);
     default: return hipErrorInvalidValue;
   }
+}
+hipError_t launch_partial(GemmArgs& g, int layout, bool dual, bool pipe, hipStream_t stream, hipEvent_t start) {
+  if (pipe && g.K > 0 && g.K % 64 == 0) return launch_partial_tile<TileL4>(g, layout, dual, stream, start);
+  return launch_partial_tile<TileL>(g, layout, dual, stream, start);
 }
 
 template <class TL>
@@ -973,20 +1091,31 @@ hipError_t launch_tile(GemmArgs& g, int layout, int epi, hipStream_t stream, hip
   }
 }
 
-// The four-wave pipelined tiles take forward products only, unsplit, with K a multiple of 64
-// (checked by the launcher).
+// The four-wave pipelined tiles take products with K a multiple of 64 and no accumulation into an
+// fp32 output (checked by the launcher); 256 x 160 only forward ones without the SwiGLU pairing.
 template <class TL>
-hipError_t launch_pipe(GemmArgs& g, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_pipe(GemmArgs& g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const int out_bn = epi == kEpiSwiglu ? TL::BN / 2 : TL::BN;
   g.tiles_m = (g.M + TL::BM - 1) / TL::BM;
   g.tiles_n = (g.N + out_bn - 1) / out_bn;
-  switch (epi) {
-    case kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
-    case kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
-    case kEpiSwiglu:
-      if constexpr (TL::kDualOk) return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
-      else return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+  if constexpr (TL::kNcA && TL::kNcB && TL::kDualOk) {
+    switch (layout * 8 + epi) {
+      case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
+      case kFwd * 8 + kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
+      case kFwd * 8 + kEpiSwiglu: return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiBf16: return launch_one<TL, kDgrad, kEpiBf16>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiDgelu: return launch_one<TL, kDgrad, kEpiDgelu>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiDswiglu: return launch_one<TL, kDgrad, kEpiDswiglu>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiF32: return launch_one<TL, kDgrad, kEpiF32>(g, stream, start, stop);
+      case kWgrad * 8 + kEpiF32: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, stop);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (layout * 8 + epi) {
+      case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
+      case kFwd * 8 + kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
@@ -997,7 +1126,7 @@ struct TileChoice {
   bool fit_only;  // considered only when the product runs alone (see choose_tile)
   bool fwd_only;  // operands read along k only, with a bf16 or activation epilogue
   bool glu_ok;    // takes the SwiGLU pairing
-  bool k64;       // K a multiple of 64 only
+  bool pipe;      // four-wave pipelined: K a multiple of 64 only, no accumulation into fp32 outputs
   double rate;
 };
 // The four-wave rates: 8192^3 (256 x 256) and a 4096 x 2560 x 5120 product (256 x 160, one round
@@ -1009,14 +1138,14 @@ constexpr TileChoice kTiles[] = {
     {kTile128x320, 128, 320, 1, true, true, false, false, 0.73},
     {kTile128x256, 128, 256, 1, true, false, true, false, 0.77},
     {kTile128x128w8, 128, 128, 1, true, false, true, false, 0.50},
-    {kTile256x256w4, 256, 256, 1, false, true, true, true, 1.10},
+    {kTile256x256w4, 256, 256, 1, false, false, true, true, 1.10},
     {kTile256x160w4, 256, 160, 1, true, true, false, true, 0.83},
 };
 
-bool tile_supports(const TileChoice& t, int64_t K, int layout, int epi) {
+bool tile_supports(const TileChoice& t, int64_t K, int layout, int epi, bool accumulate) {
   if (t.fwd_only && (layout != kFwd || (epi != kEpiBf16 && epi != kEpiGelu && epi != kEpiSwiglu))) return false;
   if (!t.glu_ok && epi == kEpiSwiglu) return false;
-  return !t.k64 || (K > 0 && K % 64 == 0);
+  return !t.pipe || (K > 0 && K % 64 == 0 && !(accumulate && epi == kEpiF32));
 }
 
 uint32_t extent_bytes(int64_t rows, int64_t ld, int64_t cols) {
@@ -1045,7 +1174,7 @@ double tile_cost(const TileChoice& t, int64_t M, int64_t N, int epi, double* fil
 
 }  // namespace
 
-int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, double* fill) {
+int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, double* fill, bool accumulate) {
   // A product that runs alone gets the tile with the smallest estimated time, including the
   // tiles that exist to fill the last round. When products of adjacent slices share the GPU, the
   // CUs one leaves idle run the other's blocks, so only per-CU throughput counts: the 256 x 256
@@ -1053,7 +1182,7 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone
   int best = kTile256x256;
   double best_cost = 1e300, best_fill = 1.0;
   for (const TileChoice& t : kTiles) {
-    if (!tile_supports(t, K, layout, epi) || (t.fit_only && !alone)) continue;
+    if (!tile_supports(t, K, layout, epi, accumulate) || (t.fit_only && !alone)) continue;
     double f = 1.0;
     const double cost = tile_cost(t, M, N, epi, &f);
     if (cost < best_cost - 1e-9) { best_cost = cost; best = t.id; best_fill = f; }
@@ -1075,18 +1204,19 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipE
   if (tile != kTileAuto) {
     // a requested tile that cannot take this product falls back to the automatic choice
     bool ok = false;
-    for (const TileChoice& t : kTiles) ok = ok || (t.id == tile && tile_supports(t, g.K, layout, epi));
+    for (const TileChoice& t : kTiles)
+      ok = ok || (t.id == tile && tile_supports(t, g.K, layout, epi, g.accumulate != 0));
     if (!ok) tile = kTileAuto;
   }
-  if (tile == kTileAuto) tile = choose_tile(g.M, g.N, g.K, layout, epi, alone);
+  if (tile == kTileAuto) tile = choose_tile(g.M, g.N, g.K, layout, epi, alone, nullptr, g.accumulate != 0);
   switch (tile) {
     case kTile128x128: return launch_tile<TileS>(g, layout, epi, stream, start, stop);
     case kTile256x320: return launch_tile<TileW>(g, layout, epi, stream, start, stop);
     case kTile128x320: return launch_tile<TileN>(g, layout, epi, stream, start, stop);
     case kTile128x256: return launch_tile<TileM>(g, layout, epi, stream, start, stop);
     case kTile128x128w8: return launch_tile<TileT>(g, layout, epi, stream, start, stop);
-    case kTile256x256w4: return launch_pipe<TileL4>(g, epi, stream, start, stop);
-    case kTile256x160w4: return launch_pipe<TileH4>(g, epi, stream, start, stop);
+    case kTile256x256w4: return launch_pipe<TileL4>(g, layout, epi, stream, start, stop);
+    case kTile256x160w4: return launch_pipe<TileH4>(g, layout, epi, stream, start, stop);
     default: return launch_tile<TileL>(g, layout, epi, stream, start, stop);
   }
 }
@@ -1191,7 +1321,7 @@ size_t split_partials_bytes(int64_t M, int64_t N, int splits) {
 }
 
 hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float* partials, hipStream_t stream,
-                             hipEvent_t start, hipEvent_t stop) {
+                             hipEvent_t start, hipEvent_t stop, int tile) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const bool dual = epi == kEpiSwiglu;
   if (splits < 2 || splits > 64 || !partials || (dual && layout != kFwd)) return hipErrorInvalidValue;
@@ -1213,7 +1343,8 @@ hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float*
   if (dual && g.half != g.N) return hipErrorInvalidValue;  // offset (SwiGLU: half = F' = N)
   p.accumulate = 0;
   p.bias = nullptr; p.aux_in = nullptr; p.aux_out = nullptr;
-  hipError_t e = launch_partial(p, layout, dual, stream, start);
+  const bool pipe = tile == kTileAuto || tile == kTile256x256w4;
+  hipError_t e = launch_partial(p, layout, dual, pipe, stream, start);
   if (e != hipSuccess) return e;
   switch (epi) {
     case kEpiBf16: return launch_split_epilogue<kEpiBf16>(g, partials, splits, p.part_stride, ldp, stream, stop);

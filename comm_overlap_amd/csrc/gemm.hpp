@@ -52,8 +52,9 @@ struct GemmArgs {
 
 // Block tile of a launch. Every tile reduces k in the same order, so the choice never changes a
 // result bit. The 320-wide tiles take only products whose operands are both read along k, without
-// the SwiGLU pairing, and the four-wave tiles only forward products with K a multiple of 64; a
-// request a tile cannot serve falls back to kTileAuto.
+// the SwiGLU pairing, the four-wave tiles only products with K a multiple of 64 that do not
+// accumulate into an fp32 output (256 x 160: forward only); a request a tile cannot serve falls
+// back to kTileAuto.
 enum GemmTile : int {
   kTileAuto = 0,
   kTile256x256 = 1,
@@ -62,8 +63,8 @@ enum GemmTile : int {
   kTile128x320 = 4,
   kTile128x256 = 5,
   kTile128x128w8 = 6,  // 128 x 128 with 8 waves, one block per CU
-  kTile256x256w4 = 7,  // 256 x 256 with 4 waves and a software-pipelined loop: forward products
-                       // with K a multiple of 64 only
+  kTile256x256w4 = 7,  // 256 x 256 with 4 waves and a software-pipelined loop: products with K a
+                       // multiple of 64 and no accumulation into an fp32 output
   kTile256x160w4 = 8,  // 256 x 160, likewise, without the SwiGLU pairing
   kTileCount = 9
 };
@@ -72,7 +73,9 @@ enum GemmTile : int {
 // has the GPU to itself (no products of other slices run beside it), so tiles that fill the last
 // round of blocks are worth their lower per-CU rate. `fill` (optional) receives the share of the
 // block slots the chosen tile occupies over its rounds.
-int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, double* fill = nullptr);
+// `accumulate`: an fp32 output is added to (the four-wave tiles do not take these).
+int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, double* fill = nullptr,
+                bool accumulate = false);
 
 // Queue one GEMM on `stream`. With `start`/`stop` events the launch records the kernel's own start
 // and end times in them (timestamps of the dispatch itself, no extra marker packets).
@@ -102,10 +105,12 @@ double estimate_product_us(int64_t M, int64_t N, int64_t K, int layout, int epi,
 // Bytes of partial buffers of an M x N product (N: both halves for SwiGLU) split `splits` ways
 // (0 when splits == 1).
 size_t split_partials_bytes(int64_t M, int64_t N, int splits);
-// Queue a split product: the GEMM into `partials` (fp32, 256 x 256 tiles), then the reduction
-// with epilogue `epi` into g's outputs, on `stream`. `start`/`stop` bracket both when tracing.
+// Queue a split product: the GEMM into `partials` (fp32), then the reduction with epilogue `epi`
+// into g's outputs, on `stream`. `start`/`stop` bracket both when tracing. The partial products
+// run 256 x 256 tiles: the four-wave pipelined ones when K is a multiple of 64 and `tile` is
+// kTileAuto or kTile256x256w4, else the eight-wave ones (the same bits).
 hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float* partials, hipStream_t stream,
-                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr, int tile = kTileAuto);
 
 // A one-wave kernel that does nothing. Queued on a stream after DMA-engine copies it completes only
 // after them (stream order), so an event recorded after it marks the copies' completion.

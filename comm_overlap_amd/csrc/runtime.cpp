@@ -376,7 +376,8 @@ struct Schedule {
       e0 = rt->tpool[t.ev0];
       e1 = rt->tpool[t.ev1];
     }
-    hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1);
+    const int tile = int((p->desc.flags & TPSLICE_F_TILE_MASK) >> TPSLICE_F_TILE_SHIFT);
+    hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1, tile);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "split GEMM launch: %s", hipGetErrorString(e));
     if (i >= 0 && i == lead_slice) {
       TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));

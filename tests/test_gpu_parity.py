@@ -71,6 +71,50 @@ def test_four_wave_tiles(w):
         assert torch.equal(out["Zh"], out["Z"]), tile
 
 
+# Backward products for the four-wave tiles: every k (h, the FFN shard, the token count) a multiple
+# of 64, with odd k block counts and ragged rows and columns; operands stored across k (weights in
+# the activation gradients, both operands of the weight gradients) go through transposing reads.
+BWD64_GELU = synth.custom("bwd64_gelu", 910, tokens=1088, hidden=1216, ffn=1344, tp=1, act="gelu", bias=True,
+                          row_slices=2, col_slices=2, backward=True)
+BWD64_SWIGLU = synth.custom("bwd64_swiglu", 911, tokens=1024, hidden=1280, ffn=2752, tp=2, act="swiglu",
+                            bias=False, row_slices=2, col_slices=1, backward=True)
+BWD64_ATTN = synth.custom("bwd64_attn", 912, tokens=1088, hidden=1344, ffn=64, tp=2, act="gelu", bias=False,
+                          row_slices=2, col_slices=1, heads=6, kv_heads=2, head_dim=64, backward=True)
+
+
+@pytest.mark.parametrize("w", [BWD64_GELU, BWD64_SWIGLU], ids=lambda w: w.key)
+def test_four_wave_tiles_mlp_backward(w):
+    """MLP backward with the four-wave tiles (activation gradients, weight gradients and split
+    partial products) against the oracle, and bit for bit against the eight-wave 256 x 256 tile,
+    twice in a row."""
+    inp = synth.make_inputs(w)
+    ref = L.mlp_bwd(f64(inp["X_mlp"]), f64(inp["W1"]), f64(inp["W2"]), f64(inp["U_saved"]), f64(inp["dY"]),
+                    w.act, with_bias=w.bias)
+    base = G.run_mlp_bwd(T.plan_for(w, tile="256x256"), inp, with_bias=w.bias)
+    keys = ("dX", "dW1", "dW2") + (("db1",) if w.bias else ())
+    for tile in ("256x256w4", "auto", "256x256w4"):
+        _print_case("four_wave_bwd", key=w.key, tile=tile)
+        out = G.run_mlp_bwd(T.plan_for(w, tile=tile), inp, with_bias=w.bias)
+        for k in keys:
+            G.assert_parity(out[k], ref[k], k)
+            assert torch.equal(out[k], base[k]), (tile, k)
+        assert torch.equal(out["dXh"], out["dX"]), tile
+
+
+def test_four_wave_tiles_attn_backward():
+    w = BWD64_ATTN
+    inp = synth.make_inputs(w)
+    ref = L.attnproj_bwd(f64(inp["X"]), f64(inp["Wqkv"]), f64(inp["dQKV"]), f64(inp["C"]), f64(inp["Wo"]),
+                         f64(inp["dY_attn"]), with_bias=True)
+    base = G.run_attn_bwd(T.plan_for(w, tile="256x256"), inp, with_bias=True)
+    for tile in ("256x256w4", "auto"):
+        _print_case("four_wave_attn_bwd", key=w.key, tile=tile)
+        out = G.run_attn_bwd(T.plan_for(w, tile=tile), inp, with_bias=True)
+        for k in ("dX", "dC", "dWqkv", "dWo", "dbqkv"):
+            G.assert_parity(out[k], ref[k], k)
+            assert torch.equal(out[k], base[k]), (tile, k)
+
+
 AUTO = synth.custom("auto_slices", 909, tokens=2048, hidden=1024, ffn=4096, tp=1, act="gelu", bias=True,
                     row_slices=1, col_slices=1)
 
