@@ -43,9 +43,13 @@ def parse():
     ap.add_argument("--row-slices", type=int, default=0, help="row slices (0 = the workload's)")
     ap.add_argument("--col-slices", type=int, default=0, help="column slices (0 = the workload's)")
     ap.add_argument("--tile", default="auto",
-                    choices=["auto", "256x256", "128x128", "256x320", "128x320", "128x256", "128x128w8", "large", "small"],
+                    choices=["auto", "256x256", "128x128", "256x320", "128x320", "128x256", "128x128w8", "256x256w4",
+                             "256x160w4", "large", "small"],
                     help="block tile of every product (auto = chosen per product, the default)")
     ap.add_argument("--copy-blit", action="store_true", help="hand-off by copy kernel instead of DMA")
+    ap.add_argument("--handoff-pieces", action="store_true",
+                    help="column slices: a 2D copy per (row, column) piece (a copy kernel on the compute units) "
+                         "instead of the default one contiguous DMA copy per row slice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
     ap.add_argument("--strands", type=int, default=1, choices=[1, 2],
@@ -308,7 +312,8 @@ def main():
     log(f"workload {w.key}: generating inputs")
     inp = synth.make_inputs(w)
     flops = sum(w.gemm_flops().values())
-    kw = dict(n_streams=args.streams, n_copy_streams=args.copy_streams, copy_blit=args.copy_blit, tile=args.tile)
+    kw = dict(n_streams=args.streams, n_copy_streams=args.copy_streams, copy_blit=args.copy_blit, tile=args.tile,
+              handoff_rows=not args.handoff_pieces)
     if args.row_slices:
         kw["n_row_slices"] = args.row_slices
     if args.col_slices:
@@ -396,7 +401,9 @@ def main():
                    "heads_shard": [w.q_heads_shard, w.kv_heads_shard] if w.has_attn else None,
                    "worker_streams": info.n_streams, "copy_streams": info.n_copy_streams,
                    "tile": args.tile,
-                   "handoff": "blit" if args.copy_blit else "dma", "chain": "pipelined"},
+                   "handoff": "blit" if args.copy_blit else (
+                       "dma, whole row slices" if not args.handoff_pieces and info.n_col_slices > 1
+                                                              else "dma"), "chain": "pipelined"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "hidden_copy_pct": None if hidden is None else round(100.0 * hidden, 1),
         "hidden_copy_pct_single_call": None if hidden_single is None else round(100.0 * hidden_single, 1),

@@ -1161,15 +1161,18 @@ namespace {
 // Estimated time of an M x N product with tile t, in units of one 256 x 256 tile's work at that
 // tile's rate: whole rounds of resident blocks (256 CUs x blocks per CU), each round `blocks`
 // tiles' work per CU at the tile's rate. `fill` receives the share of the block slots the product
-// occupies over those rounds.
-double tile_cost(const TileChoice& t, int64_t M, int64_t N, int epi, double* fill) {
+// occupies over those rounds. When the products of two adjacent row slices share the GPU
+// (`alone` false), the slots one product leaves empty run the other's blocks: the cost is half the
+// rounds of two such products together.
+double tile_cost(const TileChoice& t, int64_t M, int64_t N, int epi, bool alone, double* fill) {
   const int64_t bn = epi == kEpiSwiglu ? t.bn / 2 : t.bn;
   const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + bn - 1) / bn);
   const int64_t slots = int64_t(kCUs) * t.blocks;
   const int64_t rounds = (tiles + slots - 1) / slots;
   if (fill) *fill = rounds ? double(tiles) / double(rounds * slots) : 1.0;
   const double work = double(t.bm) * double(t.bn) / (256.0 * 256.0);
-  return double(rounds) * t.blocks * work / t.rate;
+  const double r = alone ? double(rounds) : double((2 * tiles + slots - 1) / slots) / 2.0;
+  return r * t.blocks * work / t.rate;
 }
 
 }  // namespace
@@ -1177,14 +1180,15 @@ double tile_cost(const TileChoice& t, int64_t M, int64_t N, int epi, double* fil
 int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, double* fill, bool accumulate) {
   // A product that runs alone gets the tile with the smallest estimated time, including the
   // tiles that exist to fill the last round. When products of adjacent slices share the GPU, the
-  // CUs one leaves idle run the other's blocks, so only per-CU throughput counts: the 256 x 256
-  // tile, or 128 x 128 when 256 x 256 tiles would leave most CUs idle.
+  // CUs one leaves idle run the other's blocks, and two products that leave half the CUs idle
+  // each fill them together. (A plan whose row slices' first product takes the four-wave 256 x 256
+  // tile requests that tile for all its products; see plan.cpp.)
   int best = kTile256x256;
   double best_cost = 1e300, best_fill = 1.0;
   for (const TileChoice& t : kTiles) {
     if (!tile_supports(t, K, layout, epi, accumulate) || (t.fit_only && !alone)) continue;
     double f = 1.0;
-    const double cost = tile_cost(t, M, N, epi, &f);
+    const double cost = tile_cost(t, M, N, epi, alone, &f);
     if (cost < best_cost - 1e-9) { best_cost = cost; best = t.id; best_fill = f; }
   }
   if (fill) *fill = best_fill;
@@ -1290,9 +1294,11 @@ double estimate_product_us(int64_t M, int64_t N, int64_t K, int layout, int epi,
     const double red_us = double(2 * splits + 2) * double(M) * double(Nt) * 4.0 / 5e12 * 1e6;
     return double((T * splits + kCUs - 1) / kCUs) * double(kbs) * kBlockUs + red_us + 2 * kLaunchUs;
   }
-  const int id = choose_tile(M, N, K, layout, epi, alone);
+  // not alone: M rows of two products side by side, each taking the tile the launcher picks for
+  // M / 2 rows; the cost is their rounds together
+  const int id = choose_tile(alone ? M : (M + 1) / 2, N, K, layout, epi, alone);
   for (const TileChoice& t : kTiles)
-    if (t.id == id) return tile_cost(t, M, N, epi, nullptr) * double(nk) * kBlockUs + kLaunchUs;
+    if (t.id == id) return tile_cost(t, M, N, epi, true, nullptr) * double(nk) * kBlockUs + kLaunchUs;
   return 0.0;
 }
 

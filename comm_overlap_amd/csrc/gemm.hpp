@@ -97,7 +97,7 @@ int choose_split(int64_t M, int64_t N, int64_t K);
 constexpr int64_t kSplitRefRows = 2048;
 inline int choose_slice_split(int64_t N, int64_t K) { return choose_split(kSplitRefRows, N, K); }
 // Estimated time (us) of one M x N x K product on this GPU (N: output columns; SwiGLU: of each
-// half), with the tile choose_tile picks and
+// half; not `alone`: two products of M / 2 rows side by side), with the tile choose_tile picks and
 // `splits` k splits (1: none), from the same per-tile cost model: rounds of 256 CUs times the k
 // blocks per run at about 1.9 us per 64-wide k block of a 256 x 256 tile, plus the split
 // reduction's HBM passes and a fixed launch cost. Used to compare slicings, not as a timing.

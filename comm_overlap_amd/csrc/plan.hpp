@@ -17,6 +17,7 @@ struct tpslice_plan_s {
   // k splits (1: none) of the products over all tokens (dW1, dW2, dC, dWo, dWqkv) and of the row
   // slices' first products (up-projection, QKV projection, dH)
   int32_t sp_dw1, sp_dw2, sp_dc, sp_dwo, sp_dwqkv, sp_up, sp_qkv, sp_dh;
+  int32_t tile;                    // tile requested for every product (GemmTile; 0: per product)
   void* rt;                        // device resources (streams, events), created on first execution
 };
 

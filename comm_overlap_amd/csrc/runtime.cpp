@@ -291,17 +291,25 @@ struct Schedule {
     char* d = static_cast<char*>(dst) + row0 * pitch + col0 * 2;
     const hipMemcpyKind kind =
         (p->desc.flags & TPSLICE_F_COPY_BLIT) ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
-    const double piece_bytes = double(p->Ms) * double(p->hc) * 2.0;
+    // whole row slices: one contiguous copy after the slice's last column piece
+    const bool rows = p->c > 1 && (p->desc.flags & TPSLICE_F_HANDOFF_ROWS);
+    if (rows) {
+      if (j < p->c - 1) return TPSLICE_OK;
+      s = static_cast<const char*>(src) + row0 * pitch;
+      d = static_cast<char*>(dst) + row0 * pitch;
+    }
+    const bool contiguous = p->c == 1 || rows;
+    const double piece_bytes = double(p->Ms) * double(contiguous ? p->h : p->hc) * 2.0;
     if (serial) {
       return traced(caller, -1, TPSLICE_TRACE_COPY, TPSLICE_STEP_HANDOFF, i, j, 0.0, piece_bytes, [&] {
-        if (p->c == 1) TPS_HIP(hipMemcpyAsync(d, s, size_t(p->Ms) * pitch, kind, caller));
+        if (contiguous) TPS_HIP(hipMemcpyAsync(d, s, size_t(p->Ms) * pitch, kind, caller));
         else TPS_HIP(hipMemcpy2DAsync(d, pitch, s, pitch, size_t(p->hc) * 2, size_t(p->Ms), kind, caller));
         return TPSLICE_OK;
       });
     }
     hipEvent_t ev = rt->piece[size_t(i) * p->c + j];
     TPS_HIP(hipEventRecord(ev, worker(i)));
-    if (p->c == 1) {
+    if (contiguous) {
       // a whole-row piece is contiguous: spread it over the copy streams in equal row chunks
       const int64_t E = p->E;
       for (int64_t k = 0; k < E; ++k) {
@@ -343,8 +351,7 @@ struct Schedule {
       e0 = rt->tpool[t.ev0];
       e1 = rt->tpool[t.ev1];
     }
-    const int tile = int((p->desc.flags & TPSLICE_F_TILE_MASK) >> TPSLICE_F_TILE_SHIFT);
-    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1, tile, serial || p->S == 1);
+    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1, p->tile, serial || p->S == 1);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
     if (i >= 0 && i == lead_slice) {
       TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
@@ -376,8 +383,7 @@ struct Schedule {
       e0 = rt->tpool[t.ev0];
       e1 = rt->tpool[t.ev1];
     }
-    const int tile = int((p->desc.flags & TPSLICE_F_TILE_MASK) >> TPSLICE_F_TILE_SHIFT);
-    hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1, tile);
+    hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1, p->tile);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "split GEMM launch: %s", hipGetErrorString(e));
     if (i >= 0 && i == lead_slice) {
       TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libtpslice.so")
 
 OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 ACT_GELU, ACT_SWIGLU = 1, 2
-F_SERIALIZE, F_COPY_BLIT, F_PIPELINE, F_CALLER_WORKER = 0x1, 0x2, 0x4, 0x40
+F_SERIALIZE, F_COPY_BLIT, F_PIPELINE, F_HANDOFF_ROWS, F_CALLER_WORKER = 0x1, 0x2, 0x4, 0x8, 0x40
 F_TILE_SHIFT = 8
 # block tile ids (flags bits 8..11); "large" / "small" name the 256 x 256 / 128 x 128 tiles
 TILES = {"auto": 0, "256x256": 1, "128x128": 2, "256x320": 3, "128x320": 4, "128x256": 5,
@@ -148,6 +148,7 @@ class Config:
     copy_blit: bool = False
     pipeline: bool = False
     caller_worker: bool = False  # worker stream 0 is the caller's stream
+    handoff_rows: bool = False  # c > 1: one contiguous copy per row slice instead of per piece
     tile: str = "auto"  # a key of TILES
     handoff_gbps: float = 0.0  # hand-off rate the automatic slice counts assume (0: local DMA copy)
 
@@ -158,6 +159,7 @@ class Config:
                     self.n_copy_streams,
                     (F_SERIALIZE if self.serialize else 0) | (F_COPY_BLIT if self.copy_blit else 0)
                     | (F_PIPELINE if self.pipeline else 0) | (F_CALLER_WORKER if self.caller_worker else 0)
+                    | (F_HANDOFF_ROWS if self.handoff_rows else 0)
                     | (TILES[self.tile] << F_TILE_SHIFT), float(self.handoff_gbps))
 
 

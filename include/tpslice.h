@@ -75,6 +75,13 @@ typedef enum {
                                     Abstract: independent pieces pipelined across the batch's work).
                                     Use tpslice_handoff_wait() before reading a hand-off buffer on
                                     another stream, or before freeing buffers the copies touch.    */
+#define TPSLICE_F_HANDOFF_ROWS 0x8u /* with column slices (c > 1): hand off each row slice as one
+                                    contiguous copy on the DMA engines once its last column piece is
+                                    done, instead of each (row, column) piece on its own. A piece
+                                    is a strided 2D region, which the HIP runtime copies with a kernel
+                                    on the compute units (taking them from the products); a whole
+                                    row slice is contiguous. The same bytes arrive; they leave a
+                                    row slice's last piece later.                                  */
 #define TPSLICE_F_CALLER_WORKER 0x40u /* worker stream 0 is the caller's stream (no stream of its own):
                                     one fork and join fewer per call, and one hardware queue fewer
                                     (a process has four by default), so that two plans with their
@@ -86,8 +93,9 @@ typedef enum {
    changes a result bit. Ids: 1 = 256 x 256, 2 = 128 x 128 (4 waves, two blocks per CU),
    3 = 256 x 320, 4 = 128 x 320, 5 = 128 x 256, 6 = 128 x 128 (8 waves, one block per CU),
    7 = 256 x 256 and 8 = 256 x 160 (4 waves, software-pipelined). The 320-wide tiles and id 8
-   serve only forward products without the SwiGLU pairing, ids 7 and 8 only forward products whose
-   k is a multiple of 64; other products then take the automatic choice.                       */
+   serve only forward products without the SwiGLU pairing, ids 7 and 8 only products whose k is a
+   multiple of 64 and that do not add to an fp32 output (accumulate = 1); other products then take
+   the automatic choice.                                                                        */
 #define TPSLICE_F_TILE_SHIFT 8
 #define TPSLICE_F_TILE_MASK (0xFu << TPSLICE_F_TILE_SHIFT)
 #define TPSLICE_F_TILE(id) (((uint32_t)(id) << TPSLICE_F_TILE_SHIFT) & TPSLICE_F_TILE_MASK)
