@@ -7,6 +7,13 @@
                                                --calib-kernel NAME --calib-bytes N
         HBM bytes per dispatch of NAME from a FETCH_SIZE pass and a WRITE_SIZE pass, each scaled
         by what the same counter reads for a calibration copy kernel that moves N bytes each way
+    python -m comm_overlap_amd.profile_summary counters RESULTS.db [--match gemm_kernel]
+        per kernel (medians over its dispatches) from a pass with GRBM_GUI_ACTIVE,
+        SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_WAVE_CYCLES, SQ_WAIT_ANY:
+        GRBM_GUI_ACTIVE reads the sum over the 8 XCDs, so one XCD's busy cycles are a eighth of it:
+        clock = busy cycles / duration, MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (busy cycles x 1024
+        SIMDs), wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES, LDS conflicts = SQ_LDS_BANK_CONFLICT /
+        SQ_LDS_IDX_ACTIVE
 """
 from __future__ import annotations
 
@@ -118,6 +125,43 @@ def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes):
     return 0
 
 
+def counters(db, match, simds=1024, xcds=8):
+    c = sqlite3.connect(db)
+    vals = collections.defaultdict(dict)
+    names = {}
+    for name, disp, cname, val in c.execute(
+            "select name, dispatch_id, counter_name, counter_value from pmc_events"):
+        vals[disp][cname] = vals[disp].get(cname, 0.0) + val
+        names[disp] = name
+    dur = {}
+    try:
+        for disp, s, e in c.execute("select dispatch_id, start, end from kernels"):
+            dur[disp] = (e - s) * 1e-9
+    except sqlite3.OperationalError:
+        pass
+    per = collections.defaultdict(list)
+    for disp, v in vals.items():
+        if match in names[disp]:
+            per[names[disp]].append((disp, v))
+
+    def med(xs):
+        xs = sorted(x for x in xs if x is not None)
+        return xs[len(xs) // 2] if xs else float("nan")
+
+    for name, rows in sorted(per.items(), key=lambda kv: -len(kv[1])):
+        d = [dur.get(k) for k, _ in rows]
+        g = [v.get("GRBM_GUI_ACTIVE", 0.0) / xcds for _, v in rows]
+        clk = med([gg / dd / 1e9 if gg and dd else None for gg, dd in zip(g, d)])
+        busy = med([v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gg * simds) if gg else None
+                    for gg, (_, v) in zip(g, rows)])
+        wait = med([v.get("SQ_WAIT_ANY", 0.0) / v["SQ_WAVE_CYCLES"] if v.get("SQ_WAVE_CYCLES") else None
+                    for _, v in rows])
+        lds = med([v.get("SQ_LDS_BANK_CONFLICT", 0.0) / v["SQ_LDS_IDX_ACTIVE"] if v.get("SQ_LDS_IDX_ACTIVE") else None
+                   for _, v in rows])
+        print(f"  {name[:70]}: {len(rows)} dispatches, {med(d) * 1e6:.1f} us, clk {clk:.2f} GHz, "
+              f"mfma_busy {100 * busy:.1f}%, WAIT_ANY {100 * wait:.1f}%, ldsconf {100 * lds:.1f}%")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -130,9 +174,15 @@ def main(argv=None):
     r.add_argument("--kernel", required=True)
     r.add_argument("--calib-kernel", required=True)
     r.add_argument("--calib-bytes", type=float, required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("db")
+    k.add_argument("--match", default="gemm_kernel")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         trace(a.db, a.match)
+        return 0
+    if a.cmd == "counters":
+        counters(a.db, a.match)
         return 0
     return traffic(a.fetch_db, a.write_db, a.kernel, a.calib_kernel, a.calib_bytes)
 

@@ -218,3 +218,15 @@ def test_caller_worker_flag():
     import ctypes
     h = ctypes.c_void_p()
     assert T.lib.tpslice_plan(ctypes.byref(d), ctypes.byref(h)) == T.ERR_INVALID
+
+
+def test_handoff_rows_flag():
+    """Whole-row hand-off is accepted with and without column slices and pipelining; the plan's
+    slicing is unchanged by it."""
+    for c in (1, 2):
+        for pipeline in (False, True):
+            p = T.Plan(T.Config(tokens=64, hidden=64, ffn=64, n_row_slices=2, n_col_slices=c, pipeline=pipeline,
+                                handoff_rows=True))
+            assert (p.info.n_row_slices, p.info.n_col_slices) == (2, c)
+            p.close()
+    assert T.F_HANDOFF_ROWS == 0x8

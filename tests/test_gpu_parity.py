@@ -496,13 +496,58 @@ def test_handoff_complete_when_caller_stream_passes(copy_blit):
         assert torch.equal(snap, Z), f"rep {rep}: hand-off not complete at the join"
 
 
-@pytest.mark.parametrize("streams", [1, 2])
-def test_pipelined_chain_matches_joined(streams):
+ATTN_C2 = synth.custom("attn_c2", 913, tokens=520, hidden=272, ffn=64, tp=2, act="gelu", bias=False,
+                       row_slices=2, col_slices=2, heads=6, kv_heads=2, head_dim=40, backward=True)
+
+
+@pytest.mark.parametrize("w", [SMALL_GELU, SMALL_SWIGLU, ATTN_C2], ids=lambda w: w.key)
+def test_handoff_whole_row_slices(w):
+    """Whole-row hand-off (one contiguous copy per row slice after its last column piece) moves
+    the same bytes: every output and hand-off buffer equals the per-piece run bit for bit, and
+    work queued on the caller's stream right after the call sees the finished copies."""
+    _print_case("handoff_rows", key=w.key)
+    inp = synth.make_inputs(w)
+    rows = T.plan_for(w, handoff_rows=True)
+    pieces = T.plan_for(w)
+    assert rows.info.n_col_slices > 1
+    a, b = G.run_mlp_fwd(rows, inp, sync=False), None
+    snap = a["Zh"].clone()
+    torch.cuda.synchronize()
+    b = G.run_mlp_fwd(pieces, inp)
+    for k in ("Z", "U", "Zh"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(snap, a["Z"])
+    if w.backward:
+        a = G.run_mlp_bwd(rows, inp, with_bias=w.bias)
+        b = G.run_mlp_bwd(pieces, inp, with_bias=w.bias)
+        for k in ("dX", "dXh", "dW1", "dW2", "db1"):
+            if a[k] is not None:
+                assert torch.equal(a[k], b[k]), k
+        assert torch.equal(a["dXh"], a["dX"])
+    if w.has_attn:
+        a = G.run_attn_fwd(rows, inp)
+        b = G.run_attn_fwd(pieces, inp)
+        for k in ("QKV", "Z", "Zh"):
+            assert torch.equal(a[k], b[k]), k
+        a = G.run_attn_bwd(rows, inp, with_bias=True)
+        b = G.run_attn_bwd(pieces, inp, with_bias=True)
+        for k in ("dX", "dXh", "dC", "dWqkv", "dWo", "dbqkv"):
+            assert torch.equal(a[k], b[k]), k
+    src = torch.randn(w.tokens, w.hidden, device="cuda").to(torch.bfloat16)
+    dst = torch.zeros_like(src)
+    rows.handoff_copy(src, dst)
+    snap = dst.clone()
+    torch.cuda.synchronize()
+    assert torch.equal(snap, src)
+
+
+@pytest.mark.parametrize("streams,rows", [(1, False), (2, False), (2, True)])
+def test_pipelined_chain_matches_joined(streams, rows):
     """Four chained MLP calls, each reading the previous call's hand-off buffer as its input: the
     pipelined mode (per-slice waits instead of a full join) gives bitwise the same results."""
     w = synth.custom("chain", 906, tokens=1024, hidden=512, ffn=2048, tp=2, act="gelu", bias=True,
                      row_slices=4, col_slices=2)
-    _print_case("pipeline", key=w.key, streams=streams)
+    _print_case("pipeline", key=w.key, streams=streams, rows=rows)
     inp = synth.make_inputs(w)
     X0, W1, b1, W2 = (G.dev(inp[k]) for k in ("X_mlp", "W1", "b1", "W2"))
 
@@ -521,7 +566,7 @@ def test_pipelined_chain_matches_joined(streams):
         return Hs
 
     ref = chain(T.plan_for(w), False)
-    got = chain(T.plan_for(w, pipeline=True, n_streams=streams), True)
+    got = chain(T.plan_for(w, pipeline=True, n_streams=streams, handoff_rows=rows), True)
     for n in range(4):
         assert torch.equal(got[n], ref[n]), f"layer {n}"
     r1 = G.oracle_mlp_fwd(inp, w.act)
