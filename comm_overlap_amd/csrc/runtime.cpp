@@ -89,8 +89,14 @@ void destroy_runtime(Runtime* rt) {
   delete rt;
 }
 
-tpslice_status_t make_event(hipEvent_t* e) {
-  TPS_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
+// Events that order products on worker streams against each other and against the caller's stream
+// (`local`) skip the system-scope fence of their release and acquire: the products and their
+// consumers are kernels on this GPU, ordered at device scope. Events in front of a DMA-engine copy
+// and after one keep the system-scope fence. Measured on the same GPU in alternation: Llama-2 13B
+// layer 732 -> 750 TFLOP/s, Llama-2 7B MLP 931 -> 954; with every event local, the 7B MLP varied
+// 914-959 and hid less of its copy time.
+tpslice_status_t make_event(hipEvent_t* e, bool local = false) {
+  TPS_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming | (local ? hipEventDisableSystemFence : 0u)));
   return TPSLICE_OK;
 }
 
@@ -122,21 +128,21 @@ tpslice_status_t ensure_runtime(tpslice_plan_s* p, Runtime** out) {
       TPS_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
       rt->copiers.push_back(s);
     }
-    tpslice_status_t st = make_event(&rt->fork);
+    tpslice_status_t st = make_event(&rt->fork, true);
     if (st) return st;
-    if ((st = make_event(&rt->call_done))) return st;
+    if ((st = make_event(&rt->call_done, true))) return st;
     rt->join_w.resize(p->S);
     rt->join_c.resize(p->E);
-    for (auto& e : rt->join_w) if ((st = make_event(&e))) return st;
+    for (auto& e : rt->join_w) if ((st = make_event(&e, true))) return st;
     for (auto& e : rt->join_c) if ((st = make_event(&e))) return st;
     rt->piece.resize(size_t(p->r) * p->c);
     rt->slice.resize(p->r);
     rt->lead.resize(p->r);
     rt->gather.resize(p->S);
     for (auto& e : rt->piece) if ((st = make_event(&e))) return st;
-    for (auto& e : rt->slice) if ((st = make_event(&e))) return st;
-    for (auto& e : rt->lead) if ((st = make_event(&e))) return st;
-    for (auto& e : rt->gather) if ((st = make_event(&e))) return st;
+    for (auto& e : rt->slice) if ((st = make_event(&e, true))) return st;
+    for (auto& e : rt->lead) if ((st = make_event(&e, true))) return st;
+    for (auto& e : rt->gather) if ((st = make_event(&e, true))) return st;
     rt->copied.resize(size_t(p->r) * p->E);
     for (auto& e : rt->copied) if ((st = make_event(&e))) return st;
     rt->copied_pending.assign(size_t(p->r) * p->E, 0);
