@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--col-slices", type=int, default=0, help="column slices (0 = the workload's)")
     ap.add_argument("--tile", default="auto",
                     choices=["auto", "256x256", "128x128", "256x320", "128x320", "128x256", "128x128w8", "256x256w4",
-                             "256x160w4", "large", "small"],
+                             "256x160w4", "256x320w4", "large", "small"],
                     help="block tile of every product (auto = chosen per product, the default)")
     ap.add_argument("--copy-blit", action="store_true", help="hand-off by copy kernel instead of DMA")
     ap.add_argument("--handoff-pieces", action="store_true",

@@ -82,6 +82,9 @@ using TileT = Tile<128, 128, 2, 4, 1>;
 // loop (gemm_kernel); for forward products whose K is a multiple of 64.
 using TileL4 = Tile<256, 256, 2, 2, 1>;
 using TileH4 = Tile<256, 160, 2, 2, 1>;
+// 256 x 320 with four waves of 128 x 160: 320 accumulator registers per lane, more than the 256
+// AGPRs, so the last accumulator columns live in VGPRs (the MFMA takes either)
+using TileW4 = Tile<256, 320, 2, 2, 1>;
 
 namespace {
 
@@ -784,10 +787,17 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
         dma16<(j - kARuns) * 1024>(bl.rb, lds_wave_b + stage * TL::kStageBytes + TL::kATileBytes,
                                    b_voff[j - kARuns], bl.sb);
     };
+    // accumulator columns [0, kAccA) in AGPRs, the rest (wide tiles) in VGPRs
+    constexpr int kAccA = kFM * kFN * 4 <= 256 ? kFN : 256 / (4 * kFM);
     auto mf = [&](int kk, int idx) {
       const int im = idx / kFN, in = idx % kFN;
-      if (kk) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[im][in]) : "v"(b1[in]), "v"(a1[im]));
-      else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[im][in]) : "v"(b0[in]), "v"(a0[im]));
+      if (in < kAccA) {
+        if (kk) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[im][in]) : "v"(b1[in]), "v"(a1[im]));
+        else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[im][in]) : "v"(b0[in]), "v"(a0[im]));
+      } else {
+        if (kk) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[im][in]) : "v"(b1[in]), "v"(a1[im]));
+        else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[im][in]) : "v"(b0[in]), "v"(a0[im]));
+      }
     };
     auto block = [&](int kb, int stage) {
 #pragma unroll
@@ -831,7 +841,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
 #pragma unroll
     for (int im = 0; im < kFM; ++im)
 #pragma unroll
-      for (int in = 0; in < kFN; ++in) asm volatile("" : "+a"(acc[im][in]));
+      for (int in = 0; in < kFN; ++in) {
+        if (in < kAccA) asm volatile("" : "+a"(acc[im][in]));
+        else asm volatile("" : "+v"(acc[im][in]));
+      }
   } else {
     // Main loop. Block kb+1 is loaded while block kb is multiplied, its load runs placed between the
     // MFMA row groups of the first 32-wide step (pinned by scheduling barriers) so that load issue
@@ -1000,6 +1013,8 @@ template __global__ void gemm_kernel<TileL4, kDgrad, kEpiF32>(GemmArgs);
 template __global__ void gemm_kernel<TileL4, kWgrad, kEpiF32>(GemmArgs);
 template __global__ void gemm_kernel<TileL4, kFwd, kEpiF32>(GemmArgs);
 template __global__ void gemm_kernel<TileL4, kFwd, kEpiPartialDual>(GemmArgs);
+template __global__ void gemm_kernel<TileW4, kFwd, kEpiBf16>(GemmArgs);
+template __global__ void gemm_kernel<TileW4, kFwd, kEpiGelu>(GemmArgs);
 template __global__ void gemm_kernel<TileH4, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileH4, kFwd, kEpiGelu>(GemmArgs);
 
@@ -1140,6 +1155,7 @@ constexpr TileChoice kTiles[] = {
     {kTile128x128w8, 128, 128, 1, true, false, true, false, 0.50},
     {kTile256x256w4, 256, 256, 1, false, false, true, true, 1.10},
     {kTile256x160w4, 256, 160, 1, true, true, false, true, 0.83},
+    {kTile256x320w4, 256, 320, 1, true, true, false, true, 1.00},
 };
 
 bool tile_supports(const TileChoice& t, int64_t K, int layout, int epi, bool accumulate) {
@@ -1221,6 +1237,7 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipE
     case kTile128x128w8: return launch_tile<TileT>(g, layout, epi, stream, start, stop);
     case kTile256x256w4: return launch_pipe<TileL4>(g, layout, epi, stream, start, stop);
     case kTile256x160w4: return launch_pipe<TileH4>(g, layout, epi, stream, start, stop);
+    case kTile256x320w4: return launch_pipe<TileW4>(g, layout, epi, stream, start, stop);
     default: return launch_tile<TileL>(g, layout, epi, stream, start, stop);
   }
 }

@@ -61,7 +61,7 @@ def test_four_wave_tiles(w):
     inp = synth.make_inputs(w)
     ref = G.oracle_mlp_fwd(inp, w.act)
     base = G.run_mlp_fwd(T.plan_for(w, tile="256x256"), inp)
-    for tile in ("256x256w4", "256x160w4", "auto", "256x256w4"):
+    for tile in ("256x256w4", "256x160w4", "256x320w4", "auto", "256x256w4", "256x320w4"):
         _print_case("four_wave", key=w.key, tile=tile)
         out = G.run_mlp_fwd(T.plan_for(w, tile=tile), inp)
         G.assert_parity(out["Z"], ref["Z"], "Z")
