@@ -185,7 +185,9 @@ struct Schedule {
   // call's hand-off of row slice i.
   tpslice_status_t slice_begin(int i) {
     if (serial) return TPSLICE_OK;
-    lead_slice = i;
+    // the next slice waits for this one's first product only from another worker stream (one
+    // worker: stream order already does it, and an event between two products costs their gap)
+    lead_slice = i + 1 < p->r && worker(i + 1) != worker(i) ? i : -1;
     if (i > 0 && lead_done == i - 1 && worker(i) != worker(i - 1))
       TPS_HIP(hipStreamWaitEvent(worker(i), rt->lead[i - 1], 0));
     if (!pipelined()) return TPSLICE_OK;
