@@ -259,9 +259,16 @@ struct Schedule {
     if (serial) return TPSLICE_OK;
     if (rt->first_own_worker && rt->have_last && rt->last_caller != caller)
       TPS_HIP(hipStreamWaitEvent(caller, rt->call_done, 0));
+    // With worker 0 on the caller's stream every copy waits for a piece event recorded on a worker
+    // stream that is itself ordered after the caller's earlier work (worker 0 is the caller, the
+    // others wait for the fork), so the copy streams need no fork of their own; with no other
+    // worker stream there is nothing to fork.
+    const bool copier_fork = !rt->first_own_worker;
+    if (rt->workers.empty() && !copier_fork) return TPSLICE_OK;
     TPS_HIP(hipEventRecord(rt->fork, caller));
     for (auto s : rt->workers) TPS_HIP(hipStreamWaitEvent(s, rt->fork, 0));
-    for (auto s : rt->copiers) TPS_HIP(hipStreamWaitEvent(s, rt->fork, 0));
+    if (copier_fork)
+      for (auto s : rt->copiers) TPS_HIP(hipStreamWaitEvent(s, rt->fork, 0));
     return TPSLICE_OK;
   }
 

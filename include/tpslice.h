@@ -87,7 +87,9 @@ typedef enum {
                                     (a process has four by default), so that two plans with their
                                     own copy streams can run side by side, e.g. the forward of one
                                     micro-batch beside the backward of another. A call from a
-                                    different stream than the previous call waits for it first.    */
+                                    different stream than the previous call waits for it first.
+                                    A plan with one worker stream (not serialized) always works
+                                    this way.                                                      */
 /* Block tile of every product (ablation, testing): flags |= TPSLICE_F_TILE(id). By default (id 0)
    each product takes the tile with the smallest estimated time on the 256 CUs. The tile never
    changes a result bit. Ids: 1 = 256 x 256, 2 = 128 x 128 (4 waves, two blocks per CU),
