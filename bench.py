@@ -47,6 +47,8 @@ def parse():
                              "256x160w4", "256x320w4", "large", "small"],
                     help="block tile of every product (auto = chosen per product, the default)")
     ap.add_argument("--copy-blit", action="store_true", help="hand-off by copy kernel instead of DMA")
+    ap.add_argument("--caller-worker", action="store_true",
+                    help="worker stream 0 is the caller's stream (plans with one worker stream always do this)")
     ap.add_argument("--handoff-pieces", action="store_true",
                     help="column slices: a 2D copy per (row, column) piece (a copy kernel on the compute units) "
                          "instead of the default one contiguous DMA copy per row slice")
@@ -313,7 +315,7 @@ def main():
     inp = synth.make_inputs(w)
     flops = sum(w.gemm_flops().values())
     kw = dict(n_streams=args.streams, n_copy_streams=args.copy_streams, copy_blit=args.copy_blit, tile=args.tile,
-              handoff_rows=not args.handoff_pieces)
+              handoff_rows=not args.handoff_pieces, caller_worker=args.caller_worker)
     if args.row_slices:
         kw["n_row_slices"] = args.row_slices
     if args.col_slices:
