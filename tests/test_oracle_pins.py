@@ -1,5 +1,6 @@
 """Pins of the fp64 oracle (CPU only), and planted mistakes that the pins must catch."""
 import copy
+import math
 import types
 
 import numpy as np
@@ -214,3 +215,67 @@ def test_planted_row_parallel_bias_added_to_every_partial():
         return o
     bad = _mutant(mlp_fwd=mlp_fwd)
     assert _fails(lambda: pins.check_tp_sum(bad, "gelu"))
+
+
+# ---------------------------------------------------------------- attention core (causal, GQA)
+from oracle import attention as A  # noqa: E402
+
+
+def _brute_attn(QKV, qh, kvh, d, S):
+    """Triple loop with math.exp: the definition on tiny shapes."""
+    M = len(QKV)
+    out = [[0.0] * (qh * d) for _ in range(M)]
+    for b in range(M // S):
+        for h in range(qh):
+            g = h // (qh // kvh)
+            for t in range(S):
+                T = b * S + t
+                sc = []
+                for s_ in range(t + 1):
+                    Ss = b * S + s_
+                    sc.append(sum(QKV[T][h * d + i] * QKV[Ss][(qh + g) * d + i] for i in range(d)) / math.sqrt(d))
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                z = sum(w)
+                for i in range(d):
+                    out[T][h * d + i] = sum(w[j] * QKV[b * S + j][(qh + kvh + g) * d + i] for j in range(t + 1)) / z
+    return np.array(out)
+
+
+def test_attention_brute_force():
+    rng = np.random.default_rng(3)
+    for qh, kvh, d, S, nb in [(2, 1, 3, 5, 2), (4, 2, 4, 4, 1), (3, 3, 2, 6, 1)]:
+        QKV = rng.standard_normal((S * nb, (qh + 2 * kvh) * d))
+        got = A.attn_core_fwd(QKV, qh, kvh, d, S)
+        ref = _brute_attn(QKV.tolist(), qh, kvh, d, S)
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(4)
+    qh, kvh, d, S = 4, 2, 8, 16
+    QKV = rng.standard_normal((2 * S, (qh + 2 * kvh) * d))
+    q, k, v = A.split_qkv(QKV, qh, kvh, d)
+    C = A.attn_core_fwd(QKV, qh, kvh, d, S).reshape(2 * S, qh, d)
+    # the first token of each sequence sees only itself: C = its own V, exactly
+    for b in range(2):
+        for h in range(qh):
+            assert np.array_equal(C[b * S, h], v[b * S, h // 2])
+    # zero keys: uniform weights, C[t] = mean of V[0..t] of the sequence
+    Z = QKV.copy()
+    Z[:, qh * d:(qh + kvh) * d] = 0.0
+    Cz = A.attn_core_fwd(Z, qh, kvh, d, S).reshape(2 * S, qh, d)
+    for t in range(S):
+        np.testing.assert_allclose(Cz[S + t, 1], v[S:S + t + 1, 0].mean(axis=0), rtol=0, atol=1e-13)
+    # a constant vector added to every key of a head shifts a row's scores by one amount: no change
+    Sh = QKV.copy()
+    Sh[:, qh * d:(qh + 1) * d] += rng.standard_normal(d)
+    np.testing.assert_allclose(A.attn_core_fwd(Sh, qh, kvh, d, S), A.attn_core_fwd(QKV, qh, kvh, d, S),
+                               rtol=0, atol=1e-12)
+    # query heads of one group with the same queries give the same outputs (grouped KV heads)
+    G = QKV.copy()
+    G[:, d:2 * d] = G[:, 0:d]
+    Cg = A.attn_core_fwd(G, qh, kvh, d, S).reshape(2 * S, qh, d)
+    assert np.array_equal(Cg[:, 0], Cg[:, 1])
+    # sequences are independent: each sequence alone gives the same rows
+    np.testing.assert_array_equal(A.attn_core_fwd(QKV[S:], qh, kvh, d, S), A.attn_core_fwd(QKV, qh, kvh, d, S)[S:])
