@@ -1,0 +1,193 @@
+// Causal attention core between the QKV and the output projections, forward, for gfx950.
+//
+// One block computes 64 query rows of one query head of one sequence (four waves of 16 rows) and
+// walks the key blocks of 64 up to the diagonal, keeping the softmax online (running row maximum
+// and row sum, the output rescaled when the maximum grows): the tiled form of softmax attention
+// that the FlashAttention titles in the Domino page's builds-on list describe. Per key block:
+//   S = Q K^T   v_mfma_f32_16x16x32_bf16, Q fragments held in registers for the whole walk, K from
+//               LDS by ds_read_b128 (rows XOR-swizzled by 16-byte chunk);
+//   P = exp2(S log2(e) / sqrt(d) - m), rounded to bf16; the mask zeroes keys past the query on the
+//               diagonal block;
+//   O += P V    the same MFMA, P taken straight from S's accumulator layout (no LDS round trip)
+//               and V read across keys with ds_read_b64_tr_b16.
+// S's accumulator gives lane l the keys 16 j + 4 (l / 16) + 0..3 of tile j for row l % 16. The PV
+// product takes a 32-key step from tiles 2c and 2c + 1 and lets lane l's eight k slots stand for
+// keys 32c + 4 (l / 16) + 0..3 and 32c + 16 + 4 (l / 16) + 0..3; the V fragment is read for the same
+// keys in the same slots, so the product is the plain sum over the step's keys.
+// K and V tiles (64 keys x 128 dims bf16, 16 KB each) come in through registers (16-byte global
+// loads, then ds_write_b128); four or more blocks share a CU, so one block's loads hide under the
+// others' MFMAs. Heavier query blocks (more key blocks under the diagonal) start first.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "attn.hpp"
+
+namespace tps {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kD = kAttnHeadDim;  // 128
+constexpr int kBQ = 64;           // query rows per block
+constexpr int kBK = 64;           // keys per block
+constexpr int kRowB = kD * 2;     // bytes of one K or V row in LDS
+constexpr int kThreads = 256;
+
+// 16-byte chunk swizzles: K rows are read 16 rows at one chunk per quarter wave (chunk ^ row%16
+// spreads them over all banks); V rows are read 16 rows x two chunks per transposing read (chunk ^
+// 2 (row % 8) leaves two reads per bank group, the minimum for 512 bytes).
+__device__ inline int swz_k(int row) { return row & 15; }
+__device__ inline int swz_v(int row) { return (row & 7) << 1; }
+
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char k_lds[kBK * kRowB];
+  __shared__ __attribute__((aligned(16))) char v_lds[kBK * kRowB];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int nqb = a.seq_len / kBQ;
+  const int qb = nqb - 1 - int(blockIdx.x);  // heavier blocks first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (a.q_heads / a.kv_heads);
+  const int64_t seq0 = int64_t(b) * a.seq_len;  // first token row of the sequence
+  const unsigned short* qkv = reinterpret_cast<const unsigned short*>(a.QKV);
+  const int64_t ld = a.ld_qkv;
+  const int64_t kcol = int64_t(a.q_heads + g) * kD, vcol = int64_t(a.q_heads + a.kv_heads + g) * kD;
+
+  const int lr = lane & 15, lg = lane >> 4;
+  const int q_row = qb * kBQ + wave * 16 + lr;  // this lane's query row within the sequence
+
+  // Q fragments of the lane's row: dims 32 kk + 8 lg .. +7 (kept for the whole walk)
+  bf16x8 qf[kD / 32];
+  {
+    const unsigned short* qp = qkv + (seq0 + q_row) * ld + int64_t(h) * kD + 8 * lg;
+#pragma unroll
+    for (int kk = 0; kk < kD / 32; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
+  }
+
+  f32x4 o[kD / 16];
+#pragma unroll
+  for (int j = 0; j < kD / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.0f;
+  const float sl2 = a.scale_log2;
+
+  for (int kb = 0; kb <= qb; ++kb) {
+    // ---- K and V tiles of this key block into LDS (each thread four 16-byte chunks of each)
+    __syncthreads();  // every wave is done reading the previous tiles
+#pragma unroll
+    for (int p = 0; p < kBK * kRowB / (16 * kThreads); ++p) {
+      const int idx = p * kThreads + t;
+      const int row = idx >> 4, ch = idx & 15;
+      const int64_t grow = seq0 + int64_t(kb) * kBK + row;
+      const i32x4 kv = *reinterpret_cast<const i32x4*>(qkv + grow * ld + kcol + ch * 8);
+      const i32x4 vv = *reinterpret_cast<const i32x4*>(qkv + grow * ld + vcol + ch * 8);
+      *reinterpret_cast<i32x4*>(k_lds + row * kRowB + ((ch ^ swz_k(row)) << 4)) = kv;
+      *reinterpret_cast<i32x4*>(v_lds + row * kRowB + ((ch ^ swz_v(row)) << 4)) = vv;
+    }
+    __syncthreads();
+
+    // ---- S = Q K^T for the wave's 16 rows x 64 keys: four 16-key tiles
+    f32x4 s[kBK / 16];
+#pragma unroll
+    for (int j = 0; j < kBK / 16; ++j) {
+      s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int krow = 16 * j + lr;
+#pragma unroll
+      for (int kk = 0; kk < kD / 32; ++kk) {
+        const int ch = 4 * kk + lg;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + krow * kRowB + ((ch ^ swz_k(krow)) << 4));
+        // first operand K (rows = keys), second Q: lane l gets S[q row lr][key 16 j + 4 lg + v]
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[j], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax over the block's keys (scores in log2 units)
+    const bool diag = kb == qb;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kBK / 16; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x = s[j][v] * sl2;
+        if (diag && kb * kBK + 16 * j + 4 * lg + v > q_row) x = -INFINITY;
+        s[j][v] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
+    float rs = 0.0f;
+    bf16x8 pf[kBK / 32];
+#pragma unroll
+    for (int c = 0; c < kBK / 32; ++c) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float p = __builtin_amdgcn_exp2f(s[2 * c + half][v] - m_new);
+          rs += p;
+          pf[c][4 * half + v] = (__bf16)p;
+        }
+    }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int j = 0; j < kD / 16; ++j) o[j] *= alpha;
+
+    // ---- O += P V: for each 32-key step, the V fragment of keys 32c + 4 lg + 0..3 and
+    // 32c + 16 + 4 lg + 0..3 in the lane's k slots, dims 16 jd + lr
+    const int vq = lane & 3, vv4 = (lane & 15) >> 2;
+#pragma unroll
+    for (int c = 0; c < kBK / 32; ++c) {
+      const int k0 = 32 * c + 4 * lg + vv4, k1 = k0 + 16;
+#pragma unroll
+      for (int jd = 0; jd < kD / 16; ++jd) {
+        const int ch = 2 * jd + (vq >> 1);  // 16-byte chunk of dims 16 jd + 4 vq .. +3
+        const int bin = (vq & 1) << 3;
+        const char* p0 = v_lds + k0 * kRowB + ((ch ^ swz_v(k0)) << 4) + bin;
+        const char* p1 = v_lds + k1 * kRowB + ((ch ^ swz_v(k1)) << 4) + bin;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+        const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        // first operand V (rows = dims), second P: lane l gets O[q row lr][dim 16 jd + 4 lg + v]
+        o[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pf[c], o[jd], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- C = O / l (bf16), the lane's row and dims 16 jd + 4 lg .. +3
+  const float inv = 1.0f / l;
+  unsigned short* C = reinterpret_cast<unsigned short*>(a.C) + (seq0 + q_row) * a.ld_c + int64_t(h) * kD + 4 * lg;
+#pragma unroll
+  for (int jd = 0; jd < kD / 16; ++jd) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 r = {(__bf16)(o[jd][0] * inv), (__bf16)(o[jd][1] * inv), (__bf16)(o[jd][2] * inv),
+                      (__bf16)(o[jd][3] * inv)};
+    *reinterpret_cast<i32x2*>(C + 16 * jd) = __builtin_bit_cast(i32x2, r);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (a.tokens <= 0) return hipSuccess;
+  const dim3 grid(unsigned(a.seq_len / kBQ), unsigned(a.q_heads), unsigned(a.tokens / a.seq_len));
+  if (start || stop)
+    hipExtLaunchKernelGGL(attn_fwd_kernel, grid, dim3(kThreads), 0, stream, start, stop, 0, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tps

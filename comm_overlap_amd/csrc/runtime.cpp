@@ -15,6 +15,7 @@
 #include <new>
 #include <vector>
 
+#include "attn.hpp"
 #include "gemm.hpp"
 #include "plan.hpp"
 
@@ -621,6 +622,26 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
                           reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw2_split), 1));
   if (db1) TPS_TRY(S.colsum(dU, p->N1, p->M, p->N1, partials, db1, accumulate, 1));
   return S.join();
+}
+
+extern "C" tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t p, const void* QKV, void* C, int64_t seq_len,
+                                                  void* stream) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (p->M > 0) { TPS_REQ(QKV); TPS_REQ(C); } else { TPS_OPT(QKV); TPS_OPT(C); }
+  if (!p->qh) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads");
+  if (p->desc.head_dim != kAttnHeadDim)
+    return fail(TPSLICE_ERR_UNSUPPORTED, "head_dim %d: the attention core takes %d", p->desc.head_dim, kAttnHeadDim);
+  if (seq_len <= 0 || seq_len % kAttnBlock != 0 || seq_len > (int64_t(1) << 30) || p->M % seq_len != 0)
+    return fail(TPSLICE_ERR_SHAPE, "seq_len %lld must be a positive multiple of %d dividing the %lld tokens",
+                (long long)seq_len, kAttnBlock, (long long)p->M);
+  if (p->qh % p->kvh != 0) return fail(TPSLICE_ERR_SHAPE, "%d query heads over %d kv heads", p->qh, p->kvh);
+  if (p->M == 0) return TPSLICE_OK;
+  AttnArgs a{QKV, C, p->qkv, p->ctx, p->M, int32_t(seq_len), p->qh, p->kvh,
+             float(1.4426950408889634 / std::sqrt(double(kAttnHeadDim)))};
+  hipError_t e = launch_attn_fwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  return TPSLICE_OK;
 }
 
 extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X, const void* Wqkv,

@@ -28,7 +28,8 @@ OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD = range(4)
 EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice_plan_piece",
            "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",
            "tpslice_attnproj_bwd", "tpslice_trace_enable", "tpslice_trace_read",
-           "tpslice_handoff_copy", "tpslice_handoff_wait", "tpslice_error_string", "tpslice_last_error")
+           "tpslice_handoff_copy", "tpslice_handoff_wait", "tpslice_attn_core_fwd", "tpslice_error_string",
+           "tpslice_last_error")
 TRACE_GEMM, TRACE_COPY, TRACE_COLSUM = range(3)
 STEPS = ("mlp_up", "mlp_down", "qkv", "out", "mlp_dh", "mlp_dx", "mlp_dw1", "mlp_dw2", "attn_dx", "attn_dc",
          "attn_dwqkv", "attn_dwo", "bias_grad", "handoff")
@@ -89,7 +90,8 @@ def _load():
     lib.tpslice_trace_read.argtypes = [vp, ctypes.POINTER(TraceRec), i32, ctypes.POINTER(i32)]
     lib.tpslice_handoff_copy.argtypes = [vp, vp, vp, vp]
     lib.tpslice_handoff_wait.argtypes = [vp, vp]
-    for name in EXPORTS[:13]:
+    lib.tpslice_attn_core_fwd.argtypes = [vp, vp, vp, ctypes.c_int64, vp]
+    for name in EXPORTS[:14]:
         getattr(lib, name).restype = st
     lib.tpslice_error_string.argtypes = [st]
     lib.tpslice_error_string.restype = ctypes.c_char_p
@@ -287,6 +289,14 @@ class Plan:
                                    _ptr(dX_handoff, name="dX_handoff"), _ptr(dW1, f32, "dW1"),
                                    _ptr(db1, f32, "db1"), _ptr(dW2, f32, "dW2"), int(bool(accumulate)),
                                    wp, wn, _stream(stream)))
+
+    def attn_core_fwd(self, QKV, C, seq_len, stream=None):
+        """Causal attention of every sequence (seq_len consecutive token rows) and query head:
+        QKV [tokens][(q + 2 kv) head_dim] -> C [tokens][q head_dim], bf16."""
+        i = self.info
+        _shape(QKV, (i.tokens, i.qkv_width), "QKV")
+        _shape(C, (i.tokens, i.ctx_width), "C")
+        _check(lib.tpslice_attn_core_fwd(self._h, _ptr(QKV), _ptr(C), int(seq_len), _stream(stream)))
 
     def attnproj_bwd(self, X, Wqkv, dQKV, C, Wo, dY, dX, dC, dWqkv, dWo, dbqkv=None, dX_handoff=None,
                      accumulate=False, workspace=None, stream=None):

@@ -220,6 +220,19 @@ TPSLICE_API tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t plan, const voi
                                       float* dWqkv, float* dbqkv, float* dWo, int32_t accumulate,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Causal attention core between the two projections, forward (the tiled softmax attention of the
+ * FlashAttention titles on the Domino page's builds-on list, computed exactly up to rounding):
+ *   C[t, h] = sum over s <= t of softmax_s(Q[t, h] . K[s, g] / sqrt(head_dim)) V[s, g],
+ *   g = h / (q_heads / kv_heads), t and s positions in the same sequence.
+ * Inputs : QKV [M][(q + 2 kv) head_dim] bf16 as tpslice_attnproj_fwd writes it (Q heads, K heads,
+ *          V heads); the sequences are consecutive runs of `seq_len` token rows.
+ * Outputs: C [M][q head_dim] bf16, the context the output projection reads.
+ * Requires the plan's head_dim = 128 (else TPSLICE_ERR_UNSUPPORTED), seq_len a multiple of 64
+ * that divides the token count (else TPSLICE_ERR_SHAPE). Softmax in fp32; the probabilities are
+ * rounded to bf16 for the product with V. Runs on `stream` (no slicing, no hand-off). */
+TPSLICE_API tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t plan, const void* QKV, void* C, int64_t seq_len,
+                                       void* stream);
+
 /* Tracing. When enabled, every product and every hand-off copy is bracketed by timing events on
  * the stream it runs on. Records accumulate over calls until they are read; times are milliseconds
  * from the start (on the caller stream) of the first call traced since the last read, and `call`

@@ -230,3 +230,20 @@ def test_handoff_rows_flag():
             assert (p.info.n_row_slices, p.info.n_col_slices) == (2, c)
             p.close()
     assert T.F_HANDOFF_ROWS == 0x8
+
+
+def test_attention_core_argument_errors():
+    """The attention core checks its plan and sizes before any GPU work (pointers never read)."""
+    lib = T.lib
+    A = _fake(0x100000)
+    no_heads = T.Plan(T.Config(tokens=256, hidden=64, ffn=64))
+    assert lib.tpslice_attn_core_fwd(no_heads._h, A, A, 128, None) == T.ERR_UNSUPPORTED
+    d64 = T.Plan(T.Config(tokens=256, hidden=512, ffn=64, n_heads=4, n_kv_heads=2, head_dim=64))
+    assert lib.tpslice_attn_core_fwd(d64._h, A, A, 128, None) == T.ERR_UNSUPPORTED
+    assert b"head_dim 64" in lib.tpslice_last_error()
+    p = T.Plan(T.Config(tokens=256, hidden=512, ffn=64, n_heads=4, n_kv_heads=2, head_dim=128))
+    for bad in (0, -64, 96, 192, 512):  # not a multiple of 64, or not dividing the 256 tokens
+        assert lib.tpslice_attn_core_fwd(p._h, A, A, bad, None) == T.ERR_SHAPE, bad
+    assert lib.tpslice_attn_core_fwd(p._h, None, A, 128, None) == T.ERR_INVALID
+    assert lib.tpslice_attn_core_fwd(p._h, A, _fake(0x100008), 128, None) == T.ERR_INVALID
+    assert lib.tpslice_attn_core_fwd(None, A, A, 128, None) == T.ERR_INVALID
