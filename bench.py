@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
     ap.add_argument("--strands", type=int, default=1, choices=[1, 2],
                     help="2: also time two micro-batches in flight, forward beside backward (layer workloads)")
+    ap.add_argument("--attn-seq", type=int, default=2048,
+                    help="sequence length for the attention-core leg of layer workloads")
+    ap.add_argument("--no-attn-core", action="store_true", help="skip the attention-core leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="finish with plain 256 MiB device copies (counter calibration for profiles)")
     return ap.parse_args()
@@ -255,6 +258,37 @@ def kernel_stats(recs):
     return by
 
 
+def attn_core(w, inp, seq_len, steps):
+    """The causal attention core between the projections (tpslice_attn_core_fwd) over the layer's
+    tokens as sequences of seq_len rows, timed alone on the caller's stream (not part of the
+    layer's GEMM chain above). Flops: 2 seq_len^2 head_dim per query head and sequence (the causal
+    half of QK^T and PV)."""
+    import torch
+    from comm_overlap_amd import synth
+    from comm_overlap_amd import tpslice as T
+    if w.tokens % seq_len:
+        return None
+    plan = T.plan_for(w)
+    qkv = synth.randn_bf16((w.tokens, w.qkv_width), 1.0, 7).cuda()
+    c = torch.empty(w.tokens, plan.info.ctx_width, dtype=torch.bfloat16, device="cuda")
+    for _ in range(5):
+        plan.attn_core_fwd(qkv, c, seq_len)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(10, steps)
+    e0.record()
+    for _ in range(n):
+        plan.attn_core_fwd(qkv, c, seq_len)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 2.0 * seq_len * seq_len * 128 * w.q_heads_shard * (w.tokens // seq_len)
+    plan.close()
+    return {"seq_len": seq_len, "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "q_heads": w.q_heads_shard, "kv_heads": w.kv_heads_shard, "head_dim": 128}
+
+
 def cpu_baseline(w, inp, target_s):
     """The fp64 oracle, as it stands, on the host's cores over a bounded row sample of the workload."""
     from oracle import layer as L
@@ -423,6 +457,9 @@ def main():
     }
     if two is not None:
         out["two_strands"] = two
+    if w.has_attn and not args.no_attn_core:
+        log("attention core")
+        out["attn_core"] = attn_core(w, inp, args.attn_seq, args.steps)
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
