@@ -1,6 +1,6 @@
 // Causal attention core between the QKV and the output projections, forward, for gfx950.
 //
-// One block computes 64 query rows of one query head of one sequence (four waves of 16 rows) and
+// One block computes 128 query rows of one query head of one sequence (eight waves of 16 rows) and
 // walks the key blocks of 64 up to the diagonal, keeping the softmax online (running row maximum
 // and row sum, the output rescaled when the maximum grows): the tiled form of softmax attention
 // that the FlashAttention titles in the Domino page's builds-on list describe. Per key block:
@@ -15,11 +15,12 @@
 // keys 32c + 4 (l / 16) + 0..3 and 32c + 16 + 4 (l / 16) + 0..3; the V fragment is read for the same
 // keys in the same slots, so the product is the plain sum over the step's keys.
 // K and V tiles (64 keys x 128 dims bf16, 16 KB each) come in through registers (16-byte global
-// loads one key block ahead, then ds_write_b128); two blocks share a CU (register-bound), so one
-// block's loads and barriers hide under the other's MFMAs. Measured on the Llama shard shapes at
-// 2048 and 4096 tokens per sequence: 190-330 TFLOP/s; 128-row blocks (two row tiles per wave
-// sharing each K and V fragment) needed 280 registers, one block per CU, and ran 125-207.
-// Heavier query blocks (more key blocks under the diagonal) start first.
+// loads one key block ahead, then ds_write_b128), shared by the block's eight waves. Measured on
+// the Llama shard shapes at 2048-token sequences: 234 and 381 TFLOP/s, against 190 and 264 with
+// four-wave 64-row blocks (each staging its own K and V) and 125-207 with four waves of two row
+// tiles (280 registers, one block per CU). The diagonal spans the block's last two key blocks;
+// a row whose keys in such a block are all masked keeps its maximum (finite from key block 0 on)
+// and adds nothing. Heavier query blocks (more key blocks under the diagonal) start first.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -39,10 +40,12 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kD = kAttnHeadDim;  // 128
-constexpr int kBQ = 64;           // query rows per block
+constexpr int kWaves = 8;
+constexpr int kBQ = 16 * kWaves;  // query rows per block
+static_assert(kBQ == kAttnBlock, "the launcher's block size");
 constexpr int kBK = 64;           // keys per block
 constexpr int kRowB = kD * 2;     // bytes of one K or V row in LDS
-constexpr int kThreads = 256;
+constexpr int kThreads = 64 * kWaves;
 
 // 16-byte chunk swizzles: K rows are read 16 rows at one chunk per quarter wave (chunk ^ row%16
 // spreads them over all banks); V rows are read 16 rows x two chunks per transposing read (chunk ^
@@ -96,8 +99,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
       vreg[p] = *reinterpret_cast<const i32x4*>(qkv + grow * ld + vcol + ch * 8);
     }
   };
+  const int nkb = (qb * kBQ + kBQ - 1) / kBK + 1;
+  const int first_diag = (qb * kBQ) / kBK;
   fetch(0);
-  for (int kb = 0; kb <= qb; ++kb) {
+  for (int kb = 0; kb < nkb; ++kb) {
     // ---- K and V tiles of this key block into LDS
     __syncthreads();  // every wave is done reading the previous tiles
 #pragma unroll
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
       *reinterpret_cast<i32x4*>(v_lds + row * kRowB + ((ch ^ swz_v(row)) << 4)) = vreg[p];
     }
     __syncthreads();
-    if (kb < qb) fetch(kb + 1);
+    if (kb + 1 < nkb) fetch(kb + 1);
 
     // ---- S = Q K^T for the wave's 16 rows x 64 keys: four 16-key tiles
     f32x4 s[kBK / 16];
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
     }
 
     // ---- online softmax over the block's keys (scores in log2 units)
-    const bool diag = kb == qb;
+    const bool diag = kb >= first_diag;
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kBK / 16; ++j)

@@ -8,7 +8,7 @@
 namespace tps {
 
 constexpr int kAttnHeadDim = 128;  // the one head size the kernel takes
-constexpr int kAttnBlock = 64;     // query rows and keys per block: seq_len must be a multiple
+constexpr int kAttnBlock = 128;    // query rows per block: seq_len must be a multiple
 
 struct AttnArgs {
   const void* QKV;     // [tokens][ld_qkv] bf16: Q heads, K heads, V heads of kAttnHeadDim columns each

@@ -227,7 +227,7 @@ TPSLICE_API tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t plan, const voi
  * Inputs : QKV [M][(q + 2 kv) head_dim] bf16 as tpslice_attnproj_fwd writes it (Q heads, K heads,
  *          V heads); the sequences are consecutive runs of `seq_len` token rows.
  * Outputs: C [M][q head_dim] bf16, the context the output projection reads.
- * Requires the plan's head_dim = 128 (else TPSLICE_ERR_UNSUPPORTED), seq_len a multiple of 64
+ * Requires the plan's head_dim = 128 (else TPSLICE_ERR_UNSUPPORTED), seq_len a multiple of 128
  * that divides the token count (else TPSLICE_ERR_SHAPE). Softmax in fp32; the probabilities are
  * rounded to bf16 for the product with V. Runs on `stream` (no slicing, no hand-off). */
 TPSLICE_API tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t plan, const void* QKV, void* C, int64_t seq_len,

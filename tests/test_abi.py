@@ -242,7 +242,7 @@ def test_attention_core_argument_errors():
     assert lib.tpslice_attn_core_fwd(d64._h, A, A, 128, None) == T.ERR_UNSUPPORTED
     assert b"head_dim 64" in lib.tpslice_last_error()
     p = T.Plan(T.Config(tokens=256, hidden=512, ffn=64, n_heads=4, n_kv_heads=2, head_dim=128))
-    for bad in (0, -64, 96, 160, 512):  # not a multiple of 64, or not dividing the 256 tokens
+    for bad in (0, -128, 64, 96, 192, 512):  # not a multiple of 128, or not dividing the 256 tokens
         assert lib.tpslice_attn_core_fwd(p._h, A, A, bad, None) == T.ERR_SHAPE, bad
     assert lib.tpslice_attn_core_fwd(p._h, None, A, 128, None) == T.ERR_INVALID
     assert lib.tpslice_attn_core_fwd(p._h, A, _fake(0x100008), 128, None) == T.ERR_INVALID
