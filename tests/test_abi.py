@@ -247,3 +247,14 @@ def test_attention_core_argument_errors():
     assert lib.tpslice_attn_core_fwd(p._h, None, A, 128, None) == T.ERR_INVALID
     assert lib.tpslice_attn_core_fwd(p._h, A, _fake(0x100008), 128, None) == T.ERR_INVALID
     assert lib.tpslice_attn_core_fwd(None, A, A, 128, None) == T.ERR_INVALID
+
+
+def test_bench_rejects_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus above 1 exits with a message before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2 and "one GPU" in r.stderr
