@@ -7,10 +7,11 @@
 //     both read along k, without the SwiGLU pairing), one block per CU;
 //   * 128 x 256, 8 waves, waves of 64 x 64, one block per CU (96 KB LDS);
 //   * 128 x 128, 4 waves (2 x 2), waves of 64 x 64, two blocks per CU (64 KB LDS each);
-//   * 256 x 256 and 256 x 160 with 4 waves (2 x 2, one wave per SIMD), waves of 128 x 128 / 128 x
-//     80, one block per CU, for forward products with k a multiple of 64: a software-pipelined
-//     loop (barrier between the two k steps, loads two blocks ahead, LDS reads and load issue
-//     interleaved one by one with the MFMAs) that leaves no wait to another wave.
+//   * 256 x 256, 256 x 160 and 256 x 320 with 4 waves (2 x 2, one wave per SIMD), waves of
+//     128 x 128 / 128 x 80 / 128 x 160, one block per CU, for products with k a multiple of 64
+//     (256 x 256 in every operand layout and for split runs; the others forward only): a
+//     software-pipelined loop (barrier between the two k steps, loads two blocks ahead, LDS reads
+//     and load issue interleaved one by one with the MFMAs) that leaves no wait to another wave.
 // The launcher picks per product the tile with the smallest estimated time on 256 CUs: whole
 // rounds of resident blocks times the tile's work over its measured per-CU rate. Larger tiles move
 // fewer bytes per flop; the others cut the last, partly filled round (e.g. a 4096 x 5120 product is
@@ -79,7 +80,7 @@ using TileN = Tile<128, 320, 2, 4, 1>;
 using TileM = Tile<128, 256, 2, 4, 1>;
 using TileT = Tile<128, 128, 2, 4, 1>;
 // Four waves, one per SIMD, each 128 rows x (BN / 2) columns, with the software-pipelined main
-// loop (gemm_kernel); for forward products whose K is a multiple of 64.
+// loop (gemm_kernel); for products whose K is a multiple of 64 (256 x 160: forward only).
 using TileL4 = Tile<256, 256, 2, 2, 1>;
 using TileH4 = Tile<256, 160, 2, 2, 1>;
 // 256 x 320 with four waves of 128 x 160: 320 accumulator registers per lane, more than the 256
