@@ -15,12 +15,18 @@
 // keys 32c + 4 (l / 16) + 0..3 and 32c + 16 + 4 (l / 16) + 0..3; the V fragment is read for the same
 // keys in the same slots, so the product is the plain sum over the step's keys.
 // K and V tiles (64 keys x 128 dims bf16, 16 KB each) come in through registers (16-byte global
-// loads one key block ahead, then ds_write_b128), shared by the block's eight waves. Measured on
-// the Llama shard shapes at 2048-token sequences: 234 and 381 TFLOP/s, against 190 and 264 with
-// four-wave 64-row blocks (each staging its own K and V) and 125-207 with four waves of two row
-// tiles (280 registers, one block per CU). The diagonal spans the block's last two key blocks;
-// a row whose keys in such a block are all masked keeps its maximum (finite from key block 0 on)
-// and adds nothing. Heavier query blocks (more key blocks under the diagonal) start first.
+// loads one key block ahead, then ds_write_b128), shared by the block's eight waves. The row maximum
+// is reduced over the row's four lanes with VALU lane swaps; each lane keeps its own share of the
+// row sum until the end. The diagonal spans the block's last two key blocks; a row whose keys in
+// such a block are all masked keeps its maximum (finite from key block 0 on) and adds nothing.
+// Measured on the Llama shard shapes (13B: 5 query and key/value heads; 70B: 8 query heads, 1
+// key/value head) at 2048-token sequences: dealing the query blocks so that each XCD reads the K/V
+// rows of few heads (its L2) and each workgroup takes a heavy and a light block raised 236 and 382
+// TFLOP/s to 353 and 514. Not adopted: four-wave 64-row blocks (each staging its own K and V, 190
+// and 264 before the dealing), four waves of two row tiles (280 registers, one block per CU,
+// 125-207), double-buffered K/V with one barrier per key block (more registers; slower even with
+// them capped for two blocks per CU), and capping this kernel at 128 registers for two blocks per
+// CU (a few spills; 70B 3-6% faster, 13B 18% slower). With 156 registers one block runs per CU.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -53,149 +59,186 @@ constexpr int kThreads = 64 * kWaves;
 __device__ inline int swz_k(int row) { return row & 15; }
 __device__ inline int swz_v(int row) { return (row & 7) << 1; }
 
+// max / sum of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes holding one S row), on VALU
+// lane swaps; every lane of the group gets the same bits
+__device__ inline float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float row_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Pairing of query blocks qb and nqb - 1 - qb in one workgroup (needs an even nqb and a whole number
+// of pairs per XCD).
+__host__ __device__ inline bool attn_paired(int nqb, int total) { return (nqb & 1) == 0 && (total & 15) == 0; }
+
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k_lds[kBK * kRowB];
   __shared__ __attribute__((aligned(16))) char v_lds[kBK * kRowB];
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  // Work items (sequence, head, query block qb). Query blocks qb and nqb - 1 - qb together cost the
+  // same (2 nqb + 2 key blocks), so where the item count allows, one workgroup takes such a pair,
+  // the heavy block first, and every workgroup does the same work. Workgroups go to the eight XCDs
+  // round robin by launch index; the pairs are dealt so that each XCD takes one contiguous run of
+  // them (those of a few heads of one or two sequences), whose K/V rows stay in its own L2.
   const int nqb = a.seq_len / kBQ;
-  const int qb = nqb - 1 - int(blockIdx.x);  // heavier blocks first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (a.q_heads / a.kv_heads);
-  const int64_t seq0 = int64_t(b) * a.seq_len;  // first token row of the sequence
-  const unsigned short* qkv = reinterpret_cast<const unsigned short*>(a.QKV);
-  const int64_t ld = a.ld_qkv;
-  const int64_t kcol = int64_t(a.q_heads + g) * kD, vcol = int64_t(a.q_heads + a.kv_heads + g) * kD;
-
-  const int lr = lane & 15, lg = lane >> 4;
-  const int q_row = qb * kBQ + wave * 16 + lr;  // this lane's query row within the sequence
-
-  // Q fragments of the lane's row: dims 32 kk + 8 lg .. +7 (kept for the whole walk)
-  bf16x8 qf[kD / 32];
-  {
-    const unsigned short* qp = qkv + (seq0 + q_row) * ld + int64_t(h) * kD + 8 * lg;
-#pragma unroll
-    for (int kk = 0; kk < kD / 32; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
-  }
-
-  f32x4 o[kD / 16];
-#pragma unroll
-  for (int j = 0; j < kD / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.0f;
-  const float sl2 = a.scale_log2;
-
-  // K and V chunks of a key block: each thread four 16-byte chunks of each, loaded into registers
-  // one block ahead (the loads of block kb + 1 fly while block kb is multiplied)
-  constexpr int kLoads = kBK * kRowB / (16 * kThreads);
-  i32x4 kreg[kLoads], vreg[kLoads];
-  auto fetch = [&](int kb) {
-#pragma unroll
-    for (int p = 0; p < kLoads; ++p) {
-      const int idx = p * kThreads + t;
-      const int row = idx >> 4, ch = idx & 15;
-      const int64_t grow = seq0 + int64_t(kb) * kBK + row;
-      kreg[p] = *reinterpret_cast<const i32x4*>(qkv + grow * ld + kcol + ch * 8);
-      vreg[p] = *reinterpret_cast<const i32x4*>(qkv + grow * ld + vcol + ch * 8);
+  const int total = nqb * a.q_heads * (a.tokens / a.seq_len), li = int(blockIdx.x);
+  const bool paired = attn_paired(nqb, total);
+#pragma clang loop unroll(disable)
+  for (int it = 0; it < (paired ? 2 : 1); ++it) {
+    int bh, qb;
+    if (paired) {
+      const int per_xcd = total >> 4;  // pairs per XCD
+      const int u = (li & 7) * per_xcd + (li >> 3);
+      const int half = nqb >> 1;
+      bh = u / half;
+      const int pi = u - bh * half;
+      qb = it == 0 ? nqb - 1 - pi : pi;
+    } else {
+      bh = li / nqb;
+      qb = nqb - 1 - (li - bh * nqb);  // heavier blocks of a head first
     }
-  };
-  const int nkb = (qb * kBQ + kBQ - 1) / kBK + 1;
-  const int first_diag = (qb * kBQ) / kBK;
-  fetch(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    // ---- K and V tiles of this key block into LDS
-    __syncthreads();  // every wave is done reading the previous tiles
-#pragma unroll
-    for (int p = 0; p < kLoads; ++p) {
-      const int idx = p * kThreads + t;
-      const int row = idx >> 4, ch = idx & 15;
-      *reinterpret_cast<i32x4*>(k_lds + row * kRowB + ((ch ^ swz_k(row)) << 4)) = kreg[p];
-      *reinterpret_cast<i32x4*>(v_lds + row * kRowB + ((ch ^ swz_v(row)) << 4)) = vreg[p];
-    }
-    __syncthreads();
-    if (kb + 1 < nkb) fetch(kb + 1);
+    const int b = bh / a.q_heads, h = bh - b * a.q_heads;
+    const int g = h / (a.q_heads / a.kv_heads);
+    const int64_t seq0 = int64_t(b) * a.seq_len;  // first token row of the sequence
+    const unsigned short* qkv = reinterpret_cast<const unsigned short*>(a.QKV);
+    const int64_t ld = a.ld_qkv;
+    const int64_t kcol = int64_t(a.q_heads + g) * kD, vcol = int64_t(a.q_heads + a.kv_heads + g) * kD;
 
-    // ---- S = Q K^T for the wave's 16 rows x 64 keys: four 16-key tiles
-    f32x4 s[kBK / 16];
-#pragma unroll
-    for (int j = 0; j < kBK / 16; ++j) {
-      s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int krow = 16 * j + lr;
-#pragma unroll
-      for (int kk = 0; kk < kD / 32; ++kk) {
-        const int ch = 4 * kk + lg;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + krow * kRowB + ((ch ^ swz_k(krow)) << 4));
-        // first operand K (rows = keys), second Q: lane l gets S[q row lr][key 16 j + 4 lg + v]
-        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[j], 0, 0, 0);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int q_row = qb * kBQ + wave * 16 + lr;  // this lane's query row within the sequence
+
+    // Q fragments of the lane's row: dims 32 kk + 8 lg .. +7 (kept for the whole walk)
+    bf16x8 qf[kD / 32];
+    {
+      const unsigned short* qp = qkv + (seq0 + q_row) * ld + int64_t(h) * kD + 8 * lg;
+  #pragma unroll
+      for (int kk = 0; kk < kD / 32; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
+    }
+
+    f32x4 o[kD / 16];
+  #pragma unroll
+    for (int j = 0; j < kD / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.0f;
+    const float sl2 = a.scale_log2;
+
+    // K and V chunks of a key block: each thread four 16-byte chunks of each, loaded into registers
+    // one block ahead (the loads of block kb + 1 fly while block kb is multiplied)
+    constexpr int kLoads = kBK * kRowB / (16 * kThreads);
+    i32x4 kreg[kLoads], vreg[kLoads];
+    auto fetch = [&](int kb) {
+  #pragma unroll
+      for (int p = 0; p < kLoads; ++p) {
+        const int idx = p * kThreads + t;
+        const int row = idx >> 4, ch = idx & 15;
+        const int64_t grow = seq0 + int64_t(kb) * kBK + row;
+        kreg[p] = *reinterpret_cast<const i32x4*>(qkv + grow * ld + kcol + ch * 8);
+        vreg[p] = *reinterpret_cast<const i32x4*>(qkv + grow * ld + vcol + ch * 8);
       }
-    }
-
-    // ---- online softmax over the block's keys (scores in log2 units)
-    const bool diag = kb >= first_diag;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kBK / 16; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x = s[j][v] * sl2;
-        if (diag && kb * kBK + 16 * j + 4 * lg + v > q_row) x = -INFINITY;
-        s[j][v] = x;
-        mx = fmaxf(mx, x);
+    };
+    const int nkb = (qb * kBQ + kBQ - 1) / kBK + 1;
+    const int first_diag = (qb * kBQ) / kBK;
+    fetch(0);
+    for (int kb = 0; kb < nkb; ++kb) {
+      // ---- K and V tiles of this key block into LDS
+      __syncthreads();  // every wave is done reading the previous tiles
+  #pragma unroll
+      for (int p = 0; p < kLoads; ++p) {
+        const int idx = p * kThreads + t;
+        const int row = idx >> 4, ch = idx & 15;
+        *reinterpret_cast<i32x4*>(k_lds + row * kRowB + ((ch ^ swz_k(row)) << 4)) = kreg[p];
+        *reinterpret_cast<i32x4*>(v_lds + row * kRowB + ((ch ^ swz_v(row)) << 4)) = vreg[p];
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
-    float rs = 0.0f;
-    bf16x8 pf[kBK / 32];
-#pragma unroll
-    for (int c = 0; c < kBK / 32; ++c) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = __builtin_amdgcn_exp2f(s[2 * c + half][v] - m_new);
-          rs += p;
-          pf[c][4 * half + v] = (__bf16)p;
+      __syncthreads();
+      if (kb + 1 < nkb) fetch(kb + 1);
+
+      // ---- S = Q K^T for the wave's 16 rows x 64 keys: four 16-key tiles
+      f32x4 s[kBK / 16];
+  #pragma unroll
+      for (int j = 0; j < kBK / 16; ++j) {
+        s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int krow = 16 * j + lr;
+  #pragma unroll
+        for (int kk = 0; kk < kD / 32; ++kk) {
+          const int ch = 4 * kk + lg;
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + krow * kRowB + ((ch ^ swz_k(krow)) << 4));
+          // first operand K (rows = keys), second Q: lane l gets S[q row lr][key 16 j + 4 lg + v]
+          s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[j], 0, 0, 0);
         }
-    }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int j = 0; j < kD / 16; ++j) o[j] *= alpha;
+      }
 
-    // ---- O += P V: for each 32-key step, the V fragment of keys 32c + 4 lg + 0..3 and
-    // 32c + 16 + 4 lg + 0..3 in the lane's k slots, dims 16 jd + lr
-    const int vq = lane & 3, vv4 = (lane & 15) >> 2;
-#pragma unroll
-    for (int c = 0; c < kBK / 32; ++c) {
-      const int k0 = 32 * c + 4 * lg + vv4, k1 = k0 + 16;
-#pragma unroll
-      for (int jd = 0; jd < kD / 16; ++jd) {
-        const int ch = 2 * jd + (vq >> 1);  // 16-byte chunk of dims 16 jd + 4 vq .. +3
-        const int bin = (vq & 1) << 3;
-        const char* p0 = v_lds + k0 * kRowB + ((ch ^ swz_v(k0)) << 4) + bin;
-        const char* p1 = v_lds + k1 * kRowB + ((ch ^ swz_v(k1)) << 4) + bin;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-        const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        // first operand V (rows = dims), second P: lane l gets O[q row lr][dim 16 jd + 4 lg + v]
-        o[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pf[c], o[jd], 0, 0, 0);
+      // ---- online softmax over the block's keys (scores in log2 units)
+      const bool diag = kb >= first_diag;
+      float mx = -INFINITY;
+  #pragma unroll
+      for (int j = 0; j < kBK / 16; ++j)
+  #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = s[j][v] * sl2;
+          if (diag && kb * kBK + 16 * j + 4 * lg + v > q_row) x = -INFINITY;
+          s[j][v] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = row_max4(mx);
+      const float m_new = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
+      float rs = 0.0f;
+      bf16x8 pf[kBK / 32];
+  #pragma unroll
+      for (int c = 0; c < kBK / 32; ++c) {
+  #pragma unroll
+        for (int half = 0; half < 2; ++half)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float p = __builtin_amdgcn_exp2f(s[2 * c + half][v] - m_new);
+            rs += p;
+            pf[c][4 * half + v] = (__bf16)p;
+          }
+      }
+      l = l * alpha + rs;  // the lane's share of the row sum
+      m = m_new;
+  #pragma unroll
+      for (int j = 0; j < kD / 16; ++j) o[j] *= alpha;
+
+      // ---- O += P V: for each 32-key step, the V fragment of keys 32c + 4 lg + 0..3 and
+      // 32c + 16 + 4 lg + 0..3 in the lane's k slots, dims 16 jd + lr
+      const int vq = lane & 3, vv4 = (lane & 15) >> 2;
+  #pragma unroll
+      for (int c = 0; c < kBK / 32; ++c) {
+        const int k0 = 32 * c + 4 * lg + vv4, k1 = k0 + 16;
+  #pragma unroll
+        for (int jd = 0; jd < kD / 16; ++jd) {
+          const int ch = 2 * jd + (vq >> 1);  // 16-byte chunk of dims 16 jd + 4 vq .. +3
+          const int bin = (vq & 1) << 3;
+          const char* p0 = v_lds + k0 * kRowB + ((ch ^ swz_v(k0)) << 4) + bin;
+          const char* p1 = v_lds + k1 * kRowB + ((ch ^ swz_v(k1)) << 4) + bin;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+          const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          // first operand V (rows = dims), second P: lane l gets O[q row lr][dim 16 jd + 4 lg + v]
+          o[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pf[c], o[jd], 0, 0, 0);
+        }
       }
     }
-  }
 
-  // ---- C = O / l (bf16), the lane's row and dims 16 jd + 4 lg .. +3
-  const float inv = 1.0f / l;
-  unsigned short* C = reinterpret_cast<unsigned short*>(a.C) + (seq0 + q_row) * a.ld_c + int64_t(h) * kD + 4 * lg;
-#pragma unroll
-  for (int jd = 0; jd < kD / 16; ++jd) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const bf16x4 r = {(__bf16)(o[jd][0] * inv), (__bf16)(o[jd][1] * inv), (__bf16)(o[jd][2] * inv),
-                      (__bf16)(o[jd][3] * inv)};
-    *reinterpret_cast<i32x2*>(C + 16 * jd) = __builtin_bit_cast(i32x2, r);
+    // ---- C = O / l (bf16), the lane's row and dims 16 jd + 4 lg .. +3
+    const float inv = 1.0f / row_sum4(l);
+    unsigned short* C = reinterpret_cast<unsigned short*>(a.C) + (seq0 + q_row) * a.ld_c + int64_t(h) * kD + 4 * lg;
+  #pragma unroll
+    for (int jd = 0; jd < kD / 16; ++jd) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 r = {(__bf16)(o[jd][0] * inv), (__bf16)(o[jd][1] * inv), (__bf16)(o[jd][2] * inv),
+                        (__bf16)(o[jd][3] * inv)};
+      *reinterpret_cast<i32x2*>(C + 16 * jd) = __builtin_bit_cast(i32x2, r);
+    }
   }
 }
 
@@ -203,7 +246,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (a.tokens <= 0) return hipSuccess;
-  const dim3 grid(unsigned(a.seq_len / kBQ), unsigned(a.q_heads), unsigned(a.tokens / a.seq_len));
+  const int nqb = a.seq_len / kBQ;
+  const int total = nqb * a.q_heads * int(a.tokens / a.seq_len);
+  const dim3 grid(unsigned(attn_paired(nqb, total) ? total / 2 : total));
   if (start || stop)
     hipExtLaunchKernelGGL(attn_fwd_kernel, grid, dim3(kThreads), 0, stream, start, stop, 0, a);
   else

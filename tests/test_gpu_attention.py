@@ -30,7 +30,9 @@ def _run(w, QKV, seq_len):
 
 
 # (tokens, seq_len, heads, kv_heads, tp): q/kv heads per rank = heads/tp, max(1, kv_heads/tp)
-SMALL = [(512, 256, 8, 2, 2), (384, 128, 5, 5, 1), (256, 256, 8, 8, 8), (640, 128, 16, 2, 2)]
+# the first and last cases take the paired dealing of query blocks (the last with pairs that straddle
+# heads), the others the one-block-per-workgroup order
+SMALL = [(512, 256, 8, 2, 2), (384, 128, 5, 5, 1), (256, 256, 8, 8, 8), (640, 128, 16, 2, 2), (2048, 1024, 5, 5, 1)]
 
 
 @pytest.mark.parametrize("tokens,seq_len,heads,kv_heads,tp", SMALL)
