@@ -1,7 +1,7 @@
 // Causal attention core between the QKV and the output projections, forward, for gfx950.
 //
 // One block computes 128 query rows of one query head of one sequence (eight waves of 16 rows) and
-// walks the key blocks of 64 up to the diagonal, keeping the softmax online (running row maximum
+// walks the key blocks of 128 up to the diagonal, keeping the softmax online (running row maximum
 // and row sum, the output rescaled when the maximum grows): the tiled form of softmax attention
 // that the FlashAttention titles in the Domino page's builds-on list describe. Per key block:
 //   S = Q K^T   v_mfma_f32_16x16x32_bf16, Q fragments held in registers for the whole walk, K from
@@ -14,11 +14,11 @@
 // product takes a 32-key step from tiles 2c and 2c + 1 and lets lane l's eight k slots stand for
 // keys 32c + 4 (l / 16) + 0..3 and 32c + 16 + 4 (l / 16) + 0..3; the V fragment is read for the same
 // keys in the same slots, so the product is the plain sum over the step's keys.
-// K and V tiles (64 keys x 128 dims bf16, 16 KB each) come in through registers (16-byte global
+// K and V tiles (128 keys x 128 dims bf16, 32 KB each) come in through registers (16-byte global
 // loads one key block ahead, then ds_write_b128), shared by the block's eight waves. The row maximum
 // is reduced over the row's four lanes with VALU lane swaps; each lane keeps its own share of the
-// row sum until the end. The diagonal spans the block's last two key blocks; a row whose keys in
-// such a block are all masked keeps its maximum (finite from key block 0 on) and adds nothing.
+// row sum until the end. The diagonal is the block's last key block (query and key blocks are both
+// 128 rows), masked per row; its maximum is finite from its first key on.
 // Measured on the Llama shard shapes (13B: 5 query and key/value heads; 70B: 8 query heads, 1
 // key/value head) at 2048-token sequences: dealing the query blocks so that each XCD reads the K/V
 // rows of few heads (its L2) and each workgroup takes a heavy and a light block raised 236 and 382
@@ -26,7 +26,9 @@
 // and 264 before the dealing), four waves of two row tiles (280 registers, one block per CU,
 // 125-207), double-buffered K/V with one barrier per key block (more registers; slower even with
 // them capped for two blocks per CU), and capping this kernel at 128 registers for two blocks per
-// CU (a few spills; 70B 3-6% faster, 13B 18% slower). With 156 registers one block runs per CU.
+// CU (a few spills; 70B 3-6% faster, 13B 18% slower). 128-key blocks (half the barriers and
+// softmax rounds of 64-key ones, twice the independent S tiles) ran 4-5% faster than 64-key ones;
+// with 242 registers one block runs per CU.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -49,7 +51,7 @@ constexpr int kD = kAttnHeadDim;  // 128
 constexpr int kWaves = 8;
 constexpr int kBQ = 16 * kWaves;  // query rows per block
 static_assert(kBQ == kAttnBlock, "the launcher's block size");
-constexpr int kBK = 64;           // keys per block
+constexpr int kBK = 128;          // keys per block
 constexpr int kRowB = kD * 2;     // bytes of one K or V row in LDS
 constexpr int kThreads = 64 * kWaves;
 
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   // Work items (sequence, head, query block qb). Query blocks qb and nqb - 1 - qb together cost the
-  // same (2 nqb + 2 key blocks), so where the item count allows, one workgroup takes such a pair,
+  // same (nqb + 1 key blocks), so where the item count allows, one workgroup takes such a pair,
   // the heavy block first, and every workgroup does the same work. Workgroups go to the eight XCDs
   // round robin by launch index; the pairs are dealt so that each XCD takes one contiguous run of
   // them (those of a few heads of one or two sequences), whose K/V rows stay in its own L2.
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
       __syncthreads();
       if (kb + 1 < nkb) fetch(kb + 1);
 
-      // ---- S = Q K^T for the wave's 16 rows x 64 keys: four 16-key tiles
+      // ---- S = Q K^T for the wave's 16 rows x 128 keys: eight 16-key tiles
       f32x4 s[kBK / 16];
   #pragma unroll
       for (int j = 0; j < kBK / 16; ++j) {
