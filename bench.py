@@ -180,8 +180,9 @@ class TwoStrands:
             kw = dict(kw, pipeline=True, caller_worker=True, n_streams=1, n_copy_streams=1)
         else:
             kw = dict(kw, serialize=True, copy_blit=mode == "kernel")
-        self.fwd_plan = T.plan_for(w, **kw)
-        self.bwd_plan = T.plan_for(w, **kw)
+        # each strand's plan has worker and copy streams of its own
+        self.fwd_plan = T.plan_for(w, streams=T.Streams.new(1, 1), **kw)
+        self.bwd_plan = T.plan_for(w, streams=T.Streams.new(1, 1), **kw)
         self.chain = Chain(w, self.fwd_plan, inp)  # activation and output buffers of both sets
         self.bwd_ws = Chain(w, self.bwd_plan, inp)  # the backward plan's workspaces and gradients
         self.sa, self.sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority

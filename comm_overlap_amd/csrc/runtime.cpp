@@ -30,9 +30,8 @@ struct TraceSlot {
 
 struct Runtime {
   int device = -1;
-  // worker streams of their own: all S of them, or workers 1..S-1 when worker 0 is the caller's
-  // stream (TPSLICE_F_CALLER_WORKER)
-  std::vector<hipStream_t> workers, copiers;
+  // worker 0 is the caller's stream (TPSLICE_F_CALLER_WORKER): the caller passes S - 1 worker
+  // streams, else S
   int32_t first_own_worker = 0;
   hipEvent_t fork = nullptr;
   // end of the latest call on its caller's stream (TPSLICE_F_CALLER_WORKER: a call from another
@@ -41,7 +40,6 @@ struct Runtime {
   hipStream_t last_caller = nullptr;
   bool have_last = false;
   std::vector<hipEvent_t> piece;   // one per hand-off piece (and reused per call)
-  std::vector<hipEvent_t> slice;   // one per row slice: its products are done
   std::vector<hipEvent_t> lead;    // one per row slice: its first product is done
   std::vector<hipEvent_t> gather;  // one per worker stream: its queued products are done
   std::vector<hipEvent_t> join_w, join_c;
@@ -69,24 +67,23 @@ struct Runtime {
     if (e_ != hipSuccess) return fail(TPSLICE_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
   } while (0)
 
+// Every event is waited for before it is destroyed, so no queued work - on the caller's stream (a
+// one-worker plan's products, the join), a worker or a copy stream - still records or waits on
+// it. The streams belong to the caller and are left alone.
+void drop_event(hipEvent_t& e) {
+  if (!e) return;
+  (void)hipEventSynchronize(e);
+  (void)hipEventDestroy(e);
+  e = nullptr;
+}
+
 void destroy_runtime(Runtime* rt) {
   if (!rt) return;
-  // let queued work (e.g. pipelined hand-off copies) drain before the streams go away
-  for (auto s : rt->workers) (void)hipStreamSynchronize(s);
-  for (auto s : rt->copiers) (void)hipStreamSynchronize(s);
-  for (auto s : rt->workers) (void)hipStreamDestroy(s);
-  for (auto s : rt->copiers) (void)hipStreamDestroy(s);
-  if (rt->fork) (void)hipEventDestroy(rt->fork);
-  if (rt->call_done) (void)hipEventDestroy(rt->call_done);
-  for (auto e : rt->piece) (void)hipEventDestroy(e);
-  for (auto e : rt->slice) (void)hipEventDestroy(e);
-  for (auto e : rt->lead) (void)hipEventDestroy(e);
-  for (auto e : rt->gather) (void)hipEventDestroy(e);
-  for (auto e : rt->join_w) (void)hipEventDestroy(e);
-  for (auto e : rt->join_c) (void)hipEventDestroy(e);
-  for (auto e : rt->copied) (void)hipEventDestroy(e);
-  if (rt->t0) (void)hipEventDestroy(rt->t0);
-  for (auto e : rt->tpool) (void)hipEventDestroy(e);
+  drop_event(rt->fork);
+  drop_event(rt->call_done);
+  for (auto* v : {&rt->piece, &rt->lead, &rt->gather, &rt->join_w, &rt->join_c, &rt->copied, &rt->tpool})
+    for (auto& e : *v) drop_event(e);
+  drop_event(rt->t0);
   delete rt;
 }
 
@@ -101,7 +98,29 @@ tpslice_status_t make_event(hipEvent_t* e, bool local = false) {
   return TPSLICE_OK;
 }
 
-// Streams and events are created on first use, on the device current at that time.
+// The plan's events are created on its first call, on the device current at that time. A failure
+// part way leaves no runtime behind (the next call starts over).
+tpslice_status_t build_runtime(tpslice_plan_s* p, Runtime* rt) {
+  if (p->desc.flags & TPSLICE_F_SERIALIZE) return TPSLICE_OK;  // one stream, no events
+  rt->first_own_worker = (p->desc.flags & TPSLICE_F_CALLER_WORKER) ? 1 : 0;
+  rt->join_w.assign(p->S, nullptr);
+  rt->join_c.assign(p->E, nullptr);
+  rt->piece.assign(size_t(p->r) * p->c, nullptr);
+  rt->lead.assign(p->r, nullptr);
+  rt->gather.assign(p->S, nullptr);
+  rt->copied.assign(size_t(p->r) * p->E, nullptr);
+  rt->copied_pending.assign(size_t(p->r) * p->E, 0);
+  TPS_TRY_(make_event(&rt->fork, true));
+  TPS_TRY_(make_event(&rt->call_done, true));
+  for (auto& e : rt->join_w) TPS_TRY_(make_event(&e, true));
+  for (auto& e : rt->join_c) TPS_TRY_(make_event(&e));
+  for (auto& e : rt->piece) TPS_TRY_(make_event(&e));
+  for (auto& e : rt->lead) TPS_TRY_(make_event(&e, true));
+  for (auto& e : rt->gather) TPS_TRY_(make_event(&e, true));
+  for (auto& e : rt->copied) TPS_TRY_(make_event(&e));
+  return TPSLICE_OK;
+}
+
 tpslice_status_t ensure_runtime(tpslice_plan_s* p, Runtime** out) {
   int dev = -1;
   TPS_HIP(hipGetDevice(&dev));
@@ -115,39 +134,12 @@ tpslice_status_t ensure_runtime(tpslice_plan_s* p, Runtime** out) {
   rt = new (std::nothrow) Runtime();
   if (!rt) return fail(TPSLICE_ERR_INVALID, "out of host memory");
   rt->device = dev;
-  p->rt = rt;  // owned by the plan from here on, also on partial failure
-  const bool serial = p->desc.flags & TPSLICE_F_SERIALIZE;
-  if (!serial) {
-    rt->first_own_worker = (p->desc.flags & TPSLICE_F_CALLER_WORKER) ? 1 : 0;
-    for (int i = rt->first_own_worker; i < p->S; ++i) {
-      hipStream_t s;
-      TPS_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));  // default priority
-      rt->workers.push_back(s);
-    }
-    for (int i = 0; i < p->E; ++i) {
-      hipStream_t s;
-      TPS_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
-      rt->copiers.push_back(s);
-    }
-    tpslice_status_t st = make_event(&rt->fork, true);
-    if (st) return st;
-    if ((st = make_event(&rt->call_done, true))) return st;
-    rt->join_w.resize(p->S);
-    rt->join_c.resize(p->E);
-    for (auto& e : rt->join_w) if ((st = make_event(&e, true))) return st;
-    for (auto& e : rt->join_c) if ((st = make_event(&e))) return st;
-    rt->piece.resize(size_t(p->r) * p->c);
-    rt->slice.resize(p->r);
-    rt->lead.resize(p->r);
-    rt->gather.resize(p->S);
-    for (auto& e : rt->piece) if ((st = make_event(&e))) return st;
-    for (auto& e : rt->slice) if ((st = make_event(&e, true))) return st;
-    for (auto& e : rt->lead) if ((st = make_event(&e, true))) return st;
-    for (auto& e : rt->gather) if ((st = make_event(&e, true))) return st;
-    rt->copied.resize(size_t(p->r) * p->E);
-    for (auto& e : rt->copied) if ((st = make_event(&e))) return st;
-    rt->copied_pending.assign(size_t(p->r) * p->E, 0);
+  const tpslice_status_t st = build_runtime(p, rt);
+  if (st != TPSLICE_OK) {
+    destroy_runtime(rt);
+    return st;
   }
+  p->rt = rt;
   *out = rt;
   return TPSLICE_OK;
 }
@@ -160,6 +152,8 @@ struct Schedule {
   Runtime* rt;
   hipStream_t caller;
   bool serial;
+  const hipStream_t* own_workers;  // the caller's worker streams (workers first_own_worker..S-1)
+  const hipStream_t* copiers;      // the caller's copy streams (E of them), or NULL: no hand-off
   uint32_t copied = 0;  // bit k: copy stream k received a copy in this call (bit 31: caller stream)
   uint32_t slice_streams = 0;  // copy streams used by the current row slice's pieces
   int lead_slice = -1;         // row slice whose first product has not been queued yet
@@ -173,8 +167,9 @@ struct Schedule {
 
   // worker stream k: the caller's stream when serialized, or for k = 0 with TPSLICE_F_CALLER_WORKER
   hipStream_t wk(int k) const {
-    return serial || k < rt->first_own_worker ? caller : rt->workers[k - rt->first_own_worker];
+    return serial || k < rt->first_own_worker ? caller : own_workers[k - rt->first_own_worker];
   }
+  hipStream_t cp(int k) const { return copiers[k]; }
   hipStream_t worker(int i) const { return wk(i % p->S); }
   int worker_id(int i) const { return serial ? -1 : i % p->S; }
   bool pipelined() const { return !serial && (p->desc.flags & TPSLICE_F_PIPELINE); }
@@ -204,9 +199,9 @@ struct Schedule {
     if (!pipelined()) return TPSLICE_OK;
     for (int k = 0; k < p->E; ++k) {
       if (!(streams_used & (1u << k))) continue;
-      TPS_TRY_(fence(rt->copiers[k]));
+      TPS_TRY_(fence(cp(k)));
       const size_t x = size_t(i) * p->E + k;
-      TPS_HIP(hipEventRecord(rt->copied[x], rt->copiers[k]));
+      TPS_HIP(hipEventRecord(rt->copied[x], cp(k)));
       rt->copied_pending[x] = 1;
     }
     return TPSLICE_OK;
@@ -264,12 +259,12 @@ struct Schedule {
     // stream that is itself ordered after the caller's earlier work (worker 0 is the caller, the
     // others wait for the fork), so the copy streams need no fork of their own; with no other
     // worker stream there is nothing to fork.
-    const bool copier_fork = !rt->first_own_worker;
-    if (rt->workers.empty() && !copier_fork) return TPSLICE_OK;
+    const bool copier_fork = !rt->first_own_worker && copiers;
+    if (rt->first_own_worker >= p->S && !copier_fork) return TPSLICE_OK;
     TPS_HIP(hipEventRecord(rt->fork, caller));
-    for (auto s : rt->workers) TPS_HIP(hipStreamWaitEvent(s, rt->fork, 0));
+    for (int k = rt->first_own_worker; k < p->S; ++k) TPS_HIP(hipStreamWaitEvent(wk(k), rt->fork, 0));
     if (copier_fork)
-      for (auto s : rt->copiers) TPS_HIP(hipStreamWaitEvent(s, rt->fork, 0));
+      for (int k = 0; k < p->E; ++k) TPS_HIP(hipStreamWaitEvent(cp(k), rt->fork, 0));
     return TPSLICE_OK;
   }
 
@@ -284,10 +279,10 @@ struct Schedule {
       TPS_HIP(hipEventRecord(rt->join_w[k], wk(k)));
       TPS_HIP(hipStreamWaitEvent(caller, rt->join_w[k], 0));
     }
-    if (!pipelined()) {  // (pipelined: hand-off copies are joined per slice by later calls)
+    if (!pipelined() && copiers) {  // (pipelined: hand-off copies are joined per slice by later calls)
       for (int k = 0; k < p->E; ++k) {
-        if (copied & (1u << k)) TPS_TRY_(fence(rt->copiers[k]));
-        TPS_HIP(hipEventRecord(rt->join_c[k], rt->copiers[k]));
+        if (copied & (1u << k)) TPS_TRY_(fence(cp(k)));
+        TPS_HIP(hipEventRecord(rt->join_c[k], cp(k)));
         TPS_HIP(hipStreamWaitEvent(caller, rt->join_c[k], 0));
       }
     }
@@ -331,7 +326,7 @@ struct Schedule {
       for (int64_t k = 0; k < E; ++k) {
         const int64_t r0 = p->Ms * k / E, r1 = p->Ms * (k + 1) / E;
         if (r1 <= r0) continue;
-        hipStream_t cs = rt->copiers[k];
+        hipStream_t cs = cp(k);
         TPS_HIP(hipStreamWaitEvent(cs, ev, 0));
         const size_t nbytes = size_t(r1 - r0) * pitch;
         TPS_TRY_(traced(cs, p->S + int(k), TPSLICE_TRACE_COPY, TPSLICE_STEP_HANDOFF, i, j, 0.0, double(nbytes), [&] {
@@ -341,7 +336,7 @@ struct Schedule {
       }
     } else {
       const int k = int((size_t(i) * p->c + j) % p->E);
-      hipStream_t cs = rt->copiers[k];
+      hipStream_t cs = cp(k);
       TPS_HIP(hipStreamWaitEvent(cs, ev, 0));
       TPS_TRY_(traced(cs, p->S + k, TPSLICE_TRACE_COPY, TPSLICE_STEP_HANDOFF, i, j, 0.0, piece_bytes, [&] {
         TPS_HIP(hipMemcpy2DAsync(d, pitch, s, pitch, size_t(p->hc) * 2, size_t(p->Ms), kind, cs));
@@ -438,6 +433,48 @@ struct Schedule {
   }
 };
 
+// The caller's streams for one call, checked before anything is queued. With
+// TPSLICE_F_CALLER_WORKER worker 0 is the caller's stream and the caller passes S - 1 worker
+// streams, else S; a call with hand-off copies also takes E copy streams. The streams one call
+// uses must all differ. A serialized plan uses the caller's stream only.
+struct CallStreams {
+  hipStream_t caller = nullptr;
+  bool serial = false;
+  hipStream_t workers[kMaxStreams] = {};
+  hipStream_t copiers[kMaxCopyStreams] = {};
+  bool have_copiers = false;
+};
+
+tpslice_status_t call_streams(const tpslice_plan_s* p, const tpslice_streams_t* s, bool copies, CallStreams* out) {
+  out->caller = s ? static_cast<hipStream_t>(s->caller) : nullptr;
+  out->serial = p->desc.flags & TPSLICE_F_SERIALIZE;
+  if (out->serial) return TPSLICE_OK;
+  const int need_w = p->S - ((p->desc.flags & TPSLICE_F_CALLER_WORKER) ? 1 : 0);
+  const int need_c = copies ? p->E : 0;
+  const int have_w = s ? s->n_workers : 0, have_c = s ? s->n_copiers : 0;
+  if (have_w < need_w || (need_w > 0 && !s->workers))
+    return fail(TPSLICE_ERR_INVALID, "the plan runs on %d worker stream(s) of the caller's, %d given", need_w,
+                have_w);
+  if (have_c < need_c || (need_c > 0 && !s->copiers))
+    return fail(TPSLICE_ERR_INVALID, "the hand-off needs %d copy stream(s), %d given", need_c, have_c);
+  hipStream_t used[1 + kMaxStreams + kMaxCopyStreams];
+  int n = 0;
+  used[n++] = out->caller;
+  for (int k = 0; k < need_w; ++k) used[n++] = out->workers[k] = static_cast<hipStream_t>(s->workers[k]);
+  for (int k = 0; k < need_c; ++k) used[n++] = out->copiers[k] = static_cast<hipStream_t>(s->copiers[k]);
+  for (int a = 0; a < n; ++a)
+    for (int b = a + 1; b < n; ++b)
+      if (used[a] == used[b])
+        return fail(TPSLICE_ERR_INVALID, "the call's streams must differ (the caller, %d worker and %d copy "
+                    "stream(s); positions %d and %d are the same stream)", need_w, need_c, a, b);
+  out->have_copiers = need_c > 0;
+  return TPSLICE_OK;
+}
+
+Schedule schedule(tpslice_plan_s* p, Runtime* rt, const CallStreams& cs) {
+  return Schedule{p, rt, cs.caller, cs.serial, cs.workers, cs.have_copiers ? cs.copiers : nullptr};
+}
+
 GemmArgs args(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int64_t M,
               int64_t N, int64_t K) {
   GemmArgs g;
@@ -492,7 +529,7 @@ extern "C" tpslice_status_t tpslice_plan_destroy(tpslice_plan_t p) {
 
 extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, const void* W1, const void* b1,
                                             const void* W2, void* Z, void* U_save, void* Z_handoff, void* ws,
-                                            size_t ws_bytes, void* stream) {
+                                            size_t ws_bytes, const tpslice_streams_t* streams) {
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   TPS_REQ(W1); TPS_REQ(W2);
@@ -500,10 +537,12 @@ extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, con
   TPS_OPT(b1); TPS_OPT(U_save); TPS_OPT(Z_handoff);
   const MlpFwdWs L = mlp_fwd_ws(p);
   TPS_TRY(check_ws(ws, ws_bytes, L.total));
+  CallStreams cs;
+  TPS_TRY(call_streams(p, streams, Z_handoff != nullptr, &cs));
   if (p->M == 0) return TPSLICE_OK;
   Runtime* rt = nullptr;
   TPS_TRY(ensure_runtime(p, &rt));
-  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  Schedule S = schedule(p, rt, cs);
   char* H = static_cast<char*>(ws) + L.H;
   const int epi = p->desc.act == TPSLICE_ACT_GELU ? kEpiGelu : kEpiSwiglu;
   TPS_TRY(S.fork());
@@ -532,7 +571,7 @@ extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, con
 extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X, const void* Wqkv,
                                                  const void* bqkv, void* QKV, const void* C, const void* Wo,
                                                  void* Z, void* Z_handoff, void* ws, size_t ws_bytes,
-                                                 void* stream) {
+                                                 const tpslice_streams_t* streams) {
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   if (p->qh == 0) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads (n_heads = 0)");
@@ -542,10 +581,12 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
   TPS_OPT(bqkv); TPS_OPT(Z_handoff);
   const AttnFwdWs L = attn_fwd_ws(p);
   TPS_TRY(check_ws(ws, ws_bytes, L.total));
+  CallStreams cs;
+  TPS_TRY(call_streams(p, streams, Z_handoff != nullptr, &cs));
   if (p->M == 0) return TPSLICE_OK;
   Runtime* rt = nullptr;
   TPS_TRY(ensure_runtime(p, &rt));
-  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  Schedule S = schedule(p, rt, cs);
   TPS_TRY(S.fork());
   for (int i = 0; i < p->r; ++i) {
     const int64_t r0 = int64_t(i) * p->Ms;
@@ -571,7 +612,7 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
 extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, const void* W1, const void* W2,
                                             const void* U, const void* dY, void* dX, void* dX_handoff,
                                             float* dW1, float* db1, float* dW2, int32_t accumulate, void* ws,
-                                            size_t ws_bytes, void* stream) {
+                                            size_t ws_bytes, const tpslice_streams_t* streams) {
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   TPS_REQ(W1); TPS_REQ(W2); TPS_REQ(dW1); TPS_REQ(dW2);
@@ -581,9 +622,11 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
   if (accumulate != 0 && accumulate != 1) return fail(TPSLICE_ERR_INVALID, "accumulate must be 0 or 1");
   const MlpBwdWs L = mlp_bwd_ws(p);
   TPS_TRY(check_ws(ws, ws_bytes, L.total));
+  CallStreams cs;
+  TPS_TRY(call_streams(p, streams, dX_handoff != nullptr, &cs));
   Runtime* rt = nullptr;
   TPS_TRY(ensure_runtime(p, &rt));
-  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  Schedule S = schedule(p, rt, cs);
   char* dU = static_cast<char*>(ws) + L.dU;
   char* H = static_cast<char*>(ws) + L.H;
   float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
@@ -625,7 +668,7 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
 }
 
 extern "C" tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t p, const void* QKV, void* C, int64_t seq_len,
-                                                  void* stream) {
+                                                  const tpslice_streams_t* streams) {
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   if (p->M > 0) { TPS_REQ(QKV); TPS_REQ(C); } else { TPS_OPT(QKV); TPS_OPT(C); }
@@ -639,7 +682,7 @@ extern "C" tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t p, const void* 
   if (p->M == 0) return TPSLICE_OK;
   AttnArgs a{QKV, C, p->qkv, p->ctx, p->M, int32_t(seq_len), p->qh, p->kvh,
              float(1.4426950408889634 / std::sqrt(double(kAttnHeadDim)))};
-  hipError_t e = launch_attn_fwd(a, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_attn_fwd(a, streams ? static_cast<hipStream_t>(streams->caller) : nullptr);
   if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return TPSLICE_OK;
 }
@@ -648,7 +691,7 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
                                                  const void* dQKV, const void* C, const void* Wo, const void* dY,
                                                  void* dX, void* dX_handoff, void* dC, float* dWqkv,
                                                  float* dbqkv, float* dWo, int32_t accumulate, void* ws,
-                                                 size_t ws_bytes, void* stream) {
+                                                 size_t ws_bytes, const tpslice_streams_t* streams) {
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   if (p->qh == 0) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads (n_heads = 0)");
@@ -659,9 +702,11 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
   if (accumulate != 0 && accumulate != 1) return fail(TPSLICE_ERR_INVALID, "accumulate must be 0 or 1");
   const AttnBwdWs L = attn_bwd_ws(p);
   TPS_TRY(check_ws(ws, ws_bytes, L.total));
+  CallStreams cs;
+  TPS_TRY(call_streams(p, streams, dX_handoff != nullptr, &cs));
   Runtime* rt = nullptr;
   TPS_TRY(ensure_runtime(p, &rt));
-  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  Schedule S = schedule(p, rt, cs);
   float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
   TPS_TRY(S.fork());
   for (int i = 0; i < p->r && p->M > 0; ++i) {
@@ -736,25 +781,26 @@ extern "C" tpslice_status_t tpslice_handoff_wait(tpslice_plan_t p, void* stream)
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   Runtime* rt = static_cast<Runtime*>(p->rt);
-  if (!rt || rt->copiers.empty()) return TPSLICE_OK;
+  if (!rt) return TPSLICE_OK;
+  // a pipelined call leaves the end of each row slice's copies in `copied`; other calls join
+  // their copies before they return
   hipStream_t s = static_cast<hipStream_t>(stream);
-  for (int k = 0; k < p->E; ++k) {
-    hipError_t e = launch_fence(rt->copiers[k]);
-    if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "fence launch: %s", hipGetErrorString(e));
-    TPS_HIP(hipEventRecord(rt->join_c[k], rt->copiers[k]));
-    TPS_HIP(hipStreamWaitEvent(s, rt->join_c[k], 0));
-  }
+  for (size_t x = 0; x < rt->copied.size(); ++x)
+    if (rt->copied_pending[x]) TPS_HIP(hipStreamWaitEvent(s, rt->copied[x], 0));
   return TPSLICE_OK;
 }
 
-extern "C" tpslice_status_t tpslice_handoff_copy(tpslice_plan_t p, const void* src, void* dst, void* stream) {
+extern "C" tpslice_status_t tpslice_handoff_copy(tpslice_plan_t p, const void* src, void* dst,
+                                                const tpslice_streams_t* streams) {
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   if (p->M > 0) { TPS_REQ(src); TPS_REQ(dst); }
+  CallStreams cs;
+  TPS_TRY(call_streams(p, streams, true, &cs));
   if (p->M == 0) return TPSLICE_OK;
   Runtime* rt = nullptr;
   TPS_TRY(ensure_runtime(p, &rt));
-  Schedule S{p, rt, static_cast<hipStream_t>(stream), bool(p->desc.flags & TPSLICE_F_SERIALIZE)};
+  Schedule S = schedule(p, rt, cs);
   TPS_TRY(S.fork());
   for (int i = 0; i < p->r; ++i) {
     TPS_TRY(S.slice_begin(i));

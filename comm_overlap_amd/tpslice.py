@@ -1,9 +1,11 @@
 """Python binding of libtpslice.so: argument marshalling only.
 
-Every function here passes raw device pointers (`tensor.data_ptr()`) and the caller's HIP stream
+Every function here passes raw device pointers (`tensor.data_ptr()`) and HIP streams
 (`torch.cuda.Stream.cuda_stream`) to the C ABI declared in include/tpslice.h; all arithmetic runs in
-the library's HIP kernels. PyTorch provides device memory and streams. Importing this module fails
-loudly if the library has not been built; there is no fallback path.
+the library's HIP kernels. PyTorch provides device memory and streams: the worker and copy streams a
+plan runs on are torch streams, by default from a per-device set this module creates once and keeps
+for the life of the process (the library creates and destroys no stream). Importing this module
+fails loudly if the library has not been built; there is no fallback path.
 """
 from __future__ import annotations
 
@@ -72,6 +74,12 @@ class TraceRec(ctypes.Structure):
                 ("end_ms", ctypes.c_float)]
 
 
+class StreamsC(ctypes.Structure):
+    _fields_ = [("caller", ctypes.c_void_p), ("workers", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_workers", ctypes.c_int32), ("copiers", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_copiers", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m comm_overlap_amd.build`")
@@ -82,15 +90,16 @@ def _load():
     lib.tpslice_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.tpslice_plan_piece.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int64)]
     lib.tpslice_workspace_size.argtypes = [vp, i32, ctypes.POINTER(sz)]
-    lib.tpslice_mlp_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.tpslice_attnproj_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.tpslice_mlp_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
-    lib.tpslice_attnproj_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    ss = ctypes.POINTER(StreamsC)
+    lib.tpslice_mlp_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ss]
+    lib.tpslice_attnproj_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ss]
+    lib.tpslice_mlp_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, ss]
+    lib.tpslice_attnproj_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, ss]
     lib.tpslice_trace_enable.argtypes = [vp, i32]
     lib.tpslice_trace_read.argtypes = [vp, ctypes.POINTER(TraceRec), i32, ctypes.POINTER(i32)]
-    lib.tpslice_handoff_copy.argtypes = [vp, vp, vp, vp]
+    lib.tpslice_handoff_copy.argtypes = [vp, vp, vp, ss]
     lib.tpslice_handoff_wait.argtypes = [vp, vp]
-    lib.tpslice_attn_core_fwd.argtypes = [vp, vp, vp, ctypes.c_int64, vp]
+    lib.tpslice_attn_core_fwd.argtypes = [vp, vp, vp, ctypes.c_int64, ss]
     for name in EXPORTS[:14]:
         getattr(lib, name).restype = st
     lib.tpslice_error_string.argtypes = [st]
@@ -125,6 +134,59 @@ def _stream(stream) -> Optional[ctypes.c_void_p]:
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Streams:
+    """Worker and copy streams for a plan's calls (torch streams, default priority). The caller owns
+    them; the library only queues work on them. A plan takes the first n_streams (or n_streams - 1
+    when worker 0 is the caller's stream) workers and the first n_copy_streams copiers; the caller's
+    stream must not be one of them."""
+
+    def __init__(self, workers=(), copiers=()):
+        self.workers = list(workers)
+        self.copiers = list(copiers)
+
+    @classmethod
+    def new(cls, n_workers: int, n_copiers: int, device=None):
+        return cls([torch.cuda.Stream(device=device) for _ in range(n_workers)],
+                   [torch.cuda.Stream(device=device) for _ in range(n_copiers)])
+
+
+# One set per device, created on first use and kept for the life of the process.
+_POOL = {}
+
+
+def default_streams(n_workers: int, n_copiers: int, caller=None, device=None) -> Streams:
+    """The process-wide stream set of `device` (current by default), grown to at least the given
+    counts of streams that differ from `caller`."""
+    dev = torch.cuda.current_device() if device is None else torch.device(device).index
+    pool = _POOL.setdefault(dev, Streams())
+    skip = None if caller is None else caller.cuda_stream
+
+    def pick(lst, n):
+        out = [s for s in lst if s.cuda_stream != skip]
+        while len(out) < n:
+            s = torch.cuda.Stream(device=dev)
+            lst.append(s)
+            if s.cuda_stream != skip and all(s.cuda_stream != o.cuda_stream for o in out):
+                out.append(s)
+        return out[:max(n, 0)]
+
+    w = pick(pool.workers, n_workers)
+    used = {s.cuda_stream for s in w}
+    c = [s for s in pick(pool.copiers, n_copiers + len(used)) if s.cuda_stream not in used][:n_copiers]
+    return Streams(w, c)
+
+
+# Plans dropped without close() are destroyed at the next plan's construction (or by collect()),
+# not inside the garbage collector.
+_DROPPED = []
+
+
+def collect():
+    """Destroy plans that were dropped without close() (blocks until their queued work is done)."""
+    while _DROPPED:
+        lib.tpslice_plan_destroy(_DROPPED.pop())
 
 
 def _shape(t: Optional[torch.Tensor], shape, name):
@@ -168,8 +230,10 @@ class Config:
 class Plan:
     """A validated plan (host memory; streams and events are made on first use)."""
 
-    def __init__(self, cfg: Config):
+    def __init__(self, cfg: Config, streams: Optional[Streams] = None):
+        collect()
         self.cfg = cfg
+        self.streams = streams  # None: the process-wide set of the device in use at each call
         h = ctypes.c_void_p()
         d = cfg.desc()
         _check(lib.tpslice_plan(ctypes.byref(d), ctypes.byref(h)))
@@ -185,10 +249,30 @@ class Plan:
             self._h = None
 
     def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _DROPPED.append(h)
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _call_streams(self, stream=None, hand_off=True):
+        """The C stream set of one call: `stream` (default: torch's current stream) as the caller,
+        the plan's worker and copy streams after it."""
+        caller = torch.cuda.current_stream() if stream is None else stream
+        i = self.info
+        serial = self.cfg.serialize
+        n_w = 0 if serial else i.n_streams - (1 if (self.cfg.caller_worker or i.n_streams == 1) else 0)
+        n_c = 0 if serial or not hand_off else i.n_copy_streams
+        s = self.streams if self.streams is not None else default_streams(n_w, n_c, caller)
+        w = (ctypes.c_void_p * max(1, len(s.workers)))(*[x.cuda_stream for x in s.workers])
+        c = (ctypes.c_void_p * max(1, len(s.copiers)))(*[x.cuda_stream for x in s.copiers])
+        self._keep = (w, c)  # alive until the next call; the library reads them during the call only
+        return ctypes.byref(StreamsC(caller.cuda_stream, w, len(s.workers), c, len(s.copiers)))
 
     def trace(self, enable=True, products=True, copies=True):
         """Enable tracing (products and/or hand-off copies) or disable it (enable=False)."""
@@ -214,7 +298,8 @@ class Plan:
         """Only the hand-off copies of a [tokens][hidden] bf16 tensor (no products)."""
         i = self.info
         _shape(src, (i.tokens, i.hidden), "src"); _shape(dst, (i.tokens, i.hidden), "dst")
-        _check(lib.tpslice_handoff_copy(self._h, _ptr(src, name="src"), _ptr(dst, name="dst"), _stream(stream)))
+        _check(lib.tpslice_handoff_copy(self._h, _ptr(src, name="src"), _ptr(dst, name="dst"),
+                                        self._call_streams(stream)))
 
     def handoff_wait(self, stream=None):
         """Make `stream` (default: current) wait for every hand-off copy queued so far."""
@@ -258,7 +343,8 @@ class Plan:
         wp, wn = self._ws_args(ws)
         _check(lib.tpslice_mlp_fwd(self._h, _ptr(X, name="X"), _ptr(W1, name="W1"), _ptr(b1, name="b1"),
                                    _ptr(W2, name="W2"), _ptr(Z, name="Z"), _ptr(U_save, name="U_save"),
-                                   _ptr(Z_handoff, name="Z_handoff"), wp, wn, _stream(stream)))
+                                   _ptr(Z_handoff, name="Z_handoff"), wp, wn,
+                                   self._call_streams(stream, Z_handoff is not None)))
 
     def attnproj_fwd(self, X, Wqkv, bqkv, QKV, C, Wo, Z, Z_handoff=None, workspace=None, stream=None):
         i = self.info
@@ -271,7 +357,8 @@ class Plan:
         _check(lib.tpslice_attnproj_fwd(self._h, _ptr(X, name="X"), _ptr(Wqkv, name="Wqkv"),
                                         _ptr(bqkv, name="bqkv"), _ptr(QKV, name="QKV"), _ptr(C, name="C"),
                                         _ptr(Wo, name="Wo"), _ptr(Z, name="Z"),
-                                        _ptr(Z_handoff, name="Z_handoff"), wp, wn, _stream(stream)))
+                                        _ptr(Z_handoff, name="Z_handoff"), wp, wn,
+                                        self._call_streams(stream, Z_handoff is not None)))
 
     def mlp_bwd(self, X, W1, W2, U_saved, dY, dX, dW1, dW2, db1=None, dX_handoff=None, accumulate=False,
                 workspace=None, stream=None):
@@ -288,7 +375,7 @@ class Plan:
                                    _ptr(U_saved, name="U_saved"), _ptr(dY, name="dY"), _ptr(dX, name="dX"),
                                    _ptr(dX_handoff, name="dX_handoff"), _ptr(dW1, f32, "dW1"),
                                    _ptr(db1, f32, "db1"), _ptr(dW2, f32, "dW2"), int(bool(accumulate)),
-                                   wp, wn, _stream(stream)))
+                                   wp, wn, self._call_streams(stream, dX_handoff is not None)))
 
     def attn_core_fwd(self, QKV, C, seq_len, stream=None):
         """Causal attention of every sequence (seq_len consecutive token rows) and query head:
@@ -296,7 +383,7 @@ class Plan:
         i = self.info
         _shape(QKV, (i.tokens, i.qkv_width), "QKV")
         _shape(C, (i.tokens, i.ctx_width), "C")
-        _check(lib.tpslice_attn_core_fwd(self._h, _ptr(QKV), _ptr(C), int(seq_len), _stream(stream)))
+        _check(lib.tpslice_attn_core_fwd(self._h, _ptr(QKV), _ptr(C), int(seq_len), self._call_streams(stream, False)))
 
     def attnproj_bwd(self, X, Wqkv, dQKV, C, Wo, dY, dX, dC, dWqkv, dWo, dbqkv=None, dX_handoff=None,
                      accumulate=False, workspace=None, stream=None):
@@ -315,13 +402,14 @@ class Plan:
                                         _ptr(dY, name="dY"), _ptr(dX, name="dX"),
                                         _ptr(dX_handoff, name="dX_handoff"), _ptr(dC, name="dC"),
                                         _ptr(dWqkv, f32, "dWqkv"), _ptr(dbqkv, f32, "dbqkv"),
-                                        _ptr(dWo, f32, "dWo"), int(bool(accumulate)), wp, wn, _stream(stream)))
+                                        _ptr(dWo, f32, "dWo"), int(bool(accumulate)), wp, wn,
+                                        self._call_streams(stream, dX_handoff is not None)))
 
 
-def plan_for(workload, **overrides) -> Plan:
+def plan_for(workload, streams: Optional[Streams] = None, **overrides) -> Plan:
     """A plan for a synthetic workload description (comm_overlap_amd.synth.Workload)."""
     kw = dict(tokens=workload.tokens, hidden=workload.hidden, ffn=workload.ffn, tp_size=workload.tp,
               n_row_slices=workload.row_slices, n_col_slices=workload.col_slices, n_heads=workload.heads,
               n_kv_heads=workload.kv_heads, head_dim=workload.head_dim, act=workload.act)
     kw.update(overrides)
-    return Plan(Config(**kw))
+    return Plan(Config(**kw), streams)

@@ -22,16 +22,16 @@
  *     W2 [h][F'], Wqkv [(q+2kv)d][h] with rows [Q | K | V], Wo [h][q d].
  *     Activations: X, Z, dY, dX [M][h]; U [M][N1]; C, dC [M][q d]; QKV, dQKV [M][(q+2kv)d].
  *     Weight and bias gradients are fp32 in the weight's own layout.
- *   - `stream` is the caller's hipStream_t (NULL = the null stream). Calls are asynchronous and
- *     stream-ordered: they start after work already queued on `stream`, and every output (the
- *     hand-off copy included) is complete when `stream` reaches the point after the call. Internally
- *     the plan forks onto its own worker and copy streams and joins back onto `stream`.
+ *   - Streams belong to the caller (tpslice_streams_t below): the library creates and destroys no
+ *     stream. Calls are asynchronous and stream-ordered: they start after work already queued on
+ *     the caller's stream, fork onto the caller's worker and copy streams, and join back, so every
+ *     output (the hand-off copy included) is complete when the caller's stream reaches the point
+ *     after the call (TPSLICE_F_PIPELINE relaxes this for the hand-off copies only).
  *   - Outputs must not alias inputs or each other. Results are deterministic: the same plan and
  *     inputs give bitwise identical outputs, whatever the slice timing.
  *   - Errors are reported by status code only; argument, shape and workspace errors are detected
  *     before any GPU work is queued. tpslice_last_error() gives the text of the calling thread's last
- *     failure. A plan must not be used from two host threads at once, nor destroyed while its work
- *     is still in flight.
+ *     failure. A plan must not be used from two host threads at once.
  */
 #ifndef TPSLICE_H
 #define TPSLICE_H
@@ -136,6 +136,23 @@ typedef struct {
 
 typedef struct tpslice_plan_s* tpslice_plan_t;
 
+/* The streams of one call (all hipStream_t, passed as void*). The caller owns them; the library only
+ * queues work on them and records and waits on events of its own plan. With TPSLICE_F_CALLER_WORKER
+ * (always set for a plan with one worker stream) worker 0 is `caller` and `workers` holds the other
+ * n_streams - 1, else all n_streams (tpslice_plan_info reports n_streams and n_copy_streams; extra
+ * entries are ignored). A call that hands off (a non-NULL hand-off buffer, tpslice_handoff_copy)
+ * also takes n_copy_streams copy streams. The streams one call uses must all differ. A serialized
+ * plan (TPSLICE_F_SERIALIZE) uses `caller` only. A NULL tpslice_streams_t* means the null stream
+ * as caller and no other streams. Different calls of one plan may use different streams.          */
+typedef struct {
+  void* caller;            /* the stream the call is ordered on (NULL: the null stream)               */
+  void* const* workers;    /* worker streams for the row slices                                        */
+  int32_t n_workers;
+  void* const* copiers;    /* side streams for the hand-off copies                                     */
+  int32_t n_copiers;
+} tpslice_streams_t;
+
+
 typedef struct {
   int64_t tokens, hidden, ffn_shard, n1, qkv_width, ctx_width;
   int64_t rows_per_slice;       /* M / r                                                             */
@@ -166,7 +183,8 @@ typedef enum {
  * not divide or are not multiples of 8, or whose operands exceed 4 GiB. On error *out is NULL.     */
 TPSLICE_API tpslice_status_t tpslice_plan(const tpslice_desc_t* desc, tpslice_plan_t* out);
 
-/* Release the plan, its streams and events. NULL is a no-op. Work in flight must have finished.   */
+/* Release the plan and its events. NULL is a no-op. Blocks until the plan's queued work (products,
+ * hand-off copies) has finished, so it may be called with work in flight; no stream is touched.   */
 TPSLICE_API tpslice_status_t tpslice_plan_destroy(tpslice_plan_t plan);
 
 /* Sizes the plan derived from its descriptor.                                                     */
@@ -179,7 +197,10 @@ TPSLICE_API tpslice_status_t tpslice_plan_piece(tpslice_plan_t plan, int32_t ind
 /* Bytes of device workspace that `op` needs (may be 0). Workspace must be 256-byte aligned.       */
 TPSLICE_API tpslice_status_t tpslice_workspace_size(tpslice_plan_t plan, int32_t op, size_t* bytes);
 
-/* MLP forward (one rank's share).
+/* MLP forward (one rank's share). Defined by: the Megatron-LM layer that Domino starts from (Domino
+ * page, Abstract, and its builds-on list: "Megatron-LM", "GLU Variants Improve Transformer" for
+ * SwiGLU), cut into the independent pieces whose hand-off overlaps later pieces' computation (Domino
+ * page, Abstract) with communication offloaded to DMA engines (FiCCO page, Abstract).
  *   U = X W1^T + b1;  H = act(U);  Z = H W2^T   (Z: this rank's partial sum, no row-parallel bias)
  * Inputs : X [M][h], W1 [N1][h], b1 [N1] bf16 or NULL, W2 [h][F'].
  * Outputs: Z [M][h] bf16; U_save [M][N1] bf16 or NULL (pre-activation kept for the backward pass);
@@ -188,18 +209,23 @@ TPSLICE_API tpslice_status_t tpslice_workspace_size(tpslice_plan_t plan, int32_t
  * Workspace: tpslice_workspace_size(TPSLICE_OP_MLP_FWD) bytes (holds H).                          */
 TPSLICE_API tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t plan, const void* X, const void* W1, const void* b1,
                                  const void* W2, void* Z, void* U_save, void* Z_handoff,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 void* workspace, size_t workspace_bytes, const tpslice_streams_t* streams);
 
-/* Attention input/output projections, forward (one rank's heads).
+/* Attention input/output projections, forward (one rank's heads). Defined by: the same Megatron-LM
+ * split applied to the attention block's projections, sliced and handed off as the MLP's (Domino
+ * page, Abstract).
  *   QKV = X Wqkv^T (+ bqkv)   column-parallel;   Z = C Wo^T   row-parallel partial sum
- * C is the attention context of this rank's heads (an input: the attention core is not part of this
- * library). Z_handoff as in tpslice_mlp_fwd. Needs n_heads > 0 in the plan.                       */
+ * C is the attention context of this rank's heads (an input here; tpslice_attn_core_fwd computes it
+ * from QKV). Z_handoff as in tpslice_mlp_fwd. Needs n_heads > 0 in the plan.                      */
 TPSLICE_API tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t plan, const void* X, const void* Wqkv,
                                       const void* bqkv, void* QKV, const void* C, const void* Wo,
                                       void* Z, void* Z_handoff, void* workspace,
-                                      size_t workspace_bytes, void* stream);
+                                      size_t workspace_bytes, const tpslice_streams_t* streams);
 
-/* MLP backward, given the saved pre-activation U [M][N1] and the upstream gradient dY [M][h]:
+/* MLP backward. Defined by: the gradient of tpslice_mlp_fwd (chain rule), the backward pass whose
+ * tensor-parallel communication the pages hide the same way as the forward's (Domino page, Abstract;
+ * the micro-batch co-execution review, "What carries the argument": forward of one micro-batch beside
+ * the backward of another). Given the saved pre-activation U [M][N1] and upstream gradient dY [M][h]:
  *   dH = dY W2;  dU = dH * act'(U) (SwiGLU: [dH V silu'(G) | dH silu(G)]);  dX = dU W1
  *   dW1 (+)= dU^T X;  db1 (+)= column sums of dU;  dW2 (+)= dY^T act(U)
  * dX [M][h] bf16 is this rank's partial sum and the hand-off tensor (dX_handoff as Z_handoff above).
@@ -208,17 +234,19 @@ TPSLICE_API tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t plan, const voi
 TPSLICE_API tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t plan, const void* X, const void* W1, const void* W2,
                                  const void* U_saved, const void* dY, void* dX, void* dX_handoff,
                                  float* dW1, float* db1, float* dW2, int32_t accumulate,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 void* workspace, size_t workspace_bytes, const tpslice_streams_t* streams);
 
-/* Attention projections backward, given dQKV [M][(q+2kv)d] (from the attention core) and dY [M][h]
- * (into the output projection):
+/* Attention projections backward. Defined by: the gradient of tpslice_attnproj_fwd (chain rule),
+ * sliced and handed off as tpslice_mlp_bwd. Given dQKV [M][(q+2kv)d] (from the attention core) and
+ * dY [M][h] (into the output projection):
  *   dC = dY Wo;  dWo (+)= dY^T C;  dX = dQKV Wqkv (partial sum, hand-off);  dWqkv (+)= dQKV^T X;
  *   dbqkv (+)= column sums of dQKV (or NULL).  dC bf16; weight/bias gradients fp32.              */
 TPSLICE_API tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t plan, const void* X, const void* Wqkv,
                                       const void* dQKV, const void* C, const void* Wo,
                                       const void* dY, void* dX, void* dX_handoff, void* dC,
                                       float* dWqkv, float* dbqkv, float* dWo, int32_t accumulate,
-                                      void* workspace, size_t workspace_bytes, void* stream);
+                                      void* workspace, size_t workspace_bytes,
+                                      const tpslice_streams_t* streams);
 
 /* Causal attention core between the two projections, forward (the tiled softmax attention of the
  * FlashAttention titles on the Domino page's builds-on list, computed exactly up to rounding):
@@ -229,9 +257,9 @@ TPSLICE_API tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t plan, const voi
  * Outputs: C [M][q head_dim] bf16, the context the output projection reads.
  * Requires the plan's head_dim = 128 (else TPSLICE_ERR_UNSUPPORTED), seq_len a multiple of 128
  * that divides the token count (else TPSLICE_ERR_SHAPE). Softmax in fp32; the probabilities are
- * rounded to bf16 for the product with V. Runs on `stream` (no slicing, no hand-off). */
+ * rounded to bf16 for the product with V. Runs on streams->caller (no slicing, no hand-off).      */
 TPSLICE_API tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t plan, const void* QKV, void* C, int64_t seq_len,
-                                       void* stream);
+                                       const tpslice_streams_t* streams);
 
 /* Tracing. When enabled, every product and every hand-off copy is bracketed by timing events on
  * the stream it runs on. Records accumulate over calls until they are read; times are milliseconds
@@ -280,7 +308,7 @@ TPSLICE_API tpslice_status_t tpslice_trace_read(tpslice_plan_t plan, tpslice_tra
  * hands off its partial sums (same pieces, copy streams and engines), with no products. This is the
  * communication-only run that the overlap measurement compares against.                         */
 TPSLICE_API tpslice_status_t tpslice_handoff_copy(tpslice_plan_t plan, const void* src, void* dst,
-                                                  void* stream);
+                                                  const tpslice_streams_t* streams);
 
 /* Make `stream` wait until every hand-off copy the plan has queued so far is complete (needed only
  * with TPSLICE_F_PIPELINE; a no-op before the plan's first call).                                */

@@ -148,7 +148,9 @@ def test_two_strands_match_separate_calls(mode):
         kw = dict(pipeline=True, caller_worker=True, n_streams=1, n_copy_streams=1)
     else:
         kw = dict(serialize=True, copy_blit=mode == "kernel")
-    fwd_plan, bwd_plan = T.plan_for(w, **kw), T.plan_for(w, **kw)
+    # each strand's plan has copy streams of its own, so that the two strands' copies overlap
+    fwd_plan = T.plan_for(w, streams=T.Streams.new(0, 1), **kw)
+    bwd_plan = T.plan_for(w, streams=T.Streams.new(0, 1), **kw)
 
     def forward(sync):
         return G.run_attn_fwd(fwd_plan, inp, sync=sync), G.run_mlp_fwd(fwd_plan, inp, sync=sync)
