@@ -10,12 +10,19 @@ the plan pipelines the hand-off: row slice i of a call waits only for row slice 
 call's hand-off, so a call's last copies overlap the next call's first products. Inputs are
 synthetic, seeded, and resident in HBM before timing starts.
 
+Order of a run: W warm-up steps; R rounds of five legs taken in alternation (the pipelined chain,
+the same chain without hand-off copies, the hand-off copies alone, isolated calls with and without
+copies), which give the wall form of the hidden copy time from the legs' medians and also bring the
+clocks to steady state; then the K timed steps of the headline; then the same K steps traced (every
+product's launch timed by HIP events that the dispatches record themselves, on the streams they run
+on), and traced again with the copies, for the trace form of the hidden copy time (the share of the
+copies' time during which a product ran) in steady state and for isolated calls.
+
 Prints ONE JSON line: TFLOP/s (algorithmic 2*M*N*K flops of every product / wall time of the K
-timed steps), the fraction of the dense bf16 MFMA peak, the fraction of hand-off copy time hidden
-behind compute (steady state, and for an isolated call), the roofline of the dominant kernel (a
-second pass over the same K steps times every launch with HIP events recorded by the dispatches
-themselves, on the streams they ran on), and the fp64 CPU oracle timed on the host's cores (a
-baseline, not a target).
+timed steps), the fraction of the dense bf16 MFMA peak, the hidden copy time (trace form as the
+headline, wall form beside it), the roofline of the dominant product (the largest share of the
+step's product time), and the fp64 CPU oracle timed on the host's cores over a bounded row sample
+(a baseline, not a target).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload KEY]
 """
@@ -29,14 +36,16 @@ import time
 
 METRIC = "TFLOP/s and % of bf16 MFMA peak per TP-shard layer; % copy time hidden"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-DEFAULT_WORKLOAD = "gpt3_2.7b_mlp"
+DEFAULT_WORKLOAD = "llama3_70b_layer"
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rounds", type=int, default=5,
+                    help="rounds of the alternating hand-off legs (wall form of the hidden copy time)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--streams", type=int, default=0, help="worker streams (0 = plan default)")
     ap.add_argument("--copy-streams", type=int, default=0, help="copy streams (0 = plan default)")
@@ -68,9 +77,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CALIB_BYTES = 256 << 20
 
 
-def recorded_traffic(workload):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary, if that
-    summary was taken on the current GEMM source (else None)."""
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` (template parameters and grid) from the committed counter
+    summary of this workload, if that summary covers this kernel and was taken on the current GEMM
+    source (else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"gemm_kernel_{workload}_traffic.txt")
     src = os.path.join(ROOT, "comm_overlap_amd", "csrc", "gemm.hip")
@@ -82,7 +92,9 @@ def recorded_traffic(workload):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("gemm.hip sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("gemm.hip sha256") != sha or fields.get("kernel") != kernel:
+        return None
+    if "traffic_bytes_per_launch" not in fields:
         return None
     return float(fields["traffic_bytes_per_launch"])
 
@@ -93,34 +105,39 @@ def log(*a):
 
 class Chain:
     """Device buffers and calls of chained steps. Step n writes hand-off buffer set n % 2 and reads
-    the other set as its input, as consecutive layers would."""
+    the other set as its input, as consecutive layers would. `dev`: the workload's inputs in HBM
+    (shared by every chain); `share`: another chain whose activation buffers and gradients this one
+    reuses (legs that never run at the same time)."""
 
-    def __init__(self, w, plan, inp, handoff=True):
+    def __init__(self, w, plan, dev, handoff=True, share=None):
         import torch
-        self.w, self.plan, self.handoff = w, plan, handoff
-        self.t = {k: v.to("cuda").contiguous() for k, v in inp.items()}
+        self.w, self.plan, self.handoff, self.t = w, plan, handoff, dev
         i = plan.info
         bf, f32 = torch.bfloat16, torch.float32
         e = lambda *s, dt=bf: torch.empty(*s, dtype=dt, device="cuda")
-        self.sets = []
-        for _ in range(2):
-            o = {"Z": e(i.tokens, i.hidden), "Zh": e(i.tokens, i.hidden), "U": e(i.tokens, i.n1)}
-            if w.has_attn:
-                o.update(QKV=e(i.tokens, i.qkv_width), Za=e(i.tokens, i.hidden), Zah=e(i.tokens, i.hidden))
-            if w.backward:
-                o.update(dX=e(i.tokens, i.hidden), dXh=e(i.tokens, i.hidden))
+        if share is not None:
+            self.sets, self.g = share.sets, share.g
+        else:
+            self.sets = []
+            for _ in range(2):
+                o = {"Z": e(i.tokens, i.hidden), "Zh": e(i.tokens, i.hidden), "U": e(i.tokens, i.n1)}
                 if w.has_attn:
-                    o.update(dXa=e(i.tokens, i.hidden), dXah=e(i.tokens, i.hidden), dC=e(i.tokens, i.ctx_width))
-            self.sets.append(o)
-        # the chain's first input is the seeded X; later steps read the previous step's output
-        for o in self.sets:
-            o["Zh"].copy_(self.t["X" if w.has_attn else "X_mlp"])
-            o["Z"].copy_(o["Zh"])
-        self.g = {"dW1": e(i.n1, i.hidden, dt=f32), "dW2": e(i.hidden, i.ffn_shard, dt=f32)}
-        if w.bias:
-            self.g["db1"] = e(i.n1, dt=f32)
-        if w.has_attn:
-            self.g.update(dWqkv=e(i.qkv_width, i.hidden, dt=f32), dWo=e(i.hidden, i.ctx_width, dt=f32))
+                    o.update(QKV=e(i.tokens, i.qkv_width), Za=e(i.tokens, i.hidden), Zah=e(i.tokens, i.hidden))
+                if w.backward:
+                    o.update(dX=e(i.tokens, i.hidden), dXh=e(i.tokens, i.hidden))
+                    if w.has_attn:
+                        o.update(dXa=e(i.tokens, i.hidden), dXah=e(i.tokens, i.hidden),
+                                 dC=e(i.tokens, i.ctx_width))
+                self.sets.append(o)
+            # the chain's first input is the seeded X; later steps read the previous step's output
+            for o in self.sets:
+                o["Zh"].copy_(self.t["X" if w.has_attn else "X_mlp"])
+                o["Z"].copy_(o["Zh"])
+            self.g = {"dW1": e(i.n1, i.hidden, dt=f32), "dW2": e(i.hidden, i.ffn_shard, dt=f32)}
+            if w.bias:
+                self.g["db1"] = e(i.n1, dt=f32)
+            if w.has_attn:
+                self.g.update(dWqkv=e(i.qkv_width, i.hidden, dt=f32), dWo=e(i.hidden, i.ctx_width, dt=f32))
         for op in range(4):
             plan.workspace(op)
         self.n = 0
@@ -172,7 +189,7 @@ class TwoStrands:
     pipelined plan whose worker is the strand's stream and whose DMA copies run on a copy stream
     of its own (four streams in all, one per hardware queue)."""
 
-    def __init__(self, w, inp, kw, mode):
+    def __init__(self, w, dev, kw, mode):
         import torch
         from comm_overlap_amd import tpslice as T
         self.w, self.mode = w, mode
@@ -183,8 +200,8 @@ class TwoStrands:
         # each strand's plan has worker and copy streams of its own
         self.fwd_plan = T.plan_for(w, streams=T.Streams.new(1, 1), **kw)
         self.bwd_plan = T.plan_for(w, streams=T.Streams.new(1, 1), **kw)
-        self.chain = Chain(w, self.fwd_plan, inp)  # activation and output buffers of both sets
-        self.bwd_ws = Chain(w, self.bwd_plan, inp)  # the backward plan's workspaces and gradients
+        self.chain = Chain(w, self.fwd_plan, dev)  # activation and output buffers of both sets
+        self.bwd_ws = Chain(w, self.bwd_plan, dev, share=self.chain)  # the backward plan's workspaces
         self.sa, self.sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
         self.fwd_done = [torch.cuda.Event(), torch.cuda.Event()]
         self.bwd_done = [torch.cuda.Event(), torch.cuda.Event()]
@@ -230,33 +247,73 @@ class TwoStrands:
         self.bwd_plan.handoff_wait()
 
 
-def timed(fn, steps, warmup, plan=None):
-    """Wall time per step of `steps` back-to-back calls, bracketed by full synchronization."""
+def timed(fn, steps, warmup, plans=()):
+    """Wall time per step of `steps` back-to-back calls, bracketed by full synchronization (and by
+    waits for the pipelined hand-off copies of `plans`)."""
     import torch
     for _ in range(warmup):
         fn()
-    if plan is not None:
-        plan.handoff_wait()
+    for p in plans:
+        p.handoff_wait()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         fn()
-    if plan is not None:
-        plan.handoff_wait()
+    for p in plans:
+        p.handoff_wait()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / max(1, steps)
 
 
-def kernel_stats(recs):
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def kernel_stats(recs, key):
+    """GEMM launches grouped by `key` ("step": the product; "kernel": the kernel's identity, i.e.
+    its template parameters and grid, as a kernel profiler groups dispatches)."""
     by = {}
     for r in recs:
-        if r["kind"] == "copy":
+        if r["kind"] != "gemm":
             continue
-        d = by.setdefault(r["step"], {"n": 0, "ms": 0.0, "flops": 0.0})
+        d = by.setdefault(r[key], {"n": 0, "ms": 0.0, "flops": 0.0, "steps": set(), "grid_x": r["grid_x"]})
         d["n"] += 1
         d["ms"] += r["end_ms"] - r["start_ms"]
         d["flops"] += r["flops"]
+        d["steps"].add(r["step"])
     return by
+
+
+def union(iv):
+    out = []
+    for s, e in sorted(iv):
+        if out and s <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], e)
+        else:
+            out.append([s, e])
+    return out
+
+
+def hidden_from_trace(recs):
+    """The trace form of the hidden hand-off: the share of the copies' time during which at least
+    one product ran, from the plan's own events (copy intervals from the copy stream reaching the
+    copy to the fence after it; product intervals from the dispatches' own timestamps)."""
+    busy = union([(r["start_ms"], r["end_ms"]) for r in recs if r["kind"] != "copy"])
+    tot = hid = 0.0
+    for r in recs:
+        if r["kind"] != "copy":
+            continue
+        s, e = r["start_ms"], r["end_ms"]
+        tot += e - s
+        for a, b in busy:
+            if b <= s:
+                continue
+            if a >= e:
+                break
+            hid += min(e, b) - max(s, a)
+    return (hid / tot if tot > 0 else None), tot
 
 
 def attn_core(w, inp, seq_len, steps):
@@ -348,6 +405,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     log(f"workload {w.key}: generating inputs")
     inp = synth.make_inputs(w)
+    dev = {k: v.to("cuda").contiguous() for k, v in inp.items()}
     flops = sum(w.gemm_flops().values())
     kw = dict(n_streams=args.streams, n_copy_streams=args.copy_streams, copy_blit=args.copy_blit, tile=args.tile,
               handoff_rows=not args.handoff_pieces, caller_worker=args.caller_worker)
@@ -355,76 +413,93 @@ def main():
         kw["n_row_slices"] = args.row_slices
     if args.col_slices:
         kw["n_col_slices"] = args.col_slices
-    plan = T.plan_for(w, pipeline=True, **kw)
-    chain = Chain(w, plan, inp)
-    torch.cuda.synchronize()
-
-    # 1) headline: K chained steps with the pipelined hand-off, untraced
-    log(f"warmup {args.warmup}")
-    timed(chain, 0, args.warmup, plan)
-    log(f"timed region: {args.steps} steps")
-    ms = timed(chain, args.steps, 0, plan)
-    # the same K steps again with every product's launch timed by HIP events recorded by the
-    # dispatches themselves (on the streams they run on): the roofline's per-launch durations
-    log(f"traced pass: {args.steps} steps")
-    plan.trace(True, products=True, copies=False)
-    ms_traced = timed(chain, args.steps, 0, plan)
-    recs = plan.trace_read()
-    plan.trace(False)
-    by = kernel_stats(recs)
-
-    # 2) the same chain without hand-off copies, and the hand-off copies alone. The copies alone
-    # run through a plan without pipelining: every piece's copy back to back on the copy streams,
-    # one completion fence per call (the pipelined plan closes every row slice's copies with a
-    # fence of its own, whose latency would inflate the copy time the chain has to hide).
-    log("compute only / copies only")
-    nocopy = Chain(w, plan, inp, handoff=False)
-    ms_comp = timed(nocopy, args.steps, 2, plan)
-    del nocopy
+    plan = T.plan_for(w, pipeline=True, **kw)  # the headline: chained steps, pipelined hand-off
+    jplan = T.plan_for(w, **kw)                # every call joined: isolated calls, copies alone
+    chain = Chain(w, plan, dev)
+    nocopy = Chain(w, plan, dev, handoff=False, share=chain)
+    jchain = Chain(w, jplan, dev, share=chain)
+    jnocopy = Chain(w, jplan, dev, handoff=False, share=chain)
     pairs = chain.handoff_tensors()
-    ms_copy_sliced = timed(lambda: [plan.handoff_copy(s, d) for s, d in pairs], args.steps, 2, plan)
-    # the process has few hardware queues (four by default): release this plan's streams before
-    # the second plan creates its own, so that no two streams share a queue
+
+    def copies():
+        for s, d in pairs:
+            jplan.handoff_copy(s, d)
+
+    torch.cuda.synchronize()
+    K = args.steps
+    log(f"warmup {args.warmup}")
+    timed(chain, 0, args.warmup, [plan])
+
+    # 1) the wall form of the hidden hand-off, from legs taken in alternation over several rounds
+    # (medians): the pipelined chain, the same chain without hand-off copies, the copies alone, and
+    # the same pair for isolated (joined) calls. These legs also bring the clocks to steady state
+    # before the headline.
+    rounds = max(1, args.rounds)
+    log(f"hand-off legs: {rounds} rounds x 5 legs x {K} steps")
+    legs = {k: [] for k in ("chain", "nocopy", "copies", "iso", "iso_nocopy")}
+    for _ in range(rounds):
+        legs["chain"].append(timed(chain, K, 1, [plan]))
+        legs["nocopy"].append(timed(nocopy, K, 1, [plan]))
+        legs["copies"].append(timed(copies, K, 1, [jplan]))
+        legs["iso"].append(timed(jchain, K, 1))
+        legs["iso_nocopy"].append(timed(jnocopy, K, 1))
+    med = {k: median(v) for k, v in legs.items()}
+    hw = lambda a, b: max(0.0, min(1.0, 1.0 - (a - b) / med["copies"])) if med["copies"] > 0 else None
+    hidden_wall = hw(med["chain"], med["nocopy"])
+    hidden_wall_single = hw(med["iso"], med["iso_nocopy"])
+
+    # 2) headline: K chained steps with the pipelined hand-off, untraced
+    log(f"timed region: {K} steps")
+    ms = timed(chain, K, 0, [plan])
+
+    # 3) the same K steps with every product's launch timed by HIP events that the dispatches record
+    # themselves, on the streams they run on: the roofline's per-launch durations
+    log(f"traced pass (products): {K} steps")
+    plan.trace(True, products=True, copies=False)
+    ms_traced = timed(chain, K, 0, [plan])
+    recs = plan.trace_read()
+    by = kernel_stats(recs, "step")
+    by_kernel = kernel_stats(recs, "kernel")
+    # 4) products and copies traced: the trace form of the hidden hand-off, in steady state (the
+    # pipelined chain) and for isolated calls (each call joined)
+    log(f"traced pass (products and copies): {K} steps, chained and isolated")
+    plan.trace(True, products=True, copies=True)
+    timed(chain, K, 0, [plan])
+    hidden_trace, copy_ms = hidden_from_trace(plan.trace_read())
+    plan.trace(False)
+    jplan.trace(True, products=True, copies=True)
+    timed(jchain, K, 0)
+    hidden_trace_single, _ = hidden_from_trace(jplan.trace_read())
+    jplan.trace(False)
     info = plan.info
-    plan.close()
-    jplan = T.plan_for(w, **kw)
-    ms_copy = timed(lambda: [jplan.handoff_copy(s, d) for s, d in pairs], args.steps, 2)
-    hidden = max(0.0, min(1.0, 1.0 - (ms - ms_comp) / ms_copy)) if ms_copy > 0 else None
 
-    # 3) an isolated call (full join, nothing after it to hide the last pieces' copies)
-    log("isolated calls")
-    jchain = Chain(w, jplan, inp)
-    jnocopy = Chain(w, jplan, inp, handoff=False)
-    ms_j = timed(jchain, max(5, args.steps // 4), 2)
-    ms_jc = timed(jnocopy, max(5, args.steps // 4), 2)
-    hidden_single = max(0.0, min(1.0, 1.0 - (ms_j - ms_jc) / ms_copy)) if ms_copy > 0 else None
-    del jchain, jnocopy
-
-    # 4) optional: two micro-batches in flight (forward of one beside backward of the other)
+    # 5) optional: two micro-batches in flight (forward of one beside backward of the other)
     two = None
     if args.strands == 2 and w.backward:
         log("two strands")
-        jplan.handoff_wait()
-        torch.cuda.synchronize()
-        jplan.close()  # its streams, so that the two strands' streams have queues of their own
         two = {}
         for mode in ("pipelined", "dma", "kernel"):
-            ts = TwoStrands(w, inp, kw, mode)
-            ms_two = timed(ts, args.steps, max(2, args.warmup), ts)
+            ts = TwoStrands(w, dev, kw, mode)
+            ms_two = timed(ts, K, max(2, args.warmup), [ts.fwd_plan, ts.bwd_plan])
             two[mode] = {"ms_per_step": round(ms_two, 4), "tflops": round(flops / (ms_two * 1e-3) / 1e12, 2),
                          "speedup_vs_one_strand": round(ms / ms_two, 3)}
+            ts.fwd_plan.close()
+            ts.bwd_plan.close()
             del ts
 
     tflops = flops / (ms * 1e-3) / 1e12
-    dom_name, dom = max(by.items(), key=lambda kv: kv[1]["ms"])
+    # the dominant kernel: the GEMM kernel (template parameters and grid) with the largest share of
+    # the step's product time; its launches may serve more than one product of that grid
+    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
     dom_ms = dom["ms"] / dom["n"]
     achieved = dom["flops"] / dom["n"] / (dom_ms * 1e-3) / 1e12
+    pct = lambda x: None if x is None else round(100.0 * x, 1)
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
@@ -440,19 +515,21 @@ def main():
                    "tile": args.tile,
                    "handoff": "blit" if args.copy_blit else (
                        "dma, whole row slices" if not args.handoff_pieces and info.n_col_slices > 1
-                                                              else "dma"), "chain": "pipelined"},
+                       else "dma"), "chain": "pipelined"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "hidden_copy_pct": None if hidden is None else round(100.0 * hidden, 1),
-        "hidden_copy_pct_single_call": None if hidden_single is None else round(100.0 * hidden_single, 1),
+        "hidden_copy_pct": pct(hidden_trace),
+        "hidden_copy_pct_single_call": pct(hidden_trace_single),
+        "hidden_copy_wall_pct": pct(hidden_wall),
+        "hidden_copy_wall_pct_single_call": pct(hidden_wall_single),
+        "handoff_copy_ms_per_step_traced": round(copy_ms / max(1, K), 4),
+        "legs_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "legs_rounds": rounds,
         "ms_per_step_traced": round(ms_traced, 4),
-        "ms_per_step_without_handoff": round(ms_comp, 4),
-        "ms_handoff_copies_alone": round(ms_copy, 4),
-        "ms_handoff_copies_alone_per_slice_fences": round(ms_copy_sliced, 4),
-        "ms_per_isolated_call": round(ms_j, 4),
-        "roofline": {"bound": "mfma", "kernel": f"gemm_kernel ({dom_name})", "achieved": round(achieved, 1),
+        "roofline": {"bound": "mfma", "kernel": dom_name, "products": sorted(dom["steps"]),
+                     "grid_x": dom["grid_x"], "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic(w.key), "launches": dom["n"],
-                     "avg_launch_ms": round(dom_ms, 4)},
+                     "traffic": recorded_traffic(w.key, dom_name), "launches_per_step": dom["n"] / K,
+                     "avg_launch_ms": round(dom_ms, 4), "flops_per_launch": dom["flops"] / dom["n"]},
         "kernels": {k: {"launches": v["n"], "avg_ms": round(v["ms"] / v["n"], 4),
                         "tflops": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 1)} for k, v in by.items()},
     }
@@ -460,12 +537,11 @@ def main():
         out["two_strands"] = two
     if w.has_attn and not args.no_attn_core:
         log("attention core")
-        out["attn_core"] = attn_core(w, inp, args.attn_seq, args.steps)
+        out["attn_core"] = attn_core(w, inp, args.attn_seq, K)
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
-    if two is None:
-        jplan.handoff_wait()
+    plan.handoff_wait()
     torch.cuda.synchronize()
     if args.calib_copy:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -473,6 +549,8 @@ def main():
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)  # elementwise kernel: reads and writes CALIB_BYTES
         torch.cuda.synchronize()
+    plan.close()
+    jplan.close()
     print(json.dumps(out), flush=True)
     return 0
 

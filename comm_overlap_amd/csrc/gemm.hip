@@ -1046,6 +1046,8 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* partials
 
 __global__ void fence_kernel() {}
 
+thread_local LaunchInfo g_last_launch;
+
 template <class TL, int L, int E>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   static const hipError_t attr =
@@ -1053,6 +1055,7 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEve
                           hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLdsBytes);
   if (attr != hipSuccess) return attr;
   const int grid = g.tiles_m * g.tiles_n * g.splits;
+  g_last_launch = LaunchInfo{TL::BM, TL::BN, TL::kWavesM, TL::kWavesN, TL::kBlocksPerCU, L, E, grid, TL::kThreads};
   if (start || stop)
     hipExtLaunchKernelGGL((gemm_kernel<TL, L, E>), dim3(grid), dim3(TL::kThreads), TL::kLdsBytes, s, start, stop,
                           0, g);
@@ -1064,21 +1067,23 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEve
 // The fp32 partial product of a split product (256 x 256 tiles; the four-wave pipelined ones when
 // K is a multiple of 64 and `pipe` allows it; either gives the same bits).
 template <class TL>
-hipError_t launch_partial_tile(GemmArgs& g, int layout, bool dual, hipStream_t stream, hipEvent_t start) {
+hipError_t launch_partial_tile(GemmArgs& g, int layout, bool dual, hipStream_t stream, hipEvent_t start,
+                               hipEvent_t stop) {
   const int out_bn = dual ? TL::BN / 2 : TL::BN;
   g.tiles_m = (g.M + TL::BM - 1) / TL::BM;
   g.tiles_n = (g.N + out_bn - 1) / out_bn;
-  if (dual) return launch_one<TL, kFwd, kEpiPartialDual>(g, stream, start, nullptr);
+  if (dual) return launch_one<TL, kFwd, kEpiPartialDual>(g, stream, start, stop);
   switch (layout) {
-    case kFwd: return launch_one<TL, kFwd, kEpiF32>(g, stream, start, nullptr);
-    case kDgrad: return launch_one<TL, kDgrad, kEpiF32>(g, stream, start, nullptr);
-    case kWgrad: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, nullptr);
+    case kFwd: return launch_one<TL, kFwd, kEpiF32>(g, stream, start, stop);
+    case kDgrad: return launch_one<TL, kDgrad, kEpiF32>(g, stream, start, stop);
+    case kWgrad: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, stop);
     default: return hipErrorInvalidValue;
   }
 }
-hipError_t launch_partial(GemmArgs& g, int layout, bool dual, bool pipe, hipStream_t stream, hipEvent_t start) {
-  if (pipe && g.K > 0 && g.K % 64 == 0) return launch_partial_tile<TileL4>(g, layout, dual, stream, start);
-  return launch_partial_tile<TileL>(g, layout, dual, stream, start);
+hipError_t launch_partial(GemmArgs& g, int layout, bool dual, bool pipe, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
+  if (pipe && g.K > 0 && g.K % 64 == 0) return launch_partial_tile<TileL4>(g, layout, dual, stream, start, stop);
+  return launch_partial_tile<TileL>(g, layout, dual, stream, start, stop);
 }
 
 template <class TL>
@@ -1290,8 +1295,8 @@ hipError_t launch_split_epilogue(const GemmArgs& g, const float* P, int splits, 
   const int64_t vecs = int64_t(g.M) * (g.N / 4);
   const int blocks = int(std::min<int64_t>((vecs + 255) / 256, int64_t(4) * kCUs));
   if (stop)
-    hipExtLaunchKernelGGL(split_epilogue_kernel<EPI>, dim3(blocks), dim3(256), 0, s, nullptr, stop, 0, g, P, splits,
-                          stride, ldp);
+    hipExtLaunchKernelGGL(split_epilogue_kernel<EPI>, dim3(blocks), dim3(256), 0, s, nullptr, stop, 0, g, P,
+                          splits, stride, ldp);
   else
     hipLaunchKernelGGL(split_epilogue_kernel<EPI>, dim3(blocks), dim3(256), 0, s, g, P, splits, stride, ldp);
   return hipGetLastError();
@@ -1345,7 +1350,7 @@ size_t split_partials_bytes(int64_t M, int64_t N, int splits) {
 }
 
 hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float* partials, hipStream_t stream,
-                             hipEvent_t start, hipEvent_t stop, int tile) {
+                             hipEvent_t start, hipEvent_t stop, int tile, hipEvent_t gemm_stop) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const bool dual = epi == kEpiSwiglu;
   if (splits < 2 || splits > 64 || !partials || (dual && layout != kFwd)) return hipErrorInvalidValue;
@@ -1368,7 +1373,7 @@ hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float*
   p.accumulate = 0;
   p.bias = nullptr; p.aux_in = nullptr; p.aux_out = nullptr;
   const bool pipe = tile == kTileAuto || tile == kTile256x256w4;
-  hipError_t e = launch_partial(p, layout, dual, pipe, stream, start);
+  hipError_t e = launch_partial(p, layout, dual, pipe, stream, start, gemm_stop);
   if (e != hipSuccess) return e;
   switch (epi) {
     case kEpiBf16: return launch_split_epilogue<kEpiBf16>(g, partials, splits, p.part_stride, ldp, stream, stop);
@@ -1381,6 +1386,8 @@ hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float*
     default: return hipErrorInvalidValue;
   }
 }
+
+LaunchInfo last_launch() { return g_last_launch; }
 
 hipError_t launch_fence(hipStream_t stream) {
   hipLaunchKernelGGL(fence_kernel, dim3(1), dim3(64), 0, stream);

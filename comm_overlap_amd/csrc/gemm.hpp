@@ -78,6 +78,15 @@ enum GemmTile : int {
 int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone, double* fill = nullptr,
                 bool accumulate = false);
 
+// The kernel of the latest GEMM launch from this thread (launch_gemm, or the partial product of
+// launch_gemm_split): its Tile<BM, BN, waves_m, waves_n, blocks_per_cu> parameters, layout and
+// epilogue, and its grid (blocks of `threads` work-items). Traces name each launch's kernel by it.
+struct LaunchInfo {
+  int32_t bm = 0, bn = 0, waves_m = 0, waves_n = 0, blocks_per_cu = 0, layout = 0, epi = 0;
+  int32_t blocks = 0, threads = 0;
+};
+LaunchInfo last_launch();
+
 // Queue one GEMM on `stream`. With `start`/`stop` events the launch records the kernel's own start
 // and end times in them (timestamps of the dispatch itself, no extra marker packets).
 // Returns hipSuccess or the launch error.
@@ -107,11 +116,13 @@ double estimate_product_us(int64_t M, int64_t N, int64_t K, int layout, int epi,
 // (0 when splits == 1).
 size_t split_partials_bytes(int64_t M, int64_t N, int splits);
 // Queue a split product: the GEMM into `partials` (fp32), then the reduction with epilogue `epi`
-// into g's outputs, on `stream`. `start`/`stop` bracket both when tracing. The partial products
+// into g's outputs, on `stream`. When tracing, `start`/`gemm_stop` bracket the GEMM and
+// `gemm_stop`/`stop` the reduction. The partial products
 // run 256 x 256 tiles: the four-wave pipelined ones when K is a multiple of 64 and `tile` is
 // kTileAuto or kTile256x256w4, else the eight-wave ones (the same bits).
 hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float* partials, hipStream_t stream,
-                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr, int tile = kTileAuto);
+                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr, int tile = kTileAuto,
+                             hipEvent_t gemm_stop = nullptr);
 
 // A one-wave kernel that does nothing. Queued on a stream after DMA-engine copies it completes only
 // after them (stream order), so an event recorded after it marks the copies' completion.

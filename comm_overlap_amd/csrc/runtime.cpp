@@ -346,7 +346,15 @@ struct Schedule {
     return TPSLICE_OK;
   }
 
-  // Queue one product on worker(i) (i = -1: worker 0, all tokens), traced as `step`. A traced
+  // The kernel identity of the latest GEMM launch, for a trace record.
+  static void tag_kernel(tpslice_trace_rec_t& rec) {
+    const LaunchInfo k = last_launch();
+    rec.tile_m = k.bm; rec.tile_n = k.bn; rec.waves_m = k.waves_m; rec.waves_n = k.waves_n;
+    rec.blocks_per_cu = k.blocks_per_cu; rec.layout = k.layout; rec.epilogue = k.epi;
+    rec.blocks = k.blocks; rec.threads = k.threads;
+  }
+
+  // Queue one product on worker(i) (i = -1: worker `on`, all tokens), traced as `step`. A traced
   // product carries its timing events on the dispatch itself.
   tpslice_status_t product(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int on = 0) {
     const int wi = i < 0 ? on : i;
@@ -369,39 +377,51 @@ struct Schedule {
       lead_slice = -1;
       lead_done = i;
     }
-    if (tr) rt->slots.push_back(t);
+    if (tr) {
+      tag_kernel(t.rec);
+      rt->slots.push_back(t);
+    }
     return TPSLICE_OK;
   }
 
-  // A product over all tokens split along k when `splits` > 1 (fp32 partials in `part`, then the
-  // ordered reduction into the output: fp32 for kEpiF32, bf16 for kEpiBf16).
   // A product split along k when `splits` > 1: fp32 partials in `part`, then the ordered
   // reduction with the product's epilogue. i >= 0: row slice i's product (on worker(i));
-  // i < 0: a product over all tokens on worker(on).
+  // i < 0: a product over all tokens on worker(on). Traced as two records: the GEMM of the
+  // partial products (with the product's flops) and the reduction.
   tpslice_status_t product_split(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int splits,
                                  float* part, int on = 0) {
     if (splits <= 1) return product(i, step, piece, g, layout, epi, on);
     const int wi = i < 0 ? on : i;
     const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    TraceSlot t{};
+    hipEvent_t e0 = nullptr, em = nullptr, e1 = nullptr;
+    TraceSlot t{}, u{};
     const bool tr = (p->trace & 1) && g.M > 0 && g.N > 0;
     if (tr) {
       t.rec.kind = TPSLICE_TRACE_GEMM; t.rec.step = step; t.rec.slice = i; t.rec.piece = piece;
       t.rec.stream = worker_id(wi); t.rec.flops = flops; t.rec.call = rt->calls - 1;
+      u.rec = t.rec;
+      u.rec.kind = TPSLICE_TRACE_SPLIT_SUM;
+      u.rec.flops = 0.0;
       TPS_TRY_(trace_event(&t.ev0));
       TPS_TRY_(trace_event(&t.ev1));
+      TPS_TRY_(trace_event(&u.ev1));
+      u.ev0 = t.ev1;
       e0 = rt->tpool[t.ev0];
-      e1 = rt->tpool[t.ev1];
+      em = rt->tpool[t.ev1];
+      e1 = rt->tpool[u.ev1];
     }
-    hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1, p->tile);
+    hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1, p->tile, em);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "split GEMM launch: %s", hipGetErrorString(e));
     if (i >= 0 && i == lead_slice) {
       TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
       lead_slice = -1;
       lead_done = i;
     }
-    if (tr) rt->slots.push_back(t);
+    if (tr) {
+      tag_kernel(t.rec);
+      rt->slots.push_back(t);
+      rt->slots.push_back(u);
+    }
     return TPSLICE_OK;
   }
 

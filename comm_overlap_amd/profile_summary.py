@@ -7,6 +7,7 @@
                                                --calib-kernel NAME --calib-bytes N
         HBM bytes per dispatch of NAME from a FETCH_SIZE pass and a WRITE_SIZE pass, each scaled
         by what the same counter reads for a calibration copy kernel that moves N bytes each way
+        (--grid G: only NAME's dispatches with grid_size_x G, i.e. one product's shape)
     python -m comm_overlap_amd.profile_summary counters RESULTS.db [--match gemm_kernel]
         per kernel (medians over its dispatches) from a pass with GRBM_GUI_ACTIVE,
         SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_WAVE_CYCLES, SQ_WAIT_ANY:
@@ -26,6 +27,11 @@ import sys
 def _kernels(db):
     c = sqlite3.connect(db)
     return list(c.execute("select name, start, end from kernels order by start"))
+
+
+def _kernels_grid(db):
+    c = sqlite3.connect(db)
+    return list(c.execute("select name, grid_x, start, end from kernels order by start"))
 
 
 def _copies(db):
@@ -56,6 +62,15 @@ def trace(db, match):
     print(f"  {'count':>6} {'avg':>10} {'min':>10} {'max':>10} {'total_ms':>10}  name")
     for name, d in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
         print(f"  {len(d):6d} {sum(d)/len(d):10.2f} {min(d):10.2f} {max(d):10.2f} {sum(d)/1e3:10.3f}  {name[:110]}")
+    by_grid = collections.OrderedDict()
+    for name, g, s, e in _kernels_grid(db):
+        if match in name:
+            by_grid.setdefault((name, g), []).append((e - s) / 1e3)
+    print(f"'{match}' dispatches by grid size (one kernel serves products of several shapes; durations in us):")
+    print(f"  {'count':>6} {'avg':>10} {'min':>10} {'max':>10} {'total_ms':>10} {'grid_x':>9}  name")
+    for (name, g), d in sorted(by_grid.items(), key=lambda kv: -sum(kv[1])):
+        print(f"  {len(d):6d} {sum(d)/len(d):10.2f} {min(d):10.2f} {max(d):10.2f} {sum(d)/1e3:10.3f} {g:9d}  "
+              f"{name[:90]}")
     cps = _copies(db)
     if not cps:
         return
@@ -84,13 +99,14 @@ def trace(db, match):
               f"of {tot / 1e6:.3f} ms")
 
 
-def _pmc(db, counter):
+def _pmc(db, counter, grid=None):
     c = sqlite3.connect(db)
     per = collections.defaultdict(float)
     names = {}
+    grids = dict(c.execute("select dispatch_id, grid_size_x from rocpd_kernel_dispatch"))
     for name, disp, cname, val in c.execute(
             "select name, dispatch_id, counter_name, counter_value from pmc_events"):
-        if cname.startswith(counter):
+        if cname.startswith(counter) and (grid is None or grids.get(disp) == grid or "calib" == name):
             per[disp] += val
             names[disp] = name
     out = collections.defaultdict(list)
@@ -99,9 +115,9 @@ def _pmc(db, counter):
     return out
 
 
-def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes):
-    f = _pmc(fetch_db, "FETCH_SIZE")
-    w = _pmc(write_db, "WRITE_SIZE")
+def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes, grid=None):
+    f, fc_all = _pmc(fetch_db, "FETCH_SIZE", grid), _pmc(fetch_db, "FETCH_SIZE")
+    w, wc_all = _pmc(write_db, "WRITE_SIZE", grid), _pmc(write_db, "WRITE_SIZE")
 
     def avg(d, match):
         vals = [v for n, vs in d.items() if match in n for v in vs]
@@ -109,8 +125,8 @@ def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes):
 
     fk, nf = avg(f, kernel)
     wk, nw = avg(w, kernel)
-    fc, _ = avg(f, calib_kernel)
-    wc, _ = avg(w, calib_kernel)
+    fc, _ = avg(fc_all, calib_kernel)
+    wc, _ = avg(wc_all, calib_kernel)
     if None in (fk, wk, fc, wc):
         print("missing dispatches for the kernel or the calibration copy", file=sys.stderr)
         return 1
@@ -119,7 +135,8 @@ def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes):
     print(f"calibration copy: FETCH_SIZE {fc:.0f} KiB, WRITE_SIZE {wc:.0f} KiB for {calib_bytes} B each way "
           f"-> scale {sf:.4f} (fetch), {sw:.4f} (write)")
     fb, wb = fk * 1024.0 * sf, wk * 1024.0 * sw
-    print(f"kernel '{kernel}': {nf} fetch / {nw} write dispatches; per dispatch FETCH {fk:.0f} KiB, "
+    gtxt = "" if grid is None else f" (grid_x {grid})"
+    print(f"kernel '{kernel}'{gtxt}: {nf} fetch / {nw} write dispatches; per dispatch FETCH {fk:.0f} KiB, "
           f"WRITE {wk:.0f} KiB -> {fb/1e6:.2f} MB read + {wb/1e6:.2f} MB written = {(fb+wb)/1e6:.2f} MB")
     print(f"traffic_bytes_per_launch: {fb + wb:.0f}")
     return 0
@@ -174,6 +191,7 @@ def main(argv=None):
     r.add_argument("--kernel", required=True)
     r.add_argument("--calib-kernel", required=True)
     r.add_argument("--calib-bytes", type=float, required=True)
+    r.add_argument("--grid", type=int, default=None, help="only dispatches with this grid_size_x")
     k = sub.add_parser("counters")
     k.add_argument("db")
     k.add_argument("--match", default="gemm_kernel")
@@ -184,7 +202,7 @@ def main(argv=None):
     if a.cmd == "counters":
         counters(a.db, a.match)
         return 0
-    return traffic(a.fetch_db, a.write_db, a.kernel, a.calib_kernel, a.calib_bytes)
+    return traffic(a.fetch_db, a.write_db, a.kernel, a.calib_kernel, a.calib_bytes, a.grid)
 
 
 if __name__ == "__main__":

@@ -32,7 +32,7 @@ EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice
            "tpslice_attnproj_bwd", "tpslice_trace_enable", "tpslice_trace_read",
            "tpslice_handoff_copy", "tpslice_handoff_wait", "tpslice_attn_core_fwd", "tpslice_error_string",
            "tpslice_last_error")
-TRACE_GEMM, TRACE_COPY, TRACE_COLSUM = range(3)
+TRACE_GEMM, TRACE_COPY, TRACE_COLSUM, TRACE_SPLIT_SUM = range(4)
 STEPS = ("mlp_up", "mlp_down", "qkv", "out", "mlp_dh", "mlp_dx", "mlp_dw1", "mlp_dw2", "attn_dx", "attn_dc",
          "attn_dwqkv", "attn_dwo", "bias_grad", "handoff")
 
@@ -71,7 +71,10 @@ class TraceRec(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("step", ctypes.c_int32), ("slice", ctypes.c_int32),
                 ("piece", ctypes.c_int32), ("stream", ctypes.c_int32), ("call", ctypes.c_int32),
                 ("flops", ctypes.c_double), ("bytes", ctypes.c_double), ("start_ms", ctypes.c_float),
-                ("end_ms", ctypes.c_float)]
+                ("end_ms", ctypes.c_float), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32), ("blocks_per_cu", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("epilogue", ctypes.c_int32), ("blocks", ctypes.c_int32),
+                ("threads", ctypes.c_int32)]
 
 
 class StreamsC(ctypes.Structure):
@@ -282,16 +285,22 @@ class Plan:
     def trace_read(self):
         """Records accumulated since the last read (then a new window starts): dicts with kind,
         step, slice, piece, stream, call, flops, bytes, start_ms, end_ms (ms from the first traced
-        call's start on the caller stream)."""
+        call's start on the caller stream), and for GEMM launches the kernel's identity (template
+        parameters and grid, as a kernel profiler names the dispatch) and grid_x (work-items)."""
         n = ctypes.c_int32()
         _check(lib.tpslice_trace_read(self._h, None, 0, ctypes.byref(n)))
         recs = (TraceRec * max(1, n.value))()
         _check(lib.tpslice_trace_read(self._h, recs, n.value, ctypes.byref(n)))
         out = []
         for r in recs[:n.value]:
-            out.append(dict(kind=("gemm", "copy", "colsum")[r.kind], step=STEPS[r.step], slice=r.slice,
-                            piece=r.piece, stream=r.stream, call=r.call, flops=r.flops, bytes=r.bytes,
-                            start_ms=r.start_ms, end_ms=r.end_ms))
+            kernel = None
+            if r.kind == TRACE_GEMM:
+                kernel = (f"gemm_kernel<Tile<{r.tile_m}, {r.tile_n}, {r.waves_m}, {r.waves_n}, {r.blocks_per_cu}>, "
+                          f"{r.layout}, {r.epilogue}> grid {r.blocks} x {r.threads}")
+            out.append(dict(kind=("gemm", "copy", "colsum", "split_sum")[r.kind], step=STEPS[r.step],
+                            slice=r.slice, piece=r.piece, stream=r.stream, call=r.call, flops=r.flops,
+                            bytes=r.bytes, start_ms=r.start_ms, end_ms=r.end_ms, kernel=kernel,
+                            grid_x=r.blocks * r.threads))
         return out
 
     def handoff_copy(self, src, dst, stream=None):

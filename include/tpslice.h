@@ -266,7 +266,12 @@ TPSLICE_API tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t plan, const vo
  * from the start (on the caller stream) of the first call traced since the last read, and `call`
  * numbers the calls from 0 in that window. Tracing adds event records to the streams; it changes
  * no result.                                                                                      */
-typedef enum { TPSLICE_TRACE_GEMM = 0, TPSLICE_TRACE_COPY = 1, TPSLICE_TRACE_COLSUM = 2 } tpslice_trace_kind_t;
+typedef enum {
+  TPSLICE_TRACE_GEMM = 0,      /* a product's GEMM kernel (for a product split along k: its partial products) */
+  TPSLICE_TRACE_COPY = 1,      /* a hand-off copy                                                       */
+  TPSLICE_TRACE_COLSUM = 2,    /* the bias gradient's column sums                                       */
+  TPSLICE_TRACE_SPLIT_SUM = 3  /* a split product's ordered reduction of its partials, with the epilogue */
+} tpslice_trace_kind_t;
 typedef enum {
   TPSLICE_STEP_MLP_UP = 0,     /* X W1^T + activation                 */
   TPSLICE_STEP_MLP_DOWN = 1,   /* H W2^T (partial sum piece)          */
@@ -293,6 +298,11 @@ typedef struct {
   double flops;     /* algorithmic flops, 2*M*N*K (0 for copies)                      */
   double bytes;     /* bytes copied (copies), 0 otherwise                             */
   float start_ms, end_ms;
+  /* the GEMM kernel of a TPSLICE_TRACE_GEMM record (zeros otherwise): its block tile
+     tile_m x tile_n, waves_m x waves_n waves, blocks_per_cu resident blocks per CU, layout
+     (0 forward, 1 activation gradient, 2 weight gradient), epilogue, and its grid of `blocks`
+     workgroups of `threads` work-items - the identity a kernel profiler reports for the launch */
+  int32_t tile_m, tile_n, waves_m, waves_n, blocks_per_cu, layout, epilogue, blocks, threads;
 } tpslice_trace_rec_t;
 
 /* enable: 0 off; bit 0 traces products (GEMMs, column sums); bit 1 traces hand-off copies (each
