@@ -92,7 +92,7 @@ static int32_t default_streams(const tpslice_plan_s* p) {
   struct P { int64_t n, k; int layout, epi; };
   const P prods[] = {
       {p->Fp, p->desc.hidden, kFwd, glu ? kEpiSwiglu : kEpiGelu},  // up-projection (+ activation)
-      {p->hc, p->Fp, kFwd, kEpiBf16},                              // down-projection piece
+      {p->pw, p->Fp, kFwd, kEpiBf16},                              // down-projection product
   };
   for (const P& q : prods) {
     double fill = 0.0;
@@ -124,22 +124,24 @@ constexpr double kSliceSyncUs1 = 20.0, kSliceSyncUs2 = 80.0;
 static double predict_forward_us(const tpslice_desc_t* d, int64_t Fp, int64_t N1, int64_t qkv, int64_t ctx, int r,
                                  int c, int S, double gbps) {
   const int64_t Ms = d->tokens / r, h = d->hidden, hc = h / c;
+  const int pc = (c > 1 && (d->flags & TPSLICE_F_HANDOFF_ROWS)) ? 1 : c;  // products per row slice
+  const int64_t pw = h / pc;
   const int pair = (S > 1 && r > 1) ? 2 : 1;
   const int64_t Mp = Ms * pair;  // rows of the products that share the GPU at once
   const bool alone = pair == 1;
   const int epi_up = d->act == TPSLICE_ACT_SWIGLU ? kEpiSwiglu : kEpiGelu;
   double group_us = estimate_product_us(Mp, Fp, h, kFwd, epi_up, alone, choose_slice_split(N1, h)) +
-                    c * estimate_product_us(Mp, hc, Fp, kFwd, kEpiBf16, alone);
+                    pc * estimate_product_us(Mp, pw, Fp, kFwd, kEpiBf16, alone);
   int tensors = 1;
   if (qkv > 0) {
     group_us += estimate_product_us(Mp, qkv, h, kFwd, kEpiBf16, alone, choose_slice_split(qkv, h)) +
-                c * estimate_product_us(Mp, hc, ctx, kFwd, kEpiBf16, alone);
+                pc * estimate_product_us(Mp, pw, ctx, kFwd, kEpiBf16, alone);
     tensors = 2;
   }
   const double comp_us = group_us * double((r + pair - 1) / pair);
   const double slice_us = comp_us / r;
-  const double piece_us = double(Ms) * double(hc) * 2.0 * tensors / (gbps * 1e3) + kCopyFixedUs * tensors;
-  const double copy_us = c * piece_us;  // one row slice's pieces
+  // one row slice's copies: c pieces, or one whole-row copy (the same bytes, one fixed cost)
+  const double copy_us = double(Ms) * double(h) * 2.0 * tensors / (gbps * 1e3) + pc * kCopyFixedUs * tensors;
   if (d->flags & TPSLICE_F_PIPELINE) return std::max(comp_us, r * (copy_us + (S > 1 ? kSliceSyncUs2 : kSliceSyncUs1)));
   return std::max(comp_us + copy_us, slice_us + r * copy_us);
 }
@@ -168,6 +170,8 @@ static void choose_slices(const tpslice_desc_t* d, int64_t Fp, int64_t N1, int64
       q.desc = *d;
       q.Fp = Fp; q.N1 = N1; q.qkv = qkv; q.ctx = ctx; q.qh = qkv > 0 ? 1 : 0;
       q.r = r; q.c = c; q.Ms = d->tokens / r; q.hc = d->hidden / c;
+      q.pc = (c > 1 && (d->flags & TPSLICE_F_HANDOFF_ROWS)) ? 1 : c;
+      q.pw = d->hidden / q.pc;
       const int S = (d->flags & TPSLICE_F_SERIALIZE) ? 1 : d->n_streams > 0 ? d->n_streams : default_streams(&q);
       const double t = predict_forward_us(d, Fp, N1, qkv, ctx, r, c, S, gbps);
       const int pieces = r * c;
@@ -255,6 +259,8 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   p->desc.n_row_slices = p->r;
   p->desc.n_col_slices = p->c;
   p->Ms = M / p->r; p->hc = h / p->c;
+  p->pc = (p->c > 1 && (d->flags & TPSLICE_F_HANDOFF_ROWS)) ? 1 : p->c;
+  p->pw = h / p->pc;
   const bool serial = d->flags & TPSLICE_F_SERIALIZE;
   p->qh = qh; p->kvh = kvh;
   p->S = serial ? 1 : (d->n_streams ? d->n_streams : default_streams(p));

@@ -11,6 +11,11 @@ struct tpslice_plan_s {
   tpslice_desc_t desc;
   int64_t M, h, Fp, N1, qkv, ctx;  // tokens, hidden, F', up-projection width, QKV width, context width
   int64_t Ms, hc;                  // rows per row slice, hand-off columns per column slice
+  // products per row slice of each hand-off output and their width: c pieces of hc columns, or
+  // with whole-row hand-off (TPSLICE_F_HANDOFF_ROWS, c > 1) one product of all h columns, since
+  // the row slice's copy waits for every column piece anyway
+  int32_t pc;
+  int64_t pw;
   int32_t r, c, S, E;              // row slices, column slices, worker streams, copy streams
   int32_t qh, kvh;                 // this rank's query / key-value heads
   int32_t trace;                   // tracing enabled

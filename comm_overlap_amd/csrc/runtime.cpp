@@ -302,10 +302,11 @@ struct Schedule {
     char* d = static_cast<char*>(dst) + row0 * pitch + col0 * 2;
     const hipMemcpyKind kind =
         (p->desc.flags & TPSLICE_F_COPY_BLIT) ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
-    // whole row slices: one contiguous copy after the slice's last column piece
+    // whole row slices: one contiguous copy after the slice's last product (its products then
+    // span all columns: p->pc == 1)
     const bool rows = p->c > 1 && (p->desc.flags & TPSLICE_F_HANDOFF_ROWS);
     if (rows) {
-      if (j < p->c - 1) return TPSLICE_OK;
+      if (j < p->pc - 1) return TPSLICE_OK;
       s = static_cast<const char*>(src) + row0 * pitch;
       d = static_cast<char*>(dst) + row0 * pitch;
     }
@@ -576,10 +577,10 @@ extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, con
     if (U_save) { g1.aux_out = bfw(U_save, r0 * p->N1); g1.ld_out = p->N1; }
     TPS_TRY(S.product_split(i, TPSLICE_STEP_MLP_UP, -1, g1, kFwd, epi, p->sp_up,
                             S.slice_part(static_cast<char*>(ws) + L.up_split, L.up_split_bytes, i)));
-    for (int j = 0; j < p->c; ++j) {
-      const int64_t c0 = int64_t(j) * p->hc;
+    for (int j = 0; j < p->pc; ++j) {
+      const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs g2 = args(bf(H, r0 * p->Fp), p->Fp, bf(W2, c0 * p->Fp), p->Fp, bfw(Z, r0 * p->h + c0), p->h,
-                         p->Ms, p->hc, p->Fp);
+                         p->Ms, p->pw, p->Fp);
       TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DOWN, j, g2, kFwd, kEpiBf16));
       if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
     }
@@ -613,10 +614,10 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
     TPS_TRY(S.slice_begin(i));
     S.slice_streams = 0;
     // output projection first: its pieces are the hand-off, the QKV product then runs under the copies
-    for (int j = 0; j < p->c; ++j) {
-      const int64_t c0 = int64_t(j) * p->hc;
+    for (int j = 0; j < p->pc; ++j) {
+      const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs g = args(bf(C, r0 * p->ctx), p->ctx, bf(Wo, c0 * p->ctx), p->ctx, bfw(Z, r0 * p->h + c0), p->h,
-                        p->Ms, p->hc, p->ctx);
+                        p->Ms, p->pw, p->ctx);
       TPS_TRY(S.product(i, TPSLICE_STEP_OUT, j, g, kFwd, kEpiBf16));
       if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
     }
@@ -663,9 +664,9 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
     g.half = p->Fp;
     TPS_TRY(S.product_split(i, TPSLICE_STEP_MLP_DH, -1, g, kDgrad, glu ? kEpiDswiglu : kEpiDgelu, p->sp_dh,
                             S.slice_part(static_cast<char*>(ws) + L.dh_split, L.dh_split_bytes, i)));
-    for (int j = 0; j < p->c; ++j) {
-      const int64_t c0 = int64_t(j) * p->hc;
-      GemmArgs gx = args(bf(dU, r0 * p->N1), p->N1, bf(W1, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms, p->hc,
+    for (int j = 0; j < p->pc; ++j) {
+      const int64_t c0 = int64_t(j) * p->pw;
+      GemmArgs gx = args(bf(dU, r0 * p->N1), p->N1, bf(W1, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms, p->pw,
                          p->N1);
       TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DX, j, gx, kDgrad, kEpiBf16));
       if (dX_handoff) TPS_TRY(S.handoff(i, j, dX, dX_handoff));
@@ -733,10 +734,10 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
     const int64_t r0 = int64_t(i) * p->Ms;
     TPS_TRY(S.slice_begin(i));
     S.slice_streams = 0;
-    for (int j = 0; j < p->c; ++j) {
-      const int64_t c0 = int64_t(j) * p->hc;
+    for (int j = 0; j < p->pc; ++j) {
+      const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs gx = args(bf(dQKV, r0 * p->qkv), p->qkv, bf(Wqkv, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms,
-                         p->hc, p->qkv);
+                         p->pw, p->qkv);
       TPS_TRY(S.product(i, TPSLICE_STEP_ATTN_DX, j, gx, kDgrad, kEpiBf16));
       if (dX_handoff) TPS_TRY(S.handoff(i, j, dX, dX_handoff));
     }
@@ -825,7 +826,7 @@ extern "C" tpslice_status_t tpslice_handoff_copy(tpslice_plan_t p, const void* s
   for (int i = 0; i < p->r; ++i) {
     TPS_TRY(S.slice_begin(i));
     S.slice_streams = 0;
-    for (int j = 0; j < p->c; ++j) TPS_TRY(S.handoff(i, j, src, dst));
+    for (int j = 0; j < p->pc; ++j) TPS_TRY(S.handoff(i, j, src, dst));
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
   }
   return S.join();

@@ -76,12 +76,14 @@ typedef enum {
                                     Use tpslice_handoff_wait() before reading a hand-off buffer on
                                     another stream, or before freeing buffers the copies touch.    */
 #define TPSLICE_F_HANDOFF_ROWS 0x8u /* with column slices (c > 1): hand off each row slice as one
-                                    contiguous copy on the DMA engines once its last column piece is
-                                    done, instead of each (row, column) piece on its own. A piece
-                                    is a strided 2D region, which the HIP runtime copies with a kernel
-                                    on the compute units (taking them from the products); a whole
-                                    row slice is contiguous. The same bytes arrive; they leave a
-                                    row slice's last piece later.                                  */
+                                    contiguous copy on the DMA engines once the row slice is done,
+                                    instead of each (row, column) piece on its own. A piece is a
+                                    strided 2D region, which the HIP runtime copies with a kernel on
+                                    the compute units (taking them from the products); a whole row
+                                    slice is contiguous. Since the copy then waits for every column
+                                    of the row slice, the row slice's product runs as one launch over
+                                    all h columns (c times the blocks of a piece: the GPU's compute
+                                    units filled by one product; same k order, same bits).        */
 #define TPSLICE_F_CALLER_WORKER 0x40u /* worker stream 0 is the caller's stream (no stream of its own):
                                     one fork and join fewer per call, and one hardware queue fewer
                                     (a process has four by default), so that two plans with their

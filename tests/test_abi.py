@@ -176,6 +176,28 @@ def test_automatic_slice_counts_are_valid(key, pipeline, gbps):
     assert p.info.predicted_forward_us <= best * 1.02 + 1e-9
 
 
+def test_slow_handoff_slices_a_small_layer():
+    """The slicing the GPU test of automatic slice counts runs (2048 tokens, h 1024, F 4096, GeLU):
+    with a 25 GB/s hand-off the model slices it, with the local DMA copy it does not (pins the
+    chooser's own worker-stream count, which must use the plan's product widths)."""
+    w = synth.custom("auto_slices", 909, tokens=2048, hidden=1024, ffn=4096, tp=1, act="gelu", bias=True,
+                     row_slices=1, col_slices=1)
+    slow = T.plan_for(w, n_row_slices=0, n_col_slices=0, handoff_gbps=25.0)
+    assert slow.info.n_row_slices * slow.info.n_col_slices > 1
+    fast = T.plan_for(w, n_row_slices=0, n_col_slices=0)
+    assert fast.info.n_row_slices * fast.info.n_col_slices >= 1
+
+
+def test_whole_row_handoff_runs_one_product_per_row_slice():
+    """With whole-row hand-off the chooser and the plan model one product of h columns per row
+    slice: the prediction equals that of the same plan with one column slice."""
+    w = synth.WORKLOADS["llama3_70b_layer"]
+    rows = T.plan_for(w, handoff_rows=True, n_streams=2)
+    one = T.plan_for(w, n_col_slices=1, n_streams=2)
+    assert rows.info.n_col_slices == 2
+    assert rows.info.predicted_forward_us == pytest.approx(one.info.predicted_forward_us, rel=1e-12)
+
+
 def test_given_slice_counts_are_kept():
     w = synth.WORKLOADS["llama3_70b_layer"]
     for gbps in (0.0, 25.0):
