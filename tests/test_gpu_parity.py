@@ -434,7 +434,7 @@ def test_full_layer_workload(key):
     _print_case("full_layer", key=key)
     inp = synth.make_inputs(w)
     plan = T.plan_for(w)
-    rows = G.sample_rows(w.tokens, w.row_slices, per_slice=4)
+    rows = G.sample_rows(w.tokens, w.row_slices, per_slice=max(4, 32 // w.row_slices))
     # forward
     fo = G.run_mlp_fwd(plan, inp)
     ref = G.oracle_mlp_fwd(inp, w.act, rows=rows)
@@ -455,7 +455,7 @@ def test_full_layer_workload(key):
                    f64(inp["dY"][rows]), w.act)
     G.assert_parity(bo["dX"].cpu()[rows], rb["dX"], "dX rows")
     Fp = w.ffn_shard
-    J = G.sample_cols(Fp, 6)
+    J = G.sample_cols(Fp, 32)
     rows1 = np.concatenate([J, Fp + J])
     rj = L.mlp_bwd(f64(inp["X_mlp"]), f64(inp["W1"][rows1]), f64(inp["W2"][:, J]),
                    f64(inp["U_saved"][:, rows1]), f64(inp["dY"]), w.act)
@@ -470,8 +470,8 @@ def test_full_layer_workload(key):
     G.assert_parity(go["dX"].cpu()[rows], rg["dX"], "attn dX rows")
     G.assert_parity(go["dC"].cpu()[rows], rg["dC"], "dC rows")
     # weight gradients on sampled output rows: the oracle on that subset of the projections
-    Jq = G.sample_cols(w.qkv_width, 6)
-    Jh = G.sample_cols(w.hidden, 6)
+    Jq = G.sample_cols(w.qkv_width, 32)
+    Jh = G.sample_cols(w.hidden, 32)
     rs = L.attnproj_bwd(f64(inp["X"]), f64(inp["Wqkv"][Jq]), f64(inp["dQKV"][:, Jq]), f64(inp["C"]),
                         f64(inp["Wo"][Jh]), f64(inp["dY_attn"][:, Jh]))
     G.assert_parity(go["dWqkv"].cpu()[Jq], rs["dWqkv"], "dWqkv rows")
@@ -603,3 +603,77 @@ def test_tracing_changes_no_result_and_times_every_launch():
     assert all(r["end_ms"] > r["start_ms"] >= 0 for r in gemms)
     fl = w.gemm_flops()
     assert sum(r["flops"] for r in gemms) == pytest.approx(fl["mlp_up"] + fl["mlp_down"])
+
+
+def _chain_step(plan, w, d, x, o, g, dy_mlp):
+    """One layer step as the benchmark chains them: the attention projections read `x`, the MLP reads
+    their hand-off, the MLP backward takes `dy_mlp`, the attention backward the MLP's dX hand-off."""
+    if w.has_attn:
+        plan.attnproj_fwd(x, d["Wqkv"], None, o["QKV"], d["C"], d["Wo"], o["Za"], o["Zah"])
+        x_mlp = o["Zah"]
+    else:
+        x_mlp = x
+    plan.mlp_fwd(x_mlp, d["W1"], d.get("b1"), d["W2"], o["Z"], o["U"], o["Zh"])
+    if w.backward:
+        plan.mlp_bwd(x_mlp, d["W1"], d["W2"], d["U_saved"], dy_mlp, o["dX"], g["dW1"], g["dW2"],
+                     db1=g.get("db1"), dX_handoff=o["dXh"])
+        if w.has_attn:
+            plan.attnproj_bwd(x, d["Wqkv"], d["dQKV"], d["C"], d["Wo"], o["dXh"], o["dXa"], o["dC"], g["dWqkv"],
+                              g["dWo"], dX_handoff=o["dXah"])
+
+
+def _chain_buffers(w, i):
+    e = lambda *s, dt=torch.bfloat16: torch.full(s, float("nan"), dtype=dt, device="cuda")
+    o = {"Z": e(i.tokens, i.hidden), "Zh": e(i.tokens, i.hidden), "U": e(i.tokens, i.n1)}
+    if w.has_attn:
+        o.update(QKV=e(i.tokens, i.qkv_width), Za=e(i.tokens, i.hidden), Zah=e(i.tokens, i.hidden))
+    g = {}
+    if w.backward:
+        o.update(dX=e(i.tokens, i.hidden), dXh=e(i.tokens, i.hidden))
+        g = {"dW1": e(i.n1, i.hidden, dt=torch.float32), "dW2": e(i.hidden, i.ffn_shard, dt=torch.float32)}
+        if w.bias:
+            g["db1"] = e(i.n1, dt=torch.float32)
+        if w.has_attn:
+            o.update(dXa=e(i.tokens, i.hidden), dXah=e(i.tokens, i.hidden), dC=e(i.tokens, i.ctx_width))
+            g.update(dWqkv=e(i.qkv_width, i.hidden, dt=torch.float32), dWo=e(i.hidden, i.ctx_width, dt=torch.float32))
+    return o, g
+
+
+@pytest.mark.parametrize("key", ["llama2_7b_mlp", "llama3_70b_layer"])
+def test_benchmark_mode_full_size(key):
+    """The plan flags the benchmark times (pipelined hand-off, whole-row copies, default streams) over
+    two chained layer steps at full size, each step reading the previous step's hand-off: every
+    output and hand-off buffer equals bit for bit the same steps run with joined calls (whose outputs
+    the full-size tests above check against the oracle), and the first step's MLP output on sampled
+    rows of every row slice matches the oracle."""
+    w = synth.WORKLOADS[key]
+    _print_case("bench_mode", key=key)
+    inp = synth.make_inputs(w)
+    d = {k: v.to("cuda").contiguous() for k, v in inp.items()}
+    bench_plan = T.plan_for(w, pipeline=True, handoff_rows=True)
+    joined = T.plan_for(w)
+    assert bench_plan.info.n_col_slices == w.col_slices
+    x0 = d["X"] if w.has_attn else d["X_mlp"]
+    dy = d.get("dY")
+    outs = {}
+    for name, plan in (("bench", bench_plan), ("joined", joined)):
+        o1, g1 = _chain_buffers(w, plan.info)
+        o2, g2 = _chain_buffers(w, plan.info)
+        _chain_step(plan, w, d, x0, o1, g1, dy)
+        _chain_step(plan, w, d, o1["Zh"], o2, g2, dy)
+        plan.handoff_wait()
+        torch.cuda.synchronize()
+        outs[name] = (o1, g1, o2, g2)
+    for a, b in zip(outs["bench"], outs["joined"]):
+        for k in a:
+            assert torch.equal(a[k], b[k]), k
+    o1 = outs["bench"][0]
+    for k in ("Zh", "dXh", "Zah", "dXah"):
+        if k in o1:
+            assert torch.equal(o1[k], o1[k[:-1]]), k
+    if not w.has_attn:
+        rows = G.sample_rows(w.tokens, w.row_slices, per_slice=max(4, 32 // w.row_slices))
+        ref = G.oracle_mlp_fwd(inp, w.act, rows=rows)
+        G.assert_parity(o1["Z"].cpu()[rows], ref["Z"], "Z rows")
+    bench_plan.close()
+    joined.close()
