@@ -20,6 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtpslice.so")
 
 OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
+STATIC_SCRATCH_BYTES = 64 << 20  # TPSLICE_STATIC_SCRATCH_BYTES
 ACT_GELU, ACT_SWIGLU = 1, 2
 F_SERIALIZE, F_COPY_BLIT, F_PIPELINE, F_HANDOFF_ROWS, F_CALLER_WORKER = 0x1, 0x2, 0x4, 0x8, 0x40
 F_TILE_SHIFT = 8
@@ -30,8 +31,8 @@ OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD = range(4)
 EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice_plan_piece",
            "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",
            "tpslice_attnproj_bwd", "tpslice_trace_enable", "tpslice_trace_read",
-           "tpslice_handoff_copy", "tpslice_handoff_wait", "tpslice_attn_core_fwd", "tpslice_error_string",
-           "tpslice_last_error")
+           "tpslice_handoff_copy", "tpslice_handoff_wait", "tpslice_attn_core_fwd", "tpslice_mlp_fwd_static",
+           "tpslice_error_string", "tpslice_last_error")
 TRACE_GEMM, TRACE_COPY, TRACE_COLSUM, TRACE_SPLIT_SUM = range(4)
 STEPS = ("mlp_up", "mlp_down", "qkv", "out", "mlp_dh", "mlp_dx", "mlp_dw1", "mlp_dw2", "attn_dx", "attn_dc",
          "attn_dwqkv", "attn_dwo", "bias_grad", "handoff")
@@ -103,7 +104,8 @@ def _load():
     lib.tpslice_handoff_copy.argtypes = [vp, vp, vp, ss]
     lib.tpslice_handoff_wait.argtypes = [vp, vp]
     lib.tpslice_attn_core_fwd.argtypes = [vp, vp, vp, ctypes.c_int64, ss]
-    for name in EXPORTS[:14]:
+    lib.tpslice_mlp_fwd_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ss]
+    for name in EXPORTS[:15]:
         getattr(lib, name).restype = st
     lib.tpslice_error_string.argtypes = [st]
     lib.tpslice_error_string.restype = ctypes.c_char_p
@@ -354,6 +356,18 @@ class Plan:
                                    _ptr(W2, name="W2"), _ptr(Z, name="Z"), _ptr(U_save, name="U_save"),
                                    _ptr(Z_handoff, name="Z_handoff"), wp, wn,
                                    self._call_streams(stream, Z_handoff is not None)))
+
+    def mlp_fwd_static(self, X, W1, b1, W2, Z, U_save=None, Z_handoff=None, stream=None):
+        """mlp_fwd with the library's own fixed device scratch as workspace (no allocation)."""
+        i = self.info
+        _shape(X, (i.tokens, i.hidden), "X"); _shape(W1, (i.n1, i.hidden), "W1")
+        _shape(b1, (i.n1,), "b1"); _shape(W2, (i.hidden, i.ffn_shard), "W2")
+        _shape(Z, (i.tokens, i.hidden), "Z"); _shape(U_save, (i.tokens, i.n1), "U_save")
+        _shape(Z_handoff, (i.tokens, i.hidden), "Z_handoff")
+        _check(lib.tpslice_mlp_fwd_static(self._h, _ptr(X, name="X"), _ptr(W1, name="W1"), _ptr(b1, name="b1"),
+                                          _ptr(W2, name="W2"), _ptr(Z, name="Z"), _ptr(U_save, name="U_save"),
+                                          _ptr(Z_handoff, name="Z_handoff"),
+                                          self._call_streams(stream, Z_handoff is not None)))
 
     def attnproj_fwd(self, X, Wqkv, bqkv, QKV, C, Wo, Z, Z_handoff=None, workspace=None, stream=None):
         i = self.info

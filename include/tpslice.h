@@ -263,6 +263,20 @@ TPSLICE_API tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t plan, const voi
 TPSLICE_API tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t plan, const void* QKV, void* C, int64_t seq_len,
                                        const tpslice_streams_t* streams);
 
+/* Allocation-free MLP forward, for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid allocation): tpslice_mlp_fwd with its
+ * workspace in a fixed device array of the library (TPSLICE_STATIC_SCRATCH_BYTES per GPU, held from
+ * the library's first use on that GPU until the process ends) instead of a caller buffer. Same
+ * arguments, semantics and results as tpslice_mlp_fwd; a plan whose MLP forward workspace
+ * (tpslice_workspace_size, TPSLICE_OP_MLP_FWD) exceeds the array gets TPSLICE_ERR_WORKSPACE before
+ * anything is queued. It calls no device allocation (the array's address is looked up on the first
+ * call on each GPU, and a plan creates its events on its first call of any entry point). Every call
+ * on one GPU uses the same array: calls that overlap in time on one GPU race on it.               */
+#define TPSLICE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+TPSLICE_API tpslice_status_t tpslice_mlp_fwd_static(tpslice_plan_t plan, const void* X, const void* W1,
+                                                    const void* b1, const void* W2, void* Z, void* U_save,
+                                                    void* Z_handoff, const tpslice_streams_t* streams);
+
 /* Tracing. When enabled, every product and every hand-off copy is bracketed by timing events on
  * the stream it runs on. Records accumulate over calls until they are read; times are milliseconds
  * from the start (on the caller stream) of the first call traced since the last read, and `call`

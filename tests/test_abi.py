@@ -280,3 +280,16 @@ def test_bench_rejects_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120, cwd=root)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_static_scratch_entry_rejects_before_any_gpu_work():
+    """The allocation-free forward checks its plan and the workspace size before it looks up the
+    device array or queues anything (the pointers below are never dereferenced)."""
+    lib = T.lib
+    A = _fake(0x100000)
+    assert lib.tpslice_mlp_fwd_static(None, A, A, None, A, A, None, None, None) == T.ERR_INVALID
+    big = T.Plan(T.Config(tokens=8192, hidden=1024, ffn=8192, n_row_slices=2))
+    assert big.workspace_size(T.OP_MLP_FWD) > T.STATIC_SCRATCH_BYTES
+    assert lib.tpslice_mlp_fwd_static(big._h, A, A, None, A, A, None, None, None) == T.ERR_WORKSPACE
+    assert b"static scratch" in lib.tpslice_last_error()
+    big.close()
