@@ -288,3 +288,69 @@ def check_tp_sum(oracle_layer, act, tp=4, seed=0, M=16, h=32, F=64, bias=True):
     else:
         H = U[:, :F] / (1.0 + np.exp(-U[:, :F])) * U[:, F:]
     assert_close(acc + b2, H @ W2_full.T + b2, 1e-12, "unsharded layer")
+
+
+# ------------------------------------------------------------------- attention core, backward
+def check_fd_attn_core(attn, seed=0, qh=4, kvh=2, d=3, S=4, nb=2, tol=1e-7):
+    """Every entry of the oracle's dQKV against central differences of L = <dC, C(QKV)>, with C from
+    the oracle's forward (itself pinned by a brute-force loop)."""
+    rng = np.random.default_rng(seed)
+    M = S * nb
+    QKV = rng.standard_normal((M, (qh + 2 * kvh) * d))
+    dC = rng.standard_normal((M, qh * d))
+    g = attn.attn_core_bwd(QKV, dC, qh, kvh, d, S)
+    assert g.shape == QKV.shape
+
+    def L(v):
+        return float(np.sum(dC * attn.attn_core_fwd(v, qh, kvh, d, S)))
+
+    for idx in np.ndindex(*QKV.shape):
+        fd = _fd(L, QKV, idx)
+        assert abs(fd - g[idx]) <= tol * (1 + abs(fd)), f"dQKV{idx}: fd {fd} vs {g[idx]}"
+
+
+def check_torch_attn_core(attn, seed=0, qh=4, kvh=1, d=5, S=6, nb=2):
+    """The oracle's dQKV against torch autograd (fp64, CPU) through a torch statement of the
+    forward pass: the gradient comes from the library's own differentiation."""
+    import torch
+    rng = np.random.default_rng(seed)
+    M = S * nb
+    QKV = rng.standard_normal((M, (qh + 2 * kvh) * d))
+    dC = rng.standard_normal((M, qh * d))
+    x = torch.tensor(QKV, dtype=torch.float64, requires_grad=True)
+    q = x[:, :qh * d].reshape(nb, S, qh, d).permute(0, 2, 1, 3)
+    k = x[:, qh * d:(qh + kvh) * d].reshape(nb, S, kvh, d).permute(0, 2, 1, 3)
+    v = x[:, (qh + kvh) * d:].reshape(nb, S, kvh, d).permute(0, 2, 1, 3)
+    k = k.repeat_interleave(qh // kvh, dim=1)
+    v = v.repeat_interleave(qh // kvh, dim=1)
+    sc = (q @ k.transpose(-1, -2)) / np.sqrt(d)
+    mask = torch.ones(S, S, dtype=torch.bool).tril()
+    sc = sc.masked_fill(~mask, float("-inf"))
+    out = torch.softmax(sc, dim=-1) @ v                      # [nb][qh][S][d]
+    out = out.permute(0, 2, 1, 3).reshape(M, qh * d)
+    out.backward(torch.tensor(dC, dtype=torch.float64))
+    got = attn.attn_core_bwd(QKV, dC, qh, kvh, d, S)
+    assert_close(got, x.grad.numpy(), 1e-12, "dQKV (torch autograd)")
+
+
+def check_lse(attn, seed=0, qh=3, kvh=1, d=4, S=5, nb=2):
+    """Row log-sum-exp: a brute-force loop with math.exp / math.log, and the closed form log(t + 1)
+    at zero keys (every score 0)."""
+    rng = np.random.default_rng(seed)
+    M = S * nb
+    QKV = rng.standard_normal((M, (qh + 2 * kvh) * d))
+    got = attn.attn_core_lse(QKV, qh, kvh, d, S)
+    for b in range(nb):
+        for h in range(qh):
+            g = h // (qh // kvh)
+            for t in range(S):
+                T = b * S + t
+                sc = [sum(QKV[T, h * d + i] * QKV[b * S + s, (qh + g) * d + i] for i in range(d)) / math.sqrt(d)
+                      for s in range(t + 1)]
+                ref = math.log(sum(math.exp(x) for x in sc))
+                assert abs(got[T, h] - ref) <= 1e-12 * (1 + abs(ref)), (T, h, got[T, h], ref)
+    Z = QKV.copy()
+    Z[:, qh * d:(qh + kvh) * d] = 0.0
+    z = attn.attn_core_lse(Z, qh, kvh, d, S)
+    for t in range(S):
+        assert abs(z[t, 0] - math.log(t + 1)) <= 1e-15 * (1 + math.log(t + 1))

@@ -279,3 +279,81 @@ def test_attention_closed_forms():
     assert np.array_equal(Cg[:, 0], Cg[:, 1])
     # sequences are independent: each sequence alone gives the same rows
     np.testing.assert_array_equal(A.attn_core_fwd(QKV[S:], qh, kvh, d, S), A.attn_core_fwd(QKV, qh, kvh, d, S)[S:])
+
+
+def test_attention_backward_finite_differences():
+    for qh, kvh, d, S, nb in [(4, 2, 3, 4, 2), (2, 1, 4, 5, 1), (3, 3, 2, 3, 2)]:
+        pins.check_fd_attn_core(A, seed=qh + d, qh=qh, kvh=kvh, d=d, S=S, nb=nb)
+
+
+def test_attention_backward_torch_autograd():
+    pins.check_torch_attn_core(A, qh=4, kvh=1)
+    pins.check_torch_attn_core(A, seed=1, qh=4, kvh=2, d=8, S=7, nb=3)
+
+
+def test_attention_lse():
+    pins.check_lse(A)
+    pins.check_lse(A, seed=2, qh=4, kvh=2)
+
+
+def test_attention_backward_closed_forms():
+    rng = np.random.default_rng(6)
+    qh, kvh, d, S = 4, 2, 6, 8
+    QKV = rng.standard_normal((2 * S, (qh + 2 * kvh) * d))
+    dC = rng.standard_normal((2 * S, qh * d))
+    # zero upstream gradient: zero everywhere, exactly
+    assert not np.any(A.attn_core_bwd(QKV, np.zeros_like(dC), qh, kvh, d, S))
+    # zero values: dP = 0, so dQ = dK = 0 exactly; dV[s] = sum over the group's heads and t >= s of P[t, s] dC[t]
+    Z = QKV.copy()
+    Z[:, (qh + kvh) * d:] = 0.0
+    g = A.attn_core_bwd(Z, dC, qh, kvh, d, S)
+    assert not np.any(g[:, :(qh + kvh) * d])
+    # the last token of a sequence is seen only by itself: its dV is P[last, last] dC[last] summed over heads
+    q, k, _ = A.split_qkv(Z, qh, kvh, d)
+    lse = A.attn_core_lse(Z, qh, kvh, d, S)
+    last = S - 1
+    for gi in range(kvh):
+        ref = sum(np.exp(q[last, h] @ k[last, gi] / np.sqrt(d) - lse[last, h]) * dC[last, h * d:(h + 1) * d]
+                  for h in range(gi * 2, gi * 2 + 2))
+        np.testing.assert_allclose(g[last, (qh + kvh + gi) * d:(qh + kvh + gi + 1) * d], ref, rtol=1e-13, atol=1e-14)
+    # sequences are independent
+    np.testing.assert_array_equal(A.attn_core_bwd(QKV[S:], dC[S:], qh, kvh, d, S),
+                                  A.attn_core_bwd(QKV, dC, qh, kvh, d, S)[S:])
+
+
+def _mutant_attn(**overrides):
+    m = types.ModuleType("attention_mutant")
+    m.__dict__.update(A.__dict__)
+    m.__dict__.update(overrides)
+    return m
+
+
+def test_planted_attention_dk_dv_swapped():
+    def attn_core_bwd(QKV, dC, qh, kvh, d, S):
+        g = A.attn_core_bwd(QKV, dC, qh, kvh, d, S)
+        k0, v0 = qh * d, (qh + kvh) * d
+        return np.concatenate([g[:, :k0], g[:, v0:], g[:, k0:v0]], axis=1)
+    assert _fails(lambda: pins.check_fd_attn_core(_mutant_attn(attn_core_bwd=attn_core_bwd)))
+
+
+def test_planted_attention_dq_scale_missing():
+    def attn_core_bwd(QKV, dC, qh, kvh, d, S):
+        g = A.attn_core_bwd(QKV, dC, qh, kvh, d, S).copy()
+        g[:, :qh * d] *= np.sqrt(d)
+        return g
+    assert _fails(lambda: pins.check_fd_attn_core(_mutant_attn(attn_core_bwd=attn_core_bwd)))
+
+
+def test_planted_attention_gqa_gradient_not_summed():
+    def attn_core_bwd(QKV, dC, qh, kvh, d, S):
+        # each key/value head keeps only its last query head's share (assignment instead of a sum)
+        g = A.attn_core_bwd(QKV, dC, qh, kvh, d, S).copy()
+        keep = dC.copy()
+        grp = qh // kvh
+        for h in range(qh):
+            if h % grp != grp - 1:
+                keep[:, h * d:(h + 1) * d] = 0.0
+        part = A.attn_core_bwd(QKV, keep, qh, kvh, d, S)
+        g[:, qh * d:] = part[:, qh * d:]
+        return g
+    assert _fails(lambda: pins.check_fd_attn_core(_mutant_attn(attn_core_bwd=attn_core_bwd)))
