@@ -231,8 +231,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
       }
     }
 
-    // ---- C = O / l (bf16), the lane's row and dims 16 jd + 4 lg .. +3
-    const float inv = 1.0f / row_sum4(l);
+    // ---- C = O / l (bf16), the lane's row and dims 16 jd + 4 lg .. +3; the row's log-sum-exp
+    // (natural log) m + log2(l) in log2 units, for the backward pass
+    const float lsum = row_sum4(l);
+    const float inv = 1.0f / lsum;
+    if (a.lse && lg == 0) a.lse[(seq0 + q_row) * a.q_heads + h] = (m + __log2f(lsum)) * 0.69314718055994531f;
     unsigned short* C = reinterpret_cast<unsigned short*>(a.C) + (seq0 + q_row) * a.ld_c + int64_t(h) * kD + 4 * lg;
   #pragma unroll
     for (int jd = 0; jd < kD / 16; ++jd) {

@@ -8,6 +8,7 @@
 #include <new>
 
 #include "plan.hpp"
+#include "attn.hpp"
 #include "gemm.hpp"
 
 namespace tps {
@@ -338,6 +339,7 @@ extern "C" tpslice_status_t tpslice_workspace_size(tpslice_plan_t p, int32_t op,
     case TPSLICE_OP_MLP_BWD: *bytes = mlp_bwd_ws(p).total; return TPSLICE_OK;
     case TPSLICE_OP_ATTNPROJ_FWD: *bytes = attn_fwd_ws(p).total; return TPSLICE_OK;
     case TPSLICE_OP_ATTNPROJ_BWD: *bytes = attn_bwd_ws(p).total; return TPSLICE_OK;
+    case TPSLICE_OP_ATTN_CORE_BWD: *bytes = p->qh ? attn_bwd_workspace_bytes(p->M, p->qh, p->kvh) : 0; return TPSLICE_OK;
     default: return fail(TPSLICE_ERR_INVALID, "unknown op %d", op);
   }
 }

@@ -688,11 +688,8 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
   return S.join();
 }
 
-extern "C" tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t p, const void* QKV, void* C, int64_t seq_len,
-                                                  const tpslice_streams_t* streams) {
-  clear_error();
-  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
-  if (p->M > 0) { TPS_REQ(QKV); TPS_REQ(C); } else { TPS_OPT(QKV); TPS_OPT(C); }
+// Checks shared by the attention core's entry points (before anything is queued).
+static tpslice_status_t check_attn_core(const tpslice_plan_s* p, int64_t seq_len) {
   if (!p->qh) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads");
   if (p->desc.head_dim != kAttnHeadDim)
     return fail(TPSLICE_ERR_UNSUPPORTED, "head_dim %d: the attention core takes %d", p->desc.head_dim, kAttnHeadDim);
@@ -700,11 +697,39 @@ extern "C" tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t p, const void* 
     return fail(TPSLICE_ERR_SHAPE, "seq_len %lld must be a positive multiple of %d dividing the %lld tokens",
                 (long long)seq_len, kAttnBlock, (long long)p->M);
   if (p->qh % p->kvh != 0) return fail(TPSLICE_ERR_SHAPE, "%d query heads over %d kv heads", p->qh, p->kvh);
+  return TPSLICE_OK;
+}
+
+extern "C" tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t p, const void* QKV, void* C, float* lse,
+                                                  int64_t seq_len, const tpslice_streams_t* streams) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (p->M > 0) { TPS_REQ(QKV); TPS_REQ(C); } else { TPS_OPT(QKV); TPS_OPT(C); }
+  TPS_OPT(lse);
+  TPS_TRY(check_attn_core(p, seq_len));
   if (p->M == 0) return TPSLICE_OK;
-  AttnArgs a{QKV, C, p->qkv, p->ctx, p->M, int32_t(seq_len), p->qh, p->kvh,
+  AttnArgs a{QKV, C, lse, p->qkv, p->ctx, p->M, int32_t(seq_len), p->qh, p->kvh,
              float(1.4426950408889634 / std::sqrt(double(kAttnHeadDim)))};
   hipError_t e = launch_attn_fwd(a, streams ? static_cast<hipStream_t>(streams->caller) : nullptr);
   if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  return TPSLICE_OK;
+}
+
+extern "C" tpslice_status_t tpslice_attn_core_bwd(tpslice_plan_t p, const void* QKV, const void* C,
+                                                  const float* lse, const void* dC, void* dQKV, int64_t seq_len,
+                                                  void* ws, size_t ws_bytes, const tpslice_streams_t* streams) {
+  clear_error();
+  if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
+  if (p->M > 0) { TPS_REQ(QKV); TPS_REQ(C); TPS_REQ(lse); TPS_REQ(dC); TPS_REQ(dQKV); }
+  else { TPS_OPT(QKV); TPS_OPT(C); TPS_OPT(lse); TPS_OPT(dC); TPS_OPT(dQKV); }
+  TPS_TRY(check_attn_core(p, seq_len));
+  TPS_TRY(check_ws(ws, ws_bytes, attn_bwd_workspace_bytes(p->M, p->qh, p->kvh)));
+  if (p->M == 0) return TPSLICE_OK;
+  const double sc = 1.0 / std::sqrt(double(kAttnHeadDim));
+  AttnBwdArgs a{QKV, C, dC, lse, dQKV, nullptr, nullptr, p->qkv, p->ctx, p->M, int32_t(seq_len), p->qh, p->kvh,
+                float(sc), float(1.4426950408889634 * sc)};
+  hipError_t e = launch_attn_bwd(a, ws, streams ? static_cast<hipStream_t>(streams->caller) : nullptr);
+  if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "attention backward launch: %s", hipGetErrorString(e));
   return TPSLICE_OK;
 }
 

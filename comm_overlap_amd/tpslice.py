@@ -27,11 +27,12 @@ F_TILE_SHIFT = 8
 # block tile ids (flags bits 8..11); "large" / "small" name the 256 x 256 / 128 x 128 tiles
 TILES = {"auto": 0, "256x256": 1, "128x128": 2, "256x320": 3, "128x320": 4, "128x256": 5,
          "128x128w8": 6, "256x256w4": 7, "256x160w4": 8, "256x320w4": 9, "large": 1, "small": 2}
-OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD = range(4)
+OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD, OP_ATTN_CORE_BWD = range(5)
 EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice_plan_piece",
            "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",
            "tpslice_attnproj_bwd", "tpslice_trace_enable", "tpslice_trace_read",
-           "tpslice_handoff_copy", "tpslice_handoff_wait", "tpslice_attn_core_fwd", "tpslice_mlp_fwd_static",
+           "tpslice_handoff_copy", "tpslice_handoff_wait", "tpslice_attn_core_fwd", "tpslice_attn_core_bwd",
+           "tpslice_mlp_fwd_static",
            "tpslice_error_string", "tpslice_last_error")
 TRACE_GEMM, TRACE_COPY, TRACE_COLSUM, TRACE_SPLIT_SUM = range(4)
 STEPS = ("mlp_up", "mlp_down", "qkv", "out", "mlp_dh", "mlp_dx", "mlp_dw1", "mlp_dw2", "attn_dx", "attn_dc",
@@ -103,9 +104,10 @@ def _load():
     lib.tpslice_trace_read.argtypes = [vp, ctypes.POINTER(TraceRec), i32, ctypes.POINTER(i32)]
     lib.tpslice_handoff_copy.argtypes = [vp, vp, vp, ss]
     lib.tpslice_handoff_wait.argtypes = [vp, vp]
-    lib.tpslice_attn_core_fwd.argtypes = [vp, vp, vp, ctypes.c_int64, ss]
+    lib.tpslice_attn_core_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ss]
+    lib.tpslice_attn_core_bwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, sz, ss]
     lib.tpslice_mlp_fwd_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ss]
-    for name in EXPORTS[:15]:
+    for name in EXPORTS[:16]:
         getattr(lib, name).restype = st
     lib.tpslice_error_string.argtypes = [st]
     lib.tpslice_error_string.restype = ctypes.c_char_p
@@ -400,13 +402,31 @@ class Plan:
                                    _ptr(db1, f32, "db1"), _ptr(dW2, f32, "dW2"), int(bool(accumulate)),
                                    wp, wn, self._call_streams(stream, dX_handoff is not None)))
 
-    def attn_core_fwd(self, QKV, C, seq_len, stream=None):
+    def attn_core_fwd(self, QKV, C, seq_len, lse=None, stream=None):
         """Causal attention of every sequence (seq_len consecutive token rows) and query head:
-        QKV [tokens][(q + 2 kv) head_dim] -> C [tokens][q head_dim], bf16."""
+        QKV [tokens][(q + 2 kv) head_dim] -> C [tokens][q head_dim], bf16; lse [tokens][q] fp32 (each
+        row's log-sum-exp, for the backward pass) when given."""
         i = self.info
         _shape(QKV, (i.tokens, i.qkv_width), "QKV")
         _shape(C, (i.tokens, i.ctx_width), "C")
-        _check(lib.tpslice_attn_core_fwd(self._h, _ptr(QKV), _ptr(C), int(seq_len), self._call_streams(stream, False)))
+        _shape(lse, (i.tokens, i.q_heads), "lse")
+        _check(lib.tpslice_attn_core_fwd(self._h, _ptr(QKV, name="QKV"), _ptr(C, name="C"),
+                                         _ptr(lse, torch.float32, "lse"), int(seq_len),
+                                         self._call_streams(stream, False)))
+
+    def attn_core_bwd(self, QKV, C, lse, dC, dQKV, seq_len, workspace=None, stream=None):
+        """Gradient of the attention core: dQKV [tokens][(q + 2 kv) head_dim] bf16 from the forward's
+        QKV, C and lse and the gradient dC of C."""
+        i = self.info
+        _shape(QKV, (i.tokens, i.qkv_width), "QKV"); _shape(C, (i.tokens, i.ctx_width), "C")
+        _shape(lse, (i.tokens, i.q_heads), "lse"); _shape(dC, (i.tokens, i.ctx_width), "dC")
+        _shape(dQKV, (i.tokens, i.qkv_width), "dQKV")
+        ws = workspace if workspace is not None else self.workspace(OP_ATTN_CORE_BWD)
+        wp, wn = self._ws_args(ws)
+        _check(lib.tpslice_attn_core_bwd(self._h, _ptr(QKV, name="QKV"), _ptr(C, name="C"),
+                                         _ptr(lse, torch.float32, "lse"), _ptr(dC, name="dC"),
+                                         _ptr(dQKV, name="dQKV"), int(seq_len), wp, wn,
+                                         self._call_streams(stream, False)))
 
     def attnproj_bwd(self, X, Wqkv, dQKV, C, Wo, dY, dX, dC, dWqkv, dWo, dbqkv=None, dX_handoff=None,
                      accumulate=False, workspace=None, stream=None):

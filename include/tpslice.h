@@ -175,7 +175,8 @@ typedef enum {
   TPSLICE_OP_MLP_FWD = 0,
   TPSLICE_OP_ATTNPROJ_FWD = 1,
   TPSLICE_OP_MLP_BWD = 2,
-  TPSLICE_OP_ATTNPROJ_BWD = 3
+  TPSLICE_OP_ATTNPROJ_BWD = 3,
+  TPSLICE_OP_ATTN_CORE_BWD = 4
 } tpslice_op_t;
 
 /* Validate `desc` and build a plan (host memory only; no GPU call is made). The slice geometry is
@@ -256,12 +257,33 @@ TPSLICE_API tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t plan, const voi
  *   g = h / (q_heads / kv_heads), t and s positions in the same sequence.
  * Inputs : QKV [M][(q + 2 kv) head_dim] bf16 as tpslice_attnproj_fwd writes it (Q heads, K heads,
  *          V heads); the sequences are consecutive runs of `seq_len` token rows.
- * Outputs: C [M][q head_dim] bf16, the context the output projection reads.
+ * Outputs: C [M][q head_dim] bf16, the context the output projection reads; lse [M][q] fp32 or
+ *          NULL: each row's log-sum-exp of its scaled scores (natural log), which
+ *          tpslice_attn_core_bwd takes.
  * Requires the plan's head_dim = 128 (else TPSLICE_ERR_UNSUPPORTED), seq_len a multiple of 128
  * that divides the token count (else TPSLICE_ERR_SHAPE). Softmax in fp32; the probabilities are
  * rounded to bf16 for the product with V. Runs on streams->caller (no slicing, no hand-off).      */
-TPSLICE_API tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t plan, const void* QKV, void* C, int64_t seq_len,
-                                       const tpslice_streams_t* streams);
+TPSLICE_API tpslice_status_t tpslice_attn_core_fwd(tpslice_plan_t plan, const void* QKV, void* C, float* lse,
+                                                   int64_t seq_len, const tpslice_streams_t* streams);
+
+/* Causal attention core, backward: the gradient of tpslice_attn_core_fwd by the chain rule through
+ * the softmax, computed in tiles from the forward's inputs, output and row log-sum-exp (the
+ * FlashAttention titles on the Domino page's builds-on list):
+ *   dV[s, g] = sum over the group's heads h, t >= s of P[t, s] dC[t, h]
+ *   dA[t, s] = P[t, s] (dC[t, h] . V[s, g] - dC[t, h] . C[t, h])
+ *   dQ[t, h] = sum over s <= t of dA[t, s] K[s, g] / sqrt(head_dim)
+ *   dK[s, g] = sum over the group's heads h, t >= s of dA[t, s] Q[t, h] / sqrt(head_dim)
+ * Inputs : QKV, C and lse as the forward took and wrote them; dC [M][q head_dim] bf16, the gradient
+ *          of C (tpslice_attnproj_bwd's dC).
+ * Outputs: dQKV [M][(q + 2 kv) head_dim] bf16 in QKV's column layout (the dQKV that
+ *          tpslice_attnproj_bwd takes). Grouped key/value heads sum their query heads' shares in
+ *          head order (deterministic).
+ * Workspace: tpslice_workspace_size(TPSLICE_OP_ATTN_CORE_BWD) bytes. Same requirements as the
+ * forward. Runs on streams->caller.                                                              */
+TPSLICE_API tpslice_status_t tpslice_attn_core_bwd(tpslice_plan_t plan, const void* QKV, const void* C,
+                                                   const float* lse, const void* dC, void* dQKV, int64_t seq_len,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   const tpslice_streams_t* streams);
 
 /* Allocation-free MLP forward, for callers that cannot allocate device memory (code under stream
  * capture, tight serving loops, harnesses that forbid allocation): tpslice_mlp_fwd with its

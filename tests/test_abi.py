@@ -255,20 +255,34 @@ def test_handoff_rows_flag():
 
 
 def test_attention_core_argument_errors():
-    """The attention core checks its plan and sizes before any GPU work (pointers never read)."""
+    """The attention core (forward and backward) checks its plan, sizes, pointers and workspace
+    before any GPU work (pointers never read)."""
     lib = T.lib
     A = _fake(0x100000)
     no_heads = T.Plan(T.Config(tokens=256, hidden=64, ffn=64))
-    assert lib.tpslice_attn_core_fwd(no_heads._h, A, A, 128, None) == T.ERR_UNSUPPORTED
+    assert lib.tpslice_attn_core_fwd(no_heads._h, A, A, None, 128, None) == T.ERR_UNSUPPORTED
     d64 = T.Plan(T.Config(tokens=256, hidden=512, ffn=64, n_heads=4, n_kv_heads=2, head_dim=64))
-    assert lib.tpslice_attn_core_fwd(d64._h, A, A, 128, None) == T.ERR_UNSUPPORTED
+    assert lib.tpslice_attn_core_fwd(d64._h, A, A, None, 128, None) == T.ERR_UNSUPPORTED
     assert b"head_dim 64" in lib.tpslice_last_error()
     p = T.Plan(T.Config(tokens=256, hidden=512, ffn=64, n_heads=4, n_kv_heads=2, head_dim=128))
     for bad in (0, -128, 64, 96, 192, 512):  # not a multiple of 128, or not dividing the 256 tokens
-        assert lib.tpslice_attn_core_fwd(p._h, A, A, bad, None) == T.ERR_SHAPE, bad
-    assert lib.tpslice_attn_core_fwd(p._h, None, A, 128, None) == T.ERR_INVALID
-    assert lib.tpslice_attn_core_fwd(p._h, A, _fake(0x100008), 128, None) == T.ERR_INVALID
-    assert lib.tpslice_attn_core_fwd(None, A, A, 128, None) == T.ERR_INVALID
+        assert lib.tpslice_attn_core_fwd(p._h, A, A, None, bad, None) == T.ERR_SHAPE, bad
+    assert lib.tpslice_attn_core_fwd(p._h, None, A, None, 128, None) == T.ERR_INVALID
+    assert lib.tpslice_attn_core_fwd(p._h, A, _fake(0x100008), None, 128, None) == T.ERR_INVALID
+    assert lib.tpslice_attn_core_fwd(p._h, A, A, _fake(0x100004), 128, None) == T.ERR_INVALID
+    assert lib.tpslice_attn_core_fwd(None, A, A, None, 128, None) == T.ERR_INVALID
+    # backward: the workspace holds D per (token, query head) and, with grouped heads (4 query
+    # heads over 2 key/value heads here), fp32 dK and dV partials of every query head
+    need = p.workspace_size(T.OP_ATTN_CORE_BWD)
+    assert need >= 256 * 4 * 4 + 2 * 4 * 256 * 128 * 4
+    bwd = lib.tpslice_attn_core_bwd
+    assert bwd(p._h, A, A, A, A, A, 128, A, need - 1, None) == T.ERR_WORKSPACE
+    assert bwd(p._h, A, A, A, A, A, 128, None, 0, None) == T.ERR_WORKSPACE
+    assert bwd(p._h, A, A, None, A, A, 128, A, need, None) == T.ERR_INVALID
+    assert bwd(p._h, A, A, A, A, A, 96, A, need, None) == T.ERR_SHAPE
+    assert bwd(d64._h, A, A, A, A, A, 128, A, need, None) == T.ERR_UNSUPPORTED
+    ungrouped = T.Plan(T.Config(tokens=256, hidden=512, ffn=64, n_heads=4, n_kv_heads=4, head_dim=128))
+    assert ungrouped.workspace_size(T.OP_ATTN_CORE_BWD) == 256 * 4 * 4  # D only
 
 
 def test_bench_rejects_more_than_one_gpu():

@@ -83,3 +83,87 @@ def test_attention_core_workload_sequence(key):
     _, C = _run(w, QKV, seq)
     ref = A.attn_core_fwd(L.as_f64(QKV[-seq:]), w.q_heads_shard, w.kv_heads_shard, 128, seq)
     G.assert_parity(C[-seq:], ref, "C (last sequence)")
+
+
+# ------------------------------------------------------------------------------------- backward
+def _run_bwd(w, QKV, dC, seq_len):
+    """Forward with the row log-sum-exp, then the backward; (C, lse, dQKV) on the GPU."""
+    plan = T.plan_for(w)
+    i = plan.info
+    C = torch.full((i.tokens, i.ctx_width), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((i.tokens, i.q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    dQKV = torch.full((i.tokens, i.qkv_width), float("nan"), dtype=torch.bfloat16, device="cuda")
+    q = G.dev(QKV)
+    plan.attn_core_fwd(q, C, seq_len, lse=lse)
+    plan.attn_core_bwd(q, C, lse, G.dev(dC), dQKV, seq_len)
+    torch.cuda.synchronize()
+    plan.close()
+    return C, lse, dQKV
+
+
+def _check_dqkv(dQKV, ref, qh, kvh, label=""):
+    """Parity of dQ, dK and dV (each a tensor of its own) with the oracle."""
+    q0, k0 = qh * 128, (qh + kvh) * 128
+    G.assert_parity(dQKV[:, :q0], ref[:, :q0], "dQ" + label)
+    G.assert_parity(dQKV[:, q0:k0], ref[:, q0:k0], "dK" + label)
+    G.assert_parity(dQKV[:, k0:], ref[:, k0:], "dV" + label)
+
+
+@pytest.mark.parametrize("tokens,seq_len,heads,kv_heads,tp", SMALL)
+def test_attention_core_backward_small(tokens, seq_len, heads, kv_heads, tp):
+    """dQ, dK and dV against the oracle's gradient (several key and query blocks per sequence,
+    several sequences, grouped and ungrouped key/value heads); the forward's row log-sum-exp against
+    the oracle's; the same bits on a second run; a sequence alone gives its rows of the batch."""
+    w = synth.custom("attn_bwd", 940, tokens=tokens, hidden=256, ffn=64, tp=tp, act="gelu", bias=False,
+                     row_slices=1, col_slices=1, heads=heads, kv_heads=kv_heads, head_dim=128)
+    qh, kvh = w.q_heads_shard, w.kv_heads_shard
+    _case("backward", tokens=tokens, seq_len=seq_len, q=qh, kv=kvh)
+    QKV = synth.randn_bf16((tokens, w.qkv_width), 1.0, 941)
+    dC = synth.randn_bf16((tokens, w.ctx_width), 1.0, 942)
+    C, lse, dQKV = _run_bwd(w, QKV, dC, seq_len)
+    f = L.as_f64
+    ref_lse = A.attn_core_lse(f(QKV), qh, kvh, 128, seq_len)
+    G.assert_parity(lse, ref_lse, "lse")
+    ref = A.attn_core_bwd(f(QKV), f(dC), qh, kvh, 128, seq_len)
+    _check_dqkv(dQKV, ref, qh, kvh)
+    _, _, again = _run_bwd(w, QKV, dC, seq_len)
+    assert torch.equal(again, dQKV)
+    if tokens // seq_len > 1:
+        w1 = synth.custom("attn_bwd1", 940, tokens=seq_len, hidden=256, ffn=64, tp=tp, act="gelu", bias=False,
+                          row_slices=1, col_slices=1, heads=heads, kv_heads=kv_heads, head_dim=128)
+        _, _, one = _run_bwd(w1, QKV[-seq_len:].contiguous(), dC[-seq_len:].contiguous(), seq_len)
+        assert torch.equal(one, dQKV[-seq_len:])
+
+
+def test_attention_core_backward_closed_forms():
+    """Zero upstream gradient: dQKV is zero exactly. Zero values: dQ = dK = 0 exactly (dP = 0)."""
+    w = synth.custom("attn_bwd_cf", 943, tokens=256, hidden=256, ffn=64, tp=2, act="gelu", bias=False,
+                     row_slices=1, col_slices=1, heads=8, kv_heads=2, head_dim=128)
+    qh, kvh = w.q_heads_shard, w.kv_heads_shard
+    QKV = synth.randn_bf16((256, w.qkv_width), 1.0, 944)
+    dC = synth.randn_bf16((256, w.ctx_width), 1.0, 945)
+    _, _, d0 = _run_bwd(w, QKV, torch.zeros_like(dC), 128)
+    assert torch.count_nonzero(d0.float()) == 0
+    Z = QKV.clone()
+    Z[:, (qh + kvh) * 128:] = 0
+    _, _, dz = _run_bwd(w, Z, dC, 128)
+    assert torch.count_nonzero(dz[:, :(qh + kvh) * 128].float()) == 0
+    ref = A.attn_core_bwd(L.as_f64(Z), L.as_f64(dC), qh, kvh, 128, 128)
+    G.assert_parity(dz[:, (qh + kvh) * 128:], ref[:, (qh + kvh) * 128:], "dV (zero values)")
+
+
+@pytest.mark.parametrize("key", ["llama2_13b_layer", "llama3_70b_layer"])
+def test_attention_core_backward_workload_sequence(key):
+    """The workload's shard shape at 2048-token sequences: every row of the first and the last
+    sequence against the oracle (sequences are independent)."""
+    w = synth.WORKLOADS[key]
+    seq = 2048
+    qh, kvh = w.q_heads_shard, w.kv_heads_shard
+    _case("backward workload", key=key, tokens=w.tokens, seq_len=seq)
+    QKV = synth.randn_bf16((w.tokens, w.qkv_width), 1.0, 946)
+    dC = synth.randn_bf16((w.tokens, w.ctx_width), 1.0, 947)
+    _, _, dQKV = _run_bwd(w, QKV, dC, seq)
+    f = L.as_f64
+    for rows, label in ((slice(0, seq), " (first sequence)"), (slice(w.tokens - seq, w.tokens), " (last sequence)")):
+        ref = A.attn_core_bwd(f(QKV[rows]), f(dC[rows]), qh, kvh, 128, seq)
+        _check_dqkv(dQKV[rows], ref, qh, kvh, label)
