@@ -316,35 +316,95 @@ def hidden_from_trace(recs):
     return (hid / tot if tot > 0 else None), tot
 
 
+def core_flops(w, seq_len):
+    """Algorithmic flops of the causal attention core over the layer's tokens: per query head and
+    sequence, the causal pairs (t >= s: seq_len (seq_len + 1) / 2) times 2 head_dim for each product;
+    two products forward (S, PV), four backward (dV, dP, dK, dQ; recomputing S is not counted)."""
+    pairs = seq_len * (seq_len + 1) / 2.0
+    per = pairs * 2.0 * 128 * w.q_heads_shard * (w.tokens // seq_len)
+    return 2.0 * per, 4.0 * per
+
+
 def attn_core(w, inp, seq_len, steps):
-    """The causal attention core between the projections (tpslice_attn_core_fwd) over the layer's
-    tokens as sequences of seq_len rows, timed alone on the caller's stream (not part of the
-    layer's GEMM chain above). Flops: 2 seq_len^2 head_dim per query head and sequence (the causal
-    half of QK^T and PV)."""
+    """The causal attention core between the projections (tpslice_attn_core_fwd and _bwd) over the
+    layer's tokens as sequences of seq_len rows, each timed alone on the caller's stream."""
     import torch
     from comm_overlap_amd import synth
     from comm_overlap_amd import tpslice as T
     if w.tokens % seq_len:
         return None
     plan = T.plan_for(w)
+    i = plan.info
     qkv = synth.randn_bf16((w.tokens, w.qkv_width), 1.0, 7).cuda()
-    c = torch.empty(w.tokens, plan.info.ctx_width, dtype=torch.bfloat16, device="cuda")
-    for _ in range(5):
-        plan.attn_core_fwd(qkv, c, seq_len)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = max(10, steps)
-    e0.record()
-    for _ in range(n):
-        plan.attn_core_fwd(qkv, c, seq_len)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
-    flops = 2.0 * seq_len * seq_len * 128 * w.q_heads_shard * (w.tokens // seq_len)
+    dc = synth.randn_bf16((w.tokens, i.ctx_width), 1.0, 8).cuda()
+    c = torch.empty(w.tokens, i.ctx_width, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(w.tokens, i.q_heads, dtype=torch.float32, device="cuda")
+    dqkv = torch.empty_like(qkv)
+    plan.workspace(T.OP_ATTN_CORE_BWD)
+    fwd = lambda: plan.attn_core_fwd(qkv, c, seq_len, lse=lse)
+    bwd = lambda: plan.attn_core_bwd(qkv, c, lse, dc, dqkv, seq_len)
+    out = {"seq_len": seq_len, "q_heads": w.q_heads_shard, "kv_heads": w.kv_heads_shard, "head_dim": 128}
+    fl = dict(zip(("fwd", "bwd"), core_flops(w, seq_len)))
+    for name, fn in (("fwd", fwd), ("bwd", bwd)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(10, steps)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        tf = fl[name] / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     plan.close()
-    return {"seq_len": seq_len, "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-            "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "q_heads": w.q_heads_shard, "kv_heads": w.kv_heads_shard, "head_dim": 128}
+    return out
+
+
+class LayerWithCore:
+    """The whole layer step with the attention core between the projections: QKV, the core, the
+    output projection (hand-off) and the MLP (hand-off); backward: the MLP, the output projection's
+    dC, the core's backward and the QKV projection's dX (hand-off) and weight gradients. Steps are
+    chained as in Chain (each reads the previous step's hand-off)."""
+
+    def __init__(self, w, plan, dev, seq_len):
+        import torch
+        self.w, self.p, self.t, self.seq = w, plan, dev, seq_len
+        i = plan.info
+        bf, f32 = torch.bfloat16, torch.float32
+        e = lambda *s, dt=bf: torch.empty(*s, dtype=dt, device="cuda")
+        self.sets = []
+        for _ in range(2):
+            self.sets.append(dict(QKV=e(i.tokens, i.qkv_width), C=e(i.tokens, i.ctx_width),
+                                  lse=e(i.tokens, i.q_heads, dt=f32), Za=e(i.tokens, i.hidden),
+                                  Zah=e(i.tokens, i.hidden), U=e(i.tokens, i.n1), Z=e(i.tokens, i.hidden),
+                                  Zh=e(i.tokens, i.hidden), dX=e(i.tokens, i.hidden), dXh=e(i.tokens, i.hidden),
+                                  dC=e(i.tokens, i.ctx_width), dQKV=e(i.tokens, i.qkv_width),
+                                  dXa=e(i.tokens, i.hidden), dXah=e(i.tokens, i.hidden)))
+        for o in self.sets:
+            o["Zh"].copy_(dev["X"])
+        self.g = dict(dW1=e(i.n1, i.hidden, dt=f32), dW2=e(i.hidden, i.ffn_shard, dt=f32),
+                      dWo=e(i.hidden, i.ctx_width, dt=f32), dWqkv=e(i.qkv_width, i.hidden, dt=f32))
+        for op in range(5):
+            plan.workspace(op)
+        self.n = 0
+
+    def __call__(self):
+        p, t, g, s = self.p, self.t, self.g, self.seq
+        o, prev = self.sets[self.n % 2], self.sets[(self.n + 1) % 2]
+        x = prev["Zh"]
+        p.attnproj_fwd(x, t["Wqkv"], None, o["QKV"], None, None, None)
+        p.attn_core_fwd(o["QKV"], o["C"], s, lse=o["lse"])
+        p.attnproj_fwd(None, None, None, None, o["C"], t["Wo"], o["Za"], o["Zah"])
+        p.mlp_fwd(o["Zah"], t["W1"], t.get("b1"), t["W2"], o["Z"], o["U"], o["Zh"])
+        p.mlp_bwd(o["Zah"], t["W1"], t["W2"], o["U"], t["dY"], o["dX"], g["dW1"], g["dW2"], dX_handoff=o["dXh"])
+        p.attnproj_bwd(None, None, None, o["C"], t["Wo"], o["dXh"], None, o["dC"], None, g["dWo"])
+        p.attn_core_bwd(o["QKV"], o["C"], o["lse"], o["dC"], o["dQKV"], s)
+        p.attnproj_bwd(x, t["Wqkv"], o["dQKV"], None, None, None, o["dXa"], None, g["dWqkv"], None,
+                       dX_handoff=o["dXah"])
+        self.n += 1
 
 
 def cpu_baseline(w, inp, target_s):
@@ -487,6 +547,20 @@ def main():
             ts.bwd_plan.close()
             del ts
 
+    # 6) the whole layer with the attention core between the projections (layer workloads)
+    layer_core = None
+    if w.has_attn and w.backward and not args.no_attn_core and w.tokens % args.attn_seq == 0:
+        log("layer step with the attention core")
+        lc = LayerWithCore(w, plan, dev, args.attn_seq)
+        ms_lc = timed(lc, K, 2, [plan])
+        cf, cb = core_flops(w, args.attn_seq)
+        fl_lc = flops + cf + cb
+        layer_core = {"seq_len": args.attn_seq, "ms_per_step": round(ms_lc, 4),
+                      "tflops": round(fl_lc / (ms_lc * 1e-3) / 1e12, 2),
+                      "pct_of_peak": round(100.0 * fl_lc / (ms_lc * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                      "gflop_per_step": round(fl_lc / 1e9, 1), "core_gflop_per_step": round((cf + cb) / 1e9, 1)}
+        del lc
+
     tflops = flops / (ms * 1e-3) / 1e12
     # the dominant kernel: the GEMM kernel (template parameters and grid) with the largest share of
     # the step's product time; its launches may serve more than one product of that grid
@@ -535,6 +609,8 @@ def main():
     }
     if two is not None:
         out["two_strands"] = two
+    if layer_core is not None:
+        out["layer_with_attention_core"] = layer_core
     if w.has_attn and not args.no_attn_core:
         log("attention core")
         out["attn_core"] = attn_core(w, inp, args.attn_seq, K)

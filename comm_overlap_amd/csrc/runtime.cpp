@@ -596,10 +596,22 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   if (p->qh == 0) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads (n_heads = 0)");
-  TPS_REQ(Wqkv); TPS_REQ(Wo);
-  if (p->M > 0) { TPS_REQ(X); TPS_REQ(QKV); TPS_REQ(C); TPS_REQ(Z); }
-  else { TPS_OPT(X); TPS_OPT(QKV); TPS_OPT(C); TPS_OPT(Z); }
-  TPS_OPT(bqkv); TPS_OPT(Z_handoff);
+  // Wqkv NULL: no QKV projection (X, bqkv, QKV unused); Wo NULL: no output projection (C, Z,
+  // Z_handoff unused), e.g. with the attention core between the two
+  const bool do_qkv = Wqkv != nullptr, do_out = Wo != nullptr;
+  if (!do_qkv && !do_out) return fail(TPSLICE_ERR_INVALID, "Wqkv and Wo are both NULL: nothing to compute");
+  if (do_qkv) {
+    TPS_REQ(Wqkv);
+    if (p->M > 0) { TPS_REQ(X); TPS_REQ(QKV); } else { TPS_OPT(X); TPS_OPT(QKV); }
+    TPS_OPT(bqkv);
+  }
+  if (do_out) {
+    TPS_REQ(Wo);
+    if (p->M > 0) { TPS_REQ(C); TPS_REQ(Z); } else { TPS_OPT(C); TPS_OPT(Z); }
+    TPS_OPT(Z_handoff);
+  } else {
+    Z_handoff = nullptr;
+  }
   const AttnFwdWs L = attn_fwd_ws(p);
   TPS_TRY(check_ws(ws, ws_bytes, L.total));
   CallStreams cs;
@@ -614,7 +626,7 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
     TPS_TRY(S.slice_begin(i));
     S.slice_streams = 0;
     // output projection first: its pieces are the hand-off, the QKV product then runs under the copies
-    for (int j = 0; j < p->pc; ++j) {
+    for (int j = 0; do_out && j < p->pc; ++j) {
       const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs g = args(bf(C, r0 * p->ctx), p->ctx, bf(Wo, c0 * p->ctx), p->ctx, bfw(Z, r0 * p->h + c0), p->h,
                         p->Ms, p->pw, p->ctx);
@@ -622,10 +634,12 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
       if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
     }
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
-    GemmArgs q = args(bf(X, r0 * p->h), p->h, Wqkv, p->h, bfw(QKV, r0 * p->qkv), p->qkv, p->Ms, p->qkv, p->h);
-    q.bias = bqkv;
-    TPS_TRY(S.product_split(i, TPSLICE_STEP_QKV, -1, q, kFwd, kEpiBf16, p->sp_qkv,
-                            S.slice_part(static_cast<char*>(ws) + L.qkv_split, L.qkv_split_bytes, i)));
+    if (do_qkv) {
+      GemmArgs q = args(bf(X, r0 * p->h), p->h, Wqkv, p->h, bfw(QKV, r0 * p->qkv), p->qkv, p->Ms, p->qkv, p->h);
+      q.bias = bqkv;
+      TPS_TRY(S.product_split(i, TPSLICE_STEP_QKV, -1, q, kFwd, kEpiBf16, p->sp_qkv,
+                              S.slice_part(static_cast<char*>(ws) + L.qkv_split, L.qkv_split_bytes, i)));
+    }
   }
   return S.join();
 }
@@ -674,7 +688,8 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
   }
   // weight gradients over all tokens at once (one k run, no split of the token sum), under the
-  // last pieces' copies; dW1 and dW2 run side by side on two workers
+  // last pieces' copies, one after another on worker 0 (side by side on two workers each took half
+  // the CUs for the same total time)
   TPS_TRY(S.gather_slices());
   GemmArgs g1 = args(dU, p->N1, X, p->h, dW1, p->h, p->N1, p->h, p->M);
   g1.accumulate = accumulate;
@@ -683,8 +698,8 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
   GemmArgs g2 = args(dY, p->h, H, p->Fp, dW2, p->Fp, p->h, p->Fp, p->M);
   g2.accumulate = accumulate;
   TPS_TRY(S.product_split(-1, TPSLICE_STEP_MLP_DW2, -1, g2, kWgrad, kEpiF32, p->sp_dw2,
-                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw2_split), 1));
-  if (db1) TPS_TRY(S.colsum(dU, p->N1, p->M, p->N1, partials, db1, accumulate, 1));
+                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw2_split), 0));
+  if (db1) TPS_TRY(S.colsum(dU, p->N1, p->M, p->N1, partials, db1, accumulate, 0));
   return S.join();
 }
 
@@ -741,10 +756,23 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
   clear_error();
   if (!plan_ok(p)) return fail(TPSLICE_ERR_INVALID, "invalid plan handle");
   if (p->qh == 0) return fail(TPSLICE_ERR_UNSUPPORTED, "the plan has no attention heads (n_heads = 0)");
-  TPS_REQ(Wqkv); TPS_REQ(Wo); TPS_REQ(dWqkv); TPS_REQ(dWo);
-  if (p->M > 0) { TPS_REQ(X); TPS_REQ(dQKV); TPS_REQ(C); TPS_REQ(dY); TPS_REQ(dX); TPS_REQ(dC); }
-  else { TPS_OPT(X); TPS_OPT(dQKV); TPS_OPT(C); TPS_OPT(dY); TPS_OPT(dX); TPS_OPT(dC); }
-  TPS_OPT(dbqkv); TPS_OPT(dX_handoff);
+  // Wo NULL: no output-projection gradients (C, dY, dC, dWo unused); Wqkv NULL: no QKV-projection
+  // gradients (X, dQKV, dX, dX_handoff, dWqkv, dbqkv unused). With the attention core between them,
+  // the first half gives dC for the core's backward, whose dQKV the second half takes.
+  const bool do_out = Wo != nullptr, do_qkv = Wqkv != nullptr;
+  if (!do_qkv && !do_out) return fail(TPSLICE_ERR_INVALID, "Wqkv and Wo are both NULL: nothing to compute");
+  if (do_out) {
+    TPS_REQ(Wo); TPS_REQ(dWo);
+    if (p->M > 0) { TPS_REQ(C); TPS_REQ(dY); TPS_REQ(dC); } else { TPS_OPT(C); TPS_OPT(dY); TPS_OPT(dC); }
+  }
+  if (do_qkv) {
+    TPS_REQ(Wqkv); TPS_REQ(dWqkv);
+    if (p->M > 0) { TPS_REQ(X); TPS_REQ(dQKV); TPS_REQ(dX); } else { TPS_OPT(X); TPS_OPT(dQKV); TPS_OPT(dX); }
+    TPS_OPT(dbqkv); TPS_OPT(dX_handoff);
+  } else {
+    dX_handoff = nullptr;
+    dbqkv = nullptr;
+  }
   if (accumulate != 0 && accumulate != 1) return fail(TPSLICE_ERR_INVALID, "accumulate must be 0 or 1");
   const AttnBwdWs L = attn_bwd_ws(p);
   TPS_TRY(check_ws(ws, ws_bytes, L.total));
@@ -755,7 +783,7 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
   Schedule S = schedule(p, rt, cs);
   float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + L.partials);
   TPS_TRY(S.fork());
-  for (int i = 0; i < p->r && p->M > 0; ++i) {
+  for (int i = 0; i < p->r && p->M > 0 && do_qkv; ++i) {
     const int64_t r0 = int64_t(i) * p->Ms;
     TPS_TRY(S.slice_begin(i));
     S.slice_streams = 0;
@@ -769,22 +797,28 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
   }
   // dC is handed to the attention core, not off the GPU: it runs over all tokens (narrow output,
-  // so the whole batch fills the CUs better than a slice), beside the weight gradients
+  // so the whole batch fills the CUs better than a slice), then the weight gradients, one after
+  // another on worker 0 (measured on the Llama-3 70B shard: side by side on two workers, each at
+  // half the CUs, they took 0.81 ms against 0.74 ms in sequence)
   TPS_TRY(S.gather_slices());
-  if (p->M > 0) {
-    GemmArgs gc = args(dY, p->h, Wo, p->ctx, dC, p->ctx, p->M, p->ctx, p->h);
-    TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DC, -1, gc, kDgrad, kEpiBf16, p->sp_dc,
-                            reinterpret_cast<float*>(static_cast<char*>(ws) + L.dc_split), 1));
+  if (do_out) {
+    if (p->M > 0) {
+      GemmArgs gc = args(dY, p->h, Wo, p->ctx, dC, p->ctx, p->M, p->ctx, p->h);
+      TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DC, -1, gc, kDgrad, kEpiBf16, p->sp_dc,
+                              reinterpret_cast<float*>(static_cast<char*>(ws) + L.dc_split), 0));
+    }
+    GemmArgs go = args(dY, p->h, C, p->ctx, dWo, p->ctx, p->h, p->ctx, p->M);
+    go.accumulate = accumulate;
+    TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DWO, -1, go, kWgrad, kEpiF32, p->sp_dwo,
+                            reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwo_split), 0));
   }
-  GemmArgs go = args(dY, p->h, C, p->ctx, dWo, p->ctx, p->h, p->ctx, p->M);
-  go.accumulate = accumulate;
-  TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DWO, -1, go, kWgrad, kEpiF32, p->sp_dwo,
-                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwo_split), 1));
-  GemmArgs gq = args(dQKV, p->qkv, X, p->h, dWqkv, p->h, p->qkv, p->h, p->M);
-  gq.accumulate = accumulate;
-  TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DWQKV, -1, gq, kWgrad, kEpiF32, p->sp_dwqkv,
-                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwqkv_split), 0));
-  if (dbqkv) TPS_TRY(S.colsum(dQKV, p->qkv, p->M, p->qkv, partials, dbqkv, accumulate, 0));
+  if (do_qkv) {
+    GemmArgs gq = args(dQKV, p->qkv, X, p->h, dWqkv, p->h, p->qkv, p->h, p->M);
+    gq.accumulate = accumulate;
+    TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DWQKV, -1, gq, kWgrad, kEpiF32, p->sp_dwqkv,
+                            reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwqkv_split), 0));
+    if (dbqkv) TPS_TRY(S.colsum(dQKV, p->qkv, p->M, p->qkv, partials, dbqkv, accumulate, 0));
+  }
   return S.join();
 }
 

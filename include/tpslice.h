@@ -219,7 +219,10 @@ TPSLICE_API tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t plan, const void* X,
  * page, Abstract).
  *   QKV = X Wqkv^T (+ bqkv)   column-parallel;   Z = C Wo^T   row-parallel partial sum
  * C is the attention context of this rank's heads (an input here; tpslice_attn_core_fwd computes it
- * from QKV). Z_handoff as in tpslice_mlp_fwd. Needs n_heads > 0 in the plan.                      */
+ * from QKV). Z_handoff as in tpslice_mlp_fwd. Needs n_heads > 0 in the plan. Either projection may
+ * be left out: Wqkv = NULL skips QKV (X, bqkv, QKV unused), Wo = NULL skips Z (C, Z, Z_handoff
+ * unused), so that a layer can run QKV, then tpslice_attn_core_fwd, then the output projection;
+ * both NULL is TPSLICE_ERR_INVALID.                                                              */
 TPSLICE_API tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t plan, const void* X, const void* Wqkv,
                                       const void* bqkv, void* QKV, const void* C, const void* Wo,
                                       void* Z, void* Z_handoff, void* workspace,
@@ -243,7 +246,10 @@ TPSLICE_API tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t plan, const void* X,
  * sliced and handed off as tpslice_mlp_bwd. Given dQKV [M][(q+2kv)d] (from the attention core) and
  * dY [M][h] (into the output projection):
  *   dC = dY Wo;  dWo (+)= dY^T C;  dX = dQKV Wqkv (partial sum, hand-off);  dWqkv (+)= dQKV^T X;
- *   dbqkv (+)= column sums of dQKV (or NULL).  dC bf16; weight/bias gradients fp32.              */
+ *   dbqkv (+)= column sums of dQKV (or NULL).  dC bf16; weight/bias gradients fp32.
+ * Either half may be left out: Wo = NULL skips dC and dWo (C, dY, dC, dWo unused), Wqkv = NULL skips
+ * dX, dWqkv and dbqkv (X, dQKV, dX, dX_handoff, dWqkv, dbqkv unused), so that a layer can take dC to
+ * tpslice_attn_core_bwd and its dQKV back here; both NULL is TPSLICE_ERR_INVALID.                */
 TPSLICE_API tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t plan, const void* X, const void* Wqkv,
                                       const void* dQKV, const void* C, const void* Wo,
                                       const void* dY, void* dX, void* dX_handoff, void* dC,
