@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtpslice.so")
-SOURCES = ["plan.cpp", "runtime.cpp", "static_scratch.cpp", "gemm.hip", "attn.hip", "attn_bwd.hip"]
+SOURCES = ["plan.cpp", "strands.cpp", "runtime.cpp", "static_scratch.cpp", "gemm.hip", "attn.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",

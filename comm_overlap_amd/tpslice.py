@@ -32,7 +32,7 @@ EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice
            "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",
            "tpslice_attnproj_bwd", "tpslice_trace_enable", "tpslice_trace_read",
            "tpslice_handoff_copy", "tpslice_handoff_wait", "tpslice_attn_core_fwd", "tpslice_attn_core_bwd",
-           "tpslice_mlp_fwd_static",
+           "tpslice_mlp_fwd_static", "tpslice_strand_schedule",
            "tpslice_error_string", "tpslice_last_error")
 TRACE_GEMM, TRACE_COPY, TRACE_COLSUM, TRACE_SPLIT_SUM = range(4)
 STEPS = ("mlp_up", "mlp_down", "qkv", "out", "mlp_dh", "mlp_dx", "mlp_dw1", "mlp_dw2", "attn_dx", "attn_dc",
@@ -107,7 +107,9 @@ def _load():
     lib.tpslice_attn_core_fwd.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ss]
     lib.tpslice_attn_core_bwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, sz, ss]
     lib.tpslice_mlp_fwd_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ss]
-    for name in EXPORTS[:16]:
+    lib.tpslice_strand_schedule.argtypes = [ctypes.POINTER(ctypes.c_double), i32, i32, ctypes.POINTER(i32),
+                                            ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]
+    for name in EXPORTS[:17]:
         getattr(lib, name).restype = st
     lib.tpslice_error_string.argtypes = [st]
     lib.tpslice_error_string.restype = ctypes.c_char_p
@@ -456,3 +458,17 @@ def plan_for(workload, streams: Optional[Streams] = None, **overrides) -> Plan:
               n_kv_heads=workload.kv_heads, head_dim=workload.head_dim, act=workload.act)
     kw.update(overrides)
     return Plan(Config(**kw), streams)
+
+
+def strand_schedule(P):
+    """The pairing of least total time of two strands' segments (tpslice_strand_schedule).
+    P: (nf + 1) x (nb + 1) nested sequence of measured times as the C function takes them.
+    Returns (steps, makespan): steps a list of (forward, backward) 1-based segment numbers, 0 for
+    none, in execution order."""
+    nf, nb = len(P) - 1, len(P[0]) - 1
+    flat = (ctypes.c_double * ((nf + 1) * (nb + 1)))(*[float(v) for row in P for v in row])
+    steps = (ctypes.c_int32 * max(2, 2 * (nf + nb)))()
+    n = ctypes.c_int32()
+    t = ctypes.c_double()
+    _check(lib.tpslice_strand_schedule(flat, nf, nb, steps, ctypes.byref(n), ctypes.byref(t)))
+    return [(steps[2 * k], steps[2 * k + 1]) for k in range(n.value)], t.value

@@ -368,6 +368,21 @@ TPSLICE_API tpslice_status_t tpslice_handoff_copy(tpslice_plan_t plan, const voi
  * with TPSLICE_F_PIPELINE; a no-op before the plan's first call).                                */
 TPSLICE_API tpslice_status_t tpslice_handoff_wait(tpslice_plan_t plan, void* stream);
 
+/* Two-strand pairing (host only; no GPU work). The forward segments 1..nf of one micro-batch and
+ * the backward segments 1..nb of another run in order within each strand; each step of a pairing
+ * runs one forward segment alone, one backward segment alone, or one of each side by side (the
+ * strand interleaving of the micro-batch co-execution review, "What carries the argument"). With
+ * P the measured times - P[i (nb + 1) + j] for forward segment i beside backward segment j,
+ * P[i (nb + 1)] for forward segment i alone, P[j] for backward segment j alone (P[0] unused) - the
+ * pairing of least total time follows the review's recurrence
+ *   T(i, j) = min{ T(i-1, j) + P(i, none), T(i, j-1) + P(none, j), T(i-1, j-1) + P(i, j) }.
+ * Outputs: steps [2 (nf + nb)] int32 (capacity), filled with *n_steps (forward, backward) pairs of
+ * segment numbers in execution order, 0 meaning none; *makespan = T(nf, nb). Ties take the pair,
+ * then the forward segment alone. TPSLICE_ERR_INVALID for a NULL pointer or a negative or
+ * non-finite time, TPSLICE_ERR_SHAPE for counts outside [0, 4096].                              */
+TPSLICE_API tpslice_status_t tpslice_strand_schedule(const double* P, int32_t nf, int32_t nb, int32_t* steps,
+                                                     int32_t* n_steps, double* makespan);
+
 /* Static text for a status code.                                                                   */
 TPSLICE_API const char* tpslice_error_string(tpslice_status_t status);
 
