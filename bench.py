@@ -63,8 +63,11 @@ def parse():
                          "instead of the default one contiguous DMA copy per row slice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
-    ap.add_argument("--strands", type=int, default=1, choices=[1, 2],
-                    help="2: also time two micro-batches in flight, forward beside backward (layer workloads)")
+    ap.add_argument("--no-strands", action="store_true",
+                    help="skip the two-strand leg (layer workloads: forward of one micro-batch beside the backward "
+                         "of another, paired by the library's schedule from a measured pairwise profile)")
+    ap.add_argument("--strands-exhaustive", action="store_true",
+                    help="also measure every pairing of the two strands' segments (the schedule's check)")
     ap.add_argument("--attn-seq", type=int, default=2048,
                     help="sequence length for the attention-core leg of layer workloads")
     ap.add_argument("--no-attn-core", action="store_true", help="skip the attention-core leg")
@@ -174,77 +177,6 @@ class Chain:
                 p.attnproj_bwd(x_prev, t["Wqkv"], t["dQKV"], t["C"], t["Wo"], dy_attn, o["dXa"], o["dC"],
                                g["dWqkv"], g["dWo"], dX_handoff=out("dXah"))
         self.n += 1
-
-
-class TwoStrands:
-    """Two micro-batches in flight (strand interleaving, Hiding Communication Cost in Distributed
-    LLM Training via Micro-batch Co-execution page, "What carries the argument"), on one GPU: the
-    forward of micro-batch n on one stream beside the backward of micro-batch n-1 on another, so
-    that each strand's products fill the CUs the other's thin products and hand-off copies leave
-    idle. Micro-batch n-1's backward waits for its forward and that forward's hand-off copies;
-    micro-batch n+1's forward waits until that backward has read the activation buffers it reuses.
-
-    mode "dma" / "kernel": each strand a serialized plan (products and copies in order on its
-    stream; the copy by the DMA engines or by a copy kernel). mode "pipelined": each strand a
-    pipelined plan whose worker is the strand's stream and whose DMA copies run on a copy stream
-    of its own (four streams in all, one per hardware queue)."""
-
-    def __init__(self, w, dev, kw, mode):
-        import torch
-        from comm_overlap_amd import tpslice as T
-        self.w, self.mode = w, mode
-        if mode == "pipelined":
-            kw = dict(kw, pipeline=True, caller_worker=True, n_streams=1, n_copy_streams=1)
-        else:
-            kw = dict(kw, serialize=True, copy_blit=mode == "kernel")
-        # each strand's plan has worker and copy streams of its own
-        self.fwd_plan = T.plan_for(w, streams=T.Streams.new(1, 1), **kw)
-        self.bwd_plan = T.plan_for(w, streams=T.Streams.new(1, 1), **kw)
-        self.chain = Chain(w, self.fwd_plan, dev)  # activation and output buffers of both sets
-        self.bwd_ws = Chain(w, self.bwd_plan, dev, share=self.chain)  # the backward plan's workspaces
-        self.sa, self.sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
-        self.fwd_done = [torch.cuda.Event(), torch.cuda.Event()]
-        self.bwd_done = [torch.cuda.Event(), torch.cuda.Event()]
-        self.n = 0
-
-    def __call__(self):
-        import torch
-        c, w, t = self.chain, self.w, self.chain.t
-        n = self.n
-        o, prev = c.sets[n % 2], c.sets[(n + 1) % 2]
-        if n >= 1:
-            with torch.cuda.stream(self.sb):  # backward of micro-batch n-1, from its set `prev`
-                self.sb.wait_event(self.fwd_done[(n + 1) % 2])
-                if self.mode == "pipelined":
-                    # the forward's hand-off copies queued so far are exactly micro-batch n-1's
-                    self.fwd_plan.handoff_wait(self.sb)
-                p, g, q = self.bwd_plan, self.bwd_ws.g, prev
-                # micro-batch n-1's own layer input is being overwritten by micro-batch n's forward
-                # (it was the hand-off of n-2), so the attention backward reads the seeded input
-                x_in = t["X"] if w.has_attn else q["Zh"]
-                x_mlp = q["Zah"] if w.has_attn else t["X_mlp"]
-                p.mlp_bwd(x_mlp, t["W1"], t["W2"], t["U_saved"], t["dY"], q["dX"], g["dW1"], g["dW2"],
-                          db1=g.get("db1"), dX_handoff=q["dXh"])
-                if w.has_attn:
-                    p.attnproj_bwd(x_in, t["Wqkv"], t["dQKV"], t["C"], t["Wo"], q["dXh"], q["dXa"], q["dC"],
-                                   g["dWqkv"], g["dWo"], dX_handoff=q["dXah"])
-                self.bwd_done[(n + 1) % 2].record(self.sb)
-        with torch.cuda.stream(self.sa):  # forward of micro-batch n
-            if n >= 2:
-                self.sa.wait_event(self.bwd_done[n % 2])
-            p = self.fwd_plan
-            x_prev = prev["Zh"]
-            if w.has_attn:
-                p.attnproj_fwd(x_prev, t["Wqkv"], None, o["QKV"], t["C"], t["Wo"], o["Za"], o["Zah"])
-            x_mlp = o["Zah"] if w.has_attn else x_prev
-            p.mlp_fwd(x_mlp, t["W1"], t.get("b1"), t["W2"], o["Z"], o["U"], o["Zh"])
-            self.fwd_done[n % 2].record(self.sa)
-        self.n += 1
-
-    def handoff_wait(self):
-        """Make the current stream wait for both strands' hand-off copies (timing boundaries)."""
-        self.fwd_plan.handoff_wait()
-        self.bwd_plan.handoff_wait()
 
 
 def timed(fn, steps, warmup, plans=()):
@@ -533,19 +465,41 @@ def main():
     jplan.trace(False)
     info = plan.info
 
-    # 5) optional: two micro-batches in flight (forward of one beside backward of the other)
+    # 5) two strands (layer workloads): the forward of one micro-batch beside the backward of another,
+    # in segments of half a micro-batch; the pairwise profile P measured here, the pairing chosen by
+    # the library's schedule, then measured; the same segments in sequence for comparison
     two = None
-    if args.strands == 2 and w.backward:
-        log("two strands")
-        two = {}
-        for mode in ("pipelined", "dma", "kernel"):
-            ts = TwoStrands(w, dev, kw, mode)
-            ms_two = timed(ts, K, max(2, args.warmup), [ts.fwd_plan, ts.bwd_plan])
-            two[mode] = {"ms_per_step": round(ms_two, 4), "tflops": round(flops / (ms_two * 1e-3) / 1e12, 2),
-                         "speedup_vs_one_strand": round(ms / ms_two, 3)}
-            ts.fwd_plan.close()
-            ts.bwd_plan.close()
-            del ts
+    if w.has_attn and w.backward and not args.no_strands:
+        from comm_overlap_amd import strands as ST
+        log("two strands: pairwise profile, schedule, measured pairing")
+        sp = ST.StrandPair(w, dev, dict(tile=args.tile, copy_blit=args.copy_blit))
+        P = sp.profile(reps=3)
+        plan_steps, predicted = ST.schedule(P)
+        measured = sp.time(plan_steps, reps=5)
+        seq_ms = sp.time(sp.sequential(), reps=5)
+        two = {"segments": {"forward": ["attnproj_fwd half 1", "attnproj_fwd half 2", "mlp_fwd half 1",
+                                        "mlp_fwd half 2"],
+                            "backward": ["mlp_bwd half 1", "mlp_bwd half 2", "attnproj_bwd half 1",
+                                         "attnproj_bwd half 2"]},
+               "P_ms": [[round(x, 4) for x in row] for row in P], "plan": plan_steps,
+               "predicted_ms": round(predicted, 4), "measured_ms": round(measured, 4),
+               "sequential_ms": round(seq_ms, 4), "speedup_vs_sequential": round(seq_ms / measured, 3),
+               "tflops": round(flops / (measured * 1e-3) / 1e12, 2)}
+        if args.strands_exhaustive:
+            log("two strands: every pairing")
+            allp = ST.pairings(len(sp.fwd), len(sp.bwd))
+            meas = [(sp.time(s, reps=3), s) for s in allp]
+            meas.sort(key=lambda x: x[0])
+            pred = {tuple(s): sum(P[i][j] for i, j in s) for s in allp}
+            rank = next(k for k, (_, s) in enumerate(meas) if s == plan_steps)
+            errs = sorted(abs(m - pred[tuple(s)]) / m for m, s in meas)
+            two["exhaustive"] = {"pairings": len(allp), "best_measured_ms": round(meas[0][0], 4),
+                                 "best_plan": meas[0][1], "schedule_rank": rank,
+                                 "schedule_vs_best": round(measured / meas[0][0], 4),
+                                 "median_prediction_error": round(errs[len(errs) // 2], 4),
+                                 "max_prediction_error": round(errs[-1], 4)}
+        sp.close()
+        del sp
 
     # 6) the whole layer with the attention core between the projections (layer workloads)
     layer_core = None
