@@ -86,6 +86,10 @@ using TileH4 = Tile<256, 160, 2, 2, 1>;
 // 256 x 320 with four waves of 128 x 160: 320 accumulator registers per lane, more than the 256
 // AGPRs, so the last accumulator columns live in VGPRs (the MFMA takes either)
 using TileW4 = Tile<256, 320, 2, 2, 1>;
+// 256 x 224 with four waves stacked along m (64 x 224 each), forward SwiGLU products only: 112 gate
+// and 112 up columns per block, so a 2048-row slice of a 3584-wide FFN shard makes 8 x 32 = 256
+// blocks, one per CU, where 256 x 256 makes 224 (the Llama-3 70B shard's up-projection)
+using TileG4 = Tile<256, 224, 4, 1, 1>;
 
 namespace {
 
@@ -696,7 +700,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   if constexpr (kPipe) {
     constexpr int kItems = kFM + kFN;  // fragment reads per k step
     constexpr int kStepM = kFM * kFN;  // MFMAs per k step
-    static_assert(kARuns + kBRuns == kItems, "one load run per fragment read");
+    static_assert(kARuns + kBRuns <= kItems, "at most one load run per fragment read");
     static_assert(2 * kItems <= kStepM, "a fragment read after every other MFMA of step 0");
     static_assert((kItems - 1) * kStepM / kItems + 1 < kStepM, "every load run has a slot in step 1");
     const int lr16 = lane & 15;
@@ -815,21 +819,21 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
           constexpr int i = decltype(ic)::value;
           constexpr int at = i * kStepM / kItems;  // read i after MFMA `at`, load run i one MFMA later
           if constexpr (at == p) item(stage ^ 1, 0, i);
-          if constexpr (at + 1 == p) load_run(bl, stage, ic);
+          if constexpr (at + 1 == p && i < kRuns) load_run(bl, stage, ic);
         });
       });
     };
     // this block's k blocks start at kb0 (a split product's run; 0 otherwise)
     {
       const BlockLoads bl = block_loads(kb0);
-      static_for<0, kItems>([&](auto jc) { load_run(bl, 0, jc); });
+      static_for<0, kRuns>([&](auto jc) { load_run(bl, 0, jc); });
     }
     wait_all_and_barrier();
 #pragma unroll
     for (int i = 0; i < kItems; ++i) item(0, 0, i);
     {
       const BlockLoads bl = block_loads(kb0 + 1);
-      static_for<0, kItems>([&](auto jc) { load_run(bl, 1, jc); });
+      static_for<0, kRuns>([&](auto jc) { load_run(bl, 1, jc); });
     }
     __builtin_amdgcn_sched_barrier(0);
     for (int kb = kb0;; kb += 2) {  // leaves at the bottom only
@@ -1018,6 +1022,7 @@ template __global__ void gemm_kernel<TileW4, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileW4, kFwd, kEpiGelu>(GemmArgs);
 template __global__ void gemm_kernel<TileH4, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileH4, kFwd, kEpiGelu>(GemmArgs);
+template __global__ void gemm_kernel<TileG4, kFwd, kEpiSwiglu>(GemmArgs);
 
 namespace {
 
@@ -1131,6 +1136,10 @@ hipError_t launch_pipe(GemmArgs& g, int layout, int epi, hipStream_t stream, hip
       case kWgrad * 8 + kEpiF32: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, stop);
       default: return hipErrorInvalidValue;
     }
+  } else if constexpr (TL::kDualOk && TL::kWavesN == 1) {
+    // forward SwiGLU only (the 256 x 224 tile)
+    if (layout == kFwd && epi == kEpiSwiglu) return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
+    return hipErrorInvalidValue;
   } else {
     switch (layout * 8 + epi) {
       case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
@@ -1147,26 +1156,29 @@ struct TileChoice {
   bool fit_only;  // considered only when the product runs alone (see choose_tile)
   bool fwd_only;  // operands read along k only, with a bf16 or activation epilogue
   bool glu_ok;    // takes the SwiGLU pairing
+  bool glu_only;  // takes only the SwiGLU pairing
   bool pipe;      // four-wave pipelined: K a multiple of 64 only, no accumulation into fp32 outputs
   double rate;
 };
 // The four-wave rates: 8192^3 (256 x 256) and a 4096 x 2560 x 5120 product (256 x 160, one round
 // of tiles against 256 x 256's 160 tiles).
 constexpr TileChoice kTiles[] = {
-    {kTile256x256, 256, 256, 1, false, false, true, false, 1.00},
-    {kTile128x128, 128, 128, 2, false, false, true, false, 0.70},
-    {kTile256x320, 256, 320, 1, true, true, false, false, 0.92},
-    {kTile128x320, 128, 320, 1, true, true, false, false, 0.73},
-    {kTile128x256, 128, 256, 1, true, false, true, false, 0.77},
-    {kTile128x128w8, 128, 128, 1, true, false, true, false, 0.50},
-    {kTile256x256w4, 256, 256, 1, false, false, true, true, 1.10},
-    {kTile256x160w4, 256, 160, 1, true, true, false, true, 0.83},
-    {kTile256x320w4, 256, 320, 1, true, true, false, true, 1.00},
+    {kTile256x256, 256, 256, 1, false, false, true, false, false, 1.00},
+    {kTile128x128, 128, 128, 2, false, false, true, false, false, 0.70},
+    {kTile256x320, 256, 320, 1, true, true, false, false, false, 0.92},
+    {kTile128x320, 128, 320, 1, true, true, false, false, false, 0.73},
+    {kTile128x256, 128, 256, 1, true, false, true, false, false, 0.77},
+    {kTile128x128w8, 128, 128, 1, true, false, true, false, false, 0.50},
+    {kTile256x256w4, 256, 256, 1, false, false, true, false, true, 1.10},
+    {kTile256x160w4, 256, 160, 1, true, true, false, false, true, 0.83},
+    {kTile256x320w4, 256, 320, 1, true, true, false, false, true, 1.00},
+    {kTile256x224w4, 256, 224, 1, false, true, true, true, true, 1.05},
 };
 
 bool tile_supports(const TileChoice& t, int64_t K, int layout, int epi, bool accumulate) {
   if (t.fwd_only && (layout != kFwd || (epi != kEpiBf16 && epi != kEpiGelu && epi != kEpiSwiglu))) return false;
   if (!t.glu_ok && epi == kEpiSwiglu) return false;
+  if (t.glu_only && epi != kEpiSwiglu) return false;
   return !t.pipe || (K > 0 && K % 64 == 0 && !(accumulate && epi == kEpiF32));
 }
 
@@ -1244,6 +1256,7 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipE
     case kTile256x256w4: return launch_pipe<TileL4>(g, layout, epi, stream, start, stop);
     case kTile256x160w4: return launch_pipe<TileH4>(g, layout, epi, stream, start, stop);
     case kTile256x320w4: return launch_pipe<TileW4>(g, layout, epi, stream, start, stop);
+    case kTile256x224w4: return launch_pipe<TileG4>(g, layout, epi, stream, start, stop);
     default: return launch_tile<TileL>(g, layout, epi, stream, start, stop);
   }
 }

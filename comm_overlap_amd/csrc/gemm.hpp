@@ -67,7 +67,8 @@ enum GemmTile : int {
                        // multiple of 64 and no accumulation into an fp32 output
   kTile256x160w4 = 8,  // 256 x 160, likewise, forward products without the SwiGLU pairing
   kTile256x320w4 = 9,  // 256 x 320, likewise (accumulators partly in VGPRs)
-  kTileCount = 10
+  kTile256x224w4 = 10, // 256 x 224 (112 gate + 112 up columns), 4 waves along m: forward SwiGLU only
+  kTileCount = 11
 };
 
 // The tile kTileAuto resolves to for an M x N x K product (N: output columns). `alone`: the product

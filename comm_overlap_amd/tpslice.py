@@ -26,7 +26,8 @@ F_SERIALIZE, F_COPY_BLIT, F_PIPELINE, F_HANDOFF_ROWS, F_CALLER_WORKER = 0x1, 0x2
 F_TILE_SHIFT = 8
 # block tile ids (flags bits 8..11); "large" / "small" name the 256 x 256 / 128 x 128 tiles
 TILES = {"auto": 0, "256x256": 1, "128x128": 2, "256x320": 3, "128x320": 4, "128x256": 5,
-         "128x128w8": 6, "256x256w4": 7, "256x160w4": 8, "256x320w4": 9, "large": 1, "small": 2}
+         "128x128w8": 6, "256x256w4": 7, "256x160w4": 8, "256x320w4": 9, "256x224w4": 10, "large": 1,
+         "small": 2}
 OP_MLP_FWD, OP_ATTNPROJ_FWD, OP_MLP_BWD, OP_ATTNPROJ_BWD, OP_ATTN_CORE_BWD = range(5)
 EXPORTS = ("tpslice_plan", "tpslice_plan_destroy", "tpslice_plan_info", "tpslice_plan_piece",
            "tpslice_workspace_size", "tpslice_mlp_fwd", "tpslice_attnproj_fwd", "tpslice_mlp_bwd",

@@ -146,7 +146,7 @@ def test_pipeline_flag_and_handoff_wait_without_gpu_work():
 def test_plan_tile_flags():
     import ctypes
     d = T.Config(tokens=64, hidden=64, ffn=64).desc()
-    d.flags = 10 << T.F_TILE_SHIFT  # ids run 0..9
+    d.flags = 11 << T.F_TILE_SHIFT  # ids run 0..10
     h = ctypes.c_void_p()
     assert T.lib.tpslice_plan(ctypes.byref(d), ctypes.byref(h)) == T.ERR_INVALID
     assert b"tile id" in T.lib.tpslice_last_error()

@@ -29,7 +29,7 @@ def _print_case(name, **kw):
     print(f"[case] {name} {kw}", flush=True)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x128", "256x320", "128x320", "128x256", "128x128w8"])
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "256x320", "128x320", "128x256", "128x128w8", "256x224w4"])
 @pytest.mark.parametrize("w", [SMALL_GELU, SMALL_SWIGLU], ids=lambda w: w.key)
 def test_mlp_fwd_small(w, tile):
     _print_case("mlp_fwd", key=w.key, tile=tile)
@@ -61,7 +61,7 @@ def test_four_wave_tiles(w):
     inp = synth.make_inputs(w)
     ref = G.oracle_mlp_fwd(inp, w.act)
     base = G.run_mlp_fwd(T.plan_for(w, tile="256x256"), inp)
-    for tile in ("256x256w4", "256x160w4", "256x320w4", "auto", "256x256w4", "256x320w4"):
+    for tile in ("256x256w4", "256x160w4", "256x320w4", "256x224w4", "auto", "256x256w4", "256x224w4"):
         _print_case("four_wave", key=w.key, tile=tile)
         out = G.run_mlp_fwd(T.plan_for(w, tile=tile), inp)
         G.assert_parity(out["Z"], ref["Z"], "Z")
