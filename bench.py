@@ -406,7 +406,10 @@ def main():
     if args.col_slices:
         kw["n_col_slices"] = args.col_slices
     plan = T.plan_for(w, pipeline=True, **kw)  # the headline: chained steps, pipelined hand-off
-    jplan = T.plan_for(w, **kw)                # every call joined: isolated calls, copies alone
+    jplan = T.plan_for(w, **kw)                # every call joined: isolated calls
+    # the copies alone: every piece's copy back to back behind a one-worker plan's events, so that the
+    # time is the copies' own (a plan with more worker streams adds event hops between them)
+    cplan = T.plan_for(w, **dict(kw, n_streams=1))
     chain = Chain(w, plan, dev)
     nocopy = Chain(w, plan, dev, handoff=False, share=chain)
     jchain = Chain(w, jplan, dev, share=chain)
@@ -415,7 +418,7 @@ def main():
 
     def copies():
         for s, d in pairs:
-            jplan.handoff_copy(s, d)
+            cplan.handoff_copy(s, d)
 
     torch.cuda.synchronize()
     K = args.steps
@@ -432,7 +435,7 @@ def main():
     for _ in range(rounds):
         legs["chain"].append(timed(chain, K, 1, [plan]))
         legs["nocopy"].append(timed(nocopy, K, 1, [plan]))
-        legs["copies"].append(timed(copies, K, 1, [jplan]))
+        legs["copies"].append(timed(copies, K, 1, [cplan]))
         legs["iso"].append(timed(jchain, K, 1))
         legs["iso_nocopy"].append(timed(jnocopy, K, 1))
     med = {k: median(v) for k, v in legs.items()}
@@ -581,6 +584,7 @@ def main():
         torch.cuda.synchronize()
     plan.close()
     jplan.close()
+    cplan.close()
     print(json.dumps(out), flush=True)
     return 0
 

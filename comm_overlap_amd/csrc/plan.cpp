@@ -83,29 +83,44 @@ static bool fits_4g(int64_t rows, int64_t cols, int64_t elem) {
   return rows >= 0 && cols >= 0 && bytes < 4294967296.0 - 4096.0;
 }
 
-// Worker streams when the descriptor leaves them open. One stream (slices in order) if every
-// per-slice product fills its rounds of blocks on the 256 CUs with some tile (>= 90% of the slots);
-// otherwise two, so that each slice's products share the CUs with the next slice's first product
-// (the schedule choice between finer pieces and more overlap: FiCCO page, Abstract).
+// Worker streams when the descriptor leaves them open. The share of a row slice's forward product
+// work that leaves compute units idle: each product's flops times the share of its rounds of blocks
+// it leaves empty on the 256 CUs (with the tile it takes alone; a product split along k counts the
+// blocks of its 256 x 256 partial products). One stream (slices in order) when that share is at most
+// 5%; otherwise two, so that each slice's products share the CUs with the next slice's first product
+// (the schedule choice between finer pieces and more overlap, by the products' static sizes: FiCCO
+// page, Abstract). Measured with 2048-row slices: the Llama-2 7B MLP (its up-projection fills 200
+// of 256 CUs: 31% idle work) 914 TFLOP/s with one stream against 972 with two; the Llama-3 70B
+// layer (only the QKV projection, 10% of the work, fills 200 blocks of 256: 2% idle) 1130 with one
+// against 1140 with two, within run-to-run spread, and one stream's launches do not share the GPU.
 static int32_t default_streams(const tpslice_plan_s* p) {
+  constexpr int64_t kCUs = 256;
   if (p->r <= 1) return 1;
   const bool glu = p->desc.act == TPSLICE_ACT_SWIGLU;
-  struct P { int64_t n, k; int layout, epi; };
+  const int64_t h = p->desc.hidden;
+  struct P { int64_t n, k; int epi; int splits; double flops; };
   const P prods[] = {
-      {p->Fp, p->desc.hidden, kFwd, glu ? kEpiSwiglu : kEpiGelu},  // up-projection (+ activation)
-      {p->pw, p->Fp, kFwd, kEpiBf16},                              // down-projection product
+      {p->Fp, h, glu ? kEpiSwiglu : kEpiGelu, choose_slice_split(p->N1, h), double(p->N1) * double(h)},
+      {p->pw, p->Fp, kEpiBf16, 1, double(h) * double(p->Fp)},
+      {p->qh ? p->qkv : 0, h, kEpiBf16, p->qh ? choose_slice_split(p->qkv, h) : 1, double(p->qkv) * double(h)},
+      {p->qh ? p->pw : 0, p->ctx, kEpiBf16, 1, double(h) * double(p->ctx)},
   };
+  double idle = 0.0, total = 0.0;
   for (const P& q : prods) {
+    if (q.n <= 0 || q.k <= 0) continue;
     double fill = 0.0;
-    choose_tile(p->Ms, q.n, q.k, q.layout, q.epi, true, &fill);
-    if (fill < 0.9) return 2;
+    if (q.splits > 1) {
+      const int64_t nt = q.epi == kEpiSwiglu ? 2 * q.n : q.n;  // both halves: the split partials' width
+      const int64_t blocks = ((p->Ms + 255) / 256) * ((nt + 255) / 256) * q.splits;
+      const int64_t rounds = (blocks + kCUs - 1) / kCUs;
+      fill = double(blocks) / double(rounds * kCUs);
+    } else {
+      choose_tile(p->Ms, q.n, q.k, kFwd, q.epi, true, &fill);
+    }
+    idle += q.flops * (1.0 - fill);
+    total += q.flops;
   }
-  if (p->qh) {
-    double fill = 0.0;
-    choose_tile(p->Ms, p->qkv, p->desc.hidden, kFwd, kEpiBf16, true, &fill);
-    if (fill < 0.9) return 2;
-  }
-  return 1;
+  return total > 0.0 && idle > 0.05 * total ? 2 : 1;
 }
 
 // Rate of this GPU's local hand-off copy for large pieces (DMA engine, measured 550-760 GB/s for

@@ -260,7 +260,7 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
+        if h is not None and h.value and _DROPPED is not None:  # (None while the interpreter shuts down)
             _DROPPED.append(h)
             self._h = None
 

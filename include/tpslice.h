@@ -118,9 +118,11 @@ typedef struct {
   int32_t n_kv_heads;     /* full-model key/value heads (GQA); this rank holds max(1, n_kv/tp_size)   */
   int32_t head_dim;       /* d; multiple of 8                                                          */
   int32_t act;            /* tpslice_act_t                                                              */
-  int32_t n_streams;      /* worker streams for the slices (0 = default: 2 when there are several row
-                             slices, else 1); slice i runs on stream i mod n_streams and starts once
-                             slice i-1's first product is done                                     */
+  int32_t n_streams;      /* worker streams for the slices (0 = default: 1 for one row slice; for
+                             several, 2 when the per-slice forward products, each alone with its
+                             tile, leave more than 5% of their flop-weighted block rounds empty on
+                             the 256 CUs, else 1); slice i runs on stream i mod n_streams and
+                             starts once slice i-1's first product is done                       */
   int32_t n_copy_streams; /* side streams for hand-off copies (0 = default: 1)                        */
   uint32_t flags;         /* TPSLICE_F_*                                                                */
   float handoff_gbps;     /* hand-off rate in GB/s that the automatic slice counts assume (0: the

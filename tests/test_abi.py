@@ -208,12 +208,14 @@ def test_given_slice_counts_are_kept():
     assert p.info.n_row_slices == 4 and p.info.n_col_slices in (1, 2, 4)
 
 
+@pytest.mark.parametrize("streams", [1, 2])
 @pytest.mark.parametrize("key", LARGE)
-def test_slower_handoff_never_takes_fewer_row_slices_for_isolated_calls(key):
+def test_slower_handoff_never_takes_fewer_row_slices_for_isolated_calls(key, streams):
     """Isolated calls expose the last row slice's hand-off, so a slower hand-off is worth at least
-    as many row slices."""
+    as many row slices, for a given number of worker streams (left open, the stream count follows
+    the slice size, which can turn a finer slicing into the faster one at a faster hand-off)."""
     w = synth.WORKLOADS[key]
-    rs = [T.plan_for(w, n_row_slices=0, n_col_slices=1, handoff_gbps=g).info.n_row_slices
+    rs = [T.plan_for(w, n_row_slices=0, n_col_slices=1, handoff_gbps=g, n_streams=streams).info.n_row_slices
           for g in (0.0, 200.0, 100.0, 50.0)]
     assert rs == sorted(rs), rs
 
