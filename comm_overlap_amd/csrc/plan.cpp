@@ -40,9 +40,9 @@ MlpFwdWs mlp_fwd_ws(const tpslice_plan_s* p) {
 
 AttnFwdWs attn_fwd_ws(const tpslice_plan_s* p) {
   AttnFwdWs w{};
-  w.qkv_split = 0;
-  w.qkv_split_bytes = align_up(split_partials_bytes(p->Ms, p->qkv, p->sp_qkv), kWsAlign);
-  w.total = w.qkv_split_bytes * size_t(worker_regions(p));
+  w.qkv_split = 0;  // QKV runs over all tokens: one partials region
+  w.qkv_split_bytes = align_up(split_partials_bytes(p->M, p->qkv, p->sp_qkv), kWsAlign);
+  w.total = w.qkv_split_bytes;
   return w;
 }
 
@@ -89,10 +89,11 @@ static bool fits_4g(int64_t rows, int64_t cols, int64_t elem) {
 // blocks of its 256 x 256 partial products). One stream (slices in order) when that share is at most
 // 5%; otherwise two, so that each slice's products share the CUs with the next slice's first product
 // (the schedule choice between finer pieces and more overlap, by the products' static sizes: FiCCO
-// page, Abstract). Measured with 2048-row slices: the Llama-2 7B MLP (its up-projection fills 200
-// of 256 CUs: 31% idle work) 914 TFLOP/s with one stream against 972 with two; the Llama-3 70B
-// layer (only the QKV projection, 10% of the work, fills 200 blocks of 256: 2% idle) 1130 with one
-// against 1140 with two, within run-to-run spread, and one stream's launches do not share the GPU.
+// page, Abstract). The QKV projection runs over all tokens after the slices and does not count.
+// Measured with 2048-row slices: the Llama-2 7B MLP (its up-projection fills 200 of 256 CUs: 31%
+// idle work) 914 TFLOP/s with one stream against 972 with two; the Llama-3 70B layer (every
+// per-slice product fills its rounds) 1130 with one against 1140 with two, within run-to-run
+// spread, and one stream's launches do not share the GPU.
 static int32_t default_streams(const tpslice_plan_s* p) {
   constexpr int64_t kCUs = 256;
   if (p->r <= 1) return 1;
@@ -102,7 +103,6 @@ static int32_t default_streams(const tpslice_plan_s* p) {
   const P prods[] = {
       {p->Fp, h, glu ? kEpiSwiglu : kEpiGelu, choose_slice_split(p->N1, h), double(p->N1) * double(h)},
       {p->pw, p->Fp, kEpiBf16, 1, double(h) * double(p->Fp)},
-      {p->qh ? p->qkv : 0, h, kEpiBf16, p->qh ? choose_slice_split(p->qkv, h) : 1, double(p->qkv) * double(h)},
       {p->qh ? p->pw : 0, p->ctx, kEpiBf16, 1, double(h) * double(p->ctx)},
   };
   double idle = 0.0, total = 0.0;
@@ -136,10 +136,10 @@ constexpr double kSliceSyncUs1 = 20.0, kSliceSyncUs2 = 80.0;
 // per-slice products from the GEMM cost model, the hand-off pieces at `gbps` plus a fixed cost per
 // copy. With two worker streams, adjacent row slices run side by side, which the model takes as
 // one product over twice the rows for each pair. Row slice i's copies run while later slices
-// compute.
+// compute, the last ones under the QKV projection over all tokens (which follows the slices).
 static double predict_forward_us(const tpslice_desc_t* d, int64_t Fp, int64_t N1, int64_t qkv, int64_t ctx, int r,
                                  int c, int S, double gbps) {
-  const int64_t Ms = d->tokens / r, h = d->hidden, hc = h / c;
+  const int64_t M = d->tokens, Ms = M / r, h = d->hidden;
   const int pc = (c > 1 && (d->flags & TPSLICE_F_HANDOFF_ROWS)) ? 1 : c;  // products per row slice
   const int64_t pw = h / pc;
   const int pair = (S > 1 && r > 1) ? 2 : 1;
@@ -149,17 +149,21 @@ static double predict_forward_us(const tpslice_desc_t* d, int64_t Fp, int64_t N1
   double group_us = estimate_product_us(Mp, Fp, h, kFwd, epi_up, alone, choose_slice_split(N1, h)) +
                     pc * estimate_product_us(Mp, pw, Fp, kFwd, kEpiBf16, alone);
   int tensors = 1;
+  double tail_us = 0.0;  // products over all tokens after the slices
   if (qkv > 0) {
-    group_us += estimate_product_us(Mp, qkv, h, kFwd, kEpiBf16, alone, choose_slice_split(qkv, h)) +
-                pc * estimate_product_us(Mp, pw, ctx, kFwd, kEpiBf16, alone);
+    group_us += pc * estimate_product_us(Mp, pw, ctx, kFwd, kEpiBf16, alone);
+    const int s = choose_split(M, qkv, h);
+    tail_us = std::min(estimate_product_us(M, qkv, h, kFwd, kEpiBf16, true, s),
+                       estimate_product_us(M, qkv, h, kFwd, kEpiBf16, true, 1));
     tensors = 2;
   }
-  const double comp_us = group_us * double((r + pair - 1) / pair);
-  const double slice_us = comp_us / r;
+  const double sliced_us = group_us * double((r + pair - 1) / pair);
+  const double slice_us = sliced_us / r;
   // one row slice's copies: c pieces, or one whole-row copy (the same bytes, one fixed cost)
   const double copy_us = double(Ms) * double(h) * 2.0 * tensors / (gbps * 1e3) + pc * kCopyFixedUs * tensors;
-  if (d->flags & TPSLICE_F_PIPELINE) return std::max(comp_us, r * (copy_us + (S > 1 ? kSliceSyncUs2 : kSliceSyncUs1)));
-  return std::max(comp_us + copy_us, slice_us + r * copy_us);
+  if (d->flags & TPSLICE_F_PIPELINE)
+    return std::max(sliced_us + tail_us, r * (copy_us + (S > 1 ? kSliceSyncUs2 : kSliceSyncUs1)));
+  return std::max({sliced_us + tail_us, sliced_us + copy_us, slice_us + r * copy_us});
 }
 
 // Slice counts for a descriptor with r or c = 0 (the header describes the rule).
@@ -294,8 +298,18 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   p->sp_dc = qh ? choose_split(M, ctx, h) : 1;
   p->sp_dwo = qh ? choose_split(h, ctx, M) : 1;
   p->sp_dwqkv = qh ? choose_split(qkv, h, M) : 1;
+  // QKV over all tokens runs alone (after the slices), where the forward-only tiles that fill the
+  // last round compete with a split of 256 x 256 tiles: the split only when the model prefers it
+  if (qh) {
+    const int s = choose_split(M, qkv, h);
+    p->sp_qkv = s > 1 && estimate_product_us(M, qkv, h, kFwd, kEpiBf16, true, s) <
+                             estimate_product_us(M, qkv, h, kFwd, kEpiBf16, true, 1) ? s : 1;
+  } else {
+    p->sp_qkv = 1;
+  }
+  // k splits of the per-slice products: a function of the product's width and depth only, so that
+  // every slicing of the same batch reduces k in the same order
   p->sp_up = choose_slice_split(N1, h);
-  p->sp_qkv = qh ? choose_slice_split(qkv, h) : 1;
   p->sp_dh = choose_slice_split(Fp, h);
   // Products of adjacent row slices share the GPU on two worker streams. A compute unit holding a
   // 128 x 128 block (64 KB of LDS) has no room for a four-wave 256 x 256 block (128 KB) of the

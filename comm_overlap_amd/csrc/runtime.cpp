@@ -194,6 +194,16 @@ struct Schedule {
     return TPSLICE_OK;
   }
 
+  // Pipelined mode: worker k waits for every hand-off copy of the previous calls that has not been
+  // waited for, before a product over all tokens that no row slice of this call precedes (it may
+  // read rows of every slice of a previous call's hand-off buffer).
+  tpslice_status_t wait_all_handoffs(int k) {
+    if (!pipelined()) return TPSLICE_OK;
+    for (size_t x = 0; x < rt->copied_pending.size(); ++x)
+      if (rt->copied_pending[x]) TPS_HIP(hipStreamWaitEvent(wk(k), rt->copied[x], 0));
+    return TPSLICE_OK;
+  }
+
   // Pipelined mode: mark the end of row slice i's hand-off copies on each copy stream it used.
   tpslice_status_t slice_handed_off(int i, uint32_t streams_used) {
     if (!pipelined()) return TPSLICE_OK;
@@ -357,7 +367,10 @@ struct Schedule {
 
   // Queue one product on worker(i) (i = -1: worker `on`, all tokens), traced as `step`. A traced
   // product carries its timing events on the dispatch itself.
-  tpslice_status_t product(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int on = 0) {
+  // `alone`: nothing else runs beside this product (an all-token product after the slices), so the
+  // tile choice may take the tiles that fill the last round
+  tpslice_status_t product(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int on = 0,
+                           bool alone = false) {
     const int wi = i < 0 ? on : i;
     const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
     hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -371,7 +384,7 @@ struct Schedule {
       e0 = rt->tpool[t.ev0];
       e1 = rt->tpool[t.ev1];
     }
-    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1, p->tile, serial || p->S == 1);
+    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1, p->tile, alone || serial || p->S == 1);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
     if (i >= 0 && i == lead_slice) {
       TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
@@ -390,8 +403,8 @@ struct Schedule {
   // i < 0: a product over all tokens on worker(on). Traced as two records: the GEMM of the
   // partial products (with the product's flops) and the reduction.
   tpslice_status_t product_split(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int splits,
-                                 float* part, int on = 0) {
-    if (splits <= 1) return product(i, step, piece, g, layout, epi, on);
+                                 float* part, int on = 0, bool alone = false) {
+    if (splits <= 1) return product(i, step, piece, g, layout, epi, on, alone);
     const int wi = i < 0 ? on : i;
     const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
     hipEvent_t e0 = nullptr, em = nullptr, e1 = nullptr;
@@ -621,12 +634,12 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
   TPS_TRY(ensure_runtime(p, &rt));
   Schedule S = schedule(p, rt, cs);
   TPS_TRY(S.fork());
-  for (int i = 0; i < p->r; ++i) {
+  // the output projection by row slices: its pieces are the hand-off
+  for (int i = 0; do_out && i < p->r; ++i) {
     const int64_t r0 = int64_t(i) * p->Ms;
     TPS_TRY(S.slice_begin(i));
     S.slice_streams = 0;
-    // output projection first: its pieces are the hand-off, the QKV product then runs under the copies
-    for (int j = 0; do_out && j < p->pc; ++j) {
+    for (int j = 0; j < p->pc; ++j) {
       const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs g = args(bf(C, r0 * p->ctx), p->ctx, bf(Wo, c0 * p->ctx), p->ctx, bfw(Z, r0 * p->h + c0), p->h,
                         p->Ms, p->pw, p->ctx);
@@ -634,12 +647,17 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
       if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
     }
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
-    if (do_qkv) {
-      GemmArgs q = args(bf(X, r0 * p->h), p->h, Wqkv, p->h, bfw(QKV, r0 * p->qkv), p->qkv, p->Ms, p->qkv, p->h);
-      q.bias = bqkv;
-      TPS_TRY(S.product_split(i, TPSLICE_STEP_QKV, -1, q, kFwd, kEpiBf16, p->sp_qkv,
-                              S.slice_part(static_cast<char*>(ws) + L.qkv_split, L.qkv_split_bytes, i)));
-    }
+  }
+  // QKV over all tokens at once, under the last pieces' copies: nothing hands it off and nothing in
+  // this call reads it, so slicing it would only cut it into products too small to fill the GPU
+  // (the 70B shard's 2048-row slices made 8 x 5 tiles of 256 x 256 each)
+  if (do_qkv) {
+    if (do_out) TPS_TRY(S.gather_slices());
+    else TPS_TRY(S.wait_all_handoffs(0));
+    GemmArgs q = args(X, p->h, Wqkv, p->h, QKV, p->qkv, p->M, p->qkv, p->h);
+    q.bias = bqkv;
+    TPS_TRY(S.product_split(-1, TPSLICE_STEP_QKV, -1, q, kFwd, kEpiBf16, p->sp_qkv,
+                            reinterpret_cast<float*>(static_cast<char*>(ws) + L.qkv_split), 0, true));
   }
   return S.join();
 }
@@ -801,6 +819,7 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
   // another on worker 0 (measured on the Llama-3 70B shard: side by side on two workers, each at
   // half the CUs, they took 0.81 ms against 0.74 ms in sequence)
   TPS_TRY(S.gather_slices());
+  if (!do_qkv) TPS_TRY(S.wait_all_handoffs(0));
   if (do_out) {
     if (p->M > 0) {
       GemmArgs gc = args(dY, p->h, Wo, p->ctx, dC, p->ctx, p->M, p->ctx, p->h);

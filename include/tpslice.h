@@ -69,9 +69,11 @@ typedef enum {
                                     engines (uses compute units; for comparison)                       */
 #define TPSLICE_F_PIPELINE 0x4u  /* pipelined hand-off: the caller's stream waits for the products
                                     only; a later call's row slice i waits just for this call's
-                                    hand-off copies of row slice i. Chained calls (a layer reading
-                                    the previous layer's hand-off) then overlap the last pieces'
-                                    copies with the next call's first pieces (Domino page,
+                                    hand-off copies of row slice i (a product over all tokens that
+                                    no row slice of its call precedes: for all of them). Chained
+                                    calls (a layer reading the previous layer's hand-off) then
+                                    overlap the last pieces' copies with the next call's first
+                                    pieces (Domino page,
                                     Abstract: independent pieces pipelined across the batch's work).
                                     Use tpslice_handoff_wait() before reading a hand-off buffer on
                                     another stream, or before freeing buffers the copies touch.    */
@@ -164,10 +166,10 @@ typedef struct {
   int64_t handoff_cols;         /* h / c                                                             */
   int32_t n_row_slices, n_col_slices, n_streams, n_copy_streams;
   int32_t q_heads, kv_heads;    /* this rank's head counts                                           */
-  /* k splits (1 = none) the plan takes for, in order: the up-projection, the QKV projection and dH
-     of each row slice, then dW1, dW2, dC, dWo, dWqkv over all tokens. A split product sums its k
-     runs' fp32 partials in order before the epilogue: the same bits for every slicing of the same
-     batch, other rounding than an unsplit product.                                            */
+  /* k splits (1 = none) the plan takes for, in order: the up-projection of each row slice, the QKV
+     projection over all tokens, dH of each row slice, then dW1, dW2, dC, dWo, dWqkv over all
+     tokens. A split product sums its k runs' fp32 partials in order before the epilogue: the same
+     bits for every slicing of the same batch, other rounding than an unsplit product.          */
   int32_t k_splits[8];
   /* the slice-count model's predicted time (us) of one call of the forward products with this
      plan's r and c (see the automatic slice counts above); a comparison figure, not a timing */
@@ -222,7 +224,9 @@ TPSLICE_API tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t plan, const void* X,
  * page, Abstract).
  *   QKV = X Wqkv^T (+ bqkv)   column-parallel;   Z = C Wo^T   row-parallel partial sum
  * C is the attention context of this rank's heads (an input here; tpslice_attn_core_fwd computes it
- * from QKV). Z_handoff as in tpslice_mlp_fwd. Needs n_heads > 0 in the plan. Either projection may
+ * from QKV). Z_handoff as in tpslice_mlp_fwd. Z runs by row slices (its pieces are the hand-off);
+ * QKV, which nothing hands off, runs after them as one product over all tokens, under the last
+ * pieces' copies. Needs n_heads > 0 in the plan. Either projection may
  * be left out: Wqkv = NULL skips QKV (X, bqkv, QKV unused), Wo = NULL skips Z (C, Z, Z_handoff
  * unused), so that a layer can run QKV, then tpslice_attn_core_fwd, then the output projection;
  * both NULL is TPSLICE_ERR_INVALID.                                                              */
