@@ -53,8 +53,10 @@ def parse():
     ap.add_argument("--col-slices", type=int, default=0, help="column slices (0 = the workload's)")
     ap.add_argument("--tile", default="auto",
                     choices=["auto", "256x256", "128x128", "256x320", "128x320", "128x256", "128x128w8", "256x256w4",
-                             "256x160w4", "256x320w4", "large", "small"],
+                             "256x160w4", "256x320w4", "256x224w4", "large", "small"],
                     help="block tile of every product (auto = chosen per product, the default)")
+    ap.add_argument("--dh-group", type=int, default=0,
+                    help="row slices per dH product of the MLP backward (0 = plan default)")
     ap.add_argument("--copy-blit", action="store_true", help="hand-off by copy kernel instead of DMA")
     ap.add_argument("--caller-worker", action="store_true",
                     help="worker stream 0 is the caller's stream (plans with one worker stream always do this)")
@@ -400,7 +402,7 @@ def main():
     dev = {k: v.to("cuda").contiguous() for k, v in inp.items()}
     flops = sum(w.gemm_flops().values())
     kw = dict(n_streams=args.streams, n_copy_streams=args.copy_streams, copy_blit=args.copy_blit, tile=args.tile,
-              handoff_rows=not args.handoff_pieces, caller_worker=args.caller_worker)
+              handoff_rows=not args.handoff_pieces, caller_worker=args.caller_worker, dh_group=args.dh_group)
     if args.row_slices:
         kw["n_row_slices"] = args.row_slices
     if args.col_slices:
@@ -543,6 +545,7 @@ def main():
                    "col_slices": info.n_col_slices, "backward": w.backward,
                    "heads_shard": [w.q_heads_shard, w.kv_heads_shard] if w.has_attn else None,
                    "worker_streams": info.n_streams, "copy_streams": info.n_copy_streams,
+                   "dh_group_slices": info.dh_group_slices if w.backward else None,
                    "tile": args.tile,
                    "handoff": "blit" if args.copy_blit else (
                        "dma, whole row slices" if not args.handoff_pieces and info.n_col_slices > 1

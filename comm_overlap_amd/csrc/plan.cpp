@@ -58,7 +58,7 @@ MlpBwdWs mlp_bwd_ws(const tpslice_plan_s* p) {
   w.dw1_split = w.partials + align_up(partials_bytes(p->M, p->N1), kWsAlign);
   w.dw2_split = w.dw1_split + align_up(split_partials_bytes(p->N1, p->h, p->sp_dw1), kWsAlign);
   w.dh_split = w.dw2_split + align_up(split_partials_bytes(p->h, p->Fp, p->sp_dw2), kWsAlign);
-  w.dh_split_bytes = align_up(split_partials_bytes(p->Ms, p->Fp, p->sp_dh), kWsAlign);
+  w.dh_split_bytes = align_up(split_partials_bytes(p->Ms * p->gdh, p->Fp, p->sp_dh), kWsAlign);
   w.total = w.dh_split + w.dh_split_bytes * size_t(worker_regions(p));
   return w;
 }
@@ -83,27 +83,28 @@ static bool fits_4g(int64_t rows, int64_t cols, int64_t elem) {
   return rows >= 0 && cols >= 0 && bytes < 4294967296.0 - 4096.0;
 }
 
-// Worker streams when the descriptor leaves them open. The share of a row slice's forward product
-// work that leaves compute units idle: each product's flops times the share of its rounds of blocks
-// it leaves empty on the 256 CUs (with the tile it takes alone; a product split along k counts the
-// blocks of its 256 x 256 partial products). One stream (slices in order) when that share is at most
-// 5%; otherwise two, so that each slice's products share the CUs with the next slice's first product
-// (the schedule choice between finer pieces and more overlap, by the products' static sizes: FiCCO
-// page, Abstract). The QKV projection runs over all tokens after the slices and does not count.
-// Measured with 2048-row slices: the Llama-2 7B MLP (its up-projection fills 200 of 256 CUs: 31%
-// idle work) 914 TFLOP/s with one stream against 972 with two; the Llama-3 70B layer (every
-// per-slice product fills its rounds) 1130 with one against 1140 with two, within run-to-run
-// spread, and one stream's launches do not share the GPU.
+// Worker streams when the descriptor leaves them open. For an MLP shard (no attention heads): the
+// share of a row slice's forward product work that leaves compute units idle, each product's flops
+// times the share of its rounds of blocks it leaves empty on the 256 CUs (with the tile it takes
+// alone; a product split along k counts the blocks of its 256 x 256 partial products). One stream
+// (slices in order) when that share is at most 5%; otherwise two, so that each slice's products
+// share the CUs with the next slice's first product (the schedule choice between finer pieces and
+// more overlap, by the products' static sizes: FiCCO page, Abstract). A layer shard (attention
+// heads) takes one stream: its QKV projection, dC and every weight gradient run over all tokens on
+// worker 0 and dH over groups of row slices, so only the hand-off products could share the CUs,
+// and a second stream's event hops cost more than that gains. Measured with 2048-row slices: the
+// Llama-2 7B MLP (its up-projection fills 200 of 256 CUs: 31% idle work) 914 TFLOP/s with one
+// stream against 972 with two; the Llama-2 13B layer 802 with one against 709 with two; the
+// Llama-3 70B layer 1130 against 1140, within run-to-run spread.
 static int32_t default_streams(const tpslice_plan_s* p) {
   constexpr int64_t kCUs = 256;
-  if (p->r <= 1) return 1;
+  if (p->r <= 1 || p->qh > 0) return 1;
   const bool glu = p->desc.act == TPSLICE_ACT_SWIGLU;
   const int64_t h = p->desc.hidden;
   struct P { int64_t n, k; int epi; int splits; double flops; };
   const P prods[] = {
       {p->Fp, h, glu ? kEpiSwiglu : kEpiGelu, choose_slice_split(p->N1, h), double(p->N1) * double(h)},
       {p->pw, p->Fp, kEpiBf16, 1, double(h) * double(p->Fp)},
-      {p->qh ? p->pw : 0, p->ctx, kEpiBf16, 1, double(h) * double(p->ctx)},
   };
   double idle = 0.0, total = 0.0;
   for (const P& q : prods) {
@@ -243,6 +244,8 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   if (d->n_col_slices > 0 && (d->hidden % d->n_col_slices || (d->hidden / d->n_col_slices) % 8))
     return fail(TPSLICE_ERR_SHAPE, "%d column slices of hidden %lld must be equal multiples of 8",
                 d->n_col_slices, (long long)d->hidden);
+  if (d->dh_group < 0 || (d->dh_group & (d->dh_group - 1)) != 0)
+    return fail(TPSLICE_ERR_INVALID, "dh_group %d must be 0 or a power of two", d->dh_group);
   if (d->n_streams < 0 || d->n_streams > kMaxStreams)
     return fail(TPSLICE_ERR_SHAPE, "n_streams %d outside [0, %d]", d->n_streams, kMaxStreams);
   if (d->n_copy_streams < 0 || d->n_copy_streams > kMaxCopyStreams)
@@ -310,7 +313,32 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   // k splits of the per-slice products: a function of the product's width and depth only, so that
   // every slicing of the same batch reduces k in the same order
   p->sp_up = choose_slice_split(N1, h);
-  p->sp_dh = choose_slice_split(Fp, h);
+  // dH over groups of row slices: the k split is the whole batch's (so every slicing of the same
+  // batch sums k in the same order), the group the fewest row slices whose product, so split, comes
+  // within 5% of the best time per row slice. On the 70B shard a 2048-row slice's dH is 112 tiles
+  // of 256 x 256 (44% of the CUs); two row slices make 224, with no split and no reduction pass.
+  p->sp_dh = choose_split(M, Fp, h);
+  {
+    const int epi_dh = d->act == TPSLICE_ACT_SWIGLU ? kEpiDswiglu : kEpiDgelu;
+    double best = 1e300;
+    double per[6] = {0};
+    int n = 0;
+    for (int g = 1; g <= p->r && n < 6; g *= 2, ++n) {
+      per[n] = p->r % g ? 1e300 : estimate_product_us(p->Ms * g, Fp, h, kDgrad, epi_dh, true, p->sp_dh) / g;
+      best = std::min(best, per[n]);
+    }
+    p->gdh = 1;
+    for (int k = 0, g = 1; k < n; ++k, g *= 2)
+      if (per[k] <= best * 1.05) { p->gdh = g; break; }
+    if (d->dh_group > 0) {
+      if (p->r % d->dh_group != 0) {
+        const int32_t r = p->r;
+        delete p;
+        return fail(TPSLICE_ERR_INVALID, "dh_group %d does not divide the %d row slices", d->dh_group, r);
+      }
+      p->gdh = d->dh_group;
+    }
+  }
   // Products of adjacent row slices share the GPU on two worker streams. A compute unit holding a
   // 128 x 128 block (64 KB of LDS) has no room for a four-wave 256 x 256 block (128 KB) of the
   // product beside it, so mixing the two leaves units waiting: when the row slices' first product
@@ -340,6 +368,7 @@ extern "C" tpslice_status_t tpslice_plan_info(tpslice_plan_t p, tpslice_plan_inf
   const int32_t sp[8] = {p->sp_up, p->sp_qkv, p->sp_dh, p->sp_dw1, p->sp_dw2, p->sp_dc, p->sp_dwo, p->sp_dwqkv};
   for (int k = 0; k < 8; ++k) info->k_splits[k] = sp[k];
   const double gbps = p->desc.handoff_gbps > 0.0f ? double(p->desc.handoff_gbps) : kLocalHandoffGbps;
+  info->dh_group_slices = p->gdh;
   info->predicted_forward_us =
       predict_forward_us(&p->desc, p->Fp, p->N1, p->qh ? p->qkv : 0, p->ctx, p->r, p->c, p->S, gbps);
   return TPSLICE_OK;

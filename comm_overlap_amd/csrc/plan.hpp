@@ -19,9 +19,12 @@ struct tpslice_plan_s {
   int32_t r, c, S, E;              // row slices, column slices, worker streams, copy streams
   int32_t qh, kvh;                 // this rank's query / key-value heads
   int32_t trace;                   // tracing enabled
-  // k splits (1: none) of the products over all tokens (dW1, dW2, dC, dWo, dWqkv) and of the row
-  // slices' first products (up-projection, QKV projection, dH)
+  // k splits (1: none) of the products over all tokens (dW1, dW2, dC, dWo, dWqkv, QKV), of the
+  // row slices' up-projection and of the dH groups
   int32_t sp_dw1, sp_dw2, sp_dc, sp_dwo, sp_dwqkv, sp_up, sp_qkv, sp_dh;
+  // row slices per dH product: dH runs over groups of gdh consecutive row slices (it is not handed
+  // off; each row slice's dX product and hand-off follow it)
+  int32_t gdh;
   int32_t tile;                    // tile requested for every product (GemmTile; 0: per product)
   void* rt;                        // device resources (streams, events), created on first execution
 };

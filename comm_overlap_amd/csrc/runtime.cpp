@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -179,7 +180,9 @@ struct Schedule {
   // units they leave idle) and the slices finish one after another, each hand-off starting while
   // later slices still compute. Pipelined mode: row slice i's products also wait for the previous
   // call's hand-off of row slice i.
-  tpslice_status_t slice_begin(int i) {
+  // `span`: row slices i .. i + span - 1 whose rows the slice's first product reads (a product over
+  // a group of row slices waits for the previous call's hand-off of each of them).
+  tpslice_status_t slice_begin(int i, int span = 1) {
     if (serial) return TPSLICE_OK;
     // the next slice waits for this one's first product only from another worker stream (one
     // worker: stream order already does it, and an event between two products costs their gap)
@@ -187,10 +190,11 @@ struct Schedule {
     if (i > 0 && lead_done == i - 1 && worker(i) != worker(i - 1))
       TPS_HIP(hipStreamWaitEvent(worker(i), rt->lead[i - 1], 0));
     if (!pipelined()) return TPSLICE_OK;
-    for (int k = 0; k < p->E; ++k) {
-      const size_t x = size_t(i) * p->E + k;
-      if (rt->copied_pending[x]) TPS_HIP(hipStreamWaitEvent(worker(i), rt->copied[x], 0));
-    }
+    for (int q = i; q < i + span && q < p->r; ++q)
+      for (int k = 0; k < p->E; ++k) {
+        const size_t x = size_t(q) * p->E + k;
+        if (rt->copied_pending[x]) TPS_HIP(hipStreamWaitEvent(worker(i), rt->copied[x], 0));
+      }
     return TPSLICE_OK;
   }
 
@@ -687,15 +691,20 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
   TPS_TRY(S.fork());
   for (int i = 0; i < p->r && p->M > 0; ++i) {
     const int64_t r0 = int64_t(i) * p->Ms;
-    TPS_TRY(S.slice_begin(i));
+    const bool group = i % p->gdh == 0;  // row slice i starts a dH group
+    TPS_TRY(S.slice_begin(i, group ? p->gdh : 1));
     S.slice_streams = 0;
-    // dH = dY W2 with the activation's derivative fused: writes dU and (recomputed) H
-    GemmArgs g = args(bf(dY, r0 * p->h), p->h, W2, p->Fp, bfw(dU, r0 * p->N1), p->N1, p->Ms, p->Fp, p->h);
-    g.aux_in = bf(U, r0 * p->N1); g.ld_in = p->N1;
-    g.aux_out = bfw(H, r0 * p->Fp); g.ld_out = p->Fp;
-    g.half = p->Fp;
-    TPS_TRY(S.product_split(i, TPSLICE_STEP_MLP_DH, -1, g, kDgrad, glu ? kEpiDswiglu : kEpiDgelu, p->sp_dh,
-                            S.slice_part(static_cast<char*>(ws) + L.dh_split, L.dh_split_bytes, i)));
+    if (group) {
+      // dH = dY W2 with the activation's derivative fused, over the group's rows: writes dU and
+      // (recomputed) H
+      const int64_t rows = std::min<int64_t>(p->gdh, p->r - i) * p->Ms;
+      GemmArgs g = args(bf(dY, r0 * p->h), p->h, W2, p->Fp, bfw(dU, r0 * p->N1), p->N1, rows, p->Fp, p->h);
+      g.aux_in = bf(U, r0 * p->N1); g.ld_in = p->N1;
+      g.aux_out = bfw(H, r0 * p->Fp); g.ld_out = p->Fp;
+      g.half = p->Fp;
+      TPS_TRY(S.product_split(i, TPSLICE_STEP_MLP_DH, -1, g, kDgrad, glu ? kEpiDswiglu : kEpiDgelu, p->sp_dh,
+                              S.slice_part(static_cast<char*>(ws) + L.dh_split, L.dh_split_bytes, i)));
+    }
     for (int j = 0; j < p->pc; ++j) {
       const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs gx = args(bf(dU, r0 * p->N1), p->N1, bf(W1, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms, p->pw,

@@ -128,7 +128,10 @@ typedef struct {
   int32_t n_copy_streams; /* side streams for hand-off copies (0 = default: 1)                        */
   uint32_t flags;         /* TPSLICE_F_*                                                                */
   float handoff_gbps;     /* hand-off rate in GB/s that the automatic slice counts assume (0: the
-                             local DMA copy of this GPU, about 400 GB/s); ignored for given counts */
+                             local DMA copy of this GPU, about 600 GB/s); ignored for given counts */
+  int32_t dh_group;       /* row slices per dH product of the MLP backward (0: automatic, see
+                             tpslice_plan_info_t.dh_group_slices); else a power of two dividing
+                             the row slice count                                                  */
 } tpslice_desc_t;
 
 /* Automatic slice counts (Design Space Exploration of DMA based Finer-Grain Compute Communication
@@ -167,13 +170,17 @@ typedef struct {
   int32_t n_row_slices, n_col_slices, n_streams, n_copy_streams;
   int32_t q_heads, kv_heads;    /* this rank's head counts                                           */
   /* k splits (1 = none) the plan takes for, in order: the up-projection of each row slice, the QKV
-     projection over all tokens, dH of each row slice, then dW1, dW2, dC, dWo, dWqkv over all
-     tokens. A split product sums its k runs' fp32 partials in order before the epilogue: the same
-     bits for every slicing of the same batch, other rounding than an unsplit product.          */
+     projection over all tokens, dH of each group of row slices, then dW1, dW2, dC, dWo, dWqkv over
+     all tokens. A split product sums its k runs' fp32 partials in order before the epilogue: the
+     same bits for every slicing of the same batch, other rounding than an unsplit product.     */
   int32_t k_splits[8];
   /* the slice-count model's predicted time (us) of one call of the forward products with this
      plan's r and c (see the automatic slice counts above); a comparison figure, not a timing */
   double predicted_forward_us;
+  /* row slices per dH product of the MLP backward (dH is not handed off: it runs over groups of
+     consecutive row slices large enough to fill the GPU, each row slice's dX product and hand-off
+     after it)                                                                                  */
+  int32_t dh_group_slices;
 } tpslice_plan_info_t;
 
 typedef enum {
@@ -243,7 +250,9 @@ TPSLICE_API tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t plan, const voi
  *   dW1 (+)= dU^T X;  db1 (+)= column sums of dU;  dW2 (+)= dY^T act(U)
  * dX [M][h] bf16 is this rank's partial sum and the hand-off tensor (dX_handoff as Z_handoff above).
  * dW1 [N1][h], dW2 [h][F'] and db1 [N1] (or NULL) are fp32; accumulate = 0 overwrites them,
- * 1 adds to their contents. Workspace: tpslice_workspace_size(TPSLICE_OP_MLP_BWD).               */
+ * 1 adds to their contents. Workspace: tpslice_workspace_size(TPSLICE_OP_MLP_BWD).
+ * dH, which is not handed off, runs over groups of consecutive row slices (plan info
+ * dh_group_slices); each row slice's dX product and hand-off follow its group's dH.               */
 TPSLICE_API tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t plan, const void* X, const void* W1, const void* W2,
                                  const void* U_saved, const void* dY, void* dX, void* dX_handoff,
                                  float* dW1, float* db1, float* dW2, int32_t accumulate,

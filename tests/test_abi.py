@@ -198,6 +198,31 @@ def test_whole_row_handoff_runs_one_product_per_row_slice():
     assert rows.info.predicted_forward_us == pytest.approx(one.info.predicted_forward_us, rel=1e-12)
 
 
+@pytest.mark.parametrize("key", LARGE)
+def test_dh_groups_divide_the_row_slices_and_keep_the_split(key):
+    """dH runs over groups of row slices: the group size divides r, and the k split (the whole
+    batch's) is the same for every slicing, so that sliced and unsliced backward passes keep the
+    same bits. On the 70B shard a 2048-row slice's dH fills 112 of 256 CUs: two row slices a group."""
+    w = synth.WORKLOADS[key]
+    base = T.plan_for(w, n_row_slices=1, n_col_slices=1).info
+    assert base.dh_group_slices == 1
+    for r in (1, 2, 4, 8):
+        if w.tokens % r:
+            continue
+        i = T.plan_for(w, n_row_slices=r).info
+        assert r % i.dh_group_slices == 0
+        assert i.splits()["dh"] == base.splits()["dh"]
+    if key == "llama3_70b_layer":
+        assert T.plan_for(w).info.dh_group_slices == 2
+    # a requested group size is kept; one that does not divide r, or is no power of two, is refused
+    r = T.plan_for(w).info.n_row_slices
+    assert T.plan_for(w, dh_group=r).info.dh_group_slices == r
+    for bad in (2 * r, 3, -1):
+        with pytest.raises(T.TpsliceError) as e:
+            T.plan_for(w, dh_group=bad)
+        assert e.value.code == T.ERR_INVALID
+
+
 def test_given_slice_counts_are_kept():
     w = synth.WORKLOADS["llama3_70b_layer"]
     for gbps in (0.0, 25.0):

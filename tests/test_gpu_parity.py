@@ -344,8 +344,9 @@ def test_split_k_backward():
             assert torch.equal(a2[k], aout[k]), (kw, k)
 
 
-# A long reduction (h = 2048) with narrow projections: the row slices' first products (up, QKV,
-# dH) are split along k; the split count does not depend on the slice height.
+# A long reduction (h = 2048) with narrow projections: the up-projection of each row slice, the QKV
+# projection over all tokens and dH over each group of row slices are split along k; the split
+# counts do not depend on the slicing.
 SLICE_SPLIT = [synth.custom("slice_split_gelu", 907, tokens=1024, hidden=2048, ffn=264, tp=1, act="gelu",
                             bias=True, row_slices=2, col_slices=1, heads=6, kv_heads=2, head_dim=40,
                             backward=True),
