@@ -50,7 +50,7 @@ int main() {
   (void)hipFuncSetAttribute((const void*)probe<0>, hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
   (void)hipFuncSetAttribute((const void*)probe<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
   struct C { const char* name; int mode; uint32_t region; };
-  const C cs[] = {{"dma  L2-resident (256 KB/CU)", 0, 1u << 18}, {"vgpr L2-resident (256 KB/CU)", 1, 1u << 18},
+  const C cs[] = {{"dma  past L2 (256 KB/CU)", 0, 1u << 18}, {"vgpr past L2 (256 KB/CU)", 1, 1u << 18},
                   {"dma  HBM stream (4 MB/CU)", 0, 1u << 22}, {"vgpr HBM stream (4 MB/CU)", 1, 1u << 22},
                   {"dma  L2-resident (64 KB/CU)", 0, 1u << 16}, {"vgpr L2-resident (64 KB/CU)", 1, 1u << 16}};
   for (int rep = 0; rep < 2; ++rep)

@@ -52,19 +52,26 @@ __global__ __launch_bounds__(256) void k32(int iters, float* out, unsigned long 
 template <class K>
 static void run(const char* name, K kern, int blocks, int iters, double flops_per_wave_iter) {
   float* out; unsigned long long* clk;
-  hipMalloc(&out, size_t(blocks) * 256 * sizeof(float));
-  hipMalloc(&clk, 2 * sizeof(unsigned long long));
-  hipEvent_t e0, e1; hipEventCreate(&e0); hipEventCreate(&e1);
+  if (hipMalloc(&out, size_t(blocks) * 256 * sizeof(float)) != hipSuccess ||
+      hipMalloc(&clk, 2 * sizeof(unsigned long long)) != hipSuccess) {
+    printf("allocation failed\n");
+    return;
+  }
+  hipEvent_t e0, e1;
+  (void)hipEventCreate(&e0);
+  (void)hipEventCreate(&e1);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, 0, iters / 4, out, clk);  // warm
-  hipDeviceSynchronize();
+  (void)hipDeviceSynchronize();
   std::vector<double> tf, ghz;
   for (int r = 0; r < 5; ++r) {
-    hipEventRecord(e0, 0);
+    (void)hipEventRecord(e0, 0);
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, 0, iters, out, clk);
-    hipEventRecord(e1, 0);
-    hipEventSynchronize(e1);
-    float ms; hipEventElapsedTime(&ms, e0, e1);
-    unsigned long long c[2]; hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost);
+    (void)hipEventRecord(e1, 0);
+    (void)hipEventSynchronize(e1);
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    unsigned long long c[2] = {0, 1};
+    (void)hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost);
     const double fl = double(blocks) * 4 * iters * flops_per_wave_iter;
     tf.push_back(fl / (ms * 1e-3) / 1e12);
     ghz.push_back(double(c[0]) / double(c[1]) * 0.1);
@@ -72,7 +79,10 @@ static void run(const char* name, K kern, int blocks, int iters, double flops_pe
   std::sort(tf.begin(), tf.end()); std::sort(ghz.begin(), ghz.end());
   printf("%-28s blocks %5d: %.1f TFLOP/s (median of 5; min %.1f max %.1f), clock %.3f GHz (memtime/realtime)\n", name,
          blocks, tf[2], tf[0], tf[4], ghz[2]);
-  hipFree(out); hipFree(clk);
+  (void)hipFree(out);
+  (void)hipFree(clk);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
 }
 
 int main() {
