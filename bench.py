@@ -57,6 +57,8 @@ def parse():
                     help="block tile of every product (auto = chosen per product, the default)")
     ap.add_argument("--dh-group", type=int, default=0,
                     help="row slices per dH product of the MLP backward (0 = plan default)")
+    ap.add_argument("--up-group", type=int, default=0,
+                    help="row slices per up-projection of the MLP forward (0 = plan default)")
     ap.add_argument("--copy-blit", action="store_true", help="hand-off by copy kernel instead of DMA")
     ap.add_argument("--caller-worker", action="store_true",
                     help="worker stream 0 is the caller's stream (plans with one worker stream always do this)")
@@ -402,7 +404,8 @@ def main():
     dev = {k: v.to("cuda").contiguous() for k, v in inp.items()}
     flops = sum(w.gemm_flops().values())
     kw = dict(n_streams=args.streams, n_copy_streams=args.copy_streams, copy_blit=args.copy_blit, tile=args.tile,
-              handoff_rows=not args.handoff_pieces, caller_worker=args.caller_worker, dh_group=args.dh_group)
+              handoff_rows=not args.handoff_pieces, caller_worker=args.caller_worker, dh_group=args.dh_group,
+              up_group=args.up_group)
     if args.row_slices:
         kw["n_row_slices"] = args.row_slices
     if args.col_slices:
@@ -545,6 +548,7 @@ def main():
                    "col_slices": info.n_col_slices, "backward": w.backward,
                    "heads_shard": [w.q_heads_shard, w.kv_heads_shard] if w.has_attn else None,
                    "worker_streams": info.n_streams, "copy_streams": info.n_copy_streams,
+                   "up_group_slices": info.up_group_slices,
                    "dh_group_slices": info.dh_group_slices if w.backward else None,
                    "tile": args.tile,
                    "handoff": "blit" if args.copy_blit else (

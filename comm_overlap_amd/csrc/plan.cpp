@@ -33,7 +33,7 @@ MlpFwdWs mlp_fwd_ws(const tpslice_plan_s* p) {
   MlpFwdWs w{};
   w.H = 0;
   w.up_split = align_up(size_t(p->M) * size_t(p->Fp) * 2, kWsAlign);
-  w.up_split_bytes = align_up(split_partials_bytes(p->Ms, p->N1, p->sp_up), kWsAlign);
+  w.up_split_bytes = align_up(split_partials_bytes(p->Ms * p->gup, p->N1, p->sp_up), kWsAlign);
   w.total = w.up_split + w.up_split_bytes * size_t(worker_regions(p));
   return w;
 }
@@ -83,6 +83,22 @@ static bool fits_4g(int64_t rows, int64_t cols, int64_t elem) {
   return rows >= 0 && cols >= 0 && bytes < 4294967296.0 - 4096.0;
 }
 
+// Row slices per product of a producer that is not handed off (the up-projection, dH): the fewest
+// (a power of two dividing r) whose product over that many row slices, with `splits` k splits,
+// comes within 5% of the best estimated time per row slice.
+static int32_t slice_group(int32_t r, int64_t Ms, int64_t N, int64_t K, int layout, int epi, int splits) {
+  if (Ms <= 0) return 1;
+  double per[6] = {0}, best = 1e300;
+  int n = 0;
+  for (int g = 1; g <= r && n < 6; g *= 2, ++n) {
+    per[n] = r % g ? 1e300 : estimate_product_us(Ms * g, N, K, layout, epi, true, splits) / g;
+    best = std::min(best, per[n]);
+  }
+  for (int k = 0, g = 1; k < n; ++k, g *= 2)
+    if (per[k] <= best * 1.05) return g;
+  return 1;
+}
+
 // Worker streams when the descriptor leaves them open. For an MLP shard (no attention heads): the
 // share of a row slice's forward product work that leaves compute units idle, each product's flops
 // times the share of its rounds of blocks it leaves empty on the 256 CUs (with the tile it takes
@@ -92,19 +108,24 @@ static bool fits_4g(int64_t rows, int64_t cols, int64_t elem) {
 // more overlap, by the products' static sizes: FiCCO page, Abstract). A layer shard (attention
 // heads) takes one stream: its QKV projection, dC and every weight gradient run over all tokens on
 // worker 0 and dH over groups of row slices, so only the hand-off products could share the CUs,
-// and a second stream's event hops cost more than that gains. Measured with 2048-row slices: the
-// Llama-2 7B MLP (its up-projection fills 200 of 256 CUs: 31% idle work) 914 TFLOP/s with one
-// stream against 972 with two; the Llama-2 13B layer 802 with one against 709 with two; the
-// Llama-3 70B layer 1130 against 1140, within run-to-run spread.
+// and a second stream's event hops cost more than that gains. So does a shard whose up-projection
+// runs over groups of row slices. Measured with 2048-row slices: the Llama-2 7B MLP (its
+// up-projection per row slice fills 200 of 256 CUs: 31% idle work) 914 TFLOP/s with one stream
+// against 972 with two, and 971 with one stream and the up-projection over all four row slices
+// (668 with two: each row slice's down-projection then waits for the one before on the other
+// stream); the Llama-2 13B layer 802 with one against 709 with two; the Llama-3 70B layer 1130
+// against 1140, within run-to-run spread.
 static int32_t default_streams(const tpslice_plan_s* p) {
   constexpr int64_t kCUs = 256;
-  if (p->r <= 1 || p->qh > 0) return 1;
+  // (an up-projection over groups of row slices fills the GPU by itself and leaves each row slice
+  // one product, the down-projection: two streams would only order those across streams)
+  if (p->r <= 1 || p->qh > 0 || p->gup > 1) return 1;
   const bool glu = p->desc.act == TPSLICE_ACT_SWIGLU;
   const int64_t h = p->desc.hidden;
-  struct P { int64_t n, k; int epi; int splits; double flops; };
+  struct P { int64_t rows, n, k; int epi; int splits; double flops; };
   const P prods[] = {
-      {p->Fp, h, glu ? kEpiSwiglu : kEpiGelu, choose_slice_split(p->N1, h), double(p->N1) * double(h)},
-      {p->pw, p->Fp, kEpiBf16, 1, double(h) * double(p->Fp)},
+      {p->Ms * p->gup, p->Fp, h, glu ? kEpiSwiglu : kEpiGelu, p->sp_up, double(p->N1) * double(h)},
+      {p->Ms, p->pw, p->Fp, kEpiBf16, 1, double(h) * double(p->Fp)},
   };
   double idle = 0.0, total = 0.0;
   for (const P& q : prods) {
@@ -112,16 +133,33 @@ static int32_t default_streams(const tpslice_plan_s* p) {
     double fill = 0.0;
     if (q.splits > 1) {
       const int64_t nt = q.epi == kEpiSwiglu ? 2 * q.n : q.n;  // both halves: the split partials' width
-      const int64_t blocks = ((p->Ms + 255) / 256) * ((nt + 255) / 256) * q.splits;
+      const int64_t blocks = ((q.rows + 255) / 256) * ((nt + 255) / 256) * q.splits;
       const int64_t rounds = (blocks + kCUs - 1) / kCUs;
       fill = double(blocks) / double(rounds * kCUs);
     } else {
-      choose_tile(p->Ms, q.n, q.k, kFwd, q.epi, true, &fill);
+      choose_tile(q.rows, q.n, q.k, kFwd, q.epi, true, &fill);
     }
     idle += q.flops * (1.0 - fill);
     total += q.flops;
   }
   return total > 0.0 && idle > 0.05 * total ? 2 : 1;
+}
+
+// The forward schedule of a plan whose geometry (r, c, Ms, pc, pw) is set: the up-projection's k
+// split (the whole batch's), its row-slice group and the worker streams. Two worker streams and
+// grouped up-projections exclude each other: with two streams each row slice's up-projection fills
+// the CUs the other stream's products leave idle; grouped, it fills them by itself, and the row
+// slices are left one product each.
+static void forward_schedule(tpslice_plan_s* q) {
+  const tpslice_desc_t* d = &q->desc;
+  const int epi_up = d->act == TPSLICE_ACT_SWIGLU ? kEpiSwiglu : kEpiGelu;
+  q->sp_up = choose_split(d->tokens, q->N1, d->hidden);
+  const bool forced = d->up_group > 0 && q->r % d->up_group == 0;
+  q->gup = forced ? d->up_group : 1;
+  if (d->flags & TPSLICE_F_SERIALIZE) q->S = 1;
+  else if (d->n_streams > 0) q->S = d->n_streams;
+  else q->S = default_streams(q);
+  if (!forced && q->S == 1) q->gup = slice_group(q->r, q->Ms, q->Fp, d->hidden, kFwd, epi_up, q->sp_up);
 }
 
 // Rate of this GPU's local hand-off copy for large pieces (DMA engine, measured 550-760 GB/s for
@@ -139,7 +177,7 @@ constexpr double kSliceSyncUs1 = 20.0, kSliceSyncUs2 = 80.0;
 // one product over twice the rows for each pair. Row slice i's copies run while later slices
 // compute, the last ones under the QKV projection over all tokens (which follows the slices).
 static double predict_forward_us(const tpslice_desc_t* d, int64_t Fp, int64_t N1, int64_t qkv, int64_t ctx, int r,
-                                 int c, int S, double gbps) {
+                                 int c, int S, int gup, double gbps) {
   const int64_t M = d->tokens, Ms = M / r, h = d->hidden;
   const int pc = (c > 1 && (d->flags & TPSLICE_F_HANDOFF_ROWS)) ? 1 : c;  // products per row slice
   const int64_t pw = h / pc;
@@ -147,8 +185,11 @@ static double predict_forward_us(const tpslice_desc_t* d, int64_t Fp, int64_t N1
   const int64_t Mp = Ms * pair;  // rows of the products that share the GPU at once
   const bool alone = pair == 1;
   const int epi_up = d->act == TPSLICE_ACT_SWIGLU ? kEpiSwiglu : kEpiGelu;
-  double group_us = estimate_product_us(Mp, Fp, h, kFwd, epi_up, alone, choose_slice_split(N1, h)) +
-                    pc * estimate_product_us(Mp, pw, Fp, kFwd, kEpiBf16, alone);
+  // the up-projection over groups of row slices (see tpslice_plan), its time shared by the group
+  const int sp_up = choose_split(M, N1, h);
+  const double up_us = gup > 1 ? pair * estimate_product_us(Ms * gup, Fp, h, kFwd, epi_up, true, sp_up) / gup
+                               : estimate_product_us(Mp, Fp, h, kFwd, epi_up, alone, sp_up);
+  double group_us = up_us + pc * estimate_product_us(Mp, pw, Fp, kFwd, kEpiBf16, alone);
   int tensors = 1;
   double tail_us = 0.0;  // products over all tokens after the slices
   if (qkv > 0) {
@@ -193,8 +234,8 @@ static void choose_slices(const tpslice_desc_t* d, int64_t Fp, int64_t N1, int64
       q.r = r; q.c = c; q.Ms = d->tokens / r; q.hc = d->hidden / c;
       q.pc = (c > 1 && (d->flags & TPSLICE_F_HANDOFF_ROWS)) ? 1 : c;
       q.pw = d->hidden / q.pc;
-      const int S = (d->flags & TPSLICE_F_SERIALIZE) ? 1 : d->n_streams > 0 ? d->n_streams : default_streams(&q);
-      const double t = predict_forward_us(d, Fp, N1, qkv, ctx, r, c, S, gbps);
+      forward_schedule(&q);
+      const double t = predict_forward_us(d, Fp, N1, qkv, ctx, r, c, q.S, q.gup, gbps);
       const int pieces = r * c;
       // candidates with more pieces must be 2% faster to be taken
       const bool better = pieces <= best_pieces ? t < best : t < best * 0.98;
@@ -244,8 +285,10 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   if (d->n_col_slices > 0 && (d->hidden % d->n_col_slices || (d->hidden / d->n_col_slices) % 8))
     return fail(TPSLICE_ERR_SHAPE, "%d column slices of hidden %lld must be equal multiples of 8",
                 d->n_col_slices, (long long)d->hidden);
-  if (d->dh_group < 0 || (d->dh_group & (d->dh_group - 1)) != 0)
-    return fail(TPSLICE_ERR_INVALID, "dh_group %d must be 0 or a power of two", d->dh_group);
+  if (d->dh_group < 0 || (d->dh_group & (d->dh_group - 1)) != 0 || d->up_group < 0 ||
+      (d->up_group & (d->up_group - 1)) != 0)
+    return fail(TPSLICE_ERR_INVALID, "up_group %d and dh_group %d must be 0 or powers of two", d->up_group,
+                d->dh_group);
   if (d->n_streams < 0 || d->n_streams > kMaxStreams)
     return fail(TPSLICE_ERR_SHAPE, "n_streams %d outside [0, %d]", d->n_streams, kMaxStreams);
   if (d->n_copy_streams < 0 || d->n_copy_streams > kMaxCopyStreams)
@@ -284,9 +327,26 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   p->Ms = M / p->r; p->hc = h / p->c;
   p->pc = (p->c > 1 && (d->flags & TPSLICE_F_HANDOFF_ROWS)) ? 1 : p->c;
   p->pw = h / p->pc;
-  const bool serial = d->flags & TPSLICE_F_SERIALIZE;
+  // The up-projection and dH are not handed off (the down-projection and dX after them are): each
+  // runs over groups of row slices, the fewest whose product comes within 5% of the best time per
+  // row slice, with the whole batch's k split, so that every slicing of the same batch sums k in
+  // the same order. On the 70B shard a 2048-row slice's dH is 112 tiles of 256 x 256 (44% of the
+  // CUs); two row slices make 224, with no split and no reduction pass. On the 13B shard a row
+  // slice's up-projection is 128 tiles of 256 x 224; all four make 512.
   p->qh = qh; p->kvh = kvh;
-  p->S = serial ? 1 : (d->n_streams ? d->n_streams : default_streams(p));
+  forward_schedule(p);
+  p->sp_dh = choose_split(M, Fp, h);
+  p->gdh = slice_group(p->r, p->Ms, Fp, h, kDgrad, d->act == TPSLICE_ACT_SWIGLU ? kEpiDswiglu : kEpiDgelu,
+                       p->sp_dh);
+  for (const int32_t want : {d->up_group, d->dh_group}) {
+    if (want > 0 && p->r % want != 0) {
+      const int32_t r = p->r;
+      delete p;
+      return fail(TPSLICE_ERR_INVALID, "a group of %d row slices does not divide the %d row slices", want, r);
+    }
+  }
+  if (d->dh_group > 0) p->gdh = d->dh_group;
+  const bool serial = d->flags & TPSLICE_F_SERIALIZE;
   p->E = serial ? 1 : (d->n_copy_streams ? d->n_copy_streams : 1);
   // One worker stream: it is the caller's stream. A worker stream of its own would only add a
   // fork and a join per call (about 13 us at each call boundary; GPT-3 2.7B MLP chain 1095 ->
@@ -309,35 +369,6 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
                              estimate_product_us(M, qkv, h, kFwd, kEpiBf16, true, 1) ? s : 1;
   } else {
     p->sp_qkv = 1;
-  }
-  // k splits of the per-slice products: a function of the product's width and depth only, so that
-  // every slicing of the same batch reduces k in the same order
-  p->sp_up = choose_slice_split(N1, h);
-  // dH over groups of row slices: the k split is the whole batch's (so every slicing of the same
-  // batch sums k in the same order), the group the fewest row slices whose product, so split, comes
-  // within 5% of the best time per row slice. On the 70B shard a 2048-row slice's dH is 112 tiles
-  // of 256 x 256 (44% of the CUs); two row slices make 224, with no split and no reduction pass.
-  p->sp_dh = choose_split(M, Fp, h);
-  {
-    const int epi_dh = d->act == TPSLICE_ACT_SWIGLU ? kEpiDswiglu : kEpiDgelu;
-    double best = 1e300;
-    double per[6] = {0};
-    int n = 0;
-    for (int g = 1; g <= p->r && n < 6; g *= 2, ++n) {
-      per[n] = p->r % g ? 1e300 : estimate_product_us(p->Ms * g, Fp, h, kDgrad, epi_dh, true, p->sp_dh) / g;
-      best = std::min(best, per[n]);
-    }
-    p->gdh = 1;
-    for (int k = 0, g = 1; k < n; ++k, g *= 2)
-      if (per[k] <= best * 1.05) { p->gdh = g; break; }
-    if (d->dh_group > 0) {
-      if (p->r % d->dh_group != 0) {
-        const int32_t r = p->r;
-        delete p;
-        return fail(TPSLICE_ERR_INVALID, "dh_group %d does not divide the %d row slices", d->dh_group, r);
-      }
-      p->gdh = d->dh_group;
-    }
   }
   // Products of adjacent row slices share the GPU on two worker streams. A compute unit holding a
   // 128 x 128 block (64 KB of LDS) has no room for a four-wave 256 x 256 block (128 KB) of the
@@ -369,8 +400,9 @@ extern "C" tpslice_status_t tpslice_plan_info(tpslice_plan_t p, tpslice_plan_inf
   for (int k = 0; k < 8; ++k) info->k_splits[k] = sp[k];
   const double gbps = p->desc.handoff_gbps > 0.0f ? double(p->desc.handoff_gbps) : kLocalHandoffGbps;
   info->dh_group_slices = p->gdh;
+  info->up_group_slices = p->gup;
   info->predicted_forward_us =
-      predict_forward_us(&p->desc, p->Fp, p->N1, p->qh ? p->qkv : 0, p->ctx, p->r, p->c, p->S, gbps);
+      predict_forward_us(&p->desc, p->Fp, p->N1, p->qh ? p->qkv : 0, p->ctx, p->r, p->c, p->S, p->gup, gbps);
   return TPSLICE_OK;
 }
 

@@ -25,6 +25,9 @@ struct tpslice_plan_s {
   // row slices per dH product: dH runs over groups of gdh consecutive row slices (it is not handed
   // off; each row slice's dX product and hand-off follow it)
   int32_t gdh;
+  // row slices per up-projection of the MLP forward (likewise: only the down-projection after it is
+  // handed off)
+  int32_t gup;
   int32_t tile;                    // tile requested for every product (GemmTile; 0: per product)
   void* rt;                        // device resources (streams, events), created on first execution
 };

@@ -586,14 +586,18 @@ extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, con
   TPS_TRY(S.fork());
   for (int i = 0; i < p->r; ++i) {
     const int64_t r0 = int64_t(i) * p->Ms;
-    TPS_TRY(S.slice_begin(i));
+    const bool group = i % p->gup == 0;  // row slice i starts an up-projection group
+    TPS_TRY(S.slice_begin(i, group ? p->gup : 1));
     S.slice_streams = 0;
-    GemmArgs g1 = args(bf(X, r0 * p->h), p->h, W1, p->h, bfw(H, r0 * p->Fp), p->Fp, p->Ms, p->Fp, p->h);
-    g1.bias = b1;
-    g1.half = p->Fp;
-    if (U_save) { g1.aux_out = bfw(U_save, r0 * p->N1); g1.ld_out = p->N1; }
-    TPS_TRY(S.product_split(i, TPSLICE_STEP_MLP_UP, -1, g1, kFwd, epi, p->sp_up,
-                            S.slice_part(static_cast<char*>(ws) + L.up_split, L.up_split_bytes, i)));
+    if (group) {
+      const int64_t rows = std::min<int64_t>(p->gup, p->r - i) * p->Ms;
+      GemmArgs g1 = args(bf(X, r0 * p->h), p->h, W1, p->h, bfw(H, r0 * p->Fp), p->Fp, rows, p->Fp, p->h);
+      g1.bias = b1;
+      g1.half = p->Fp;
+      if (U_save) { g1.aux_out = bfw(U_save, r0 * p->N1); g1.ld_out = p->N1; }
+      TPS_TRY(S.product_split(i, TPSLICE_STEP_MLP_UP, -1, g1, kFwd, epi, p->sp_up,
+                              S.slice_part(static_cast<char*>(ws) + L.up_split, L.up_split_bytes, i)));
+    }
     for (int j = 0; j < p->pc; ++j) {
       const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs g2 = args(bf(H, r0 * p->Fp), p->Fp, bf(W2, c0 * p->Fp), p->Fp, bfw(Z, r0 * p->h + c0), p->h,

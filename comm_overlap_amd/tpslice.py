@@ -52,7 +52,8 @@ class Desc(ctypes.Structure):
                 ("n_col_slices", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("n_streams", ctypes.c_int32), ("n_copy_streams", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("handoff_gbps", ctypes.c_float), ("dh_group", ctypes.c_int32)]
+                ("flags", ctypes.c_uint32), ("handoff_gbps", ctypes.c_float), ("dh_group", ctypes.c_int32),
+                ("up_group", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -62,7 +63,8 @@ class PlanInfo(ctypes.Structure):
                 ("n_row_slices", ctypes.c_int32), ("n_col_slices", ctypes.c_int32),
                 ("n_streams", ctypes.c_int32), ("n_copy_streams", ctypes.c_int32),
                 ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("k_splits", ctypes.c_int32 * 8),
-                ("predicted_forward_us", ctypes.c_double), ("dh_group_slices", ctypes.c_int32)]
+                ("predicted_forward_us", ctypes.c_double), ("dh_group_slices", ctypes.c_int32),
+                ("up_group_slices", ctypes.c_int32)]
 
     SPLIT_NAMES = ("up", "qkv", "dh", "dw1", "dw2", "dc", "dwo", "dwqkv")
 
@@ -226,6 +228,7 @@ class Config:
     tile: str = "auto"  # a key of TILES
     handoff_gbps: float = 0.0  # hand-off rate the automatic slice counts assume (0: local DMA copy)
     dh_group: int = 0  # row slices per dH product of the MLP backward (0: automatic)
+    up_group: int = 0  # row slices per up-projection of the MLP forward (0: automatic)
 
     def desc(self) -> Desc:
         return Desc(self.tokens, self.hidden, self.ffn, self.tp_size, self.n_row_slices, self.n_col_slices,
@@ -235,7 +238,8 @@ class Config:
                     (F_SERIALIZE if self.serialize else 0) | (F_COPY_BLIT if self.copy_blit else 0)
                     | (F_PIPELINE if self.pipeline else 0) | (F_CALLER_WORKER if self.caller_worker else 0)
                     | (F_HANDOFF_ROWS if self.handoff_rows else 0)
-                    | (TILES[self.tile] << F_TILE_SHIFT), float(self.handoff_gbps), int(self.dh_group))
+                    | (TILES[self.tile] << F_TILE_SHIFT), float(self.handoff_gbps), int(self.dh_group),
+                    int(self.up_group))
 
 
 class Plan:

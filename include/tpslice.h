@@ -132,6 +132,7 @@ typedef struct {
   int32_t dh_group;       /* row slices per dH product of the MLP backward (0: automatic, see
                              tpslice_plan_info_t.dh_group_slices); else a power of two dividing
                              the row slice count                                                  */
+  int32_t up_group;       /* row slices per up-projection of the MLP forward, likewise            */
 } tpslice_desc_t;
 
 /* Automatic slice counts (Design Space Exploration of DMA based Finer-Grain Compute Communication
@@ -169,9 +170,9 @@ typedef struct {
   int64_t handoff_cols;         /* h / c                                                             */
   int32_t n_row_slices, n_col_slices, n_streams, n_copy_streams;
   int32_t q_heads, kv_heads;    /* this rank's head counts                                           */
-  /* k splits (1 = none) the plan takes for, in order: the up-projection of each row slice, the QKV
-     projection over all tokens, dH of each group of row slices, then dW1, dW2, dC, dWo, dWqkv over
-     all tokens. A split product sums its k runs' fp32 partials in order before the epilogue: the
+  /* k splits (1 = none) the plan takes for, in order: the up-projection of each group of row
+     slices, the QKV projection over all tokens, dH of each group of row slices, then dW1, dW2, dC,
+     dWo, dWqkv over all tokens. A split product sums its k runs' fp32 partials in order before the epilogue: the
      same bits for every slicing of the same batch, other rounding than an unsplit product.     */
   int32_t k_splits[8];
   /* the slice-count model's predicted time (us) of one call of the forward products with this
@@ -181,6 +182,9 @@ typedef struct {
      consecutive row slices large enough to fill the GPU, each row slice's dX product and hand-off
      after it)                                                                                  */
   int32_t dh_group_slices;
+  /* row slices per up-projection of the MLP forward (likewise: only the down-projection after it is
+     handed off, each row slice's after its group's up-projection)                              */
+  int32_t up_group_slices;
 } tpslice_plan_info_t;
 
 typedef enum {

@@ -223,6 +223,32 @@ def test_dh_groups_divide_the_row_slices_and_keep_the_split(key):
         assert e.value.code == T.ERR_INVALID
 
 
+@pytest.mark.parametrize("key", LARGE)
+def test_up_groups_divide_the_row_slices_and_keep_the_split(key):
+    """The up-projection runs over groups of row slices: the group divides r, the k split (the whole
+    batch's) is the same for every slicing, a plan with two worker streams keeps one row slice per
+    up-projection, and a requested group is kept (or refused when it does not divide r)."""
+    w = synth.WORKLOADS[key]
+    base = T.plan_for(w, n_row_slices=1, n_col_slices=1).info
+    assert base.up_group_slices == 1
+    for r in (1, 2, 4, 8):
+        if w.tokens % r:
+            continue
+        i = T.plan_for(w, n_row_slices=r).info
+        assert r % i.up_group_slices == 0
+        assert i.splits()["up"] == base.splits()["up"]
+        if i.n_streams > 1:
+            assert i.up_group_slices == 1
+        assert T.plan_for(w, n_row_slices=r, n_streams=2).info.up_group_slices == 1
+    r = T.plan_for(w).info.n_row_slices
+    assert T.plan_for(w, up_group=r).info.up_group_slices == r
+    with pytest.raises(T.TpsliceError) as e:
+        T.plan_for(w, up_group=2 * r)
+    assert e.value.code == T.ERR_INVALID
+    if key == "llama3_70b_layer":  # 8 x 32 tiles of 256 x 224 per row slice; all 16384 rows: 1792 of 256 x 256
+        assert T.plan_for(w).info.up_group_slices == 8
+
+
 def test_given_slice_counts_are_kept():
     w = synth.WORKLOADS["llama3_70b_layer"]
     for gbps in (0.0, 25.0):
