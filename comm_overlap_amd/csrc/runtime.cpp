@@ -506,6 +506,16 @@ tpslice_status_t call_streams(const tpslice_plan_s* p, const tpslice_streams_t* 
         return fail(TPSLICE_ERR_INVALID, "the call's streams must differ (the caller, %d worker and %d copy "
                     "stream(s); positions %d and %d are the same stream)", need_w, need_c, a, b);
   out->have_copiers = need_c > 0;
+  // Graph capture is supported for joined plans with one worker stream. A pipelined call waits for
+  // events of earlier calls, and capturing a plan with more worker streams has crashed the HIP
+  // runtime while it ended the capture; both are refused before anything is queued.
+  if (p->S > 1 || (p->desc.flags & TPSLICE_F_PIPELINE)) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(out->caller, &st) == hipSuccess && st != hipStreamCaptureStatusNone)
+      return fail(TPSLICE_ERR_UNSUPPORTED, "the caller's stream is capturing a graph: only a plan with one worker "
+                  "stream and no pipelining can be captured (this one: %d worker streams%s)", p->S,
+                  (p->desc.flags & TPSLICE_F_PIPELINE) ? ", pipelined" : "");
+  }
   return TPSLICE_OK;
 }
 

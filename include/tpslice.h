@@ -27,6 +27,11 @@
  *     the caller's stream, fork onto the caller's worker and copy streams, and join back, so every
  *     output (the hand-off copy included) is complete when the caller's stream reaches the point
  *     after the call (TPSLICE_F_PIPELINE relaxes this for the hand-off copies only).
+ *   - The calls of a joined plan (no TPSLICE_F_PIPELINE) with one worker stream may be captured into
+ *     a HIP graph on the caller's stream: they allocate nothing, synchronize nothing and clear no
+ *     memory, and the hand-off copies become graph copy nodes; each replay gives the bits of the
+ *     same calls run eagerly. A pipelined plan, or one with more worker streams, returns
+ *     TPSLICE_ERR_UNSUPPORTED when the caller's stream is capturing, before queueing anything.
  *   - Outputs must not alias inputs or each other. Results are deterministic: the same plan and
  *     inputs give bitwise identical outputs, whatever the slice timing.
  *   - Errors are reported by status code only; argument, shape and workspace errors are detected
