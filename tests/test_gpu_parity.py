@@ -678,3 +678,34 @@ def test_benchmark_mode_full_size(key):
         G.assert_parity(o1["Z"].cpu()[rows], ref["Z"], "Z rows")
     bench_plan.close()
     joined.close()
+
+
+# Producers over groups of row slices: the up-projection and dH take the whole batch's k split,
+# so every group size gives the same bits; the grouped plan also matches the oracle.
+GROUPS = synth.custom("groups", 912, tokens=2048, hidden=512, ffn=1536, tp=2, act="swiglu", bias=True,
+                      row_slices=8, col_slices=2, backward=True)
+
+
+@pytest.mark.parametrize("group", [2, 8])
+def test_producer_groups_keep_the_bits(group):
+    w = GROUPS
+    _print_case("producer_groups", key=w.key, group=group)
+    inp = synth.make_inputs(w)
+    base = T.plan_for(w, up_group=1, dh_group=1, handoff_rows=True)
+    grouped = T.plan_for(w, up_group=group, dh_group=group, handoff_rows=True)
+    assert grouped.info.up_group_slices == group and grouped.info.dh_group_slices == group
+    assert grouped.info.splits() == base.info.splits()
+    fa, fb = G.run_mlp_fwd(base, inp), G.run_mlp_fwd(grouped, inp)
+    for k in ("Z", "U", "Zh"):
+        assert torch.equal(fa[k], fb[k]), k
+    ba, bb = G.run_mlp_bwd(base, inp, with_bias=True), G.run_mlp_bwd(grouped, inp, with_bias=True)
+    for k in ("dX", "dXh", "dW1", "dW2", "db1"):
+        assert torch.equal(ba[k], bb[k]), k
+    ref = G.oracle_mlp_fwd(inp, w.act)
+    G.assert_parity(fb["Z"], ref["Z"], "Z")
+    rb = L.mlp_bwd(f64(inp["X_mlp"]), f64(inp["W1"]), f64(inp["W2"]), f64(inp["U_saved"]), f64(inp["dY"]),
+                   w.act, with_bias=True)
+    for k in ("dX", "dW1", "dW2", "db1"):
+        G.assert_parity(bb[k], rb[k], k)
+    base.close()
+    grouped.close()
