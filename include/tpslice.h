@@ -125,11 +125,12 @@ typedef struct {
   int32_t n_kv_heads;     /* full-model key/value heads (GQA); this rank holds max(1, n_kv/tp_size)   */
   int32_t head_dim;       /* d; multiple of 8                                                          */
   int32_t act;            /* tpslice_act_t                                                              */
-  int32_t n_streams;      /* worker streams for the slices (0 = default: 1 for one row slice; for
-                             several, 2 when the per-slice forward products, each alone with its
-                             tile, leave more than 5% of their flop-weighted block rounds empty on
-                             the 256 CUs, else 1); slice i runs on stream i mod n_streams and
-                             starts once slice i-1's first product is done                       */
+  int32_t n_streams;      /* worker streams for the slices (0 = default: 1 for one row slice, for a
+                             layer shard (n_heads > 0) and when the up-projection runs over groups
+                             of row slices; otherwise 2 when the per-slice forward products, each
+                             alone with its tile, leave more than 5% of their flop-weighted block
+                             rounds empty on the 256 CUs, else 1); slice i runs on stream
+                             i mod n_streams and starts once slice i-1's first product is done     */
   int32_t n_copy_streams; /* side streams for hand-off copies (0 = default: 1)                        */
   uint32_t flags;         /* TPSLICE_F_*                                                                */
   float handoff_gbps;     /* hand-off rate in GB/s that the automatic slice counts assume (0: the
@@ -177,8 +178,9 @@ typedef struct {
   int32_t q_heads, kv_heads;    /* this rank's head counts                                           */
   /* k splits (1 = none) the plan takes for, in order: the up-projection of each group of row
      slices, the QKV projection over all tokens, dH of each group of row slices, then dW1, dW2, dC,
-     dWo, dWqkv over all tokens. A split product sums its k runs' fp32 partials in order before the epilogue: the
-     same bits for every slicing of the same batch, other rounding than an unsplit product.     */
+     dWo, dWqkv over all tokens. A split product sums its k runs' fp32 partials in order before the
+     epilogue: the same bits for every slicing of the same batch, other rounding than an unsplit
+     product.                                                                                   */
   int32_t k_splits[8];
   /* the slice-count model's predicted time (us) of one call of the forward products with this
      plan's r and c (see the automatic slice counts above); a comparison figure, not a timing */
