@@ -686,13 +686,16 @@ GROUPS = synth.custom("groups", 912, tokens=2048, hidden=512, ffn=1536, tp=2, ac
                       row_slices=8, col_slices=2, backward=True)
 
 
-@pytest.mark.parametrize("group", [2, 8])
-def test_producer_groups_keep_the_bits(group):
+@pytest.mark.parametrize("group,streams", [(2, 1), (8, 1), (2, 2)])
+def test_producer_groups_keep_the_bits(group, streams):
+    """Groups of one, two and all eight row slices, on one worker stream and on two (a group's
+    producer then runs on the first slice's worker and the other slices wait for it)."""
     w = GROUPS
-    _print_case("producer_groups", key=w.key, group=group)
+    _print_case("producer_groups", key=w.key, group=group, streams=streams)
     inp = synth.make_inputs(w)
     base = T.plan_for(w, up_group=1, dh_group=1, handoff_rows=True)
-    grouped = T.plan_for(w, up_group=group, dh_group=group, handoff_rows=True)
+    grouped = T.plan_for(w, up_group=group, dh_group=group, handoff_rows=True, n_streams=streams)
+    assert grouped.info.n_streams == streams
     assert grouped.info.up_group_slices == group and grouped.info.dh_group_slices == group
     assert grouped.info.splits() == base.info.splits()
     fa, fb = G.run_mlp_fwd(base, inp), G.run_mlp_fwd(grouped, inp)
