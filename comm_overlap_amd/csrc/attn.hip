@@ -22,11 +22,13 @@
 // Measured on the Llama shard shapes (13B: 5 query and key/value heads; 70B: 8 query heads, 1
 // key/value head) at 2048-token sequences: dealing the query blocks so that each XCD reads the K/V
 // rows of few heads (its L2) and each workgroup takes a heavy and a light block raised 236 and 382
-// TFLOP/s to 353 and 514. Not adopted: four-wave 64-row blocks (each staging its own K and V, 190
-// and 264 before the dealing), four waves of two row tiles (280 registers, one block per CU,
-// 125-207), double-buffered K/V with one barrier per key block (more registers; slower even with
-// them capped for two blocks per CU), and capping this kernel at 128 registers for two blocks per
-// CU (a few spills; 70B 3-6% faster, 13B 18% slower). 128-key blocks (half the barriers and
+// TFLOP/s to 353 and 514. Four waves of two row tiles staged through registers needed 280
+// registers (one block per CU, 125-207 TFLOP/s); with direct global -> LDS loads they fit in 252
+// and two blocks per CU: attn_fwd_kernel2 below, taken when there are enough work items. Not
+// adopted: four-wave 64-row blocks (each staging its own K and V, 190 and 264 before the dealing),
+// double-buffered K/V with one barrier per key block (more registers; slower even with them capped
+// for two blocks per CU), and capping this kernel at 128 registers for two blocks per CU (a few
+// spills; 70B 3-6% faster, 13B 18% slower). 128-key blocks (half the barriers and
 // softmax rounds of 64-key ones, twice the independent S tiles) ran 4-5% faster than 64-key ones;
 // with 242 registers one block runs per CU.
 #include <hip/hip_ext.h>
@@ -247,17 +249,197 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+
+// The same attention with four waves of 32 query rows (two 16-row tiles each) per 128-row block: each
+// K and V fragment read from LDS serves twice the rows. K and V tiles come by direct global -> LDS
+// loads (buffer_load_dwordx4 ... lds; lane l of a 1-KB run fetches the chunk the swizzle puts at
+// its LDS slot), which keeps the staging registers free: 252 registers, two blocks per CU. Taken
+// when the paired work items give at least two workgroups per CU; with fewer, most CUs would hold
+// one four-wave block, which has no second wave per SIMD to hide its waits (the 13B shard's 160
+// pairs: 82.5 us against the eight-wave kernel's 61.9), so the eight-wave kernel runs. Measured at
+// the 70B shard (512 pairs): 110.3 us against 127.5, the same bits.
+constexpr int kWaves2 = 4, kRT2 = 2;             // waves per block, row tiles per wave
+constexpr int kBQ2 = 16 * kRT2 * kWaves2;          // 128 query rows per block
+constexpr int kThreads2 = 64 * kWaves2;
+static_assert(kBQ2 == kAttnBlock, "the launcher's block size");
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(kThreads2, 2) void attn_fwd_kernel2(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char k_lds[kBK * kRowB];
+  __shared__ __attribute__((aligned(1024))) char v_lds[kBK * kRowB];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int nqb = a.seq_len / kBQ2;
+  const int total = nqb * a.q_heads * int(a.tokens / a.seq_len), li = int(blockIdx.x);
+  const bool pr = attn_paired(nqb, total);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.QKV), (short)0, (int)(uint32_t)(a.tokens * a.ld_qkv * 2), 0x00020000);
+#pragma clang loop unroll(disable)
+  for (int it = 0; it < (pr ? 2 : 1); ++it) {
+    int bh, qb;
+    if (pr) {
+      const int per_xcd = total >> 4;
+      const int u = (li & 7) * per_xcd + (li >> 3);
+      const int half = nqb >> 1;
+      bh = u / half;
+      const int pi = u - bh * half;
+      qb = it == 0 ? nqb - 1 - pi : pi;
+    } else {
+      bh = li / nqb;
+      qb = nqb - 1 - (li - bh * nqb);
+    }
+    const int b = bh / a.q_heads, h = bh - b * a.q_heads;
+    const int g = h / (a.q_heads / a.kv_heads);
+    const int64_t seq0 = int64_t(b) * a.seq_len;
+    const unsigned short* qkv = reinterpret_cast<const unsigned short*>(a.QKV);
+    const int64_t ld = a.ld_qkv;
+    const int64_t kcol = int64_t(a.q_heads + g) * kD, vcol = int64_t(a.q_heads + a.kv_heads + g) * kD;
+    const int lr = lane & 15, lg = lane >> 4;
+    int q_row[kRT2];
+    bf16x8 qf[kRT2][kD / 32];
+#pragma unroll
+    for (int r = 0; r < kRT2; ++r) {
+      q_row[r] = qb * kBQ2 + (wave * kRT2 + r) * 16 + lr;
+      const unsigned short* qp = qkv + (seq0 + q_row[r]) * ld + int64_t(h) * kD + 8 * lg;
+#pragma unroll
+      for (int kk = 0; kk < kD / 32; ++kk) qf[r][kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
+    }
+    f32x4 o[kRT2][kD / 16];
+#pragma unroll
+    for (int r = 0; r < kRT2; ++r)
+#pragma unroll
+      for (int j = 0; j < kD / 16; ++j) o[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m[kRT2], l[kRT2];
+#pragma unroll
+    for (int r = 0; r < kRT2; ++r) { m[r] = -INFINITY; l[r] = 0.f; }
+    const float sl2 = a.scale_log2;
+    // this thread's 8 runs (1 KB each) of the K tile and of the V tile: run q = wave * 8 + p covers
+    // key rows 4q .. 4q + 3; lane l writes LDS bytes 16 l of the run, which hold row 4q + l / 16,
+    // slot l % 16, i.e. logical chunk slot ^ swizzle(row)
+    // (the swizzles repeat every 16 rows, i.e. every 4 runs: runs p and p + 4 share their lane
+    // offsets, 16 rows apart through the scalar offset)
+    uint32_t koff[4], voff[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int row = (wave * 8 + p) * 4 + (lane >> 4), slot = lane & 15;
+      koff[p] = uint32_t((int64_t(row) * ld + kcol + ((slot ^ swz_k(row)) << 3)) * 2);
+      voff[p] = uint32_t((int64_t(row) * ld + vcol + ((slot ^ swz_v(row)) << 3)) * 2);
+    }
+    const uint32_t row16 = uint32_t(16 * ld * 2);
+    const int nkb = qb + 1;  // key blocks up to the diagonal (block sizes equal)
+    for (int kb = 0; kb < nkb; ++kb) {
+      __syncthreads();
+      const uint32_t soff = uint32_t((seq0 + int64_t(kb) * kBK) * ld * 2);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const uint32_t so = soff + uint32_t(p >> 2) * row16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(k_lds + (wave * 8 + p) * 1024), 16, koff[p & 3], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(v_lds + (wave * 8 + p) * 1024), 16, voff[p & 3], so, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // (vmcnt 0)
+      __syncthreads();
+      f32x4 s[kRT2][kBK / 16];
+#pragma unroll
+      for (int j = 0; j < kBK / 16; ++j) {
+#pragma unroll
+        for (int r = 0; r < kRT2; ++r) s[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int krow = 16 * j + lr;
+#pragma unroll
+        for (int kk = 0; kk < kD / 32; ++kk) {
+          const int ch = 4 * kk + lg;
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + krow * kRowB + ((ch ^ swz_k(krow)) << 4));
+#pragma unroll
+          for (int r = 0; r < kRT2; ++r) s[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[r][kk], s[r][j], 0, 0, 0);
+        }
+      }
+      const bool diag = kb == nkb - 1;
+      bf16x8 pf[kRT2][kBK / 32];
+#pragma unroll
+      for (int r = 0; r < kRT2; ++r) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kBK / 16; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float x = s[r][j][v] * sl2;
+            if (diag && kb * kBK + 16 * j + 4 * lg + v > q_row[r]) x = -INFINITY;
+            s[r][j][v] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = row_max4(mx);
+        const float m_new = fmaxf(m[r], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[r] - m_new);
+        float rsum = 0.f;
+#pragma unroll
+        for (int c = 0; c < kBK / 32; ++c)
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float pv = __builtin_amdgcn_exp2f(s[r][2 * c + half][v] - m_new);
+              rsum += pv;
+              pf[r][c][4 * half + v] = (__bf16)pv;
+            }
+        l[r] = l[r] * alpha + rsum;
+        m[r] = m_new;
+#pragma unroll
+        for (int j = 0; j < kD / 16; ++j) o[r][j] *= alpha;
+      }
+      const int vq = lane & 3, vv4 = (lane & 15) >> 2;
+#pragma unroll
+      for (int c = 0; c < kBK / 32; ++c) {
+        const int k0 = 32 * c + 4 * lg + vv4, k1 = k0 + 16;
+#pragma unroll
+        for (int jd = 0; jd < kD / 16; ++jd) {
+          const int ch = 2 * jd + (vq >> 1);
+          const int bin = (vq & 1) << 3;
+          const char* p0 = v_lds + k0 * kRowB + ((ch ^ swz_v(k0)) << 4) + bin;
+          const char* p1 = v_lds + k1 * kRowB + ((ch ^ swz_v(k1)) << 4) + bin;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+          const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+          for (int r = 0; r < kRT2; ++r) o[r][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[r][c], o[r][jd], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRT2; ++r) {
+      const float lsum = row_sum4(l[r]);
+      const float inv = 1.0f / lsum;
+      if (a.lse && lg == 0) a.lse[(seq0 + q_row[r]) * a.q_heads + h] = (m[r] + __log2f(lsum)) * 0.69314718055994531f;
+      unsigned short* C = reinterpret_cast<unsigned short*>(a.C) + (seq0 + q_row[r]) * a.ld_c + int64_t(h) * kD + 4 * lg;
+#pragma unroll
+      for (int jd = 0; jd < kD / 16; ++jd) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 rr = {(__bf16)(o[r][jd][0] * inv), (__bf16)(o[r][jd][1] * inv), (__bf16)(o[r][jd][2] * inv),
+                           (__bf16)(o[r][jd][3] * inv)};
+        *reinterpret_cast<i32x2*>(C + 16 * jd) = __builtin_bit_cast(i32x2, rr);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (a.tokens <= 0) return hipSuccess;
   const int nqb = a.seq_len / kBQ;
   const int total = nqb * a.q_heads * int(a.tokens / a.seq_len);
-  const dim3 grid(unsigned(attn_paired(nqb, total) ? total / 2 : total));
-  if (start || stop)
+  const bool paired = attn_paired(nqb, total);
+  const dim3 grid(unsigned(paired ? total / 2 : total));
+  const bool four_waves = paired && total / 2 >= 2 * 256;
+  if (four_waves) {
+    if (start || stop)
+      hipExtLaunchKernelGGL(attn_fwd_kernel2, grid, dim3(kThreads2), 0, stream, start, stop, 0, a);
+    else
+      hipLaunchKernelGGL(attn_fwd_kernel2, grid, dim3(kThreads2), 0, stream, a);
+  } else if (start || stop) {
     hipExtLaunchKernelGGL(attn_fwd_kernel, grid, dim3(kThreads), 0, stream, start, stop, 0, a);
-  else
+  } else {
     hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
