@@ -36,6 +36,10 @@ import time
 
 METRIC = "TFLOP/s and % of bf16 MFMA peak per TP-shard layer; % copy time hidden"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+# The rate register-only MFMA chains reach on this GPU, with no memory traffic (2.44 PFLOP/s at
+# 2.39 GHz; comm_overlap_amd/probes/mfma_rate.hip, summary in profiles/mfma_rate.txt): the ceiling
+# a kernel of this library can approach, reported beside the published peak.
+MFMA_CEILING_TFLOPS = 2440.0
 DEFAULT_WORKLOAD = "llama3_70b_layer"
 
 
@@ -75,6 +79,8 @@ def parse():
     ap.add_argument("--attn-seq", type=int, default=2048,
                     help="sequence length for the attention-core leg of layer workloads")
     ap.add_argument("--no-attn-core", action="store_true", help="skip the attention-core leg")
+    ap.add_argument("--no-blas-context", action="store_true",
+                    help="skip timing each product's shape with torch.matmul (vendor BLAS) for context")
     ap.add_argument("--calib-copy", action="store_true",
                     help="finish with plain 256 MiB device copies (counter calibration for profiles)")
     return ap.parse_args()
@@ -259,6 +265,59 @@ def core_flops(w, seq_len):
     pairs = seq_len * (seq_len + 1) / 2.0
     per = pairs * 2.0 * 128 * w.q_heads_shard * (w.tokens // seq_len)
     return 2.0 * per, 4.0 * per
+
+
+def product_shapes(w, info):
+    """(M, N, K, operand orientation) of each product of a step as one plain matmul: "nt" A @ B^T,
+    "nn" A @ B, "tn" A^T @ B (the weight gradients, over all tokens)."""
+    M, h, Fp, N1 = info.tokens, info.hidden, info.ffn_shard, info.n1
+    Ms = info.rows_per_slice
+    out = {"mlp_up": (Ms * info.up_group_slices, N1, h, "nt"), "mlp_down": (Ms, h, Fp, "nt")}
+    if w.backward:
+        out.update(mlp_dh=(Ms * info.dh_group_slices, Fp, h, "nn"), mlp_dx=(Ms, h, N1, "nn"),
+                   mlp_dw1=(N1, h, M, "tn"), mlp_dw2=(h, Fp, M, "tn"))
+    if w.has_attn:
+        q, c = info.qkv_width, info.ctx_width
+        out.update(qkv=(M, q, h, "nt"), out=(Ms, h, c, "nt"))
+        if w.backward:
+            out.update(attn_dx=(Ms, h, q, "nn"), attn_dc=(M, c, h, "nn"), attn_dwo=(h, c, M, "tn"),
+                       attn_dwqkv=(q, h, M, "tn"))
+    return out
+
+
+def blas_context(w, info, kernels):
+    """Context, not a target: each product's shape as one torch.matmul in bf16 (the vendor BLAS that
+    torch's preferred BLAS library names; bf16 output, where this library's weight gradients write
+    fp32), median of 10 timed calls, beside this library's per-launch rate of the same product in
+    the traced steps."""
+    import torch
+    res = {"blas_library": str(torch.backends.cuda.preferred_blas_library()).split(".")[-1]}
+    for name, (M, N, K, form) in product_shapes(w, info).items():
+        if name not in kernels:
+            continue
+        a = torch.randn(K, M, device="cuda").to(torch.bfloat16) if form == "tn" else \
+            torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        b = torch.randn(N, K, device="cuda").to(torch.bfloat16) if form == "nt" else \
+            torch.randn(K, N, device="cuda").to(torch.bfloat16)
+        fn = {"nt": lambda: torch.matmul(a, b.t()), "nn": lambda: torch.matmul(a, b),
+              "tn": lambda: torch.matmul(a.t(), b)}[form]
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        res[name] = {"shape": [M, N, K], "torch_matmul_tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                     "tpslice_tflops": kernels[name]["tflops"]}
+        del a, b
+    torch.cuda.synchronize()
+    return res
 
 
 def attn_core(w, inp, seq_len, steps):
@@ -555,6 +614,7 @@ def main():
                        "dma, whole row slices" if not args.handoff_pieces and info.n_col_slices > 1
                        else "dma"), "chain": "pipelined"},
         "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "pct_of_mfma_ceiling": round(100.0 * tflops / MFMA_CEILING_TFLOPS, 2),
         "hidden_copy_pct": pct(hidden_trace),
         "hidden_copy_pct_single_call": pct(hidden_trace_single),
         "hidden_copy_wall_pct": pct(hidden_wall),
@@ -578,6 +638,9 @@ def main():
     if w.has_attn and not args.no_attn_core:
         log("attention core")
         out["attn_core"] = attn_core(w, inp, args.attn_seq, K)
+    if not args.no_blas_context:
+        log("vendor BLAS context")
+        out["blas_context"] = blas_context(w, info, out["kernels"])
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
