@@ -203,8 +203,13 @@ static double predict_forward_us(const tpslice_desc_t* d, int64_t Fp, int64_t N1
   const double slice_us = sliced_us / r;
   // one row slice's copies: c pieces, or one whole-row copy (the same bytes, one fixed cost)
   const double copy_us = double(Ms) * double(h) * 2.0 * tensors / (gbps * 1e3) + pc * kCopyFixedUs * tensors;
-  if (d->flags & TPSLICE_F_PIPELINE)
-    return std::max(sliced_us + tail_us, r * (copy_us + (S > 1 ? kSliceSyncUs2 : kSliceSyncUs1)));
+  // Pipelined: the next call's row slice 0 waits for this call's copy of row slice 0, which the rest
+  // of this call (its later slices and the all-token products) covers only in part; with one row
+  // slice nothing covers it.
+  if (d->flags & TPSLICE_F_PIPELINE) {
+    const double exposed = std::max(0.0, copy_us - (sliced_us - slice_us + tail_us));
+    return std::max(sliced_us + tail_us, r * (copy_us + (S > 1 ? kSliceSyncUs2 : kSliceSyncUs1))) + exposed;
+  }
   return std::max({sliced_us + tail_us, sliced_us + copy_us, slice_us + r * copy_us});
 }
 

@@ -147,8 +147,10 @@ typedef struct {
  * {1, 2, 4, 8, 16} dividing tokens and c in {1, 2, 4} keeping h/c a multiple of 8, for the smallest
  * predicted time of one call of the forward products: the per-slice products' estimated times
  * (tile, split and launch costs of this GPU) plus the hand-off's exposed time at `handoff_gbps`
- * (with TPSLICE_F_PIPELINE: the larger of compute and copies per call; without: the copies of the
- * last row slice, or of all slices when copying is the slower side). Within 2%, fewer pieces win.
+ * (with TPSLICE_F_PIPELINE: the larger of compute and copies per call, plus the part of the first
+ * row slice's copy that the rest of the call does not cover, since the next call's first row slice
+ * waits for it; without: the copies of the last row slice, or of all slices when copying is the
+ * slower side). Within 2%, fewer pieces win.
  * tpslice_plan_info reports the counts taken.                                                    */
 
 typedef struct tpslice_plan_s* tpslice_plan_t;

@@ -279,11 +279,22 @@ def test_slower_handoff_never_takes_fewer_row_slices_for_isolated_calls(key, str
 
 
 @pytest.mark.parametrize("key", LARGE)
-def test_pipelined_chain_on_one_gpu_is_fastest_unsliced(key):
-    """With the local DMA hand-off, a pipelined chain hides the copies of one call behind the next:
-    the model, like the measured sweep, prefers the unsliced products."""
-    p = T.plan_for(synth.WORKLOADS[key], n_row_slices=0, n_col_slices=0, pipeline=True)
-    assert p.info.n_row_slices == 1
+def test_pipelined_chain_slices_to_hide_its_copy(key):
+    """In a pipelined chain the next call's row slice 0 waits for this call's copy of row slice 0,
+    so one row slice leaves its whole copy exposed: with the local DMA hand-off the model slices
+    (the measured sweep: GPT-3 2.7B 1109-1124 TFLOP/s at r = 2 against 1059-1067 unsliced), and
+    with a hand-off that costs nothing it keeps the products whole."""
+    w = synth.WORKLOADS[key]
+    p = T.plan_for(w, n_row_slices=0, n_col_slices=0, pipeline=True, handoff_rows=True)
+    assert p.info.n_row_slices >= 2
+    free = T.plan_for(w, n_row_slices=0, n_col_slices=0, pipeline=True, handoff_rows=True, handoff_gbps=1e6)
+    assert free.info.n_row_slices <= p.info.n_row_slices
+    if free.info.n_streams == 1:  # (two worker streams may slice for the products' own overlap)
+        assert free.info.n_row_slices * free.info.n_col_slices == 1
+    one = T.plan_for(w, n_row_slices=1, n_col_slices=1, pipeline=True, handoff_rows=True).info.predicted_forward_us
+    one_free = T.plan_for(w, n_row_slices=1, n_col_slices=1, pipeline=True, handoff_rows=True,
+                          handoff_gbps=1e6).info.predicted_forward_us
+    assert one > one_free  # the exposed copy
 
 
 def test_caller_worker_flag():
