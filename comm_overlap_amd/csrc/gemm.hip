@@ -1358,15 +1358,53 @@ int choose_split(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
+SplitChoice choose_split_tail(int64_t M, int64_t N, int64_t K) {
+  // Costs in units of one 64-wide k block of a 256 x 256 tile (about 1.9 us), as choose_split.
+  const int whole = choose_split(M, N, K);
+  const int64_t Tm = (M + 255) / 256, Tn = (N + 255) / 256, nk = (K + kBK - 1) / kBK;
+  if (Tm < 2 || Tn <= 0 || nk <= 0) return SplitChoice{whole, 0};
+  const double kBlockUs = 1.9, kLaunchUs = 6.0;
+  auto rounds = [](int64_t items) { return double((items + kCUs - 1) / kCUs); };
+  auto red = [&](int64_t rows, int sp) { return double(2 * sp + 2) * double(rows) * double(N) * 4.0 / 5e12 * 1e6 / kBlockUs; };
+  double best = whole > 1 ? rounds(Tm * Tn * whole) * double((nk + whole - 1) / whole) + red(M, whole)
+                          : rounds(Tm * Tn) * double(nk);
+  SplitChoice choice{whole, 0};
+  for (int64_t t = 1; t < Tm; ++t) {
+    const int64_t head_rows = (Tm - t) * 256, tail_rows = M - head_rows;
+    const double head = rounds((Tm - t) * Tn) * double(nk);
+    for (int sp = 2; sp <= 8; ++sp) {
+      const int64_t kbs = (nk + sp - 1) / sp;
+      if (kbs < 8) break;  // at least 512 of k per split
+      const double cost = head + rounds(t * Tn * sp) * double(kbs) + red(tail_rows, sp) + kLaunchUs / kBlockUs;
+      if (cost < best * 0.95) { best = cost; choice = SplitChoice{sp, tail_rows}; }
+    }
+  }
+  return choice;
+}
+
 size_t split_partials_bytes(int64_t M, int64_t N, int splits) {
   return splits > 1 ? size_t(splits) * size_t(M) * size_t(N) * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float* partials, hipStream_t stream,
-                             hipEvent_t start, hipEvent_t stop, int tile, hipEvent_t gemm_stop) {
+                             hipEvent_t start, hipEvent_t stop, int tile, hipEvent_t gemm_stop, int64_t tail_rows) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const bool dual = epi == kEpiSwiglu;
   if (splits < 2 || splits > 64 || !partials || (dual && layout != kFwd)) return hipErrorInvalidValue;
+  GemmArgs head{};
+  if (tail_rows > 0 && tail_rows < g.M) {
+    // the unsplit rows [0, M - tail_rows) and the split tail: g moves to the tail's first row
+    const int64_t h = int64_t(g.M) - tail_rows;
+    if (dual || h % 256 != 0) return hipErrorInvalidValue;
+    head = g;
+    head.M = int32_t(h);
+    const size_t c_elem = epi == kEpiF32 ? sizeof(float) : 2;
+    g.A = static_cast<const char*>(g.A) + (layout == kWgrad ? h : h * g.lda) * 2;
+    g.C = static_cast<char*>(g.C) + h * g.ldc * int64_t(c_elem);
+    if (g.aux_in) g.aux_in = static_cast<const char*>(g.aux_in) + h * g.ld_in * 2;
+    if (g.aux_out) g.aux_out = static_cast<char*>(g.aux_out) + h * g.ld_out * 2;
+    g.M = int32_t(tail_rows);
+  }
   // operand extents for the buffer range checks (as launch_gemm)
   GemmArgs p = g;
   if (layout == kWgrad) p.a_bytes = extent_bytes(p.K, p.lda, p.M);
@@ -1386,8 +1424,13 @@ hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float*
   p.accumulate = 0;
   p.bias = nullptr; p.aux_in = nullptr; p.aux_out = nullptr;
   const bool pipe = tile == kTileAuto || tile == kTile256x256w4;
-  hipError_t e = launch_partial(p, layout, dual, pipe, stream, start, gemm_stop);
+  hipError_t e = launch_partial(p, layout, dual, pipe, stream, start, head.M > 0 ? nullptr : gemm_stop);
   if (e != hipSuccess) return e;
+  if (head.M > 0) {
+    // after the tail's partials, so that the last GEMM launch is the bulk of the product
+    e = launch_gemm(head, layout, epi, stream, nullptr, gemm_stop, tile, true);
+    if (e != hipSuccess) return e;
+  }
   switch (epi) {
     case kEpiBf16: return launch_split_epilogue<kEpiBf16>(g, partials, splits, p.part_stride, ldp, stream, stop);
     case kEpiGelu: return launch_split_epilogue<kEpiGelu>(g, partials, splits, p.part_stride, ldp, stream, stop);

@@ -103,6 +103,20 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipE
 // the sums differ in rounding from an unsplit product.
 // choose_split: split count for an M x N x K product (N: output columns; SwiGLU: both halves).
 int choose_split(int64_t M, int64_t N, int64_t K);
+// A split of only the last rows of a product ("tail split"): the first M - tail_rows rows (a
+// multiple of 256) run unsplit in whole rounds of 256 x 256 tiles, and the tiles of the remaining
+// rows, which would leave the last round partly empty, run split along k into a full round. Each
+// output element still gets one fixed summation order (its rows' part decides which), so every run
+// of the same product shape gets the same bits. tail_rows == 0: the split (if any) covers the whole
+// product, as choose_split decides.
+struct SplitChoice {
+  int splits;         // 1: no split
+  int64_t tail_rows;  // rows the split covers (the last ones); 0: all of them
+};
+// For an M x N x K weight-gradient product (both operands read across k; 256 x 256 tiles): the
+// whole-product split of choose_split, or a tail split when the same cost model (rounds of 256
+// CUs x k blocks per run, the reduction's HBM passes, a launch) puts it at least 5% below.
+SplitChoice choose_split_tail(int64_t M, int64_t N, int64_t K);
 // Split count of a per-slice product. It must not depend on the slice height, or slicing would
 // change a product's rounding; it is chosen for 2048-row slices (the workloads' slice height).
 constexpr int64_t kSplitRefRows = 2048;
@@ -121,9 +135,13 @@ size_t split_partials_bytes(int64_t M, int64_t N, int splits);
 // `gemm_stop`/`stop` the reduction. The partial products
 // run 256 x 256 tiles: the four-wave pipelined ones when K is a multiple of 64 and `tile` is
 // kTileAuto or kTile256x256w4, else the eight-wave ones (the same bits).
+// tail_rows in (0, M) with M - tail_rows a multiple of 256: a tail split (choose_split_tail). The
+// partial products of the last tail_rows rows run first, then the unsplit product of the other
+// rows (launch_gemm with `tile`), then the reduction of the tail rows; `partials` holds the tail's
+// partials only, and `gemm_stop` marks the end of the unsplit part. Not for SwiGLU products.
 hipError_t launch_gemm_split(GemmArgs g, int layout, int epi, int splits, float* partials, hipStream_t stream,
                              hipEvent_t start = nullptr, hipEvent_t stop = nullptr, int tile = kTileAuto,
-                             hipEvent_t gemm_stop = nullptr);
+                             hipEvent_t gemm_stop = nullptr, int64_t tail_rows = 0);
 
 // A one-wave kernel that does nothing. Queued on a stream after DMA-engine copies it completes only
 // after them (stream order), so an event recorded after it marks the copies' completion.

@@ -56,8 +56,8 @@ MlpBwdWs mlp_bwd_ws(const tpslice_plan_s* p) {
   w.H = align_up(size_t(p->M) * size_t(p->N1) * 2, kWsAlign);
   w.partials = w.H + align_up(size_t(p->M) * size_t(p->Fp) * 2, kWsAlign);
   w.dw1_split = w.partials + align_up(partials_bytes(p->M, p->N1), kWsAlign);
-  w.dw2_split = w.dw1_split + align_up(split_partials_bytes(p->N1, p->h, p->sp_dw1), kWsAlign);
-  w.dh_split = w.dw2_split + align_up(split_partials_bytes(p->h, p->Fp, p->sp_dw2), kWsAlign);
+  w.dw2_split = w.dw1_split + align_up(split_partials_bytes(p->tl_dw1 ? p->tl_dw1 : p->N1, p->h, p->sp_dw1), kWsAlign);
+  w.dh_split = w.dw2_split + align_up(split_partials_bytes(p->tl_dw2 ? p->tl_dw2 : p->h, p->Fp, p->sp_dw2), kWsAlign);
   w.dh_split_bytes = align_up(split_partials_bytes(p->Ms * p->gdh, p->Fp, p->sp_dh), kWsAlign);
   w.total = w.dh_split + w.dh_split_bytes * size_t(worker_regions(p));
   return w;
@@ -68,8 +68,9 @@ AttnBwdWs attn_bwd_ws(const tpslice_plan_s* p) {
   w.partials = 0;
   w.dc_split = align_up(partials_bytes(p->M, p->qkv), kWsAlign);
   w.dwo_split = w.dc_split + align_up(split_partials_bytes(p->M, p->ctx, p->sp_dc), kWsAlign);
-  w.dwqkv_split = w.dwo_split + align_up(split_partials_bytes(p->h, p->ctx, p->sp_dwo), kWsAlign);
-  w.total = w.dwqkv_split + align_up(split_partials_bytes(p->qkv, p->h, p->sp_dwqkv), kWsAlign);
+  w.dwqkv_split = w.dwo_split + align_up(split_partials_bytes(p->tl_dwo ? p->tl_dwo : p->h, p->ctx, p->sp_dwo), kWsAlign);
+  w.total = w.dwqkv_split +
+            align_up(split_partials_bytes(p->tl_dwqkv ? p->tl_dwqkv : p->qkv, p->h, p->sp_dwqkv), kWsAlign);
   return w;
 }
 
@@ -360,12 +361,16 @@ extern "C" tpslice_status_t tpslice_plan(const tpslice_desc_t* d, tpslice_plan_t
   p->qh = qh; p->kvh = kvh;
   p->trace = 0;
   p->rt = nullptr;
-  // k splits of the products over all tokens (each a function of that product's shape only)
-  p->sp_dw1 = choose_split(N1, h, M);
-  p->sp_dw2 = choose_split(h, Fp, M);
+  // k splits of the products over all tokens (each a function of that product's shape only); the
+  // weight gradients may split only their last rows
+  const SplitChoice s_dw1 = choose_split_tail(N1, h, M), s_dw2 = choose_split_tail(h, Fp, M);
+  const SplitChoice s_dwo = qh ? choose_split_tail(h, ctx, M) : SplitChoice{1, 0};
+  const SplitChoice s_dwqkv = qh ? choose_split_tail(qkv, h, M) : SplitChoice{1, 0};
+  p->sp_dw1 = s_dw1.splits; p->tl_dw1 = s_dw1.tail_rows;
+  p->sp_dw2 = s_dw2.splits; p->tl_dw2 = s_dw2.tail_rows;
   p->sp_dc = qh ? choose_split(M, ctx, h) : 1;
-  p->sp_dwo = qh ? choose_split(h, ctx, M) : 1;
-  p->sp_dwqkv = qh ? choose_split(qkv, h, M) : 1;
+  p->sp_dwo = s_dwo.splits; p->tl_dwo = s_dwo.tail_rows;
+  p->sp_dwqkv = s_dwqkv.splits; p->tl_dwqkv = s_dwqkv.tail_rows;
   // QKV over all tokens runs alone (after the slices), where the forward-only tiles that fill the
   // last round compete with a split of 256 x 256 tiles: the split only when the model prefers it
   if (qh) {
@@ -403,6 +408,11 @@ extern "C" tpslice_status_t tpslice_plan_info(tpslice_plan_t p, tpslice_plan_inf
   info->q_heads = p->qh; info->kv_heads = p->kvh;
   const int32_t sp[8] = {p->sp_up, p->sp_qkv, p->sp_dh, p->sp_dw1, p->sp_dw2, p->sp_dc, p->sp_dwo, p->sp_dwqkv};
   for (int k = 0; k < 8; ++k) info->k_splits[k] = sp[k];
+  // rows each split covers: a tail split's last rows, else the product's rows
+  const int64_t rows[8] = {int64_t(p->Ms) * p->gup, p->M, int64_t(p->Ms) * p->gdh,
+                           p->tl_dw1 ? p->tl_dw1 : p->N1, p->tl_dw2 ? p->tl_dw2 : p->h, p->M,
+                           p->tl_dwo ? p->tl_dwo : p->h, p->tl_dwqkv ? p->tl_dwqkv : p->qkv};
+  for (int k = 0; k < 8; ++k) info->k_split_rows[k] = sp[k] > 1 ? int32_t(rows[k]) : 0;
   const double gbps = p->desc.handoff_gbps > 0.0f ? double(p->desc.handoff_gbps) : kLocalHandoffGbps;
   info->dh_group_slices = p->gdh;
   info->up_group_slices = p->gup;

@@ -22,6 +22,9 @@ struct tpslice_plan_s {
   // k splits (1: none) of the products over all tokens (dW1, dW2, dC, dWo, dWqkv, QKV), of the
   // row slices' up-projection and of the dH groups
   int32_t sp_dw1, sp_dw2, sp_dc, sp_dwo, sp_dwqkv, sp_up, sp_qkv, sp_dh;
+  // rows of each weight gradient that its k split covers: its last rows (a tail split, the others
+  // unsplit), or 0 for the whole product
+  int64_t tl_dw1, tl_dw2, tl_dwo, tl_dwqkv;
   // row slices per dH product: dH runs over groups of gdh consecutive row slices (it is not handed
   // off; each row slice's dX product and hand-off follow it)
   int32_t gdh;

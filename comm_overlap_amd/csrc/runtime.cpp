@@ -404,10 +404,12 @@ struct Schedule {
 
   // A product split along k when `splits` > 1: fp32 partials in `part`, then the ordered
   // reduction with the product's epilogue. i >= 0: row slice i's product (on worker(i));
-  // i < 0: a product over all tokens on worker(on). Traced as two records: the GEMM of the
-  // partial products (with the product's flops) and the reduction.
+  // i < 0: a product over all tokens on worker(on). tail_rows > 0: only the product's last
+  // tail_rows rows are split, the others run unsplit between the partials and the reduction.
+  // Traced as two records: the GEMM of the partial products and of the unsplit rows (with the
+  // product's flops) and the reduction.
   tpslice_status_t product_split(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int splits,
-                                 float* part, int on = 0, bool alone = false) {
+                                 float* part, int on = 0, bool alone = false, int64_t tail_rows = 0) {
     if (splits <= 1) return product(i, step, piece, g, layout, epi, on, alone);
     const int wi = i < 0 ? on : i;
     const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
@@ -428,7 +430,7 @@ struct Schedule {
       em = rt->tpool[t.ev1];
       e1 = rt->tpool[u.ev1];
     }
-    hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1, p->tile, em);
+    hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1, p->tile, em, tail_rows);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "split GEMM launch: %s", hipGetErrorString(e));
     if (i >= 0 && i == lead_slice) {
       TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
@@ -735,11 +737,11 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
   GemmArgs g1 = args(dU, p->N1, X, p->h, dW1, p->h, p->N1, p->h, p->M);
   g1.accumulate = accumulate;
   TPS_TRY(S.product_split(-1, TPSLICE_STEP_MLP_DW1, -1, g1, kWgrad, kEpiF32, p->sp_dw1,
-                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw1_split), 0));
+                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw1_split), 0, false, p->tl_dw1));
   GemmArgs g2 = args(dY, p->h, H, p->Fp, dW2, p->Fp, p->h, p->Fp, p->M);
   g2.accumulate = accumulate;
   TPS_TRY(S.product_split(-1, TPSLICE_STEP_MLP_DW2, -1, g2, kWgrad, kEpiF32, p->sp_dw2,
-                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw2_split), 0));
+                          reinterpret_cast<float*>(static_cast<char*>(ws) + L.dw2_split), 0, false, p->tl_dw2));
   if (db1) TPS_TRY(S.colsum(dU, p->N1, p->M, p->N1, partials, db1, accumulate, 0));
   return S.join();
 }
@@ -852,13 +854,14 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
     GemmArgs go = args(dY, p->h, C, p->ctx, dWo, p->ctx, p->h, p->ctx, p->M);
     go.accumulate = accumulate;
     TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DWO, -1, go, kWgrad, kEpiF32, p->sp_dwo,
-                            reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwo_split), 0));
+                            reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwo_split), 0, false, p->tl_dwo));
   }
   if (do_qkv) {
     GemmArgs gq = args(dQKV, p->qkv, X, p->h, dWqkv, p->h, p->qkv, p->h, p->M);
     gq.accumulate = accumulate;
     TPS_TRY(S.product_split(-1, TPSLICE_STEP_ATTN_DWQKV, -1, gq, kWgrad, kEpiF32, p->sp_dwqkv,
-                            reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwqkv_split), 0));
+                            reinterpret_cast<float*>(static_cast<char*>(ws) + L.dwqkv_split), 0, false,
+                            p->tl_dwqkv));
     if (dbqkv) TPS_TRY(S.colsum(dQKV, p->qkv, p->M, p->qkv, partials, dbqkv, accumulate, 0));
   }
   return S.join();

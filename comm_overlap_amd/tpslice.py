@@ -64,12 +64,15 @@ class PlanInfo(ctypes.Structure):
                 ("n_streams", ctypes.c_int32), ("n_copy_streams", ctypes.c_int32),
                 ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("k_splits", ctypes.c_int32 * 8),
                 ("predicted_forward_us", ctypes.c_double), ("dh_group_slices", ctypes.c_int32),
-                ("up_group_slices", ctypes.c_int32)]
+                ("up_group_slices", ctypes.c_int32), ("k_split_rows", ctypes.c_int32 * 8)]
 
     SPLIT_NAMES = ("up", "qkv", "dh", "dw1", "dw2", "dc", "dwo", "dwqkv")
 
     def splits(self):
         return dict(zip(self.SPLIT_NAMES, list(self.k_splits)))
+
+    def split_rows(self):
+        return dict(zip(self.SPLIT_NAMES, list(self.k_split_rows)))
 
 
 class TraceRec(ctypes.Structure):

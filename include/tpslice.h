@@ -182,7 +182,7 @@ typedef struct {
      slices, the QKV projection over all tokens, dH of each group of row slices, then dW1, dW2, dC,
      dWo, dWqkv over all tokens. A split product sums its k runs' fp32 partials in order before the
      epilogue: the same bits for every slicing of the same batch, other rounding than an unsplit
-     product.                                                                                   */
+     product. k_split_rows says which rows a split covers.                                       */
   int32_t k_splits[8];
   /* the slice-count model's predicted time (us) of one call of the forward products with this
      plan's r and c (see the automatic slice counts above); a comparison figure, not a timing */
@@ -194,6 +194,12 @@ typedef struct {
   /* row slices per up-projection of the MLP forward (likewise: only the down-projection after it is
      handed off, each row slice's after its group's up-projection)                              */
   int32_t up_group_slices;
+  /* rows of each product in k_splits (same order) that its split covers: 0 when it is not split,
+     the product's rows when the whole product is split, fewer for a weight gradient whose last
+     rows alone are split (a "tail split": its other rows, a whole number of rounds of 256 x 256
+     tiles on the 256 CUs, run unsplit, and the tail's split fills the last round instead of
+     leaving it part empty; each output element still has one fixed summation order)           */
+  int32_t k_split_rows[8];
 } tpslice_plan_info_t;
 
 typedef enum {

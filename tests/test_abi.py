@@ -249,6 +249,36 @@ def test_up_groups_divide_the_row_slices_and_keep_the_split(key):
         assert T.plan_for(w).info.up_group_slices == 8
 
 
+@pytest.mark.parametrize("key", sorted(synth.WORKLOADS))
+def test_tail_splits_cover_the_last_rows_of_weight_gradients(key):
+    """A split covers the whole product, or only a weight gradient's last rows (a tail split: the
+    other rows, a multiple of 256, run unsplit). The choice depends on the product's shape only, so
+    every slicing gets the same one; the tail's partial buffers are all the workspace holds for it."""
+    w = synth.WORKLOADS[key]
+    i = T.plan_for(w).info
+    product_rows = {"dw1": i.n1, "dw2": i.hidden, "dwo": i.hidden, "dwqkv": i.qkv_width, "qkv": i.tokens,
+                    "dc": i.tokens}
+    sp, rows = i.splits(), i.split_rows()
+    for k in T.PlanInfo.SPLIT_NAMES:
+        assert (rows[k] == 0) == (sp[k] == 1), (k, sp[k], rows[k])
+        if sp[k] > 1 and k in product_rows and rows[k] != product_rows[k]:
+            assert k in ("dw1", "dw2", "dwo", "dwqkv"), k
+            assert 0 < rows[k] < product_rows[k] and (product_rows[k] - rows[k]) % 256 == 0, (k, rows[k])
+    for r in (1, 2, 4, 8):
+        if w.tokens % r:
+            continue
+        j = T.plan_for(w, n_row_slices=r).info
+        for k in ("dw1", "dw2", "dwo", "dwqkv"):
+            assert (j.splits()[k], j.split_rows()[k]) == (sp[k], rows[k]), (r, k)
+    expect = {"llama3_70b_layer": (2, 1024), "llama2_13b_layer": (4, 384)}
+    if key in expect:
+        # 70B dW1: 28 x 32 tiles = 3.5 rounds -> 24 tile rows unsplit, the last 4 split in two;
+        # 13B dW1: 14 x 20 tiles -> 12 tile rows unsplit (one round), the last 384 rows split in four
+        assert (sp["dw1"], rows["dw1"]) == expect[key]
+        whole = sp["dw1"] * i.n1 * i.hidden * 4  # what a split of the whole product would need
+        assert T.plan_for(w).workspace_size(T.OP_MLP_BWD) < whole
+
+
 def test_given_slice_counts_are_kept():
     w = synth.WORKLOADS["llama3_70b_layer"]
     for gbps in (0.0, 25.0):

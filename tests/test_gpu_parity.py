@@ -344,6 +344,42 @@ def test_split_k_backward():
             assert torch.equal(a2[k], aout[k]), (kw, k)
 
 
+# Weight gradients whose 256 x 256 tiles make one whole round of the 256 CUs plus a short tail
+# (dW1: 17 tile rows of 16 tiles): only the tail rows are split along k, into one full round; the
+# other rows run unsplit. Each element keeps one summation order, whatever the slicing or tile.
+TAIL_SPLIT = [synth.custom("tail_split_swiglu", 913, tokens=2048, hidden=4096, ffn=2176, tp=1, act="swiglu",
+                           bias=True, row_slices=2, col_slices=1, backward=True),
+              synth.custom("tail_split_gelu", 914, tokens=2048, hidden=4096, ffn=4352, tp=1, act="gelu",
+                           bias=True, row_slices=2, col_slices=2, backward=True)]
+
+
+@pytest.mark.parametrize("w", TAIL_SPLIT, ids=lambda w: w.key)
+def test_tail_split_weight_gradients(w):
+    _print_case("tail_split", key=w.key)
+    inp = synth.make_inputs(w)
+    plan = T.plan_for(w)
+    info = plan.info
+    tail = info.split_rows()["dw1"]
+    assert info.splits()["dw1"] > 1 and 0 < tail < info.n1 and (info.n1 - tail) % 256 == 0, info.split_rows()
+    out = G.run_mlp_bwd(plan, inp, with_bias=True)
+    ref = L.mlp_bwd(f64(inp["X_mlp"]), f64(inp["W1"]), f64(inp["W2"]), f64(inp["U_saved"]), f64(inp["dY"]),
+                    w.act, with_bias=True)
+    for k in ("dX", "dW1", "dW2", "db1"):
+        G.assert_parity(out[k], ref[k], k)
+    # both parts of dW1 on their own (the unsplit rows, the split tail)
+    head = info.n1 - tail
+    G.assert_parity(out["dW1"][:head], ref["dW1"][:head], "dW1 unsplit rows")
+    G.assert_parity(out["dW1"][head:], ref["dW1"][head:], "dW1 tail rows")
+    init = (torch.randn_like(out["dW1"]), torch.randn_like(out["dW2"]), torch.randn_like(out["db1"]))
+    acc = G.run_mlp_bwd(plan, inp, with_bias=True, accumulate=True, init=init)
+    G.assert_parity(acc["dW1"], f64(init[0].cpu()) + ref["dW1"], "dW1 accumulated")
+    G.assert_parity(acc["dW2"], f64(init[1].cpu()) + ref["dW2"], "dW2 accumulated")
+    for kw in (dict(n_row_slices=1), dict(tile="128x128"), dict(tile="256x256"), dict(serialize=True)):
+        o2 = G.run_mlp_bwd(T.plan_for(w, **kw), inp, with_bias=True)
+        for k in ("dX", "dW1", "dW2", "db1"):
+            assert torch.equal(o2[k], out[k]), (kw, k)
+
+
 # A long reduction (h = 2048) with narrow projections: the up-projection of each row slice, the QKV
 # projection over all tokens and dH over each group of row slices are split along k; the split
 # counts do not depend on the slicing.
