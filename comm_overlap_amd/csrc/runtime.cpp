@@ -47,6 +47,10 @@ struct Runtime {
   // pipelined hand-off: per (row slice, copy stream) completion of the latest call's copies
   std::vector<hipEvent_t> copied;       // [r][E]
   std::vector<uint8_t> copied_pending;  // [r][E]: recorded and not yet superseded
+  // [r][E]: bit k set once worker stream k has waited for the current record of `copied` in the
+  // current call (stream order then covers every later wait of that worker); cleared when the
+  // event is recorded again and at the start of every call (the caller may pass other streams)
+  std::vector<uint32_t> copied_waited;
   // tracing: timing events, recorded around each product / copy of the latest call
   hipEvent_t t0 = nullptr;
   bool window_open = false;
@@ -111,11 +115,15 @@ tpslice_status_t build_runtime(tpslice_plan_s* p, Runtime* rt) {
   rt->gather.assign(p->S, nullptr);
   rt->copied.assign(size_t(p->r) * p->E, nullptr);
   rt->copied_pending.assign(size_t(p->r) * p->E, 0);
+  rt->copied_waited.assign(size_t(p->r) * p->E, 0);
   TPS_TRY_(make_event(&rt->fork, true));
   TPS_TRY_(make_event(&rt->call_done, true));
   for (auto& e : rt->join_w) TPS_TRY_(make_event(&e, true));
   for (auto& e : rt->join_c) TPS_TRY_(make_event(&e));
-  for (auto& e : rt->piece) TPS_TRY_(make_event(&e));
+  // the hand-off events ride on the products' launches (hipExtLaunchKernelGGL's stop event), whose
+  // documented use is a timing event: created with timing, and with the system-scope fence that
+  // the DMA engine's copy after them needs
+  for (auto& e : rt->piece) TPS_HIP(hipEventCreateWithFlags(&e, hipEventDefault));
   for (auto& e : rt->lead) TPS_TRY_(make_event(&e, true));
   for (auto& e : rt->gather) TPS_TRY_(make_event(&e, true));
   for (auto& e : rt->copied) TPS_TRY_(make_event(&e));
@@ -159,6 +167,9 @@ struct Schedule {
   uint32_t slice_streams = 0;  // copy streams used by the current row slice's pieces
   int lead_slice = -1;         // row slice whose first product has not been queued yet
   int lead_done = -1;          // latest row slice whose first-product event this call recorded
+  bool attached = false;       // the latest product's launch records its hand-off event itself
+  bool capturing = false;      // the caller's stream is capturing a graph: events are recorded by
+                               // markers (an event bound to a captured launch orders nothing)
 
   tpslice_status_t fence(hipStream_t s) {
     hipError_t e = launch_fence(s);
@@ -191,10 +202,19 @@ struct Schedule {
       TPS_HIP(hipStreamWaitEvent(worker(i), rt->lead[i - 1], 0));
     if (!pipelined()) return TPSLICE_OK;
     for (int q = i; q < i + span && q < p->r; ++q)
-      for (int k = 0; k < p->E; ++k) {
-        const size_t x = size_t(q) * p->E + k;
-        if (rt->copied_pending[x]) TPS_HIP(hipStreamWaitEvent(worker(i), rt->copied[x], 0));
-      }
+      for (int k = 0; k < p->E; ++k) TPS_TRY_(wait_copied(size_t(q) * p->E + k, i % p->S));
+    return TPSLICE_OK;
+  }
+
+  // Worker stream w waits for the current record of copied[x], unless it already has in this call
+  // (a wait between two products costs their gap: a producer over a group of row slices waits for
+  // each of them, and the row slices after it need not again).
+  tpslice_status_t wait_copied(size_t x, int w) {
+    if (!rt->copied_pending[x]) return TPSLICE_OK;
+    const uint32_t bit = w < 32 ? (1u << w) : 0u;
+    if (rt->copied_waited[x] & bit) return TPSLICE_OK;
+    TPS_HIP(hipStreamWaitEvent(wk(w), rt->copied[x], 0));
+    rt->copied_waited[x] |= bit;
     return TPSLICE_OK;
   }
 
@@ -203,8 +223,7 @@ struct Schedule {
   // read rows of every slice of a previous call's hand-off buffer).
   tpslice_status_t wait_all_handoffs(int k) {
     if (!pipelined()) return TPSLICE_OK;
-    for (size_t x = 0; x < rt->copied_pending.size(); ++x)
-      if (rt->copied_pending[x]) TPS_HIP(hipStreamWaitEvent(wk(k), rt->copied[x], 0));
+    for (size_t x = 0; x < rt->copied_pending.size(); ++x) TPS_TRY_(wait_copied(x, k));
     return TPSLICE_OK;
   }
 
@@ -217,6 +236,7 @@ struct Schedule {
       const size_t x = size_t(i) * p->E + k;
       TPS_HIP(hipEventRecord(rt->copied[x], cp(k)));
       rt->copied_pending[x] = 1;
+      rt->copied_waited[x] = 0;
     }
     return TPSLICE_OK;
   }
@@ -257,6 +277,7 @@ struct Schedule {
   }
 
   tpslice_status_t fork() {
+    std::fill(rt->copied_waited.begin(), rt->copied_waited.end(), 0u);
     if (p->trace) {
       if (!rt->window_open) {
         if (!rt->t0) TPS_HIP(hipEventCreate(&rt->t0));
@@ -334,7 +355,8 @@ struct Schedule {
       });
     }
     hipEvent_t ev = rt->piece[size_t(i) * p->c + j];
-    TPS_HIP(hipEventRecord(ev, worker(i)));
+    if (!attached) TPS_HIP(hipEventRecord(ev, worker(i)));
+    attached = false;
     if (contiguous) {
       // a whole-row piece is contiguous: spread it over the copy streams in equal row chunks
       const int64_t E = p->E;
@@ -373,8 +395,11 @@ struct Schedule {
   // product carries its timing events on the dispatch itself.
   // `alone`: nothing else runs beside this product (an all-token product after the slices), so the
   // tile choice may take the tiles that fill the last round
+  // `handoff`: piece (i, piece) of this product is handed off next (handoff()); an untraced launch
+  // then records the piece's event itself at the kernel's end, with no marker between this product
+  // and the next (a marker costs the gap between two products, about 5 us).
   tpslice_status_t product(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int on = 0,
-                           bool alone = false) {
+                           bool alone = false, bool handoff = false) {
     const int wi = i < 0 ? on : i;
     const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
     hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -388,8 +413,13 @@ struct Schedule {
       e0 = rt->tpool[t.ev0];
       e1 = rt->tpool[t.ev1];
     }
-    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, e1, p->tile, alone || serial || p->S == 1);
+    hipEvent_t done = nullptr;
+    if (handoff && !serial && !tr && !capturing && i >= 0 && g.M > 0 && g.N > 0)
+      done = rt->piece[size_t(i) * p->c + size_t(piece)];
+    hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, done ? done : e1, p->tile,
+                               alone || serial || p->S == 1);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
+    attached = done != nullptr;
     if (i >= 0 && i == lead_slice) {
       TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
       lead_slice = -1;
@@ -483,6 +513,7 @@ struct CallStreams {
   hipStream_t workers[kMaxStreams] = {};
   hipStream_t copiers[kMaxCopyStreams] = {};
   bool have_copiers = false;
+  bool capturing = false;  // the caller's stream is capturing a HIP graph
 };
 
 tpslice_status_t call_streams(const tpslice_plan_s* p, const tpslice_streams_t* s, bool copies, CallStreams* out) {
@@ -511,18 +542,21 @@ tpslice_status_t call_streams(const tpslice_plan_s* p, const tpslice_streams_t* 
   // Graph capture is supported for joined plans with one worker stream. A pipelined call waits for
   // events of earlier calls, and capturing a plan with more worker streams has crashed the HIP
   // runtime while it ended the capture; both are refused before anything is queued.
-  if (p->S > 1 || (p->desc.flags & TPSLICE_F_PIPELINE)) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(out->caller, &st) == hipSuccess && st != hipStreamCaptureStatusNone)
-      return fail(TPSLICE_ERR_UNSUPPORTED, "the caller's stream is capturing a graph: only a plan with one worker "
-                  "stream and no pipelining can be captured (this one: %d worker streams%s)", p->S,
-                  (p->desc.flags & TPSLICE_F_PIPELINE) ? ", pipelined" : "");
-  }
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  const hipError_t qe = hipStreamIsCapturing(out->caller, &st);
+  if (qe != hipSuccess) (void)hipGetLastError();  // a failed query must not read as the next launch's error
+  out->capturing = qe == hipSuccess && st != hipStreamCaptureStatusNone;
+  if (out->capturing && (p->S > 1 || (p->desc.flags & TPSLICE_F_PIPELINE)))
+    return fail(TPSLICE_ERR_UNSUPPORTED, "the caller's stream is capturing a graph: only a plan with one worker "
+                "stream and no pipelining can be captured (this one: %d worker streams%s)", p->S,
+                (p->desc.flags & TPSLICE_F_PIPELINE) ? ", pipelined" : "");
   return TPSLICE_OK;
 }
 
 Schedule schedule(tpslice_plan_s* p, Runtime* rt, const CallStreams& cs) {
-  return Schedule{p, rt, cs.caller, cs.serial, cs.workers, cs.have_copiers ? cs.copiers : nullptr};
+  Schedule S{p, rt, cs.caller, cs.serial, cs.workers, cs.have_copiers ? cs.copiers : nullptr};
+  S.capturing = cs.capturing;
+  return S;
 }
 
 GemmArgs args(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int64_t M,
@@ -614,7 +648,7 @@ extern "C" tpslice_status_t tpslice_mlp_fwd(tpslice_plan_t p, const void* X, con
       const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs g2 = args(bf(H, r0 * p->Fp), p->Fp, bf(W2, c0 * p->Fp), p->Fp, bfw(Z, r0 * p->h + c0), p->h,
                          p->Ms, p->pw, p->Fp);
-      TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DOWN, j, g2, kFwd, kEpiBf16));
+      TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DOWN, j, g2, kFwd, kEpiBf16, 0, false, Z_handoff != nullptr));
       if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
     }
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
@@ -663,7 +697,7 @@ extern "C" tpslice_status_t tpslice_attnproj_fwd(tpslice_plan_t p, const void* X
       const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs g = args(bf(C, r0 * p->ctx), p->ctx, bf(Wo, c0 * p->ctx), p->ctx, bfw(Z, r0 * p->h + c0), p->h,
                         p->Ms, p->pw, p->ctx);
-      TPS_TRY(S.product(i, TPSLICE_STEP_OUT, j, g, kFwd, kEpiBf16));
+      TPS_TRY(S.product(i, TPSLICE_STEP_OUT, j, g, kFwd, kEpiBf16, 0, false, Z_handoff != nullptr));
       if (Z_handoff) TPS_TRY(S.handoff(i, j, Z, Z_handoff));
     }
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
@@ -725,7 +759,7 @@ extern "C" tpslice_status_t tpslice_mlp_bwd(tpslice_plan_t p, const void* X, con
       const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs gx = args(bf(dU, r0 * p->N1), p->N1, bf(W1, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms, p->pw,
                          p->N1);
-      TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DX, j, gx, kDgrad, kEpiBf16));
+      TPS_TRY(S.product(i, TPSLICE_STEP_MLP_DX, j, gx, kDgrad, kEpiBf16, 0, false, dX_handoff != nullptr));
       if (dX_handoff) TPS_TRY(S.handoff(i, j, dX, dX_handoff));
     }
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
@@ -834,7 +868,7 @@ extern "C" tpslice_status_t tpslice_attnproj_bwd(tpslice_plan_t p, const void* X
       const int64_t c0 = int64_t(j) * p->pw;
       GemmArgs gx = args(bf(dQKV, r0 * p->qkv), p->qkv, bf(Wqkv, c0), p->h, bfw(dX, r0 * p->h + c0), p->h, p->Ms,
                          p->pw, p->qkv);
-      TPS_TRY(S.product(i, TPSLICE_STEP_ATTN_DX, j, gx, kDgrad, kEpiBf16));
+      TPS_TRY(S.product(i, TPSLICE_STEP_ATTN_DX, j, gx, kDgrad, kEpiBf16, 0, false, dX_handoff != nullptr));
       if (dX_handoff) TPS_TRY(S.handoff(i, j, dX, dX_handoff));
     }
     TPS_TRY(S.slice_handed_off(i, S.slice_streams));
