@@ -47,10 +47,21 @@ struct Runtime {
   // pipelined hand-off: per (row slice, copy stream) completion of the latest call's copies
   std::vector<hipEvent_t> copied;       // [r][E]
   std::vector<uint8_t> copied_pending;  // [r][E]: recorded and not yet superseded
-  // [r][E]: bit k set once worker stream k has waited for the current record of `copied` in the
-  // current call (stream order then covers every later wait of that worker); cleared when the
-  // event is recorded again and at the start of every call (the caller may pass other streams)
-  std::vector<uint32_t> copied_waited;
+  // Order of the records of `copied`: copied_seq[x] numbers the latest record of event x, and
+  // copied_on[x] names the (copy stream, call) it was recorded in. A stream completes its work in
+  // order, so a wait for one record covers every earlier record that the same call queued on the
+  // same stream (records of different calls are not compared: the caller may pass other streams).
+  // covered[w]: per (stream, call), the latest record that worker stream w has waited for in the
+  // current call (cleared at each call's start).
+  struct CopyKey {
+    hipStream_t stream;
+    uint64_t call;
+    bool operator==(const CopyKey& o) const { return stream == o.stream && call == o.call; }
+  };
+  uint64_t copy_seq = 0, call_serial = 0;
+  std::vector<uint64_t> copied_seq;
+  std::vector<CopyKey> copied_on;
+  std::vector<std::vector<std::pair<CopyKey, uint64_t>>> covered;
   // tracing: timing events, recorded around each product / copy of the latest call
   hipEvent_t t0 = nullptr;
   bool window_open = false;
@@ -115,7 +126,10 @@ tpslice_status_t build_runtime(tpslice_plan_s* p, Runtime* rt) {
   rt->gather.assign(p->S, nullptr);
   rt->copied.assign(size_t(p->r) * p->E, nullptr);
   rt->copied_pending.assign(size_t(p->r) * p->E, 0);
-  rt->copied_waited.assign(size_t(p->r) * p->E, 0);
+  rt->copied_seq.assign(size_t(p->r) * p->E, 0);
+  rt->copied_on.assign(size_t(p->r) * p->E, Runtime::CopyKey{nullptr, 0});
+  rt->covered.assign(size_t(p->S), {});
+  for (auto& c : rt->covered) c.reserve(size_t(kMaxCopyStreams) * 2);
   TPS_TRY_(make_event(&rt->fork, true));
   TPS_TRY_(make_event(&rt->call_done, true));
   for (auto& e : rt->join_w) TPS_TRY_(make_event(&e, true));
@@ -201,21 +215,41 @@ struct Schedule {
     if (i > 0 && lead_done == i - 1 && worker(i) != worker(i - 1))
       TPS_HIP(hipStreamWaitEvent(worker(i), rt->lead[i - 1], 0));
     if (!pipelined()) return TPSLICE_OK;
-    for (int q = i; q < i + span && q < p->r; ++q)
-      for (int k = 0; k < p->E; ++k) TPS_TRY_(wait_copied(size_t(q) * p->E + k, i % p->S));
-    return TPSLICE_OK;
+    return wait_copies(i % p->S, i, std::min(i + span, p->r));
   }
 
-  // Worker stream w waits for the current record of copied[x], unless it already has in this call
-  // (a wait between two products costs their gap: a producer over a group of row slices waits for
-  // each of them, and the row slices after it need not again).
-  tpslice_status_t wait_copied(size_t x, int w) {
-    if (!rt->copied_pending[x]) return TPSLICE_OK;
-    const uint32_t bit = w < 32 ? (1u << w) : 0u;
-    if (rt->copied_waited[x] & bit) return TPSLICE_OK;
-    TPS_HIP(hipStreamWaitEvent(wk(w), rt->copied[x], 0));
-    rt->copied_waited[x] |= bit;
-    return TPSLICE_OK;
+  // Worker stream w waits for the pending copies of row slices [q0, q1): on each copy stream, one
+  // wait for the latest of their records that w has not yet covered in this call (each wait costs
+  // the gap between two products: a producer over a group of row slices needs one per copy stream,
+  // not one per row slice, and the row slices after it none).
+  tpslice_status_t wait_copies(int w, int q0, int q1) {
+    auto& cov = rt->covered[size_t(w)];
+    auto covered_seq = [&](const Runtime::CopyKey& st) -> uint64_t* {
+      for (auto& c : cov)
+        if (c.first == st) return &c.second;
+      return nullptr;
+    };
+    // one round per stream that holds uncovered records of the range (normally one per copy
+    // stream): a wait for that stream's latest uncovered record covers all of them
+    auto uncovered = [&](size_t x) {
+      if (!rt->copied_pending[x]) return false;
+      const uint64_t* c = covered_seq(rt->copied_on[x]);
+      return !c || rt->copied_seq[x] > *c;
+    };
+    const size_t x0 = size_t(q0) * p->E, x1 = size_t(q1) * p->E;
+    for (;;) {
+      size_t first = SIZE_MAX;
+      for (size_t x = x0; x < x1 && first == SIZE_MAX; ++x)
+        if (uncovered(x)) first = x;
+      if (first == SIZE_MAX) return TPSLICE_OK;
+      const Runtime::CopyKey st = rt->copied_on[first];
+      size_t best = first;
+      for (size_t x = first + 1; x < x1; ++x)
+        if (uncovered(x) && rt->copied_on[x] == st && rt->copied_seq[x] > rt->copied_seq[best]) best = x;
+      TPS_HIP(hipStreamWaitEvent(wk(w), rt->copied[best], 0));
+      if (uint64_t* c = covered_seq(st)) *c = rt->copied_seq[best];
+      else cov.emplace_back(st, rt->copied_seq[best]);
+    }
   }
 
   // Pipelined mode: worker k waits for every hand-off copy of the previous calls that has not been
@@ -223,8 +257,7 @@ struct Schedule {
   // read rows of every slice of a previous call's hand-off buffer).
   tpslice_status_t wait_all_handoffs(int k) {
     if (!pipelined()) return TPSLICE_OK;
-    for (size_t x = 0; x < rt->copied_pending.size(); ++x) TPS_TRY_(wait_copied(x, k));
-    return TPSLICE_OK;
+    return wait_copies(k, 0, p->r);
   }
 
   // Pipelined mode: mark the end of row slice i's hand-off copies on each copy stream it used.
@@ -236,7 +269,8 @@ struct Schedule {
       const size_t x = size_t(i) * p->E + k;
       TPS_HIP(hipEventRecord(rt->copied[x], cp(k)));
       rt->copied_pending[x] = 1;
-      rt->copied_waited[x] = 0;
+      rt->copied_seq[x] = ++rt->copy_seq;
+      rt->copied_on[x] = Runtime::CopyKey{cp(k), rt->call_serial};
     }
     return TPSLICE_OK;
   }
@@ -277,7 +311,8 @@ struct Schedule {
   }
 
   tpslice_status_t fork() {
-    std::fill(rt->copied_waited.begin(), rt->copied_waited.end(), 0u);
+    for (auto& c : rt->covered) c.clear();
+    ++rt->call_serial;
     if (p->trace) {
       if (!rt->window_open) {
         if (!rt->t0) TPS_HIP(hipEventCreate(&rt->t0));
