@@ -40,6 +40,10 @@ struct Runtime {
   hipEvent_t call_done = nullptr;
   hipStream_t last_caller = nullptr;
   bool have_last = false;
+  // the latest call queued products over all tokens after its last hand-off (weight gradients,
+  // the QKV projection): its copies ran under them, so the next call's first row slice can wait
+  // for all of them at once, at no cost, instead of each row slice for its own
+  bool tail_after_copies = false;
   std::vector<hipEvent_t> piece;   // one per hand-off piece (and reused per call)
   std::vector<hipEvent_t> lead;    // one per row slice: its first product is done
   std::vector<hipEvent_t> gather;  // one per worker stream: its queued products are done
@@ -182,6 +186,8 @@ struct Schedule {
   int lead_slice = -1;         // row slice whose first product has not been queued yet
   int lead_done = -1;          // latest row slice whose first-product event this call recorded
   bool attached = false;       // the latest product's launch records its hand-off event itself
+  bool tail = false;           // a product over all tokens follows this call's latest hand-off
+  bool eager = false;          // the first row slice waits for every pending copy of earlier calls
   bool capturing = false;      // the caller's stream is capturing a graph: events are recorded by
                                // markers (an event bound to a captured launch orders nothing)
 
@@ -215,6 +221,10 @@ struct Schedule {
     if (i > 0 && lead_done == i - 1 && worker(i) != worker(i - 1))
       TPS_HIP(hipStreamWaitEvent(worker(i), rt->lead[i - 1], 0));
     if (!pipelined()) return TPSLICE_OK;
+    if (eager) {
+      eager = false;
+      return wait_copies(i % p->S, 0, p->r);
+    }
     return wait_copies(i % p->S, i, std::min(i + span, p->r));
   }
 
@@ -313,6 +323,7 @@ struct Schedule {
   tpslice_status_t fork() {
     for (auto& c : rt->covered) c.clear();
     ++rt->call_serial;
+    eager = rt->tail_after_copies;
     if (p->trace) {
       if (!rt->window_open) {
         if (!rt->t0) TPS_HIP(hipEventCreate(&rt->t0));
@@ -341,6 +352,7 @@ struct Schedule {
   // The caller's stream waits for every worker and copy stream. DMA-engine copies are closed by a
   // fence kernel first, so that the join event covers their completion.
   tpslice_status_t join() {
+    rt->tail_after_copies = tail;
     if (serial) {
       if (copied) TPS_TRY_(fence(caller));
       return TPSLICE_OK;
@@ -392,6 +404,7 @@ struct Schedule {
     hipEvent_t ev = rt->piece[size_t(i) * p->c + j];
     if (!attached) TPS_HIP(hipEventRecord(ev, worker(i)));
     attached = false;
+    tail = false;
     if (contiguous) {
       // a whole-row piece is contiguous: spread it over the copy streams in equal row chunks
       const int64_t E = p->E;
@@ -455,6 +468,7 @@ struct Schedule {
                                alone || serial || p->S == 1);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
     attached = done != nullptr;
+    if (i < 0) tail = true;
     if (i >= 0 && i == lead_slice) {
       TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
       lead_slice = -1;
@@ -476,6 +490,7 @@ struct Schedule {
   tpslice_status_t product_split(int i, int step, int piece, const GemmArgs& g, int layout, int epi, int splits,
                                  float* part, int on = 0, bool alone = false, int64_t tail_rows = 0) {
     if (splits <= 1) return product(i, step, piece, g, layout, epi, on, alone);
+    if (i < 0) tail = true;
     const int wi = i < 0 ? on : i;
     const double flops = 2.0 * double(g.M) * double(g.N) * double(g.K) * (epi == kEpiSwiglu ? 2.0 : 1.0);
     hipEvent_t e0 = nullptr, em = nullptr, e1 = nullptr;
