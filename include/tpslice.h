@@ -73,9 +73,12 @@ typedef enum {
 #define TPSLICE_F_COPY_BLIT 0x2u /* hand-off copies by the runtime's copy kernel instead of the DMA
                                     engines (uses compute units; for comparison)                       */
 #define TPSLICE_F_PIPELINE 0x4u  /* pipelined hand-off: the caller's stream waits for the products
-                                    only; a later call's row slice i waits just for this call's
-                                    hand-off copies of row slice i (a product over all tokens that
-                                    no row slice of its call precedes: for all of them). Chained
+                                    only; a later call's row slice i waits for this call's hand-off
+                                    copies of row slice i (a product over all tokens that no row
+                                    slice of its call precedes: for all of them). It may wait for
+                                    more: after a call that queued products over all tokens behind
+                                    its last copies, the next call's first row slice waits for all
+                                    of that call's copies, which ran under those products. Chained
                                     calls (a layer reading the previous layer's hand-off) then
                                     overlap the last pieces' copies with the next call's first
                                     pieces (Domino page,
