@@ -716,6 +716,69 @@ def test_benchmark_mode_full_size(key):
     joined.close()
 
 
+# Pipelined calls whose caller passes another set of worker and copy streams each time: a call's
+# waits for earlier calls' copies must hold whatever streams those copies ran on (a wait for one
+# copy record is taken to cover earlier ones only within one call and one stream), and the first
+# row slice after a call that ran products over all tokens behind its copies waits for all of them.
+STREAMS_LAYER = synth.custom("streams_layer", 915, tokens=2048, hidden=512, ffn=1024, tp=2, act="swiglu",
+                             bias=False, row_slices=4, col_slices=2, heads=8, kv_heads=2, head_dim=64,
+                             backward=True)
+
+
+@pytest.mark.parametrize("streams", [1, 2])
+def test_pipelined_calls_with_changing_streams(streams):
+    w = STREAMS_LAYER
+    _print_case("changing_streams", key=w.key, streams=streams)
+    inp = synth.make_inputs(w)
+    d = {k: v.to("cuda").contiguous() for k, v in inp.items()}
+    plan = T.plan_for(w, pipeline=True, handoff_rows=True, n_streams=streams, n_copy_streams=2)
+    joined = T.plan_for(w)
+    i = plan.info
+    assert i.n_streams == streams and i.n_copy_streams == 2
+    sets = [T.Streams.new(i.n_streams if i.n_streams > 1 else 0, 2) for _ in range(3)]
+    calls = [0]
+
+    def rotate():
+        plan.streams = sets[calls[0] % len(sets)]
+        calls[0] += 1
+
+    def step(pl, x, o, g, turn):
+        if turn: rotate()
+        pl.attnproj_fwd(x, d["Wqkv"], None, o["QKV"], d["C"], d["Wo"], o["Za"], o["Zah"])
+        if turn: rotate()
+        pl.mlp_fwd(o["Zah"], d["W1"], None, d["W2"], o["Z"], o["U"], o["Zh"])
+        if turn: rotate()
+        pl.mlp_bwd(o["Zah"], d["W1"], d["W2"], d["U_saved"], o["Zh"], o["dX"], g["dW1"], g["dW2"],
+                   dX_handoff=o["dXh"])
+        if turn: rotate()
+        pl.attnproj_bwd(x, d["Wqkv"], d["dQKV"], d["C"], d["Wo"], o["dXh"], o["dXa"], o["dC"], g["dWqkv"],
+                        g["dWo"], dX_handoff=o["dXah"])
+
+    outs = {}
+    for name, pl, turn in (("pipelined", plan, True), ("joined", joined, False)):
+        bufs = [_chain_buffers(w, pl.info) for _ in range(3)]
+        x = d["X"]
+        for o, g in bufs:
+            step(pl, x, o, g, turn)
+            x = o["dXah"]
+        if turn:
+            for s in sets:
+                plan.streams = s
+                plan.handoff_wait()
+        torch.cuda.synchronize()
+        outs[name] = bufs
+    for n, ((o1, g1), (o2, g2)) in enumerate(zip(outs["pipelined"], outs["joined"])):
+        for k in o1:
+            assert torch.equal(o1[k], o2[k]), (n, k)
+        for k in g1:
+            assert torch.equal(g1[k], g2[k]), (n, k)
+    o = outs["joined"][0][0]
+    for k in ("Zh", "dXh", "Zah", "dXah"):
+        assert torch.equal(o[k], o[k[:-1]]), k
+    plan.close()
+    joined.close()
+
+
 # Producers over groups of row slices: the up-projection and dH take the whole batch's k split,
 # so every group size gives the same bits; the grouped plan also matches the oracle.
 GROUPS = synth.custom("groups", 912, tokens=2048, hidden=512, ffn=1536, tp=2, act="swiglu", bias=True,
