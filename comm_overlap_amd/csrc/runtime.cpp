@@ -142,7 +142,9 @@ tpslice_status_t build_runtime(tpslice_plan_s* p, Runtime* rt) {
   // documented use is a timing event: created with timing, and with the system-scope fence that
   // the DMA engine's copy after them needs
   for (auto& e : rt->piece) TPS_HIP(hipEventCreateWithFlags(&e, hipEventDefault));
-  for (auto& e : rt->lead) TPS_TRY_(make_event(&e, true));
+  // the first-product events ride on launches too (see the hand-off events): with timing, and
+  // without the system-scope fence (their consumers are kernels on this GPU)
+  for (auto& e : rt->lead) TPS_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   for (auto& e : rt->gather) TPS_TRY_(make_event(&e, true));
   for (auto& e : rt->copied) TPS_TRY_(make_event(&e));
   return TPSLICE_OK;
@@ -443,6 +445,20 @@ struct Schedule {
   // product carries its timing events on the dispatch itself.
   // `alone`: nothing else runs beside this product (an all-token product after the slices), so the
   // tile choice may take the tiles that fill the last round
+  // A launch may record an ordering event itself (its dispatch's stop event) instead of a marker
+  // after it: not when traced (the dispatch carries the timing events), not under graph capture
+  // (an event bound to a captured launch orders nothing) and not on the serialized stream.
+  bool bind_ok(bool traced) const { return !serial && !traced && !capturing; }
+
+  // After row slice i's first product: the next row slice (on another worker) waits for it.
+  tpslice_status_t lead_recorded(int i, bool bound) {
+    if (i < 0 || i != lead_slice) return TPSLICE_OK;
+    if (!bound) TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
+    lead_slice = -1;
+    lead_done = i;
+    return TPSLICE_OK;
+  }
+
   // `handoff`: piece (i, piece) of this product is handed off next (handoff()); an untraced launch
   // then records the piece's event itself at the kernel's end, with no marker between this product
   // and the next (a marker costs the gap between two products, about 5 us).
@@ -461,19 +477,20 @@ struct Schedule {
       e0 = rt->tpool[t.ev0];
       e1 = rt->tpool[t.ev1];
     }
+    // the event this launch records at its end: the piece's hand-off event, else the row slice's
+    // first-product event that the next row slice (on another worker) waits for
     hipEvent_t done = nullptr;
-    if (handoff && !serial && !tr && !capturing && i >= 0 && g.M > 0 && g.N > 0)
-      done = rt->piece[size_t(i) * p->c + size_t(piece)];
+    bool lead_bound = false;
+    if (bind_ok(tr) && i >= 0 && g.M > 0 && g.N > 0) {
+      if (handoff) done = rt->piece[size_t(i) * p->c + size_t(piece)];
+      else if (i == lead_slice) { done = rt->lead[i]; lead_bound = true; }
+    }
     hipError_t e = launch_gemm(g, layout, epi, worker(wi), e0, done ? done : e1, p->tile,
                                alone || serial || p->S == 1);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
-    attached = done != nullptr;
+    attached = done != nullptr && !lead_bound;
     if (i < 0) tail = true;
-    if (i >= 0 && i == lead_slice) {
-      TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
-      lead_slice = -1;
-      lead_done = i;
-    }
+    TPS_TRY_(lead_recorded(i, lead_bound));
     if (tr) {
       tag_kernel(t.rec);
       rt->slots.push_back(t);
@@ -510,13 +527,11 @@ struct Schedule {
       em = rt->tpool[t.ev1];
       e1 = rt->tpool[u.ev1];
     }
+    const bool lead_bound = bind_ok(tr) && i >= 0 && i == lead_slice && g.M > 0 && g.N > 0;
+    if (lead_bound) e1 = rt->lead[i];  // the reduction, the product's last launch, records it
     hipError_t e = launch_gemm_split(g, layout, epi, splits, part, worker(wi), e0, e1, p->tile, em, tail_rows);
     if (e != hipSuccess) return fail(TPSLICE_ERR_HIP, "split GEMM launch: %s", hipGetErrorString(e));
-    if (i >= 0 && i == lead_slice) {
-      TPS_HIP(hipEventRecord(rt->lead[i], worker(i)));
-      lead_slice = -1;
-      lead_done = i;
-    }
+    TPS_TRY_(lead_recorded(i, lead_bound));
     if (tr) {
       tag_kernel(t.rec);
       rt->slots.push_back(t);
