@@ -67,12 +67,25 @@ struct Tile {
   static constexpr int kBRuns = kBTileBytes / 1024 / kWaves;
   // an operand read across k is staged as [64 k][tile columns]: a 1-KB load run must hold whole
   // k rows, and the SwiGLU pairing needs an even number of MFMA columns per wave
-  static constexpr bool kNcA = 1024 % (BM * 2) == 0, kNcB = 1024 % (BN * 2) == 0;
+  static constexpr bool kNcA = 1024 % (BM * 2) == 0;
   static constexpr bool kDualOk = kFN % 2 == 0;
+  // LDS columns of a B tile read across k: BN itself when its k rows fill 1-KB runs whole, else
+  // (narrower four-wave tiles: 160, 224 columns) 256, the columns past BN loaded but never read,
+  // so that the runs and the conflict-free swizzle of 256-column rows serve it unchanged; 0: none
+  static constexpr int kBnL = 1024 % (BN * 2) == 0 ? BN : (WM * WN == 4 && BM == 256 && BN < 256) ? 256 : 0;
+  static constexpr bool kNcB = kBnL > 0;
+  static constexpr int kBNcTileBytes = kBnL * kBKTile * 2;
   static_assert(kARuns >= 1 && kBRuns >= 1 && kATileBytes % (1024 * kWaves) == 0 &&
                 kBTileBytes % (1024 * kWaves) == 0, "tiles load in whole 1-KB runs per wave");
-  static_assert(kLdsBytes * BLOCKS <= 160 * 1024, "LDS per CU");
+  static_assert(kLdsBytes * BLOCKS <= 160 * 1024 && 2 * (kATileBytes + kBNcTileBytes) * BLOCKS <= 160 * 1024,
+                "LDS per CU");
 };
+// Operand stage and LDS bytes of a tile in one operand layout (a B tile read across k may be wider
+// in LDS than in the product)
+template <class TL, int LAYOUT>
+constexpr int stage_bytes() { return TL::kATileBytes + (LAYOUT == kFwd ? TL::kBTileBytes : TL::kBNcTileBytes); }
+template <class TL, int LAYOUT>
+constexpr int lds_bytes() { return 2 * stage_bytes<TL, LAYOUT>(); }
 using TileL = Tile<256, 256, 2, 4, 1>;
 using TileS = Tile<128, 128, 2, 2, 2>;
 using TileW = Tile<256, 320, 2, 4, 1>;
@@ -80,7 +93,10 @@ using TileN = Tile<128, 320, 2, 4, 1>;
 using TileM = Tile<128, 256, 2, 4, 1>;
 using TileT = Tile<128, 128, 2, 4, 1>;
 // Four waves, one per SIMD, each 128 rows x (BN / 2) columns, with the software-pipelined main
-// loop (gemm_kernel); for products whose K is a multiple of 64 (256 x 160: forward only).
+// loop (gemm_kernel); for products whose K is a multiple of 64. 256 x 160 serves forward products
+// and activation gradients with a bf16 or GeLU-gradient epilogue (its B tile, read across k there,
+// padded to 256 columns in LDS): a 2048-row slice of a 5120-wide output makes 8 x 32 = 256 blocks,
+// one per CU, where 256 x 256 makes 160.
 using TileL4 = Tile<256, 256, 2, 2, 1>;
 using TileH4 = Tile<256, 160, 2, 2, 1>;
 // 256 x 320 with four waves of 128 x 160: 320 accumulator registers per lane, more than the 256
@@ -232,6 +248,9 @@ __device__ inline void store_bf16x4(void* base, int64_t elem, float a, float b, 
 //   KC tile [rows][64 k]: run s holds rows 8s..8s+7; lane l -> row 8s + l/8, slot chunk l%8.
 //   NC tile [64 k][COLS]: run s holds 1024 / (2 COLS) k rows; lane l -> k row
 //                         s * (1024 / (2 COLS)) + l / (COLS / 8), slot chunk l % (COLS / 8).
+//                         In a padded tile (width `used` < COLS, used >= COLS / 2) the slots of
+//                         columns past `used` repeat chunk ch % (COLS / 16) of the same k row, a
+//                         column the same load instruction already reads; they are never read.
 
 template <int RUNS>
 struct KcLoader {
@@ -279,14 +298,16 @@ struct NcLoader {
   static constexpr int kKpr = 1024 / (COLS * 2);      // k rows per run
   uint32_t col_off[RUNS];  // byte offset of the lane's chunk within a k row
   uint32_t krow[RUNS];     // tile k row of the lane's chunk
-  uint32_t valid;          // bit j: the chunk's columns lie inside the operand
+  uint32_t valid;          // bit j: the chunk's columns lie inside the operand and the tile
   uint32_t ld_bytes;
-  __device__ void init(int wave, int lane, int64_t ld, int col0, int col_limit) {
+  // tile columns [col0, col0 + used), COLS / 2 <= used <= COLS
+  __device__ void init(int wave, int lane, int64_t ld, int col0, int col_limit, int used) {
     valid = 0;
     ld_bytes = uint32_t(ld * 2);
     for (int j = 0; j < RUNS; ++j) {
       const int k = (wave * RUNS + j) * kKpr + lane / kCpr;
-      const int ch = (lane % kCpr) ^ swz_nc(k);
+      int ch = (lane % kCpr) ^ swz_nc(k);
+      if (ch * 8 >= used) ch %= kCpr / 2;
       const int c = col0 + ch * 8;
       const bool ok = c < col_limit;
       col_off[j] = ok ? uint32_t(c) * 2 : 0u;
@@ -533,9 +554,14 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   constexpr int kFM = TL::kFM, kFN = TL::kFN;
   constexpr int kOutBN = kDual ? TL::BN / 2 : TL::BN;  // output columns per block
   constexpr int kWaveN = kOutBN / TL::kWavesN;         // output columns per wave
-  constexpr int kARuns = TL::kARuns, kBRuns = TL::kBRuns;
+  // the four-wave software-pipelined loop (the others: eight or four waves, one stage in flight)
+  constexpr bool kPipe = TL::kWaves == 4 && TL::BM == 256;
+  constexpr int kBL = kBDirect ? TL::BN : TL::kBnL;  // LDS columns of a B tile read across k
+  constexpr int kStage = stage_bytes<TL, LAYOUT>();
+  constexpr int kARuns = TL::kARuns, kBRuns = (kStage - TL::kATileBytes) / 1024 / TL::kWaves;
   static_assert((kADirect || TL::kNcA) && (kBDirect || TL::kNcB) && (!kDual || TL::kDualOk),
                 "tile does not support this operand layout");
+  static_assert(kBL == TL::BN || (kPipe && 2 * TL::BN >= kBL), "padded B tiles: pipelined loop, at least half used");
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -569,11 +595,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   KcLoader<kARuns> aK;
   KcLoader<kBRuns> bK;
   NcLoader<kARuns, TL::BM> aN;
-  NcLoader<kBRuns, TL::BN> bN;
+  NcLoader<kBRuns, kBL> bN;
   if constexpr (kADirect) aK.init(wave, lane, g.lda, m0, g.M, false, 0, TL::BM);
-  else aN.init(wave, lane, g.lda, m0, g.M);
+  else aN.init(wave, lane, g.lda, m0, g.M, TL::BM);
   if constexpr (kBDirect) bK.init(wave, lane, g.ldb, n0, g.N, kDual, g.half, TL::BN / 2);
-  else bN.init(wave, lane, g.ldb, n0, g.N);
+  else bN.init(wave, lane, g.ldb, n0, g.N, TL::BN);
 
   // B-tile column of fragment `in` (SwiGLU: the first half of the fragments gate, the second
   // half up, for the same output columns)
@@ -595,7 +621,6 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
 
   // (the four-wave pipelined tiles never take accumulate = 1: the launcher checks this, since their
   // accumulators are inline-asm operands that nothing the compiler places may write late)
-  constexpr bool kPipe = TL::kWaves == 4 && TL::BM == 256;
   if constexpr (EPI == kEpiF32 && !kPipe) {
     if (g.accumulate) {
       const float* C = reinterpret_cast<const float*>(g.C);
@@ -624,7 +649,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   // Queue load runs [lo, hi) of block kb: the wave's A runs are numbered first, then its B runs.
   constexpr int kRuns = kARuns + kBRuns;
   auto issue = [&](int kb, int lo, int hi) {
-    char* a_tile = smem + (kb & 1) * TL::kStageBytes;
+    char* a_tile = smem + (kb & 1) * kStage;
     char* b_tile = a_tile + TL::kATileBytes;
     const int k0 = kb * kBK;
     const int a0 = lo < kARuns ? lo : kARuns, a1 = hi < kARuns ? hi : kARuns;
@@ -650,12 +675,12 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
     }
   };
   auto frags = [&](int kb, bf16x8 (&af)[kFM], bf16x8 (&bf)[kFN], int kk) {
-    const char* a_tile = smem + (kb & 1) * TL::kStageBytes;
+    const char* a_tile = smem + (kb & 1) * kStage;
     const char* b_tile = a_tile + TL::kATileBytes;
 #pragma unroll
     for (int in = 0; in < kFN; ++in) {
       if constexpr (kBDirect) bf[in] = frag_kc(b_tile, bcol(in), lane, kk);
-      else bf[in] = frag_nc<TL::BN>(b_tile, bcol(in), lane, kk);
+      else bf[in] = frag_nc<kBL>(b_tile, bcol(in), lane, kk);
     }
 #pragma unroll
     for (int im = 0; im < kFM; ++im) {
@@ -700,7 +725,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   if constexpr (kPipe) {
     constexpr int kItems = kFM + kFN;  // fragment reads per k step
     constexpr int kStepM = kFM * kFN;  // MFMAs per k step
-    static_assert(kARuns + kBRuns <= kItems, "at most one load run per fragment read");
+    // load runs ride one MFMA after a fragment read each; tiles with more runs than reads (a
+    // padded B tile) spread them evenly over the k step instead
+    constexpr bool kRunPerItem = kARuns + kBRuns <= kItems;
+    static_assert(kRunPerItem || (kARuns + kBRuns - 1) * (kStepM - 1) / (kARuns + kBRuns) + 1 < kStepM,
+                  "every load run has a slot in step 1");
     static_assert(2 * kItems <= kStepM, "a fragment read after every other MFMA of step 0");
     static_assert((kItems - 1) * kStepM / kItems + 1 < kStepM, "every load run has a slot in step 1");
     const int lr16 = lane & 15;
@@ -726,7 +755,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
     }
     if constexpr (!kBDirect) {
 #pragma unroll
-      for (int in = 0; in < kFN; ++in) b_nc[in] = TL::kATileBytes + nc_off(bcol(in), TL::BN);
+      for (int in = 0; in < kFN; ++in) b_nc[in] = TL::kATileBytes + nc_off(bcol(in), kBL);
     }
     auto read_nc = [](const char* p, int row_bytes) {
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
@@ -760,7 +789,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
     // fragment read `i` of a k step, in the order the MFMAs first need them: A row 0, the B
     // columns, the other A rows
     auto item = [&](int stage, int kk, int i) {
-      const char* st = smem + stage * TL::kStageBytes;
+      const char* st = smem + stage * kStage;
       const uint32_t lo = kk ? lo1 : lo0;
       bf16x8(&af)[kFM] = kk ? a1 : a0;
       bf16x8(&bf)[kFN] = kk ? b1 : b0;
@@ -772,7 +801,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
         const int in = i - 1;
         if constexpr (kBDirect)
           bf[in] = *reinterpret_cast<const bf16x8*>(st + b_wave + lo + (bcol(in) - wn * kWaveN) * kRowBytes);
-        else bf[in] = read_nc(st + b_nc[in] + kk * 32 * TL::BN * 2, TL::BN * 2);
+        else bf[in] = read_nc(st + b_nc[in] + kk * 32 * kBL * 2, kBL * 2);
       }
     };
     // load run j of block kb into `stage` (the wave's A runs, then its B runs); blocks past the end
@@ -787,9 +816,9 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
     auto load_run = [&](const BlockLoads& bl, int stage, auto jc) {
       constexpr int j = decltype(jc)::value;
       if constexpr (j < kARuns)
-        dma16<j * 1024>(bl.ra, lds_wave + stage * TL::kStageBytes, a_voff[j], bl.sa);
+        dma16<j * 1024>(bl.ra, lds_wave + stage * kStage, a_voff[j], bl.sa);
       else
-        dma16<(j - kARuns) * 1024>(bl.rb, lds_wave_b + stage * TL::kStageBytes + TL::kATileBytes,
+        dma16<(j - kARuns) * 1024>(bl.rb, lds_wave_b + stage * kStage + TL::kATileBytes,
                                    b_voff[j - kARuns], bl.sb);
     };
     // accumulator columns [0, kAccA) in AGPRs, the rest (wide tiles) in VGPRs
@@ -819,8 +848,14 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
           constexpr int i = decltype(ic)::value;
           constexpr int at = i * kStepM / kItems;  // read i after MFMA `at`, load run i one MFMA later
           if constexpr (at == p) item(stage ^ 1, 0, i);
-          if constexpr (at + 1 == p && i < kRuns) load_run(bl, stage, ic);
+          if constexpr (kRunPerItem && at + 1 == p && i < kRuns) load_run(bl, stage, ic);
         });
+        if constexpr (!kRunPerItem) {
+          static_for<0, kRuns>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (j * (kStepM - 1) / kRuns + 1 == p) load_run(bl, stage, jc);
+          });
+        }
       });
     };
     // this block's k blocks start at kb0 (a split product's run; 0 otherwise)
@@ -878,13 +913,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
       const bool more = kb + 1 < nk;
       bf16x8 af[kFM], bf[kFN], bf1[kFN];
       frags(kb, af, bf, 0);
-      const char* a_tile = smem + (kb & 1) * TL::kStageBytes;
+      const char* a_tile = smem + (kb & 1) * kStage;
       const char* b_tile = a_tile + TL::kATileBytes;
       auto read_b1 = [&]() {
   #pragma unroll
         for (int in = 0; in < kFN; ++in) {
           if constexpr (kBDirect) bf1[in] = frag_kc(b_tile, bcol(in), lane, 1);
-          else bf1[in] = frag_nc<TL::BN>(b_tile, bcol(in), lane, 1);
+          else bf1[in] = frag_nc<kBL>(b_tile, bcol(in), lane, 1);
         }
       };
       auto read_a1 = [&](int im0, int im1) {
@@ -1022,6 +1057,8 @@ template __global__ void gemm_kernel<TileW4, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileW4, kFwd, kEpiGelu>(GemmArgs);
 template __global__ void gemm_kernel<TileH4, kFwd, kEpiBf16>(GemmArgs);
 template __global__ void gemm_kernel<TileH4, kFwd, kEpiGelu>(GemmArgs);
+template __global__ void gemm_kernel<TileH4, kDgrad, kEpiBf16>(GemmArgs);
+template __global__ void gemm_kernel<TileH4, kDgrad, kEpiDgelu>(GemmArgs);
 template __global__ void gemm_kernel<TileG4, kFwd, kEpiSwiglu>(GemmArgs);
 
 namespace {
@@ -1055,17 +1092,18 @@ thread_local LaunchInfo g_last_launch;
 
 template <class TL, int L, int E>
 hipError_t launch_one(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  constexpr int kLds = lds_bytes<TL, L>();
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<TL, L, E>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, TL::kLdsBytes);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (attr != hipSuccess) return attr;
   const int grid = g.tiles_m * g.tiles_n * g.splits;
   g_last_launch = LaunchInfo{TL::BM, TL::BN, TL::kWavesM, TL::kWavesN, TL::kBlocksPerCU, L, E, grid, TL::kThreads};
   if (start || stop)
-    hipExtLaunchKernelGGL((gemm_kernel<TL, L, E>), dim3(grid), dim3(TL::kThreads), TL::kLdsBytes, s, start, stop,
+    hipExtLaunchKernelGGL((gemm_kernel<TL, L, E>), dim3(grid), dim3(TL::kThreads), kLds, s, start, stop,
                           0, g);
   else
-    hipLaunchKernelGGL((gemm_kernel<TL, L, E>), dim3(grid), dim3(TL::kThreads), TL::kLdsBytes, s, g);
+    hipLaunchKernelGGL((gemm_kernel<TL, L, E>), dim3(grid), dim3(TL::kThreads), kLds, s, g);
   return hipGetLastError();
 }
 
@@ -1118,14 +1156,22 @@ hipError_t launch_tile(GemmArgs& g, int layout, int epi, hipStream_t stream, hip
 }
 
 // The four-wave pipelined tiles take products with K a multiple of 64 and no accumulation into an
-// fp32 output (checked by the launcher); 256 x 160 only forward ones without the SwiGLU pairing.
-template <class TL>
+// fp32 output (checked by the launcher), each tile a set of layouts and epilogues.
+enum PipeSet : int {
+  kPipeAll,     // 256 x 256: every layout and epilogue
+  kPipeNarrow,  // 256 x 160: forward products without the SwiGLU pairing, activation gradients
+                // with a bf16 or GeLU-gradient epilogue
+  kPipeFwd,     // 256 x 320: forward products without the SwiGLU pairing
+  kPipeGlu      // 256 x 224 (4 x 1 waves): forward SwiGLU products
+};
+template <class TL, int SET>
 hipError_t launch_pipe(GemmArgs& g, int layout, int epi, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const int out_bn = epi == kEpiSwiglu ? TL::BN / 2 : TL::BN;
   g.tiles_m = (g.M + TL::BM - 1) / TL::BM;
   g.tiles_n = (g.N + out_bn - 1) / out_bn;
-  if constexpr (TL::kNcA && TL::kNcB && TL::kDualOk) {
-    switch (layout * 8 + epi) {
+  const int kind = layout * 8 + epi;
+  if constexpr (SET == kPipeAll) {
+    switch (kind) {
       case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
       case kFwd * 8 + kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
       case kFwd * 8 + kEpiSwiglu: return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
@@ -1136,16 +1182,23 @@ hipError_t launch_pipe(GemmArgs& g, int layout, int epi, hipStream_t stream, hip
       case kWgrad * 8 + kEpiF32: return launch_one<TL, kWgrad, kEpiF32>(g, stream, start, stop);
       default: return hipErrorInvalidValue;
     }
-  } else if constexpr (TL::kDualOk && TL::kWavesN == 1) {
-    // forward SwiGLU only (the 256 x 224 tile)
-    if (layout == kFwd && epi == kEpiSwiglu) return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
-    return hipErrorInvalidValue;
-  } else {
-    switch (layout * 8 + epi) {
+  } else if constexpr (SET == kPipeNarrow) {
+    switch (kind) {
+      case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
+      case kFwd * 8 + kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiBf16: return launch_one<TL, kDgrad, kEpiBf16>(g, stream, start, stop);
+      case kDgrad * 8 + kEpiDgelu: return launch_one<TL, kDgrad, kEpiDgelu>(g, stream, start, stop);
+      default: return hipErrorInvalidValue;
+    }
+  } else if constexpr (SET == kPipeFwd) {
+    switch (kind) {
       case kFwd * 8 + kEpiBf16: return launch_one<TL, kFwd, kEpiBf16>(g, stream, start, stop);
       case kFwd * 8 + kEpiGelu: return launch_one<TL, kFwd, kEpiGelu>(g, stream, start, stop);
       default: return hipErrorInvalidValue;
     }
+  } else {
+    if (kind == kFwd * 8 + kEpiSwiglu) return launch_one<TL, kFwd, kEpiSwiglu>(g, stream, start, stop);
+    return hipErrorInvalidValue;
   }
 }
 
@@ -1155,28 +1208,35 @@ struct TileChoice {
   int id, bm, bn, blocks;
   bool fit_only;  // considered only when the product runs alone (see choose_tile)
   bool fwd_only;  // operands read along k only, with a bf16 or activation epilogue
+  bool dgrad_ok;  // (fwd_only tiles) also activation gradients with a bf16 or GeLU-gradient epilogue
   bool glu_ok;    // takes the SwiGLU pairing
   bool glu_only;  // takes only the SwiGLU pairing
   bool pipe;      // four-wave pipelined: K a multiple of 64 only, no accumulation into fp32 outputs
   double rate;
+  double rate_dgrad;  // dgrad_ok tiles: the rate on activation gradients
 };
 // The four-wave rates: 8192^3 (256 x 256) and a 4096 x 2560 x 5120 product (256 x 160, one round
-// of tiles against 256 x 256's 160 tiles).
+// of tiles against 256 x 256's 160 tiles; as an activation gradient its B tile is padded in LDS
+// and it loads 256 columns for 160).
 constexpr TileChoice kTiles[] = {
-    {kTile256x256, 256, 256, 1, false, false, true, false, false, 1.00},
-    {kTile128x128, 128, 128, 2, false, false, true, false, false, 0.70},
-    {kTile256x320, 256, 320, 1, true, true, false, false, false, 0.92},
-    {kTile128x320, 128, 320, 1, true, true, false, false, false, 0.73},
-    {kTile128x256, 128, 256, 1, true, false, true, false, false, 0.77},
-    {kTile128x128w8, 128, 128, 1, true, false, true, false, false, 0.50},
-    {kTile256x256w4, 256, 256, 1, false, false, true, false, true, 1.10},
-    {kTile256x160w4, 256, 160, 1, true, true, false, false, true, 0.83},
-    {kTile256x320w4, 256, 320, 1, true, true, false, false, true, 1.00},
-    {kTile256x224w4, 256, 224, 1, false, true, true, true, true, 1.05},
+    {kTile256x256, 256, 256, 1, false, false, false, true, false, false, 1.00, 1.00},
+    {kTile128x128, 128, 128, 2, false, false, false, true, false, false, 0.70, 0.70},
+    {kTile256x320, 256, 320, 1, true, true, false, false, false, false, 0.92, 0.0},
+    {kTile128x320, 128, 320, 1, true, true, false, false, false, false, 0.73, 0.0},
+    {kTile128x256, 128, 256, 1, true, false, false, true, false, false, 0.77, 0.77},
+    {kTile128x128w8, 128, 128, 1, true, false, false, true, false, false, 0.50, 0.50},
+    {kTile256x256w4, 256, 256, 1, false, false, false, true, false, true, 1.10, 1.10},
+    {kTile256x160w4, 256, 160, 1, true, true, true, false, false, true, 0.83, 0.76},
+    {kTile256x320w4, 256, 320, 1, true, true, false, false, false, true, 1.00, 0.0},
+    {kTile256x224w4, 256, 224, 1, false, true, false, true, true, true, 1.05, 0.0},
 };
 
 bool tile_supports(const TileChoice& t, int64_t K, int layout, int epi, bool accumulate) {
-  if (t.fwd_only && (layout != kFwd || (epi != kEpiBf16 && epi != kEpiGelu && epi != kEpiSwiglu))) return false;
+  if (t.fwd_only) {
+    const bool fwd = layout == kFwd && (epi == kEpiBf16 || epi == kEpiGelu || epi == kEpiSwiglu);
+    const bool dgrad = t.dgrad_ok && layout == kDgrad && (epi == kEpiBf16 || epi == kEpiDgelu);
+    if (!fwd && !dgrad) return false;
+  }
   if (!t.glu_ok && epi == kEpiSwiglu) return false;
   if (t.glu_only && epi != kEpiSwiglu) return false;
   return !t.pipe || (K > 0 && K % 64 == 0 && !(accumulate && epi == kEpiF32));
@@ -1198,7 +1258,7 @@ namespace {
 // occupies over those rounds. When the products of two adjacent row slices share the GPU
 // (`alone` false), the slots one product leaves empty run the other's blocks: the cost is half the
 // rounds of two such products together.
-double tile_cost(const TileChoice& t, int64_t M, int64_t N, int epi, bool alone, double* fill) {
+double tile_cost(const TileChoice& t, int64_t M, int64_t N, int layout, int epi, bool alone, double* fill) {
   const int64_t bn = epi == kEpiSwiglu ? t.bn / 2 : t.bn;
   const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + bn - 1) / bn);
   const int64_t slots = int64_t(kCUs) * t.blocks;
@@ -1206,7 +1266,7 @@ double tile_cost(const TileChoice& t, int64_t M, int64_t N, int epi, bool alone,
   if (fill) *fill = rounds ? double(tiles) / double(rounds * slots) : 1.0;
   const double work = double(t.bm) * double(t.bn) / (256.0 * 256.0);
   const double r = alone ? double(rounds) : double((2 * tiles + slots - 1) / slots) / 2.0;
-  return r * t.blocks * work / t.rate;
+  return r * t.blocks * work / (layout == kDgrad ? t.rate_dgrad : t.rate);
 }
 
 }  // namespace
@@ -1222,7 +1282,7 @@ int choose_tile(int64_t M, int64_t N, int64_t K, int layout, int epi, bool alone
   for (const TileChoice& t : kTiles) {
     if (!tile_supports(t, K, layout, epi, accumulate) || (t.fit_only && !alone)) continue;
     double f = 1.0;
-    const double cost = tile_cost(t, M, N, epi, alone, &f);
+    const double cost = tile_cost(t, M, N, layout, epi, alone, &f);
     if (cost < best_cost - 1e-9) { best_cost = cost; best = t.id; best_fill = f; }
   }
   if (fill) *fill = best_fill;
@@ -1253,10 +1313,10 @@ hipError_t launch_gemm(GemmArgs g, int layout, int epi, hipStream_t stream, hipE
     case kTile128x320: return launch_tile<TileN>(g, layout, epi, stream, start, stop);
     case kTile128x256: return launch_tile<TileM>(g, layout, epi, stream, start, stop);
     case kTile128x128w8: return launch_tile<TileT>(g, layout, epi, stream, start, stop);
-    case kTile256x256w4: return launch_pipe<TileL4>(g, layout, epi, stream, start, stop);
-    case kTile256x160w4: return launch_pipe<TileH4>(g, layout, epi, stream, start, stop);
-    case kTile256x320w4: return launch_pipe<TileW4>(g, layout, epi, stream, start, stop);
-    case kTile256x224w4: return launch_pipe<TileG4>(g, layout, epi, stream, start, stop);
+    case kTile256x256w4: return launch_pipe<TileL4, kPipeAll>(g, layout, epi, stream, start, stop);
+    case kTile256x160w4: return launch_pipe<TileH4, kPipeNarrow>(g, layout, epi, stream, start, stop);
+    case kTile256x320w4: return launch_pipe<TileW4, kPipeFwd>(g, layout, epi, stream, start, stop);
+    case kTile256x224w4: return launch_pipe<TileG4, kPipeGlu>(g, layout, epi, stream, start, stop);
     default: return launch_tile<TileL>(g, layout, epi, stream, start, stop);
   }
 }
@@ -1334,7 +1394,7 @@ double estimate_product_us(int64_t M, int64_t N, int64_t K, int layout, int epi,
   // M / 2 rows; the cost is their rounds together
   const int id = choose_tile(alone ? M : (M + 1) / 2, N, K, layout, epi, alone);
   for (const TileChoice& t : kTiles)
-    if (t.id == id) return tile_cost(t, M, N, epi, true, nullptr) * double(nk) * kBlockUs + kLaunchUs;
+    if (t.id == id) return tile_cost(t, M, N, layout, epi, true, nullptr) * double(nk) * kBlockUs + kLaunchUs;
   return 0.0;
 }
 

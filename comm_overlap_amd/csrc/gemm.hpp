@@ -53,8 +53,9 @@ struct GemmArgs {
 // Block tile of a launch. Every tile reduces k in the same order, so the choice never changes a
 // result bit. The 320-wide tiles take only products whose operands are both read along k, without
 // the SwiGLU pairing, the four-wave tiles only products with K a multiple of 64 that do not
-// accumulate into an fp32 output (256 x 160 and 256 x 320: forward only); a request a tile
-// cannot serve falls back to kTileAuto.
+// accumulate into an fp32 output (256 x 320: forward only; 256 x 160: forward, and activation
+// gradients with a bf16 or GeLU-gradient epilogue); a request a tile cannot serve falls back to
+// kTileAuto.
 enum GemmTile : int {
   kTileAuto = 0,
   kTile256x256 = 1,
@@ -65,8 +66,11 @@ enum GemmTile : int {
   kTile128x128w8 = 6,  // 128 x 128 with 8 waves, one block per CU
   kTile256x256w4 = 7,  // 256 x 256 with 4 waves and a software-pipelined loop: products with K a
                        // multiple of 64 and no accumulation into an fp32 output
-  kTile256x160w4 = 8,  // 256 x 160, likewise, forward products without the SwiGLU pairing
-  kTile256x320w4 = 9,  // 256 x 320, likewise (accumulators partly in VGPRs)
+  kTile256x160w4 = 8,  // 256 x 160, likewise, forward products without the SwiGLU pairing and
+                       // activation gradients with a bf16 or GeLU-gradient epilogue (their B tile
+                       // padded to 256 columns in LDS)
+  kTile256x320w4 = 9,  // 256 x 320, likewise, forward products without the pairing (accumulators
+                       // partly in VGPRs)
   kTile256x224w4 = 10, // 256 x 224 (112 gate + 112 up columns), 4 waves along m: forward SwiGLU only
   kTileCount = 11
 };

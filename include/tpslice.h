@@ -107,10 +107,11 @@ typedef enum {
    changes a result bit. Ids: 1 = 256 x 256, 2 = 128 x 128 (4 waves, two blocks per CU),
    3 = 256 x 320, 4 = 128 x 320, 5 = 128 x 256, 6 = 128 x 128 (8 waves, one block per CU),
    7 = 256 x 256, 8 = 256 x 160, 9 = 256 x 320 and 10 = 256 x 224 (4 waves, software-pipelined).
-   The 320-wide tiles and id 8 serve only forward products without the SwiGLU pairing, id 10 only
-   forward SwiGLU products (112 gate and 112 up columns per block), ids 7-10 only products whose k
-   is a multiple of 64 and that do not add to an fp32 output (accumulate = 1); other products then
-   take the automatic choice.                                                                     */
+   The 320-wide tiles serve only forward products without the SwiGLU pairing, id 8 those and
+   activation gradients with a bf16 or GeLU-gradient epilogue, id 10 only forward SwiGLU products
+   (112 gate and 112 up columns per block), ids 7-10 only products whose k is a multiple of 64 and
+   that do not add to an fp32 output (accumulate = 1); other products then take the automatic
+   choice.                                                                                        */
 #define TPSLICE_F_TILE_SHIFT 8
 #define TPSLICE_F_TILE_MASK (0xFu << TPSLICE_F_TILE_SHIFT)
 #define TPSLICE_F_TILE(id) (((uint32_t)(id) << TPSLICE_F_TILE_SHIFT) & TPSLICE_F_TILE_MASK)

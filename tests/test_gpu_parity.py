@@ -74,6 +74,8 @@ def test_four_wave_tiles(w):
 # Backward products for the four-wave tiles: every k (h, the FFN shard, the token count) a multiple
 # of 64, with odd k block counts and ragged rows and columns; operands stored across k (weights in
 # the activation gradients, both operands of the weight gradients) go through transposing reads.
+# 256 x 160 takes the activation gradients with a bf16 or GeLU-gradient epilogue, its B tile padded
+# to 256 columns in LDS (dX: 1216, 1280, 1344 columns; GeLU dH: 1344).
 BWD64_GELU = synth.custom("bwd64_gelu", 910, tokens=1088, hidden=1216, ffn=1344, tp=1, act="gelu", bias=True,
                           row_slices=2, col_slices=2, backward=True)
 BWD64_SWIGLU = synth.custom("bwd64_swiglu", 911, tokens=1024, hidden=1280, ffn=2752, tp=2, act="swiglu",
@@ -92,7 +94,7 @@ def test_four_wave_tiles_mlp_backward(w):
                     w.act, with_bias=w.bias)
     base = G.run_mlp_bwd(T.plan_for(w, tile="256x256"), inp, with_bias=w.bias)
     keys = ("dX", "dW1", "dW2") + (("db1",) if w.bias else ())
-    for tile in ("256x256w4", "auto", "256x256w4"):
+    for tile in ("256x256w4", "256x160w4", "auto", "256x256w4", "256x160w4"):
         _print_case("four_wave_bwd", key=w.key, tile=tile)
         out = G.run_mlp_bwd(T.plan_for(w, tile=tile), inp, with_bias=w.bias)
         for k in keys:
@@ -107,7 +109,7 @@ def test_four_wave_tiles_attn_backward():
     ref = L.attnproj_bwd(f64(inp["X"]), f64(inp["Wqkv"]), f64(inp["dQKV"]), f64(inp["C"]), f64(inp["Wo"]),
                          f64(inp["dY_attn"]), with_bias=True)
     base = G.run_attn_bwd(T.plan_for(w, tile="256x256"), inp, with_bias=True)
-    for tile in ("256x256w4", "auto"):
+    for tile in ("256x256w4", "256x160w4", "auto"):
         _print_case("four_wave_attn_bwd", key=w.key, tile=tile)
         out = G.run_attn_bwd(T.plan_for(w, tile=tile), inp, with_bias=True)
         for k in ("dX", "dC", "dWqkv", "dWo", "dbqkv"):
