@@ -374,11 +374,12 @@ __device__ inline bf16x8 frag_nc(const char* tile, int cb, int lane, int kk) {
 
 // ----------------------------------------------------------------------------------- epilogue
 // Where the epilogue reads and writes. GlobalIO addresses row m of each operand through plain
-// pointers (the split-k reduction kernel). BandIO serves one 16-row band of a GEMM block: each
-// operand is a buffer resource over the band's rows that lie inside it, so rows past M read as
-// zero and drop their stores in the memory unit, and each lane's byte offset at its first column
+// pointers (the split-k reduction kernel). BandIO serves the stores of one 16-row band of a GEMM
+// block: each output is a buffer resource over the band's rows that lie inside it, so stores to
+// rows past M are dropped in the memory unit, and each lane's byte offset at its first column
 // col0 is computed once; a column col then costs an immediate offset (col - col0 is a constant
-// for all but the SwiGLU second half).
+// for all but the SwiGLU second half). The GEMM kernel loads its saved inputs itself, the same
+// way (rows past M read as zero).
 // epilogues that add a bias [N] (SwiGLU: [2 half], gate then up) before their activation
 template <int EPI>
 constexpr bool epi_has_bias() { return EPI == kEpiBf16 || EPI == kEpiGelu || EPI == kEpiSwiglu; }
@@ -403,16 +404,9 @@ __device__ inline __amdgpu_buffer_rsrc_t band_rsrc(const void* p, int64_t ld, in
 }
 
 struct BandIO {
-  __amdgpu_buffer_rsrc_t c, out, in;
-  uint32_t oc, oo, oi;  // lane byte offsets at (band row lane % 16, column col0)
+  __amdgpu_buffer_rsrc_t c, out;
+  uint32_t oc, oo;  // lane byte offsets at (band row lane % 16, column col0)
   int col0;
-  __device__ void load_in(int col, float (&o)[4]) const {
-    const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(in, oi + uint32_t(col - col0) * 2, 0, 0);
-    o[0] = __uint_as_float(uint32_t(v[0]) << 16);
-    o[1] = __uint_as_float(uint32_t(v[0]) & 0xffff0000u);
-    o[2] = __uint_as_float(uint32_t(v[1]) << 16);
-    o[3] = __uint_as_float(uint32_t(v[1]) & 0xffff0000u);
-  }
   __device__ void store_c(int col, float a, float b, float c_, float d) const {
     __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(a, b, c_, d), c, oc + uint32_t(col - col0) * 2, 0, 0);
   }
@@ -449,9 +443,23 @@ __device__ constexpr int ep_writes() {
        : kWc | kWc2 | kWo;  // kEpiDswiglu
 }
 
-template <int EPI, class IO>
-__device__ __forceinline__ void ep_compute(const GemmArgs& g, const IO& io, int n, const float (&x)[4],
-                                           const float (&y)[4], EpOut& r) {
+// The epilogue's saved inputs: U (GeLU gradient) or G and V (SwiGLU gradient) at columns n and
+// half + n, four each.
+template <int EPI>
+constexpr int ep_inputs() { return EPI == kEpiDswiglu ? 2 : EPI == kEpiDgelu ? 1 : 0; }
+
+__device__ inline void unpack_bf16x4(i32x2 v, float (&o)[4]) {
+  o[0] = __uint_as_float(uint32_t(v[0]) << 16);
+  o[1] = __uint_as_float(uint32_t(v[0]) & 0xffff0000u);
+  o[2] = __uint_as_float(uint32_t(v[1]) << 16);
+  o[3] = __uint_as_float(uint32_t(v[1]) & 0xffff0000u);
+}
+
+// Results of one accumulator from its sums and, for the gradient epilogues, the saved inputs
+// u0 = aux_in[., n] and u1 = aux_in[., half + n] (already loaded).
+template <int EPI>
+__device__ __forceinline__ void ep_apply(const float (&x)[4], const float (&y)[4], const float (&u0)[4],
+                                         const float (&u1)[4], EpOut& r) {
   if constexpr (EPI == kEpiF32 || EPI == kEpiBf16) {
     for (int v = 0; v < 4; ++v) r.c[v] = x[v];
   } else if constexpr (EPI == kEpiPartialDual) {
@@ -465,25 +473,30 @@ __device__ __forceinline__ void ep_compute(const GemmArgs& g, const IO& io, int 
       r.c[v] = x[v] * sigmoid_f(x[v]) * y[v];
     }
   } else if constexpr (EPI == kEpiDgelu) {
-    float u[4];
-    io.load_in(n, u);
     for (int v = 0; v < 4; ++v) {
       float d;
-      gelu_and_grad(u[v], r.o[v], d);
+      gelu_and_grad(u0[v], r.o[v], d);
       r.c[v] = x[v] * d;
     }
   } else if constexpr (EPI == kEpiDswiglu) {
-    float G[4], V[4];
-    io.load_in(n, G);
-    io.load_in(int(g.half) + n, V);
     for (int v = 0; v < 4; ++v) {
-      const float sg = sigmoid_f(G[v]);
-      const float sl = G[v] * sg;
-      r.c[v] = x[v] * V[v] * (sg * (1.0f + G[v] * (1.0f - sg)));
+      const float G = u0[v], V = u1[v];
+      const float sg = sigmoid_f(G);
+      const float sl = G * sg;
+      r.c[v] = x[v] * V * (sg * (1.0f + G * (1.0f - sg)));
       r.c2[v] = x[v] * sl;
-      r.o[v] = sl * V[v];
+      r.o[v] = sl * V;
     }
   }
+}
+
+template <int EPI, class IO>
+__device__ __forceinline__ void ep_compute(const GemmArgs& g, const IO& io, int n, const float (&x)[4],
+                                           const float (&y)[4], EpOut& r) {
+  float u0[4] = {0.f, 0.f, 0.f, 0.f}, u1[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (ep_inputs<EPI>() >= 1) io.load_in(n, u0);
+  if constexpr (ep_inputs<EPI>() == 2) io.load_in(int(g.half) + n, u1);
+  ep_apply<EPI>(x, y, u0, u1, r);
 }
 
 // Stores of one accumulator's results, four columns (8 bytes of bf16, 16 of fp32) per lane.
@@ -957,6 +970,29 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
   const uint32_t oc = uint32_t((int64_t(lr) * g.ldc + col0) * kEs);
   const uint32_t oo = uint32_t((int64_t(lr) * g.ld_out + col0) * 2);
   const uint32_t oi = uint32_t((int64_t(lr) * g.ld_in + col0) * 2);
+  // fp32 outputs already store 16 bytes per lane: no pairs
+  constexpr int kPaired = kEs == 2 ? kOutFN / 2 * 2 : 0;
+  // The saved inputs of the gradient epilogues (U, or G and V) are loaded one band ahead: band
+  // im + 1's loads go out before band im's stores. Loads issued after a band's stores would wait
+  // for those stores as well (the vector memory counter completes in order), and each band would
+  // pay a whole memory round trip.
+  constexpr int kIns = ep_inputs<EPI>();
+  i32x2 pin[2][kOutFN][2];
+  auto fetch_in = [&](__amdgpu_buffer_rsrc_t rin, int buf) {
+    if constexpr (kIns > 0) {
+#pragma unroll
+      for (int in = 0; in < kOutFN; ++in) {
+        const int n = ocol(in) + 4 * lq;
+        // as the stores: paired accumulators load for every lane, single ones inside N only
+        const bool ok = in < kPaired || !col_edge || n < g.N;
+        const i32x2 z = {0, 0};
+        pin[buf][in][0] = ok ? __builtin_amdgcn_raw_buffer_load_b64(rin, oi + uint32_t(n - col0) * 2, 0, 0) : z;
+        if constexpr (kIns == 2)
+          pin[buf][in][1] =
+              ok ? __builtin_amdgcn_raw_buffer_load_b64(rin, oi + uint32_t(int(g.half) + n - col0) * 2, 0, 0) : z;
+      }
+    }
+  };
   // the bias of the lane's columns, read once for all bands (SwiGLU: gate in bx, up in by)
   const bool has_bias = epi_has_bias<EPI>() && g.bias != nullptr;
   float bx[kOutFN][4], by[kOutFN][4];
@@ -969,18 +1005,23 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
       if constexpr (kDual) load_bf16x4(g.bias, g.half + n, by[in]);
     }
   }
+  fetch_in(band_rsrc(g.aux_in, g.ld_in, 2, m0 + wm * TL::kWaveM, min(16, g.M - (m0 + wm * TL::kWaveM))), 0);
 #pragma unroll
   for (int im = 0; im < kFM; ++im) {
     const int row = m0 + wm * TL::kWaveM + 16 * im;
     if (row >= g.M) break;
     const int rows = min(16, g.M - row);
+    // the next band's saved inputs (a band past M reads zeros through an empty descriptor). Its row
+    // count is wave-uniform; the clamp compiles to a vector instruction, so it is read back into a
+    // scalar register (a descriptor in vector registers costs a loop per load).
+    if (im + 1 < kFM)
+      fetch_in(band_rsrc(g.aux_in, g.ld_in, 2, row + 16, __builtin_amdgcn_readfirstlane(max(0, min(16, g.M - row - 16)))),
+               (im + 1) & 1);
     BandIO io;
     io.c = band_rsrc(g.C, g.ldc, kEs, row, rows);
     io.out = band_rsrc(g.aux_out, g.ld_out, 2, row, rows);
-    io.in = band_rsrc(g.aux_in, g.ld_in, 2, row, rows);
     io.oc = oc;
     io.oo = oo;
-    io.oi = oi;
     io.col0 = col0;
     // accumulator `in`'s results (a zero bias when there is none: one add instead of a select)
     auto compute = [&](int in, EpOut& r) {
@@ -988,18 +1029,19 @@ __global__ __launch_bounds__(TL::kThreads, TL::kBlocksPerCU) void gemm_kernel(Ge
       float x[4] = {xv[0], xv[1], xv[2], xv[3]};
       if constexpr (epi_has_bias<EPI>())
         for (int v = 0; v < 4; ++v) x[v] += bx[in][v];
+      float u0[4] = {0.f, 0.f, 0.f, 0.f}, u1[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kIns >= 1) unpack_bf16x4(pin[im & 1][in][0], u0);
+      if constexpr (kIns == 2) unpack_bf16x4(pin[im & 1][in][1], u1);
       if constexpr (kDual) {
         const f32x4 yv = acc[im][in + kFN / 2];
         float y[4] = {yv[0], yv[1], yv[2], yv[3]};
         if constexpr (epi_has_bias<EPI>())
           for (int v = 0; v < 4; ++v) y[v] += by[in][v];
-        ep_compute<EPI>(g, io, ocol(in) + 4 * lq, x, y, r);
+        ep_apply<EPI>(x, y, u0, u1, r);
       } else {
-        ep_compute<EPI>(g, io, ocol(in) + 4 * lq, x, x, r);
+        ep_apply<EPI>(x, x, u0, u1, r);
       }
     };
-    // fp32 outputs already store 16 bytes per lane: no pairs
-    constexpr int kPaired = kEs == 2 ? kOutFN / 2 * 2 : 0;
 #pragma unroll
     for (int in = 0; in < kPaired; in += 2) {
       // every lane takes part in the regrouping; only the stores test the columns
