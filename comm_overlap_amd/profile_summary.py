@@ -15,6 +15,13 @@
         clock = busy cycles / duration, MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (busy cycles x 1024
         SIMDs), wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES, LDS conflicts = SQ_LDS_BANK_CONFLICT /
         SQ_LDS_IDX_ACTIVE
+    python -m comm_overlap_amd.profile_summary requests P1.db P2.db P3.db P4.db [--match gemm_kernel]
+        L1 -> L2 read requests of one kernel from four passes (SQ wave and LDS counters; TA/TD;
+        TCP stalls; TCP -> L2 requests and L2 hits, misses and miss latency), each counter summed
+        over its instances and taken as the median over the kernel's dispatches: hit rate, average
+        request and miss latencies (latency sums / request counts), requests in flight per CU
+        (request latency sum / (cycles x 256 CUs)) and the per-CU shares of cycles; cycles are
+        GRBM_GUI_ACTIVE / 8 of the same pass
 """
 from __future__ import annotations
 
@@ -179,6 +186,48 @@ def counters(db, match, simds=1024, xcds=8):
               f"mfma_busy {100 * busy:.1f}%, WAIT_ANY {100 * wait:.1f}%, ldsconf {100 * lds:.1f}%")
 
 
+def _pass_medians(db, match):
+    c = sqlite3.connect(db)
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for name, disp, cname, val in c.execute(
+            "select name, dispatch_id, counter_name, counter_value from pmc_events"):
+        if match in name:
+            per[disp][cname] += val
+    dur = {d: (e - s) * 1e-9 for d, s, e in c.execute("select dispatch_id, start, end from kernels")}
+    disps = sorted(per)
+    if not disps:
+        raise SystemExit(f"{db}: no dispatch of {match}")
+
+    def med(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2]
+
+    m = {cn: med([per[d][cn] for d in disps]) for cn in per[disps[0]]}
+    m["_dur"] = med([dur[d] for d in disps])
+    m["_n"] = len(disps)
+    m["_cyc"] = m["GRBM_GUI_ACTIVE"] / 8
+    return m
+
+
+def requests(dbs, match, cus=256):
+    p1, p2, p3, p4 = (_pass_medians(db, match) for db in dbs)
+    req = p4["TCP_TCC_READ_REQ"]
+    print(f"  dispatches {p4['_n']}, duration under counters {p4['_dur'] * 1e6:.0f} us, "
+          f"clock {p4['_cyc'] / p4['_dur'] / 1e9:.2f} GHz")
+    print(f"  TCP -> L2 read requests {req:.4g} ({req * 128 / 1e9:.2f} GB at 128 B)")
+    print(f"  L2 hit rate {p4['TCC_HIT'] / (p4['TCC_HIT'] + p4['TCC_MISS']):.3f}, miss requests to the "
+          f"fabric {p4['TCC_EA0_RDREQ']:.3g} ({p4['TCC_EA0_RDREQ'] * 128 / 1e9:.1f} GB)")
+    print(f"  average TCP -> L2 read latency {p4['TCP_TCC_READ_REQ_LATENCY'] / req:.0f} cycles, "
+          f"average L2 miss latency {p4['TCC_EA0_RDREQ_LEVEL'] / p4['TCC_EA0_RDREQ']:.0f} cycles")
+    print(f"  TCP -> L2 reads in flight per CU {p4['TCP_TCC_READ_REQ_LATENCY'] / (p4['_cyc'] * cus):.1f}")
+    print(f"  TCP stalled on pending misses {p3['TCP_PENDING_STALL_CYCLES'] / (p3['_cyc'] * cus):.2f} of cycles per CU")
+    print(f"  TD busy {p2['TD_TD_BUSY'] / (p2['_cyc'] * cus):.2f}, stalled on the L1 "
+          f"{p2['TD_TC_STALL'] / (p2['_cyc'] * cus):.2f}, TA busy {p2['TA_TA_BUSY'] / (p2['_cyc'] * cus):.2f} "
+          f"of cycles per CU")
+    print(f"  LDS data FIFO full {p1['SQ_LDS_DATA_FIFO_FULL']:.0f} cycles, waves waiting on LDS "
+          f"{p1['SQ_WAIT_INST_LDS'] / p1['SQ_WAVE_CYCLES']:.2f} of wave cycles")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -195,7 +244,13 @@ def main(argv=None):
     k = sub.add_parser("counters")
     k.add_argument("db")
     k.add_argument("--match", default="gemm_kernel")
+    q = sub.add_parser("requests")
+    q.add_argument("dbs", nargs=4)
+    q.add_argument("--match", default="gemm_kernel")
     a = ap.parse_args(argv)
+    if a.cmd == "requests":
+        requests(a.dbs, a.match)
+        return 0
     if a.cmd == "trace":
         trace(a.db, a.match)
         return 0
