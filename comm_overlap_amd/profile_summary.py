@@ -90,7 +90,6 @@ def trace(db, match):
         print(f"  {len(d):6d} x {size:>11d} B  avg {sum(d)/len(d):9.2f}  ({gbs:6.1f} GB/s each)  {name}")
     busy = _union([(s, e) for name, s, e in ks if match in name])
     tot = hid = 0.0
-    j = 0
     for name, s, e, size in cps:
         if "DEVICE_TO_DEVICE" not in name:
             continue
