@@ -6,8 +6,8 @@
 // that the FlashAttention titles in the Domino page's builds-on list describe. Per key block:
 //   S = Q K^T   v_mfma_f32_16x16x32_bf16, Q fragments held in registers for the whole walk, K from
 //               LDS by ds_read_b128 (rows XOR-swizzled by 16-byte chunk);
-//   P = exp2(S log2(e) / sqrt(d) - m), rounded to bf16; the mask zeroes keys past the query on the
-//               diagonal block;
+//   P = exp2(S log2(e) / sqrt(d) - m), rounded to bf16, m the row's reference maximum (kLazy
+//               below); the mask zeroes keys past the query on the diagonal block;
 //   O += P V    the same MFMA, P taken straight from S's accumulator layout (no LDS round trip)
 //               and V read across keys with ds_read_b64_tr_b16.
 // S's accumulator gives lane l the keys 16 j + 4 (l / 16) + 0..3 of tile j for row l % 16. The PV
@@ -62,6 +62,13 @@ constexpr int kThreads = 64 * kWaves;
 // 2 (row % 8) leaves two reads per bank group, the minimum for 512 bytes).
 __device__ inline int swz_k(int row) { return row & 15; }
 __device__ inline int swz_v(int row) { return (row & 7) << 1; }
+
+// Online softmax with a lazy reference: a row keeps its reference maximum m (log2 units) until a
+// key block's maximum exceeds it by more than kLazy, so most blocks neither rescale the output nor
+// the row sum. P = exp2(S scale_log2 - m) then stays below 2^kLazy, and the row's log-sum-exp is
+// m + log2(l) for whatever m it ended with. The decision depends only on the row's own scores, so
+// every kernel that walks the same key blocks takes the same references and gets the same bits.
+constexpr float kLazy = 8.0f;
 
 // max / sum of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes holding one S row), on VALU
 // lane swaps; every lane of the group gets the same bits
@@ -179,21 +186,26 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
         }
       }
 
-      // ---- online softmax over the block's keys (scores in log2 units)
-      const bool diag = kb >= first_diag;
+      // ---- online softmax over the block's keys (log2 units: the scale folds into the exponent's
+      // fma; the maximum of the raw scores times the positive scale is the scaled maximum)
+      // (the mask in a branch of its own: folded into one per-element test, it cost a compare and
+      // a select per score on every key block)
+      if (kb >= first_diag) {
+  #pragma unroll
+        for (int j = 0; j < kBK / 16; ++j)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (kb * kBK + 16 * j + 4 * lg + v > q_row) s[j][v] = -INFINITY;
+      }
       float mx = -INFINITY;
   #pragma unroll
       for (int j = 0; j < kBK / 16; ++j)
   #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float x = s[j][v] * sl2;
-          if (diag && kb * kBK + 16 * j + 4 * lg + v > q_row) x = -INFINITY;
-          s[j][v] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = row_max4(mx);
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first block (m = -inf)
+        for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[j][v]);
+      mx = row_max4(mx) * sl2;
+      const bool move = mx > m + kLazy;  // always on the first block (m = -inf)
+      const float m_new = move ? mx : m;
+      const float alpha = move ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;  // 0 on the first block
       float rs = 0.0f;
       bf16x8 pf[kBK / 32];
   #pragma unroll
@@ -202,15 +214,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
         for (int half = 0; half < 2; ++half)
   #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float p = __builtin_amdgcn_exp2f(s[2 * c + half][v] - m_new);
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[2 * c + half][v], sl2, -m_new));
             rs += p;
             pf[c][4 * half + v] = (__bf16)p;
           }
       }
       l = l * alpha + rs;  // the lane's share of the row sum
       m = m_new;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {  // (alpha = 1 on the other lanes)
   #pragma unroll
-      for (int j = 0; j < kD / 16; ++j) o[j] *= alpha;
+        for (int j = 0; j < kD / 16; ++j) o[j] *= alpha;
+      }
 
       // ---- O += P V: for each 32-key step, the V fragment of keys 32c + 4 lg + 0..3 and
       // 32c + 16 + 4 lg + 0..3 in the lane's k slots, dims 16 jd + lr
@@ -354,21 +368,29 @@ __global__ __launch_bounds__(kThreads2, 2) void attn_fwd_kernel2(AttnArgs a) {
       }
       const bool diag = kb == nkb - 1;
       bf16x8 pf[kRT2][kBK / 32];
+      float alpha[kRT2];
+      bool moved = false;
+      if (diag) {  // (a branch of its own, as in the eight-wave kernel)
+#pragma unroll
+        for (int r = 0; r < kRT2; ++r)
+#pragma unroll
+          for (int j = 0; j < kBK / 16; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (kb * kBK + 16 * j + 4 * lg + v > q_row[r]) s[r][j][v] = -INFINITY;
+      }
 #pragma unroll
       for (int r = 0; r < kRT2; ++r) {
         float mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < kBK / 16; ++j)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float x = s[r][j][v] * sl2;
-            if (diag && kb * kBK + 16 * j + 4 * lg + v > q_row[r]) x = -INFINITY;
-            s[r][j][v] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = row_max4(mx);
-        const float m_new = fmaxf(m[r], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[r] - m_new);
+          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[r][j][v]);
+        mx = row_max4(mx) * sl2;
+        const bool move = mx > m[r] + kLazy;
+        const float m_new = move ? mx : m[r];
+        alpha[r] = move ? __builtin_amdgcn_exp2f(m[r] - m_new) : 1.0f;
+        moved = moved || move;
         float rsum = 0.f;
 #pragma unroll
         for (int c = 0; c < kBK / 32; ++c)
@@ -376,14 +398,18 @@ __global__ __launch_bounds__(kThreads2, 2) void attn_fwd_kernel2(AttnArgs a) {
           for (int half = 0; half < 2; ++half)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              const float pv = __builtin_amdgcn_exp2f(s[r][2 * c + half][v] - m_new);
+              const float pv = __builtin_amdgcn_exp2f(fmaf(s[r][2 * c + half][v], sl2, -m_new));
               rsum += pv;
               pf[r][c][4 * half + v] = (__bf16)pv;
             }
-        l[r] = l[r] * alpha + rsum;
+        l[r] = l[r] * alpha[r] + rsum;
         m[r] = m_new;
+      }
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // (alpha = 1 where a row kept its reference)
 #pragma unroll
-        for (int j = 0; j < kD / 16; ++j) o[r][j] *= alpha;
+        for (int r = 0; r < kRT2; ++r)
+#pragma unroll
+          for (int j = 0; j < kD / 16; ++j) o[r][j] *= alpha[r];
       }
       const int vq = lane & 3, vv4 = (lane & 15) >> 2;
 #pragma unroll

@@ -7,7 +7,8 @@
 //   2. attn_bwd_dkv_kernel   one block per (sequence, query head, 128-key block), 8 waves of 16
 //                            keys, walking the 64-query blocks from the diagonal to the end:
 //                              S^T and dP^T by MFMA with the wave's K / V rows as register operands
-//                              and Q / dO rows from LDS; P = exp2(S log2(e) / sqrt(d) - lse2),
+//                              and Q / dO rows from LDS; P = exp2(S log2(e) / sqrt(d) - lse2) (one
+//                              fma and an exp2; masked scores are set to -inf on diagonal steps),
 //                              dS = P (dP - D); dV += P^T dO and dK += dS^T Q with dO and Q read
 //                              across queries (ds_read_b64_tr_b16) and P, dS taken straight from the
 //                              accumulator layout (the same 32-step slot mapping as the forward's
@@ -208,16 +209,23 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
     }
     // P and dS, packed for the 32-query products: slot 4 half + v of step c holds query
     // 32 c + 16 half + 4 (l / 16) + v
-    const bool diag = qs * kQStep < kb * kKeyBlock + kKeyBlock;
+    // the causal mask in a branch of its own (a masked score is -inf, its P zero): folded into one
+    // per-element test it cost a compare and a select per score on every step
     const int key = key0 + lr;
+    if (qs * kQStep < kb * kKeyBlock + kKeyBlock) {
+#pragma unroll
+      for (int jq = 0; jq < kQStep / 16; ++jq)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (key > qs * kQStep + 16 * jq + 4 * lg + v) s[jq][v] = -INFINITY;
+    }
     bf16x8 pf[kQStep / 32], sf[kQStep / 32];
 #pragma unroll
     for (int jq = 0; jq < kQStep / 16; ++jq)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int qi = 16 * jq + 4 * lg + v;
-        float p = __builtin_amdgcn_exp2f(s[jq][v] * sl2 - lse_s[qi]);
-        if (diag && key > qs * kQStep + qi) p = 0.0f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[jq][v], sl2, -lse_s[qi]));
         const float ds = p * (dp[jq][v] - dd_s[qi]);
         pf[jq >> 1][4 * (jq & 1) + v] = (__bf16)p;
         sf[jq >> 1][4 * (jq & 1) + v] = (__bf16)ds;
@@ -365,15 +373,19 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) {
         dp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag_row(v_r, 16 * j, lane, kk), of[kk], dp[j], 0, 0, 0);
       }
     }
-    const bool diag = kb >= first_diag;
+    if (kb >= first_diag) {  // the mask in a branch of its own, as in the dK/dV kernel
+#pragma unroll
+      for (int j = 0; j < kKStep / 16; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (kb * kKStep + 16 * j + 4 * lg + v > q_row) s[j][v] = -INFINITY;
+    }
     bf16x8 sf[kKStep / 32];
 #pragma unroll
     for (int j = 0; j < kKStep / 16; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int kj = 16 * j + 4 * lg + v;
-        float p = __builtin_amdgcn_exp2f(s[j][v] * sl2 - lse2);
-        if (diag && kb * kKStep + kj > q_row) p = 0.0f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], sl2, -lse2));
         sf[j >> 1][4 * (j & 1) + v] = (__bf16)(p * (dp[j][v] - dd));
       }
     // dQ += dS K: lane l accumulates query q_row, dims 16 jd + 4 (l / 16) + v
