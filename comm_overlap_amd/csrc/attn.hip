@@ -16,8 +16,8 @@
 // keys in the same slots, so the product is the plain sum over the step's keys.
 // K and V tiles (128 keys x 128 dims bf16, 32 KB each) come in through registers (16-byte global
 // loads one key block ahead, then ds_write_b128), shared by the block's eight waves. The row maximum
-// is reduced over the row's four lanes with VALU lane swaps; each lane keeps its own share of the
-// row sum until the end. The diagonal is the block's last key block (query and key blocks are both
+// is reduced over the row's four lanes with VALU lane swaps; the row sum of the bf16 P values comes
+// out of one more MFMA per 32-key step, with a fragment of ones in V's place. The diagonal is the block's last key block (query and key blocks are both
 // 128 rows), masked per row; its maximum is finite from its first key on.
 // Measured on the Llama shard shapes (13B: 5 query and key/value heads; 70B: 8 query heads, 1
 // key/value head) at 2048-token sequences: dealing the query blocks so that each XCD reads the K/V
@@ -70,19 +70,13 @@ __device__ inline int swz_v(int row) { return (row & 7) << 1; }
 // every kernel that walks the same key blocks takes the same references and gets the same bits.
 constexpr float kLazy = 8.0f;
 
-// max / sum of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes holding one S row), on VALU
-// lane swaps; every lane of the group gets the same bits
+// max of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes holding one S row), on VALU lane
+// swaps; every lane of the group gets the same bits
 __device__ inline float row_max4(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ inline float row_sum4(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Pairing of query blocks qb and nqb - 1 - qb in one workgroup (needs an even nqb and a whole number
@@ -138,7 +132,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
     f32x4 o[kD / 16];
   #pragma unroll
     for (int j = 0; j < kD / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.0f;
+    // the row sum of P comes out of the PV product: one more MFMA per 32-key step with a fragment
+    // of ones in V's place gives every lane its row's sum of the bf16 P values (the weights O uses)
+    float m = -INFINITY;
+    f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                         (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
     const float sl2 = a.scale_log2;
 
     // K and V chunks of a key block: each thread four 16-byte chunks of each, loaded into registers
@@ -206,24 +205,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
       const bool move = mx > m + kLazy;  // always on the first block (m = -inf)
       const float m_new = move ? mx : m;
       const float alpha = move ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;  // 0 on the first block
-      float rs = 0.0f;
       bf16x8 pf[kBK / 32];
   #pragma unroll
       for (int c = 0; c < kBK / 32; ++c) {
   #pragma unroll
         for (int half = 0; half < 2; ++half)
   #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[2 * c + half][v], sl2, -m_new));
-            rs += p;
-            pf[c][4 * half + v] = (__bf16)p;
-          }
+          for (int v = 0; v < 4; ++v)
+            pf[c][4 * half + v] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * c + half][v], sl2, -m_new));
       }
-      l = l * alpha + rs;  // the lane's share of the row sum
       m = m_new;
       if (__builtin_amdgcn_ballot_w64(move) != 0) {  // (alpha = 1 on the other lanes)
   #pragma unroll
         for (int j = 0; j < kD / 16; ++j) o[j] *= alpha;
+        lacc *= alpha;
       }
 
       // ---- O += P V: for each 32-key step, the V fragment of keys 32c + 4 lg + 0..3 and
@@ -244,12 +239,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
           // first operand V (rows = dims), second P: lane l gets O[q row lr][dim 16 jd + 4 lg + v]
           o[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pf[c], o[jd], 0, 0, 0);
         }
+        lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[c], lacc, 0, 0, 0);
       }
     }
 
     // ---- C = O / l (bf16), the lane's row and dims 16 jd + 4 lg .. +3; the row's log-sum-exp
     // (natural log) m + log2(l) in log2 units, for the backward pass
-    const float lsum = row_sum4(l);
+    const float lsum = lacc[0];
     const float inv = 1.0f / lsum;
     if (a.lse && lg == 0) a.lse[(seq0 + q_row) * a.q_heads + h] = (m + __log2f(lsum)) * 0.69314718055994531f;
     unsigned short* C = reinterpret_cast<unsigned short*>(a.C) + (seq0 + q_row) * a.ld_c + int64_t(h) * kD + 4 * lg;
@@ -323,9 +319,13 @@ __global__ __launch_bounds__(kThreads2, 2) void attn_fwd_kernel2(AttnArgs a) {
     for (int r = 0; r < kRT2; ++r)
 #pragma unroll
       for (int j = 0; j < kD / 16; ++j) o[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[kRT2], l[kRT2];
+    // row sums from the PV product, as in the eight-wave kernel
+    float m[kRT2];
+    f32x4 lacc[kRT2];
 #pragma unroll
-    for (int r = 0; r < kRT2; ++r) { m[r] = -INFINITY; l[r] = 0.f; }
+    for (int r = 0; r < kRT2; ++r) { m[r] = -INFINITY; lacc[r] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                         (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
     const float sl2 = a.scale_log2;
     // this thread's 8 runs (1 KB each) of the K tile and of the V tile: run q = wave * 8 + p covers
     // key rows 4q .. 4q + 3; lane l writes LDS bytes 16 l of the run, which hold row 4q + l / 16,
@@ -391,25 +391,22 @@ __global__ __launch_bounds__(kThreads2, 2) void attn_fwd_kernel2(AttnArgs a) {
         const float m_new = move ? mx : m[r];
         alpha[r] = move ? __builtin_amdgcn_exp2f(m[r] - m_new) : 1.0f;
         moved = moved || move;
-        float rsum = 0.f;
 #pragma unroll
         for (int c = 0; c < kBK / 32; ++c)
 #pragma unroll
           for (int half = 0; half < 2; ++half)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float pv = __builtin_amdgcn_exp2f(fmaf(s[r][2 * c + half][v], sl2, -m_new));
-              rsum += pv;
-              pf[r][c][4 * half + v] = (__bf16)pv;
-            }
-        l[r] = l[r] * alpha[r] + rsum;
+            for (int v = 0; v < 4; ++v)
+              pf[r][c][4 * half + v] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[r][2 * c + half][v], sl2, -m_new));
         m[r] = m_new;
       }
       if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // (alpha = 1 where a row kept its reference)
 #pragma unroll
-        for (int r = 0; r < kRT2; ++r)
+        for (int r = 0; r < kRT2; ++r) {
 #pragma unroll
           for (int j = 0; j < kD / 16; ++j) o[r][j] *= alpha[r];
+          lacc[r] *= alpha[r];
+        }
       }
       const int vq = lane & 3, vv4 = (lane & 15) >> 2;
 #pragma unroll
@@ -428,11 +425,13 @@ __global__ __launch_bounds__(kThreads2, 2) void attn_fwd_kernel2(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < kRT2; ++r) o[r][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[r][c], o[r][jd], 0, 0, 0);
         }
+#pragma unroll
+        for (int r = 0; r < kRT2; ++r) lacc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[r][c], lacc[r], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int r = 0; r < kRT2; ++r) {
-      const float lsum = row_sum4(l[r]);
+      const float lsum = lacc[r][0];
       const float inv = 1.0f / lsum;
       if (a.lse && lg == 0) a.lse[(seq0 + q_row[r]) * a.q_heads + h] = (m[r] + __log2f(lsum)) * 0.69314718055994531f;
       unsigned short* C = reinterpret_cast<unsigned short*>(a.C) + (seq0 + q_row[r]) * a.ld_c + int64_t(h) * kD + 4 * lg;
