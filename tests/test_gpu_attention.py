@@ -167,3 +167,88 @@ def test_attention_core_backward_workload_sequence(key):
     for rows, label in ((slice(0, seq), " (first sequence)"), (slice(w.tokens - seq, w.tokens), " (last sequence)")):
         ref = A.attn_core_bwd(f(QKV[rows]), f(dC[rows]), qh, kvh, 128, seq)
         _check_dqkv(dQKV[rows], ref, qh, kvh, label)
+
+
+def _ramped_qkv(w, seq, seed):
+    """QKV whose scores (log2 units, scale 1/sqrt(128) log2 e) follow a chosen level per 128-key block
+    of each sequence: every query is 8 e1 and every key a_b e1 plus small noise, so a query's score
+    against a key of block b is about 1.02 a_b. The levels make the row maximum stay within 2^8 of
+    the first block's (a_1 = 5), jump past it (a_2 = 20), fall (a_3 = -10), rise to just under 2^8
+    above the reference (a_4 = 27) and past it (a_5 = 29), then return near 0."""
+    qh, kvh = w.q_heads_shard, w.kv_heads_shard
+    g = torch.Generator().manual_seed(seed)
+    QKV = (0.1 * torch.randn((w.tokens, w.qkv_width), generator=g)).float()
+    levels = [0.0, 5.0, 20.0, -10.0, 27.0, 29.0] + [0.0] * 10
+    pos = torch.arange(w.tokens) % seq
+    a = torch.tensor([levels[p // 128] for p in pos.tolist()]) + 0.25 * torch.randn(w.tokens, generator=g)
+    for h in range(qh):
+        QKV[:, h * 128] = 8.0
+    for k in range(kvh):
+        QKV[:, (qh + k) * 128] = a
+    return QKV.to(torch.bfloat16)
+
+
+def _dq_large_key_bound(Q, K, V, dO, scale, qh):
+    """Element bound on dQ[t, h, 0] (the dimension that carries the large keys) from the arithmetic
+    of the backward: dQ = scale * sum_s dS[t, s] K[s] with dS = P (dP - D) rounded to bf16 (relative
+    2^-9 each, taken as 2^-8), D = sum_d dO O computed from the forward's bf16 O (absolute error at
+    most 2^-8 sum_d |dO O|, which enters every dS of the row times P), and dQ itself rounded to bf16.
+    Since sum_s dS = 0, dQ along a direction where every key is large is a cancelling sum: its error
+    follows sum_s |dS| |K|, not |dQ|. fp64, causal, one key/value head."""
+    n = Q.shape[0]
+    mask = np.tril(np.ones((n, n), dtype=bool))
+    k0 = np.abs(K[:, 0])
+    out = np.zeros((n, qh))
+    for h in range(qh):
+        q = Q[:, h * 128:(h + 1) * 128]
+        S = np.where(mask, (q @ K.T) * scale, -np.inf)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        do = dO[:, h * 128:(h + 1) * 128]
+        O = P @ V
+        dP = do @ V.T
+        D = (do * O).sum(axis=1, keepdims=True)
+        dS = P * (dP - D)
+        dq0 = scale * (dS @ K[:, 0])
+        d_err = 2.0 ** -8 * np.abs(do * O).sum(axis=1)
+        out[:, h] = 2.0 ** -8 * (scale * (np.abs(dS) @ k0) + np.abs(dq0)) + scale * d_err * (P @ k0) + 1e-6
+    return out
+
+
+def test_attention_core_moving_row_maximum():
+    """Scores whose row maximum rises by less than 2^8 (the row keeps its softmax reference, P up to
+    about 2^7) and by more (the reference moves), at the 70B shard shape (the four-wave forward
+    kernel): the forward, the row log-sum-exp and the backward of the last sequence against the
+    oracle, and that sequence alone (the eight-wave kernel) bit-equal to its rows of the batch.
+    dQ along the large keys' dimension is checked against the bound of _dq_large_key_bound (the
+    library before the lazy reference missed the plain Frobenius bound there by the same amount,
+    4.6e-2 against 5e-3: bf16 dS times keys of 20-30)."""
+    w = synth.WORKLOADS["llama3_70b_layer"]
+    seq = 2048
+    qh, kvh = w.q_heads_shard, w.kv_heads_shard
+    _case("moving maximum", key=w.key, tokens=w.tokens, seq_len=seq)
+    QKV = _ramped_qkv(w, seq, 950)
+    dC = synth.randn_bf16((w.tokens, w.ctx_width), 1.0, 951)
+    C, lse, dQKV = _run_bwd(w, QKV, dC, seq)
+    f = L.as_f64
+    last = slice(w.tokens - seq, w.tokens)
+    G.assert_parity(C[last], A.attn_core_fwd(f(QKV[last]), qh, kvh, 128, seq), "C (last sequence)")
+    G.assert_parity(lse[last], A.attn_core_lse(f(QKV[last]), qh, kvh, 128, seq), "lse (last sequence)")
+    ref = A.attn_core_bwd(f(QKV[last]), f(dC[last]), qh, kvh, 128, seq)
+    q0, k0 = qh * 128, (qh + kvh) * 128
+    G.assert_parity(dQKV[last][:, q0:k0], ref[:, q0:k0], "dK (last sequence)")
+    G.assert_parity(dQKV[last][:, k0:], ref[:, k0:], "dV (last sequence)")
+    other = [c for c in range(q0) if c % 128 != 0]
+    G.assert_parity(dQKV[last][:, other], ref[:, other], "dQ except the large keys' dimension")
+    Qf, Kf, Vf = f(QKV[last])[:, :q0], f(QKV[last])[:, q0:k0], f(QKV[last])[:, k0:]
+    bound = _dq_large_key_bound(Qf, Kf, Vf, f(dC[last]), 1.0 / np.sqrt(128.0), qh)
+    err = np.abs(dQKV[last][:, 0:q0:128].float().cpu().numpy() - ref[:, 0:q0:128])
+    worst = float((err / bound).max())
+    print(f"dQ along the large keys: max error / bound {worst:.3f}", flush=True)
+    assert worst <= 1.0
+    w1 = synth.custom("attn_move1", 952, tokens=seq, hidden=8192, ffn=64, tp=8, act="swiglu", bias=False,
+                      row_slices=1, col_slices=1, heads=64, kv_heads=8, head_dim=128)
+    assert (w1.q_heads_shard, w1.kv_heads_shard) == (qh, kvh)
+    C1, lse1, _ = _run_bwd(w1, QKV[last].contiguous(), dC[last].contiguous(), seq)
+    assert torch.equal(C1, C[last])
+    assert torch.equal(lse1, lse[last])
