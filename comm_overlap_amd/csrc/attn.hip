@@ -30,7 +30,7 @@
 // for two blocks per CU), and capping this kernel at 128 registers for two blocks per CU (a few
 // spills; 70B 3-6% faster, 13B 18% slower). 128-key blocks (half the barriers and
 // softmax rounds of 64-key ones, twice the independent S tiles) ran 4-5% faster than 64-key ones;
-// with 242 registers one block runs per CU.
+// with 217 registers one block runs per CU.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 // The same attention with four waves of 32 query rows (two 16-row tiles each) per 128-row block: each
 // K and V fragment read from LDS serves twice the rows. K and V tiles come by direct global -> LDS
 // loads (buffer_load_dwordx4 ... lds; lane l of a 1-KB run fetches the chunk the swizzle puts at
-// its LDS slot), which keeps the staging registers free: 252 registers, two blocks per CU. Taken
+// its LDS slot), which keeps the staging registers free: 230 registers, two blocks per CU. Taken
 // when the paired work items give at least two workgroups per CU; with fewer, most CUs would hold
 // one four-wave block, which has no second wave per SIMD to hide its waits (the 13B shard's 160
 // pairs: 82.5 us against the eight-wave kernel's 61.9), so the eight-wave kernel runs. Measured at
