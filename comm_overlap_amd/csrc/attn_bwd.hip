@@ -16,7 +16,8 @@
 //   3. attn_bwd_dq_kernel    one block per (sequence, query head, 128-query block), 8 waves of 16
 //                            queries, walking the key blocks up to the diagonal (the forward's
 //                            structure): S and dP with K / V rows from LDS, dS as above, dQ += dS K
-//                            with K read across keys.
+//                            with K read across keys. With enough blocks for two per CU,
+//                            attn_bwd_dq_kernel2: four waves of two 16-query tiles (the same bits).
 // A key/value head shared by several query heads (grouped heads) gets per-head fp32 partials of dK
 // and dV, summed in head order by attn_bwd_group_kernel, so the result does not depend on timing.
 // Every product is v_mfma_f32_16x16x32_bf16; P and dS are rounded to bf16 for their products.
@@ -39,6 +40,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = kAttnHeadDim;   // 128
 constexpr int kWaves = 8;
@@ -402,6 +404,150 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     store_bf16x4(out + 16 * jd, dq[jd][0] * scale, dq[jd][1] * scale, dq[jd][2] * scale, dq[jd][3] * scale);
 }
 
+// ------------------------------------------------------- 3b. dQ with four waves of two query tiles
+// The same dQ with four waves of two 16-query tiles each (128 queries per block) walking 64-key
+// steps: each K or V fragment read from LDS serves both tiles, half the LDS reads per MFMA of
+// attn_bwd_dq_kernel, and K and V come by direct global -> LDS loads (one 1-KB run per load; lane l
+// fetches the chunk the swizzle puts at its slot), so 48 KB of LDS and two blocks per CU. Every dQ
+// element sums the same 32-key chunks in the same order as attn_bwd_dq_kernel, and S, P and dS are
+// the same expressions: the same bits. Taken when the work items give two blocks per CU.
+constexpr int kWaves2 = 4, kRT2 = 2, kThreads2 = 64 * kWaves2;
+constexpr int kKStep2 = 64;                  // keys per step
+constexpr int kDq2Tile = kKStep2 * kRowB;    // 16 KB per tile: K by rows, K across, V by rows
+static_assert(16 * kRT2 * kWaves2 == kQBlock, "query rows per block");
+static_assert(kDq2Tile == 16 * 1024 && kWaves2 * 4 * 1024 == kDq2Tile, "four 1-KB runs per wave and tile");
+
+__global__ __launch_bounds__(kThreads2, 2) void attn_bwd_dq_kernel2(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char k_r[kDq2Tile];
+  __shared__ __attribute__((aligned(1024))) char k_t[kDq2Tile];
+  __shared__ __attribute__((aligned(1024))) char v_r[kDq2Tile];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nqb = a.seq_len / kQBlock;
+  const int nbh = int(a.tokens / a.seq_len) * a.q_heads;
+  const int item = int(blockIdx.x);
+  const int rr = item / nbh, bh = item - rr * nbh;
+  const int qb = nqb - 1 - rr;  // the blocks with the most keys first
+  const int b = bh / a.q_heads, h = bh - b * a.q_heads;
+  const int g = h / (a.q_heads / a.kv_heads);
+  const int64_t seq0 = int64_t(b) * a.seq_len;
+  const unsigned short* qkv = reinterpret_cast<const unsigned short*>(a.QKV);
+  const unsigned short* dO = reinterpret_cast<const unsigned short*>(a.dC);
+  const int64_t ld = a.ld_qkv;
+  const int64_t qcol = int64_t(h) * kD, kcol = int64_t(a.q_heads + g) * kD;
+  const int64_t vcol = int64_t(a.q_heads + a.kv_heads + g) * kD;
+
+  // the lane's rows of the wave's two query tiles: Q and dO as operands, log-sum-exp and D
+  int q_row[kRT2];
+  bf16x8 qf[kRT2][kD / 32], of[kRT2][kD / 32];
+  float lse2[kRT2], dd[kRT2];
+#pragma unroll
+  for (int r = 0; r < kRT2; ++r) {
+    q_row[r] = qb * kQBlock + (wave * kRT2 + r) * 16 + lr;
+    const unsigned short* qp = qkv + (seq0 + q_row[r]) * ld + qcol + 8 * lg;
+    const unsigned short* op = dO + (seq0 + q_row[r]) * a.ld_c + qcol + 8 * lg;
+#pragma unroll
+    for (int kk = 0; kk < kD / 32; ++kk) {
+      qf[r][kk] = load8(qp + 32 * kk);
+      of[r][kk] = load8(op + 32 * kk);
+    }
+    lse2[r] = a.lse[(seq0 + q_row[r]) * a.q_heads + h] * kLog2e;
+    dd[r] = a.Dq[(seq0 + q_row[r]) * a.q_heads + h];
+  }
+  f32x4 dq[kRT2][kD / 16];
+#pragma unroll
+  for (int r = 0; r < kRT2; ++r)
+#pragma unroll
+    for (int j = 0; j < kD / 16; ++j) dq[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this thread's four runs of each tile: run w * 4 + p holds key rows 4 (w * 4 + p) .. + 3 of the
+  // step; lane l writes LDS bytes 16 l of the run (row 4 (w * 4 + p) + l / 16, slot l % 16), which
+  // hold logical chunk slot ^ swizzle(row). Byte offsets from the step's first row; QKV spans less
+  // than 4 GiB (checked by the launcher).
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.QKV), (short)0, (int)(uint32_t)(a.tokens * ld * 2), 0x00020000);
+  uint32_t kro[4], kto[4], vro[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = (wave * 4 + p) * 4 + (lane >> 4), slot = lane & 15;
+    kro[p] = uint32_t((int64_t(row) * ld + kcol + ((slot ^ swz_r(row)) << 3)) * 2);
+    kto[p] = uint32_t((int64_t(row) * ld + kcol + ((slot ^ swz_t(row)) << 3)) * 2);
+    vro[p] = uint32_t((int64_t(row) * ld + vcol + ((slot ^ swz_r(row)) << 3)) * 2);
+  }
+  const int nks = (qb * kQBlock + kQBlock) / kKStep2;  // key steps up to the diagonal
+  const int first_diag = (qb * kQBlock) / kKStep2;
+  const float sl2 = a.scale_log2;
+  for (int ks = 0; ks < nks; ++ks) {
+    __syncthreads();  // every wave is done with the previous step's tiles
+    const uint32_t soff = uint32_t((seq0 + int64_t(ks) * kKStep2) * ld * 2);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int run = (wave * 4 + p) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(k_r + run), 16, kro[p], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(k_t + run), 16, kto[p], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(v_r + run), 16, vro[p], soff, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // (vmcnt 0)
+    __syncthreads();
+
+    // S and dP of both tiles x 64 keys; each K and V fragment serves the two tiles
+    f32x4 s[kRT2][kKStep2 / 16], dp[kRT2][kKStep2 / 16];
+#pragma unroll
+    for (int j = 0; j < kKStep2 / 16; ++j) {
+#pragma unroll
+      for (int r = 0; r < kRT2; ++r) s[r][j] = dp[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kD / 32; ++kk) {
+        const bf16x8 kf = frag_row(k_r, 16 * j, lane, kk);
+        const bf16x8 vf = frag_row(v_r, 16 * j, lane, kk);
+#pragma unroll
+        for (int r = 0; r < kRT2; ++r) {
+          s[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[r][kk], s[r][j], 0, 0, 0);
+          dp[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, of[r][kk], dp[r][j], 0, 0, 0);
+        }
+      }
+    }
+    if (ks >= first_diag) {  // the causal mask, on the diagonal steps only
+#pragma unroll
+      for (int r = 0; r < kRT2; ++r)
+#pragma unroll
+        for (int j = 0; j < kKStep2 / 16; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (ks * kKStep2 + 16 * j + 4 * lg + v > q_row[r]) s[r][j][v] = -INFINITY;
+    }
+    bf16x8 sf[kRT2][kKStep2 / 32];
+#pragma unroll
+    for (int r = 0; r < kRT2; ++r)
+#pragma unroll
+      for (int j = 0; j < kKStep2 / 16; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r][j][v], sl2, -lse2[r]));
+          sf[r][j >> 1][4 * (j & 1) + v] = (__bf16)(p * (dp[r][j][v] - dd[r]));
+        }
+    // dQ += dS K, the K fragment read across keys once for both tiles
+#pragma unroll
+    for (int c = 0; c < kKStep2 / 32; ++c)
+#pragma unroll
+      for (int jd = 0; jd < kD / 16; ++jd) {
+        const bf16x8 kt = frag_across(k_t, c, jd, lane);
+#pragma unroll
+        for (int r = 0; r < kRT2; ++r) dq[r][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, sf[r][c], dq[r][jd], 0, 0, 0);
+      }
+  }
+  const float scale = a.scale;
+#pragma unroll
+  for (int r = 0; r < kRT2; ++r) {
+    unsigned short* out = reinterpret_cast<unsigned short*>(a.dQKV) + (seq0 + q_row[r]) * a.ld_qkv + qcol + 4 * lg;
+#pragma unroll
+    for (int jd = 0; jd < kD / 16; ++jd)
+      store_bf16x4(out + 16 * jd, dq[r][jd][0] * scale, dq[r][jd][1] * scale, dq[r][jd][2] * scale,
+                   dq[r][jd][3] * scale);
+  }
+}
+
 template <class K>
 hipError_t launch(K kernel, int blocks, int threads, int lds, hipStream_t s, hipEvent_t start, hipEvent_t stop,
                   const AttnBwdArgs& a) {
@@ -451,8 +597,11 @@ hipError_t launch_attn_bwd(AttnBwdArgs a, void* ws, hipStream_t stream, hipEvent
     e = launch(attn_bwd_group_kernel, int((n + 255) / 256), 256, 0, stream, nullptr, nullptr, a);
     if (e != hipSuccess) return e;
   }
-  return launch(attn_bwd_dq_kernel, nseq * a.q_heads * (a.seq_len / kQBlock), kThreads, kDqLds, stream, nullptr,
-                stop, a);
+  const int items = nseq * a.q_heads * (a.seq_len / kQBlock);
+  // the four-wave dQ kernel when its blocks fill two per CU (and its loads' 32-bit offsets span QKV)
+  if (items >= 2 * 256 && a.tokens * a.ld_qkv * 2 < (int64_t(1) << 32))
+    return launch(attn_bwd_dq_kernel2, items, kThreads2, 0, stream, nullptr, stop, a);
+  return launch(attn_bwd_dq_kernel, items, kThreads, kDqLds, stream, nullptr, stop, a);
 }
 
 }  // namespace tps

@@ -219,7 +219,8 @@ def test_attention_core_moving_row_maximum():
     """Scores whose row maximum rises by less than 2^8 (the row keeps its softmax reference, P up to
     about 2^7) and by more (the reference moves), at the 70B shard shape (the four-wave forward
     kernel): the forward, the row log-sum-exp and the backward of the last sequence against the
-    oracle, and that sequence alone (the eight-wave kernel) bit-equal to its rows of the batch.
+    oracle, and that sequence alone (the eight-wave forward and dQ kernels) bit-equal to its rows of
+    the batch (the four-wave ones).
     dQ along the large keys' dimension is checked against the bound of _dq_large_key_bound (the
     library before the lazy reference missed the plain Frobenius bound there by the same amount,
     4.6e-2 against 5e-3: bf16 dS times keys of 20-30)."""
@@ -249,6 +250,9 @@ def test_attention_core_moving_row_maximum():
     w1 = synth.custom("attn_move1", 952, tokens=seq, hidden=8192, ffn=64, tp=8, act="swiglu", bias=False,
                       row_slices=1, col_slices=1, heads=64, kv_heads=8, head_dim=128)
     assert (w1.q_heads_shard, w1.kv_heads_shard) == (qh, kvh)
-    C1, lse1, _ = _run_bwd(w1, QKV[last].contiguous(), dC[last].contiguous(), seq)
+    C1, lse1, dQKV1 = _run_bwd(w1, QKV[last].contiguous(), dC[last].contiguous(), seq)
     assert torch.equal(C1, C[last])
     assert torch.equal(lse1, lse[last])
+    # the batch's dQ comes from the four-wave dQ kernel (1024 blocks), the sequence's from the
+    # eight-wave one (64 blocks)
+    assert torch.equal(dQKV1, dQKV[last])
