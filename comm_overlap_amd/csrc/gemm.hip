@@ -8,10 +8,13 @@
 //   * 128 x 256, 8 waves, waves of 64 x 64, one block per CU (96 KB LDS);
 //   * 128 x 128, 4 waves (2 x 2), waves of 64 x 64, two blocks per CU (64 KB LDS each);
 //   * 256 x 256, 256 x 160 and 256 x 320 with 4 waves (2 x 2, one wave per SIMD), waves of
-//     128 x 128 / 128 x 80 / 128 x 160, one block per CU, for products with k a multiple of 64
-//     (256 x 256 in every operand layout and for split runs; the others forward only): a
-//     software-pipelined loop (barrier between the two k steps, loads two blocks ahead, LDS reads
-//     and load issue interleaved one by one with the MFMAs) that leaves no wait to another wave.
+//     128 x 128 / 128 x 80 / 128 x 160, and 256 x 224 with 4 waves stacked along m (64 x 224,
+//     forward SwiGLU only), one block per CU, for products with k a multiple of 64 (256 x 256 in
+//     every operand layout and for split runs; 256 x 320 forward only; 256 x 160 forward and the
+//     activation gradients with a bf16 or GeLU-gradient epilogue, whose B tile, read across k, is
+//     padded to 256 columns in LDS): a software-pipelined loop (barrier between the two k steps,
+//     loads two blocks ahead, LDS reads and load issue interleaved one by one with the MFMAs) that
+//     leaves no wait to another wave.
 // The launcher picks per product the tile with the smallest estimated time on 256 CUs: whole
 // rounds of resident blocks times the tile's work over its measured per-CU rate. Larger tiles move
 // fewer bytes per flop; the others cut the last, partly filled round (e.g. a 4096 x 5120 product is
@@ -70,8 +73,9 @@ struct Tile {
   static constexpr bool kNcA = 1024 % (BM * 2) == 0;
   static constexpr bool kDualOk = kFN % 2 == 0;
   // LDS columns of a B tile read across k: BN itself when its k rows fill 1-KB runs whole, else
-  // (narrower four-wave tiles: 160, 224 columns) 256, the columns past BN loaded but never read,
-  // so that the runs and the conflict-free swizzle of 256-column rows serve it unchanged; 0: none
+  // (four-wave tiles narrower than 256, e.g. 256 x 160 on activation gradients) 256, the columns
+  // past BN loaded but never read, so that the runs and the conflict-free swizzle of 256-column
+  // rows serve it unchanged; 0: none
   static constexpr int kBnL = 1024 % (BN * 2) == 0 ? BN : (WM * WN == 4 && BM == 256 && BN < 256) ? 256 : 0;
   static constexpr bool kNcB = kBnL > 0;
   static constexpr int kBNcTileBytes = kBnL * kBKTile * 2;
