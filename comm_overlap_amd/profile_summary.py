@@ -15,6 +15,10 @@
         clock = busy cycles / duration, MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (busy cycles x 1024
         SIMDs), wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES, LDS conflicts = SQ_LDS_BANK_CONFLICT /
         SQ_LDS_IDX_ACTIVE
+    python -m comm_overlap_amd.profile_summary insts RESULTS.db [--match attn]
+        per kernel (medians over its dispatches) from a pass with SQ_INSTS_VALU, SQ_INSTS_MFMA,
+        SQ_INSTS_LDS and SQ_INSTS_VALU_TRANS_F32: the vector ALU, LDS and transcendental
+        instructions issued per MFMA instruction
     python -m comm_overlap_amd.profile_summary requests P1.db P2.db P3.db P4.db [--match gemm_kernel]
         L1 -> L2 read requests of one kernel from four passes (SQ wave and LDS counters; TA/TD;
         TCP stalls; TCP -> L2 requests and L2 hits, misses and miss latency), each counter summed
@@ -185,6 +189,33 @@ def counters(db, match, simds=1024, xcds=8):
               f"mfma_busy {100 * busy:.1f}%, WAIT_ANY {100 * wait:.1f}%, ldsconf {100 * lds:.1f}%")
 
 
+def insts(db, match):
+    c = sqlite3.connect(db)
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for name, disp, cname, val in c.execute(
+            "select name, dispatch_id, counter_name, counter_value from pmc_events"):
+        if match in name:
+            vals[disp][cname] += val
+            names[disp] = name
+    per = collections.defaultdict(list)
+    for disp, v in vals.items():
+        per[names[disp]].append(v)
+
+    def med(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2]
+
+    for name, rows in sorted(per.items(), key=lambda kv: -len(kv[1])):
+        mfma = med([v.get("SQ_INSTS_MFMA", 0.0) for v in rows])
+        if mfma <= 0:
+            print(f"  {name[:70]}: {len(rows)} dispatches, no MFMA instructions")
+            continue
+        ratio = {k: med([v.get(f"SQ_INSTS_{k}", 0.0) for v in rows]) / mfma for k in ("VALU", "LDS", "VALU_TRANS_F32")}
+        print(f"  {name[:70]}: {len(rows)} dispatches, per MFMA instruction: VALU {ratio['VALU']:.2f}, "
+              f"LDS {ratio['LDS']:.2f}, transcendental {ratio['VALU_TRANS_F32']:.2f}")
+
+
 def _pass_medians(db, match):
     c = sqlite3.connect(db)
     per = collections.defaultdict(lambda: collections.defaultdict(float))
@@ -243,12 +274,18 @@ def main(argv=None):
     k = sub.add_parser("counters")
     k.add_argument("db")
     k.add_argument("--match", default="gemm_kernel")
+    n = sub.add_parser("insts")
+    n.add_argument("db")
+    n.add_argument("--match", default="attn")
     q = sub.add_parser("requests")
     q.add_argument("dbs", nargs=4)
     q.add_argument("--match", default="gemm_kernel")
     a = ap.parse_args(argv)
     if a.cmd == "requests":
         requests(a.dbs, a.match)
+        return 0
+    if a.cmd == "insts":
+        insts(a.db, a.match)
         return 0
     if a.cmd == "trace":
         trace(a.db, a.match)

@@ -108,6 +108,22 @@ def test_request_latency_and_requests_in_flight(tmp_path, capsys):
     assert "waves waiting on LDS 0.05" in out
 
 
+def test_instructions_per_mfma(tmp_path, capsys):
+    pmc = []
+    for d, scale in ((0, 1.0), (1, 1.0), (2, 3.0)):  # the median dispatch is one of the first two
+        pmc += [("attn_fwd_kernel2", d, "SQ_INSTS_MFMA", 1000.0 * scale / 2), ("attn_fwd_kernel2", d, "SQ_INSTS_MFMA", 1000.0 * scale / 2),
+                ("attn_fwd_kernel2", d, "SQ_INSTS_VALU", 3300.0 * scale), ("attn_fwd_kernel2", d, "SQ_INSTS_LDS", 700.0 * scale),
+                ("attn_fwd_kernel2", d, "SQ_INSTS_VALU_TRANS_F32", 480.0 * scale)]
+    pmc += [("attn_bwd_pre_kernel", 3, "SQ_INSTS_MFMA", 0.0), ("attn_bwd_pre_kernel", 3, "SQ_INSTS_VALU", 50.0),
+            ("gemm_kernel<A>", 4, "SQ_INSTS_MFMA", 10.0)]
+    db = _db(tmp_path / "i.db", pmc=pmc)
+    assert PS.main(["insts", db]) == 0
+    out = capsys.readouterr().out
+    assert "attn_fwd_kernel2: 3 dispatches, per MFMA instruction: VALU 3.30, LDS 0.70, transcendental 0.48" in out
+    assert "attn_bwd_pre_kernel: 1 dispatches, no MFMA instructions" in out
+    assert "gemm_kernel" not in out
+
+
 def test_missing_kernel_is_an_error(tmp_path):
     db = _db(tmp_path / "e.db", kernels=[("other", 64, 0, 10)],
              pmc=[("other", 0, "GRBM_GUI_ACTIVE", 8.0)])
